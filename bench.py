@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Benchmark of the Groth16 H-polynomial pipeline on one MI355X.
+
+One step = one g16_h_compute over device-resident inputs at n = 2^20 (A, B seeded
+uniform Fr, C = A o B, tables prepared beforehand): three inverse NTTs, the coset
+shift, three forward NTTs and H = A'B' - C' in both encodings.  Prints one JSON line.
+
+Also measured (same run, reported inside the line):
+  * each kernel (stage) of the pipeline alone, with HIP events on the stream it is
+    launched on; the slowest is the dominant kernel and carries the roofline;
+  * the standalone forward NTT at 2^20 (Gbutterfly/s);
+  * the CPU oracle on the host, single-threaded, on the same 2^20 workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MAD_PEAK_T = 256 * 64 * 2.4e9 / 1e12   # v_mad_u64_u32: 256 CUs x 64 lanes x 2.4 GHz, T/s
+HBM_PEAK_GBS = 8000.0
+MADS_PER_MUL = 136                      # 8-limb CIOS Montgomery product: 2 s^2 + s
+MADS_PER_REDC = 72                      # Montgomery reduction alone: s^2 + s
+FR_BYTES = 32
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--log-n", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stage-reps", type=int, default=10)
+    return ap.parse_args()
+
+
+def stage_work(kind: str, join: bool, n_vec: int, k: int, n: int):
+    """Algorithmic (limb products, bytes) of one pipeline stage.
+
+    Strided batch of k passes on n_vec vectors: n_vec k n/2 butterflies, each one
+    twiddle product; reads and writes each element once.  Fused lowest batch: the last
+    k passes of the inverse and the first k of the forward transform (the pass on bit 0
+    of each needs no product) plus the coset multiply, and one read of the coset table
+    per vector.  Join: A'B' (one product), h_std (one reduction), reads A' and B',
+    writes h_mont and h_std instead of the vector.
+    """
+    if kind == "fused":
+        muls = n_vec * ((2 * k - 2) * n // 2 + n)
+        byts = n_vec * 3 * n * FR_BYTES
+    else:
+        muls = n_vec * k * n // 2
+        byts = n_vec * 2 * n * FR_BYTES
+    mads = muls * MADS_PER_MUL
+    if join:
+        mads += n * (MADS_PER_MUL + MADS_PER_REDC)
+        byts += 3 * n * FR_BYTES        # + A', B' reads, + the second output
+    return mads, byts
+
+
+def stage_list(plan, n_vec=3):
+    """(kind, join, n_vec, k) of each stage of g16_h_compute, in launch order."""
+    nb = len(plan)
+    out = []
+    if nb == 1:
+        return [("fused", False, 2, plan[0]), ("fused", True, 1, plan[0])]
+    for b in range(nb - 1, 0, -1):
+        out.append(("dif", False, n_vec, plan[b]))
+    out.append(("fused", False, n_vec, plan[0]))
+    for b in range(1, nb):
+        if b == nb - 1:
+            out.append(("dit", False, n_vec - 1, plan[b]))
+            out.append(("dit", True, 1, plan[b]))
+        else:
+            out.append(("dit", False, n_vec, plan[b]))
+    return out
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "groth16_polynomial_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(stage_name: str, src_hash: str):
+    """HBM bytes per dispatch of the dominant kernel, from the committed counter
+    summary, if it was taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "hbm_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha256_16") != src_hash:
+        return None
+    return d.get("stages", {}).get(stage_name, {}).get("hbm_bytes_per_dispatch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (--gpus %d requested); the "
+              "multi-GPU sharding is described in DESIGN.md and not implemented"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from groth16_polynomial_amd import binding as g
+    from groth16_polynomial_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    log_n = args.log_n
+    n = 1 << log_n
+    print("[bench] preparing 2^%d inputs" % log_n, file=sys.stderr, flush=True)
+
+    a, b = synth.h_inputs(3, log_n)
+    ad, bd = g.to_mont(g.to_device(a)), g.to_mont(g.to_device(b))
+    cd = g.fr_mul(ad, bd)
+    ctx = g.HContext(log_n)
+    hm, hs = g.empty_fr(n), g.empty_fr(n)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    # ---- the timed region: K whole pipelines
+    for _ in range(args.warmup):
+        ctx.h_compute(ad, bd, cd, hm, hs)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        ctx.h_compute(ad, bd, cd, hm, hs)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    print("[bench] h_compute 2^%d: %.4f ms/step (wall %.3f s)" % (log_n, ms_per_step, wall),
+          file=sys.stderr, flush=True)
+
+    plan = g.batch_plan(log_n)
+    butterflies = 6 * (n // 2) * log_n
+    total_muls = 0
+    total_bytes = 0
+    stages = stage_list(plan)
+    for kind, join, nv, k in stages:
+        m, by = stage_work(kind, join, nv, k, n)
+        total_muls += m
+        total_bytes += by
+
+    # ---- each stage alone, HIP events on the launch stream
+    count = ctx.stage_count()
+    assert count == len(stages)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(count)]
+    acc = [0.0] * count
+    for _ in range(args.stage_reps):
+        for i in range(count):
+            evs[i][0].record(stream)
+            ctx.h_stage(i, ad, bd, cd, hm, hs)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        for i in range(count):
+            acc[i] += evs[i][0].elapsed_time(evs[i][1])
+    stage_ms = [x / args.stage_reps for x in acc]
+    dom = int(np.argmax(stage_ms))
+    kind, join, nv, k = stages[dom]
+    dom_mads, dom_bytes = stage_work(kind, join, nv, k, n)
+    dom_s = stage_ms[dom] / 1e3
+    dom_name = "%s_k%d_v%d%s" % (kind, k, nv, "_join" if join else "")
+    achieved_t = dom_mads / dom_s / 1e12
+    src_hash = kernel_source_hash()
+    traffic = traffic_from_profiles(dom_name, src_hash)
+
+    # ---- standalone forward NTT at the same size
+    x = g.to_mont(g.to_device(synth.ntt_input(2, log_n)))
+    y = g.empty_fr(n)
+    for _ in range(3):
+        ctx.ntt_forward(x, y)
+    torch.cuda.synchronize()
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record(stream)
+    for _ in range(args.steps):
+        ctx.ntt_forward(x, y)
+    f1.record(stream)
+    torch.cuda.synchronize()
+    ntt_ms = f0.elapsed_time(f1) / args.steps
+    ntt_gbfly = (n // 2) * log_n / (ntt_ms / 1e3) / 1e9
+
+    value = butterflies / (ms_per_step / 1e3) / 1e9
+    line = {
+        "metric": "Groth16 H-pipeline ms & Fr NTT Gbutterfly/s at n=2^20; achieved HBM GB/s",
+        "value": round(value, 3),
+        "unit": "Gbutterfly/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "strong",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {
+            "workload": "H pipeline over BN254 Fr, n=2^%d: A,B seeded uniform, C=A*B, "
+                        "3 iNTT + coset shift + 3 NTT + H=A'B'-C' (h_mont, h_std)" % log_n,
+            "log_n": log_n,
+            "pass_batches": plan,
+            "stages": count,
+        },
+        "h_pipeline_ms": round(ms_per_step, 5),
+        "ntt_forward_ms": round(ntt_ms, 5),
+        "ntt_gbutterfly_s": round(ntt_gbfly, 3),
+        "hbm_gbs_algorithmic": round(total_bytes / (ms_per_step / 1e3) / 1e9, 2),
+        "pipeline_tmad_s": round(total_muls / (ms_per_step / 1e3) / 1e12, 3),
+        "pipeline_alu_frac": round(total_muls / (ms_per_step / 1e3) / 1e12 / MAD_PEAK_T, 4),
+        "stage_ms": [round(v, 5) for v in stage_ms],
+        "roofline": {
+            "bound": "alu",
+            "kernel": dom_name,
+            "achieved": round(achieved_t, 3),
+            "peak": round(MAD_PEAK_T, 3),
+            "unit": "Tmad/s",
+            "frac": round(achieved_t / MAD_PEAK_T, 4),
+            "traffic": traffic,
+            "algorithmic_bytes": dom_bytes,
+            "algorithmic_mads": dom_mads,
+            "avg_launch_ms": round(stage_ms[dom], 5),
+            "kernel_source_sha256_16": src_hash,
+        },
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        print("[bench] oracle (CPU, 1 thread) on the same 2^%d pipeline" % log_n,
+              file=sys.stderr, flush=True)
+        am, bm = oracle.to_mont(a), oracle.to_mont(b)
+        cm = oracle.pointwise_mul_mont(am, bm)
+        c0 = time.perf_counter()
+        oracle.h_pipeline(log_n, am, bm, cm)
+        cpu_s = time.perf_counter() - c0
+        line["cpu_baseline"] = {
+            "value": round(butterflies / cpu_s / 1e9, 6),
+            "unit": "Gbutterfly/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": "the whole 2^%d H pipeline once (%.1f s), single-threaded C oracle"
+                      % (log_n, cpu_s),
+        }
+    ctx.release()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,571 @@
+// libg16.so: host side of the C ABI declared in include/g16.h.
+//
+// Argument checks run on the host before anything is enqueued; every call then only
+// enqueues kernels on the caller's stream (the NTT_CU page: one stream, launches
+// queued asynchronously, one synchronisation by the caller at the end).
+#include "g16.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "kernels.hpp"
+
+using g16::Fr;
+
+namespace {
+
+constexpr uint32_t kMagic = 0x47313643u;  // "G16C"
+constexpr uint32_t kDead = 0xdeadc0deu;
+constexpr size_t kAlign = 256;
+constexpr uint32_t kThreads = 256;
+constexpr uint32_t kMaxBatches = 27;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+}  // namespace
+
+struct g16_ctx {
+    uint32_t magic;
+    uint32_t log_n;
+    int device;
+    Fr* tw_fwd;   // omega^j, j < n/2
+    Fr* tw_inv;   // omega^-j, j < n/2
+    Fr* coset;    // n^-1 s^bitrev(p), p < n
+    Fr* scratch;  // three n-element vectors
+    const uint8_t* ws_begin;
+    size_t ws_bytes;
+    Fr omega, omega_inv, shift, size_inv;  // Montgomery form
+    uint32_t n_batches;
+    uint32_t batch_k[kMaxBatches];  // lowest bits first
+};
+
+namespace {
+
+// Largest number of passes one workgroup batches in LDS (2^k elements of 32 bytes).
+uint32_t max_batch_k() {
+    const char* env = std::getenv("G16_MAX_K");
+    if (env) {
+        int v = std::atoi(env);
+        if (v >= 1 && v <= 12) return (uint32_t)v;
+    }
+    return 10u;
+}
+
+// Split log_n passes into ceil(log_n / kmax) batches of near-equal size, the larger
+// ones at the low end (the NTT_CU page, "SHARED MEMORY BUDGET" section: 18 = 9 + 9
+// rather than 10 + 8, so no batch degenerates into a tiny tail).
+uint32_t plan_batches(uint32_t log_n, uint32_t kmax, uint32_t* ks) {
+    uint32_t nb = (log_n + kmax - 1) / kmax;
+    uint32_t q = log_n / nb, rem = log_n % nb;
+    for (uint32_t i = 0; i < nb; ++i) ks[i] = q + (i < rem ? 1u : 0u);
+    return nb;
+}
+
+bool ctx_ok(const g16_ctx* c) { return c && c->magic == kMagic; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+// True when p is memory the current device can address (device or managed memory).
+bool device_pointer(const void* p) {
+    if (!p) return false;
+    hipPointerAttribute_t attr;
+    hipError_t e = hipPointerGetAttributes(&attr, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged ||
+           attr.type == hipMemoryTypeUnified;
+}
+
+int launch_status() {
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? G16_OK : G16_EHIP;
+}
+
+// Host-side domain roots (Montgomery form): g = 5, w28 = g^((r-1)/2^28),
+// s = w28^(2^(27-L)), omega = s^2.
+void domain_roots(uint32_t log_n, Fr* omega, Fr* shift, Fr* size_inv) {
+    Fr five = g16::fr_zero();
+    five.w[0] = 5u;
+    five = g16::fr_to_mont(five);
+    uint32_t e[8];
+    // (r - 1) >> 28, limb by limb
+    uint32_t rl[8];
+    for (int i = 0; i < 8; ++i) rl[i] = g16::r_limb(i);
+    rl[0] -= 1u;
+    for (int i = 0; i < 8; ++i) e[i] = (rl[i] >> 28) | (i < 7 ? (rl[i + 1] << 4) : 0u);
+    Fr s = g16::fr_pow(five, e);
+    for (uint32_t i = 0; i < 27 - log_n; ++i) s = g16::fr_mul(s, s);
+    *shift = s;
+    *omega = g16::fr_mul(s, s);
+    Fr n = g16::fr_zero();
+    if (log_n < 32) n.w[0] = 1u << log_n;
+    *size_inv = g16::fr_inv(g16::fr_to_mont(n));
+}
+
+template <g16::Mode M, bool J>
+int launch_batch(const g16::BatchParams& p, uint32_t n_vec, hipStream_t stream) {
+    const uint32_t k = p.k, L = p.log_n;
+    g16::BatchParams q = p;
+    uint32_t log_spw = 0;
+    if (k < 9) log_spw = (9 - k) < (L - k) ? (9 - k) : (L - k);
+    q.log_spw = log_spw;
+    uint64_t groups = (1ull << (L - k)) >> log_spw;
+    size_t lds = (size_t(1) << (k + log_spw)) * sizeof(Fr);
+    dim3 grid((uint32_t)groups, n_vec, 1);
+    hipLaunchKernelGGL((g16::ntt_batch_kernel<M, J>), grid, dim3(kThreads), lds, stream, q);
+    return launch_status();
+}
+
+g16::BatchParams base_params(const g16_ctx* c) {
+    g16::BatchParams p;
+    std::memset(&p, 0, sizeof p);
+    p.log_n = c->log_n;
+    return p;
+}
+
+uint32_t batch_s0(const g16_ctx* c, uint32_t idx) {
+    uint32_t s = 0;
+    for (uint32_t i = 0; i < idx; ++i) s += c->batch_k[i];
+    return s;
+}
+
+size_t vec_bytes(const g16_ctx* c) { return (size_t(1) << c->log_n) * sizeof(Fr); }
+
+// Forward (inverse = false) or inverse transform, natural order in and out.
+int run_ntt(g16_ctx* c, const void* in, void* out, void* stream, bool inverse) {
+    if (!ctx_ok(c)) return c ? G16_ESTATE : G16_EINVAL;
+    if (!in || !out) return G16_EINVAL;
+    const size_t nbytes = vec_bytes(c);
+    if (in != out && overlaps(in, nbytes, out, nbytes)) return G16_EALIAS;
+    if (overlaps(in, nbytes, c->ws_begin, c->ws_bytes) ||
+        overlaps(out, nbytes, c->ws_begin, c->ws_bytes))
+        return G16_EALIAS;
+    if (!device_pointer(in) || !device_pointer(out)) return G16_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    Fr* scr = c->scratch;
+    g16::BatchParams p = base_params(c);
+    p.tw = inverse ? c->tw_inv : c->tw_fwd;
+    p.use_kscale = inverse ? 1u : 0u;
+    p.kscale = c->size_inv;
+    p.s0 = 0;
+    p.k = c->batch_k[0];
+    p.src[0] = (const Fr*)in;
+    const bool single = c->n_batches == 1;
+    p.dst[0] = (single && in != out) ? (Fr*)out : scr;
+    int rc = launch_batch<g16::Mode::HeadBitrev, false>(p, 1, s);
+    if (rc) return rc;
+    if (single) {
+        if (in == out) {
+            if (hipMemcpyAsync(out, scr, nbytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
+                return G16_EHIP;
+        }
+        return G16_OK;
+    }
+    for (uint32_t b = 1; b < c->n_batches; ++b) {
+        g16::BatchParams t = base_params(c);
+        t.tw = p.tw;
+        t.s0 = batch_s0(c, b);
+        t.k = c->batch_k[b];
+        t.src[0] = scr;
+        t.dst[0] = (b + 1 == c->n_batches) ? (Fr*)out : scr;
+        rc = launch_batch<g16::Mode::DitStrided, false>(t, 1, s);
+        if (rc) return rc;
+    }
+    return G16_OK;
+}
+
+// One kernel launch of a pipeline: which kernel, its parameters and vector count.
+struct Launch {
+    g16::Mode mode;
+    bool join;
+    g16::BatchParams p;
+    uint32_t n_vec;
+};
+
+constexpr uint32_t kMaxLaunches = 2 * kMaxBatches + 2;
+
+int exec_launch(const Launch& l, hipStream_t s) {
+    using g16::Mode;
+    switch (l.mode) {
+        case Mode::Fused:
+            return l.join ? launch_batch<Mode::Fused, true>(l.p, l.n_vec, s)
+                          : launch_batch<Mode::Fused, false>(l.p, l.n_vec, s);
+        case Mode::DitStrided:
+            return l.join ? launch_batch<Mode::DitStrided, true>(l.p, l.n_vec, s)
+                          : launch_batch<Mode::DitStrided, false>(l.p, l.n_vec, s);
+        case Mode::DifStrided:
+            return launch_batch<Mode::DifStrided, false>(l.p, l.n_vec, s);
+        default:
+            return launch_batch<Mode::HeadBitrev, false>(l.p, l.n_vec, s);
+    }
+}
+
+// The launches of stages 1-3 for n_vec vectors srcs[v] -> coset evaluations in dsts[v]
+// (dsts may equal srcs only when the context has a single batch).  With join, the last
+// vector's final batch writes H = dsts[0] * dsts[1] - x into h_mont / h_std instead,
+// in a launch of its own after the other vectors are finished.
+uint32_t plan_coset(const g16_ctx* c, const Fr* const* srcs, Fr* const* dsts, uint32_t n_vec,
+                    bool join, Fr* h_mont, Fr* h_std, Launch* out) {
+    const uint32_t nb = c->n_batches;
+    const uint32_t plain_vec = join ? n_vec - 1 : n_vec;
+    uint32_t count = 0;
+    auto add = [&](g16::Mode m, bool j, const g16::BatchParams& p, uint32_t nv) {
+        out[count].mode = m;
+        out[count].join = j;
+        out[count].p = p;
+        out[count].n_vec = nv;
+        ++count;
+    };
+    auto joined = [&](g16::BatchParams p) {
+        p.src[0] = (nb == 1) ? srcs[n_vec - 1] : dsts[n_vec - 1];
+        p.src[1] = p.src[2] = nullptr;
+        p.dst[0] = p.dst[1] = p.dst[2] = nullptr;
+        p.join_a = dsts[0];
+        p.join_b = dsts[1];
+        p.h_mont = h_mont;
+        p.h_std = h_std;
+        return p;
+    };
+    // inverse transform, high batches first (DIF), the first one reading the inputs
+    for (uint32_t b = nb - 1; b >= 1; --b) {
+        g16::BatchParams p = base_params(c);
+        p.tw = c->tw_inv;
+        p.s0 = batch_s0(c, b);
+        p.k = c->batch_k[b];
+        for (uint32_t v = 0; v < n_vec; ++v) {
+            p.src[v] = (b == nb - 1) ? srcs[v] : dsts[v];
+            p.dst[v] = dsts[v];
+        }
+        add(g16::Mode::DifStrided, false, p, n_vec);
+    }
+    // lowest batch of both transforms with the coset multiply between them
+    g16::BatchParams f = base_params(c);
+    f.tw = c->tw_inv;
+    f.tw_fwd = c->tw_fwd;
+    f.scale = c->coset;
+    f.k = c->batch_k[0];
+    for (uint32_t v = 0; v < n_vec; ++v) {
+        f.src[v] = (nb == 1) ? srcs[v] : dsts[v];
+        f.dst[v] = dsts[v];
+    }
+    if (nb == 1) {
+        if (plain_vec) add(g16::Mode::Fused, false, f, plain_vec);
+        if (join) add(g16::Mode::Fused, true, joined(f), 1);
+        return count;
+    }
+    add(g16::Mode::Fused, false, f, n_vec);
+    // forward transform, remaining batches (DIT), low to high
+    for (uint32_t b = 1; b < nb; ++b) {
+        g16::BatchParams p = base_params(c);
+        p.tw = c->tw_fwd;
+        p.s0 = batch_s0(c, b);
+        p.k = c->batch_k[b];
+        for (uint32_t v = 0; v < n_vec; ++v) {
+            p.src[v] = dsts[v];
+            p.dst[v] = dsts[v];
+        }
+        if (b + 1 == nb && join) {
+            if (plain_vec) add(g16::Mode::DitStrided, false, p, plain_vec);
+            add(g16::Mode::DitStrided, true, joined(p), 1);
+        } else {
+            add(g16::Mode::DitStrided, false, p, n_vec);
+        }
+    }
+    return count;
+}
+
+int run_plan(const Launch* ls, uint32_t count, hipStream_t s) {
+    for (uint32_t i = 0; i < count; ++i) {
+        int rc = exec_launch(ls[i], s);
+        if (rc) return rc;
+    }
+    return G16_OK;
+}
+
+// Host checks of g16_h_compute / g16_h_stage, then the launch list.
+int plan_h(g16_ctx* ctx, const void* a_mont, const void* b_mont, const void* c_mont,
+           void* h_mont, void* h_std, Launch* ls, uint32_t* count) {
+    if (!ctx_ok(ctx)) return ctx ? G16_ESTATE : G16_EINVAL;
+    if (!a_mont || !b_mont || !c_mont || !h_mont || !h_std) return G16_EINVAL;
+    const size_t nbytes = vec_bytes(ctx);
+    const void* ins[3] = {a_mont, b_mont, c_mont};
+    const void* outs[2] = {h_mont, h_std};
+    if (overlaps(h_mont, nbytes, h_std, nbytes)) return G16_EALIAS;
+    for (const void* o : outs) {
+        for (const void* i : ins)
+            if (overlaps(o, nbytes, i, nbytes)) return G16_EALIAS;
+        if (overlaps(o, nbytes, ctx->ws_begin, ctx->ws_bytes)) return G16_EALIAS;
+    }
+    for (const void* i : ins)
+        if (overlaps(i, nbytes, ctx->ws_begin, ctx->ws_bytes)) return G16_EALIAS;
+    for (const void* p : ins)
+        if (!device_pointer(p)) return G16_EINVAL;
+    for (const void* p : outs)
+        if (!device_pointer(p)) return G16_EINVAL;
+    const size_t n = size_t(1) << ctx->log_n;
+    const Fr* srcs[3] = {(const Fr*)a_mont, (const Fr*)b_mont, (const Fr*)c_mont};
+    Fr* dsts[3] = {ctx->scratch, ctx->scratch + n, ctx->scratch + 2 * n};
+    *count = plan_coset(ctx, srcs, dsts, 3, true, (Fr*)h_mont, (Fr*)h_std, ls);
+    return G16_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+uint32_t g16_abi_version(void) { return G16_ABI_VERSION; }
+
+const char* g16_strerror(int code) {
+    switch (code) {
+        case G16_OK: return "ok";
+        case G16_EINVAL: return "invalid argument";
+        case G16_ERANGE: return "log_n out of range [1, 27]";
+        case G16_ENOSPACE: return "workspace too small";
+        case G16_EALIAS: return "buffers overlap";
+        case G16_EHIP: return "HIP runtime or launch error";
+        case G16_ESTATE: return "context released or not prepared";
+        default: return "unknown status";
+    }
+}
+
+int g16_batch_plan(uint32_t log_n, uint32_t kmax, uint32_t* ks, uint32_t cap) {
+    if (log_n < G16_MIN_LOG_N || log_n > G16_MAX_LOG_N) return G16_ERANGE;
+    if (kmax > 12 || (cap > 0 && !ks)) return G16_EINVAL;
+    if (kmax == 0) kmax = max_batch_k();
+    uint32_t tmp[kMaxBatches];
+    uint32_t nb = plan_batches(log_n, kmax, tmp);
+    for (uint32_t i = 0; i < nb && i < cap; ++i) ks[i] = tmp[i];
+    return (int)nb;
+}
+
+size_t g16_h_workspace_bytes(uint32_t log_n) {
+    if (log_n < G16_MIN_LOG_N || log_n > G16_MAX_LOG_N) return 0;
+    size_t n = size_t(1) << log_n;
+    size_t half = round_up((n / 2) * sizeof(Fr));
+    size_t full = round_up(n * sizeof(Fr));
+    return 2 * half + full + 3 * full;
+}
+
+int g16_h_prepare(uint32_t log_n, void* workspace, size_t workspace_bytes, void* stream,
+                  g16_ctx** out_ctx) {
+    if (!out_ctx || !workspace) return G16_EINVAL;
+    if (log_n < G16_MIN_LOG_N || log_n > G16_MAX_LOG_N) return G16_ERANGE;
+    if ((uintptr_t)workspace % kAlign) return G16_EINVAL;
+    if (workspace_bytes < g16_h_workspace_bytes(log_n)) return G16_ENOSPACE;
+    if (!device_pointer(workspace)) return G16_EINVAL;
+    g16_ctx* c = new (std::nothrow) g16_ctx;
+    if (!c) return G16_EINVAL;
+    std::memset(c, 0, sizeof *c);
+    c->log_n = log_n;
+    if (hipGetDevice(&c->device) != hipSuccess) {
+        delete c;
+        return G16_EHIP;
+    }
+    const size_t n = size_t(1) << log_n;
+    uint8_t* ws = (uint8_t*)workspace;
+    size_t half = round_up((n / 2) * sizeof(Fr));
+    size_t full = round_up(n * sizeof(Fr));
+    c->tw_fwd = (Fr*)ws;
+    c->tw_inv = (Fr*)(ws + half);
+    c->coset = (Fr*)(ws + 2 * half);
+    c->scratch = (Fr*)(ws + 2 * half + full);
+    c->ws_begin = ws;
+    c->ws_bytes = g16_h_workspace_bytes(log_n);
+    domain_roots(log_n, &c->omega, &c->shift, &c->size_inv);
+    c->omega_inv = g16::fr_inv(c->omega);
+    c->n_batches = plan_batches(log_n, max_batch_k(), c->batch_k);
+
+    hipStream_t s = (hipStream_t)stream;
+    const uint32_t blocks = 2048;
+    Fr one = g16::fr_mont_one();
+    hipLaunchKernelGGL(g16::table_kernel, dim3(blocks), dim3(kThreads), 0, s, c->tw_fwd,
+                       c->omega, one, (uint64_t)(n / 2), log_n, 0);
+    hipLaunchKernelGGL(g16::table_kernel, dim3(blocks), dim3(kThreads), 0, s, c->tw_inv,
+                       c->omega_inv, one, (uint64_t)(n / 2), log_n, 0);
+    hipLaunchKernelGGL(g16::table_kernel, dim3(blocks), dim3(kThreads), 0, s, c->coset,
+                       c->shift, c->size_inv, (uint64_t)n, log_n, 1);
+    int rc = launch_status();
+    if (rc) {
+        delete c;
+        return rc;
+    }
+    c->magic = kMagic;
+    *out_ctx = c;
+    return G16_OK;
+}
+
+int g16_release(g16_ctx* ctx) {
+    if (!ctx) return G16_EINVAL;
+    if (ctx->magic != kMagic) return G16_ESTATE;
+    ctx->magic = kDead;
+    delete ctx;
+    return G16_OK;
+}
+
+uint32_t g16_ctx_log_n(const g16_ctx* ctx) { return ctx_ok(ctx) ? ctx->log_n : 0u; }
+
+int g16_domain_roots(const g16_ctx* ctx, uint8_t omega_mont[32], uint8_t shift_mont[32],
+                     uint8_t size_inv_mont[32]) {
+    if (!ctx_ok(ctx)) return ctx ? G16_ESTATE : G16_EINVAL;
+    if (omega_mont) std::memcpy(omega_mont, ctx->omega.w, 32);
+    if (shift_mont) std::memcpy(shift_mont, ctx->shift.w, 32);
+    if (size_inv_mont) std::memcpy(size_inv_mont, ctx->size_inv.w, 32);
+    return G16_OK;
+}
+
+int g16_ntt_forward(g16_ctx* ctx, const void* in_mont, void* out_mont, void* stream) {
+    return run_ntt(ctx, in_mont, out_mont, stream, false);
+}
+
+int g16_ntt_inverse(g16_ctx* ctx, const void* in_mont, void* out_mont, void* stream) {
+    return run_ntt(ctx, in_mont, out_mont, stream, true);
+}
+
+
+
+int g16_coset_eval(g16_ctx* ctx, const void* in_mont, void* out_mont, void* stream) {
+    if (!ctx_ok(ctx)) return ctx ? G16_ESTATE : G16_EINVAL;
+    if (!in_mont || !out_mont) return G16_EINVAL;
+    const size_t nbytes = vec_bytes(ctx);
+    if (in_mont != out_mont && overlaps(in_mont, nbytes, out_mont, nbytes)) return G16_EALIAS;
+    if (overlaps(in_mont, nbytes, ctx->ws_begin, ctx->ws_bytes) ||
+        overlaps(out_mont, nbytes, ctx->ws_begin, ctx->ws_bytes))
+        return G16_EALIAS;
+    if (!device_pointer(in_mont) || !device_pointer(out_mont)) return G16_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    const Fr* src = (const Fr*)in_mont;
+    Launch ls[kMaxLaunches];
+    if (ctx->n_batches == 1) {
+        // one contiguous kernel: each workgroup reads its whole slice before writing it
+        Fr* dst = (Fr*)out_mont;
+        return run_plan(ls, plan_coset(ctx, &src, &dst, 1, false, nullptr, nullptr, ls), s);
+    }
+    // inverse batches write scratch first, the last forward batch writes scratch too
+    Fr* tmp = ctx->scratch;
+    int rc = run_plan(ls, plan_coset(ctx, &src, &tmp, 1, false, nullptr, nullptr, ls), s);
+    if (rc) return rc;
+    if (hipMemcpyAsync(out_mont, tmp, nbytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
+        return G16_EHIP;
+    return G16_OK;
+}
+
+int g16_h_compute(g16_ctx* ctx, const void* a_mont, const void* b_mont, const void* c_mont,
+                  void* h_mont, void* h_std, void* stream) {
+    Launch ls[kMaxLaunches];
+    uint32_t count = 0;
+    int rc = plan_h(ctx, a_mont, b_mont, c_mont, h_mont, h_std, ls, &count);
+    if (rc) return rc;
+    return run_plan(ls, count, (hipStream_t)stream);
+}
+
+int g16_h_stage_count(const g16_ctx* ctx) {
+    if (!ctx_ok(ctx)) return ctx ? G16_ESTATE : G16_EINVAL;
+    const uint32_t nb = ctx->n_batches;
+    return nb == 1 ? 2 : (int)(2 * (nb - 1) + 2);
+}
+
+int g16_h_stage(g16_ctx* ctx, uint32_t stage, const void* a_mont, const void* b_mont,
+                const void* c_mont, void* h_mont, void* h_std, void* stream) {
+    Launch ls[kMaxLaunches];
+    uint32_t count = 0;
+    int rc = plan_h(ctx, a_mont, b_mont, c_mont, h_mont, h_std, ls, &count);
+    if (rc) return rc;
+    if (stage >= count) return G16_EINVAL;
+    return exec_launch(ls[stage], (hipStream_t)stream);
+}
+
+static uint32_t ew_blocks(uint64_t n) {
+    uint64_t b = (n + kThreads - 1) / kThreads;
+    return (uint32_t)(b < 8192 ? b : 8192);
+}
+
+int g16_h_join(uint64_t n, const void* a_mont, const void* b_mont, const void* c_mont,
+               void* h_mont, void* h_std, void* stream) {
+    if (n == 0 || !a_mont || !b_mont || !c_mont || !h_mont || !h_std) return G16_EINVAL;
+    const size_t nbytes = n * sizeof(Fr);
+    const void* ins[3] = {a_mont, b_mont, c_mont};
+    if (overlaps(h_mont, nbytes, h_std, nbytes)) return G16_EALIAS;
+    for (const void* i : ins)
+        if (overlaps(h_mont, nbytes, i, nbytes) || overlaps(h_std, nbytes, i, nbytes))
+            return G16_EALIAS;
+    for (const void* p : {a_mont, b_mont, c_mont, (const void*)h_mont, (const void*)h_std})
+        if (!device_pointer(p)) return G16_EINVAL;
+    hipLaunchKernelGGL(g16::h_join_kernel, dim3(ew_blocks(n)), dim3(kThreads), 0,
+                       (hipStream_t)stream, (const Fr*)a_mont, (const Fr*)b_mont,
+                       (const Fr*)c_mont, (Fr*)h_mont, (Fr*)h_std, n);
+    return launch_status();
+}
+
+int g16_gather_abc(uint64_t n_rows, const uint32_t* row_ptr_a, const uint32_t* signal_a,
+                   const void* value_a, uint64_t nnz_a, const uint32_t* row_ptr_b,
+                   const uint32_t* signal_b, const void* value_b, uint64_t nnz_b,
+                   const void* witness, uint64_t n_witness, void* out_a, void* out_b,
+                   void* out_c, void* stream) {
+    if (n_rows == 0 || n_rows >= 0xffffffffull || !row_ptr_a || !row_ptr_b || !witness ||
+        n_witness == 0 || !out_a || !out_b || !out_c)
+        return G16_EINVAL;
+    if ((nnz_a && (!signal_a || !value_a)) || (nnz_b && (!signal_b || !value_b)))
+        return G16_EINVAL;
+    if (nnz_a > 0xffffffffull || nnz_b > 0xffffffffull) return G16_EINVAL;
+    const size_t ob = n_rows * sizeof(Fr);
+    void* outs[3] = {out_a, out_b, out_c};
+    for (int i = 0; i < 3; ++i)
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(outs[i], ob, outs[j], ob)) return G16_EALIAS;
+    const void* ins[8] = {row_ptr_a, signal_a, value_a, row_ptr_b, signal_b, value_b, witness,
+                          nullptr};
+    const size_t in_bytes[7] = {(n_rows + 1) * 4, nnz_a * 4, nnz_a * sizeof(Fr),
+                                (n_rows + 1) * 4, nnz_b * 4, nnz_b * sizeof(Fr),
+                                n_witness * sizeof(Fr)};
+    for (int o = 0; o < 3; ++o)
+        for (int i = 0; i < 7; ++i)
+            if (ins[i] && in_bytes[i] && overlaps(outs[o], ob, ins[i], in_bytes[i]))
+                return G16_EALIAS;
+    for (int i = 0; i < 7; ++i)
+        if (ins[i] && in_bytes[i] && !device_pointer(ins[i])) return G16_EINVAL;
+    for (int o = 0; o < 3; ++o)
+        if (!device_pointer(outs[o])) return G16_EINVAL;
+    uint32_t blocks = (uint32_t)((n_rows + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL(g16::gather_kernel, dim3(blocks), dim3(kThreads), 0, (hipStream_t)stream,
+                       row_ptr_a, signal_a, (const Fr*)value_a, nnz_a, row_ptr_b, signal_b,
+                       (const Fr*)value_b, nnz_b, (const Fr*)witness, n_witness, (Fr*)out_a,
+                       (Fr*)out_b, (Fr*)out_c, n_rows);
+    return launch_status();
+}
+
+static int elementwise(uint64_t n, const void* a, const void* b, void* out, int op,
+                       void* stream) {
+    if (n == 0 || !a || !out || (op == 2 && !b)) return G16_EINVAL;
+    const size_t nbytes = n * sizeof(Fr);
+    if (a != out && overlaps(a, nbytes, out, nbytes)) return G16_EALIAS;
+    if (op == 2 && b != out && overlaps(b, nbytes, out, nbytes)) return G16_EALIAS;
+    if (!device_pointer(a) || !device_pointer(out) || (op == 2 && !device_pointer(b)))
+        return G16_EINVAL;
+    hipLaunchKernelGGL(g16::elementwise_kernel, dim3(ew_blocks(n)), dim3(kThreads), 0,
+                       (hipStream_t)stream, (const Fr*)a, (const Fr*)b, (Fr*)out, n, op);
+    return launch_status();
+}
+
+int g16_to_mont(uint64_t n, const void* in_std, void* out_mont, void* stream) {
+    return elementwise(n, in_std, nullptr, out_mont, 0, stream);
+}
+
+int g16_from_mont(uint64_t n, const void* in_mont, void* out_std, void* stream) {
+    return elementwise(n, in_mont, nullptr, out_std, 1, stream);
+}
+
+int g16_fr_mul(uint64_t n, const void* a_mont, const void* b_mont, void* out_mont,
+               void* stream) {
+    return elementwise(n, a_mont, b_mont, out_mont, 2, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,189 @@
+/*
+ * g16.h -- C ABI of libg16.so, the MI355X (gfx950) Groth16 H-polynomial library.
+ *
+ * What it computes (the pages this follows are the snarkrs-gpu-kernels docs pages
+ * NTT_CU, POINTWISE_CU and GATHER_CU):
+ *   stage 0  A, B = CSR row dot products with the witness, C = A o B
+ *            (GATHER_CU, kernel description and "WHY C IS COMPUTED HERE");
+ *   stage 1  three inverse NTTs of A, B, C (evaluations on the n-th roots of unity
+ *            to coefficients), normalised by 1/n (NTT_CU, "THE ALGORITHM IS THE CPU
+ *            BACKEND'S, EXACTLY", first bullet);
+ *   stage 2  the coset shift x_j *= s^j with s a primitive 2n-th root (same section,
+ *            second bullet);
+ *   stage 3  three forward NTTs (the coset evaluations A', B', C');
+ *   stage 4  H = A' * B' - C' with no division by the vanishing polynomial, written
+ *            in Montgomery form and in standard form (POINTWISE_CU, "NO DIVISION BY
+ *            Z(coset)" and "TWO OUTPUT BUFFERS").
+ *
+ * Field and layout.  Fr is the BN254 scalar field, r = 0x30644e72e131a029b85045b6
+ * 8181585d2833e84879b9709143e1f593f0000001.  An element is 32 bytes: a little-endian
+ * 256-bit integer (eight 32-bit words, word 0 least significant; the same bytes as
+ * four little-endian 64-bit limbs).  "mont" buffers hold x * 2^256 mod r, "std"
+ * buffers hold x itself; both are canonical (< r).  Every vector is n contiguous
+ * elements in natural order, n = 2^log_n.
+ *
+ * Roots (a reading of the pages, which name no element): g = 5, w28 =
+ * g^((r-1)/2^28) is a primitive 2^28-th root of unity, the coset shift of a 2^L
+ * domain is s = w28^(2^(27-L)) and the domain root is omega = s^2.
+ *
+ * Memory and streams.  Every pointer argument named *_mont, *_std, a, b, c, h_*,
+ * in, out, witness, value_*, row_ptr_*, signal_* or workspace is a DEVICE pointer
+ * (HIP, the current device) owned by the caller.  `stream` is a hipStream_t passed as
+ * void* (NULL = the null stream).  Calls only ENQUEUE work on `stream`; none of them
+ * synchronises, and the caller keeps every buffer alive until that work is done.
+ * Device memory is never assumed to be zero: every output element is written.
+ *
+ * Errors.  Functions return G16_OK (0) or a negative code.  Argument errors are
+ * detected on the host before anything is enqueued.  G16_EHIP reports a HIP launch or
+ * runtime error seen after enqueueing; the outputs are then unspecified.
+ * Preconditions that are NOT checked (they would cost a pass over the data): inputs
+ * are canonical (< r).  Out-of-range CSR indices are caught on the device (see
+ * g16_gather_abc) and never read out of bounds.
+ */
+#ifndef G16_H
+#define G16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define G16_ABI_VERSION 1u
+
+#define G16_OK        0
+#define G16_EINVAL   (-1) /* null pointer, zero or oversized length, wrong context */
+#define G16_ERANGE   (-2) /* log_n outside [1, 27] */
+#define G16_ENOSPACE (-3) /* workspace smaller than g16_h_workspace_bytes(log_n) */
+#define G16_EALIAS   (-4) /* buffers overlap where the call forbids it */
+#define G16_EHIP     (-5) /* HIP launch or runtime error */
+#define G16_ESTATE   (-6) /* context released or not prepared */
+
+#define G16_MIN_LOG_N 1u
+#define G16_MAX_LOG_N 27u /* r - 1 = 2^28 * odd: a primitive 2n-th root exists up to n = 2^27 */
+
+typedef struct g16_ctx g16_ctx; /* opaque host object, owned by the library */
+
+/* G16_ABI_VERSION of the loaded library. */
+uint32_t g16_abi_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* g16_strerror(int code);
+
+/* Bytes of device workspace g16_h_prepare needs for a 2^log_n domain, or 0 when
+ * log_n is out of range.  The workspace holds the resident tables (the forward and
+ * inverse twiddles, n/2 elements each, and the n-element coset table
+ * n^-1 * s^bitrev(p)) plus three n-element scratch vectors: 5 * n * 32 bytes, rounded
+ * up to 256-byte sections. */
+size_t g16_h_workspace_bytes(uint32_t log_n);
+
+/* The pass batching the library uses for a 2^log_n transform when each workgroup
+ * batches at most kmax passes (kmax = 0: the library's default, which the
+ * environment variable G16_MAX_K in [1, 12] overrides): ceil(log_n / kmax) batches of
+ * near-equal size, larger ones first (the NTT_CU page, "SHARED MEMORY BUDGET": 18
+ * passes under a cap of 10 split 9 + 9, not 10 + 8).  Writes up to `cap` batch sizes,
+ * lowest bits first, and returns the number of batches, or a negative code
+ * (G16_ERANGE for log_n, G16_EINVAL for kmax > 12 or a NULL ks with cap > 0).  Host
+ * only; never touches the GPU. */
+int g16_batch_plan(uint32_t log_n, uint32_t kmax, uint32_t* ks, uint32_t cap);
+
+/* Prepares a context for the 2^log_n domain: computes the roots on the host and
+ * enqueues on `stream` the kernels that fill the resident tables inside
+ * `workspace` (the NTT_CU page: the host builds the tables once at prepare time
+ * and leaves them resident).  The workspace (device memory, >= 256-byte aligned,
+ * at least g16_h_workspace_bytes(log_n) bytes) stays owned by the caller and must
+ * outlive the context.  Work later enqueued on another stream must be ordered after
+ * this call by the caller.  On success *out_ctx receives a new context.
+ * Errors: G16_EINVAL (null out_ctx or workspace, misaligned workspace),
+ * G16_ERANGE, G16_ENOSPACE, G16_EHIP. */
+int g16_h_prepare(uint32_t log_n, void* workspace, size_t workspace_bytes, void* stream,
+                  g16_ctx** out_ctx);
+
+/* Frees the host context (not the workspace).  G16_EINVAL on NULL. */
+int g16_release(g16_ctx* ctx);
+
+/* log2 of the context's domain size, or 0 for NULL. */
+uint32_t g16_ctx_log_n(const g16_ctx* ctx);
+
+/* Host copies (32 bytes each, Montgomery form) of the domain root omega, the coset
+ * shift s and size_inv = 1/n, so a caller can check the root convention.  Any
+ * output pointer may be NULL.  Errors: G16_EINVAL. */
+int g16_domain_roots(const g16_ctx* ctx, uint8_t omega_mont[32], uint8_t shift_mont[32],
+                     uint8_t size_inv_mont[32]);
+
+/* Forward transform out_i = sum_j in_j omega^(i j), natural order in and out (the
+ * NTT_CU page: decimation in time, the bit-reverse permutation folded into the first
+ * batch's load).  in == out is allowed; partial overlap is G16_EALIAS.  Uses the
+ * context's scratch: calls on one context must not overlap in time. */
+int g16_ntt_forward(g16_ctx* ctx, const void* in_mont, void* out_mont, void* stream);
+
+/* Inverse transform out_j = n^-1 sum_i in_i omega^(-i j) (the 1/n folded into the
+ * load).  Same aliasing and scratch rules as g16_ntt_forward. */
+int g16_ntt_inverse(g16_ctx* ctx, const void* in_mont, void* out_mont, void* stream);
+
+/* Stages 1 to 3 for one vector: out_i = x(s omega^i) where x interpolates `in` on the
+ * domain (inverse transform, coset shift, forward transform).  The materialised coset
+ * vector lets a caller finish with g16_h_join (the unfused path).  in == out allowed;
+ * partial overlap is G16_EALIAS.  Uses the context's scratch. */
+int g16_coset_eval(g16_ctx* ctx, const void* in_mont, void* out_mont, void* stream);
+
+/* The whole pipeline, stages 1 to 4: h_mont and h_std receive H_i = A'_i B'_i - C'_i
+ * (Montgomery and standard form).  a, b, c are only read.  h_mont and h_std must not
+ * overlap each other, the inputs or the workspace (G16_EALIAS).  Uses the context's
+ * scratch: calls on one context must not overlap in time. */
+int g16_h_compute(g16_ctx* ctx, const void* a_mont, const void* b_mont, const void* c_mont,
+                  void* h_mont, void* h_std, void* stream);
+
+/* g16_h_compute is a fixed sequence of kernel launches ("stages"): the inverse
+ * transform's high batches, the fused lowest batch (end of the inverse, coset
+ * multiply, start of the forward transform), the forward transform's high batches,
+ * and the final batch of C with the join epilogue.  g16_h_stage_count returns their
+ * number (2 * number of pass batches), or a negative code for a bad context.
+ * g16_h_stage enqueues stage `stage` alone, with g16_h_compute's arguments and
+ * checks; enqueueing stages 0 .. count-1 in order on one stream is exactly
+ * g16_h_compute.  Lets a caller time or interleave individual kernels.
+ * G16_EINVAL for stage >= count. */
+int g16_h_stage_count(const g16_ctx* ctx);
+int g16_h_stage(g16_ctx* ctx, uint32_t stage, const void* a_mont, const void* b_mont,
+                const void* c_mont, void* h_mont, void* h_std, void* stream);
+
+/* Unfused stage 4 on materialised coset vectors: h_mont_i = a_i b_i - c_i and
+ * h_std_i = h_mont_i * 2^-256 mod r (the POINTWISE_CU page's standalone join, the
+ * reference the fused epilogue is checked against).  n >= 1.  h_mont and h_std must
+ * not overlap each other or the inputs. */
+int g16_h_join(uint64_t n, const void* a_mont, const void* b_mont, const void* c_mont,
+               void* h_mont, void* h_std, void* stream);
+
+/* Stage 0, the CSR gather (the GATHER_CU page): for each row i < n_rows,
+ *   out_a[i] = sum_{k in [row_ptr_a[i], row_ptr_a[i+1])} value_a[k] * witness[signal_a[k]]
+ *   out_b[i] = the same for B,   out_c[i] = out_a[i] * out_b[i]   (all Montgomery).
+ * row_ptr_* hold n_rows + 1 words; signal_* / value_* hold nnz_* entries; witness
+ * holds n_witness elements.  A row whose range is not within [0, nnz] or that names a
+ * witness index >= n_witness is not read out of bounds: its three outputs are set to
+ * the invalid value 2^256 - 1 (all words 0xffffffff), which no canonical element
+ * equals.  Outputs must not overlap the inputs or each other. */
+int g16_gather_abc(uint64_t n_rows,
+                   const uint32_t* row_ptr_a, const uint32_t* signal_a, const void* value_a,
+                   uint64_t nnz_a,
+                   const uint32_t* row_ptr_b, const uint32_t* signal_b, const void* value_b,
+                   uint64_t nnz_b,
+                   const void* witness, uint64_t n_witness,
+                   void* out_a, void* out_b, void* out_c, void* stream);
+
+/* Element-wise conversions (in == out allowed): standard -> Montgomery, and
+ * Montgomery -> standard (the latter is the POINTWISE_CU page's witness conversion
+ * for the MSM). */
+int g16_to_mont(uint64_t n, const void* in_std, void* out_mont, void* stream);
+int g16_from_mont(uint64_t n, const void* in_mont, void* out_std, void* stream);
+
+/* Element-wise product out_i = a_i * b_i (Montgomery in and out; out may equal a or
+ * b).  Forms C = A o B for the workloads that start from A and B. */
+int g16_fr_mul(uint64_t n, const void* a_mont, const void* b_mont, void* out_mont,
+               void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* G16_H */

@@ -360,6 +360,41 @@ int oracle_dft_naive(unsigned L, int inverse, const u64* x, u64* y) {
     return 0;
 }
 
+/* Stages 1 to 3 on one standard-form vector, in place: the inverse transform, the
+ * coset shift x_j *= shift^j, the forward transform. */
+static void coset_eval_std(fe* x, unsigned L) {
+    size_t n = (size_t)1 << L;
+    fe omega, shift, size_inv;
+    domain_roots(L, &omega, &shift, &size_inv);
+    intt_std(x, L);                              /* stage 1 */
+    fe sj = fe_small(1);                         /* stage 2: x_j *= shift^j */
+    for (size_t j = 0; j < n; ++j) {
+        x[j] = fe_mul(x[j], sj);
+        sj = fe_mul(sj, shift);
+    }
+    ntt_std(x, L);                               /* stage 3 */
+}
+
+/* One vector's coset evaluations, Montgomery in and out. */
+int oracle_coset_eval(unsigned L, const u64* in_mont, u64* out_mont) {
+    if (L < 1 || L > 27) return -1;
+    oracle_init();
+    size_t n = (size_t)1 << L;
+    fe* v = (fe*)malloc(sizeof(fe) * n);
+    if (!v) return -1;
+    for (size_t i = 0; i < n; ++i) {
+        fe y; memcpy(y.v, in_mont + 4 * i, 32);
+        v[i] = from_mont(y);
+    }
+    coset_eval_std(v, L);
+    for (size_t i = 0; i < n; ++i) {
+        fe m = to_mont(v[i]);
+        memcpy(out_mont + 4 * i, m.v, 32);
+    }
+    free(v);
+    return 0;
+}
+
 /* The H pipeline on Montgomery inputs: three inverse transforms, the coset shift,
  * three forward transforms, H = A'B' - C', written as h_mont and h_std. */
 int oracle_h_pipeline(unsigned L, const u64* a_mont, const u64* b_mont, const u64* c_mont,
@@ -367,8 +402,6 @@ int oracle_h_pipeline(unsigned L, const u64* a_mont, const u64* b_mont, const u6
     if (L < 1 || L > 27) return -1;
     oracle_init();
     size_t n = (size_t)1 << L;
-    fe omega, shift, size_inv;
-    domain_roots(L, &omega, &shift, &size_inv);
     const u64* ins[3] = {a_mont, b_mont, c_mont};
     fe* v[3];
     for (int k = 0; k < 3; ++k) {
@@ -378,13 +411,7 @@ int oracle_h_pipeline(unsigned L, const u64* a_mont, const u64* b_mont, const u6
             fe y; memcpy(y.v, ins[k] + 4 * i, 32);
             v[k][i] = from_mont(y);
         }
-        intt_std(v[k], L);                       /* stage 1 */
-        fe sj = fe_small(1);                     /* stage 2: x_j *= shift^j */
-        for (size_t j = 0; j < n; ++j) {
-            v[k][j] = fe_mul(v[k][j], sj);
-            sj = fe_mul(sj, shift);
-        }
-        ntt_std(v[k], L);                        /* stage 3 */
+        coset_eval_std(v[k], L);                 /* stages 1 to 3 */
     }
     for (size_t i = 0; i < n; ++i) {             /* stage 4 */
         fe h = fe_sub(fe_mul(v[0][i], v[1][i]), v[2][i]);

@@ -38,6 +38,7 @@ _SIGNATURES = {
     "oracle_ntt": "UIP",
     "oracle_dft_naive": "UIPP",
     "oracle_h_pipeline": "UPPPPP",
+    "oracle_coset_eval": "UPP",
     "oracle_h_at": "UPPPZPPP",
     "oracle_pointwise_mul_mont": "ZPPP",
     "oracle_gather": "ZPPPPPPPZPPP",
@@ -208,6 +209,14 @@ def dft_naive(x, log_n: int, inverse: bool = False) -> np.ndarray:
     x = _arr(x, 1 << log_n)
     out = np.empty_like(x)
     _check(_load().oracle_dft_naive(log_n, int(inverse), _ptr(x), _ptr(out)), "dft_naive")
+    return out
+
+
+def coset_eval(log_n: int, x_mont) -> np.ndarray:
+    """One vector's coset evaluations x(s w^i), Montgomery in and out."""
+    x = _arr(x_mont, 1 << log_n)
+    out = np.empty_like(x)
+    _check(_load().oracle_coset_eval(log_n, _ptr(x), _ptr(out)), "coset_eval")
     return out
 
 

@@ -1,0 +1,119 @@
+"""The C ABI on the CPU: the library loads, exports every symbol include/g16.h
+declares, and rejects bad arguments on the host before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from groth16_polynomial_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "g16.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "batch_split.txt")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from groth16_polynomial_amd import build
+        build.build()
+    return binding.load()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(g16_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_symbols()
+    assert len(names) >= 15
+    for name in names:
+        assert hasattr(lib, name), name
+    # and the binding wraps exactly the declared set
+    assert sorted(binding.SIGNATURES) == names
+
+
+def test_version_and_strerror(lib):
+    assert binding.abi_version() == 1
+    for code in range(-6, 1):
+        assert binding.strerror(code)
+    assert binding.strerror(-99) == "unknown status"
+
+
+def test_workspace_bytes(lib):
+    assert binding.workspace_bytes(0) == 0
+    assert binding.workspace_bytes(28) == 0
+    for L in (1, 2, 12, 20, 27):
+        n = 1 << L
+        half = -(-n // 2 * 32 // 256) * 256
+        full = -(-n * 32 // 256) * 256
+        assert binding.workspace_bytes(L) == 2 * half + 4 * full
+
+
+def test_batch_plan_matches_page(lib):
+    with open(GOLDEN) as f:
+        rows = [list(map(int, l.split())) for l in f if l.strip() and not l.startswith("#")]
+    for row in rows:
+        L, kmax, want = row[0], row[1], row[2:]
+        assert sorted(binding.batch_plan(L, kmax)) == sorted(want)
+
+
+@pytest.mark.parametrize("kmax", list(range(1, 13)))
+def test_batch_plan_rule(lib, kmax):
+    for L in range(1, 28):
+        ks = binding.batch_plan(L, kmax)
+        assert sum(ks) == L
+        assert len(ks) == -(-L // kmax)                 # ceil(log n / kmax) batches
+        assert max(ks) <= kmax and max(ks) - min(ks) <= 1   # near-equal, no tiny tail
+        assert ks == sorted(ks, reverse=True)
+
+
+def test_batch_plan_errors(lib):
+    for bad_L in (0, 28):
+        with pytest.raises(binding.G16Error):
+            binding.batch_plan(bad_L, 10)
+    with pytest.raises(binding.G16Error):
+        binding.batch_plan(10, 13)
+
+
+def test_host_side_argument_errors(lib):
+    """Paths that return before any HIP call."""
+    P = ctypes.c_void_p
+    ctx = ctypes.c_void_p()
+    fake = P(0x100000)  # never dereferenced: every case below fails its host checks first
+    assert lib.g16_h_prepare(20, fake, 1 << 30, None, None) == binding.G16_EINVAL
+    assert lib.g16_h_prepare(20, None, 1 << 30, None, ctypes.byref(ctx)) == binding.G16_EINVAL
+    assert lib.g16_h_prepare(0, fake, 1 << 30, None, ctypes.byref(ctx)) == binding.G16_ERANGE
+    assert lib.g16_h_prepare(28, fake, 1 << 30, None, ctypes.byref(ctx)) == binding.G16_ERANGE
+    assert lib.g16_h_prepare(20, fake, 1000, None, ctypes.byref(ctx)) == binding.G16_ENOSPACE
+    assert lib.g16_h_prepare(12, P(0x100010), 1 << 30, None, ctypes.byref(ctx)) == \
+        binding.G16_EINVAL  # misaligned
+    assert lib.g16_release(None) == binding.G16_EINVAL
+    assert lib.g16_ctx_log_n(None) == 0
+    assert lib.g16_domain_roots(None, None, None, None) == binding.G16_EINVAL
+    for f in ("g16_ntt_forward", "g16_ntt_inverse", "g16_coset_eval"):
+        assert getattr(lib, f)(None, fake, fake, None) == binding.G16_EINVAL
+    assert lib.g16_h_compute(None, fake, fake, fake, fake, fake, None) == binding.G16_EINVAL
+    # h_join: zero length, NULLs, outputs overlapping each other or an input
+    assert lib.g16_h_join(0, fake, fake, fake, P(0x200000), P(0x300000), None) == \
+        binding.G16_EINVAL
+    assert lib.g16_h_join(16, None, fake, fake, P(0x200000), P(0x300000), None) == \
+        binding.G16_EINVAL
+    assert lib.g16_h_join(16, fake, fake, fake, P(0x200000), P(0x200100), None) == \
+        binding.G16_EALIAS
+    assert lib.g16_h_join(16, fake, fake, fake, P(0x100100), P(0x300000), None) == \
+        binding.G16_EALIAS
+    # element-wise: partial overlap of in and out
+    assert lib.g16_fr_mul(16, fake, fake, P(0x100020), None) == binding.G16_EALIAS
+    assert lib.g16_to_mont(0, fake, fake, None) == binding.G16_EINVAL
+    # gather: zero rows, null witness, outputs overlapping
+    z = P(0x400000)
+    assert lib.g16_gather_abc(0, z, z, z, 1, z, z, z, 1, z, 1, P(1 << 24), P(2 << 24),
+                              P(3 << 24), None) == binding.G16_EINVAL
+    assert lib.g16_gather_abc(8, z, z, z, 1, z, z, z, 1, None, 1, P(1 << 24), P(2 << 24),
+                              P(3 << 24), None) == binding.G16_EINVAL
+    assert lib.g16_gather_abc(8, z, z, z, 1, z, z, z, 1, z, 1, P(1 << 24), P(1 << 24),
+                              P(3 << 24), None) == binding.G16_EALIAS

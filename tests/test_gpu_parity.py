@@ -1,0 +1,397 @@
+"""Parity of the HIP library (through the C ABI) with the CPU oracle, bit for bit.
+
+Every case prints what it runs before touching the GPU.  Inputs come from the seeded
+generator in standard form; the GPU side converts them with its own kernel
+(g16_to_mont) and the oracle with its own arithmetic, and the two conversions are
+compared too.  Sizes: small domains cover every code path (one batch, several
+batches, multi-slice workgroups); the workloads' full sizes run in the launch
+configuration the benchmark uses (the library's default batching).
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from groth16_polynomial_amd import binding as g
+from groth16_polynomial_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+R = synth.R_MODULUS
+EDGE_INTS = [0, 1, 2, R - 1, R - 2, (1 << 256) % R, (R - 1) // 2, 2**253, 2**64 - 1]
+
+
+def say(*a):
+    print("[gpu-parity]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    assert torch.cuda.is_available(), "the GPU tests need a HIP device"
+    g.load()
+    yield torch
+    torch.cuda.synchronize()
+
+
+def sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def host(t):
+    sync()
+    return g.to_host(t)
+
+
+def same(got, want, what):
+    got = np.asarray(got, dtype=np.uint32).reshape(-1, 8)
+    want = np.asarray(want, dtype=np.uint32).reshape(-1, 8)
+    assert got.shape == want.shape, what
+    bad = np.flatnonzero((got != want).any(axis=1))
+    assert len(bad) == 0, "%s: %d of %d elements differ, first at %s" % (
+        what, len(bad), len(got), bad[:8].tolist())
+
+
+def gpu_mont(words_std):
+    """Standard-form words -> Montgomery on the GPU with the library's own kernel."""
+    return g.to_mont(g.to_device(words_std))
+
+
+class KMax:
+    """Run a block with a given batching cap (read by the library at prepare time)."""
+
+    def __init__(self, kmax):
+        self.kmax = kmax
+
+    def __enter__(self):
+        self.prev = os.environ.get("G16_MAX_K")
+        if self.kmax is not None:
+            os.environ["G16_MAX_K"] = str(self.kmax)
+        return self
+
+    def __exit__(self, *exc):
+        if self.prev is None:
+            os.environ.pop("G16_MAX_K", None)
+        else:
+            os.environ["G16_MAX_K"] = self.prev
+        return False
+
+
+def h_inputs(workload, log_n, c_is_product=True):
+    a, b = synth.h_inputs(workload, log_n)
+    ad, bd = gpu_mont(a), gpu_mont(b)
+    am, bm = oracle.to_mont(a), oracle.to_mont(b)
+    if c_is_product:
+        cd = g.fr_mul(ad, bd)
+        cm = oracle.pointwise_mul_mont(am, bm)
+    else:
+        c = synth.random_c(workload, log_n)
+        cd, cm = gpu_mont(c), oracle.to_mont(c)
+    return (ad, bd, cd), (am, bm, cm)
+
+
+# ------------------------------------------------------------------ element-wise
+
+@pytest.mark.parametrize("n", [1, 255, 4097])
+def test_elementwise(n):
+    say("elementwise n=%d" % n)
+    x = synth.uniform_fr(41, n)
+    y = synth.uniform_fr(42, n)
+    if n > len(EDGE_INTS):
+        x[:len(EDGE_INTS)] = synth.ints_to_fr(EDGE_INTS)
+        y[:len(EDGE_INTS)] = synth.ints_to_fr(list(reversed(EDGE_INTS)))
+    xm = gpu_mont(x)
+    same(host(xm), oracle.to_mont(x), "to_mont")
+    same(host(g.from_mont(xm)), x, "from_mont")
+    ym = gpu_mont(y)
+    same(host(g.fr_mul(xm, ym)),
+         oracle.pointwise_mul_mont(oracle.to_mont(x), oracle.to_mont(y)), "fr_mul")
+    # in place
+    g.fr_mul(xm, ym, out=xm)
+    same(host(xm), oracle.pointwise_mul_mont(oracle.to_mont(x), oracle.to_mont(y)),
+         "fr_mul in place")
+
+
+@pytest.mark.parametrize("n", [1, 1000, 65536])
+def test_h_join(n):
+    say("h_join n=%d" % n)
+    a, b, c = (synth.uniform_fr(50 + i, n) for i in range(3))
+    am, bm, cm = (oracle.to_mont(v) for v in (a, b, c))
+    hm, hs = g.h_join(*(g.to_device(v) for v in (am, bm, cm)))
+    want_std = oracle.field_op("sub", oracle.field_op("mul", a, b), c)
+    same(host(hs), want_std, "h_std")
+    same(host(hm), oracle.to_mont(want_std), "h_mont")
+
+
+# ------------------------------------------------------------------ transforms
+
+def _ntt_case(log_n, kmax=None, workload=2):
+    say("ntt log_n=%d kmax=%s" % (log_n, kmax))
+    x = synth.ntt_input(workload, log_n)
+    xm = oracle.to_mont(x)
+    with KMax(kmax):
+        ctx = g.HContext(log_n)
+    xd = g.to_device(xm)
+    fwd = ctx.ntt_forward(xd)
+    inv = ctx.ntt_inverse(xd)
+    same(host(fwd), oracle.ntt_mont(xm, log_n), "forward 2^%d" % log_n)
+    same(host(inv), oracle.ntt_mont(xm, log_n, inverse=True), "inverse 2^%d" % log_n)
+    back = ctx.ntt_inverse(fwd)
+    same(host(back), xm, "round trip 2^%d" % log_n)
+    # in place
+    ctx.ntt_forward(xd, out=xd)
+    same(host(xd), host(fwd), "in-place forward 2^%d" % log_n)
+    ctx.release()
+
+
+@pytest.mark.parametrize("log_n", list(range(1, 21)) + [22])
+def test_ntt_default_batching(log_n):
+    _ntt_case(log_n)
+
+
+@pytest.mark.parametrize("log_n,kmax", [(5, 2), (7, 3), (9, 4), (12, 4), (12, 5), (13, 6),
+                                        (16, 11), (16, 12), (18, 12)])
+def test_ntt_other_batchings(log_n, kmax):
+    _ntt_case(log_n, kmax)
+
+
+def test_domain_roots_match_oracle():
+    for log_n in (1, 12, 20, 27 - 5):
+        ctx = g.HContext(log_n)
+        om, sm, im = ctx.domain_roots()
+        w, s, si = oracle.domain_roots(log_n)
+        rr = 1 << 256
+        assert (om, sm, im) == (w * rr % R, s * rr % R, si * rr % R)
+        ctx.release()
+
+
+# ------------------------------------------------------------------ H pipeline
+
+def _h_case(log_n, kmax=None, workload=1, c_is_product=True):
+    say("h_compute log_n=%d kmax=%s workload=%d c=A*B:%s" % (log_n, kmax, workload,
+                                                               c_is_product))
+    (ad, bd, cd), (am, bm, cm) = h_inputs(workload, log_n, c_is_product)
+    same(host(ad), am, "A to Montgomery")
+    same(host(cd), cm, "C = A o B")
+    with KMax(kmax):
+        ctx = g.HContext(log_n)
+    hm, hs = ctx.h_compute(ad, bd, cd)
+    want_m, want_s = oracle.h_pipeline(log_n, am, bm, cm)
+    same(host(hm), want_m, "h_mont 2^%d" % log_n)
+    same(host(hs), want_s, "h_std 2^%d" % log_n)
+    return ctx, (ad, bd, cd), (hm, hs)
+
+
+@pytest.mark.parametrize("log_n", list(range(1, 17)) + [18])
+def test_h_compute_default_batching(log_n):
+    ctx, _, _ = _h_case(log_n)
+    ctx.release()
+
+
+@pytest.mark.parametrize("log_n,kmax", [(4, 2), (8, 3), (10, 4), (12, 5), (13, 4), (14, 12),
+                                        (17, 6)])
+def test_h_compute_other_batchings(log_n, kmax):
+    ctx, _, _ = _h_case(log_n, kmax)
+    ctx.release()
+
+
+def test_h_stages_compose_to_h_compute():
+    import torch
+    for log_n, kmax in ((10, None), (16, None), (12, 4)):
+        say("h stages log_n=%d kmax=%s" % (log_n, kmax))
+        (ad, bd, cd), _ = h_inputs(8, log_n)
+        with KMax(kmax):
+            ctx = g.HContext(log_n)
+        hm, hs = ctx.h_compute(ad, bd, cd)
+        count = ctx.stage_count()
+        assert count == 2 * len(g.batch_plan(log_n, kmax or 0))
+        sm, ss = g.empty_fr(1 << log_n), g.empty_fr(1 << log_n)
+        for i in range(count):
+            ctx.h_stage(i, ad, bd, cd, sm, ss)
+        same(host(sm), host(hm), "staged h_mont")
+        same(host(ss), host(hs), "staged h_std")
+        with pytest.raises(g.G16Error):
+            ctx.h_stage(count, ad, bd, cd, sm, ss)
+        ctx.release()
+
+
+def test_h_compute_c_not_product():
+    ctx, _, _ = _h_case(11, c_is_product=False, workload=7)
+    ctx.release()
+
+
+def test_h_compute_workload_2_12():
+    """The 2^12 workload (A, B uniform, C = A o B), whole output."""
+    ctx, _, _ = _h_case(12, workload=1)
+    ctx.release()
+
+
+def test_h_compute_workload_2_20():
+    """The 2^20 workload in the benchmark's launch configuration, whole output."""
+    ctx, _, _ = _h_case(20, workload=3)
+    ctx.release()
+
+
+def test_h_compute_workload_2_22_sampled():
+    """The 2^22 workload: sampled outputs by the oracle's barycentric route, plus the
+    quotient-degree property on every output."""
+    log_n, n = 22, 1 << 22
+    say("h_compute 2^22 sampled")
+    a, b = synth.h_inputs(5, log_n)
+    ad, bd = gpu_mont(a), gpu_mont(b)
+    cd = g.fr_mul(ad, bd)
+    ctx = g.HContext(log_n)
+    hm, hs = ctx.h_compute(ad, bd, cd)
+    am, bm = host(ad), host(bd)
+    same(am[:4096], oracle.to_mont(a[:4096]), "A to Montgomery (prefix)")
+    cm = oracle.pointwise_mul_mont(am, bm)
+    same(host(cd)[:4096], cm[:4096], "C = A o B (prefix)")
+    rng = np.random.default_rng(22)
+    idx = np.array([0, 1, n - 1] + sorted(rng.integers(0, n, 2).tolist()), np.uint32)
+    want_m, want_s = oracle.h_at(log_n, am, bm, cm, idx)
+    hm_h, hs_h = host(hm), host(hs)
+    same(hm_h[idx], want_m, "h_mont 2^22 sampled")
+    same(hs_h[idx], want_s, "h_std 2^22 sampled")
+    # every output: canonical, and the two encodings agree
+    same(oracle.to_mont(hs_h[:65536]), hm_h[:65536], "dual encoding (prefix)")
+    # quotient degree <= n - 2: the top coefficient of the inverse transform is zero
+    coeffs = host(ctx.ntt_inverse(hm))
+    assert not coeffs[n - 1].any()
+    ctx.release()
+
+
+def test_fused_equals_unfused():
+    """The fused join equals coset evaluations materialised one by one and joined by the
+    standalone join (the POINTWISE_CU page keeps the unfused join for this check)."""
+    for log_n, kmax in ((9, None), (12, None), (12, 4), (18, None)):
+        say("fused vs unfused log_n=%d kmax=%s" % (log_n, kmax))
+        (ad, bd, cd), (am, bm, cm) = h_inputs(4, log_n)
+        with KMax(kmax):
+            ctx = g.HContext(log_n)
+        hm, hs = ctx.h_compute(ad, bd, cd)
+        ca, cb, cc = (ctx.coset_eval(v) for v in (ad, bd, cd))
+        if log_n <= 12:
+            same(host(ca), oracle.coset_eval(log_n, am), "coset_eval A")
+        um, us = g.h_join(ca, cb, cc)
+        same(host(um), host(hm), "fused vs unfused h_mont")
+        same(host(us), host(hs), "fused vs unfused h_std")
+        # in place coset evaluation
+        ctx.coset_eval(ad, out=ad)
+        same(host(ad), host(ca), "in-place coset_eval")
+        ctx.release()
+
+
+def test_degenerate_inputs():
+    import torch
+    for log_n in (1, 2, 10):
+        n = 1 << log_n
+        say("degenerate inputs log_n=%d" % log_n)
+        ctx = g.HContext(log_n)
+        z = torch.zeros((n, 8), dtype=torch.int32, device="cuda")
+        one = gpu_mont(synth.ints_to_fr([1] * n))
+        hm, hs = ctx.h_compute(z, z, z)
+        assert not host(hm).any() and not host(hs).any()
+        hm, hs = ctx.h_compute(one, one, z)
+        assert synth.fr_to_ints(host(hs)) == [1] * n
+        hm, hs = ctx.h_compute(one, one, one)
+        assert not host(hs).any()
+        ctx.release()
+
+
+def test_aliasing_and_bad_pointers():
+    import torch
+    log_n = 8
+    ctx = g.HContext(log_n)
+    (ad, bd, cd), _ = h_inputs(3, log_n)
+    with pytest.raises(g.G16Error) as e:
+        ctx.h_compute(ad, bd, cd, h_mont=ad)
+    assert e.value.code == g.G16_EALIAS
+    h = g.empty_fr(1 << log_n)
+    with pytest.raises(g.G16Error) as e:
+        ctx.h_compute(ad, bd, cd, h_mont=h, h_std=h)
+    assert e.value.code == g.G16_EALIAS
+    # a host pointer is refused before any launch
+    lib = g.load()
+    host_buf = np.zeros((1 << log_n, 8), np.uint32)
+    rc = lib.g16_ntt_forward(ctx.handle, host_buf.ctypes.data, ad.data_ptr(),
+                             torch.cuda.current_stream().cuda_stream)
+    assert rc == g.G16_EINVAL
+    # the workspace is not a valid output
+    rc = lib.g16_ntt_forward(ctx.handle, ad.data_ptr(), ctx.workspace.data_ptr(),
+                             torch.cuda.current_stream().cuda_stream)
+    assert rc == g.G16_EALIAS
+    ctx.release()
+    with pytest.raises(RuntimeError):
+        ctx.ntt_forward(ad)
+
+
+# ------------------------------------------------------------------ gather front end
+
+def _gather_device(ma, mb, w):
+    import torch
+
+    def idx(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.uint32).view(np.int32)).cuda()
+
+    vd_a = gpu_mont(ma.value) if ma.nnz else torch.zeros((0, 8), dtype=torch.int32,
+                                                         device="cuda")
+    vd_b = gpu_mont(mb.value) if mb.nnz else torch.zeros((0, 8), dtype=torch.int32,
+                                                         device="cuda")
+    return g.gather_abc(idx(ma.row_ptr), idx(ma.signal), vd_a, idx(mb.row_ptr),
+                        idx(mb.signal), vd_b, gpu_mont(w))
+
+
+@pytest.mark.parametrize("rows,n_witness", [(1000, 777), (4096, 3000)])
+def test_gather_small(rows, n_witness):
+    say("gather rows=%d" % rows)
+    ma, mb, w = synth.gather_inputs(4, rows=rows, n_witness=n_witness)
+    oa, ob, oc = _gather_device(ma, mb, w)
+    want = oracle.gather(ma.row_ptr, ma.signal, oracle.to_mont(ma.value), mb.row_ptr,
+                         mb.signal, oracle.to_mont(mb.value), oracle.to_mont(w))
+    for got, exp, name in zip((oa, ob, oc), want, "abc"):
+        same(host(got), exp, "gather out_" + name)
+
+
+def test_gather_bad_indices_are_flagged():
+    say("gather bad indices")
+    ma, mb, w = synth.gather_inputs(4, rows=300, n_witness=100)
+    rows_with_terms = np.flatnonzero(np.diff(ma.row_ptr.astype(np.int64)) > 0)
+    bad_row = int(rows_with_terms[3])
+    ma.signal = ma.signal.copy()
+    ma.signal[ma.row_ptr[bad_row]] = 100          # == n_witness: out of range
+    oa, ob, oc = _gather_device(ma, mb, w)
+    ha, hb, hc = host(oa), host(ob), host(oc)
+    assert (ha[bad_row] == 0xffffffff).all() and (hc[bad_row] == 0xffffffff).all()
+    good = np.ones(300, bool)
+    good[bad_row] = False
+    ma.signal[ma.row_ptr[bad_row]] = 0
+    want = oracle.gather(ma.row_ptr, ma.signal, oracle.to_mont(ma.value), mb.row_ptr,
+                         mb.signal, oracle.to_mont(mb.value), oracle.to_mont(w))
+    same(ha[good], want[0][good], "rows without bad indices")
+    # a row range past nnz is flagged too
+    ma.row_ptr = ma.row_ptr.copy()
+    ma.row_ptr[-1] = ma.nnz + 5
+    oa, _, _ = _gather_device(ma, mb, w)
+    assert (host(oa)[-1] == 0xffffffff).all()
+
+
+def test_gather_pipeline_2_18():
+    """The 2^18 gather workload end to end: gather, then the H pipeline."""
+    log_n = 18
+    say("gather + h_compute 2^18")
+    ma, mb, w = synth.gather_inputs(4)
+    oa, ob, oc = _gather_device(ma, mb, w)
+    want = oracle.gather(ma.row_ptr, ma.signal, oracle.to_mont(ma.value), mb.row_ptr,
+                         mb.signal, oracle.to_mont(mb.value), oracle.to_mont(w))
+    for got, exp, name in zip((oa, ob, oc), want, "abc"):
+        same(host(got), exp, "gather 2^18 out_" + name)
+    ctx = g.HContext(log_n)
+    hm, hs = ctx.h_compute(oa, ob, oc)
+    want_m, want_s = oracle.h_pipeline(log_n, *want)
+    same(host(hm), want_m, "gather pipeline h_mont")
+    same(host(hs), want_s, "gather pipeline h_std")
+    ctx.release()

@@ -18,8 +18,8 @@ fr = synth.ints_to_fr
 # (name, original text, planted text)
 MUTATIONS = [
     ("coset shift by the domain root", "sj = fe_mul(sj, shift);", "sj = fe_mul(sj, omega);"),
-    ("shift applied one index late", "v[k][j] = fe_mul(v[k][j], sj);\n            sj = fe_mul(sj, shift);",
-     "sj = fe_mul(sj, shift);\n            v[k][j] = fe_mul(v[k][j], sj);"),
+    ("shift applied one index late", "x[j] = fe_mul(x[j], sj);\n        sj = fe_mul(sj, shift);",
+     "sj = fe_mul(sj, shift);\n        x[j] = fe_mul(x[j], sj);"),
     ("size_inv dropped", "for (size_t i = 0; i < n; ++i) x[i] = fe_mul(x[i], size_inv);", ""),
     ("twiddle index without stride", "tw[j * step]", "tw[j]"),
     ("butterfly outputs swapped", "x[start + j] = fe_add(u, v);\n                x[start + j + half] = fe_sub(u, v);",

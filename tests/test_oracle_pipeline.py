@@ -139,3 +139,21 @@ def test_zero_and_degenerate_inputs():
     # A = 1, B = 1, C = 0: H = 1 everywhere on the coset
     hm, hs = oracle.h_pipeline(log_n, one, one, z)
     assert ints(hs) == [1] * n
+
+
+@pytest.mark.parametrize("log_n", [3, 11])
+def test_coset_eval_is_the_pipeline_first_half(log_n):
+    """Coset evaluations of one vector: Horner of its interpolant at s w^i, and the
+    pipeline's H equals the pointwise combination of three such vectors."""
+    n = 1 << log_n
+    am, bm, cm = _inputs(log_n, workload=6, c_is_product=False)
+    ca, cb, cc = (oracle.coset_eval(log_n, v) for v in (am, bm, cm))
+    omega, shift, _ = oracle.domain_roots(log_n)
+    coeffs = ints(oracle.ntt(oracle.from_mont(am), log_n, inverse=True))
+    got = ints(oracle.from_mont(ca))
+    for i in (0, 1, n // 2, n - 1):
+        assert got[i] == intref.horner(coeffs, shift * pow(omega, i, R) % R)
+    H = oracle.field_op("sub", oracle.field_op("mul", oracle.from_mont(ca), oracle.from_mont(cb)),
+                        oracle.from_mont(cc))
+    _, h_std = oracle.h_pipeline(log_n, am, bm, cm)
+    assert (H == h_std).all()
