@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--log-n", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage-reps", type=int, default=10)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (a known-size "
+                         "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
 
 
@@ -242,6 +245,17 @@ def main():
         },
         "cpu_baseline": None,
     }
+
+    if args.copy_calibration_mib:
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_calibration_bytes"] = nbytes
+        del src, dst
 
     if not args.no_cpu_baseline:
         import oracle
