@@ -3,10 +3,10 @@ from __future__ import annotations
 
 import os
 import subprocess
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "g16.hip")
 LIB = os.path.join(PKG, "libg16.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -28,19 +28,39 @@ def sources() -> list:
                   if f.endswith((".hip", ".hpp", ".h")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the library (always recompiles) and return its path."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, SRC]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
                     if "packed-fp32-ops" not in l)
     if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + out)
+        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + out)
     if verbose and out.strip():
-        print(out)
+        print(out, flush=True)
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    """Compile every translation unit (always recompiles) in parallel, link, and return
+    the library path."""
+    csrc = os.path.join(PKG, "csrc")
+    units = sorted(f for f in os.listdir(csrc) if f.endswith(".hip"))
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include")]
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    jobs = jobs or min(len(units), int(os.environ.get("MAX_JOBS", "8")), os.cpu_count() or 1)
+    objs = []
+    cmds = []
+    for u in units:
+        obj = os.path.join(objdir, u.replace(".hip", ".o"))
+        objs.append(obj)
+        cmds.append([HIPCC, *compile_flags, *inc, "-c", "-o", obj, os.path.join(csrc, u)])
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        for f in [ex.submit(_run, c, verbose) for c in cmds]:
+            f.result()
+    tmp = LIB + ".tmp%d" % os.getpid()
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -13,6 +13,8 @@
 #include <new>
 
 #include "kernels.hpp"
+#include "pointwise_kernels.hpp"
+#include "r8_launch.hpp"
 
 using g16::Fr;
 
@@ -111,8 +113,37 @@ void domain_roots(uint32_t log_n, Fr* omega, Fr* shift, Fr* size_inv) {
     *size_inv = g16::fr_inv(g16::fr_to_mont(n));
 }
 
+// The radix-8 kernel takes batches of 6..10 passes with at least one full workgroup
+// of slices; the radix-2 kernel takes the rest (small domains, other batch sizes).
+template <g16::Mode M, bool J>
+bool try_r8(const g16::BatchParams& p, uint32_t n_vec, hipStream_t stream, int* rc) {
+    const uint32_t k = p.k, L = p.log_n;
+    if (std::getenv("G16_RADIX2")) return false;
+    auto fits = [&](uint32_t spw) { return (1ull << (L - k)) >= spw; };
+    hipError_t e;
+    switch (k) {
+#define G16_R8_CASE(KK)                                                        \
+        case KK:                                                               \
+            if (!fits(g16::R8Geom<KK, g16::kR8Group>::kSpw)) return false;      \
+            e = g16::launch_r8<KK, M, J>(p, n_vec, stream);                     \
+            *rc = e == hipSuccess ? G16_OK : G16_EHIP;                          \
+            return true;
+        G16_R8_CASE(6)
+        G16_R8_CASE(7)
+        G16_R8_CASE(8)
+        G16_R8_CASE(9)
+        G16_R8_CASE(10)
+#undef G16_R8_CASE
+        default:
+            return false;
+    }
+}
+
 template <g16::Mode M, bool J>
 int launch_batch(const g16::BatchParams& p, uint32_t n_vec, hipStream_t stream) {
+    int rc = G16_OK;
+    if (try_r8<M, J>(p, n_vec, stream, &rc)) return rc;
+    // radix-2 batch kernel: small batches and small domains
     const uint32_t k = p.k, L = p.log_n;
     g16::BatchParams q = p;
     uint32_t log_spw = 0;

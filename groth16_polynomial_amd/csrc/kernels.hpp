@@ -126,9 +126,9 @@ __device__ __forceinline__ void lds_pass(Fr* sh, const Fr* tw, uint32_t log_n, u
             Fr w = ld_global(tw + ((size_t)(low + (jm << s0)) << twshift));
             if (DIF) {
                 st_lds(base + lo, fr_add(u, v));
-                st_lds(base + hi, fr_mul(fr_sub(u, v), w));
+                st_lds(base + hi, fr_mul_tab(fr_sub(u, v), w));
             } else {
-                Fr vw = fr_mul(v, w);
+                Fr vw = fr_mul_tab(v, w);
                 st_lds(base + lo, fr_add(u, vw));
                 st_lds(base + hi, fr_sub(u, vw));
             }
@@ -151,7 +151,14 @@ __global__ void __launch_bounds__(256) ntt_batch_kernel(BatchParams p) {
     const uint32_t total = spw << k;
     const Fr* src = p.src[blockIdx.y];
     Fr* dst = p.dst[blockIdx.y];
-    const uint32_t g0 = blockIdx.x << p.log_spw;  // first slice of this workgroup
+    // Workgroups are dispatched to the eight XCDs round-robin (workgroup i to XCD i mod 8),
+    // and each XCD has its own L2.  Renumber them so that each XCD takes one contiguous
+    // run of slice groups: neighbouring slices (strided batches: neighbouring columns,
+    // which share 128-byte lines of data and twiddles) and the same slice of all
+    // vectors (grid.y) then meet in one L2.
+    uint32_t wg = blockIdx.x;
+    if ((gridDim.x & 7u) == 0u) wg = (wg & 7u) * (gridDim.x >> 3) + (wg >> 3);
+    const uint32_t g0 = wg << p.log_spw;  // first slice of this workgroup
     const bool strided = (M == Mode::DitStrided || M == Mode::DifStrided);
 
     // Global index of local element (sl, m).
@@ -195,7 +202,7 @@ __global__ void __launch_bounds__(256) ntt_batch_kernel(BatchParams p) {
         for (uint32_t e = threadIdx.x; e < total; e += blockDim.x) {
             uint32_t sl = e >> k, m = e & (slice_len - 1u);
             Fr* q = sh + ((size_t)sl << k) + m;
-            st_lds(q, fr_mul(ld_lds(q), ld_global(p.scale + gindex(sl, m))));
+            st_lds(q, fr_mul_tab(ld_lds(q), ld_global(p.scale + gindex(sl, m))));
         }
         __syncthreads();
         for (uint32_t t = 0; t < k; ++t)
@@ -214,91 +221,10 @@ __global__ void __launch_bounds__(256) ntt_batch_kernel(BatchParams p) {
     }
 }
 
-// ------------------------------------------------------------------ element-wise kernels
+}  // namespace g16
 
-__global__ void __launch_bounds__(256) h_join_kernel(const Fr* a, const Fr* b, const Fr* c,
-                                                     Fr* h_mont, Fr* h_std, uint64_t n) {
-    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-         i += (uint64_t)gridDim.x * blockDim.x) {
-        Fr h = fr_sub(fr_mul(ld_global(a + i), ld_global(b + i)), ld_global(c + i));
-        st_global(h_mont + i, h);
-        st_global(h_std + i, fr_from_mont(h));
-    }
-}
+#include "ntt_r8.hpp"
 
-// op 0: to Montgomery, 1: from Montgomery, 2: product with b
-__global__ void __launch_bounds__(256) elementwise_kernel(const Fr* a, const Fr* b, Fr* out,
-                                                          uint64_t n, int op) {
-    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-         i += (uint64_t)gridDim.x * blockDim.x) {
-        Fr x = ld_global(a + i);
-        Fr y;
-        if (op == 0) y = fr_to_mont(x);
-        else if (op == 1) y = fr_from_mont(x);
-        else y = fr_mul(x, ld_global(b + i));
-        st_global(out + i, y);
-    }
-}
-
-// Table builders.  Each thread raises the base to its own exponent (prepare time only).
-//   kind 0: T[j] = base^j                         (twiddles, j < count)
-//   kind 1: T[p] = factor * base^bitrev_L(p)      (coset table, p < count = 2^L)
-__global__ void __launch_bounds__(256) table_kernel(Fr* out, Fr base, Fr factor,
-                                                    uint64_t count, uint32_t log_n, int kind) {
-    for (uint64_t j = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; j < count;
-         j += (uint64_t)gridDim.x * blockDim.x) {
-        if (kind == 0) {
-            st_global(out + j, fr_pow_u64(base, j));
-        } else {
-            uint64_t e = bitrev_bits((uint32_t)j, log_n);
-            st_global(out + j, fr_mul(factor, fr_pow_u64(base, e)));
-        }
-    }
-}
-
-// The CSR gather, one lane per row (the GATHER_CU page: rows are short and ragged, so a
-// row per lane keeps every lane busy; 64 consecutive rows share a wave here).
-__device__ __forceinline__ Fr fr_invalid() {
-    Fr z;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) z.w[i] = 0xffffffffu;
-    return z;
-}
-
-__device__ __forceinline__ bool gather_row(const uint32_t* row_ptr, const uint32_t* signal,
-                                           const Fr* value, uint64_t nnz, const Fr* witness,
-                                           uint64_t n_witness, uint64_t row, Fr& acc) {
-    uint32_t lo = row_ptr[row];
-    uint32_t hi = row_ptr[row + 1];
-    acc = fr_zero();
-    if (lo > hi || (uint64_t)hi > nnz) return false;
-    for (uint32_t k = lo; k < hi; ++k) {
-        uint32_t s = signal[k];
-        if ((uint64_t)s >= n_witness) return false;
-        acc = fr_add(acc, fr_mul(ld_global(value + k), ld_global(witness + s)));
-    }
-    return true;
-}
-
-__global__ void __launch_bounds__(256) gather_kernel(
-    const uint32_t* row_ptr_a, const uint32_t* signal_a, const Fr* value_a, uint64_t nnz_a,
-    const uint32_t* row_ptr_b, const uint32_t* signal_b, const Fr* value_b, uint64_t nnz_b,
-    const Fr* witness, uint64_t n_witness, Fr* out_a, Fr* out_b, Fr* out_c, uint64_t n_rows) {
-    uint64_t row = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (row >= n_rows) return;
-    Fr a, b;
-    bool ok = gather_row(row_ptr_a, signal_a, value_a, nnz_a, witness, n_witness, row, a);
-    ok = gather_row(row_ptr_b, signal_b, value_b, nnz_b, witness, n_witness, row, b) && ok;
-    if (ok) {
-        st_global(out_a + row, a);
-        st_global(out_b + row, b);
-        st_global(out_c + row, fr_mul(a, b));
-    } else {
-        Fr bad = fr_invalid();
-        st_global(out_a + row, bad);
-        st_global(out_b + row, bad);
-        st_global(out_c + row, bad);
-    }
-}
+namespace g16 {
 
 }  // namespace g16

@@ -1,0 +1,30 @@
+// Defines and instantiates the radix-8 launchers for one batch size G16_R8_K.
+#pragma once
+
+#include "r8_launch.hpp"
+
+namespace g16 {
+
+template <int K, Mode M, bool JOIN>
+hipError_t launch_r8(const BatchParams& p, uint32_t n_vec, hipStream_t stream) {
+    using G = R8Geom<K, kR8Group>;
+    const uint64_t groups = (1ull << (p.log_n - K)) / G::kSpw;
+    hipLaunchKernelGGL((ntt_r8_kernel<K, kR8Group, M, JOIN>), dim3((uint32_t)groups, n_vec, 1),
+                       dim3(G::kThreads), G::kLdsBytes, stream, p);
+    return hipGetLastError();
+}
+
+template hipError_t launch_r8<G16_R8_K, Mode::HeadBitrev, false>(const BatchParams&, uint32_t,
+                                                                 hipStream_t);
+template hipError_t launch_r8<G16_R8_K, Mode::DitStrided, false>(const BatchParams&, uint32_t,
+                                                                 hipStream_t);
+template hipError_t launch_r8<G16_R8_K, Mode::DitStrided, true>(const BatchParams&, uint32_t,
+                                                                hipStream_t);
+template hipError_t launch_r8<G16_R8_K, Mode::DifStrided, false>(const BatchParams&, uint32_t,
+                                                                 hipStream_t);
+template hipError_t launch_r8<G16_R8_K, Mode::Fused, false>(const BatchParams&, uint32_t,
+                                                            hipStream_t);
+template hipError_t launch_r8<G16_R8_K, Mode::Fused, true>(const BatchParams&, uint32_t,
+                                                           hipStream_t);
+
+}  // namespace g16
