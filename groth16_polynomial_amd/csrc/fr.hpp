@@ -199,34 +199,10 @@ G16_HD Fr fr_from_mont(const Fr& a) {
     return fr_reduce_once(out);
 }
 
-// ---------------------------------------------------------------- products by a table
-//
-// Twiddles and coset factors are fixed tables, so their products use a second
-// Montgomery radix, R' = 2^261, on nine 29-bit limbs: every limb product is below 2^58
-// and a column of the product holds at most nine a*b and nine m*r terms plus the carry
-// from the column below, less than 2^63, so each column accumulates in one 64-bit
-// register pair with v_mad_u64_u32 and no carry chain (finely integrated product
-// scanning, Koc-Acar-Kaliski 1996).  A table entry is stored as w * 2^261 mod r, and
-// then x (in the 2^256 Montgomery form) times it gives x w 2^256 * 2^261 / 2^261, i.e.
-// x w still in the 2^256 form.
-
+// 29-bit digit mask and 2^261 mod r (standard form), used by the digit layer (fr29.hpp)
+// to build table entries.
 constexpr uint32_t kM29 = (1u << 29) - 1u;
 
-struct F29 {
-    uint32_t l[9];  // little-endian 29-bit limbs (limb 8 holds bits 232..255)
-};
-
-// r in nine 29-bit limbs
-G16_HD constexpr uint32_t r29_limb(int k) {
-    return k == 0 ? 0x10000001u : k == 1 ? 0x1f0fac9fu : k == 2 ? 0x0e5c2450u
-         : k == 3 ? 0x07d090f3u : k == 4 ? 0x1585d283u : k == 5 ? 0x02db40c0u
-         : k == 6 ? 0x00a6e141u : k == 7 ? 0x0e5c2634u : 0x0030644eu;
-}
-// -r^-1 mod 2^29
-constexpr uint32_t kNPrime29 = kNPrime & kM29;
-static_assert(uint32_t(0x10000001u * kNPrime29) % (1u << 29) == kM29, "kNPrime29");
-
-// 2^261 mod r (standard form): multiplying a 2^256-form value by it gives the 2^261 form.
 G16_HD constexpr uint32_t c261_limb(int i) {
     return i == 0 ? 0x8fffff57u : i == 1 ? 0x2fd4e156u : i == 2 ? 0xa494b01au
          : i == 3 ? 0x75bba827u : i == 4 ? 0x819caa80u : i == 5 ? 0x5301fa84u
@@ -239,120 +215,6 @@ G16_HD Fr fr_c261() {
     for (int i = 0; i < 8; ++i) z.w[i] = c261_limb(i);
     return z;
 }
-
-G16_HD F29 unpack29(const Fr& x) {
-    F29 r;
-#pragma unroll
-    for (int k = 0; k < 9; ++k) {
-        const int bit = 29 * k, w = bit >> 5, s = bit & 31;
-        uint32_t v = x.w[w] >> s;
-        if (s > 3 && w + 1 < 8) v |= x.w[w + 1] << (32 - s);
-        r.l[k] = (k < 8) ? (v & kM29) : v;
-    }
-    return r;
-}
-
-// Limbs below 2^29 (limb 8 below 2^24) back to eight 32-bit words.
-G16_HD Fr pack29(const F29& u) {
-    Fr x;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int bit = 32 * j;
-        const int k = bit / 29, off = bit - 29 * k;
-        uint32_t v = u.l[k] >> off;
-        if (k + 1 < 9) v |= u.l[k + 1] << (29 - off);
-        if (k + 2 < 9 && 58 - off < 32) v |= u.l[k + 2] << (58 - off);
-        x.w[j] = v;
-    }
-    return x;
-}
-
-// a * b * 2^-261 mod r for any 256-bit a and canonical b (b already unpacked), NOT
-// reduced: the Montgomery sum a b + m r is below 2^256 r + 2^261 r, so the result is
-// below (1 + 2^-5) r < 2r.
-G16_HD Fr fr_mul29_lazy(const Fr& ap, const F29& b) {
-    const F29 a = unpack29(ap);
-    uint32_t m[9];
-    F29 u;
-    uint64_t acc = 0;
-#pragma unroll
-    for (int i = 0; i < 9; ++i) {
-#pragma unroll
-        for (int j = 0; j < i; ++j) {
-            acc += (uint64_t)a.l[j] * b.l[i - j];
-            acc += (uint64_t)m[j] * r29_limb(i - j);
-        }
-        acc += (uint64_t)a.l[i] * b.l[0];
-        m[i] = ((uint32_t)acc * kNPrime29) & kM29;
-        acc += (uint64_t)m[i] * r29_limb(0);  // the low 29 bits become zero
-        acc >>= 29;
-    }
-#pragma unroll
-    for (int i = 9; i < 17; ++i) {
-#pragma unroll
-        for (int j = i - 8; j < 9; ++j) {
-            acc += (uint64_t)a.l[j] * b.l[i - j];
-            acc += (uint64_t)m[j] * r29_limb(i - j);
-        }
-        u.l[i - 9] = (uint32_t)acc & kM29;
-        acc >>= 29;
-    }
-    u.l[8] = (uint32_t)acc;
-    return pack29(u);
-}
-
-// The same product reduced to [0, r).
-G16_HD Fr fr_mul29(const Fr& ap, const F29& b) { return fr_reduce_once(fr_mul29_lazy(ap, b)); }
-
-// ---------------------------------------------------------------- lazy ranges
-//
-// Inside a transform kernel values may sit in [0, 2r) or [0, 4r) between passes (4r is
-// below 2^256 because r < 2^254); every value a kernel stores to HBM is canonical.
-
-G16_HD constexpr uint32_t r2_times_limb(int i) {  // 2r, little-endian 32-bit limbs
-    return i == 0 ? 0xe0000002u : i == 1 ? 0x87c3eb27u : i == 2 ? 0xf372e122u
-         : i == 3 ? 0x5067d090u : i == 4 ? 0x0302b0bau : i == 5 ? 0x70a08b6du
-         : i == 6 ? 0xc2634053u : 0x60c89ce5u;
-}
-
-// x in [0, 4r) -> [0, 2r)
-G16_HD Fr fr_reduce_2r(const Fr& x) {
-    Fr d;
-    uint32_t borrow = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) d.w[i] = subb(x.w[i], r2_times_limb(i), borrow);
-    Fr out;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) out.w[i] = borrow ? x.w[i] : d.w[i];
-    return out;
-}
-
-// x in [0, 4r) -> canonical
-G16_HD Fr fr_canon_4r(const Fr& x) { return fr_reduce_once(fr_reduce_2r(x)); }
-
-// a + b for a + b < 2^256 (no reduction)
-G16_HD Fr fr_add_lazy(const Fr& a, const Fr& b) {
-    Fr s;
-    uint32_t c = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s.w[i] = addc(a.w[i], b.w[i], c);
-    return s;
-}
-
-// a + 2r - b for a < 2r, b <= 2r: in [0, 4r)
-G16_HD Fr fr_sub_lazy(const Fr& a, const Fr& b) {
-    Fr s;
-    uint32_t c = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s.w[i] = addc(a.w[i], r2_times_limb(i), c);
-    uint32_t borrow = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s.w[i] = subb(s.w[i], b.w[i], borrow);
-    return s;
-}
-
-// x * w for a table entry w stored in the 2^261 form (see above): x w in x's form.
-G16_HD Fr fr_mul_tab(const Fr& x, const Fr& w261) { return fr_mul29(x, unpack29(w261)); }
 
 // Standard form -> Montgomery form: x * R^2 * R^-1 = x R mod r.
 G16_HD Fr fr_to_mont(const Fr& x) { return fr_mul(x, fr_r2()); }

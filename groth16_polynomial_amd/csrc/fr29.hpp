@@ -1,0 +1,297 @@
+// Fr in nine signed 29-bit digits, kept in registers and LDS through the transform
+// passes, and the product by a fixed table entry (Shoup's method).
+//
+// Why a second representation.  On gfx950 every add-with-carry that reads the carry of
+// the previous VALU instruction waits two issue slots, so the 8 x 32-bit carry chains
+// of fr.hpp cost about three slots per limb, and a 32-bit limb product cannot be
+// accumulated without one.  With 29-bit digits a digit product is below 2^58 and a
+// column of up to 18 products plus a carry stays inside a signed 64-bit accumulator,
+// so every product is one v_mad_i64_i32 and nothing else propagates carries; adds and
+// subtracts are digit-wise 32-bit adds with no carry at all.
+//
+// Value of a V29: sum of l[k] 2^(29k) with signed 32-bit digits.  "Normalized" means
+// digits 0..7 in [-4, 2^29 + 3) (what fr29_normalize returns; a product output and a
+// freshly split canonical value have them in [0, 2^29)).  A Cooley-Tukey butterfly
+// replaces (lo, hi) by lo + t and lo - t with t = w hi a product output, so both results
+// sit one pass further from lo's last normalization than lo did, and hi's own growth
+// does not carry over.  After p passes from normalized a digit is below
+// 2^29 + 3 + p (2^29 - 1) in magnitude, so three passes still fit in 32 bits (and any
+// 32-bit digits are a valid product input).  The transforms therefore normalize, at the start of each register group of two
+// passes, only the elements that are "lo" in the group's first pass: every group output
+// is then exactly two passes from normalized.
+//
+// Product by a table entry (V. Shoup, NTL; D. Harvey, "Faster arithmetic for
+// number-theoretic transforms", J. Symb. Comp. 2014): for a fixed w < r store w and
+// w' = floor(w 2^261 / r).  Then q = floor(x w' / 2^261) is within one or two of
+// x w / r and x w - q r is x w mod r up to a few multiples of r.  Only the top columns
+// of x w' are needed for q and only the low 261 bits of x w - q r, because that
+// difference is small.  This needs 53 + 45 + 45 = 143 digit products against 162 for a
+// Montgomery product on nine digits.  The result keeps x's Montgomery factor (w is a
+// plain integer), so data stay in the 2^256 Montgomery form of the library's
+// interface.  Table digits are balanced (|digit| <= 2^28, the top digit of w' up to
+// 2^29 + 1), which halves the size of every product and so doubles the input range a
+// column can absorb.
+#pragma once
+
+#include "fr.hpp"
+
+namespace g16 {
+
+struct V29 {
+    int32_t l[9];
+};
+
+// A table entry: w and w' = floor(w 2^261 / r) in balanced 29-bit digits, padded to
+// 80 bytes so an entry is five 16-byte loads.
+struct Tw29 {
+    int32_t w[9];
+    int32_t wp[9];
+    int32_t pad[2];
+};
+static_assert(sizeof(Tw29) == 80, "table entries are 80 bytes");
+
+// -r in balanced 29-bit digits (x w - q r is formed as x w + q (-r))
+G16_HD constexpr int32_t mr29_digit(int k) {
+    return k == 0 ? 0x0fffffff : k == 1 ? 0x00f05360 : k == 2 ? -0x0e5c2451
+         : k == 3 ? -0x07d090f3 : k == 4 ? 0x0a7a2d7d : k == 5 ? -0x02db40c1
+         : k == 6 ? -0x00a6e141 : k == 7 ? -0x0e5c2634 : -0x0030644e;
+}
+// r^-1 mod 2^261 in unsigned 29-bit digits (exact division by r in the table builder)
+G16_HD constexpr uint32_t rinv261_limb(int k) {
+    return k == 0 ? 0x10000001u : k == 1 ? 0x08f05360u : k == 2 ? 0x05bb930fu
+         : k == 3 ? 0x12f36967u : k == 4 ? 0x1dc6e9a7u : k == 5 ? 0x13ebb37cu
+         : k == 6 ? 0x19347195u : k == 7 ? 0x1c5e4f97u : 0x0d8c07d0u;
+}
+
+// canonical 8 x 32-bit -> nine 29-bit digits (all in [0, 2^29))
+G16_HD V29 fr29_from_fr(const Fr& x) {
+    V29 r;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+        const int bit = 29 * k, w = bit >> 5, s = bit & 31;
+        uint32_t v = x.w[w] >> s;
+        if (s > 3 && w + 1 < 8) v |= x.w[w + 1] << (32 - s);
+        r.l[k] = (int32_t)((k < 8) ? (v & kM29) : v);
+    }
+    return r;
+}
+
+// Digits in [0, 2^29) (value below 2^256) -> eight 32-bit words.
+G16_HD Fr fr29_pack(const V29& u) {
+    Fr x;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int bit = 32 * j;
+        const int k = bit / 29, off = bit - 29 * k;
+        uint32_t v = (uint32_t)u.l[k] >> off;
+        if (k + 1 < 9) v |= (uint32_t)u.l[k + 1] << (29 - off);
+        if (k + 2 < 9 && 58 - off < 32) v |= (uint32_t)u.l[k + 2] << (58 - off);
+        x.w[j] = v;
+    }
+    return x;
+}
+
+G16_HD V29 fr29_add(const V29& a, const V29& b) {
+    V29 s;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) s.l[k] = a.l[k] + b.l[k];
+    return s;
+}
+
+G16_HD V29 fr29_sub(const V29& a, const V29& b) {
+    V29 s;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) s.l[k] = a.l[k] - b.l[k];
+    return s;
+}
+
+// Carry-save normalization: digit k keeps its low 29 bits plus the (signed) carry out of
+// digit k-1, which is in [-4, 4) for digits below 2^31 in magnitude.  The value is
+// unchanged; digit 8 absorbs the carry of digit 7.
+G16_HD V29 fr29_normalize(const V29& a) {
+    V29 o;
+    o.l[0] = a.l[0] & (int32_t)kM29;
+#pragma unroll
+    for (int k = 1; k < 8; ++k) o.l[k] = (a.l[k] & (int32_t)kM29) + (a.l[k - 1] >> 29);
+    o.l[8] = a.l[8] + (a.l[7] >> 29);
+    return o;
+}
+
+// One multiply-add of the signed column accumulators.  The empty asm statement makes the
+// running sum opaque, which keeps each column one chain of v_mad_i64_i32 starting from the
+// carry of the column below: 143 multiply-adds, 19 masks and 18 shifts per product,
+// against about 210 instructions when the compiler splits each column into parallel
+// partial sums and adds the carry separately.  It does not stop the scheduler from
+// interleaving independent chains, which shoup_mul_n relies on.
+G16_HD int64_t mad_chain(int32_t a, int32_t b, int64_t c) {
+    int64_t d = (int64_t)a * b + c;
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm("" : "+v"(d));
+#endif
+    return d;
+}
+
+// y[n] = x[n] w_n mod r up to a small multiple of r, for table entries t[n] = (w, w').
+//   Any 32-bit digits are admissible: with |digit| <= 2^31 every column stays inside the
+//   signed 64-bit range (ten products below 2^59 for the q columns, whose top w' digit
+//   may reach 2^29 + 1; nine below 2^59 plus nine below 2^57 for the low columns; plus a
+//   carry below 2^35).
+//   Result: digits 0..7 in [0, 2^29), digit 8 signed; value congruent to x w, with
+//   -7 r < value < 9 r, so |digit 8| < 2^25.
+// q is taken from columns 7..16 of x w': the dropped columns 0..6 add less than 2^237 in
+// magnitude, far below one unit of q (2^261), so q is within one of floor(x w' / 2^261),
+// and x w - q r lies within (x/2^261 +- 2) r of zero.
+template <int N>
+G16_HD void shoup_mul_n(const V29 (&xin)[N], const Tw29 (&t)[N], V29 (&y)[N]) {
+    // The input digits go through an empty asm statement too: where the compiler can
+    // prove a digit non-negative it widens it with a zero extension, and a zero-extended
+    // times a sign-extended operand has no single-instruction multiply-add (it becomes
+    // two v_mad_u64_u32 and two moves).
+    V29 x[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+#pragma unroll
+        for (int k = 0; k < 9; ++k) {
+            x[n].l[k] = xin[n].l[k];
+#if defined(__HIP_DEVICE_COMPILE__)
+            asm("" : "+v"(x[n].l[k]));
+#endif
+        }
+    }
+    int32_t q[N][9];
+    int64_t acc[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) acc[n] = 0;
+    // q: columns 7..16 of x w'; its digits are taken in [0, 2^29) (q mod 2^261 is all the
+    // low part needs)
+#pragma unroll
+    for (int c = 7; c < 17; ++c) {
+#pragma unroll
+        for (int i = 0; i < 9; ++i) {
+            const int j = c - i;
+            if (j >= 0 && j < 9) {
+#pragma unroll
+                for (int n = 0; n < N; ++n) acc[n] = mad_chain(x[n].l[i], t[n].wp[j], acc[n]);
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            if (c >= 9) q[n][c - 9] = (int32_t)((uint32_t)acc[n] & kM29);
+            acc[n] >>= 29;
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        q[n][8] = (int32_t)((uint32_t)acc[n] & kM29);
+        acc[n] = 0;
+    }
+    // y: columns 0..8 of x w + q (-r) = (x w - q r) mod 2^261; the top digit is read back
+    // as a signed 29-bit number, which is exact since |x w - q r| < 2^257
+#pragma unroll
+    for (int c = 0; c < 9; ++c) {
+#pragma unroll
+        for (int i = 0; i <= c; ++i) {
+#pragma unroll
+            for (int n = 0; n < N; ++n) acc[n] = mad_chain(x[n].l[i], t[n].w[c - i], acc[n]);
+#pragma unroll
+            for (int n = 0; n < N; ++n) acc[n] = mad_chain(q[n][i], mr29_digit(c - i), acc[n]);
+        }
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            if (c < 8) {
+                y[n].l[c] = (int32_t)((uint32_t)acc[n] & kM29);
+                acc[n] >>= 29;
+            } else {
+                y[n].l[8] = ((int32_t)((uint32_t)acc[n] << 3)) >> 3;
+            }
+        }
+    }
+}
+
+G16_HD V29 shoup_mul(const V29& x, const Tw29& t) {
+    V29 xs[1] = {x};
+    Tw29 ts[1] = {t};
+    V29 ys[1];
+    shoup_mul_n<1>(xs, ts, ys);
+    return ys[0];
+}
+
+// Any V29 with digits below 2^31 in magnitude -> canonical 8 x 32-bit.
+//   1. exact carry propagation (digits 0..7 in [0, 2^29), digit 8 signed);
+//   2. q = floor(value / r) or one less, from the top two digits in double precision
+//      (the error of the estimate is below 2^-40, the margin 2^-10);
+//   3. value - q r = (value + q (-r)) mod 2^261, in [0, 2r);
+//   4. pack and one conditional subtraction.
+G16_HD Fr fr29_canon(const V29& a) {
+    int32_t l[9];
+#pragma unroll
+    for (int k = 0; k < 9; ++k) l[k] = a.l[k];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        l[k + 1] += l[k] >> 29;
+        l[k] &= (int32_t)kM29;
+    }
+    // 2^232 / r and 2^203 / r
+    const double c8 = 0x1.5291d18988e81p-22, c7 = 0x1.5291d18988e81p-51;
+    const double qd = floor((double)l[8] * c8 + (double)l[7] * c7 - 0x1p-10);
+    const int32_t q = (int32_t)qd;
+    V29 y;
+    int64_t acc = 0;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+        acc += (int64_t)q * mr29_digit(k) + l[k];
+        y.l[k] = (int32_t)((uint32_t)acc & kM29);
+        acc >>= 29;
+    }
+    return fr_reduce_once(fr29_pack(y));
+}
+
+// Unsigned 29-bit digits (the top one below 2^29) -> balanced digits, value unchanged.
+G16_HD void balance29(const uint32_t (&d)[9], int32_t (&o)[9]) {
+    int32_t carry = 0;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+        int32_t v = (int32_t)d[k] + carry;
+        if (k < 8 && v >= (1 << 28)) {
+            v -= (1 << 29);
+            carry = 1;
+        } else {
+            carry = 0;
+        }
+        o[k] = v;
+    }
+}
+
+// The table entry for a value given in Montgomery form: w = wm 2^-256 (plain) and
+// w' = floor(w 2^261 / r).  With rem = w 2^261 mod r (fr_mul(wm, 2^261 mod r)), w 2^261
+// = w' r + rem exactly, so w' = -rem r^-1 mod 2^261 (exact division by the odd r).
+G16_HD Tw29 tw29_entry(const Fr& wm) {
+    Tw29 t;
+    const V29 w = fr29_from_fr(fr_from_mont(wm));
+    const V29 rem = fr29_from_fr(fr_mul(wm, fr_c261()));
+    // p = rem r^-1 mod 2^261 (low half product), then w' = 2^261 - p mod 2^261
+    uint32_t p[9];
+    uint64_t acc = 0;
+#pragma unroll
+    for (int c = 0; c < 9; ++c) {
+#pragma unroll
+        for (int i = 0; i <= c; ++i) acc += (uint64_t)(uint32_t)rem.l[i] * rinv261_limb(c - i);
+        p[c] = (uint32_t)acc & kM29;
+        acc >>= 29;
+    }
+    uint32_t wp[9], wd[9];
+    uint32_t borrow = 0;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+        uint32_t d = 0u - p[k] - borrow;  // digit of 2^261 - p, with borrow
+        borrow = (p[k] + borrow) != 0u ? 1u : 0u;
+        wp[k] = d & kM29;
+        wd[k] = (uint32_t)w.l[k];
+    }
+    balance29(wd, t.w);
+    balance29(wp, t.wp);
+    t.pad[0] = t.pad[1] = 0;
+    return t;
+}
+
+}  // namespace g16

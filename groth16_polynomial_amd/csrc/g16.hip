@@ -34,13 +34,14 @@ struct g16_ctx {
     uint32_t magic;
     uint32_t log_n;
     int device;
-    Fr* tw_fwd;   // omega^j, j < n/2
-    Fr* tw_inv;   // omega^-j, j < n/2
-    Fr* coset;    // n^-1 s^bitrev(p), p < n
+    g16::Tw29* tw_fwd;  // omega^j, j < n/2
+    g16::Tw29* tw_inv;  // omega^-j, j < n/2
+    g16::Tw29* coset;   // n^-1 s^bitrev(p), p < n
     Fr* scratch;  // three n-element vectors
     const uint8_t* ws_begin;
     size_t ws_bytes;
     Fr omega, omega_inv, shift, size_inv;  // Montgomery form
+    g16::Tw29 size_inv_entry;              // n^-1 as a table entry (inverse transform)
     uint32_t n_batches;
     uint32_t batch_k[kMaxBatches];  // lowest bits first
 };
@@ -186,7 +187,7 @@ int run_ntt(g16_ctx* c, const void* in, void* out, void* stream, bool inverse) {
     g16::BatchParams p = base_params(c);
     p.tw = inverse ? c->tw_inv : c->tw_fwd;
     p.use_kscale = inverse ? 1u : 0u;
-    p.kscale = c->size_inv;
+    p.kscale = c->size_inv_entry;
     p.s0 = 0;
     p.k = c->batch_k[0];
     p.src[0] = (const Fr*)in;
@@ -208,7 +209,7 @@ int run_ntt(g16_ctx* c, const void* in, void* out, void* stream, bool inverse) {
         t.k = c->batch_k[b];
         t.src[0] = scr;
         t.dst[0] = (b + 1 == c->n_batches) ? (Fr*)out : scr;
-        rc = launch_batch<g16::Mode::DitStrided, false>(t, 1, s);
+        rc = launch_batch<g16::Mode::FwdStrided, false>(t, 1, s);
         if (rc) return rc;
     }
     return G16_OK;
@@ -230,11 +231,11 @@ int exec_launch(const Launch& l, hipStream_t s) {
         case Mode::Fused:
             return l.join ? launch_batch<Mode::Fused, true>(l.p, l.n_vec, s)
                           : launch_batch<Mode::Fused, false>(l.p, l.n_vec, s);
-        case Mode::DitStrided:
-            return l.join ? launch_batch<Mode::DitStrided, true>(l.p, l.n_vec, s)
-                          : launch_batch<Mode::DitStrided, false>(l.p, l.n_vec, s);
-        case Mode::DifStrided:
-            return launch_batch<Mode::DifStrided, false>(l.p, l.n_vec, s);
+        case Mode::FwdStrided:
+            return l.join ? launch_batch<Mode::FwdStrided, true>(l.p, l.n_vec, s)
+                          : launch_batch<Mode::FwdStrided, false>(l.p, l.n_vec, s);
+        case Mode::InvStrided:
+            return launch_batch<Mode::InvStrided, false>(l.p, l.n_vec, s);
         default:
             return launch_batch<Mode::HeadBitrev, false>(l.p, l.n_vec, s);
     }
@@ -276,7 +277,7 @@ uint32_t plan_coset(const g16_ctx* c, const Fr* const* srcs, Fr* const* dsts, ui
             p.src[v] = (b == nb - 1) ? srcs[v] : dsts[v];
             p.dst[v] = dsts[v];
         }
-        add(g16::Mode::DifStrided, false, p, n_vec);
+        add(g16::Mode::InvStrided, false, p, n_vec);
     }
     // lowest batch of both transforms with the coset multiply between them
     g16::BatchParams f = base_params(c);
@@ -305,10 +306,10 @@ uint32_t plan_coset(const g16_ctx* c, const Fr* const* srcs, Fr* const* dsts, ui
             p.dst[v] = dsts[v];
         }
         if (b + 1 == nb && join) {
-            if (plain_vec) add(g16::Mode::DitStrided, false, p, plain_vec);
-            add(g16::Mode::DitStrided, true, joined(p), 1);
+            if (plain_vec) add(g16::Mode::FwdStrided, false, p, plain_vec);
+            add(g16::Mode::FwdStrided, true, joined(p), 1);
         } else {
-            add(g16::Mode::DitStrided, false, p, n_vec);
+            add(g16::Mode::FwdStrided, false, p, n_vec);
         }
     }
     return count;
@@ -381,9 +382,10 @@ int g16_batch_plan(uint32_t log_n, uint32_t kmax, uint32_t* ks, uint32_t cap) {
 size_t g16_h_workspace_bytes(uint32_t log_n) {
     if (log_n < G16_MIN_LOG_N || log_n > G16_MAX_LOG_N) return 0;
     size_t n = size_t(1) << log_n;
-    size_t half = round_up((n / 2) * sizeof(Fr));
+    size_t half_tab = round_up((n / 2) * sizeof(g16::Tw29));
+    size_t full_tab = round_up(n * sizeof(g16::Tw29));
     size_t full = round_up(n * sizeof(Fr));
-    return 2 * half + full + 3 * full;
+    return 2 * half_tab + full_tab + 3 * full;
 }
 
 int g16_h_prepare(uint32_t log_n, void* workspace, size_t workspace_bytes, void* stream,
@@ -403,16 +405,17 @@ int g16_h_prepare(uint32_t log_n, void* workspace, size_t workspace_bytes, void*
     }
     const size_t n = size_t(1) << log_n;
     uint8_t* ws = (uint8_t*)workspace;
-    size_t half = round_up((n / 2) * sizeof(Fr));
-    size_t full = round_up(n * sizeof(Fr));
-    c->tw_fwd = (Fr*)ws;
-    c->tw_inv = (Fr*)(ws + half);
-    c->coset = (Fr*)(ws + 2 * half);
-    c->scratch = (Fr*)(ws + 2 * half + full);
+    size_t half_tab = round_up((n / 2) * sizeof(g16::Tw29));
+    size_t full_tab = round_up(n * sizeof(g16::Tw29));
+    c->tw_fwd = (g16::Tw29*)ws;
+    c->tw_inv = (g16::Tw29*)(ws + half_tab);
+    c->coset = (g16::Tw29*)(ws + 2 * half_tab);
+    c->scratch = (Fr*)(ws + 2 * half_tab + full_tab);
     c->ws_begin = ws;
     c->ws_bytes = g16_h_workspace_bytes(log_n);
     domain_roots(log_n, &c->omega, &c->shift, &c->size_inv);
     c->omega_inv = g16::fr_inv(c->omega);
+    c->size_inv_entry = g16::tw29_entry(c->size_inv);
     c->n_batches = plan_batches(log_n, max_batch_k(), c->batch_k);
 
     hipStream_t s = (hipStream_t)stream;

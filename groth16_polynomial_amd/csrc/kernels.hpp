@@ -4,54 +4,63 @@
 // pairs indices that differ only in bit b.  Passes [s0, s0 + k) touch only bits
 // [s0, s0 + k), so they can run together on a "slice": the 2^k indices that agree on
 // all other bits (the NTT_CU page, "BATCHING" section).  A workgroup loads one or
-// more slices into LDS, runs the k passes with a barrier between them and writes the
+// more slices, runs the k passes with the data in registers and LDS and writes the
 // slices back, so a transform costs one HBM round trip per batch of passes.
 //
-// Two butterfly forms are used (both exact, so any schedule gives identical bits):
-//   DIT (Cooley-Tukey): (x_lo, x_hi) <- (x_lo + w x_hi, x_lo - w x_hi), passes in
-//       increasing bit order, bit-reversed input to natural output;
-//   DIF (Gentleman-Sande): (x_lo, x_hi) <- (x_lo + x_hi, (x_lo - x_hi) w), passes in
-//       decreasing bit order, natural input to bit-reversed output.
-// In both, the pass on bit b uses w = root^(j n / 2^(b+1)) with j = index mod 2^b, read
-// from a natural-order table of the root's first n/2 powers.
+// Every butterfly is the Cooley-Tukey form (x_lo, x_hi) <- (x_lo + w x_hi,
+// x_lo - w x_hi): the product output is small and normalized, so the only growth is the
+// limb-wise add or subtract of it, which keeps the 29-bit limb representation of
+// fr29.hpp within bounds for three passes between normalizations (the other butterfly,
+// (x_lo + x_hi, (x_lo - x_hi) w), adds two unnormalized values and doubles the bound
+// each pass).  Two pass orders are used, both exact, so any schedule gives the
+// same bits:
+//   forward order: bits 0, 1, ..., L-1; bit-reversed input to natural output; the pass
+//       on bit b uses w = root^((i mod 2^b) 2^(L-1-b));
+//   inverse order: bits L-1, ..., 1, 0; natural input to bit-reversed output; the pass
+//       on bit b uses w = root^(2^b bitrev_(L-1-b)(i >> (b+1))).
+// (The second splits x mod (X^(2m) - c) into x mod (X^m - sqrt c) and x mod (X^m +
+// sqrt c); with the roots visited in bit-reversed order it evaluates at every power of
+// the root and leaves the results in bit-reversed positions.)  Both read w from a
+// natural-order table of the root's first n/2 powers, i the lower index of the pair.
 //
 // Pipeline mapping (per vector; the pages fold the bit reversal into the first load,
-// here it disappears instead): the inverse transform runs as DIF on the natural-order
-// input, leaving coefficients in bit-reversed order; the coset shift and 1/n become one
-// multiply by a table S[p] = n^-1 s^bitrev(p) stored in bit-reversed order; the forward
-// transform runs as DIT on that bit-reversed vector and produces natural order.  The
-// lowest batch of passes of both transforms covers the same contiguous slices, so the
-// end of the inverse, the shift and the start of the forward transform share one
-// kernel and one HBM round trip.
+// here it disappears instead): the inverse transform runs in the inverse order on the
+// natural-order input with the powers of omega^-1, leaving coefficients in bit-reversed
+// order; the coset shift and 1/n become one multiply by a table S[p] = n^-1 s^bitrev(p)
+// stored in bit-reversed order; the forward transform runs in the forward order on that
+// bit-reversed vector and produces natural order.  The lowest batch of passes of both
+// transforms covers the same contiguous slices, so the end of the inverse, the shift
+// and the start of the forward transform share one kernel and one HBM round trip.
 #pragma once
 
-#include "fr.hpp"
+#include "fr29.hpp"
 
 namespace g16 {
 
 enum class Mode : int {
-    HeadBitrev = 0,  // load src[bitrev(i)] (optionally x kscale), DIT passes [0, k)
-    DitStrided = 1,  // DIT passes [s0, s0 + k) on slices strided by 2^s0
-    DifStrided = 2,  // DIF passes [s0 + k) down to s0 on slices strided by 2^s0
-    Fused = 3,       // contiguous slices: DIF passes k-1..0, x S[p], DIT passes 0..k-1
+    HeadBitrev = 0,  // load src[bitrev(i)] (optionally x kscale), forward passes [0, k)
+    FwdStrided = 1,  // forward-order passes [s0, s0 + k) on slices strided by 2^s0
+    InvStrided = 2,  // inverse-order passes s0 + k - 1 down to s0, slices strided by 2^s0
+    Fused = 3,       // contiguous slices: inverse passes k-1..0, x S[p], forward 0..k-1
 };
 
 struct BatchParams {
-    const Fr* src[3];    // per vector (blockIdx.y)
+    const Fr* src[3];     // per vector (blockIdx.y)
     Fr* dst[3];
-    const Fr* tw;        // twiddles of this batch's passes (Fused: the DIF table)
-    const Fr* tw_fwd;    // Fused only: the DIT table
-    const Fr* scale;     // Fused only: S[p]
-    const Fr* join_a;    // store epilogue H = A' B' - x (join kernels only)
+    const Tw29* tw;       // twiddles of this batch's passes (Fused: the inverse table)
+    const Tw29* tw_fwd;   // Fused only: the forward table
+    const Tw29* scale;    // Fused only: S[p]
+    const Fr* join_a;     // store epilogue H = A' B' - x (join kernels only)
     const Fr* join_b;
     Fr* h_mont;
     Fr* h_std;
-    Fr kscale;           // HeadBitrev: multiplier applied on load (inverse transform)
+    Tw29 kscale;          // HeadBitrev: multiplier applied on load (inverse transform)
     uint32_t log_n;
     uint32_t s0;
     uint32_t k;
-    uint32_t log_spw;    // log2 of slices per workgroup
+    uint32_t log_spw;     // log2 of slices per workgroup (radix-2 kernel)
     uint32_t use_kscale;
+    uint32_t n_vec;       // register-group kernel: number of vectors (grid = groups x n_vec)
 };
 
 __device__ __forceinline__ Fr ld_global(const Fr* p) {
@@ -70,24 +79,52 @@ __device__ __forceinline__ void st_global(Fr* p, const Fr& x) {
     q[1] = make_uint4(x.w[4], x.w[5], x.w[6], x.w[7]);
 }
 
-__device__ __forceinline__ Fr ld_lds(const Fr* p) {
-    const uint4* q = reinterpret_cast<const uint4*>(p);
-    uint4 lo = q[0];
-    uint4 hi = q[1];
-    Fr x;
-    x.w[0] = lo.x; x.w[1] = lo.y; x.w[2] = lo.z; x.w[3] = lo.w;
-    x.w[4] = hi.x; x.w[5] = hi.y; x.w[6] = hi.z; x.w[7] = hi.w;
-    return x;
-}
+__device__ __forceinline__ Fr ld_lds(const Fr* p) { return ld_global(p); }
+__device__ __forceinline__ void st_lds(Fr* p, const Fr& x) { st_global(p, x); }
 
-__device__ __forceinline__ void st_lds(Fr* p, const Fr& x) {
-    uint4* q = reinterpret_cast<uint4*>(p);
-    q[0] = make_uint4(x.w[0], x.w[1], x.w[2], x.w[3]);
-    q[1] = make_uint4(x.w[4], x.w[5], x.w[6], x.w[7]);
+// A table entry: five 16-byte vector loads.  The address goes through an opaque zero
+// held in a VGPR: an entry every lane of a wave needs would otherwise be read with
+// scalar loads into SGPRs, and the compiler lowers a signed 32 x 32-bit multiply-add
+// with a sign-extended SGPR operand as four instructions instead of one
+// v_mad_i64_i32.
+__device__ __forceinline__ Tw29 ld_tw(const Tw29* p) {
+    uint32_t z;
+    asm("v_mov_b32 %0, 0" : "=v"(z));
+    const uint4* q = reinterpret_cast<const uint4*>(p + z);
+    uint4 a = q[0], b = q[1], c = q[2], d = q[3], e = q[4];
+    Tw29 t;
+    t.w[0] = a.x; t.w[1] = a.y; t.w[2] = a.z; t.w[3] = a.w;
+    t.w[4] = b.x; t.w[5] = b.y; t.w[6] = b.z; t.w[7] = b.w;
+    t.w[8] = c.x; t.wp[0] = c.y; t.wp[1] = c.z; t.wp[2] = c.w;
+    t.wp[3] = d.x; t.wp[4] = d.y; t.wp[5] = d.z; t.wp[6] = d.w;
+    t.wp[7] = e.x; t.wp[8] = e.y; t.pad[0] = 0u; t.pad[1] = 0u;
+    return t;
 }
 
 __device__ __forceinline__ uint32_t bitrev_bits(uint32_t x, uint32_t bits) {
     return __builtin_bitreverse32(x) >> (32u - bits);  // bits in [1, 32]
+}
+
+// bit reversal over 0..31 bits (0 bits: 0)
+__device__ __forceinline__ uint32_t bitrev_w(uint32_t x, uint32_t bits) {
+    return bits ? (__builtin_bitreverse32(x) >> (32u - bits)) : 0u;
+}
+
+// Twiddle index of a forward-order pass on global bit s0 + t for the pair whose lower
+// element has column `low` (< 2^s0) and local index bits below t equal to jm.
+__device__ __forceinline__ uint32_t fwd_tw_index(uint32_t log_n, uint32_t s0, uint32_t t,
+                                                 uint32_t low, uint32_t jm) {
+    return (low + (jm << s0)) << (log_n - 1u - s0 - t);
+}
+
+// Twiddle index of an inverse-order pass on global bit b = s0 + t of a batch of k
+// passes, for the pair whose lower element has local bits above t equal to a and slice
+// row (global bits above the batch) equal to h: 2^b bitrev_(L-1-b)(i >> (b+1)) with
+// i >> (b+1) = a + h 2^(k-t-1).
+__device__ __forceinline__ uint32_t inv_tw_index(uint32_t log_n, uint32_t s0, uint32_t k,
+                                                 uint32_t t, uint32_t a, uint32_t h) {
+    const uint32_t hb = log_n - s0 - k;
+    return ((bitrev_w(a, k - t - 1u) << hb) + bitrev_w(h, hb)) << (s0 + t);
 }
 
 // The H epilogue: h_mont[i] = A'[i] B'[i] - x, h_std[i] = the same without the factor R.
@@ -97,16 +134,20 @@ __device__ __forceinline__ void store_h(const BatchParams& p, uint64_t i, const 
     st_global(p.h_std + i, fr_from_mont(h));
 }
 
-// One radix-2 pass over the workgroup's slices in LDS.
-//   bit t of the local index is flipped; the global bit is b = s0 + t;
-//   slice sl has low part low(sl) (global index bits below s0).
-template <bool DIF>
-__device__ __forceinline__ void lds_pass(Fr* sh, const Fr* tw, uint32_t log_n, uint32_t s0,
+// x w mod r, canonical, for a canonical x and a table entry (radix-2 kernel and
+// element-wise use).
+__device__ __forceinline__ Fr fr_mul_entry(const Fr& x, const Tw29& t) {
+    return fr29_canon(shoup_mul(fr29_from_fr(x), t));
+}
+
+// One radix-2 pass over the workgroup's slices in LDS (values canonical).
+//   bit t of the local index is flipped; the global bit is s0 + t; slice g0 + sl has
+//   column low = (g0 + sl) mod 2^s0 and row h = (g0 + sl) >> s0.
+template <bool INV>
+__device__ __forceinline__ void lds_pass(Fr* sh, const Tw29* tw, uint32_t log_n, uint32_t s0,
                                          uint32_t k, uint32_t t, uint32_t n_bfly,
-                                         uint32_t low_base, uint32_t strided) {
+                                         uint32_t g0) {
     const uint32_t half_k = 1u << (k - 1u);
-    const uint32_t b = s0 + t;
-    const uint32_t twshift = log_n - b - 1u;
     for (uint32_t f = threadIdx.x; f < n_bfly; f += blockDim.x) {
         uint32_t sl = f >> (k - 1u);
         uint32_t bf = f & (half_k - 1u);
@@ -116,23 +157,13 @@ __device__ __forceinline__ void lds_pass(Fr* sh, const Fr* tw, uint32_t log_n, u
         Fr* base = sh + ((size_t)sl << k);
         Fr u = ld_lds(base + lo);
         Fr v = ld_lds(base + hi);
-        // j = global index mod 2^b: the slice's low bits plus the local bits below t
-        uint32_t low = strided ? (low_base + sl) & ((1u << s0) - 1u) : 0u;
-        if (b == 0u) {
-            // the root^0 = 1 twiddle: no multiply
-            st_lds(base + lo, fr_add(u, v));
-            st_lds(base + hi, fr_sub(u, v));
-        } else {
-            Fr w = ld_global(tw + ((size_t)(low + (jm << s0)) << twshift));
-            if (DIF) {
-                st_lds(base + lo, fr_add(u, v));
-                st_lds(base + hi, fr_mul_tab(fr_sub(u, v), w));
-            } else {
-                Fr vw = fr_mul_tab(v, w);
-                st_lds(base + lo, fr_add(u, vw));
-                st_lds(base + hi, fr_sub(u, vw));
-            }
-        }
+        const uint32_t g = g0 + sl;
+        const uint32_t idx = INV ? inv_tw_index(log_n, s0, k, t, bf >> t, g >> s0)
+                                 : fwd_tw_index(log_n, s0, t, g & ((1u << s0) - 1u), jm);
+        // index 0 is the twiddle 1
+        Fr vw = idx == 0u ? v : fr_mul_entry(v, ld_tw(tw + idx));
+        st_lds(base + lo, fr_add(u, vw));
+        st_lds(base + hi, fr_sub(u, vw));
     }
     __syncthreads();
 }
@@ -151,25 +182,15 @@ __global__ void __launch_bounds__(256) ntt_batch_kernel(BatchParams p) {
     const uint32_t total = spw << k;
     const Fr* src = p.src[blockIdx.y];
     Fr* dst = p.dst[blockIdx.y];
-    // Workgroups are dispatched to the eight XCDs round-robin (workgroup i to XCD i mod 8),
-    // and each XCD has its own L2.  Renumber them so that each XCD takes one contiguous
-    // run of slice groups: neighbouring slices (strided batches: neighbouring columns,
-    // which share 128-byte lines of data and twiddles) and the same slice of all
-    // vectors (grid.y) then meet in one L2.
-    uint32_t wg = blockIdx.x;
-    if ((gridDim.x & 7u) == 0u) wg = (wg & 7u) * (gridDim.x >> 3) + (wg >> 3);
-    const uint32_t g0 = wg << p.log_spw;  // first slice of this workgroup
-    const bool strided = (M == Mode::DitStrided || M == Mode::DifStrided);
+    const uint32_t g0 = blockIdx.x << p.log_spw;  // first slice of this workgroup
+    const bool strided = (M == Mode::FwdStrided || M == Mode::InvStrided);
 
     // Global index of local element (sl, m).
     auto gindex = [&](uint32_t sl, uint32_t m) -> uint64_t {
-        if (strided) {
-            uint32_t g = g0 + sl;
-            uint64_t low = g & ((1u << s0) - 1u);
-            uint64_t high = g >> s0;
-            return low + (high << (s0 + k)) + ((uint64_t)m << s0);
-        }
-        return ((uint64_t)(g0 + sl) << k) + m;
+        uint32_t g = g0 + sl;
+        uint64_t low = g & ((1u << s0) - 1u);
+        uint64_t high = g >> s0;
+        return low + (high << (s0 + k)) + ((uint64_t)m << s0);
     };
 
     // ---- load: adjacent lanes take adjacent columns (strided) or elements (contiguous)
@@ -181,7 +202,7 @@ __global__ void __launch_bounds__(256) ntt_batch_kernel(BatchParams p) {
         Fr x;
         if (M == Mode::HeadBitrev) {
             x = ld_global(src + bitrev_bits((uint32_t)i, p.log_n));
-            if (p.use_kscale) x = fr_mul(x, p.kscale);
+            if (p.use_kscale) x = fr_mul_entry(x, p.kscale);
         } else {
             x = ld_global(src + i);
         }
@@ -190,23 +211,20 @@ __global__ void __launch_bounds__(256) ntt_batch_kernel(BatchParams p) {
     __syncthreads();
 
     const uint32_t n_bfly = spw << (k - 1u);
-    if (M == Mode::HeadBitrev || M == Mode::DitStrided) {
-        for (uint32_t t = 0; t < k; ++t)
-            lds_pass<false>(sh, p.tw, p.log_n, s0, k, t, n_bfly, g0, strided);
-    } else if (M == Mode::DifStrided) {
-        for (uint32_t t = k; t-- > 0;)
-            lds_pass<true>(sh, p.tw, p.log_n, s0, k, t, n_bfly, g0, strided);
+    if (M == Mode::HeadBitrev || M == Mode::FwdStrided) {
+        for (uint32_t t = 0; t < k; ++t) lds_pass<false>(sh, p.tw, p.log_n, s0, k, t, n_bfly, g0);
+    } else if (M == Mode::InvStrided) {
+        for (uint32_t t = k; t-- > 0;) lds_pass<true>(sh, p.tw, p.log_n, s0, k, t, n_bfly, g0);
     } else {  // Fused
-        for (uint32_t t = k; t-- > 0;)
-            lds_pass<true>(sh, p.tw, p.log_n, 0u, k, t, n_bfly, 0u, 0u);
+        for (uint32_t t = k; t-- > 0;) lds_pass<true>(sh, p.tw, p.log_n, 0u, k, t, n_bfly, g0);
         for (uint32_t e = threadIdx.x; e < total; e += blockDim.x) {
             uint32_t sl = e >> k, m = e & (slice_len - 1u);
             Fr* q = sh + ((size_t)sl << k) + m;
-            st_lds(q, fr_mul_tab(ld_lds(q), ld_global(p.scale + gindex(sl, m))));
+            st_lds(q, fr_mul_entry(ld_lds(q), ld_tw(p.scale + gindex(sl, m))));
         }
         __syncthreads();
         for (uint32_t t = 0; t < k; ++t)
-            lds_pass<false>(sh, p.tw_fwd, p.log_n, 0u, k, t, n_bfly, 0u, 0u);
+            lds_pass<false>(sh, p.tw_fwd, p.log_n, 0u, k, t, n_bfly, g0);
     }
 
     // ---- store

@@ -1,36 +1,39 @@
-// Radix-8 batch kernel: the k passes of a batch run in groups of up to three, each
-// group entirely in registers.
+// Register-group batch kernel: the k passes of a batch run in groups of up to GR
+// passes, each group entirely in registers, on the 29-bit limb representation.
 //
-// A thread owns eight elements of its slice for a group covering local index bits
+// A thread owns 2^GR elements of its slice for a group covering local index bits
 // [b0, b0 + r): the elements whose local index has the thread's value in every other
-// bit, r bits varying (for r < 3, 2^(3-r) such sets).  It runs the group's r passes on
-// them in registers and exchanges elements with the other threads through LDS between
-// groups.  The first group reads HBM directly and the last writes HBM directly, so a
-// batch of k passes costs ceil(k/3) - 1 LDS exchanges instead of k.
+// bit, r bits varying (for r < GR, 2^(GR-r) such sets).  It runs the group's r passes
+// on them in registers and exchanges elements with the other threads through LDS
+// before the next group.  A group that starts from LDS first normalizes the elements
+// that are "lo" in its first pass, which keeps every value within two passes of
+// normalized (fr29.hpp).  The first group reads HBM directly and the last
+// writes HBM directly, so a batch of k passes costs ceil(k/GR) - 1 LDS exchanges.
 //
-// LDS layout: four planes of 64-bit limb pairs (limbs 2p, 2p+1 of every element in
-// plane p), element e of slice sl at slot sl * SP + e + e/8.  The padding spreads the
-// stride-8 and block patterns of the low groups over the banks.
+// LDS layout: five planes (limb pairs 0-1, 2-3, 4-5, 6-7 as 64-bit words, limb 8 as a
+// 32-bit word).  Element e of slice sl sits at slot sl * 2^K + swz(e) (contiguous
+// batches) or swz(e) * spw + sl (strided batches, where adjacent lanes hold adjacent
+// slices), swz(e) = e ^ ((e >> 3) & 7): the XOR spreads the stride-8 pattern of the
+// lowest group over the banks without padding.
 #pragma once
 
 #include <type_traits>
 #include <utility>
 
-#include "fr.hpp"
+#include "fr29.hpp"
 
 namespace g16 {
 
 // K passes per batch in groups of GR (the last group may be shorter); each thread
-// holds E = 2^GR elements.
+// holds 2^GR elements; 2^(10-K) slices per workgroup (at most 36 KiB of LDS).
 template <int K, int GR>
 struct R8Geom {
     static constexpr int kE = 1 << GR;
     static constexpr int kThreadsPerSlice = 1 << (K - GR);
-    static constexpr int kSpw = (256 >> (K - GR)) > 0 ? (256 >> (K - GR)) : 1;  // slices / WG
+    static constexpr int kSpw = K >= 10 ? 1 : (1 << (10 - K));
     static constexpr int kThreads = kThreadsPerSlice * kSpw;
-    static constexpr int kSlotsPerSlice = (1 << K) + (1 << (K - 3)) + 4;
-    static constexpr int kPlane = kSlotsPerSlice * kSpw;                   // uint2 per plane
-    static constexpr int kLdsBytes = 4 * kPlane * 8;
+    static constexpr int kPlane = kSpw << K;                    // slots per plane
+    static constexpr int kLdsBytes = kPlane * 36;
     static constexpr int kGroups = (K + GR - 1) / GR;
     static constexpr int group_b0(int g) { return GR * g; }
     static constexpr int group_r(int g) { return (K - GR * g) < GR ? (K - GR * g) : GR; }
@@ -41,21 +44,23 @@ __device__ __forceinline__ uint32_t insert_bits(uint32_t c, uint32_t q, int b0, 
     return (c & ((1u << b0) - 1u)) | (q << b0) | ((c >> b0) << (b0 + r));
 }
 
-__device__ __forceinline__ uint32_t lds_slot(uint32_t e) { return e + (e >> 3); }
+__device__ __forceinline__ uint32_t lds_swz(uint32_t e) { return e ^ ((e >> 3) & 7u); }
 
-__device__ __forceinline__ void lds_put(uint2* lds, uint32_t plane, uint32_t slot, const Fr& x) {
-    lds[slot] = make_uint2(x.w[0], x.w[1]);
-    lds[plane + slot] = make_uint2(x.w[2], x.w[3]);
-    lds[2 * plane + slot] = make_uint2(x.w[4], x.w[5]);
-    lds[3 * plane + slot] = make_uint2(x.w[6], x.w[7]);
+__device__ __forceinline__ void lds_put(uint2* lds, uint32_t plane, uint32_t slot, const V29& x) {
+    lds[slot] = make_uint2(x.l[0], x.l[1]);
+    lds[plane + slot] = make_uint2(x.l[2], x.l[3]);
+    lds[2 * plane + slot] = make_uint2(x.l[4], x.l[5]);
+    lds[3 * plane + slot] = make_uint2(x.l[6], x.l[7]);
+    reinterpret_cast<uint32_t*>(lds + 4 * plane)[slot] = x.l[8];
 }
 
-__device__ __forceinline__ Fr lds_get(const uint2* lds, uint32_t plane, uint32_t slot) {
+__device__ __forceinline__ V29 lds_get(const uint2* lds, uint32_t plane, uint32_t slot) {
     uint2 a = lds[slot], b = lds[plane + slot], c = lds[2 * plane + slot],
           d = lds[3 * plane + slot];
-    Fr x;
-    x.w[0] = a.x; x.w[1] = a.y; x.w[2] = b.x; x.w[3] = b.y;
-    x.w[4] = c.x; x.w[5] = c.y; x.w[6] = d.x; x.w[7] = d.y;
+    V29 x;
+    x.l[0] = a.x; x.l[1] = a.y; x.l[2] = b.x; x.l[3] = b.y;
+    x.l[4] = c.x; x.l[5] = c.y; x.l[6] = d.x; x.l[7] = d.y;
+    x.l[8] = reinterpret_cast<const uint32_t*>(lds + 4 * plane)[slot];
     return x;
 }
 
@@ -70,50 +75,111 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// The R passes of one group on the set x[OFF .. OFF + 2^R) held in registers.
-//   DIT: passes u = 0 .. R-1 (increasing bit order); DIF: u = R-1 .. 0.
-//   Pass u flips local bit B0 + u (global bit B = s0 + B0 + u).  The butterfly of the
-//   pair (q, q + 2^u) uses root^(j n / 2^(B+1)), j = the lower element's global index
-//   mod 2^B = low + (((c mod 2^B0) + (q mod 2^u) 2^B0) << s0).
-template <int OFF, int R, int B0, bool DIF, bool CONTIG, int E>
-__device__ __forceinline__ void group_passes(Fr (&x)[E], uint32_t c, uint32_t low, uint32_t s0,
-                                             uint32_t log_n, const Fr* tw) {
+// Products computed together (interleaved multiply-add chains, shoup_mul_n): more
+// hides the dependent-multiply-add wait states, fewer keeps register pressure down.
+#ifndef G16_CHAINS
+#define G16_CHAINS 2
+#endif
+constexpr int kChains = G16_CHAINS;
+
+// One pass of a group on x[OFF .. OFF + 2^R): the 2^(R-1) butterflies x_lo, x_hi <-
+// x_lo + t, x_lo - t with t = w x_hi, the products computed together (shoup_mul_n).
+// Butterfly b has lower element q(b) (b with a zero inserted at bit u) and twiddle
+// index idx(b); TRIVIAL passes have twiddle 1 throughout and t = x_hi, which must then
+// be fresh (canonical or a product output).
+template <int OFF, int R, int U, bool TRIVIAL, int E, typename IdxF>
+__device__ __forceinline__ void ct_pass(V29 (&x)[E], const Tw29* tw, IdxF&& idx) {
+    constexpr int NB = 1 << (R - 1);
+    auto lower = [](int b) { return ((b >> U) << (U + 1)) | (b & ((1 << U) - 1)); };
+    V29 t[NB];
+    if constexpr (TRIVIAL) {
+        static_for<NB>([&](auto b_c) {
+            constexpr int b = decltype(b_c)::value;
+            t[b] = x[OFF + lower(b) + (1 << U)];
+        });
+    } else {
+        // products kChains at a time
+        constexpr int NC = NB < kChains ? NB : kChains;
+        static_for<NB / NC>([&](auto ch_c) {
+            constexpr int b0 = decltype(ch_c)::value * NC;
+            V29 h[NC], y[NC];
+            Tw29 w[NC];
+            static_for<NC>([&](auto j_c) {
+                constexpr int j = decltype(j_c)::value;
+                h[j] = x[OFF + lower(b0 + j) + (1 << U)];
+                w[j] = ld_tw(tw + idx(std::integral_constant<int, b0 + j>{}));
+            });
+            shoup_mul_n<NC>(h, w, y);
+            static_for<NC>([&](auto j_c) {
+                constexpr int j = decltype(j_c)::value;
+                t[b0 + j] = y[j];
+            });
+        });
+    }
+    static_for<NB>([&](auto b_c) {
+        constexpr int b = decltype(b_c)::value;
+        constexpr int q = ((b >> U) << (U + 1)) | (b & ((1 << U) - 1));
+        x[OFF + q + (1 << U)] = fr29_sub(x[OFF + q], t[b]);
+        x[OFF + q] = fr29_add(x[OFF + q], t[b]);
+    });
+}
+
+// The R forward-order passes of one group on x[OFF .. OFF + 2^R): pass u flips local
+// bit B0 + u (global bit s0 + B0 + u); the pair (q, q + 2^u) has local index bits below
+// the pass equal to (c mod 2^B0) + (q mod 2^u) 2^B0.  Global bit 0 has twiddle 1.
+template <int OFF, int R, int B0, bool NORM, int E>
+__device__ __forceinline__ void group_fwd(V29 (&x)[E], uint32_t c, uint32_t low, uint32_t s0,
+                                          uint32_t log_n, const Tw29* tw) {
     const uint32_t cl = c & ((1u << B0) - 1u);
+    if constexpr (NORM) {  // the lo elements of the first pass (u = 0): even q
+        static_for<(1 << (R - 1))>([&](auto b_c) {
+            constexpr int q = 2 * decltype(b_c)::value;
+            x[OFF + q] = fr29_normalize(x[OFF + q]);
+        });
+    }
+    static_for<R>([&](auto u_c) {
+        constexpr int u = decltype(u_c)::value;
+        const uint32_t t = (uint32_t)(B0 + u);
+        auto idx = [&](auto b_c) {
+            constexpr int m = decltype(b_c)::value & ((1 << u) - 1);
+            return fwd_tw_index(log_n, s0, t, low, cl + ((uint32_t)m << B0));
+        };
+        if constexpr (B0 + u == 0) {
+            if (s0 == 0u) ct_pass<OFF, R, u, true>(x, tw, idx);
+            else ct_pass<OFF, R, u, false>(x, tw, idx);
+        } else {
+            ct_pass<OFF, R, u, false>(x, tw, idx);
+        }
+    });
+}
+
+// The R inverse-order passes of one group, u = R-1 down to 0: the pair (q, q + 2^u) has
+// local bits above the pass a = (q >> (u+1)) + (c >> B0) 2^(R-1-u) and slice row h.
+// The pass on the transform's top bit (only in the top batch) has twiddle 1 throughout.
+template <int OFF, int R, int B0, int K, bool NORM, int E>
+__device__ __forceinline__ void group_inv(V29 (&x)[E], uint32_t c, uint32_t h, uint32_t s0,
+                                          uint32_t log_n, const Tw29* tw) {
+    const uint32_t ch = c >> B0;
+    if constexpr (NORM) {  // the lo elements of the first pass (u = R - 1): q < 2^(R-1)
+        static_for<(1 << (R - 1))>([&](auto b_c) {
+            constexpr int q = decltype(b_c)::value;
+            x[OFF + q] = fr29_normalize(x[OFF + q]);
+        });
+    }
     static_for<R>([&](auto uu_c) {
-        constexpr int uu = decltype(uu_c)::value;
-        constexpr int u = DIF ? (R - 1 - uu) : uu;
-        const uint32_t B = s0 + (uint32_t)(B0 + u);
-        F29 w[1 << u];
-        static_for<(1 << u)>([&](auto m_c) {
-            constexpr int m = decltype(m_c)::value;
-            const bool trivial = (B == 0u) || (CONTIG && B0 == 0 && u == 1 && m == 0);
-            if (!trivial) {
-                uint32_t j = low + ((cl + ((uint32_t)m << B0)) << s0);
-                w[m] = unpack29(ld_global(tw + ((size_t)j << (log_n - B - 1u))));
-            }
-        });
-        static_for<(1 << R)>([&](auto q_c) {
-            constexpr int q = decltype(q_c)::value;
-            if constexpr ((q & (1 << u)) == 0) {
-                constexpr int q2 = q + (1 << u);
-                constexpr int wi = q & ((1 << u) - 1);
-                // twiddle 1: bit 0 always; bit 1 of a contiguous slice for its first pair
-                const bool trivial = (B == 0u) || (CONTIG && B0 == 0 && u == 1 && wi == 0);
-                if (DIF) {
-                    // values in [0, 2r) before and after the pass
-                    Fr a = fr_reduce_2r(fr_add_lazy(x[OFF + q], x[OFF + q2]));
-                    Fr d = fr_sub_lazy(x[OFF + q], x[OFF + q2]);
-                    x[OFF + q2] = trivial ? fr_reduce_2r(d) : fr_mul29_lazy(d, w[wi]);
-                    x[OFF + q] = a;
-                } else {
-                    // values in [0, 4r) before and after the pass
-                    Fr uu0 = fr_reduce_2r(x[OFF + q]);
-                    Fr v = trivial ? fr_reduce_2r(x[OFF + q2]) : fr_mul29_lazy(x[OFF + q2], w[wi]);
-                    x[OFF + q2] = fr_sub_lazy(uu0, v);
-                    x[OFF + q] = fr_add_lazy(uu0, v);
-                }
-            }
-        });
+        constexpr int u = R - 1 - decltype(uu_c)::value;
+        const uint32_t t = (uint32_t)(B0 + u);
+        auto idx = [&](auto b_c) {
+            constexpr int m = decltype(b_c)::value >> u;  // = q >> (u + 1)
+            const uint32_t a = (uint32_t)m + (ch << (R - 1 - u));
+            return inv_tw_index(log_n, s0, (uint32_t)K, t, a, h);
+        };
+        if constexpr (B0 + u == K - 1) {
+            if (s0 + (uint32_t)K == log_n) ct_pass<OFF, R, u, true>(x, tw, idx);
+            else ct_pass<OFF, R, u, false>(x, tw, idx);
+        } else {
+            ct_pass<OFF, R, u, false>(x, tw, idx);
+        }
     });
 }
 
@@ -123,35 +189,40 @@ template <int K, int GR, Mode M, bool JOIN>
 __global__ void __launch_bounds__(256, 4) ntt_r8_kernel(BatchParams p) {
     using G = R8Geom<K, GR>;
     extern __shared__ uint2 lds[];
-    constexpr bool kStrided = (M == Mode::DitStrided || M == Mode::DifStrided);
+    constexpr bool kStrided = (M == Mode::FwdStrided || M == Mode::InvStrided);
     constexpr int NG = G::kGroups;
 
     const uint32_t s0 = p.s0;
     const uint32_t L = p.log_n;
-    const Fr* src = p.src[blockIdx.y];
-    Fr* dst = p.dst[blockIdx.y];
-
-    // XCD-aware renumbering (see ntt_batch_kernel)
-    uint32_t wg = blockIdx.x;
-    if ((gridDim.x & 7u) == 0u) wg = (wg & 7u) * (gridDim.x >> 3) + (wg >> 3);
+    // Workgroups are dispatched to the eight XCDs round-robin in linear order and each XCD
+    // has its own L2.  The grid is one-dimensional (slice groups x vectors); renumber it so
+    // that each XCD takes one contiguous run of slice groups and, within it, the vectors
+    // of a slice group one after another: they use the same twiddle and coset entries,
+    // which the later ones then find in that XCD's L2.
+    const uint32_t nv = p.n_vec;
+    uint32_t lin = blockIdx.x;
+    if ((gridDim.x & 7u) == 0u) lin = (lin & 7u) * (gridDim.x >> 3) + (lin >> 3);
+    const uint32_t wg = lin / nv;
+    const uint32_t vec = lin - wg * nv;
+    const Fr* src = p.src[vec];
+    Fr* dst = p.dst[vec];
     const uint32_t tid = threadIdx.x;
     // strided: adjacent lanes take adjacent columns; contiguous: one slice per run of lanes
     const uint32_t sl = kStrided ? tid % G::kSpw : tid / G::kThreadsPerSlice;
     const uint32_t t = kStrided ? tid / G::kSpw : tid % G::kThreadsPerSlice;
     const uint32_t g = wg * G::kSpw + sl;  // global slice number
-    const uint32_t low = kStrided ? (g & ((1u << s0) - 1u)) : 0u;
-    const uint64_t slice_base =
-        kStrided ? (uint64_t)low + ((uint64_t)(g >> s0) << (s0 + K)) : ((uint64_t)g << K);
-    const uint32_t estride_log = kStrided ? s0 : 0u;
-    const uint32_t lds_base = sl * G::kSlotsPerSlice;
+    const uint32_t low = g & ((1u << s0) - 1u);
+    const uint32_t row = g >> s0;
+    const uint64_t slice_base = (uint64_t)low + ((uint64_t)row << (s0 + K));
 
-    auto gidx = [&](uint32_t e) -> uint64_t {
-        return slice_base + ((uint64_t)e << estride_log);
+    auto gidx = [&](uint32_t e) -> uint64_t { return slice_base + ((uint64_t)e << s0); };
+    auto slot = [&](uint32_t e) -> uint32_t {
+        return kStrided ? lds_swz(e) * G::kSpw + sl : sl * (1u << K) + lds_swz(e);
     };
 
-    Fr x[G::kE];
+    V29 x[G::kE];
 
-    // Visits the elements of group GI: f(index into x, local element index e, set c).
+    // Visits the elements of group GI: f(index into x, local element index e).
     auto for_group = [&](auto gi_c, auto&& f) {
         constexpr int gi = decltype(gi_c)::value;
         constexpr int b0 = G::group_b0(gi), r = G::group_r(gi);
@@ -170,10 +241,10 @@ __global__ void __launch_bounds__(256, 4) ntt_r8_kernel(BatchParams p) {
             constexpr int xi = decltype(xi_c)::value;
             const uint64_t i = gidx(e);
             if constexpr (M == Mode::HeadBitrev) {
-                Fr v = ld_global(src + bitrev_bits((uint32_t)i, L));
-                x[xi] = p.use_kscale ? fr_mul(v, p.kscale) : v;
+                V29 v = fr29_from_fr(ld_global(src + bitrev_bits((uint32_t)i, L)));
+                x[xi] = p.use_kscale ? shoup_mul(v, p.kscale) : v;
             } else {
-                x[xi] = ld_global(src + i);
+                x[xi] = fr29_from_fr(ld_global(src + i));
             }
         });
     };
@@ -181,7 +252,7 @@ __global__ void __launch_bounds__(256, 4) ntt_r8_kernel(BatchParams p) {
         for_group(gi_c, [&](auto xi_c, uint32_t e) {
             constexpr int xi = decltype(xi_c)::value;
             const uint64_t i = gidx(e);
-            const Fr v = fr_canon_4r(x[xi]);
+            const Fr v = fr29_canon(x[xi]);
             if constexpr (JOIN) store_h(p, i, v);
             else st_global(dst + i, v);
         });
@@ -189,38 +260,51 @@ __global__ void __launch_bounds__(256, 4) ntt_r8_kernel(BatchParams p) {
     auto lds_write = [&](auto gi_c) {
         for_group(gi_c, [&](auto xi_c, uint32_t e) {
             constexpr int xi = decltype(xi_c)::value;
-            lds_put(lds, G::kPlane, lds_base + lds_slot(e), x[xi]);
+            lds_put(lds, G::kPlane, slot(e), x[xi]);
         });
     };
     auto lds_read = [&](auto gi_c) {
         for_group(gi_c, [&](auto xi_c, uint32_t e) {
             constexpr int xi = decltype(xi_c)::value;
-            x[xi] = lds_get(lds, G::kPlane, lds_base + lds_slot(e));
+            x[xi] = lds_get(lds, G::kPlane, slot(e));
         });
     };
-    auto passes = [&](auto gi_c, auto dif_c, const Fr* tw, uint32_t ls0, uint32_t llow) {
+    // passes of group GI in the forward or inverse order; FRESH: the elements come
+    // straight from HBM or from a product (no normalization needed)
+    auto passes = [&](auto gi_c, auto inv_c, auto fresh_c, const Tw29* tw, uint32_t ls0,
+                      uint32_t llow, uint32_t lrow) {
         constexpr int gi = decltype(gi_c)::value;
-        constexpr bool dif = decltype(dif_c)::value;
+        constexpr bool inv = decltype(inv_c)::value;
+        constexpr bool norm = !decltype(fresh_c)::value;
         constexpr int b0 = G::group_b0(gi), r = G::group_r(gi);
         constexpr int nsets = 1 << (GR - r);
         static_for<nsets>([&](auto s_c) {
             constexpr int s = decltype(s_c)::value;
-            group_passes<s * (1 << r), r, b0, dif, !kStrided, G::kE>(x, t * nsets + s, llow,
-                                                                     ls0, L, tw);
+            if constexpr (inv)
+                group_inv<s * (1 << r), r, b0, K, norm, G::kE>(x, t * nsets + s, lrow, ls0, L,
+                                                                tw);
+            else
+                group_fwd<s * (1 << r), r, b0, norm, G::kE>(x, t * nsets + s, llow, ls0, L, tw);
         });
     };
-    using DIT = std::false_type;
-    using DIF = std::true_type;
+    using FWD = std::false_type;
+    using INV = std::true_type;
+    using FRESH = std::true_type;
+    using OLD = std::false_type;
 
-    // One barrier after every LDS write: in each group every slot is read and then
-    // rewritten by the one thread that owns it, so the only ordering needed is that a
-    // group's writes land before the next group's reads.
-    if constexpr (M == Mode::DitStrided || M == Mode::HeadBitrev) {
+    // One barrier after every LDS write: a group reads and rewrites the same slots, all
+    // owned by the one thread, so the only ordering needed is that a group's writes land
+    // before the next group's reads.
+    if constexpr (M == Mode::FwdStrided || M == Mode::HeadBitrev) {
         static_for<NG>([&](auto gi_c) {
             constexpr int gi = decltype(gi_c)::value;
-            if constexpr (gi == 0) load_global(gi_c);
-            else lds_read(gi_c);
-            passes(gi_c, DIT{}, p.tw, s0, low);
+            if constexpr (gi == 0) {
+                load_global(gi_c);
+                passes(gi_c, FWD{}, FRESH{}, p.tw, s0, low, row);
+            } else {
+                lds_read(gi_c);
+                passes(gi_c, FWD{}, OLD{}, p.tw, s0, low, row);
+            }
             if constexpr (gi == NG - 1) {
                 store_global(gi_c);
             } else {
@@ -228,13 +312,17 @@ __global__ void __launch_bounds__(256, 4) ntt_r8_kernel(BatchParams p) {
                 __syncthreads();
             }
         });
-    } else if constexpr (M == Mode::DifStrided) {
+    } else if constexpr (M == Mode::InvStrided) {
         static_for<NG>([&](auto step_c) {
             constexpr int gi = NG - 1 - decltype(step_c)::value;
             using GI = std::integral_constant<int, gi>;
-            if constexpr (gi == NG - 1) load_global(GI{});
-            else lds_read(GI{});
-            passes(GI{}, DIF{}, p.tw, s0, low);
+            if constexpr (gi == NG - 1) {
+                load_global(GI{});
+                passes(GI{}, INV{}, FRESH{}, p.tw, s0, low, row);
+            } else {
+                lds_read(GI{});
+                passes(GI{}, INV{}, OLD{}, p.tw, s0, low, row);
+            }
             if constexpr (gi == 0) {
                 store_global(GI{});
             } else {
@@ -242,27 +330,51 @@ __global__ void __launch_bounds__(256, 4) ntt_r8_kernel(BatchParams p) {
                 __syncthreads();
             }
         });
-    } else {  // Fused: DIF groups high to low, coset multiply, DIT groups low to high
+    } else {  // Fused: inverse groups high to low, coset multiply, forward groups low to high
         static_for<NG>([&](auto step_c) {
             constexpr int gi = NG - 1 - decltype(step_c)::value;
             using GI = std::integral_constant<int, gi>;
-            if constexpr (gi == NG - 1) load_global(GI{});
-            else lds_read(GI{});
-            passes(GI{}, DIF{}, p.tw, 0u, 0u);
+            if constexpr (gi == NG - 1) {
+                load_global(GI{});
+                passes(GI{}, INV{}, FRESH{}, p.tw, 0u, 0u, g);
+            } else {
+                lds_read(GI{});
+                passes(GI{}, INV{}, OLD{}, p.tw, 0u, 0u, g);
+            }
             if constexpr (gi > 0) {
                 lds_write(GI{});
                 __syncthreads();
             }
         });
         // group 0 stays in registers: the coset multiply between the two transforms
+        uint32_t ce[G::kE];
         for_group(std::integral_constant<int, 0>{}, [&](auto xi_c, uint32_t e) {
-            constexpr int xi = decltype(xi_c)::value;
-            x[xi] = fr_mul29_lazy(x[xi], unpack29(ld_global(p.scale + gidx(e))));
+            ce[decltype(xi_c)::value] = e;
+        });
+        constexpr int NC = G::kE < kChains ? G::kE : kChains;
+        static_for<G::kE / NC>([&](auto ch_c) {
+            constexpr int i0 = NC * decltype(ch_c)::value;
+            V29 h[NC], y[NC];
+            Tw29 w[NC];
+            static_for<NC>([&](auto j_c) {
+                constexpr int j = decltype(j_c)::value;
+                h[j] = x[i0 + j];
+                w[j] = ld_tw(p.scale + gidx(ce[i0 + j]));
+            });
+            shoup_mul_n<NC>(h, w, y);
+            static_for<NC>([&](auto j_c) {
+                constexpr int j = decltype(j_c)::value;
+                x[i0 + j] = y[j];
+            });
         });
         static_for<NG>([&](auto gi_c) {
             constexpr int gi = decltype(gi_c)::value;
-            if constexpr (gi > 0) lds_read(gi_c);
-            passes(gi_c, DIT{}, p.tw_fwd, 0u, 0u);
+            if constexpr (gi == 0) {
+                passes(gi_c, FWD{}, FRESH{}, p.tw_fwd, 0u, 0u, g);  // coset products
+            } else {
+                lds_read(gi_c);
+                passes(gi_c, FWD{}, OLD{}, p.tw_fwd, 0u, 0u, g);
+            }
             if constexpr (gi == NG - 1) {
                 store_global(gi_c);
             } else {

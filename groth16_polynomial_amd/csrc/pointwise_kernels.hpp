@@ -31,11 +31,21 @@ __global__ void __launch_bounds__(256) elementwise_kernel(const Fr* a, const Fr*
     }
 }
 
-// Table builders.  Each thread raises the base to its own exponent (prepare time only).
-// Entries are stored in the 2^261 form the table products expect (fr_mul_tab).
+// Table builders.  Each thread raises the base to its own exponent (prepare time only)
+// and stores the entry the table products take (fr29.hpp: the plain value and its
+// Shoup companion floor(w 2^261 / r)).
 //   kind 0: T[j] = base^j                         (twiddles, j < count)
 //   kind 1: T[p] = factor * base^bitrev_L(p)      (coset table, p < count = 2^L)
-__global__ void __launch_bounds__(256) table_kernel(Fr* out, Fr base, Fr factor,
+__device__ __forceinline__ void st_tw(Tw29* p, const Tw29& t) {
+    uint4* q = reinterpret_cast<uint4*>(p);
+    q[0] = make_uint4(t.w[0], t.w[1], t.w[2], t.w[3]);
+    q[1] = make_uint4(t.w[4], t.w[5], t.w[6], t.w[7]);
+    q[2] = make_uint4(t.w[8], t.wp[0], t.wp[1], t.wp[2]);
+    q[3] = make_uint4(t.wp[3], t.wp[4], t.wp[5], t.wp[6]);
+    q[4] = make_uint4(t.wp[7], t.wp[8], 0u, 0u);
+}
+
+__global__ void __launch_bounds__(256) table_kernel(Tw29* out, Fr base, Fr factor,
                                                     uint64_t count, uint32_t log_n, int kind) {
     for (uint64_t j = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; j < count;
          j += (uint64_t)gridDim.x * blockDim.x) {
@@ -46,7 +56,7 @@ __global__ void __launch_bounds__(256) table_kernel(Fr* out, Fr base, Fr factor,
             uint64_t e = bitrev_bits((uint32_t)j, log_n);
             v = fr_mul(factor, fr_pow_u64(base, e));
         }
-        st_global(out + j, fr_mul(v, fr_c261()));
+        st_tw(out + j, tw29_entry(v));
     }
 }
 

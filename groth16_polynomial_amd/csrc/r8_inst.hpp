@@ -9,18 +9,20 @@ template <int K, Mode M, bool JOIN>
 hipError_t launch_r8(const BatchParams& p, uint32_t n_vec, hipStream_t stream) {
     using G = R8Geom<K, kR8Group>;
     const uint64_t groups = (1ull << (p.log_n - K)) / G::kSpw;
-    hipLaunchKernelGGL((ntt_r8_kernel<K, kR8Group, M, JOIN>), dim3((uint32_t)groups, n_vec, 1),
-                       dim3(G::kThreads), G::kLdsBytes, stream, p);
+    BatchParams q = p;
+    q.n_vec = n_vec;
+    hipLaunchKernelGGL((ntt_r8_kernel<K, kR8Group, M, JOIN>), dim3((uint32_t)(groups * n_vec)),
+                       dim3(G::kThreads), G::kLdsBytes, stream, q);
     return hipGetLastError();
 }
 
 template hipError_t launch_r8<G16_R8_K, Mode::HeadBitrev, false>(const BatchParams&, uint32_t,
                                                                  hipStream_t);
-template hipError_t launch_r8<G16_R8_K, Mode::DitStrided, false>(const BatchParams&, uint32_t,
+template hipError_t launch_r8<G16_R8_K, Mode::FwdStrided, false>(const BatchParams&, uint32_t,
                                                                  hipStream_t);
-template hipError_t launch_r8<G16_R8_K, Mode::DitStrided, true>(const BatchParams&, uint32_t,
+template hipError_t launch_r8<G16_R8_K, Mode::FwdStrided, true>(const BatchParams&, uint32_t,
                                                                 hipStream_t);
-template hipError_t launch_r8<G16_R8_K, Mode::DifStrided, false>(const BatchParams&, uint32_t,
+template hipError_t launch_r8<G16_R8_K, Mode::InvStrided, false>(const BatchParams&, uint32_t,
                                                                  hipStream_t);
 template hipError_t launch_r8<G16_R8_K, Mode::Fused, false>(const BatchParams&, uint32_t,
                                                             hipStream_t);

@@ -31,14 +31,8 @@ int main() {
         Fr x = parse(a), y = parse(b), z;
         if (op == "mul") z = g16::fr_mul(x, y);
         else if (op == "add") z = g16::fr_add(x, y);
-        else if (op == "mul29") z = g16::fr_mul_tab(x, y);
-        else if (op == "mul29lazy") z = g16::fr_mul29_lazy(x, g16::unpack29(y));
-        else if (op == "red2r") z = g16::fr_reduce_2r(x);
-        else if (op == "canon4r") z = g16::fr_canon_4r(x);
-        else if (op == "addlazy") z = g16::fr_add_lazy(x, y);
-        else if (op == "sublazy") z = g16::fr_sub_lazy(x, y);
-        else if (op == "unpack29") z = g16::pack29(g16::unpack29(x));
         else if (op == "sub") z = g16::fr_sub(x, y);
+        else if (op == "c261") z = g16::fr_c261();
         else if (op == "tomont") z = g16::fr_to_mont(x);
         else if (op == "frommont") z = g16::fr_from_mont(x);
         else if (op == "pow") z = g16::fr_pow_u64(x, ((uint64_t)y.w[1] << 32) | y.w[0]);

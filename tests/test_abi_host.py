@@ -48,9 +48,8 @@ def test_workspace_bytes(lib):
     assert binding.workspace_bytes(28) == 0
     for L in (1, 2, 12, 20, 27):
         n = 1 << L
-        half = -(-n // 2 * 32 // 256) * 256
-        full = -(-n * 32 // 256) * 256
-        assert binding.workspace_bytes(L) == 2 * half + 4 * full
+        rnd = lambda x: -(-x // 256) * 256
+        assert binding.workspace_bytes(L) == 2 * rnd(n // 2 * 80) + rnd(n * 80) + 3 * rnd(n * 32)
 
 
 def test_batch_plan_matches_page(lib):

@@ -1,0 +1,164 @@
+"""The library's 29-bit digit layer (fr29.hpp) compiled for the host and checked against
+Python integers: the table entry (w, floor(w 2^261 / r)) in balanced digits, the product
+by an entry for any 32-bit digits (both extremes of both signs), the carry-save
+normalization, the digit-wise subtraction and the final reduction to canonical form."""
+import os
+import random
+import subprocess
+
+import pytest
+
+from groth16_polynomial_amd import synth
+
+R = synth.R_MODULUS
+RR = 1 << 256
+M = (1 << 29) - 1
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+
+
+@pytest.fixture(scope="module")
+def driver(tmp_path_factory):
+    exe = str(tmp_path_factory.mktemp("fr29host") / "fr29_host_driver")
+    cmd = ["/opt/rocm/bin/hipcc", "--offload-host-only", "-O2", "-std=c++17",
+           "-I", os.path.join(ROOT, "groth16_polynomial_amd", "csrc"),
+           "-o", exe, os.path.join(HERE, "fr29_host_driver.cpp")]
+    subprocess.check_call(cmd, stderr=subprocess.DEVNULL)
+    return exe
+
+
+def fmt(op, args):
+    out = [op]
+    for kind, v in args:
+        out.append("%x" % v if kind == "hex" else "%d" % v)
+    return " ".join(out) + "\n"
+
+
+def run(exe, lines):
+    inp = "".join(fmt(op, args) for op, args in lines)
+    out = subprocess.run([exe], input=inp, capture_output=True, text=True, check=True).stdout
+    return out.splitlines()
+
+
+def digits(line):
+    return [int(v) for v in line.split()]
+
+
+def D(ls):
+    return [("dec", v) for v in ls]
+
+
+def H(v):
+    return [("hex", v)]
+
+
+def split(x):
+    return [(x >> (29 * k)) & M for k in range(8)] + [x >> 232]
+
+
+def val(ls):
+    return sum(v << (29 * k) for k, v in enumerate(ls))
+
+
+def mont(x):
+    return x * RR % R
+
+
+EDGE = [1, 2, R - 1, R - 2, RR % R, (R - 1) // 2, 2**253, 2**29, 2**29 - 1, 5]
+XMAX = 2**31 - 1              # any 32-bit digit is an admissible product input
+
+
+def test_split_is_exact(driver):
+    rng = random.Random(1)
+    xs = [0] + EDGE + [rng.randrange(R) for _ in range(300)]
+    got = run(driver, [("split", H(x)) for x in xs])
+    for x, line in zip(xs, got):
+        assert digits(line) == split(x)
+
+
+def test_table_entry_balanced(driver):
+    rng = random.Random(2)
+    ws = EDGE + [rng.randrange(1, R) for _ in range(500)]
+    got = run(driver, [("entry", H(mont(w))) for w in ws])
+    for w, line in zip(ws, got):
+        d = digits(line)
+        assert val(d[:9]) == w and val(d[9:]) == (w << 261) // R
+        assert all(-2**28 <= v < 2**28 for v in d[:8] + d[9:17])
+        assert 0 <= d[8] < 2**23 and -2**28 <= d[17] <= 2**29
+
+
+def test_shoup_product_bounds(driver):
+    rng = random.Random(3)
+    cases = []
+    for t in range(4000):
+        w = EDGE[t % len(EDGE)] if t < 60 else rng.randrange(1, R)
+        kind = t % 5
+        if kind == 0:
+            x = [XMAX] * 9
+        elif kind == 1:
+            x = [-XMAX - 1] * 9
+        elif kind == 2:
+            x = [rng.randrange(-XMAX, XMAX + 1) for _ in range(9)]
+        elif kind == 3:
+            x = split(rng.randrange(R))
+        else:
+            x = [rng.choice([0, XMAX, -XMAX, M, -M, 2**29]) for _ in range(9)]
+        cases.append((x, w))
+    got = run(driver, [("shoup", D(x) + H(mont(w))) for x, w in cases])
+    for (x, w), line in zip(cases, got):
+        y = digits(line)
+        assert all(0 <= v <= M for v in y[:8]) and -2**25 < y[8] < 2**25
+        assert val(y) % R == val(x) * w % R
+        assert -7 * R < val(y) < 9 * R
+
+
+def test_shoup_pair_matches_single(driver):
+    rng = random.Random(6)
+    lines, want = [], []
+    for _ in range(500):
+        x0 = [rng.randrange(-XMAX, XMAX + 1) for _ in range(9)]
+        x1 = [rng.randrange(-XMAX, XMAX + 1) for _ in range(9)]
+        w0, w1 = rng.randrange(1, R), rng.randrange(1, R)
+        lines.append(("shoup2", D(x0) + D(x1) + H(mont(w0)) + H(mont(w1))))
+        lines.append(("shoup", D(x0) + H(mont(w0))))
+        lines.append(("shoup", D(x1) + H(mont(w1))))
+    got = run(driver, lines)
+    for i in range(0, len(got), 3):
+        pair = digits(got[i])
+        assert pair[:9] == digits(got[i + 1]) and pair[9:] == digits(got[i + 2])
+
+
+def test_normalize_and_sub(driver):
+    rng = random.Random(4)
+    cases = [[rng.randrange(-2**31, 2**31) for _ in range(8)] + [rng.randrange(-2**30, 2**30)]
+             for _ in range(500)]
+    got = run(driver, [("norm", D(x)) for x in cases])
+    for x, line in zip(cases, got):
+        y = digits(line)
+        assert val(y) == val(x)
+        assert all(-4 <= v < 2**29 + 3 for v in y[:8])
+    subs = []
+    for _ in range(500):
+        a = [rng.randrange(-3 * 2**29, 3 * 2**29) for _ in range(9)]
+        b = [rng.randrange(0, 2**29) for _ in range(9)]
+        subs.append((a, b))
+    got = run(driver, [("sub", D(a) + D(b)) for a, b in subs])
+    for (a, b), line in zip(subs, got):
+        assert val(digits(line)) == val(a) - val(b)
+
+
+def test_canonical_reduction(driver):
+    rng = random.Random(5)
+    cases = [[0] * 9, split(R), split(R - 1), split(2 * R), split(2 * R - 1), split(3 * R)]
+    for _ in range(2000):
+        cases.append([rng.randrange(-2**31, 2**31) for _ in range(8)] +
+                     [rng.randrange(-2**30, 2**30)])
+    for _ in range(500):
+        cases.append(split(rng.randrange(2**261)))
+    for m in range(0, 64):
+        cases.append(split(m * R))
+        cases.append([-v for v in split(m * R)])
+        cases.append([-v for v in split(m * R + 1)])
+    got = run(driver, [("canon", D(x)) for x in cases])
+    for x, line in zip(cases, got):
+        assert int(line, 16) == val(x) % R

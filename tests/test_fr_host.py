@@ -65,43 +65,6 @@ def test_conversions_pow_inv(driver):
     assert got == [pow(x, -1, R) * RR % R for x, _ in cases]
 
 
-def test_table_product_radix_2_261(driver):
-    """fr_mul_tab: the nine-limb product with Montgomery radix 2^261, x * w * 2^-261."""
-    rng = random.Random(9)
-    xs = EDGE + [rng.randrange(R) for _ in range(3000)]
-    ws = list(reversed(EDGE)) + [rng.randrange(R) for _ in range(3000)]
-    inv261 = pow(1 << 261, -1, R)
-    got = run(driver, [("mul29", x, w) for x, w in zip(xs, ws)])
-    assert got == [x * w * inv261 % R for x, w in zip(xs, ws)]
-    # the 2^261-form table entry w * 2^261 turns it into the ordinary product form
-    got = run(driver, [("mul29", x, w * (1 << 261) % R) for x, w in zip(xs, ws)])
-    assert got == [x * w % R for x, w in zip(xs, ws)]
-    # limb repacking is the identity on 256-bit values
-    vals = [rng.randrange(1 << 256) for _ in range(200)] + [0, (1 << 256) - 1]
-    assert run(driver, [("unpack29", v, 0) for v in vals]) == vals
-
-
-def test_lazy_range_helpers(driver):
-    """The in-kernel lazy forms: [0, 4r) -> [0, 2r) and -> canonical, a + b and a + 2r - b
-    without reduction, and the unreduced 2^261 product (below 2r for any 256-bit x)."""
-    rng = random.Random(10)
-    x4 = [0, 1, R - 1, R, 2 * R - 1, 2 * R, 3 * R + 5, 4 * R - 1] + \
-        [rng.randrange(4 * R) for _ in range(2000)]
-    got = run(driver, [("red2r", x, 0) for x in x4] + [("canon4r", x, 0) for x in x4])
-    n = len(x4)
-    assert got[:n] == [x - 2 * R if x >= 2 * R else x for x in x4]
-    assert got[n:] == [x % R for x in x4]
-    a2 = [rng.randrange(2 * R) for _ in range(2000)] + [0, 2 * R - 1]
-    b2 = [rng.randrange(2 * R + 1) for _ in range(2000)] + [2 * R, 0]
-    got = run(driver, [("addlazy", a, b) for a, b in zip(a2, b2)] +
-              [("sublazy", a, b) for a, b in zip(a2, b2)])
-    m = len(a2)
-    assert got[:m] == [a + b for a, b in zip(a2, b2)]
-    assert got[m:] == [a + 2 * R - b for a, b in zip(a2, b2)]
-    assert all(0 <= v < 4 * R for v in got[m:])
-    xs = [rng.randrange(1 << 256) for _ in range(2000)] + [(1 << 256) - 1]
-    ws = [rng.randrange(R) for _ in range(len(xs) - 1)] + [R - 1]
-    inv261 = pow(1 << 261, -1, R)
-    got = run(driver, [("mul29lazy", x, w) for x, w in zip(xs, ws)])
-    assert [v % R for v in got] == [x * w * inv261 % R for x, w in zip(xs, ws)]
-    assert all(v < 2 * R for v in got)
+def test_constant_2_261(driver):
+    """2^261 mod r, the constant the table builder multiplies by."""
+    assert run(driver, [("c261", 0, 0)]) == [(1 << 261) % R]
