@@ -34,8 +34,8 @@ struct g16_ctx {
     uint32_t magic;
     uint32_t log_n;
     int device;
-    g16::Tw29* tw_fwd;  // omega^j, j < n/2
-    g16::Tw29* tw_inv;  // omega^-j, j < n/2
+    g16::Tw29* tw_fwd;  // powers of omega by level (n - 1 entries)
+    g16::Tw29* tw_inv;  // powers of omega^-1 by level, bit-reversed within each level
     g16::Tw29* coset;   // n^-1 s^bitrev(p), p < n
     Fr* scratch;  // three n-element vectors
     const uint8_t* ws_begin;
@@ -125,7 +125,7 @@ bool try_r8(const g16::BatchParams& p, uint32_t n_vec, hipStream_t stream, int* 
     switch (k) {
 #define G16_R8_CASE(KK)                                                        \
         case KK:                                                               \
-            if (!fits(g16::R8Geom<KK, g16::kR8Group>::kSpw)) return false;      \
+            if (!fits(g16::R8GeomFor<KK, g16::kR8Group, M>::kSpw)) return false; \
             e = g16::launch_r8<KK, M, J>(p, n_vec, stream);                     \
             *rc = e == hipSuccess ? G16_OK : G16_EHIP;                          \
             return true;
@@ -185,8 +185,9 @@ int run_ntt(g16_ctx* c, const void* in, void* out, void* stream, bool inverse) {
     hipStream_t s = (hipStream_t)stream;
     Fr* scr = c->scratch;
     g16::BatchParams p = base_params(c);
-    p.tw = inverse ? c->tw_inv : c->tw_fwd;
-    p.use_kscale = inverse ? 1u : 0u;
+    // both directions run the forward passes (the inverse on x[-k mod n], see head_index)
+    p.tw = c->tw_fwd;
+    p.head_inverse = inverse ? 1u : 0u;
     p.kscale = c->size_inv_entry;
     p.s0 = 0;
     p.k = c->batch_k[0];
@@ -382,10 +383,9 @@ int g16_batch_plan(uint32_t log_n, uint32_t kmax, uint32_t* ks, uint32_t cap) {
 size_t g16_h_workspace_bytes(uint32_t log_n) {
     if (log_n < G16_MIN_LOG_N || log_n > G16_MAX_LOG_N) return 0;
     size_t n = size_t(1) << log_n;
-    size_t half_tab = round_up((n / 2) * sizeof(g16::Tw29));
-    size_t full_tab = round_up(n * sizeof(g16::Tw29));
+    size_t tab = round_up(n * sizeof(g16::Tw29));
     size_t full = round_up(n * sizeof(Fr));
-    return 2 * half_tab + full_tab + 3 * full;
+    return 3 * tab + 3 * full;
 }
 
 int g16_h_prepare(uint32_t log_n, void* workspace, size_t workspace_bytes, void* stream,
@@ -405,12 +405,11 @@ int g16_h_prepare(uint32_t log_n, void* workspace, size_t workspace_bytes, void*
     }
     const size_t n = size_t(1) << log_n;
     uint8_t* ws = (uint8_t*)workspace;
-    size_t half_tab = round_up((n / 2) * sizeof(g16::Tw29));
-    size_t full_tab = round_up(n * sizeof(g16::Tw29));
+    size_t tab = round_up(n * sizeof(g16::Tw29));
     c->tw_fwd = (g16::Tw29*)ws;
-    c->tw_inv = (g16::Tw29*)(ws + half_tab);
-    c->coset = (g16::Tw29*)(ws + 2 * half_tab);
-    c->scratch = (Fr*)(ws + 2 * half_tab + full_tab);
+    c->tw_inv = (g16::Tw29*)(ws + tab);
+    c->coset = (g16::Tw29*)(ws + 2 * tab);
+    c->scratch = (Fr*)(ws + 3 * tab);
     c->ws_begin = ws;
     c->ws_bytes = g16_h_workspace_bytes(log_n);
     domain_roots(log_n, &c->omega, &c->shift, &c->size_inv);
@@ -422,9 +421,9 @@ int g16_h_prepare(uint32_t log_n, void* workspace, size_t workspace_bytes, void*
     const uint32_t blocks = 2048;
     Fr one = g16::fr_mont_one();
     hipLaunchKernelGGL(g16::table_kernel, dim3(blocks), dim3(kThreads), 0, s, c->tw_fwd,
-                       c->omega, one, (uint64_t)(n / 2), log_n, 0);
+                       c->omega, one, (uint64_t)(n - 1), log_n, 0);
     hipLaunchKernelGGL(g16::table_kernel, dim3(blocks), dim3(kThreads), 0, s, c->tw_inv,
-                       c->omega_inv, one, (uint64_t)(n / 2), log_n, 0);
+                       c->omega_inv, one, (uint64_t)(n - 1), log_n, 2);
     hipLaunchKernelGGL(g16::table_kernel, dim3(blocks), dim3(kThreads), 0, s, c->coset,
                        c->shift, c->size_inv, (uint64_t)n, log_n, 1);
     int rc = launch_status();

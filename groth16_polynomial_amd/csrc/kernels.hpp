@@ -38,7 +38,7 @@
 namespace g16 {
 
 enum class Mode : int {
-    HeadBitrev = 0,  // load src[bitrev(i)] (optionally x kscale), forward passes [0, k)
+    HeadBitrev = 0,  // load src[bitrev(i)] (inverse: src[-bitrev(i)] x kscale), forward [0, k)
     FwdStrided = 1,  // forward-order passes [s0, s0 + k) on slices strided by 2^s0
     InvStrided = 2,  // inverse-order passes s0 + k - 1 down to s0, slices strided by 2^s0
     Fused = 3,       // contiguous slices: inverse passes k-1..0, x S[p], forward 0..k-1
@@ -54,12 +54,12 @@ struct BatchParams {
     const Fr* join_b;
     Fr* h_mont;
     Fr* h_std;
-    Tw29 kscale;          // HeadBitrev: multiplier applied on load (inverse transform)
+    Tw29 kscale;          // HeadBitrev, inverse transform: multiplier applied on load
     uint32_t log_n;
     uint32_t s0;
     uint32_t k;
     uint32_t log_spw;     // log2 of slices per workgroup (radix-2 kernel)
-    uint32_t use_kscale;
+    uint32_t head_inverse;  // HeadBitrev: the inverse transform (see the head load)
     uint32_t n_vec;       // register-group kernel: number of vectors (grid = groups x n_vec)
 };
 
@@ -110,21 +110,45 @@ __device__ __forceinline__ uint32_t bitrev_w(uint32_t x, uint32_t bits) {
     return bits ? (__builtin_bitreverse32(x) >> (32u - bits)) : 0u;
 }
 
-// Twiddle index of a forward-order pass on global bit s0 + t for the pair whose lower
-// element has column `low` (< 2^s0) and local index bits below t equal to jm.
-__device__ __forceinline__ uint32_t fwd_tw_index(uint32_t log_n, uint32_t s0, uint32_t t,
-                                                 uint32_t low, uint32_t jm) {
-    return (low + (jm << s0)) << (log_n - 1u - s0 - t);
+// Twiddle tables are stored by level: level m holds n / 2^(m+1) powers of root^(2^m) at
+// offset n - n / 2^m (n - 1 entries in all), so a pass on bit b reads one level.
+__device__ __forceinline__ uint32_t level_index(uint32_t log_n, uint32_t m, uint32_t j) {
+    return (1u << log_n) - ((1u << log_n) >> m) + j;
 }
 
-// Twiddle index of an inverse-order pass on global bit b = s0 + t of a batch of k
-// passes, for the pair whose lower element has local bits above t equal to a and slice
-// row (global bits above the batch) equal to h: 2^b bitrev_(L-1-b)(i >> (b+1)) with
-// i >> (b+1) = a + h 2^(k-t-1).
+// Forward order (table of omega, natural order within each level: entry j of level m is
+// omega^(2^m j)).  The pass on global bit b = s0 + t, for the pair whose lower element
+// has column `low` (< 2^s0) and local index bits below t equal to jm, needs
+// omega^(j 2^(L-1-b)) with j = low + jm 2^s0 = i mod 2^b: level L-1-b, entry j.  Lanes
+// holding neighbouring columns of a strided batch read neighbouring entries.
+__device__ __forceinline__ uint32_t fwd_tw_exp(uint32_t s0, uint32_t low, uint32_t jm) {
+    return low + (jm << s0);
+}
+__device__ __forceinline__ uint32_t fwd_tw_index(uint32_t log_n, uint32_t s0, uint32_t t,
+                                                 uint32_t low, uint32_t jm) {
+    return level_index(log_n, log_n - 1u - s0 - t, fwd_tw_exp(s0, low, jm));
+}
+
+// Inverse order (table of omega^-1, bit-reversed within each level: entry X of level m is
+// omega^-(2^m bitrev_(L-1-m)(X))).  The pass on global bit b = s0 + t of a batch of k
+// passes needs omega^-(2^b bitrev_(L-1-b)(i >> (b+1))): level b, entry X = i >> (b+1) =
+// a + h 2^(k-t-1), for the pair whose lower element has local bits above t equal to a
+// and slice row (global bits above the batch) h.  Neighbouring lanes again read
+// neighbouring entries.
+__device__ __forceinline__ uint32_t inv_tw_exp(uint32_t k, uint32_t t, uint32_t a, uint32_t h) {
+    return a + (h << (k - t - 1u));
+}
 __device__ __forceinline__ uint32_t inv_tw_index(uint32_t log_n, uint32_t s0, uint32_t k,
                                                  uint32_t t, uint32_t a, uint32_t h) {
-    const uint32_t hb = log_n - s0 - k;
-    return ((bitrev_w(a, k - t - 1u) << hb) + bitrev_w(h, hb)) << (s0 + t);
+    return level_index(log_n, s0 + t, inv_tw_exp(k, t, a, h));
+}
+
+// Source index of the head's load: bitrev(i) for the forward transform.  The inverse
+// transform runs the same forward passes on x[-k mod n]: sum_k x[-k] omega^(jk) =
+// sum_k x[k] omega^(-jk).
+__device__ __forceinline__ uint32_t head_index(uint64_t i, uint32_t log_n, uint32_t inverse) {
+    const uint32_t br = bitrev_bits((uint32_t)i, log_n);
+    return inverse ? ((0u - br) & ((1u << log_n) - 1u)) : br;
 }
 
 // The H epilogue: h_mont[i] = A'[i] B'[i] - x, h_std[i] = the same without the factor R.
@@ -158,10 +182,12 @@ __device__ __forceinline__ void lds_pass(Fr* sh, const Tw29* tw, uint32_t log_n,
         Fr u = ld_lds(base + lo);
         Fr v = ld_lds(base + hi);
         const uint32_t g = g0 + sl;
+        const uint32_t low = g & ((1u << s0) - 1u);
+        const uint32_t ex = INV ? inv_tw_exp(k, t, bf >> t, g >> s0) : fwd_tw_exp(s0, low, jm);
         const uint32_t idx = INV ? inv_tw_index(log_n, s0, k, t, bf >> t, g >> s0)
-                                 : fwd_tw_index(log_n, s0, t, g & ((1u << s0) - 1u), jm);
-        // index 0 is the twiddle 1
-        Fr vw = idx == 0u ? v : fr_mul_entry(v, ld_tw(tw + idx));
+                                 : fwd_tw_index(log_n, s0, t, low, jm);
+        // exponent 0 is the twiddle 1
+        Fr vw = ex == 0u ? v : fr_mul_entry(v, ld_tw(tw + idx));
         st_lds(base + lo, fr_add(u, vw));
         st_lds(base + hi, fr_sub(u, vw));
     }
@@ -201,8 +227,8 @@ __global__ void __launch_bounds__(256) ntt_batch_kernel(BatchParams p) {
         uint64_t i = gindex(sl, m);
         Fr x;
         if (M == Mode::HeadBitrev) {
-            x = ld_global(src + bitrev_bits((uint32_t)i, p.log_n));
-            if (p.use_kscale) x = fr_mul_entry(x, p.kscale);
+            x = ld_global(src + head_index(i, p.log_n, p.head_inverse));
+            if (p.head_inverse) x = fr_mul_entry(x, p.kscale);
         } else {
             x = ld_global(src + i);
         }

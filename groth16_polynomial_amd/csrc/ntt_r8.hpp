@@ -24,13 +24,30 @@
 
 namespace g16 {
 
+// Slices per workgroup.  Contiguous batches: 2^(10-K) slices (36 KiB of LDS).
+// Strided batches: at least kStridedCols adjacent columns, so that the lanes reading one
+// row of a workgroup's columns read 64 contiguous bytes of the vector instead of 32; at
+// K = 10 that is 72 KiB of LDS and 512 threads, two workgroups per CU (four columns, a
+// whole 128-byte line per row in one 1024-thread workgroup, measured no faster).
+#ifndef G16_STRIDED_COLS
+#define G16_STRIDED_COLS 2
+#endif
+constexpr int kStridedCols = G16_STRIDED_COLS;
+
+constexpr bool strided_mode(Mode m) { return m == Mode::FwdStrided || m == Mode::InvStrided; }
+
+constexpr int slices_per_wg(int k, Mode m) {
+    const int base = k >= 10 ? 1 : (1 << (10 - k));
+    return strided_mode(m) && base < kStridedCols ? kStridedCols : base;
+}
+
 // K passes per batch in groups of GR (the last group may be shorter); each thread
-// holds 2^GR elements; 2^(10-K) slices per workgroup (at most 36 KiB of LDS).
-template <int K, int GR>
+// holds 2^GR elements; SPW slices per workgroup.
+template <int K, int GR, int SPW>
 struct R8Geom {
     static constexpr int kE = 1 << GR;
     static constexpr int kThreadsPerSlice = 1 << (K - GR);
-    static constexpr int kSpw = K >= 10 ? 1 : (1 << (10 - K));
+    static constexpr int kSpw = SPW;
     static constexpr int kThreads = kThreadsPerSlice * kSpw;
     static constexpr int kPlane = kSpw << K;                    // slots per plane
     static constexpr int kLdsBytes = kPlane * 36;
@@ -38,6 +55,9 @@ struct R8Geom {
     static constexpr int group_b0(int g) { return GR * g; }
     static constexpr int group_r(int g) { return (K - GR * g) < GR ? (K - GR * g) : GR; }
 };
+
+template <int K, int GR, Mode M>
+using R8GeomFor = R8Geom<K, GR, slices_per_wg(K, M)>;
 
 // c with the r bits of q inserted at bit b0
 __device__ __forceinline__ uint32_t insert_bits(uint32_t c, uint32_t q, int b0, int r) {
@@ -183,11 +203,14 @@ __device__ __forceinline__ void group_inv(V29 (&x)[E], uint32_t c, uint32_t h, u
     });
 }
 
-// Grid: x = slice groups (2^(L-K) / kSpw), y = vectors; block = R8Geom<K, GR>::kThreads;
-// dynamic LDS = R8Geom<K, GR>::kLdsBytes.
+// Grid: (2^(L-K) / kSpw) slice groups x n_vec vectors, one-dimensional;
+// block = R8GeomFor<K, GR, M>::kThreads; dynamic LDS = R8GeomFor<K, GR, M>::kLdsBytes.
+// Launch bounds: four waves per SIMD whatever the workgroup size (128 VGPRs).
 template <int K, int GR, Mode M, bool JOIN>
-__global__ void __launch_bounds__(256, 4) ntt_r8_kernel(BatchParams p) {
-    using G = R8Geom<K, GR>;
+__global__ void __launch_bounds__((R8GeomFor<K, GR, M>::kThreads),
+                                  (1024 / R8GeomFor<K, GR, M>::kThreads))
+ntt_r8_kernel(BatchParams p) {
+    using G = R8GeomFor<K, GR, M>;
     extern __shared__ uint2 lds[];
     constexpr bool kStrided = (M == Mode::FwdStrided || M == Mode::InvStrided);
     constexpr int NG = G::kGroups;
@@ -241,8 +264,8 @@ __global__ void __launch_bounds__(256, 4) ntt_r8_kernel(BatchParams p) {
             constexpr int xi = decltype(xi_c)::value;
             const uint64_t i = gidx(e);
             if constexpr (M == Mode::HeadBitrev) {
-                V29 v = fr29_from_fr(ld_global(src + bitrev_bits((uint32_t)i, L)));
-                x[xi] = p.use_kscale ? shoup_mul(v, p.kscale) : v;
+                V29 v = fr29_from_fr(ld_global(src + head_index(i, L, p.head_inverse)));
+                x[xi] = p.head_inverse ? shoup_mul(v, p.kscale) : v;
             } else {
                 x[xi] = fr29_from_fr(ld_global(src + i));
             }

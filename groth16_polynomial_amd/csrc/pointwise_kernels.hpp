@@ -34,7 +34,10 @@ __global__ void __launch_bounds__(256) elementwise_kernel(const Fr* a, const Fr*
 // Table builders.  Each thread raises the base to its own exponent (prepare time only)
 // and stores the entry the table products take (fr29.hpp: the plain value and its
 // Shoup companion floor(w 2^261 / r)).
-//   kind 0: T[j] = base^j                         (twiddles, j < count)
+//   kind 0: twiddles by level (see level_index): entry e = n - n/2^m + j of level m is
+//           base^(2^m j), for the n - 1 entries of a 2^L domain
+//   kind 2: the same levels bit-reversed: entry n - n/2^m + j is
+//           base^(2^m bitrev_(L-1-m)(j))
 //   kind 1: T[p] = factor * base^bitrev_L(p)      (coset table, p < count = 2^L)
 __device__ __forceinline__ void st_tw(Tw29* p, const Tw29& t) {
     uint4* q = reinterpret_cast<uint4*>(p);
@@ -47,11 +50,18 @@ __device__ __forceinline__ void st_tw(Tw29* p, const Tw29& t) {
 
 __global__ void __launch_bounds__(256) table_kernel(Tw29* out, Fr base, Fr factor,
                                                     uint64_t count, uint32_t log_n, int kind) {
+    const uint64_t n = 1ull << log_n;
     for (uint64_t j = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; j < count;
          j += (uint64_t)gridDim.x * blockDim.x) {
         Fr v;
-        if (kind == 0) {
-            v = fr_pow_u64(base, j);
+        if (kind == 0 || kind == 2) {
+            // level m spans [n - n/2^m, n - n/2^(m+1)) and has L-1-m index bits
+            uint32_t m = 0;
+            while (j >= n - (n >> (m + 1))) ++m;
+            uint64_t jj = j - (n - (n >> m));
+            const uint32_t bits = log_n - 1u - m;
+            if (kind == 2 && bits > 0u) jj = bitrev_bits((uint32_t)jj, bits);
+            v = fr_pow_u64(base, jj << m);
         } else {
             uint64_t e = bitrev_bits((uint32_t)j, log_n);
             v = fr_mul(factor, fr_pow_u64(base, e));

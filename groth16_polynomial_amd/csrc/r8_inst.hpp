@@ -7,7 +7,14 @@ namespace g16 {
 
 template <int K, Mode M, bool JOIN>
 hipError_t launch_r8(const BatchParams& p, uint32_t n_vec, hipStream_t stream) {
-    using G = R8Geom<K, kR8Group>;
+    using G = R8GeomFor<K, kR8Group, M>;
+    // LDS beyond the default 64 KiB has to be allowed per kernel (on the current device)
+    if constexpr (G::kLdsBytes > 65536) {
+        hipError_t e = hipFuncSetAttribute((const void*)ntt_r8_kernel<K, kR8Group, M, JOIN>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           G::kLdsBytes);
+        if (e != hipSuccess) return e;
+    }
     const uint64_t groups = (1ull << (p.log_n - K)) / G::kSpw;
     BatchParams q = p;
     q.n_vec = n_vec;
