@@ -14,7 +14,9 @@
 // freshly split canonical value have them in [0, 2^29)).  A Cooley-Tukey butterfly
 // replaces (lo, hi) by lo + t and lo - t with t = w hi a product output, so both results
 // sit one pass further from lo's last normalization than lo did, and hi's own growth
-// does not carry over.  After p passes from normalized a digit is below
+// does not carry over.  (Digit 8 is never masked: it moves by less than 2^27 a pass and
+// stays far inside 32 bits over the at most ten passes between a load or product and
+// the next canonical store.)  After p passes from normalized a digit is below
 // 2^29 + 3 + p (2^29 - 1) in magnitude, so three passes still fit in 32 bits (and any
 // 32-bit digits are a valid product input).  The transforms therefore normalize, at the start of each register group of two
 // passes, only the elements that are "lo" in the group's first pass: every group output
@@ -137,10 +139,12 @@ G16_HD int64_t mad_chain(int32_t a, int32_t b, int64_t c) {
 //   may reach 2^29 + 1; nine below 2^59 plus nine below 2^57 for the low columns; plus a
 //   carry below 2^35).
 //   Result: digits 0..7 in [0, 2^29), digit 8 signed; value congruent to x w, with
-//   -7 r < value < 9 r, so |digit 8| < 2^25.
-// q is taken from columns 7..16 of x w': the dropped columns 0..6 add less than 2^237 in
-// magnitude, far below one unit of q (2^261), so q is within one of floor(x w' / 2^261),
-// and x w - q r lies within (x/2^261 +- 2) r of zero.
+//   |value| < 23 r, so |digit 8| < 2^27.
+// q is taken from columns 8..16 of x w' (45 products): the dropped columns 0..7 add less
+// than 2^265 in magnitude, sixteen units of q (2^261), so q is within 17 of
+// x w' / 2^261, and x w - q r lies within (|x|/2^261 + 19) r of zero; |x| < 2^263 keeps
+// that below 23 r.  Dropping column 7 saves eight multiply-adds for a slightly wider
+// output range, which the digit budget of fr29 absorbs.
 template <int N>
 G16_HD void shoup_mul_n(const V29 (&xin)[N], const Tw29 (&t)[N], V29 (&y)[N]) {
     // The input digits go through an empty asm statement too: where the compiler can
@@ -162,10 +166,10 @@ G16_HD void shoup_mul_n(const V29 (&xin)[N], const Tw29 (&t)[N], V29 (&y)[N]) {
     int64_t acc[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) acc[n] = 0;
-    // q: columns 7..16 of x w'; its digits are taken in [0, 2^29) (q mod 2^261 is all the
+    // q: columns 8..16 of x w'; its digits are taken in [0, 2^29) (q mod 2^261 is all the
     // low part needs)
 #pragma unroll
-    for (int c = 7; c < 17; ++c) {
+    for (int c = 8; c < 17; ++c) {
 #pragma unroll
         for (int i = 0; i < 9; ++i) {
             const int j = c - i;
@@ -186,7 +190,7 @@ G16_HD void shoup_mul_n(const V29 (&xin)[N], const Tw29 (&t)[N], V29 (&y)[N]) {
         acc[n] = 0;
     }
     // y: columns 0..8 of x w + q (-r) = (x w - q r) mod 2^261; the top digit is read back
-    // as a signed 29-bit number, which is exact since |x w - q r| < 2^257
+    // as a signed 29-bit number, which is exact since |x w - q r| < 2^259
 #pragma unroll
     for (int c = 0; c < 9; ++c) {
 #pragma unroll

@@ -102,40 +102,58 @@ __device__ __forceinline__ void static_for(F&& f) {
 #endif
 constexpr int kChains = G16_CHAINS;
 
+// Butterflies of a pass whose twiddle is 1: bit b of the mask for butterfly b.
+template <unsigned MASK>
+constexpr int count_nontrivial(int nb) {
+    int c = 0;
+    for (int b = 0; b < nb; ++b) c += ((MASK >> b) & 1u) ? 0 : 1;
+    return c;
+}
+template <unsigned MASK>
+constexpr int nth_nontrivial(int nb, int k) {
+    for (int b = 0; b < nb; ++b)
+        if (!((MASK >> b) & 1u)) {
+            if (k == 0) return b;
+            --k;
+        }
+    return 0;
+}
+
 // One pass of a group on x[OFF .. OFF + 2^R): the 2^(R-1) butterflies x_lo, x_hi <-
-// x_lo + t, x_lo - t with t = w x_hi, the products computed together (shoup_mul_n).
-// Butterfly b has lower element q(b) (b with a zero inserted at bit u) and twiddle
-// index idx(b); TRIVIAL passes have twiddle 1 throughout and t = x_hi, which must then
-// be fresh (canonical or a product output).
-template <int OFF, int R, int U, bool TRIVIAL, int E, typename IdxF>
+// x_lo + t, x_lo - t with t = w x_hi, the products computed kChains at a time
+// (shoup_mul_n).  Butterfly b has lower element q(b) (b with a zero inserted at bit U)
+// and twiddle index idx(b).  Butterflies in TRIV have twiddle 1 and take t = x_hi; they
+// occur only where x_hi is fresh (canonical, a product output, or the sum or difference
+// of two such in the second pass of a batch's first group), which keeps every digit
+// inside 32 bits.
+template <int OFF, int R, int U, unsigned TRIV, int E, typename IdxF>
 __device__ __forceinline__ void ct_pass(V29 (&x)[E], const Tw29* tw, IdxF&& idx) {
     constexpr int NB = 1 << (R - 1);
+    constexpr int NT = count_nontrivial<TRIV>(NB);
     auto lower = [](int b) { return ((b >> U) << (U + 1)) | (b & ((1 << U) - 1)); };
     V29 t[NB];
-    if constexpr (TRIVIAL) {
-        static_for<NB>([&](auto b_c) {
-            constexpr int b = decltype(b_c)::value;
-            t[b] = x[OFF + lower(b) + (1 << U)];
+    static_for<NB>([&](auto b_c) {
+        constexpr int b = decltype(b_c)::value;
+        if constexpr ((TRIV >> b) & 1u) t[b] = x[OFF + lower(b) + (1 << U)];
+    });
+    constexpr int NC = NT < kChains ? (NT > 0 ? NT : 1) : kChains;
+    static_for<(NT + NC - 1) / NC>([&](auto ch_c) {
+        constexpr int c0 = decltype(ch_c)::value * NC;
+        constexpr int nc = (NT - c0) < NC ? (NT - c0) : NC;
+        V29 h[nc], y[nc];
+        Tw29 w[nc];
+        static_for<nc>([&](auto j_c) {
+            constexpr int j = decltype(j_c)::value;
+            constexpr int b = nth_nontrivial<TRIV>(NB, c0 + j);
+            h[j] = x[OFF + lower(b) + (1 << U)];
+            w[j] = ld_tw(tw + idx(std::integral_constant<int, b>{}));
         });
-    } else {
-        // products kChains at a time
-        constexpr int NC = NB < kChains ? NB : kChains;
-        static_for<NB / NC>([&](auto ch_c) {
-            constexpr int b0 = decltype(ch_c)::value * NC;
-            V29 h[NC], y[NC];
-            Tw29 w[NC];
-            static_for<NC>([&](auto j_c) {
-                constexpr int j = decltype(j_c)::value;
-                h[j] = x[OFF + lower(b0 + j) + (1 << U)];
-                w[j] = ld_tw(tw + idx(std::integral_constant<int, b0 + j>{}));
-            });
-            shoup_mul_n<NC>(h, w, y);
-            static_for<NC>([&](auto j_c) {
-                constexpr int j = decltype(j_c)::value;
-                t[b0 + j] = y[j];
-            });
+        shoup_mul_n<nc>(h, w, y);
+        static_for<nc>([&](auto j_c) {
+            constexpr int j = decltype(j_c)::value;
+            t[nth_nontrivial<TRIV>(NB, c0 + j)] = y[j];
         });
-    }
+    });
     static_for<NB>([&](auto b_c) {
         constexpr int b = decltype(b_c)::value;
         constexpr int q = ((b >> U) << (U + 1)) | (b & ((1 << U) - 1));
@@ -147,7 +165,7 @@ __device__ __forceinline__ void ct_pass(V29 (&x)[E], const Tw29* tw, IdxF&& idx)
 // The R forward-order passes of one group on x[OFF .. OFF + 2^R): pass u flips local
 // bit B0 + u (global bit s0 + B0 + u); the pair (q, q + 2^u) has local index bits below
 // the pass equal to (c mod 2^B0) + (q mod 2^u) 2^B0.  Global bit 0 has twiddle 1.
-template <int OFF, int R, int B0, bool NORM, int E>
+template <int OFF, int R, int B0, bool NORM, bool CONTIG, int E>
 __device__ __forceinline__ void group_fwd(V29 (&x)[E], uint32_t c, uint32_t low, uint32_t s0,
                                           uint32_t log_n, const Tw29* tw) {
     const uint32_t cl = c & ((1u << B0) - 1u);
@@ -164,12 +182,14 @@ __device__ __forceinline__ void group_fwd(V29 (&x)[E], uint32_t c, uint32_t low,
             constexpr int m = decltype(b_c)::value & ((1 << u) - 1);
             return fwd_tw_index(log_n, s0, t, low, cl + ((uint32_t)m << B0));
         };
-        if constexpr (B0 + u == 0) {
-            if (s0 == 0u) ct_pass<OFF, R, u, true>(x, tw, idx);
-            else ct_pass<OFF, R, u, false>(x, tw, idx);
-        } else {
-            ct_pass<OFF, R, u, false>(x, tw, idx);
-        }
+        // First group of a contiguous batch (s0 = 0): bit 0 has twiddle 1 throughout,
+        // bit 1 for the pairs with m = 0 (even b); the latter only in a two-pass group, the
+        // growth of a third pass would no longer fit in 32 bits.
+        constexpr unsigned all = (1u << (1 << (R - 1))) - 1u;
+        constexpr unsigned triv = (CONTIG && B0 == 0 && u == 0) ? all
+                                : (CONTIG && B0 == 0 && u == 1 && R == 2) ? (0x55555555u & all)
+                                                                          : 0u;
+        ct_pass<OFF, R, u, triv>(x, tw, idx);
     });
 }
 
@@ -186,6 +206,7 @@ __device__ __forceinline__ void group_inv(V29 (&x)[E], uint32_t c, uint32_t h, u
             x[OFF + q] = fr29_normalize(x[OFF + q]);
         });
     }
+    const bool top_batch = s0 + (uint32_t)K == log_n;
     static_for<R>([&](auto uu_c) {
         constexpr int u = R - 1 - decltype(uu_c)::value;
         const uint32_t t = (uint32_t)(B0 + u);
@@ -194,21 +215,28 @@ __device__ __forceinline__ void group_inv(V29 (&x)[E], uint32_t c, uint32_t h, u
             const uint32_t a = (uint32_t)m + (ch << (R - 1 - u));
             return inv_tw_index(log_n, s0, (uint32_t)K, t, a, h);
         };
-        if constexpr (B0 + u == K - 1) {
-            if (s0 + (uint32_t)K == log_n) ct_pass<OFF, R, u, true>(x, tw, idx);
-            else ct_pass<OFF, R, u, false>(x, tw, idx);
+        // Top group of the top batch (ch = 0 and h = 0 there): the transform's top bit has
+        // twiddle 1 throughout, the next bit for the pairs with q >> (u + 1) = 0 (only in a
+        // two-pass group, as in group_fwd).
+        constexpr unsigned all = (1u << (1 << (R - 1))) - 1u;
+        constexpr bool top_group = B0 + R == K;
+        constexpr unsigned triv = (top_group && u == R - 1) ? all
+                                : (top_group && u == 0 && R == 2) ? 1u : 0u;
+        if constexpr (triv != 0u) {
+            if (top_batch) ct_pass<OFF, R, u, triv>(x, tw, idx);
+            else ct_pass<OFF, R, u, 0u>(x, tw, idx);
         } else {
-            ct_pass<OFF, R, u, false>(x, tw, idx);
+            ct_pass<OFF, R, u, 0u>(x, tw, idx);
         }
     });
 }
 
 // Grid: (2^(L-K) / kSpw) slice groups x n_vec vectors, one-dimensional;
 // block = R8GeomFor<K, GR, M>::kThreads; dynamic LDS = R8GeomFor<K, GR, M>::kLdsBytes.
-// Launch bounds: four waves per SIMD whatever the workgroup size (128 VGPRs).
+// Launch bounds: at least four waves per SIMD (the second argument is the minimum waves
+// per execution unit), i.e. at most 128 VGPRs, whatever the workgroup size.
 template <int K, int GR, Mode M, bool JOIN>
-__global__ void __launch_bounds__((R8GeomFor<K, GR, M>::kThreads),
-                                  (1024 / R8GeomFor<K, GR, M>::kThreads))
+__global__ void __launch_bounds__((R8GeomFor<K, GR, M>::kThreads), 4)
 ntt_r8_kernel(BatchParams p) {
     using G = R8GeomFor<K, GR, M>;
     extern __shared__ uint2 lds[];
@@ -307,7 +335,8 @@ ntt_r8_kernel(BatchParams p) {
                 group_inv<s * (1 << r), r, b0, K, norm, G::kE>(x, t * nsets + s, lrow, ls0, L,
                                                                 tw);
             else
-                group_fwd<s * (1 << r), r, b0, norm, G::kE>(x, t * nsets + s, llow, ls0, L, tw);
+                group_fwd<s * (1 << r), r, b0, norm, !kStrided, G::kE>(x, t * nsets + s, llow,
+                                                                    ls0, L, tw);
         });
     };
     using FWD = std::false_type;
