@@ -74,14 +74,14 @@ def stage_list(plan, n_vec=3):
     if nb == 1:
         return [("fused", False, 2, plan[0]), ("fused", True, 1, plan[0])]
     for b in range(nb - 1, 0, -1):
-        out.append(("dif", False, n_vec, plan[b]))
+        out.append(("inv", False, n_vec, plan[b]))
     out.append(("fused", False, n_vec, plan[0]))
     for b in range(1, nb):
         if b == nb - 1:
-            out.append(("dit", False, n_vec - 1, plan[b]))
-            out.append(("dit", True, 1, plan[b]))
+            out.append(("fwd", False, n_vec - 1, plan[b]))
+            out.append(("fwd", True, 1, plan[b]))
         else:
-            out.append(("dit", False, n_vec, plan[b]))
+            out.append(("fwd", False, n_vec, plan[b]))
     return out
 
 

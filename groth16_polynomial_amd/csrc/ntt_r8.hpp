@@ -96,11 +96,10 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // Products computed together (interleaved multiply-add chains, shoup_mul_n): more
-// hides the dependent-multiply-add wait states, fewer keeps register pressure down.
-#ifndef G16_CHAINS
-#define G16_CHAINS 2
-#endif
-constexpr int kChains = G16_CHAINS;
+// hides the dependent-multiply-add wait states, fewer keeps register pressure down.  The
+// fused kernel holds three table pointers and the slice row on top of the strided
+// kernels' state, and two chains there spill to scratch memory.
+constexpr int chains_for(Mode m) { return m == Mode::Fused ? 1 : 2; }
 
 // Butterflies of a pass whose twiddle is 1: bit b of the mask for butterfly b.
 template <unsigned MASK>
@@ -120,13 +119,13 @@ constexpr int nth_nontrivial(int nb, int k) {
 }
 
 // One pass of a group on x[OFF .. OFF + 2^R): the 2^(R-1) butterflies x_lo, x_hi <-
-// x_lo + t, x_lo - t with t = w x_hi, the products computed kChains at a time
+// x_lo + t, x_lo - t with t = w x_hi, the products computed CH at a time
 // (shoup_mul_n).  Butterfly b has lower element q(b) (b with a zero inserted at bit U)
 // and twiddle index idx(b).  Butterflies in TRIV have twiddle 1 and take t = x_hi; they
 // occur only where x_hi is fresh (canonical, a product output, or the sum or difference
 // of two such in the second pass of a batch's first group), which keeps every digit
 // inside 32 bits.
-template <int OFF, int R, int U, unsigned TRIV, int E, typename IdxF>
+template <int OFF, int R, int U, unsigned TRIV, int CH, int E, typename IdxF>
 __device__ __forceinline__ void ct_pass(V29 (&x)[E], const Tw29* tw, IdxF&& idx) {
     constexpr int NB = 1 << (R - 1);
     constexpr int NT = count_nontrivial<TRIV>(NB);
@@ -136,7 +135,7 @@ __device__ __forceinline__ void ct_pass(V29 (&x)[E], const Tw29* tw, IdxF&& idx)
         constexpr int b = decltype(b_c)::value;
         if constexpr ((TRIV >> b) & 1u) t[b] = x[OFF + lower(b) + (1 << U)];
     });
-    constexpr int NC = NT < kChains ? (NT > 0 ? NT : 1) : kChains;
+    constexpr int NC = NT < CH ? (NT > 0 ? NT : 1) : CH;
     static_for<(NT + NC - 1) / NC>([&](auto ch_c) {
         constexpr int c0 = decltype(ch_c)::value * NC;
         constexpr int nc = (NT - c0) < NC ? (NT - c0) : NC;
@@ -165,7 +164,7 @@ __device__ __forceinline__ void ct_pass(V29 (&x)[E], const Tw29* tw, IdxF&& idx)
 // The R forward-order passes of one group on x[OFF .. OFF + 2^R): pass u flips local
 // bit B0 + u (global bit s0 + B0 + u); the pair (q, q + 2^u) has local index bits below
 // the pass equal to (c mod 2^B0) + (q mod 2^u) 2^B0.  Global bit 0 has twiddle 1.
-template <int OFF, int R, int B0, bool NORM, bool CONTIG, int E>
+template <int OFF, int R, int B0, bool NORM, bool CONTIG, int CH, int E>
 __device__ __forceinline__ void group_fwd(V29 (&x)[E], uint32_t c, uint32_t low, uint32_t s0,
                                           uint32_t log_n, const Tw29* tw) {
     const uint32_t cl = c & ((1u << B0) - 1u);
@@ -189,14 +188,14 @@ __device__ __forceinline__ void group_fwd(V29 (&x)[E], uint32_t c, uint32_t low,
         constexpr unsigned triv = (CONTIG && B0 == 0 && u == 0) ? all
                                 : (CONTIG && B0 == 0 && u == 1 && R == 2) ? (0x55555555u & all)
                                                                           : 0u;
-        ct_pass<OFF, R, u, triv>(x, tw, idx);
+        ct_pass<OFF, R, u, triv, CH>(x, tw, idx);
     });
 }
 
 // The R inverse-order passes of one group, u = R-1 down to 0: the pair (q, q + 2^u) has
 // local bits above the pass a = (q >> (u+1)) + (c >> B0) 2^(R-1-u) and slice row h.
 // The pass on the transform's top bit (only in the top batch) has twiddle 1 throughout.
-template <int OFF, int R, int B0, int K, bool NORM, int E>
+template <int OFF, int R, int B0, int K, bool NORM, int CH, int E>
 __device__ __forceinline__ void group_inv(V29 (&x)[E], uint32_t c, uint32_t h, uint32_t s0,
                                           uint32_t log_n, const Tw29* tw) {
     const uint32_t ch = c >> B0;
@@ -223,10 +222,10 @@ __device__ __forceinline__ void group_inv(V29 (&x)[E], uint32_t c, uint32_t h, u
         constexpr unsigned triv = (top_group && u == R - 1) ? all
                                 : (top_group && u == 0 && R == 2) ? 1u : 0u;
         if constexpr (triv != 0u) {
-            if (top_batch) ct_pass<OFF, R, u, triv>(x, tw, idx);
-            else ct_pass<OFF, R, u, 0u>(x, tw, idx);
+            if (top_batch) ct_pass<OFF, R, u, triv, CH>(x, tw, idx);
+            else ct_pass<OFF, R, u, 0u, CH>(x, tw, idx);
         } else {
-            ct_pass<OFF, R, u, 0u>(x, tw, idx);
+            ct_pass<OFF, R, u, 0u, CH>(x, tw, idx);
         }
     });
 }
@@ -332,10 +331,10 @@ ntt_r8_kernel(BatchParams p) {
         static_for<nsets>([&](auto s_c) {
             constexpr int s = decltype(s_c)::value;
             if constexpr (inv)
-                group_inv<s * (1 << r), r, b0, K, norm, G::kE>(x, t * nsets + s, lrow, ls0, L,
+                group_inv<s * (1 << r), r, b0, K, norm, chains_for(M), G::kE>(x, t * nsets + s, lrow, ls0, L,
                                                                 tw);
             else
-                group_fwd<s * (1 << r), r, b0, norm, !kStrided, G::kE>(x, t * nsets + s, llow,
+                group_fwd<s * (1 << r), r, b0, norm, !kStrided, chains_for(M), G::kE>(x, t * nsets + s, llow,
                                                                     ls0, L, tw);
         });
     };
@@ -403,7 +402,7 @@ ntt_r8_kernel(BatchParams p) {
         for_group(std::integral_constant<int, 0>{}, [&](auto xi_c, uint32_t e) {
             ce[decltype(xi_c)::value] = e;
         });
-        constexpr int NC = G::kE < kChains ? G::kE : kChains;
+        constexpr int NC = G::kE < chains_for(M) ? G::kE : chains_for(M);
         static_for<G::kE / NC>([&](auto ch_c) {
             constexpr int i0 = NC * decltype(ch_c)::value;
             V29 h[NC], y[NC];
