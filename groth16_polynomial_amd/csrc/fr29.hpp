@@ -27,13 +27,16 @@
 // w' = floor(w 2^261 / r).  Then q = floor(x w' / 2^261) is within one or two of
 // x w / r and x w - q r is x w mod r up to a few multiples of r.  Only the top columns
 // of x w' are needed for q and only the low 261 bits of x w - q r, because that
-// difference is small.  This needs 53 + 45 + 45 = 143 digit products against 162 for a
+// difference is small.  This needs 45 + 45 + 45 = 135 digit products against 162 for a
 // Montgomery product on nine digits.  The result keeps x's Montgomery factor (w is a
 // plain integer), so data stay in the 2^256 Montgomery form of the library's
 // interface.  Table digits are balanced (|digit| <= 2^28, the top digit of w' up to
 // 2^29 + 1), which halves the size of every product and so doubles the input range a
 // column can absorb.
 #pragma once
+
+#include <type_traits>
+#include <utility>
 
 #include "fr.hpp"
 
@@ -119,18 +122,165 @@ G16_HD V29 fr29_normalize(const V29& a) {
     return o;
 }
 
-// One multiply-add of the signed column accumulators.  The empty asm statement makes the
-// running sum opaque, which keeps each column one chain of v_mad_i64_i32 starting from the
-// carry of the column below: 143 multiply-adds, 19 masks and 18 shifts per product,
-// against about 210 instructions when the compiler splits each column into parallel
-// partial sums and adds the carry separately.  It does not stop the scheduler from
-// interleaving independent chains, which shoup_mul_n relies on.
-G16_HD int64_t mad_chain(int32_t a, int32_t b, int64_t c) {
-    int64_t d = (int64_t)a * b + c;
+// The product on the device: one asm block per column.  A column is one chain of
+// v_mad_i64_i32 that starts from the carry of the column below.  Written in C, the chain
+// is reassociated by the compiler into parallel partial sums with the carry added
+// separately (about 40 more instructions a product); with an empty asm statement after
+// each multiply-add the chain stays whole, but the compiler then inserts a wait state
+// after every one of them, since it has to assume that an asm statement might be an
+// instruction with a result-forwarding hazard.  One block per column leaves at most one
+// wait state per column (none where another chain's block comes in between).  The
+// multiply-adds write their unused carry-out to vcc, which each block clobbers.
 #if defined(__HIP_DEVICE_COMPILE__)
-    asm("" : "+v"(d));
+#define G16_X(i, j) "v_mad_i64_i32 %[acc], vcc, %[x" #i "], %[b" #j "], %[acc]\n\t"
+#define G16_X0(i, j) "v_mad_i64_i32 %[acc], vcc, %[x" #i "], %[b" #j "], 0\n\t"
+#define G16_Q(i, j) "v_mad_i64_i32 %[acc], vcc, %[q" #i "], %[m" #j "], %[acc]\n\t"
+#define G16_XOPS(v) \
+    [x0] "v"(v[0]), \
+    [x1] "v"(v[1]), \
+    [x2] "v"(v[2]), \
+    [x3] "v"(v[3]), \
+    [x4] "v"(v[4]), \
+    [x5] "v"(v[5]), \
+    [x6] "v"(v[6]), \
+    [x7] "v"(v[7]), \
+    [x8] "v"(v[8])
+#define G16_BOPS(v) \
+    [b0] "v"(v[0]), \
+    [b1] "v"(v[1]), \
+    [b2] "v"(v[2]), \
+    [b3] "v"(v[3]), \
+    [b4] "v"(v[4]), \
+    [b5] "v"(v[5]), \
+    [b6] "v"(v[6]), \
+    [b7] "v"(v[7]), \
+    [b8] "v"(v[8])
+#define G16_QOPS(v) \
+    [q0] "v"(v[0]), \
+    [q1] "v"(v[1]), \
+    [q2] "v"(v[2]), \
+    [q3] "v"(v[3]), \
+    [q4] "v"(v[4]), \
+    [q5] "v"(v[5]), \
+    [q6] "v"(v[6]), \
+    [q7] "v"(v[7]), \
+    [q8] "v"(v[8])
+#define G16_MOPS \
+    [m0] "s"(mr29_digit(0)), \
+    [m1] "s"(mr29_digit(1)), \
+    [m2] "s"(mr29_digit(2)), \
+    [m3] "s"(mr29_digit(3)), \
+    [m4] "s"(mr29_digit(4)), \
+    [m5] "s"(mr29_digit(5)), \
+    [m6] "s"(mr29_digit(6)), \
+    [m7] "s"(mr29_digit(7)), \
+    [m8] "s"(mr29_digit(8))
+
+// Column C (8..16) of x b: acc = carry + sum of x_i b_(C-i); column 8 starts from zero.
+template <int C>
+__device__ __forceinline__ void col_q(int64_t& acc, const int32_t (&x)[9], const int32_t (&b)[9]) {
+    if constexpr (C == 8) {
+        asm(G16_X0(0, 8) G16_X(1, 7) G16_X(2, 6) G16_X(3, 5) G16_X(4, 4) G16_X(5, 3) G16_X(6, 2)
+            G16_X(7, 1) G16_X(8, 0)
+            : [acc] "=&v"(acc) : G16_XOPS(x), G16_BOPS(b) : "vcc");
+    } else if constexpr (C == 9) {
+        asm(G16_X(1, 8) G16_X(2, 7) G16_X(3, 6) G16_X(4, 5) G16_X(5, 4) G16_X(6, 3) G16_X(7, 2)
+            G16_X(8, 1)
+            : [acc] "+v"(acc) : G16_XOPS(x), G16_BOPS(b) : "vcc");
+    } else if constexpr (C == 10) {
+        asm(G16_X(2, 8) G16_X(3, 7) G16_X(4, 6) G16_X(5, 5) G16_X(6, 4) G16_X(7, 3) G16_X(8, 2)
+            : [acc] "+v"(acc) : G16_XOPS(x), G16_BOPS(b) : "vcc");
+    } else if constexpr (C == 11) {
+        asm(G16_X(3, 8) G16_X(4, 7) G16_X(5, 6) G16_X(6, 5) G16_X(7, 4) G16_X(8, 3)
+            : [acc] "+v"(acc) : G16_XOPS(x), G16_BOPS(b) : "vcc");
+    } else if constexpr (C == 12) {
+        asm(G16_X(4, 8) G16_X(5, 7) G16_X(6, 6) G16_X(7, 5) G16_X(8, 4)
+            : [acc] "+v"(acc) : G16_XOPS(x), G16_BOPS(b) : "vcc");
+    } else if constexpr (C == 13) {
+        asm(G16_X(5, 8) G16_X(6, 7) G16_X(7, 6) G16_X(8, 5)
+            : [acc] "+v"(acc) : G16_XOPS(x), G16_BOPS(b) : "vcc");
+    } else if constexpr (C == 14) {
+        asm(G16_X(6, 8) G16_X(7, 7) G16_X(8, 6)
+            : [acc] "+v"(acc) : G16_XOPS(x), G16_BOPS(b) : "vcc");
+    } else if constexpr (C == 15) {
+        asm(G16_X(7, 8) G16_X(8, 7)
+            : [acc] "+v"(acc) : G16_XOPS(x), G16_BOPS(b) : "vcc");
+    } else if constexpr (C == 16) {
+        asm(G16_X(8, 8)
+            : [acc] "+v"(acc) : G16_XOPS(x), G16_BOPS(b) : "vcc");
+    }
+}
+
+// Column C (0..8) of x b + q (-r): acc = carry + sum of x_i b_(C-i) + q_i (-r)_(C-i);
+// column 0 starts from zero.
+template <int C>
+__device__ __forceinline__ void col_y(int64_t& acc, const int32_t (&x)[9], const int32_t (&b)[9],
+                                      const int32_t (&q)[9]) {
+    if constexpr (C == 0) {
+        asm(G16_X0(0, 0) G16_Q(0, 0)
+            : [acc] "=&v"(acc)
+            : G16_XOPS(x), G16_BOPS(b), G16_QOPS(q), G16_MOPS : "vcc");
+    } else if constexpr (C == 1) {
+        asm(G16_X(0, 1) G16_Q(0, 1) G16_X(1, 0) G16_Q(1, 0)
+            : [acc] "+v"(acc)
+            : G16_XOPS(x), G16_BOPS(b), G16_QOPS(q), G16_MOPS : "vcc");
+    } else if constexpr (C == 2) {
+        asm(G16_X(0, 2) G16_Q(0, 2) G16_X(1, 1) G16_Q(1, 1) G16_X(2, 0) G16_Q(2, 0)
+            : [acc] "+v"(acc)
+            : G16_XOPS(x), G16_BOPS(b), G16_QOPS(q), G16_MOPS : "vcc");
+    } else if constexpr (C == 3) {
+        asm(G16_X(0, 3) G16_Q(0, 3) G16_X(1, 2) G16_Q(1, 2) G16_X(2, 1) G16_Q(2, 1) G16_X(3, 0)
+            G16_Q(3, 0)
+            : [acc] "+v"(acc)
+            : G16_XOPS(x), G16_BOPS(b), G16_QOPS(q), G16_MOPS : "vcc");
+    } else if constexpr (C == 4) {
+        asm(G16_X(0, 4) G16_Q(0, 4) G16_X(1, 3) G16_Q(1, 3) G16_X(2, 2) G16_Q(2, 2) G16_X(3, 1)
+            G16_Q(3, 1) G16_X(4, 0) G16_Q(4, 0)
+            : [acc] "+v"(acc)
+            : G16_XOPS(x), G16_BOPS(b), G16_QOPS(q), G16_MOPS : "vcc");
+    } else if constexpr (C == 5) {
+        asm(G16_X(0, 5) G16_Q(0, 5) G16_X(1, 4) G16_Q(1, 4) G16_X(2, 3) G16_Q(2, 3) G16_X(3, 2)
+            G16_Q(3, 2) G16_X(4, 1) G16_Q(4, 1) G16_X(5, 0) G16_Q(5, 0)
+            : [acc] "+v"(acc)
+            : G16_XOPS(x), G16_BOPS(b), G16_QOPS(q), G16_MOPS : "vcc");
+    } else if constexpr (C == 6) {
+        asm(G16_X(0, 6) G16_Q(0, 6) G16_X(1, 5) G16_Q(1, 5) G16_X(2, 4) G16_Q(2, 4) G16_X(3, 3)
+            G16_Q(3, 3) G16_X(4, 2) G16_Q(4, 2) G16_X(5, 1) G16_Q(5, 1) G16_X(6, 0) G16_Q(6, 0)
+            : [acc] "+v"(acc)
+            : G16_XOPS(x), G16_BOPS(b), G16_QOPS(q), G16_MOPS : "vcc");
+    } else if constexpr (C == 7) {
+        asm(G16_X(0, 7) G16_Q(0, 7) G16_X(1, 6) G16_Q(1, 6) G16_X(2, 5) G16_Q(2, 5) G16_X(3, 4)
+            G16_Q(3, 4) G16_X(4, 3) G16_Q(4, 3) G16_X(5, 2) G16_Q(5, 2) G16_X(6, 1) G16_Q(6, 1)
+            G16_X(7, 0) G16_Q(7, 0)
+            : [acc] "+v"(acc)
+            : G16_XOPS(x), G16_BOPS(b), G16_QOPS(q), G16_MOPS : "vcc");
+    } else if constexpr (C == 8) {
+        asm(G16_X(0, 8) G16_Q(0, 8) G16_X(1, 7) G16_Q(1, 7) G16_X(2, 6) G16_Q(2, 6) G16_X(3, 5)
+            G16_Q(3, 5) G16_X(4, 4) G16_Q(4, 4) G16_X(5, 3) G16_Q(5, 3) G16_X(6, 2) G16_Q(6, 2)
+            G16_X(7, 1) G16_Q(7, 1) G16_X(8, 0) G16_Q(8, 0)
+            : [acc] "+v"(acc)
+            : G16_XOPS(x), G16_BOPS(b), G16_QOPS(q), G16_MOPS : "vcc");
+    }
+}
+
+#undef G16_X
+#undef G16_X0
+#undef G16_Q
+#undef G16_XOPS
+#undef G16_BOPS
+#undef G16_QOPS
+#undef G16_MOPS
 #endif
-    return d;
+
+// Compile-time loop: f(std::integral_constant<int, I>{}) for I = 0 .. N-1, so that every
+// register array index is a constant and arrays stay in registers.
+template <typename F, int... I>
+G16_HD void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+G16_HD void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // y[n] = x[n] w_n mod r up to a small multiple of r, for table entries t[n] = (w, w').
@@ -143,63 +293,32 @@ G16_HD int64_t mad_chain(int32_t a, int32_t b, int64_t c) {
 // q is taken from columns 8..16 of x w' (45 products): the dropped columns 0..7 add less
 // than 2^265 in magnitude, sixteen units of q (2^261), so q is within 17 of
 // x w' / 2^261, and x w - q r lies within (|x|/2^261 + 19) r of zero; |x| < 2^263 keeps
-// that below 23 r.  Dropping column 7 saves eight multiply-adds for a slightly wider
-// output range, which the digit budget of fr29 absorbs.
+// that below 23 r.  The N products run as N interleaved chains.
 template <int N>
-G16_HD void shoup_mul_n(const V29 (&xin)[N], const Tw29 (&t)[N], V29 (&y)[N]) {
-    // The input digits go through an empty asm statement too: where the compiler can
-    // prove a digit non-negative it widens it with a zero extension, and a zero-extended
-    // times a sign-extended operand has no single-instruction multiply-add (it becomes
-    // two v_mad_u64_u32 and two moves).
-    V29 x[N];
-#pragma unroll
-    for (int n = 0; n < N; ++n) {
-#pragma unroll
-        for (int k = 0; k < 9; ++k) {
-            x[n].l[k] = xin[n].l[k];
-#if defined(__HIP_DEVICE_COMPILE__)
-            asm("" : "+v"(x[n].l[k]));
-#endif
-        }
-    }
+G16_HD void shoup_mul_n(const V29 (&x)[N], const Tw29 (&t)[N], V29 (&y)[N]) {
     int32_t q[N][9];
     int64_t acc[N];
-#pragma unroll
-    for (int n = 0; n < N; ++n) acc[n] = 0;
+#if defined(__HIP_DEVICE_COMPILE__)
     // q: columns 8..16 of x w'; its digits are taken in [0, 2^29) (q mod 2^261 is all the
     // low part needs)
+    static_for<9>([&](auto c_c) {
+        constexpr int c = 8 + decltype(c_c)::value;
 #pragma unroll
-    for (int c = 8; c < 17; ++c) {
-#pragma unroll
-        for (int i = 0; i < 9; ++i) {
-            const int j = c - i;
-            if (j >= 0 && j < 9) {
-#pragma unroll
-                for (int n = 0; n < N; ++n) acc[n] = mad_chain(x[n].l[i], t[n].wp[j], acc[n]);
-            }
-        }
+        for (int n = 0; n < N; ++n) col_q<c>(acc[n], x[n].l, t[n].wp);
 #pragma unroll
         for (int n = 0; n < N; ++n) {
             if (c >= 9) q[n][c - 9] = (int32_t)((uint32_t)acc[n] & kM29);
             acc[n] >>= 29;
         }
-    }
+    });
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
-        q[n][8] = (int32_t)((uint32_t)acc[n] & kM29);
-        acc[n] = 0;
-    }
+    for (int n = 0; n < N; ++n) q[n][8] = (int32_t)((uint32_t)acc[n] & kM29);
     // y: columns 0..8 of x w + q (-r) = (x w - q r) mod 2^261; the top digit is read back
     // as a signed 29-bit number, which is exact since |x w - q r| < 2^259
+    static_for<9>([&](auto c_c) {
+        constexpr int c = decltype(c_c)::value;
 #pragma unroll
-    for (int c = 0; c < 9; ++c) {
-#pragma unroll
-        for (int i = 0; i <= c; ++i) {
-#pragma unroll
-            for (int n = 0; n < N; ++n) acc[n] = mad_chain(x[n].l[i], t[n].w[c - i], acc[n]);
-#pragma unroll
-            for (int n = 0; n < N; ++n) acc[n] = mad_chain(q[n][i], mr29_digit(c - i), acc[n]);
-        }
+        for (int n = 0; n < N; ++n) col_y<c>(acc[n], x[n].l, t[n].w, q[n]);
 #pragma unroll
         for (int n = 0; n < N; ++n) {
             if (c < 8) {
@@ -209,7 +328,33 @@ G16_HD void shoup_mul_n(const V29 (&xin)[N], const Tw29 (&t)[N], V29 (&y)[N]) {
                 y[n].l[8] = ((int32_t)((uint32_t)acc[n] << 3)) >> 3;
             }
         }
+    });
+#else
+    // The same columns in C (host builds).
+    for (int n = 0; n < N; ++n) {
+        acc[n] = 0;
+        for (int c = 8; c < 17; ++c) {
+            for (int i = 0; i < 9; ++i)
+                if (c - i >= 0 && c - i < 9) acc[n] += (int64_t)x[n].l[i] * t[n].wp[c - i];
+            if (c >= 9) q[n][c - 9] = (int32_t)((uint32_t)acc[n] & kM29);
+            acc[n] >>= 29;
+        }
+        q[n][8] = (int32_t)((uint32_t)acc[n] & kM29);
+        acc[n] = 0;
+        for (int c = 0; c < 9; ++c) {
+            for (int i = 0; i <= c; ++i) {
+                acc[n] += (int64_t)x[n].l[i] * t[n].w[c - i];
+                acc[n] += (int64_t)q[n][i] * mr29_digit(c - i);
+            }
+            if (c < 8) {
+                y[n].l[c] = (int32_t)((uint32_t)acc[n] & kM29);
+                acc[n] >>= 29;
+            } else {
+                y[n].l[8] = ((int32_t)((uint32_t)acc[n] << 3)) >> 3;
+            }
+        }
     }
+#endif
 }
 
 G16_HD V29 shoup_mul(const V29& x, const Tw29& t) {

@@ -84,17 +84,6 @@ __device__ __forceinline__ V29 lds_get(const uint2* lds, uint32_t plane, uint32_
     return x;
 }
 
-// Compile-time loop: f(std::integral_constant<int, I>{}) for I = 0 .. N-1, so that every
-// register array index below is a constant and the element arrays stay in VGPRs.
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-    (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-    static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
 // Products computed together (interleaved multiply-add chains, shoup_mul_n): more
 // hides the dependent-multiply-add wait states, fewer keeps register pressure down.  The
 // fused kernel holds three table pointers and the slice row on top of the strided
