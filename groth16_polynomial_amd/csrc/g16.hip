@@ -417,15 +417,22 @@ int g16_h_prepare(uint32_t log_n, void* workspace, size_t workspace_bytes, void*
     c->size_inv_entry = g16::tw29_entry(c->size_inv);
     c->n_batches = plan_batches(log_n, max_batch_k(), c->batch_k);
 
+    // bits where the plan's batches start (the forward table's layout follows them)
+    uint32_t starts = 0, bit = 0;
+    for (uint32_t i = 0; i < c->n_batches; ++i) {
+        starts |= 1u << bit;
+        bit += c->batch_k[i];
+    }
+
     hipStream_t s = (hipStream_t)stream;
     const uint32_t blocks = 2048;
     Fr one = g16::fr_mont_one();
     hipLaunchKernelGGL(g16::table_kernel, dim3(blocks), dim3(kThreads), 0, s, c->tw_fwd,
-                       c->omega, one, (uint64_t)(n - 1), log_n, 0);
+                       c->omega, one, (uint64_t)(n - 1), log_n, 0, starts);
     hipLaunchKernelGGL(g16::table_kernel, dim3(blocks), dim3(kThreads), 0, s, c->tw_inv,
-                       c->omega_inv, one, (uint64_t)(n - 1), log_n, 2);
+                       c->omega_inv, one, (uint64_t)(n - 1), log_n, 2, starts);
     hipLaunchKernelGGL(g16::table_kernel, dim3(blocks), dim3(kThreads), 0, s, c->coset,
-                       c->shift, c->size_inv, (uint64_t)n, log_n, 1);
+                       c->shift, c->size_inv, (uint64_t)n, log_n, 1, starts);
     int rc = launch_status();
     if (rc) {
         delete c;

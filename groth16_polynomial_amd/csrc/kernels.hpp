@@ -82,7 +82,7 @@ __device__ __forceinline__ void st_global(Fr* p, const Fr& x) {
 __device__ __forceinline__ Fr ld_lds(const Fr* p) { return ld_global(p); }
 __device__ __forceinline__ void st_lds(Fr* p, const Fr& x) { st_global(p, x); }
 
-// A table entry: five 16-byte vector loads.  The address goes through an opaque zero
+// A table entry: four 16-byte and one 8-byte vector load.  The address goes through an opaque zero
 // held in a VGPR: an entry every lane of a wave needs would otherwise be read with
 // scalar loads into SGPRs, and the compiler lowers a signed 32 x 32-bit multiply-add
 // with a sign-extended SGPR operand as four instructions instead of one
@@ -91,7 +91,8 @@ __device__ __forceinline__ Tw29 ld_tw(const Tw29* p) {
     uint32_t z;
     asm("v_mov_b32 %0, 0" : "=v"(z));
     const uint4* q = reinterpret_cast<const uint4*>(p + z);
-    uint4 a = q[0], b = q[1], c = q[2], d = q[3], e = q[4];
+    uint4 a = q[0], b = q[1], c = q[2], d = q[3];
+    uint2 e = *reinterpret_cast<const uint2*>(q + 4);
     Tw29 t;
     t.w[0] = a.x; t.w[1] = a.y; t.w[2] = a.z; t.w[3] = a.w;
     t.w[4] = b.x; t.w[5] = b.y; t.w[6] = b.z; t.w[7] = b.w;
@@ -116,17 +117,19 @@ __device__ __forceinline__ uint32_t level_index(uint32_t log_n, uint32_t m, uint
     return (1u << log_n) - ((1u << log_n) >> m) + j;
 }
 
-// Forward order (table of omega, natural order within each level: entry j of level m is
-// omega^(2^m j)).  The pass on global bit b = s0 + t, for the pair whose lower element
-// has column `low` (< 2^s0) and local index bits below t equal to jm, needs
-// omega^(j 2^(L-1-b)) with j = low + jm 2^s0 = i mod 2^b: level L-1-b, entry j.  Lanes
-// holding neighbouring columns of a strided batch read neighbouring entries.
+// Forward order (table of omega): level m serves the pass on bit b = L-1-m and holds the
+// 2^b powers omega^(2^m j), j < 2^b.  The pass on global bit b = s0 + t of a batch that
+// starts at bit s0, for the pair whose lower element has column `low` (< 2^s0) and local
+// index bits below t equal to jm, needs j = low + jm 2^s0 = i mod 2^b.  The level stores
+// that entry at position jm + low 2^t (j itself when s0 = 0 or t = 0): the lanes of one
+// column of a strided batch, which differ in jm, read consecutive entries.  The table
+// builder therefore takes the batch plan (the bits where batches start).
 __device__ __forceinline__ uint32_t fwd_tw_exp(uint32_t s0, uint32_t low, uint32_t jm) {
     return low + (jm << s0);
 }
 __device__ __forceinline__ uint32_t fwd_tw_index(uint32_t log_n, uint32_t s0, uint32_t t,
                                                  uint32_t low, uint32_t jm) {
-    return level_index(log_n, log_n - 1u - s0 - t, fwd_tw_exp(s0, low, jm));
+    return level_index(log_n, log_n - 1u - s0 - t, jm + (low << t));
 }
 
 // Inverse order (table of omega^-1, bit-reversed within each level: entry X of level m is

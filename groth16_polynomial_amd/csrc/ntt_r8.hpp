@@ -84,11 +84,14 @@ __device__ __forceinline__ V29 lds_get(const uint2* lds, uint32_t plane, uint32_
     return x;
 }
 
-// Products computed together (interleaved multiply-add chains, shoup_mul_n): more
-// hides the dependent-multiply-add wait states, fewer keeps register pressure down.  The
-// fused kernel holds three table pointers and the slice row on top of the strided
-// kernels' state, and two chains there spill to scratch memory.
-constexpr int chains_for(Mode m) { return m == Mode::Fused ? 1 : 2; }
+// Products computed together (interleaved multiply-add chains, shoup_mul_n).  One chain
+// issues as fast as two at four waves per SIMD now that a column is one asm block, and
+// it leaves the registers for loading table entries ahead.
+constexpr int chains_for(Mode) { return 1; }
+
+// Table loads one product ahead (two_passes) where the registers allow it without
+// spills: the forward batches, whose top passes read one table entry per butterfly.
+constexpr bool prefetch_for(Mode m) { return m == Mode::FwdStrided || m == Mode::HeadBitrev; }
 
 // Butterflies of a pass whose twiddle is 1: bit b of the mask for butterfly b.
 template <unsigned MASK>
@@ -107,15 +110,38 @@ constexpr int nth_nontrivial(int nb, int k) {
     return 0;
 }
 
+// The table entries of one pass's butterflies whose twiddle is not 1 (bit b of TRIV set:
+// butterfly b has twiddle 1), in butterfly order.
+template <int R, unsigned TRIV>
+struct PassTw {
+    static constexpr int NB = 1 << (R - 1);
+    static constexpr int NT = count_nontrivial<TRIV>(NB);
+    Tw29 w[NT > 0 ? NT : 1];
+};
+
+// Loads entries J0 .. J1-1 of one pass: butterfly b's entry is tw[idx(b)].
+template <int J0, int J1, int R, unsigned TRIV, typename IdxF>
+__device__ __forceinline__ void fetch_pass(PassTw<R, TRIV>& pw, const Tw29* tw, IdxF&& idx) {
+    constexpr int hi = J1 < PassTw<R, TRIV>::NT ? J1 : PassTw<R, TRIV>::NT;
+    if constexpr (J0 < hi) {
+        static_for<hi - J0>([&](auto j_c) {
+            constexpr int j = J0 + decltype(j_c)::value;
+            constexpr int b = nth_nontrivial<TRIV>(PassTw<R, TRIV>::NB, j);
+            pw.w[j] = ld_tw(tw + idx(std::integral_constant<int, b>{}));
+        });
+    }
+}
+
 // One pass of a group on x[OFF .. OFF + 2^R): the 2^(R-1) butterflies x_lo, x_hi <-
 // x_lo + t, x_lo - t with t = w x_hi, the products computed CH at a time
 // (shoup_mul_n).  Butterfly b has lower element q(b) (b with a zero inserted at bit U)
-// and twiddle index idx(b).  Butterflies in TRIV have twiddle 1 and take t = x_hi; they
+// and its entry in pw (LAZY: loaded here, from tw[idx(b)], just before its product).  Butterflies in TRIV have twiddle 1 and take t = x_hi; they
 // occur only where x_hi is fresh (canonical, a product output, or the sum or difference
 // of two such in the second pass of a batch's first group), which keeps every digit
 // inside 32 bits.
-template <int OFF, int R, int U, unsigned TRIV, int CH, int E, typename IdxF>
-__device__ __forceinline__ void ct_pass(V29 (&x)[E], const Tw29* tw, IdxF&& idx) {
+template <int OFF, int R, int U, unsigned TRIV, int CH, bool LAZY, int E, typename IdxF>
+__device__ __forceinline__ void ct_pass(V29 (&x)[E], const PassTw<R, TRIV>& pw, const Tw29* tw,
+                                        IdxF&& idx) {
     constexpr int NB = 1 << (R - 1);
     constexpr int NT = count_nontrivial<TRIV>(NB);
     auto lower = [](int b) { return ((b >> U) << (U + 1)) | (b & ((1 << U) - 1)); };
@@ -134,7 +160,8 @@ __device__ __forceinline__ void ct_pass(V29 (&x)[E], const Tw29* tw, IdxF&& idx)
             constexpr int j = decltype(j_c)::value;
             constexpr int b = nth_nontrivial<TRIV>(NB, c0 + j);
             h[j] = x[OFF + lower(b) + (1 << U)];
-            w[j] = ld_tw(tw + idx(std::integral_constant<int, b>{}));
+            if constexpr (LAZY) w[j] = ld_tw(tw + idx(std::integral_constant<int, b>{}));
+            else w[j] = pw.w[c0 + j];
         });
         shoup_mul_n<nc>(h, w, y);
         static_for<nc>([&](auto j_c) {
@@ -150,73 +177,103 @@ __device__ __forceinline__ void ct_pass(V29 (&x)[E], const Tw29* tw, IdxF&& idx)
     });
 }
 
+// Two passes (or one) of a group, with the table loads one product ahead: the first
+// pass's entries (its butterflies share one entry in both orders) and the second pass's
+// first entry are loaded before the normalization and the first pass, the second pass's
+// other entry before the second pass.  At most two entries are live at a time, which
+// keeps four waves per SIMD without spills; the scheduling barriers keep the compiler
+// from sinking the loads to their uses.  NORM: the elements that are "lo" in the first
+// pass (bits of LO0) are normalized first.  Without PF each entry is loaded just before
+// its product, which needs fewer registers.
+template <int OFF, int R, int U0, int U1, unsigned T0, unsigned T1, bool NORM, unsigned LO0,
+          int CH, bool PF, int E, typename Idx0, typename Idx1>
+__device__ __forceinline__ void two_passes(V29 (&x)[E], const Tw29* tw, Idx0&& idx0,
+                                           Idx1&& idx1) {
+    PassTw<R, T0> pw0;
+    PassTw<R, T1> pw1;
+    if constexpr (PF) {
+        fetch_pass<0, 2>(pw0, tw, idx0);
+        if constexpr (R == 2) fetch_pass<0, 1>(pw1, tw, idx1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (NORM) {
+        static_for<(1 << R)>([&](auto q_c) {
+            constexpr int q = decltype(q_c)::value;
+            if constexpr ((LO0 >> q) & 1u) x[OFF + q] = fr29_normalize(x[OFF + q]);
+        });
+    }
+    ct_pass<OFF, R, U0, T0, CH, !PF>(x, pw0, tw, idx0);
+    if constexpr (R == 2) {
+        if constexpr (PF) {
+            fetch_pass<1, 2>(pw1, tw, idx1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        ct_pass<OFF, R, U1, T1, CH, !PF>(x, pw1, tw, idx1);
+    }
+}
+
 // The R forward-order passes of one group on x[OFF .. OFF + 2^R): pass u flips local
 // bit B0 + u (global bit s0 + B0 + u); the pair (q, q + 2^u) has local index bits below
 // the pass equal to (c mod 2^B0) + (q mod 2^u) 2^B0.  Global bit 0 has twiddle 1.
-template <int OFF, int R, int B0, bool NORM, bool CONTIG, int CH, int E>
+template <int OFF, int R, int B0, bool NORM, bool CONTIG, int CH, bool PF, int E>
 __device__ __forceinline__ void group_fwd(V29 (&x)[E], uint32_t c, uint32_t low, uint32_t s0,
                                           uint32_t log_n, const Tw29* tw) {
     const uint32_t cl = c & ((1u << B0) - 1u);
-    if constexpr (NORM) {  // the lo elements of the first pass (u = 0): even q
-        static_for<(1 << (R - 1))>([&](auto b_c) {
-            constexpr int q = 2 * decltype(b_c)::value;
-            x[OFF + q] = fr29_normalize(x[OFF + q]);
-        });
-    }
-    static_for<R>([&](auto u_c) {
+    auto idx_for = [&](auto u_c) {
         constexpr int u = decltype(u_c)::value;
-        const uint32_t t = (uint32_t)(B0 + u);
-        auto idx = [&](auto b_c) {
+        return [&](auto b_c) {
             constexpr int m = decltype(b_c)::value & ((1 << u) - 1);
-            return fwd_tw_index(log_n, s0, t, low, cl + ((uint32_t)m << B0));
+            return fwd_tw_index(log_n, s0, (uint32_t)(B0 + u), low, cl + ((uint32_t)m << B0));
         };
-        // First group of a contiguous batch (s0 = 0): bit 0 has twiddle 1 throughout,
-        // bit 1 for the pairs with m = 0 (even b); the latter only in a two-pass group, the
-        // growth of a third pass would no longer fit in 32 bits.
-        constexpr unsigned all = (1u << (1 << (R - 1))) - 1u;
-        constexpr unsigned triv = (CONTIG && B0 == 0 && u == 0) ? all
-                                : (CONTIG && B0 == 0 && u == 1 && R == 2) ? (0x55555555u & all)
-                                                                          : 0u;
-        ct_pass<OFF, R, u, triv, CH>(x, tw, idx);
-    });
+    };
+    // First group of a contiguous batch (s0 = 0): bit 0 has twiddle 1 throughout, bit 1
+    // for the pairs with m = 0 (even b); the latter only in a two-pass group, the growth
+    // of a third pass would no longer fit in 32 bits.
+    constexpr unsigned all = (1u << (1 << (R - 1))) - 1u;
+    constexpr unsigned t0 = (CONTIG && B0 == 0) ? all : 0u;
+    constexpr unsigned t1 = (CONTIG && B0 == 0 && R == 2) ? (0x55555555u & all) : 0u;
+    // the lo elements of the first pass (u = 0): even q
+    two_passes<OFF, R, 0, 1, t0, t1, NORM, 0x55555555u, CH, PF>(
+        x, tw, idx_for(std::integral_constant<int, 0>{}),
+        idx_for(std::integral_constant<int, (R == 2 ? 1 : 0)>{}));
 }
 
 // The R inverse-order passes of one group, u = R-1 down to 0: the pair (q, q + 2^u) has
 // local bits above the pass a = (q >> (u+1)) + (c >> B0) 2^(R-1-u) and slice row h.
 // The pass on the transform's top bit (only in the top batch) has twiddle 1 throughout.
-template <int OFF, int R, int B0, int K, bool NORM, int CH, int E>
+template <int OFF, int R, int B0, int K, bool NORM, int CH, bool PF, int E>
 __device__ __forceinline__ void group_inv(V29 (&x)[E], uint32_t c, uint32_t h, uint32_t s0,
                                           uint32_t log_n, const Tw29* tw) {
     const uint32_t ch = c >> B0;
-    if constexpr (NORM) {  // the lo elements of the first pass (u = R - 1): q < 2^(R-1)
-        static_for<(1 << (R - 1))>([&](auto b_c) {
-            constexpr int q = decltype(b_c)::value;
-            x[OFF + q] = fr29_normalize(x[OFF + q]);
-        });
-    }
-    const bool top_batch = s0 + (uint32_t)K == log_n;
-    static_for<R>([&](auto uu_c) {
-        constexpr int u = R - 1 - decltype(uu_c)::value;
-        const uint32_t t = (uint32_t)(B0 + u);
-        auto idx = [&](auto b_c) {
+    auto idx_for = [&](auto u_c) {
+        constexpr int u = decltype(u_c)::value;
+        return [&](auto b_c) {
             constexpr int m = decltype(b_c)::value >> u;  // = q >> (u + 1)
             const uint32_t a = (uint32_t)m + (ch << (R - 1 - u));
-            return inv_tw_index(log_n, s0, (uint32_t)K, t, a, h);
+            return inv_tw_index(log_n, s0, (uint32_t)K, (uint32_t)(B0 + u), a, h);
         };
-        // Top group of the top batch (ch = 0 and h = 0 there): the transform's top bit has
-        // twiddle 1 throughout, the next bit for the pairs with q >> (u + 1) = 0 (only in a
-        // two-pass group, as in group_fwd).
-        constexpr unsigned all = (1u << (1 << (R - 1))) - 1u;
-        constexpr bool top_group = B0 + R == K;
-        constexpr unsigned triv = (top_group && u == R - 1) ? all
-                                : (top_group && u == 0 && R == 2) ? 1u : 0u;
-        if constexpr (triv != 0u) {
-            if (top_batch) ct_pass<OFF, R, u, triv, CH>(x, tw, idx);
-            else ct_pass<OFF, R, u, 0u, CH>(x, tw, idx);
-        } else {
-            ct_pass<OFF, R, u, 0u, CH>(x, tw, idx);
-        }
-    });
+    };
+    // Top group of the top batch (ch = 0 and h = 0 there): the transform's top bit has
+    // twiddle 1 throughout, the next bit for the pairs with q >> (u + 1) = 0 (only in a
+    // two-pass group, as in group_fwd).
+    constexpr unsigned all = (1u << (1 << (R - 1))) - 1u;
+    constexpr bool top_group = B0 + R == K;
+    // the lo elements of the first pass (u = R - 1): q < 2^(R-1)
+    constexpr unsigned lo0 = (1u << (1 << (R - 1))) - 1u;
+    auto run = [&](auto triv_c) {
+        constexpr bool tv = decltype(triv_c)::value;
+        constexpr unsigned t0 = tv ? all : 0u;
+        constexpr unsigned t1 = (tv && R == 2) ? 1u : 0u;
+        two_passes<OFF, R, R - 1, 0, t0, t1, NORM, lo0, CH, PF>(
+            x, tw, idx_for(std::integral_constant<int, R - 1>{}),
+            idx_for(std::integral_constant<int, 0>{}));
+    };
+    if constexpr (top_group) {
+        if (s0 + (uint32_t)K == log_n) run(std::true_type{});
+        else run(std::false_type{});
+    } else {
+        run(std::false_type{});
+    }
 }
 
 // Grid: (2^(L-K) / kSpw) slice groups x n_vec vectors, one-dimensional;
@@ -320,10 +377,10 @@ ntt_r8_kernel(BatchParams p) {
         static_for<nsets>([&](auto s_c) {
             constexpr int s = decltype(s_c)::value;
             if constexpr (inv)
-                group_inv<s * (1 << r), r, b0, K, norm, chains_for(M), G::kE>(x, t * nsets + s, lrow, ls0, L,
+                group_inv<s * (1 << r), r, b0, K, norm, chains_for(M), prefetch_for(M), G::kE>(x, t * nsets + s, lrow, ls0, L,
                                                                 tw);
             else
-                group_fwd<s * (1 << r), r, b0, norm, !kStrided, chains_for(M), G::kE>(x, t * nsets + s, llow,
+                group_fwd<s * (1 << r), r, b0, norm, !kStrided, chains_for(M), prefetch_for(M), G::kE>(x, t * nsets + s, llow,
                                                                     ls0, L, tw);
         });
     };

@@ -48,8 +48,14 @@ __device__ __forceinline__ void st_tw(Tw29* p, const Tw29& t) {
     q[4] = make_uint4(t.wp[7], t.wp[8], 0u, 0u);
 }
 
+// Twiddle and coset tables, one 80-byte entry per thread (grid-stride loop).
+//   kind 0: forward levels (omega = base); entry positions follow fwd_tw_index, for the
+//           batch plan whose start bits are set in batch_starts (bit 0 always);
+//   kind 2: inverse levels (omega^-1 = base), bit-reversed within each level;
+//   kind 1: coset table, entry p = factor base^bitrev(p).
 __global__ void __launch_bounds__(256) table_kernel(Tw29* out, Fr base, Fr factor,
-                                                    uint64_t count, uint32_t log_n, int kind) {
+                                                    uint64_t count, uint32_t log_n, int kind,
+                                                    uint32_t batch_starts) {
     const uint64_t n = 1ull << log_n;
     for (uint64_t j = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; j < count;
          j += (uint64_t)gridDim.x * blockDim.x) {
@@ -61,6 +67,13 @@ __global__ void __launch_bounds__(256) table_kernel(Tw29* out, Fr base, Fr facto
             uint64_t jj = j - (n - (n >> m));
             const uint32_t bits = log_n - 1u - m;
             if (kind == 2 && bits > 0u) jj = bitrev_bits((uint32_t)jj, bits);
+            if (kind == 0) {
+                // position jm + low 2^t -> exponent low + jm 2^s0 (t = bits - s0)
+                const uint32_t s0 = 31u - __builtin_clz(batch_starts & ((2u << bits) - 1u));
+                const uint32_t t = bits - s0;
+                const uint64_t low = jj >> t, jm = jj & ((1ull << t) - 1ull);
+                jj = low + (jm << s0);
+            }
             v = fr_pow_u64(base, jj << m);
         } else {
             uint64_t e = bitrev_bits((uint32_t)j, log_n);
