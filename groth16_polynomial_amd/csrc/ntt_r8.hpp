@@ -13,8 +13,8 @@
 // LDS layout: five planes (limb pairs 0-1, 2-3, 4-5, 6-7 as 64-bit words, limb 8 as a
 // 32-bit word).  Element e of slice sl sits at slot sl * 2^K + swz(e) (contiguous
 // batches) or swz(e) * spw + sl (strided batches, where adjacent lanes hold adjacent
-// slices), swz(e) = e ^ ((e >> 3) & 7): the XOR spreads the stride-8 pattern of the
-// lowest group over the banks without padding.
+// slices), with a bank-conflict-free remapping swz of the element's low bits (no
+// padding; lds_swz_contig, lds_swz_strided).
 #pragma once
 
 #include <type_traits>
@@ -64,7 +64,19 @@ __device__ __forceinline__ uint32_t insert_bits(uint32_t c, uint32_t q, int b0, 
     return (c & ((1u << b0) - 1u)) | (q << b0) | ((c >> b0) << (b0 + r));
 }
 
-__device__ __forceinline__ uint32_t lds_swz(uint32_t e) { return e ^ ((e >> 3) & 7u); }
+// LDS slot of element e within its slice: e with its low bits remapped by a GF(2)-linear
+// map (a bijection on every batch size of 6..10 passes).  The lanes served in one LDS cycle
+// (the first 16, 32 or 64 of a wave, for 8- and 4-byte accesses on 32 or 64 banks) differ
+// in element bits that depend on the group; the maps are chosen so that for every group of
+// a 10-pass batch those lanes land on distinct banks.  Contiguous batches: low six bits
+// of the slot from element bits 0..7; strided batches (two columns interleaved, the
+// column is slot bit 0): low five bits of swz(e) from element bits 0..6.
+__device__ __forceinline__ uint32_t lds_swz_contig(uint32_t e) {
+    return e ^ (((e >> 4) & 3u) * 5u) ^ (((e >> 6) & 3u) << 4);
+}
+__device__ __forceinline__ uint32_t lds_swz_strided(uint32_t e) {
+    return e ^ ((e >> 2) & 0x1cu) ^ ((e >> 1) & 2u) ^ ((e >> 3) & 1u);
+}
 
 __device__ __forceinline__ void lds_put(uint2* lds, uint32_t plane, uint32_t slot, const V29& x) {
     lds[slot] = make_uint2(x.l[0], x.l[1]);
@@ -110,38 +122,17 @@ constexpr int nth_nontrivial(int nb, int k) {
     return 0;
 }
 
-// The table entries of one pass's butterflies whose twiddle is not 1 (bit b of TRIV set:
-// butterfly b has twiddle 1), in butterfly order.
-template <int R, unsigned TRIV>
-struct PassTw {
-    static constexpr int NB = 1 << (R - 1);
-    static constexpr int NT = count_nontrivial<TRIV>(NB);
-    Tw29 w[NT > 0 ? NT : 1];
-};
-
-// Loads entries J0 .. J1-1 of one pass: butterfly b's entry is tw[idx(b)].
-template <int J0, int J1, int R, unsigned TRIV, typename IdxF>
-__device__ __forceinline__ void fetch_pass(PassTw<R, TRIV>& pw, const Tw29* tw, IdxF&& idx) {
-    constexpr int hi = J1 < PassTw<R, TRIV>::NT ? J1 : PassTw<R, TRIV>::NT;
-    if constexpr (J0 < hi) {
-        static_for<hi - J0>([&](auto j_c) {
-            constexpr int j = J0 + decltype(j_c)::value;
-            constexpr int b = nth_nontrivial<TRIV>(PassTw<R, TRIV>::NB, j);
-            pw.w[j] = ld_tw(tw + idx(std::integral_constant<int, b>{}));
-        });
-    }
-}
-
 // One pass of a group on x[OFF .. OFF + 2^R): the 2^(R-1) butterflies x_lo, x_hi <-
 // x_lo + t, x_lo - t with t = w x_hi, the products computed CH at a time
 // (shoup_mul_n).  Butterfly b has lower element q(b) (b with a zero inserted at bit U)
-// and its entry in pw (LAZY: loaded here, from tw[idx(b)], just before its product).  Butterflies in TRIV have twiddle 1 and take t = x_hi; they
+// and its entry in pw[j] for the j-th butterfly not in TRIV (LAZY: loaded here, from
+// tw[idx(b)], just before its product).  Butterflies in TRIV have twiddle 1 and take t = x_hi; they
 // occur only where x_hi is fresh (canonical, a product output, or the sum or difference
 // of two such in the second pass of a batch's first group), which keeps every digit
 // inside 32 bits.
 template <int OFF, int R, int U, unsigned TRIV, int CH, bool LAZY, int E, typename IdxF>
-__device__ __forceinline__ void ct_pass(V29 (&x)[E], const PassTw<R, TRIV>& pw, const Tw29* tw,
-                                        IdxF&& idx) {
+__device__ __forceinline__ void ct_pass(V29 (&x)[E], const Tw29 (&pw)[1 << (R - 1)],
+                                        const Tw29* tw, IdxF&& idx) {
     constexpr int NB = 1 << (R - 1);
     constexpr int NT = count_nontrivial<TRIV>(NB);
     auto lower = [](int b) { return ((b >> U) << (U + 1)) | (b & ((1 << U) - 1)); };
@@ -161,7 +152,7 @@ __device__ __forceinline__ void ct_pass(V29 (&x)[E], const PassTw<R, TRIV>& pw, 
             constexpr int b = nth_nontrivial<TRIV>(NB, c0 + j);
             h[j] = x[OFF + lower(b) + (1 << U)];
             if constexpr (LAZY) w[j] = ld_tw(tw + idx(std::integral_constant<int, b>{}));
-            else w[j] = pw.w[c0 + j];
+            else w[j] = pw[c0 + j];
         });
         shoup_mul_n<nc>(h, w, y);
         static_for<nc>([&](auto j_c) {
@@ -177,39 +168,62 @@ __device__ __forceinline__ void ct_pass(V29 (&x)[E], const PassTw<R, TRIV>& pw, 
     });
 }
 
-// Two passes (or one) of a group, with the table loads one product ahead: the first
-// pass's entries (its butterflies share one entry in both orders) and the second pass's
-// first entry are loaded before the normalization and the first pass, the second pass's
-// other entry before the second pass.  At most two entries are live at a time, which
-// keeps four waves per SIMD without spills; the scheduling barriers keep the compiler
-// from sinking the loads to their uses.  NORM: the elements that are "lo" in the first
-// pass (bits of LO0) are normalized first.  Without PF each entry is loaded just before
-// its product, which needs fewer registers.
-template <int OFF, int R, int U0, int U1, unsigned T0, unsigned T1, bool NORM, unsigned LO0,
-          int CH, bool PF, int E, typename Idx0, typename Idx1>
-__device__ __forceinline__ void two_passes(V29 (&x)[E], const Tw29* tw, Idx0&& idx0,
-                                           Idx1&& idx1) {
-    PassTw<R, T0> pw0;
-    PassTw<R, T1> pw1;
+// The R passes of a group, in the order u = 0 .. R-1 (forward) or R-1 .. 0 (INV);
+// bit b of TM[u] marks the butterflies of pass u with twiddle 1.  PF: table loads one
+// product ahead: before each pass the rest of its entries and the first entry of the next
+// pass are loaded (the first pass's butterflies share one entry in both orders), behind
+// scheduling barriers that keep the compiler from sinking the loads to their uses.
+// Without PF each entry is loaded just before its product, which needs fewer registers.
+// NORM: the elements that are "lo" in the first pass are normalized first.
+template <int OFF, int R, bool INV, bool NORM, int CH, bool PF, unsigned TM0, unsigned TM1,
+          unsigned TM2, int E, typename IdxFor>
+__device__ __forceinline__ void run_passes(V29 (&x)[E], const Tw29* tw, IdxFor&& idx_for) {
+    constexpr int NB = 1 << (R - 1);
+    constexpr unsigned tm[3] = {TM0, TM1, TM2};
+    Tw29 ent[R][NB];
+    auto fetch = [&](auto s_c, auto j0_c, auto j1_c) {
+        constexpr int s = decltype(s_c)::value;
+        if constexpr (s < R) {
+            constexpr int u = INV ? R - 1 - s : s;
+            constexpr int nt = count_nontrivial<tm[u]>(NB);
+            constexpr int j0 = decltype(j0_c)::value;
+            constexpr int j1 = decltype(j1_c)::value < nt ? decltype(j1_c)::value : nt;
+            if constexpr (j0 < j1) {
+                auto idx = idx_for(std::integral_constant<int, u>{});
+                static_for<j1 - j0>([&](auto j_c) {
+                    constexpr int j = j0 + decltype(j_c)::value;
+                    constexpr int b = nth_nontrivial<tm[u]>(NB, j);
+                    ent[s][j] = ld_tw(tw + idx(std::integral_constant<int, b>{}));
+                });
+            }
+        }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using INB = std::integral_constant<int, NB>;
     if constexpr (PF) {
-        fetch_pass<0, 2>(pw0, tw, idx0);
-        if constexpr (R == 2) fetch_pass<0, 1>(pw1, tw, idx1);
+        fetch(I0{}, I0{}, INB{});
+        fetch(I1{}, I0{}, I1{});
         __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (NORM) {
+        // lo elements of the first pass: bit u0 of q clear
+        constexpr int u0 = INV ? R - 1 : 0;
         static_for<(1 << R)>([&](auto q_c) {
             constexpr int q = decltype(q_c)::value;
-            if constexpr ((LO0 >> q) & 1u) x[OFF + q] = fr29_normalize(x[OFF + q]);
+            if constexpr (((q >> u0) & 1) == 0) x[OFF + q] = fr29_normalize(x[OFF + q]);
         });
     }
-    ct_pass<OFF, R, U0, T0, CH, !PF>(x, pw0, tw, idx0);
-    if constexpr (R == 2) {
-        if constexpr (PF) {
-            fetch_pass<1, 2>(pw1, tw, idx1);
+    static_for<R>([&](auto s_c) {
+        constexpr int s = decltype(s_c)::value;
+        constexpr int u = INV ? R - 1 - s : s;
+        if constexpr (PF && s > 0) {
+            fetch(s_c, I1{}, INB{});
+            fetch(std::integral_constant<int, s + 1>{}, I0{}, I1{});
             __builtin_amdgcn_sched_barrier(0);
         }
-        ct_pass<OFF, R, U1, T1, CH, !PF>(x, pw1, tw, idx1);
-    }
+        ct_pass<OFF, R, u, tm[u], CH, !PF>(x, ent[s], tw, idx_for(std::integral_constant<int, u>{}));
+    });
 }
 
 // The R forward-order passes of one group on x[OFF .. OFF + 2^R): pass u flips local
@@ -232,10 +246,7 @@ __device__ __forceinline__ void group_fwd(V29 (&x)[E], uint32_t c, uint32_t low,
     constexpr unsigned all = (1u << (1 << (R - 1))) - 1u;
     constexpr unsigned t0 = (CONTIG && B0 == 0) ? all : 0u;
     constexpr unsigned t1 = (CONTIG && B0 == 0 && R == 2) ? (0x55555555u & all) : 0u;
-    // the lo elements of the first pass (u = 0): even q
-    two_passes<OFF, R, 0, 1, t0, t1, NORM, 0x55555555u, CH, PF>(
-        x, tw, idx_for(std::integral_constant<int, 0>{}),
-        idx_for(std::integral_constant<int, (R == 2 ? 1 : 0)>{}));
+    run_passes<OFF, R, false, NORM, CH, PF, t0, t1, 0u>(x, tw, idx_for);
 }
 
 // The R inverse-order passes of one group, u = R-1 down to 0: the pair (q, q + 2^u) has
@@ -258,15 +269,12 @@ __device__ __forceinline__ void group_inv(V29 (&x)[E], uint32_t c, uint32_t h, u
     // two-pass group, as in group_fwd).
     constexpr unsigned all = (1u << (1 << (R - 1))) - 1u;
     constexpr bool top_group = B0 + R == K;
-    // the lo elements of the first pass (u = R - 1): q < 2^(R-1)
-    constexpr unsigned lo0 = (1u << (1 << (R - 1))) - 1u;
     auto run = [&](auto triv_c) {
         constexpr bool tv = decltype(triv_c)::value;
-        constexpr unsigned t0 = tv ? all : 0u;
-        constexpr unsigned t1 = (tv && R == 2) ? 1u : 0u;
-        two_passes<OFF, R, R - 1, 0, t0, t1, NORM, lo0, CH, PF>(
-            x, tw, idx_for(std::integral_constant<int, R - 1>{}),
-            idx_for(std::integral_constant<int, 0>{}));
+        constexpr unsigned t_top = tv ? all : 0u;                // pass u = R - 1
+        constexpr unsigned t_0 = (tv && R == 2) ? 1u : 0u;       // pass u = 0 of two
+        run_passes<OFF, R, true, NORM, CH, PF, (R == 1 ? t_top : t_0), (R == 2 ? t_top : 0u),
+                   (R == 3 ? t_top : 0u)>(x, tw, idx_for);
     };
     if constexpr (top_group) {
         if (s0 + (uint32_t)K == log_n) run(std::true_type{});
@@ -313,7 +321,7 @@ ntt_r8_kernel(BatchParams p) {
 
     auto gidx = [&](uint32_t e) -> uint64_t { return slice_base + ((uint64_t)e << s0); };
     auto slot = [&](uint32_t e) -> uint32_t {
-        return kStrided ? lds_swz(e) * G::kSpw + sl : sl * (1u << K) + lds_swz(e);
+        return kStrided ? lds_swz_strided(e) * G::kSpw + sl : sl * (1u << K) + lds_swz_contig(e);
     };
 
     V29 x[G::kE];
