@@ -155,6 +155,16 @@ G16_HD V29 fr29_normalize(const V29& a) {
     [b6] "v"(v[6]), \
     [b7] "v"(v[7]), \
     [b8] "v"(v[8])
+#define G16_BOPS_S(v) \
+    [b0] "s"(v[0]), \
+    [b1] "s"(v[1]), \
+    [b2] "s"(v[2]), \
+    [b3] "s"(v[3]), \
+    [b4] "s"(v[4]), \
+    [b5] "s"(v[5]), \
+    [b6] "s"(v[6]), \
+    [b7] "s"(v[7]), \
+    [b8] "s"(v[8])
 #define G16_QOPS(v) \
     [q0] "v"(v[0]), \
     [q1] "v"(v[1]), \
@@ -177,89 +187,107 @@ G16_HD V29 fr29_normalize(const V29& a) {
     [m8] "s"(mr29_digit(8))
 
 // Column C (8..16) of x b: acc = carry + sum of x_i b_(C-i); column 8 starts from zero.
-template <int C>
-__device__ __forceinline__ void col_q(int64_t& acc, const int32_t (&x)[9], const int32_t (&b)[9]) {
-    if constexpr (C == 8) {
-        asm(G16_X0(0, 8) G16_X(1, 7) G16_X(2, 6) G16_X(3, 5) G16_X(4, 4) G16_X(5, 3) G16_X(6, 2)
-            G16_X(7, 1) G16_X(8, 0)
-            : [acc] "=&v"(acc) : G16_XOPS(x), G16_BOPS(b) : "vcc");
-    } else if constexpr (C == 9) {
-        asm(G16_X(1, 8) G16_X(2, 7) G16_X(3, 6) G16_X(4, 5) G16_X(5, 4) G16_X(6, 3) G16_X(7, 2)
-            G16_X(8, 1)
-            : [acc] "+v"(acc) : G16_XOPS(x), G16_BOPS(b) : "vcc");
-    } else if constexpr (C == 10) {
-        asm(G16_X(2, 8) G16_X(3, 7) G16_X(4, 6) G16_X(5, 5) G16_X(6, 4) G16_X(7, 3) G16_X(8, 2)
-            : [acc] "+v"(acc) : G16_XOPS(x), G16_BOPS(b) : "vcc");
-    } else if constexpr (C == 11) {
-        asm(G16_X(3, 8) G16_X(4, 7) G16_X(5, 6) G16_X(6, 5) G16_X(7, 4) G16_X(8, 3)
-            : [acc] "+v"(acc) : G16_XOPS(x), G16_BOPS(b) : "vcc");
-    } else if constexpr (C == 12) {
-        asm(G16_X(4, 8) G16_X(5, 7) G16_X(6, 6) G16_X(7, 5) G16_X(8, 4)
-            : [acc] "+v"(acc) : G16_XOPS(x), G16_BOPS(b) : "vcc");
-    } else if constexpr (C == 13) {
-        asm(G16_X(5, 8) G16_X(6, 7) G16_X(7, 6) G16_X(8, 5)
-            : [acc] "+v"(acc) : G16_XOPS(x), G16_BOPS(b) : "vcc");
-    } else if constexpr (C == 14) {
-        asm(G16_X(6, 8) G16_X(7, 7) G16_X(8, 6)
-            : [acc] "+v"(acc) : G16_XOPS(x), G16_BOPS(b) : "vcc");
-    } else if constexpr (C == 15) {
-        asm(G16_X(7, 8) G16_X(8, 7)
-            : [acc] "+v"(acc) : G16_XOPS(x), G16_BOPS(b) : "vcc");
-    } else if constexpr (C == 16) {
-        asm(G16_X(8, 8)
-            : [acc] "+v"(acc) : G16_XOPS(x), G16_BOPS(b) : "vcc");
+// BOPS names the constraint set of b (in VGPRs, or in SGPRs for an entry every lane of
+// the wave shares).
+#define G16_COL_Q(BOPS) \
+    if constexpr (C == 8) { \
+        asm(G16_X0(0, 8) G16_X(1, 7) G16_X(2, 6) G16_X(3, 5) G16_X(4, 4) G16_X(5, 3) \
+            G16_X(6, 2) G16_X(7, 1) G16_X(8, 0) \
+            : [acc] "=&v"(acc) : G16_XOPS(x), BOPS(b) : "vcc"); \
+    } else if constexpr (C == 9) { \
+        asm(G16_X(1, 8) G16_X(2, 7) G16_X(3, 6) G16_X(4, 5) G16_X(5, 4) G16_X(6, 3) \
+            G16_X(7, 2) G16_X(8, 1) \
+            : [acc] "+v"(acc) : G16_XOPS(x), BOPS(b) : "vcc"); \
+    } else if constexpr (C == 10) { \
+        asm(G16_X(2, 8) G16_X(3, 7) G16_X(4, 6) G16_X(5, 5) G16_X(6, 4) G16_X(7, 3) \
+            G16_X(8, 2) \
+            : [acc] "+v"(acc) : G16_XOPS(x), BOPS(b) : "vcc"); \
+    } else if constexpr (C == 11) { \
+        asm(G16_X(3, 8) G16_X(4, 7) G16_X(5, 6) G16_X(6, 5) G16_X(7, 4) G16_X(8, 3) \
+            : [acc] "+v"(acc) : G16_XOPS(x), BOPS(b) : "vcc"); \
+    } else if constexpr (C == 12) { \
+        asm(G16_X(4, 8) G16_X(5, 7) G16_X(6, 6) G16_X(7, 5) G16_X(8, 4) \
+            : [acc] "+v"(acc) : G16_XOPS(x), BOPS(b) : "vcc"); \
+    } else if constexpr (C == 13) { \
+        asm(G16_X(5, 8) G16_X(6, 7) G16_X(7, 6) G16_X(8, 5) \
+            : [acc] "+v"(acc) : G16_XOPS(x), BOPS(b) : "vcc"); \
+    } else if constexpr (C == 14) { \
+        asm(G16_X(6, 8) G16_X(7, 7) G16_X(8, 6) \
+            : [acc] "+v"(acc) : G16_XOPS(x), BOPS(b) : "vcc"); \
+    } else if constexpr (C == 15) { \
+        asm(G16_X(7, 8) G16_X(8, 7) \
+            : [acc] "+v"(acc) : G16_XOPS(x), BOPS(b) : "vcc"); \
+    } else if constexpr (C == 16) { \
+        asm(G16_X(8, 8) \
+            : [acc] "+v"(acc) : G16_XOPS(x), BOPS(b) : "vcc"); \
     }
-}
 
 // Column C (0..8) of x b + q (-r): acc = carry + sum of x_i b_(C-i) + q_i (-r)_(C-i);
 // column 0 starts from zero.
-template <int C>
+#define G16_COL_Y(BOPS) \
+    if constexpr (C == 0) { \
+        asm(G16_X0(0, 0) G16_Q(0, 0) \
+            : [acc] "=&v"(acc) \
+            : G16_XOPS(x), BOPS(b), G16_QOPS(q), G16_MOPS : "vcc"); \
+    } else if constexpr (C == 1) { \
+        asm(G16_X(0, 1) G16_Q(0, 1) G16_X(1, 0) G16_Q(1, 0) \
+            : [acc] "+v"(acc) \
+            : G16_XOPS(x), BOPS(b), G16_QOPS(q), G16_MOPS : "vcc"); \
+    } else if constexpr (C == 2) { \
+        asm(G16_X(0, 2) G16_Q(0, 2) G16_X(1, 1) G16_Q(1, 1) G16_X(2, 0) G16_Q(2, 0) \
+            : [acc] "+v"(acc) \
+            : G16_XOPS(x), BOPS(b), G16_QOPS(q), G16_MOPS : "vcc"); \
+    } else if constexpr (C == 3) { \
+        asm(G16_X(0, 3) G16_Q(0, 3) G16_X(1, 2) G16_Q(1, 2) G16_X(2, 1) G16_Q(2, 1) \
+            G16_X(3, 0) G16_Q(3, 0) \
+            : [acc] "+v"(acc) \
+            : G16_XOPS(x), BOPS(b), G16_QOPS(q), G16_MOPS : "vcc"); \
+    } else if constexpr (C == 4) { \
+        asm(G16_X(0, 4) G16_Q(0, 4) G16_X(1, 3) G16_Q(1, 3) G16_X(2, 2) G16_Q(2, 2) \
+            G16_X(3, 1) G16_Q(3, 1) G16_X(4, 0) G16_Q(4, 0) \
+            : [acc] "+v"(acc) \
+            : G16_XOPS(x), BOPS(b), G16_QOPS(q), G16_MOPS : "vcc"); \
+    } else if constexpr (C == 5) { \
+        asm(G16_X(0, 5) G16_Q(0, 5) G16_X(1, 4) G16_Q(1, 4) G16_X(2, 3) G16_Q(2, 3) \
+            G16_X(3, 2) G16_Q(3, 2) G16_X(4, 1) G16_Q(4, 1) G16_X(5, 0) G16_Q(5, 0) \
+            : [acc] "+v"(acc) \
+            : G16_XOPS(x), BOPS(b), G16_QOPS(q), G16_MOPS : "vcc"); \
+    } else if constexpr (C == 6) { \
+        asm(G16_X(0, 6) G16_Q(0, 6) G16_X(1, 5) G16_Q(1, 5) G16_X(2, 4) G16_Q(2, 4) \
+            G16_X(3, 3) G16_Q(3, 3) G16_X(4, 2) G16_Q(4, 2) G16_X(5, 1) G16_Q(5, 1) \
+            G16_X(6, 0) G16_Q(6, 0) \
+            : [acc] "+v"(acc) \
+            : G16_XOPS(x), BOPS(b), G16_QOPS(q), G16_MOPS : "vcc"); \
+    } else if constexpr (C == 7) { \
+        asm(G16_X(0, 7) G16_Q(0, 7) G16_X(1, 6) G16_Q(1, 6) G16_X(2, 5) G16_Q(2, 5) \
+            G16_X(3, 4) G16_Q(3, 4) G16_X(4, 3) G16_Q(4, 3) G16_X(5, 2) G16_Q(5, 2) \
+            G16_X(6, 1) G16_Q(6, 1) G16_X(7, 0) G16_Q(7, 0) \
+            : [acc] "+v"(acc) \
+            : G16_XOPS(x), BOPS(b), G16_QOPS(q), G16_MOPS : "vcc"); \
+    } else if constexpr (C == 8) { \
+        asm(G16_X(0, 8) G16_Q(0, 8) G16_X(1, 7) G16_Q(1, 7) G16_X(2, 6) G16_Q(2, 6) \
+            G16_X(3, 5) G16_Q(3, 5) G16_X(4, 4) G16_Q(4, 4) G16_X(5, 3) G16_Q(5, 3) \
+            G16_X(6, 2) G16_Q(6, 2) G16_X(7, 1) G16_Q(7, 1) G16_X(8, 0) G16_Q(8, 0) \
+            : [acc] "+v"(acc) \
+            : G16_XOPS(x), BOPS(b), G16_QOPS(q), G16_MOPS : "vcc"); \
+    }
+
+template <int C, bool BS>
+__device__ __forceinline__ void col_q(int64_t& acc, const int32_t (&x)[9], const int32_t (&b)[9]) {
+    if constexpr (BS) {
+        G16_COL_Q(G16_BOPS_S)
+    } else {
+        G16_COL_Q(G16_BOPS)
+    }
+}
+
+template <int C, bool BS>
 __device__ __forceinline__ void col_y(int64_t& acc, const int32_t (&x)[9], const int32_t (&b)[9],
                                       const int32_t (&q)[9]) {
-    if constexpr (C == 0) {
-        asm(G16_X0(0, 0) G16_Q(0, 0)
-            : [acc] "=&v"(acc)
-            : G16_XOPS(x), G16_BOPS(b), G16_QOPS(q), G16_MOPS : "vcc");
-    } else if constexpr (C == 1) {
-        asm(G16_X(0, 1) G16_Q(0, 1) G16_X(1, 0) G16_Q(1, 0)
-            : [acc] "+v"(acc)
-            : G16_XOPS(x), G16_BOPS(b), G16_QOPS(q), G16_MOPS : "vcc");
-    } else if constexpr (C == 2) {
-        asm(G16_X(0, 2) G16_Q(0, 2) G16_X(1, 1) G16_Q(1, 1) G16_X(2, 0) G16_Q(2, 0)
-            : [acc] "+v"(acc)
-            : G16_XOPS(x), G16_BOPS(b), G16_QOPS(q), G16_MOPS : "vcc");
-    } else if constexpr (C == 3) {
-        asm(G16_X(0, 3) G16_Q(0, 3) G16_X(1, 2) G16_Q(1, 2) G16_X(2, 1) G16_Q(2, 1) G16_X(3, 0)
-            G16_Q(3, 0)
-            : [acc] "+v"(acc)
-            : G16_XOPS(x), G16_BOPS(b), G16_QOPS(q), G16_MOPS : "vcc");
-    } else if constexpr (C == 4) {
-        asm(G16_X(0, 4) G16_Q(0, 4) G16_X(1, 3) G16_Q(1, 3) G16_X(2, 2) G16_Q(2, 2) G16_X(3, 1)
-            G16_Q(3, 1) G16_X(4, 0) G16_Q(4, 0)
-            : [acc] "+v"(acc)
-            : G16_XOPS(x), G16_BOPS(b), G16_QOPS(q), G16_MOPS : "vcc");
-    } else if constexpr (C == 5) {
-        asm(G16_X(0, 5) G16_Q(0, 5) G16_X(1, 4) G16_Q(1, 4) G16_X(2, 3) G16_Q(2, 3) G16_X(3, 2)
-            G16_Q(3, 2) G16_X(4, 1) G16_Q(4, 1) G16_X(5, 0) G16_Q(5, 0)
-            : [acc] "+v"(acc)
-            : G16_XOPS(x), G16_BOPS(b), G16_QOPS(q), G16_MOPS : "vcc");
-    } else if constexpr (C == 6) {
-        asm(G16_X(0, 6) G16_Q(0, 6) G16_X(1, 5) G16_Q(1, 5) G16_X(2, 4) G16_Q(2, 4) G16_X(3, 3)
-            G16_Q(3, 3) G16_X(4, 2) G16_Q(4, 2) G16_X(5, 1) G16_Q(5, 1) G16_X(6, 0) G16_Q(6, 0)
-            : [acc] "+v"(acc)
-            : G16_XOPS(x), G16_BOPS(b), G16_QOPS(q), G16_MOPS : "vcc");
-    } else if constexpr (C == 7) {
-        asm(G16_X(0, 7) G16_Q(0, 7) G16_X(1, 6) G16_Q(1, 6) G16_X(2, 5) G16_Q(2, 5) G16_X(3, 4)
-            G16_Q(3, 4) G16_X(4, 3) G16_Q(4, 3) G16_X(5, 2) G16_Q(5, 2) G16_X(6, 1) G16_Q(6, 1)
-            G16_X(7, 0) G16_Q(7, 0)
-            : [acc] "+v"(acc)
-            : G16_XOPS(x), G16_BOPS(b), G16_QOPS(q), G16_MOPS : "vcc");
-    } else if constexpr (C == 8) {
-        asm(G16_X(0, 8) G16_Q(0, 8) G16_X(1, 7) G16_Q(1, 7) G16_X(2, 6) G16_Q(2, 6) G16_X(3, 5)
-            G16_Q(3, 5) G16_X(4, 4) G16_Q(4, 4) G16_X(5, 3) G16_Q(5, 3) G16_X(6, 2) G16_Q(6, 2)
-            G16_X(7, 1) G16_Q(7, 1) G16_X(8, 0) G16_Q(8, 0)
-            : [acc] "+v"(acc)
-            : G16_XOPS(x), G16_BOPS(b), G16_QOPS(q), G16_MOPS : "vcc");
+    if constexpr (BS) {
+        G16_COL_Y(G16_BOPS_S)
+    } else {
+        G16_COL_Y(G16_BOPS)
     }
 }
 
@@ -268,6 +296,9 @@ __device__ __forceinline__ void col_y(int64_t& acc, const int32_t (&x)[9], const
 #undef G16_Q
 #undef G16_XOPS
 #undef G16_BOPS
+#undef G16_BOPS_S
+#undef G16_COL_Q
+#undef G16_COL_Y
 #undef G16_QOPS
 #undef G16_MOPS
 #endif
@@ -293,8 +324,9 @@ G16_HD void static_for(F&& f) {
 // q is taken from columns 8..16 of x w' (45 products): the dropped columns 0..7 add less
 // than 2^265 in magnitude, sixteen units of q (2^261), so q is within 17 of
 // x w' / 2^261, and x w - q r lies within (|x|/2^261 + 19) r of zero; |x| < 2^263 keeps
-// that below 23 r.  The N products run as N interleaved chains.
-template <int N>
+// that below 23 r.  The N products run as N interleaved chains.  BS: the entries are the
+// same in every lane of the wave and held in SGPRs (device builds).
+template <int N, bool BS = false>
 G16_HD void shoup_mul_n(const V29 (&x)[N], const Tw29 (&t)[N], V29 (&y)[N]) {
     int32_t q[N][9];
     int64_t acc[N];
@@ -304,7 +336,7 @@ G16_HD void shoup_mul_n(const V29 (&x)[N], const Tw29 (&t)[N], V29 (&y)[N]) {
     static_for<9>([&](auto c_c) {
         constexpr int c = 8 + decltype(c_c)::value;
 #pragma unroll
-        for (int n = 0; n < N; ++n) col_q<c>(acc[n], x[n].l, t[n].wp);
+        for (int n = 0; n < N; ++n) col_q<c, BS>(acc[n], x[n].l, t[n].wp);
 #pragma unroll
         for (int n = 0; n < N; ++n) {
             if (c >= 9) q[n][c - 9] = (int32_t)((uint32_t)acc[n] & kM29);
@@ -318,7 +350,7 @@ G16_HD void shoup_mul_n(const V29 (&x)[N], const Tw29 (&t)[N], V29 (&y)[N]) {
     static_for<9>([&](auto c_c) {
         constexpr int c = decltype(c_c)::value;
 #pragma unroll
-        for (int n = 0; n < N; ++n) col_y<c>(acc[n], x[n].l, t[n].w, q[n]);
+        for (int n = 0; n < N; ++n) col_y<c, BS>(acc[n], x[n].l, t[n].w, q[n]);
 #pragma unroll
         for (int n = 0; n < N; ++n) {
             if (c < 8) {

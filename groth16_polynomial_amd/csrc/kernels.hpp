@@ -102,6 +102,22 @@ __device__ __forceinline__ Tw29 ld_tw(const Tw29* p) {
     return t;
 }
 
+// An entry every lane of the wave needs (idx equal in all lanes, which the caller
+// guarantees): scalar loads into SGPRs, which the product takes as scalar operands and
+// which leave the vector memory path to the lanes' own data.
+__device__ __forceinline__ Tw29 ld_tw_uniform(const Tw29* tab, uint32_t idx) {
+    typedef const __attribute__((address_space(4))) uint32_t* cptr;
+    const uint32_t u = __builtin_amdgcn_readfirstlane(idx);
+    cptr q = (cptr)(tab + u);
+    Tw29 t;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) t.w[k] = (int32_t)q[k];
+#pragma unroll
+    for (int k = 0; k < 9; ++k) t.wp[k] = (int32_t)q[9 + k];
+    t.pad[0] = t.pad[1] = 0;
+    return t;
+}
+
 __device__ __forceinline__ uint32_t bitrev_bits(uint32_t x, uint32_t bits) {
     return __builtin_bitreverse32(x) >> (32u - bits);  // bits in [1, 32]
 }

@@ -126,11 +126,12 @@ constexpr int nth_nontrivial(int nb, int k) {
 // x_lo + t, x_lo - t with t = w x_hi, the products computed CH at a time
 // (shoup_mul_n).  Butterfly b has lower element q(b) (b with a zero inserted at bit U)
 // and its entry in pw[j] for the j-th butterfly not in TRIV (LAZY: loaded here, from
-// tw[idx(b)], just before its product).  Butterflies in TRIV have twiddle 1 and take t = x_hi; they
+// tw[idx(b)], just before its product; UNI: with scalar loads, the index being the same in
+// every lane of the wave).  Butterflies in TRIV have twiddle 1 and take t = x_hi; they
 // occur only where x_hi is fresh (canonical, a product output, or the sum or difference
 // of two such in the second pass of a batch's first group), which keeps every digit
 // inside 32 bits.
-template <int OFF, int R, int U, unsigned TRIV, int CH, bool LAZY, int E, typename IdxF>
+template <int OFF, int R, int U, unsigned TRIV, int CH, bool LAZY, bool UNI, int E, typename IdxF>
 __device__ __forceinline__ void ct_pass(V29 (&x)[E], const Tw29 (&pw)[1 << (R - 1)],
                                         const Tw29* tw, IdxF&& idx) {
     constexpr int NB = 1 << (R - 1);
@@ -151,10 +152,11 @@ __device__ __forceinline__ void ct_pass(V29 (&x)[E], const Tw29 (&pw)[1 << (R - 
             constexpr int j = decltype(j_c)::value;
             constexpr int b = nth_nontrivial<TRIV>(NB, c0 + j);
             h[j] = x[OFF + lower(b) + (1 << U)];
-            if constexpr (LAZY) w[j] = ld_tw(tw + idx(std::integral_constant<int, b>{}));
+            if constexpr (LAZY && UNI) w[j] = ld_tw_uniform(tw, idx(std::integral_constant<int, b>{}));
+            else if constexpr (LAZY) w[j] = ld_tw(tw + idx(std::integral_constant<int, b>{}));
             else w[j] = pw[c0 + j];
         });
-        shoup_mul_n<nc>(h, w, y);
+        shoup_mul_n<nc, LAZY && UNI>(h, w, y);
         static_for<nc>([&](auto j_c) {
             constexpr int j = decltype(j_c)::value;
             t[nth_nontrivial<TRIV>(NB, c0 + j)] = y[j];
@@ -174,9 +176,10 @@ __device__ __forceinline__ void ct_pass(V29 (&x)[E], const Tw29 (&pw)[1 << (R - 
 // pass are loaded (the first pass's butterflies share one entry in both orders), behind
 // scheduling barriers that keep the compiler from sinking the loads to their uses.
 // Without PF each entry is loaded just before its product, which needs fewer registers.
-// NORM: the elements that are "lo" in the first pass are normalized first.
-template <int OFF, int R, bool INV, bool NORM, int CH, bool PF, unsigned TM0, unsigned TM1,
-          unsigned TM2, int E, typename IdxFor>
+// NORM: the elements that are "lo" in the first pass are normalized first.  UNI: every
+// entry of the group is the same in all lanes of the wave (scalar loads; only without PF).
+template <int OFF, int R, bool INV, bool NORM, int CH, bool PF, bool UNI, unsigned TM0,
+          unsigned TM1, unsigned TM2, int E, typename IdxFor>
 __device__ __forceinline__ void run_passes(V29 (&x)[E], const Tw29* tw, IdxFor&& idx_for) {
     constexpr int NB = 1 << (R - 1);
     constexpr unsigned tm[3] = {TM0, TM1, TM2};
@@ -222,7 +225,8 @@ __device__ __forceinline__ void run_passes(V29 (&x)[E], const Tw29* tw, IdxFor&&
             fetch(std::integral_constant<int, s + 1>{}, I0{}, I1{});
             __builtin_amdgcn_sched_barrier(0);
         }
-        ct_pass<OFF, R, u, tm[u], CH, !PF>(x, ent[s], tw, idx_for(std::integral_constant<int, u>{}));
+        ct_pass<OFF, R, u, tm[u], CH, !PF, UNI && !PF>(x, ent[s], tw,
+                                                      idx_for(std::integral_constant<int, u>{}));
     });
 }
 
@@ -246,13 +250,15 @@ __device__ __forceinline__ void group_fwd(V29 (&x)[E], uint32_t c, uint32_t low,
     constexpr unsigned all = (1u << (1 << (R - 1))) - 1u;
     constexpr unsigned t0 = (CONTIG && B0 == 0) ? all : 0u;
     constexpr unsigned t1 = (CONTIG && B0 == 0 && R == 2) ? (0x55555555u & all) : 0u;
-    run_passes<OFF, R, false, NORM, CH, PF, t0, t1, 0u>(x, tw, idx_for);
+    run_passes<OFF, R, false, NORM, CH, PF, false, t0, t1, 0u>(x, tw, idx_for);
 }
 
 // The R inverse-order passes of one group, u = R-1 down to 0: the pair (q, q + 2^u) has
 // local bits above the pass a = (q >> (u+1)) + (c >> B0) 2^(R-1-u) and slice row h.
 // The pass on the transform's top bit (only in the top batch) has twiddle 1 throughout.
-template <int OFF, int R, int B0, int K, bool NORM, int CH, bool PF, int E>
+// LB: the bits of c that differ between the lanes of a wave are bits 0 .. LB-1 (and h is
+// the same in all of them), so for B0 >= LB every entry of the group is wave-uniform.
+template <int OFF, int R, int B0, int K, bool NORM, int CH, bool PF, int LB, int E>
 __device__ __forceinline__ void group_inv(V29 (&x)[E], uint32_t c, uint32_t h, uint32_t s0,
                                           uint32_t log_n, const Tw29* tw) {
     const uint32_t ch = c >> B0;
@@ -273,8 +279,8 @@ __device__ __forceinline__ void group_inv(V29 (&x)[E], uint32_t c, uint32_t h, u
         constexpr bool tv = decltype(triv_c)::value;
         constexpr unsigned t_top = tv ? all : 0u;                // pass u = R - 1
         constexpr unsigned t_0 = (tv && R == 2) ? 1u : 0u;       // pass u = 0 of two
-        run_passes<OFF, R, true, NORM, CH, PF, (R == 1 ? t_top : t_0), (R == 2 ? t_top : 0u),
-                   (R == 3 ? t_top : 0u)>(x, tw, idx_for);
+        run_passes<OFF, R, true, NORM, CH, PF, (B0 >= LB), (R == 1 ? t_top : t_0),
+                   (R == 2 ? t_top : 0u), (R == 3 ? t_top : 0u)>(x, tw, idx_for);
     };
     if constexpr (top_group) {
         if (s0 + (uint32_t)K == log_n) run(std::true_type{});
@@ -318,6 +324,13 @@ ntt_r8_kernel(BatchParams p) {
     const uint32_t low = g & ((1u << s0) - 1u);
     const uint32_t row = g >> s0;
     const uint64_t slice_base = (uint64_t)low + ((uint64_t)row << (s0 + K));
+    // Bits of t that differ between the lanes of one wave, where all lanes of a wave work
+    // on slices of one row (32: never).  Strided: t = tid / spw, so the low 6 - log2(spw)
+    // bits; the spw columns of a workgroup are adjacent and, as 2^s0 >= 64 >= spw in every
+    // strided batch this kernel takes (s0 is at least the first batch's k >= 6), share the
+    // row.  Contiguous: the low 6 bits when a wave holds one slice.
+    constexpr int kLaneBits = kStrided ? 6 - __builtin_ctz(G::kSpw)
+                                       : (G::kThreadsPerSlice >= 64 ? 6 : 32);
 
     auto gidx = [&](uint32_t e) -> uint64_t { return slice_base + ((uint64_t)e << s0); };
     auto slot = [&](uint32_t e) -> uint32_t {
@@ -385,8 +398,8 @@ ntt_r8_kernel(BatchParams p) {
         static_for<nsets>([&](auto s_c) {
             constexpr int s = decltype(s_c)::value;
             if constexpr (inv)
-                group_inv<s * (1 << r), r, b0, K, norm, chains_for(M), prefetch_for(M), G::kE>(x, t * nsets + s, lrow, ls0, L,
-                                                                tw);
+                group_inv<s * (1 << r), r, b0, K, norm, chains_for(M), prefetch_for(M),
+                          kLaneBits, G::kE>(x, t * nsets + s, lrow, ls0, L, tw);
             else
                 group_fwd<s * (1 << r), r, b0, norm, !kStrided, chains_for(M), prefetch_for(M), G::kE>(x, t * nsets + s, llow,
                                                                     ls0, L, tw);

@@ -9,7 +9,9 @@ on the CPU:
   i in 0..C;
 * the first multiply-add of columns 8 (quotient) and 0 (low) starts from zero and its
   accumulator is a write-only, early-clobber operand; every other block reads the
-  carry of the column below through a read-write operand.
+  carry of the column below through a read-write operand;
+* the table digits b come in VGPRs or SGPRs (one constraint set each), and both column
+  functions instantiate the blocks with each set.
 """
 import os
 import re
@@ -21,14 +23,16 @@ HDR = os.path.join(os.path.dirname(__file__), "..", "groth16_polynomial_amd", "c
 
 def _blocks(fn):
     src = open(HDR).read()
-    start = src.index(f"__device__ __forceinline__ void {fn}(")
-    end = src.index("\n}\n", start)
+    macro = {"col_q": "G16_COL_Q", "col_y": "G16_COL_Y"}[fn]
+    start = src.index(f"#define {macro}(BOPS)")
+    end = src.index("\n\n", start)
     body = src[start:end]
     out = {}
     for m in re.finditer(r"constexpr \(C == (\d+)\) \{(.*?)\"vcc\"\);", body, re.S):
         c = int(m.group(1))
         text = m.group(2)
         ops = [(k, int(i), int(j)) for k, i, j in re.findall(r"G16_(X0|X|Q)\((\d+), (\d+)\)", text)]
+        assert "BOPS(b)" in text, c
         acc = re.search(r"\[acc\] \"([=&+v]+)\"", text).group(1)
         out[c] = (ops, acc)
     return out
@@ -39,8 +43,8 @@ def test_macros_are_the_multiply_adds():
     assert '#define G16_X(i, j) "v_mad_i64_i32 %[acc], vcc, %[x" #i "], %[b" #j "], %[acc]' in src
     assert '#define G16_X0(i, j) "v_mad_i64_i32 %[acc], vcc, %[x" #i "], %[b" #j "], 0' in src
     assert '#define G16_Q(i, j) "v_mad_i64_i32 %[acc], vcc, %[q" #i "], %[m" #j "], %[acc]' in src
-    for tag, con, expr in (("x", "v", "v[{k}]"), ("b", "v", "v[{k}]"), ("q", "v", "v[{k}]"),
-                           ("m", "s", "mr29_digit({k})")):
+    for tag, con, expr in (("x", "v", "v[{k}]"), ("b", "v", "v[{k}]"), ("b", "s", "v[{k}]"),
+                           ("q", "v", "v[{k}]"), ("m", "s", "mr29_digit({k})")):
         for k in range(9):
             assert f'[{tag}{k}] "{con}"({expr.format(k=k)})' in src, (tag, k)
 
@@ -81,3 +85,11 @@ def test_product_count(total):
     n = sum(len(ops) for ops, _ in _blocks("col_q").values())
     n += sum(len(ops) for ops, _ in _blocks("col_y").values())
     assert n == total
+
+
+def test_both_operand_sets_instantiated():
+    src = open(HDR).read()
+    for fn, macro in (("col_q", "G16_COL_Q"), ("col_y", "G16_COL_Y")):
+        start = src.index(f"__device__ __forceinline__ void {fn}(")
+        body = src[start:src.index("\n}\n", start)]
+        assert f"{macro}(G16_BOPS_S)" in body and f"{macro}(G16_BOPS)" in body
