@@ -250,7 +250,9 @@ __device__ __forceinline__ void group_fwd(V29 (&x)[E], uint32_t c, uint32_t low,
     constexpr unsigned all = (1u << (1 << (R - 1))) - 1u;
     constexpr unsigned t0 = (CONTIG && B0 == 0) ? all : 0u;
     constexpr unsigned t1 = (CONTIG && B0 == 0 && R == 2) ? (0x55555555u & all) : 0u;
-    run_passes<OFF, R, false, NORM, CH, PF, false, t0, t1, 0u>(x, tw, idx_for);
+    // in the first group of a contiguous batch (B0 = 0, column 0) the entry index depends
+    // on the butterfly only: the same in every lane
+    run_passes<OFF, R, false, NORM, CH, PF, (CONTIG && B0 == 0), t0, t1, 0u>(x, tw, idx_for);
 }
 
 // The R inverse-order passes of one group, u = R-1 down to 0: the pair (q, q + 2^u) has
