@@ -36,9 +36,13 @@ constexpr int kStridedCols = G16_STRIDED_COLS;
 
 constexpr bool strided_mode(Mode m) { return m == Mode::FwdStrided || m == Mode::InvStrided; }
 
+// The head batch (bit-reversed load) pairs its slices the same way: slice g reads input
+// column bitrev(g), so slices g and g + 2^(L-K-1) read adjacent columns.
+constexpr bool interleaved_mode(Mode m) { return strided_mode(m) || m == Mode::HeadBitrev; }
+
 constexpr int slices_per_wg(int k, Mode m) {
     const int base = k >= 10 ? 1 : (1 << (10 - k));
-    return strided_mode(m) && base < kStridedCols ? kStridedCols : base;
+    return interleaved_mode(m) && base < kStridedCols ? kStridedCols : base;
 }
 
 // K passes per batch in groups of GR (the last group may be shorter); each thread
@@ -301,7 +305,9 @@ __global__ void __launch_bounds__((R8GeomFor<K, GR, M>::kThreads), 4)
 ntt_r8_kernel(BatchParams p) {
     using G = R8GeomFor<K, GR, M>;
     extern __shared__ uint2 lds[];
-    constexpr bool kStrided = (M == Mode::FwdStrided || M == Mode::InvStrided);
+    constexpr bool kStrided = strided_mode(M);
+    // lanes interleave the workgroup's slices (strided batches and the head batch)
+    constexpr bool kInterleaved = interleaved_mode(M);
     constexpr int NG = G::kGroups;
 
     const uint32_t s0 = p.s0;
@@ -319,10 +325,14 @@ ntt_r8_kernel(BatchParams p) {
     const Fr* src = p.src[vec];
     Fr* dst = p.dst[vec];
     const uint32_t tid = threadIdx.x;
-    // strided: adjacent lanes take adjacent columns; contiguous: one slice per run of lanes
-    const uint32_t sl = kStrided ? tid % G::kSpw : tid / G::kThreadsPerSlice;
-    const uint32_t t = kStrided ? tid / G::kSpw : tid % G::kThreadsPerSlice;
-    const uint32_t g = wg * G::kSpw + sl;  // global slice number
+    // strided and head: adjacent lanes take adjacent columns; contiguous: one slice per run
+    // of lanes
+    const uint32_t sl = kInterleaved ? tid % G::kSpw : tid / G::kThreadsPerSlice;
+    const uint32_t t = kInterleaved ? tid / G::kSpw : tid % G::kThreadsPerSlice;
+    // global slice number; the head's slices wg + j 2^(L-K) / spw read adjacent input
+    // columns bitrev(slice) (the top bits of the slice are the low bits of its column)
+    const uint32_t g = M == Mode::HeadBitrev ? wg + sl * ((1u << (L - K)) / G::kSpw)
+                                             : wg * G::kSpw + sl;
     const uint32_t low = g & ((1u << s0) - 1u);
     const uint32_t row = g >> s0;
     const uint64_t slice_base = (uint64_t)low + ((uint64_t)row << (s0 + K));
@@ -332,11 +342,11 @@ ntt_r8_kernel(BatchParams p) {
     // strided batch this kernel takes (s0 is at least the first batch's k >= 6), share the
     // row.  Contiguous: the low 6 bits when a wave holds one slice.
     constexpr int kLaneBits = kStrided ? 6 - __builtin_ctz(G::kSpw)
-                                       : (G::kThreadsPerSlice >= 64 ? 6 : 32);
+                              : kInterleaved ? 32 : (G::kThreadsPerSlice >= 64 ? 6 : 32);
 
     auto gidx = [&](uint32_t e) -> uint64_t { return slice_base + ((uint64_t)e << s0); };
     auto slot = [&](uint32_t e) -> uint32_t {
-        return kStrided ? lds_swz_strided(e) * G::kSpw + sl : sl * (1u << K) + lds_swz_contig(e);
+        return kInterleaved ? lds_swz_strided(e) * G::kSpw + sl : sl * (1u << K) + lds_swz_contig(e);
     };
 
     V29 x[G::kE];
