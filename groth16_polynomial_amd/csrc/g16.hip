@@ -114,7 +114,7 @@ void domain_roots(uint32_t log_n, Fr* omega, Fr* shift, Fr* size_inv) {
     *size_inv = g16::fr_inv(g16::fr_to_mont(n));
 }
 
-// The radix-8 kernel takes batches of 6..10 passes with at least one full workgroup
+// The register-group kernel takes batches of 6..10 passes with at least one full workgroup
 // of slices; the radix-2 kernel takes the rest (small domains, other batch sizes).
 template <g16::Mode M, bool J>
 bool try_r8(const g16::BatchParams& p, uint32_t n_vec, hipStream_t stream, int* rc) {

@@ -12,9 +12,9 @@
 //
 // LDS layout: five planes (limb pairs 0-1, 2-3, 4-5, 6-7 as 64-bit words, limb 8 as a
 // 32-bit word).  Element e of slice sl sits at slot sl * 2^K + swz(e) (contiguous
-// batches) or swz(e) * spw + sl (strided batches, where adjacent lanes hold adjacent
-// slices), with a bank-conflict-free remapping swz of the element's low bits (no
-// padding; lds_swz_contig, lds_swz_strided).
+// batches) or swz(e) * spw + sl (strided batches and the head batch, where adjacent lanes
+// hold adjacent slices), with a bank-conflict-free remapping swz of the element's low
+// bits (no padding; lds_swz_contig, lds_swz_strided).
 #pragma once
 
 #include <type_traits>
@@ -25,7 +25,8 @@
 namespace g16 {
 
 // Slices per workgroup.  Contiguous batches: 2^(10-K) slices (36 KiB of LDS).
-// Strided batches: at least kStridedCols adjacent columns, so that the lanes reading one
+// Strided batches and the head batch: at least kStridedCols slices whose data sit in
+// adjacent columns, so that the lanes reading one
 // row of a workgroup's columns read 64 contiguous bytes of the vector instead of 32; at
 // K = 10 that is 72 KiB of LDS and 512 threads, two workgroups per CU (four columns, a
 // whole 128-byte line per row in one 1024-thread workgroup, measured no faster).
@@ -413,8 +414,8 @@ ntt_r8_kernel(BatchParams p) {
                 group_inv<s * (1 << r), r, b0, K, norm, chains_for(M), prefetch_for(M),
                           kLaneBits, G::kE>(x, t * nsets + s, lrow, ls0, L, tw);
             else
-                group_fwd<s * (1 << r), r, b0, norm, !kStrided, chains_for(M), prefetch_for(M), G::kE>(x, t * nsets + s, llow,
-                                                                    ls0, L, tw);
+                group_fwd<s * (1 << r), r, b0, norm, !kStrided, chains_for(M), prefetch_for(M),
+                          G::kE>(x, t * nsets + s, llow, ls0, L, tw);
         });
     };
     using FWD = std::false_type;

@@ -1,4 +1,5 @@
-// Defines and instantiates the radix-8 launchers for one batch size G16_R8_K.
+// Defines and instantiates the launchers of the register-group batch kernel for one
+// batch size G16_R8_K.
 #pragma once
 
 #include "r8_launch.hpp"

@@ -1,5 +1,5 @@
-// Launchers of the radix-8 batch kernel, one translation unit per batch size k
-// (r8_k<k>.hip) so the large unrolled kernels compile in parallel.
+// Launchers of the register-group batch kernel (ntt_r8.hpp), one translation unit per
+// batch size k (r8_k<k>.hip) so the large unrolled kernels compile in parallel.
 #pragma once
 
 #include <hip/hip_runtime.h>
