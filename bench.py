@@ -17,6 +17,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -85,12 +86,22 @@ def stage_list(plan, n_vec=3):
     return out
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and whitespace (what the compiler sees of it, up to
+    string literals, which the kernel sources use only for asm text without '//')."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return re.sub(r"\s+", "", text)
+
+
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code (comments and whitespace ignored), which ties a
+    committed counter summary to the kernels it was measured on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "groth16_polynomial_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(f.encode() + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
