@@ -9,7 +9,14 @@
 //   norm   x[0..8]            -> digits after fr29_normalize
 //   sub    a[0..8] b[0..8]    -> digits of a - b
 //   split  x                  -> digits of a canonical 256-bit value
+//   batch  K inv triv seed x_0 .. x_{2^K-1}
+//                             -> "ok M" or "bad i": one slice of 2^K canonical values run
+//                                through K passes in the transform kernels' schedule (see
+//                                run_batch), checked against the 8 x 32-bit layer; M is
+//                                the largest digit magnitude met
+#include <cstdint>
 #include <cstdio>
+#include <vector>
 #include <iostream>
 #include <sstream>
 #include <string>
@@ -44,6 +51,125 @@ static V29 read_v(std::istream& in) {
 
 static void print_v(const int32_t* l) {
     for (int k = 0; k < 9; ++k) std::printf("%s%d", k ? " " : "", l[k]);
+}
+
+// SplitMix64 (Steele, Lea, Flood 2014): the batch op's random table values.
+static uint64_t splitmix(uint64_t& s) {
+    uint64_t z = (s += 0x9e3779b97f4a7c15ull);
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+    return z ^ (z >> 31);
+}
+
+static Fr random_canonical(uint64_t& s) {
+    for (;;) {
+        Fr x;
+        for (int i = 0; i < 4; ++i) {
+            uint64_t v = splitmix(s);
+            x.w[2 * i] = (uint32_t)v;
+            x.w[2 * i + 1] = (uint32_t)(v >> 32);
+        }
+        x.w[7] &= 0x3fffffffu;
+        Fr d;
+        uint32_t borrow = 0;
+        for (int i = 0; i < 8; ++i) d.w[i] = subb(x.w[i], r_limb(i), borrow);
+        if (borrow) return x;  // x < r
+    }
+}
+
+// Digit-wise a + b or a - b with a check that no digit leaves the int32 range; tracks the
+// largest magnitude met.
+static bool addsub_checked(const V29& a, const V29& b, bool sub, V29& out, int64_t& maxabs) {
+    for (int k = 0; k < 9; ++k) {
+        const int64_t v = sub ? (int64_t)a.l[k] - b.l[k] : (int64_t)a.l[k] + b.l[k];
+        if (v > INT32_MAX || v < INT32_MIN) return false;
+        out.l[k] = (int32_t)v;
+        if ((v < 0 ? -v : v) > maxabs) maxabs = v < 0 ? -v : v;
+    }
+    return true;
+}
+
+// One slice through K passes as the transform kernels run them: register groups of two
+// passes (one for an odd K's last group), forward order (bits 0 up) or inverse order (bits
+// K-1 down, groups from the top); before every group but the first, the elements that are
+// "lo" in the group's first pass are normalized; each butterfly is (lo + t, lo - t) with
+// t = w hi a product by a table entry, or t = hi where the kernels skip twiddle 1 (triv:
+// the first group of a contiguous forward batch: its first pass, and the second pass's
+// pairs with m = 0; the top group of an inverse top batch: its first pass, and the second
+// pass's pair with q >> 1 = 0).  Table values are random (the bounds do not depend on
+// them).  The 8 x 32-bit layer runs the same butterflies as the reference.
+static void run_batch(int K, bool inv, bool triv, uint64_t seed, std::vector<Fr> in) {
+    const int n = 1 << K;
+    std::vector<V29> x(n);
+    std::vector<Fr> ref = in;
+    int64_t maxabs = 0;
+    for (int i = 0; i < n; ++i) x[i] = fr29_from_fr(in[i]);
+    // groups: forward [0,1], [2,3], ...; inverse [K-2,K-1] from the top (lower bit B0)
+    std::vector<int> b0s;
+    for (int b0 = 0; b0 < K; b0 += 2) b0s.push_back(b0);
+    if (inv) std::vector<int>(b0s.rbegin(), b0s.rend()).swap(b0s);
+    bool first_group = true;
+    for (int b0 : b0s) {
+        const int R = (K - b0) < 2 ? (K - b0) : 2;
+        // passes of the group in execution order, as bit numbers
+        std::vector<int> bits;
+        for (int u = 0; u < R; ++u) bits.push_back(b0 + u);
+        if (inv) std::vector<int>(bits.rbegin(), bits.rend()).swap(bits);
+        if (!first_group) {  // normalize the lo elements of the group's first pass
+            for (int i = 0; i < n; ++i)
+                if (!((i >> bits[0]) & 1)) x[i] = fr29_normalize(x[i]);
+        }
+        for (int s = 0; s < R; ++s) {
+            const int b = bits[s];
+            for (int i = 0; i < n; ++i) {
+                if ((i >> b) & 1) continue;
+                const int j = i | (1 << b);
+                // trivial twiddles as in the kernels (only in the group that starts the batch)
+                bool one = false;
+                if (triv && first_group) {
+                    if (!inv) {
+                        const int m = (i >> b0) & ((1 << s) - 1);  // pair index bits below the pass
+                        one = (s == 0) || (R == 2 && s == 1 && m == 0 && b0 == 0);
+                    } else {
+                        const int a = i >> (b + 1);  // pair index bits above the pass
+                        one = (s == 0 && b == K - 1) || (R == 2 && s == 1 && a == 0);
+                    }
+                }
+                V29 t;
+                Fr tref;
+                if (one) {
+                    t = x[j];
+                    tref = ref[j];
+                } else {
+                    const Fr wm = random_canonical(seed);
+                    for (int k = 0; k < 9; ++k) {
+                        const int64_t v = x[j].l[k] < 0 ? -(int64_t)x[j].l[k] : x[j].l[k];
+                        if (v > maxabs) maxabs = v;
+                    }
+                    t = shoup_mul(x[j], tw29_entry(wm));
+                    tref = fr_mul(ref[j], wm);
+                }
+                V29 lo = x[i], hi;
+                if (!addsub_checked(lo, t, false, x[i], maxabs) ||
+                    !addsub_checked(lo, t, true, hi, maxabs)) {
+                    std::printf("bad %d", i);
+                    return;
+                }
+                x[j] = hi;
+                const Fr rl = ref[i];
+                ref[i] = fr_add(rl, tref);
+                ref[j] = fr_sub(rl, tref);
+            }
+        }
+        first_group = false;
+    }
+    for (int i = 0; i < n; ++i) {
+        if (!fr_is_equal(fr29_canon(x[i]), ref[i])) {
+            std::printf("bad %d", i);
+            return;
+        }
+    }
+    std::printf("ok %lld", (long long)maxabs);
 }
 
 int main() {
@@ -88,6 +214,17 @@ int main() {
             std::string h;
             in >> h;
             print_v(fr29_from_fr(parse_fr(h)).l);
+        } else if (op == "batch") {
+            int K, inv, triv;
+            unsigned long long seed;
+            in >> K >> inv >> triv >> seed;
+            std::vector<Fr> xs((size_t)1 << K);
+            for (auto& v : xs) {
+                std::string h;
+                in >> h;
+                v = parse_fr(h);
+            }
+            run_batch(K, inv != 0, triv != 0, seed, xs);
         } else {
             return 2;
         }

@@ -162,3 +162,41 @@ def test_canonical_reduction(driver):
     got = run(driver, [("canon", D(x)) for x in cases])
     for x, line in zip(cases, got):
         assert int(line, 16) == val(x) % R
+
+
+def _batch_inputs(K, kind, rng):
+    n = 1 << K
+    if kind == "max":
+        return [R - 1] * n
+    if kind == "edges":
+        return [EDGE[(i * 5 + (i >> 3)) % len(EDGE)] for i in range(n)]
+    return [rng.randrange(R) for _ in range(n)]
+
+
+@pytest.mark.parametrize("K", [6, 7, 8, 9, 10])
+def test_batch_schedule_stays_in_int32(driver, K):
+    """One slice through K passes in the transform kernels' schedule (two-pass register
+    groups, the first pass's lo elements normalized at each later group, products by
+    table entries, twiddle-1 butterflies where the kernels skip the product), both
+    orders: every digit of every sum and difference stays in int32 and the canonical
+    results equal the 8 x 32-bit layer's.  All inputs r - 1 drive the twiddle-1 sums of
+    sums of a batch's first group to within a few percent of the analysed bound
+    4 (2^29 - 1)."""
+    rng = random.Random(1000 + K)
+    lines = []
+    for inv in (0, 1):
+        for triv in (0, 1):
+            for kind in ("max", "edges", "random"):
+                xs = _batch_inputs(K, kind, rng)
+                lines.append(("batch", [("dec", K), ("dec", inv), ("dec", triv),
+                                        ("dec", rng.randrange(1 << 63))] + [("hex", x) for x in xs]))
+    got = run(driver, lines)
+    assert len(got) == len(lines)
+    worst = 0
+    for line in got:
+        status, value = line.split()
+        assert status == "ok", line
+        worst = max(worst, int(value))
+    assert worst <= 4 * (2**29 - 1)
+    # the bound is nearly reached (the check exercises the worst path)
+    assert worst > 3 * 2**29

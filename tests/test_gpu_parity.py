@@ -302,6 +302,45 @@ def test_degenerate_inputs():
         ctx.release()
 
 
+def _extreme_values(n, phase):
+    """Canonical inputs at the edges of the range: r - 1, r - 2^k, 2^k - 1 and 0/1, laid out so
+    that the first butterflies add and subtract the largest values (the digit and value
+    bounds of the transform passes are worst-case over canonical inputs)."""
+    big = [R - 1, R - 2, R - (1 << 29), R - (1 << 232), (1 << 253) - 1, (1 << 232) - 1,
+           (1 << 29) - 1, 1, 0]
+    return [big[(i * 7 + phase) % len(big)] if (i >> 1) % 3 else R - 1 for i in range(n)]
+
+
+def test_extreme_values():
+    """Transforms and the H pipeline on inputs at the edges of the canonical range, as
+    standard-form values converted on the device, against the oracle."""
+    for log_n in (12, 16):
+        n = 1 << log_n
+        say("extreme values log_n=%d" % log_n)
+        a = synth.ints_to_fr(_extreme_values(n, 0))
+        b = synth.ints_to_fr(_extreme_values(n, 3))
+        ad, bd = gpu_mont(a), gpu_mont(b)
+        am, bm = oracle.to_mont(a), oracle.to_mont(b)
+        same(host(ad), am, "to Montgomery")
+        ctx = g.HContext(log_n)
+        same(host(ctx.ntt_forward(ad)), oracle.ntt_mont(am, log_n), "forward 2^%d" % log_n)
+        same(host(ctx.ntt_inverse(ad)), oracle.ntt_mont(am, log_n, inverse=True),
+             "inverse 2^%d" % log_n)
+        # C = A o B, and C independent of A and B (C not a product: H is then no quotient)
+        for c_is_product in (True, False):
+            if c_is_product:
+                cd = g.fr_mul(ad, bd)
+                cm = oracle.pointwise_mul_mont(am, bm)
+            else:
+                c = synth.ints_to_fr(_extreme_values(n, 5))
+                cd, cm = gpu_mont(c), oracle.to_mont(c)
+            hm, hs = ctx.h_compute(ad, bd, cd)
+            want_m, want_s = oracle.h_pipeline(log_n, am, bm, cm)
+            same(host(hm), want_m, "h_mont 2^%d" % log_n)
+            same(host(hs), want_s, "h_std 2^%d" % log_n)
+        ctx.release()
+
+
 def test_aliasing_and_bad_pointers():
     import torch
     log_n = 8
