@@ -213,6 +213,32 @@ def main():
     ntt_ms = f0.elapsed_time(f1) / args.steps
     ntt_gbfly = (n // 2) * log_n / (ntt_ms / 1e3) / 1e9
 
+    # ---- the CSR gather front end on the 2^18 proving-key shape (its own workload: the
+    # GATHER_CU page's largest key, synthetic rows with its statistics)
+    ma, mb, wit = synth.gather_inputs(4)
+
+    def idx(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.uint32).view(np.int32)).cuda()
+
+    ga = (idx(ma.row_ptr), idx(ma.signal), g.to_mont(g.to_device(ma.value)))
+    gb = (idx(mb.row_ptr), idx(mb.signal), g.to_mont(g.to_device(mb.value)))
+    gw = g.to_mont(g.to_device(wit))
+    grows = len(ma.row_ptr) - 1
+    gouts = [g.empty_fr(grows) for _ in range(3)]
+    for _ in range(3):
+        g.gather_abc(*ga, *gb, gw, *gouts)
+    torch.cuda.synchronize()
+    f0.record(stream)
+    for _ in range(args.steps):
+        g.gather_abc(*ga, *gb, gw, *gouts)
+    f1.record(stream)
+    torch.cuda.synchronize()
+    gather_ms = f0.elapsed_time(f1) / args.steps
+    nnz = ma.nnz + mb.nnz
+    # algorithmic bytes: row pointers, column indices and coefficients of both matrices,
+    # one 32-byte witness read per non-zero, three 32-byte outputs per row
+    gather_bytes = 2 * 4 * (grows + 1) + nnz * (4 + 32 + 32) + 3 * 32 * grows
+
     value = butterflies / (ms_per_step / 1e3) / 1e9
     line = {
         "metric": "Groth16 H-pipeline ms & Fr NTT Gbutterfly/s at n=2^20; achieved HBM GB/s",
@@ -237,6 +263,9 @@ def main():
         "h_pipeline_ms": round(ms_per_step, 5),
         "ntt_forward_ms": round(ntt_ms, 5),
         "ntt_gbutterfly_s": round(ntt_gbfly, 3),
+        "gather_2_18_ms": round(gather_ms, 5),
+        "gather_gnnz_s": round(nnz / (gather_ms / 1e3) / 1e9, 3),
+        "gather_hbm_gbs_algorithmic": round(gather_bytes / (gather_ms / 1e3) / 1e9, 2),
         "hbm_gbs_algorithmic": round(total_bytes / (ms_per_step / 1e3) / 1e9, 2),
         "pipeline_tmad_s": round(total_muls / (ms_per_step / 1e3) / 1e12, 3),
         "pipeline_alu_frac": round(total_muls / (ms_per_step / 1e3) / 1e12 / MAD_PEAK_T, 4),
