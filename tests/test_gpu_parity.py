@@ -264,6 +264,80 @@ def test_h_compute_workload_2_22_sampled():
     ctx.release()
 
 
+def test_ntt_2_24():
+    """Standalone transforms at 2^24 (three batches of 8 passes): forward against the
+    oracle's whole output, inverse by the round trip."""
+    import torch
+    log_n = 24
+    say("ntt 2^24")
+    x = synth.ntt_input(6, log_n)
+    xm = oracle.to_mont(x)
+    ctx = g.HContext(log_n)
+    assert g.batch_plan(log_n) == [8, 8, 8]
+    xd = g.to_device(xm)
+    fwd = ctx.ntt_forward(xd)
+    same(host(fwd), oracle.ntt_mont(xm, log_n), "forward 2^24")
+    assert torch.equal(ctx.ntt_inverse(fwd), xd), "round trip 2^24"
+    ctx.release()
+
+
+def _gpu_canonical(n, seed):
+    """n canonical values drawn on the GPU (torch generator, fixed seed; every 32-bit word
+    uniform, the top word below 2^29, so every value is below 2^253 < r), in Montgomery
+    form.  For the property-only tests at large domains, which compare with no oracle."""
+    import torch
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    w = torch.randint(-2**31, 2**31, (n, 8), dtype=torch.int32, device="cuda", generator=gen)
+    w[:, 7] &= (1 << 29) - 1
+    return g.to_mont(w)
+
+
+def _h_large(log_n, inputs, samples):
+    """H pipeline at a large domain: outputs at `samples` indices by the oracle's
+    barycentric route (0: properties only), then on every output the quotient-degree
+    property (top coefficient of the inverse transform of H is zero) and, on a prefix,
+    the agreement of the two encodings.  inputs: (A, B) in Montgomery form on the GPU."""
+    n = 1 << log_n
+    say("h_compute 2^%d (%d sampled outputs)" % (log_n, samples))
+    ad, bd = inputs
+    cd = g.fr_mul(ad, bd)
+    ctx = g.HContext(log_n)
+    plan = g.batch_plan(log_n)
+    assert len(plan) == 3 and max(plan) - min(plan) <= 1 and plan == sorted(plan, reverse=True)
+    hm, hs = ctx.h_compute(ad, bd, cd)
+    if samples:
+        am, bm = host(ad), host(bd)
+        cm = oracle.pointwise_mul_mont(am, bm)
+        rng = np.random.default_rng(log_n)
+        idx = np.array([n - 1] + sorted(rng.integers(0, n, samples - 1).tolist()), np.uint32)
+        want_m, want_s = oracle.h_at(log_n, am, bm, cm, idx)
+        same(host(hm)[idx], want_m, "h_mont 2^%d sampled" % log_n)
+        same(host(hs)[idx], want_s, "h_std 2^%d sampled" % log_n)
+    same(oracle.to_mont(host(hs[:65536])), host(hm[:65536]), "dual encoding (prefix)")
+    coeffs = ctx.ntt_inverse(hm)
+    assert not host(coeffs[n - 1:]).any(), "quotient degree 2^%d" % log_n
+    ctx.release()
+
+
+def test_h_compute_2_24_sampled():
+    a, b = synth.h_inputs(7, 24)
+    _h_large(24, (gpu_mont(a), gpu_mont(b)), 2)
+
+
+@pytest.mark.parametrize("log_n", [23, 25, 26])
+def test_large_domains_properties(log_n):
+    """2^23, 2^25 and 2^26 (three near-equal batches each): the quotient-degree property
+    on every output, the encodings on a prefix, and the transforms' round trip."""
+    import torch
+    n = 1 << log_n
+    _h_large(log_n, (_gpu_canonical(n, log_n), _gpu_canonical(n, 100 + log_n)), 0)
+    ctx = g.HContext(log_n)
+    x = _gpu_canonical(n, 200 + log_n)
+    assert torch.equal(ctx.ntt_inverse(ctx.ntt_forward(x)), x), "round trip 2^%d" % log_n
+    ctx.release()
+
+
 def test_fused_equals_unfused():
     """The fused join equals coset evaluations materialised one by one and joined by the
     standalone join (the POINTWISE_CU page keeps the unfused join for this check)."""
