@@ -29,6 +29,9 @@ HBM_PEAK_GBS = 8000.0
 MADS_PER_MUL = 136                      # 8-limb CIOS Montgomery product: 2 s^2 + s
 MADS_PER_REDC = 72                      # Montgomery reduction alone: s^2 + s
 FR_BYTES = 32
+# (log n, proofs) of the several-proofs-per-call measurements: small domains, where one
+# call per proof is launch-bound
+BATCH_SHAPES = ((12, 64), (16, 16))
 
 
 def parse():
@@ -239,6 +242,49 @@ def main():
     # one 32-byte witness read per non-zero, three 32-byte outputs per row
     gather_bytes = 2 * 4 * (grows + 1) + nnz * (4 + 32 + 32) + 3 * 32 * grows
 
+    # ---- several proofs per call at small domains, against one call per proof
+    def time_ms(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        f0.record(stream)
+        for _ in range(reps):
+            fn()
+        f1.record(stream)
+        torch.cuda.synchronize()
+        return f0.elapsed_time(f1) / reps
+
+    proof_batches = {}
+    for blog, proofs in BATCH_SHAPES:
+        bn = 1 << blog
+        bctx = g.HContext(blog)
+        pa = torch.cat([g.to_mont(g.to_device(synth.h_inputs(2000 + q, blog)[0]))
+                        for q in range(proofs)])
+        pb = torch.cat([g.to_mont(g.to_device(synth.h_inputs(2000 + q, blog)[1]))
+                        for q in range(proofs)])
+        pc = g.fr_mul(pa, pb)
+        phm, phs = torch.empty_like(pa), torch.empty_like(pa)
+        pscr = g.empty_fr(proofs * bn)
+        batched = time_ms(lambda: bctx.h_compute_batch(pa, pb, pc, phm, phs, pscr),
+                          args.steps)
+
+        def one_by_one():
+            for q in range(proofs):
+                sl = slice(q * bn, (q + 1) * bn)
+                bctx.h_compute(pa[sl], pb[sl], pc[sl], phm[sl], phs[sl])
+
+        single = time_ms(one_by_one, max(1, args.steps // 4))
+        bfly = proofs * 6 * (bn // 2) * blog
+        proof_batches["2^%d_x%d" % (blog, proofs)] = {
+            "batch_ms": round(batched, 5),
+            "batch_gbutterfly_s": round(bfly / (batched / 1e3) / 1e9, 3),
+            "one_call_per_proof_ms": round(single, 5),
+            "one_call_per_proof_gbutterfly_s": round(bfly / (single / 1e3) / 1e9, 3),
+        }
+        bctx.release()
+        del pa, pb, pc, phm, phs, pscr
+    print("[bench] proof batches: %s" % proof_batches, file=sys.stderr, flush=True)
+
     value = butterflies / (ms_per_step / 1e3) / 1e9
     line = {
         "metric": "Groth16 H-pipeline ms & Fr NTT Gbutterfly/s at n=2^20; achieved HBM GB/s",
@@ -266,6 +312,7 @@ def main():
         "gather_2_18_ms": round(gather_ms, 5),
         "gather_gnnz_s": round(nnz / (gather_ms / 1e3) / 1e9, 3),
         "gather_hbm_gbs_algorithmic": round(gather_bytes / (gather_ms / 1e3) / 1e9, 2),
+        "proof_batches": proof_batches,
         "hbm_gbs_algorithmic": round(total_bytes / (ms_per_step / 1e3) / 1e9, 2),
         "pipeline_tmad_s": round(total_muls / (ms_per_step / 1e3) / 1e12, 3),
         "pipeline_alu_frac": round(total_muls / (ms_per_step / 1e3) / 1e12 / MAD_PEAK_T, 4),

@@ -40,6 +40,8 @@ SIGNATURES = {
     "g16_ntt_inverse": (_I, [_P, _P, _P, _P]),
     "g16_coset_eval": (_I, [_P, _P, _P, _P]),
     "g16_h_compute": (_I, [_P, _P, _P, _P, _P, _P, _P]),
+    "g16_h_batch_scratch_bytes": (_SZ, [_U32, _U64]),
+    "g16_h_compute_batch": (_I, [_P, _U64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "g16_h_stage_count": (_I, [_P]),
     "g16_h_stage": (_I, [_P, _U32, _P, _P, _P, _P, _P, _P]),
     "g16_h_join": (_I, [_U64, _P, _P, _P, _P, _P, _P]),
@@ -220,6 +222,25 @@ class HContext:
                "g16_h_compute")
         return h_mont, h_std
 
+    def h_compute_batch(self, a, b, c, h_mont=None, h_std=None, scratch=None, stream=None):
+        """H of P proofs at once: a, b, c hold P vectors of n elements back to back (for
+        instance (P, n, 8) int32); returns (h_mont, h_std) of the same shape as a."""
+        total = n_elements(a)
+        if total % self.n:
+            raise ValueError("a holds %d elements, not a whole number of %d-element vectors"
+                             % (total, self.n))
+        proofs = total // self.n
+        h_mont = _torch().empty_like(a) if h_mont is None else h_mont
+        h_std = _torch().empty_like(a) if h_std is None else h_std
+        need = load().g16_h_batch_scratch_bytes(self.log_n, proofs)
+        if scratch is None:
+            scratch = empty_fr(max(need // 32, 1), a.device)
+        sbytes = scratch.numel() * scratch.element_size()
+        _check(load().g16_h_compute_batch(
+            self.handle, proofs, _ptr(a, total, "a"), _ptr(b, total, "b"),
+            _ptr(c, total, "c"), _ptr(h_mont, total, "h_mont"), _ptr(h_std, total, "h_std"),
+            _ptr(scratch, None, "scratch"), sbytes, _stream(stream)), "g16_h_compute_batch")
+        return h_mont, h_std
 
     def stage_count(self) -> int:
         rc = load().g16_h_stage_count(self.handle)

@@ -161,6 +161,7 @@ g16::BatchParams base_params(const g16_ctx* c) {
     g16::BatchParams p;
     std::memset(&p, 0, sizeof p);
     p.log_n = c->log_n;
+    p.n_kind = 1;
     return p;
 }
 
@@ -242,24 +243,28 @@ int exec_launch(const Launch& l, hipStream_t s) {
     }
 }
 
-// The launches of stages 1-3 for n_vec vectors srcs[v] -> coset evaluations in dsts[v]
+// The launches of stages 1-3 for n_kind vectors srcs[v] -> coset evaluations in dsts[v]
+// of each of n_proof proofs, proof q's vectors vstride elements after proof q - 1's
 // (dsts may equal srcs only when the context has a single batch).  With join, the last
-// vector's final batch writes H = dsts[0] * dsts[1] - x into h_mont / h_std instead,
-// in a launch of its own after the other vectors are finished.
-uint32_t plan_coset(const g16_ctx* c, const Fr* const* srcs, Fr* const* dsts, uint32_t n_vec,
-                    bool join, Fr* h_mont, Fr* h_std, Launch* out) {
+// kind's final batch writes H = dsts[0] * dsts[1] - x into h_mont / h_std instead, in a
+// launch of its own after the other vectors are finished.
+uint32_t plan_coset(const g16_ctx* c, const Fr* const* srcs, Fr* const* dsts, uint32_t n_kind,
+                    uint32_t n_proof, uint64_t vstride, bool join, Fr* h_mont, Fr* h_std,
+                    Launch* out) {
     const uint32_t nb = c->n_batches;
-    const uint32_t plain_vec = join ? n_vec - 1 : n_vec;
+    const uint32_t plain_kind = join ? n_kind - 1 : n_kind;
     uint32_t count = 0;
-    auto add = [&](g16::Mode m, bool j, const g16::BatchParams& p, uint32_t nv) {
+    auto add = [&](g16::Mode m, bool j, g16::BatchParams p, uint32_t kinds) {
+        p.n_kind = kinds;
+        p.vstride = vstride;
         out[count].mode = m;
         out[count].join = j;
         out[count].p = p;
-        out[count].n_vec = nv;
+        out[count].n_vec = kinds * n_proof;
         ++count;
     };
     auto joined = [&](g16::BatchParams p) {
-        p.src[0] = (nb == 1) ? srcs[n_vec - 1] : dsts[n_vec - 1];
+        p.src[0] = (nb == 1) ? srcs[n_kind - 1] : dsts[n_kind - 1];
         p.src[1] = p.src[2] = nullptr;
         p.dst[0] = p.dst[1] = p.dst[2] = nullptr;
         p.join_a = dsts[0];
@@ -274,11 +279,11 @@ uint32_t plan_coset(const g16_ctx* c, const Fr* const* srcs, Fr* const* dsts, ui
         p.tw = c->tw_inv;
         p.s0 = batch_s0(c, b);
         p.k = c->batch_k[b];
-        for (uint32_t v = 0; v < n_vec; ++v) {
+        for (uint32_t v = 0; v < n_kind; ++v) {
             p.src[v] = (b == nb - 1) ? srcs[v] : dsts[v];
             p.dst[v] = dsts[v];
         }
-        add(g16::Mode::InvStrided, false, p, n_vec);
+        add(g16::Mode::InvStrided, false, p, n_kind);
     }
     // lowest batch of both transforms with the coset multiply between them
     g16::BatchParams f = base_params(c);
@@ -286,31 +291,31 @@ uint32_t plan_coset(const g16_ctx* c, const Fr* const* srcs, Fr* const* dsts, ui
     f.tw_fwd = c->tw_fwd;
     f.scale = c->coset;
     f.k = c->batch_k[0];
-    for (uint32_t v = 0; v < n_vec; ++v) {
+    for (uint32_t v = 0; v < n_kind; ++v) {
         f.src[v] = (nb == 1) ? srcs[v] : dsts[v];
         f.dst[v] = dsts[v];
     }
     if (nb == 1) {
-        if (plain_vec) add(g16::Mode::Fused, false, f, plain_vec);
+        if (plain_kind) add(g16::Mode::Fused, false, f, plain_kind);
         if (join) add(g16::Mode::Fused, true, joined(f), 1);
         return count;
     }
-    add(g16::Mode::Fused, false, f, n_vec);
+    add(g16::Mode::Fused, false, f, n_kind);
     // forward transform, remaining batches (DIT), low to high
     for (uint32_t b = 1; b < nb; ++b) {
         g16::BatchParams p = base_params(c);
         p.tw = c->tw_fwd;
         p.s0 = batch_s0(c, b);
         p.k = c->batch_k[b];
-        for (uint32_t v = 0; v < n_vec; ++v) {
+        for (uint32_t v = 0; v < n_kind; ++v) {
             p.src[v] = dsts[v];
             p.dst[v] = dsts[v];
         }
         if (b + 1 == nb && join) {
-            if (plain_vec) add(g16::Mode::FwdStrided, false, p, plain_vec);
+            if (plain_kind) add(g16::Mode::FwdStrided, false, p, plain_kind);
             add(g16::Mode::FwdStrided, true, joined(p), 1);
         } else {
-            add(g16::Mode::FwdStrided, false, p, n_vec);
+            add(g16::Mode::FwdStrided, false, p, n_kind);
         }
     }
     return count;
@@ -347,7 +352,7 @@ int plan_h(g16_ctx* ctx, const void* a_mont, const void* b_mont, const void* c_m
     const size_t n = size_t(1) << ctx->log_n;
     const Fr* srcs[3] = {(const Fr*)a_mont, (const Fr*)b_mont, (const Fr*)c_mont};
     Fr* dsts[3] = {ctx->scratch, ctx->scratch + n, ctx->scratch + 2 * n};
-    *count = plan_coset(ctx, srcs, dsts, 3, true, (Fr*)h_mont, (Fr*)h_std, ls);
+    *count = plan_coset(ctx, srcs, dsts, 3, 1, 0, true, (Fr*)h_mont, (Fr*)h_std, ls);
     return G16_OK;
 }
 
@@ -487,11 +492,11 @@ int g16_coset_eval(g16_ctx* ctx, const void* in_mont, void* out_mont, void* stre
     if (ctx->n_batches == 1) {
         // one contiguous kernel: each workgroup reads its whole slice before writing it
         Fr* dst = (Fr*)out_mont;
-        return run_plan(ls, plan_coset(ctx, &src, &dst, 1, false, nullptr, nullptr, ls), s);
+        return run_plan(ls, plan_coset(ctx, &src, &dst, 1, 1, 0, false, nullptr, nullptr, ls), s);
     }
     // inverse batches write scratch first, the last forward batch writes scratch too
     Fr* tmp = ctx->scratch;
-    int rc = run_plan(ls, plan_coset(ctx, &src, &tmp, 1, false, nullptr, nullptr, ls), s);
+    int rc = run_plan(ls, plan_coset(ctx, &src, &tmp, 1, 1, 0, false, nullptr, nullptr, ls), s);
     if (rc) return rc;
     if (hipMemcpyAsync(out_mont, tmp, nbytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
         return G16_EHIP;
@@ -504,6 +509,47 @@ int g16_h_compute(g16_ctx* ctx, const void* a_mont, const void* b_mont, const vo
     uint32_t count = 0;
     int rc = plan_h(ctx, a_mont, b_mont, c_mont, h_mont, h_std, ls, &count);
     if (rc) return rc;
+    return run_plan(ls, count, (hipStream_t)stream);
+}
+
+size_t g16_h_batch_scratch_bytes(uint32_t log_n, uint64_t n_proofs) {
+    if (log_n < G16_MIN_LOG_N || log_n > G16_MAX_LOG_N) return 0;
+    if (n_proofs > G16_MAX_PROOFS || (n_proofs << log_n) > (1ull << 31)) return 0;
+    return (size_t)(n_proofs << log_n) * sizeof(Fr);
+}
+
+int g16_h_compute_batch(g16_ctx* ctx, uint64_t n_proofs, const void* a_mont,
+                        const void* b_mont, const void* c_mont, void* h_mont, void* h_std,
+                        void* scratch, size_t scratch_bytes, void* stream) {
+    if (!ctx_ok(ctx)) return ctx ? G16_ESTATE : G16_EINVAL;
+    if (n_proofs == 0) return G16_OK;
+    if (n_proofs > G16_MAX_PROOFS || (n_proofs << ctx->log_n) > (1ull << 31))
+        return G16_EINVAL;
+    if (!a_mont || !b_mont || !c_mont || !h_mont || !h_std || !scratch) return G16_EINVAL;
+    const size_t bytes = (size_t)(n_proofs << ctx->log_n) * sizeof(Fr);
+    if (scratch_bytes < bytes) return G16_ENOSPACE;
+    const void* ins[3] = {a_mont, b_mont, c_mont};
+    void* outs[3] = {h_mont, h_std, scratch};
+    for (int o = 0; o < 3; ++o) {
+        for (int j = o + 1; j < 3; ++j)
+            if (overlaps(outs[o], bytes, outs[j], bytes)) return G16_EALIAS;
+        for (const void* i : ins)
+            if (overlaps(outs[o], bytes, i, bytes)) return G16_EALIAS;
+        if (overlaps(outs[o], bytes, ctx->ws_begin, ctx->ws_bytes)) return G16_EALIAS;
+        if (!device_pointer(outs[o])) return G16_EINVAL;
+    }
+    for (const void* i : ins) {
+        if (overlaps(i, bytes, ctx->ws_begin, ctx->ws_bytes)) return G16_EALIAS;
+        if (!device_pointer(i)) return G16_EINVAL;
+    }
+    // A' and B' live in h_mont and h_std until the join overwrites them element by
+    // element; C' (only when there is more than one batch) lives in the scratch.
+    const Fr* srcs[3] = {(const Fr*)a_mont, (const Fr*)b_mont, (const Fr*)c_mont};
+    Fr* dsts[3] = {(Fr*)h_mont, (Fr*)h_std, (Fr*)scratch};
+    Launch ls[kMaxLaunches];
+    const uint32_t count = plan_coset(ctx, srcs, dsts, 3, (uint32_t)n_proofs,
+                                      uint64_t(1) << ctx->log_n, true, (Fr*)h_mont,
+                                      (Fr*)h_std, ls);
     return run_plan(ls, count, (hipStream_t)stream);
 }
 

@@ -45,7 +45,10 @@ enum class Mode : int {
 };
 
 struct BatchParams {
-    const Fr* src[3];     // per vector (blockIdx.y)
+    // Vector v of a launch (0 <= v < n_vec) is kind v mod n_kind (A, B, C, or fewer) of
+    // proof v / n_kind; proof q's vectors start q * vstride elements after the pointers
+    // below, and so do its join inputs and outputs.
+    const Fr* src[3];
     Fr* dst[3];
     const Tw29* tw;       // twiddles of this batch's passes (Fused: the inverse table)
     const Tw29* tw_fwd;   // Fused only: the forward table
@@ -61,7 +64,17 @@ struct BatchParams {
     uint32_t log_spw;     // log2 of slices per workgroup (radix-2 kernel)
     uint32_t head_inverse;  // HeadBitrev: the inverse transform (see the head load)
     uint32_t n_vec;       // register-group kernel: number of vectors (grid = groups x n_vec)
+    uint32_t n_kind;      // vectors per proof in this launch, 1..3
+    uint64_t vstride;     // elements from one proof's vectors to the next proof's
 };
+
+// Element offset of vector v's proof, and v's kind (index into src / dst).
+__device__ __forceinline__ uint64_t proof_offset(const BatchParams& p, uint32_t v,
+                                                 uint32_t& kind) {
+    const uint32_t q = v / p.n_kind;
+    kind = v - q * p.n_kind;
+    return (uint64_t)q * p.vstride;
+}
 
 __device__ __forceinline__ Fr ld_global(const Fr* p) {
     const uint4* q = reinterpret_cast<const uint4*>(p);
@@ -171,6 +184,9 @@ __device__ __forceinline__ uint32_t head_index(uint64_t i, uint32_t log_n, uint3
 }
 
 // The H epilogue: h_mont[i] = A'[i] B'[i] - x, h_std[i] = the same without the factor R.
+// i counts from the join pointers, proof offset included.  A' and B' may be stored in
+// h_mont and h_std themselves: element i is read here before it is written, by this
+// thread alone.
 __device__ __forceinline__ void store_h(const BatchParams& p, uint64_t i, const Fr& x) {
     Fr h = fr_sub(fr_mul(ld_global(p.join_a + i), ld_global(p.join_b + i)), x);
     st_global(p.h_mont + i, h);
@@ -225,8 +241,10 @@ __global__ void __launch_bounds__(256) ntt_batch_kernel(BatchParams p) {
     const uint32_t spw = 1u << p.log_spw;
     const uint32_t slice_len = 1u << k;
     const uint32_t total = spw << k;
-    const Fr* src = p.src[blockIdx.y];
-    Fr* dst = p.dst[blockIdx.y];
+    uint32_t kind;
+    const uint64_t off = proof_offset(p, blockIdx.y, kind);
+    const Fr* src = p.src[kind] + off;
+    Fr* dst = p.dst[kind] + off;
     const uint32_t g0 = blockIdx.x << p.log_spw;  // first slice of this workgroup
     const bool strided = (M == Mode::FwdStrided || M == Mode::InvStrided);
 
@@ -279,7 +297,7 @@ __global__ void __launch_bounds__(256) ntt_batch_kernel(BatchParams p) {
         else { sl = e >> k; m = e & (slice_len - 1u); }
         uint64_t i = gindex(sl, m);
         Fr x = ld_lds(sh + ((size_t)sl << k) + m);
-        if (JOIN) store_h(p, i, x);
+        if (JOIN) store_h(p, off + i, x);
         else st_global(dst + i, x);
     }
 }

@@ -322,9 +322,10 @@ ntt_r8_kernel(BatchParams p) {
     uint32_t lin = blockIdx.x;
     if ((gridDim.x & 7u) == 0u) lin = (lin & 7u) * (gridDim.x >> 3) + (lin >> 3);
     const uint32_t wg = lin / nv;
-    const uint32_t vec = lin - wg * nv;
-    const Fr* src = p.src[vec];
-    Fr* dst = p.dst[vec];
+    uint32_t kind;
+    const uint64_t off = proof_offset(p, lin - wg * nv, kind);
+    const Fr* src = p.src[kind] + off;
+    Fr* dst = p.dst[kind] + off;
     const uint32_t tid = threadIdx.x;
     // strided and head: adjacent lanes take adjacent columns; contiguous: one slice per run
     // of lanes
@@ -383,7 +384,7 @@ ntt_r8_kernel(BatchParams p) {
             constexpr int xi = decltype(xi_c)::value;
             const uint64_t i = gidx(e);
             const Fr v = fr29_canon(x[xi]);
-            if constexpr (JOIN) store_h(p, i, v);
+            if constexpr (JOIN) store_h(p, off + i, v);
             else st_global(dst + i, v);
         });
     };

@@ -137,6 +137,25 @@ int g16_coset_eval(g16_ctx* ctx, const void* in_mont, void* out_mont, void* stre
 int g16_h_compute(g16_ctx* ctx, const void* a_mont, const void* b_mont, const void* c_mont,
                   void* h_mont, void* h_std, void* stream);
 
+/* Several proofs over one domain in one call (the same launches as g16_h_compute,
+ * each covering every proof's vectors, so small domains pay the per-launch cost once
+ * per batch rather than once per proof; the NTT_CU page's "BATCHING" section counts
+ * that cost).  a_mont, b_mont, c_mont, h_mont and h_std each hold n_proofs vectors of
+ * n elements back to back: proof q's vector starts at element q * n.  scratch is
+ * caller-owned device memory of at least g16_h_batch_scratch_bytes(log_n, n_proofs)
+ * bytes (n_proofs * n * 32; that function returns 0 for a log_n outside [1, 27] or a
+ * batch over the limits below), whose contents are overwritten.  Results equal
+ * g16_h_compute on each proof.  n_proofs == 0 enqueues nothing and returns G16_OK;
+ * n_proofs > G16_MAX_PROOFS or n_proofs * n > 2^31 is G16_EINVAL.  h_mont, h_std and
+ * scratch must not overlap each other, the inputs or the workspace (G16_EALIAS);
+ * G16_ENOSPACE for a short scratch.  The context's own scratch is not used, so batch
+ * calls on one context may overlap in time when their buffers are distinct. */
+#define G16_MAX_PROOFS 16384u
+size_t g16_h_batch_scratch_bytes(uint32_t log_n, uint64_t n_proofs);
+int g16_h_compute_batch(g16_ctx* ctx, uint64_t n_proofs, const void* a_mont,
+                        const void* b_mont, const void* c_mont, void* h_mont, void* h_std,
+                        void* scratch, size_t scratch_bytes, void* stream);
+
 /* g16_h_compute is a fixed sequence of kernel launches ("stages"): the inverse
  * transform's high batches, the fused lowest batch (end of the inverse, coset
  * multiply, start of the forward transform), the forward transform's high batches,

@@ -52,6 +52,18 @@ def test_workspace_bytes(lib):
         assert binding.workspace_bytes(L) == 3 * rnd(n * 80) + 3 * rnd(n * 32)
 
 
+def test_batch_scratch_bytes(lib):
+    f = lib.g16_h_batch_scratch_bytes
+    assert f(0, 1) == 0 and f(28, 1) == 0            # log_n out of range
+    assert f(12, 0) == 0                             # an empty batch needs nothing
+    assert f(12, 5) == 5 * 4096 * 32
+    assert f(20, 16) == 16 * (1 << 20) * 32
+    assert f(1, 16384) == 16384 * 2 * 32             # the proof-count limit itself
+    assert f(1, 16385) == 0                          # beyond it
+    assert f(27, 16) == 16 * (1 << 27) * 32          # 2^31 elements: the element limit
+    assert f(27, 17) == 0
+
+
 def test_batch_plan_matches_page(lib):
     with open(GOLDEN) as f:
         rows = [list(map(int, l.split())) for l in f if l.strip() and not l.startswith("#")]
@@ -96,6 +108,8 @@ def test_host_side_argument_errors(lib):
     for f in ("g16_ntt_forward", "g16_ntt_inverse", "g16_coset_eval"):
         assert getattr(lib, f)(None, fake, fake, None) == binding.G16_EINVAL
     assert lib.g16_h_compute(None, fake, fake, fake, fake, fake, None) == binding.G16_EINVAL
+    assert lib.g16_h_compute_batch(None, 2, fake, fake, fake, fake, fake, fake, 1 << 20,
+                                   None) == binding.G16_EINVAL
     # h_join: zero length, NULLs, outputs overlapping each other or an input
     assert lib.g16_h_join(0, fake, fake, fake, P(0x200000), P(0x300000), None) == \
         binding.G16_EINVAL

@@ -338,6 +338,80 @@ def test_large_domains_properties(log_n):
     ctx.release()
 
 
+def _batch_case(log_n, proofs, kmax=None, seed=300):
+    """proofs independent proofs stacked back to back through g16_h_compute_batch; every
+    output of every proof against the oracle.  Even proofs use C = A o B, odd ones an
+    independent C."""
+    import torch
+    say("h_compute_batch 2^%d x %d proofs kmax=%s" % (log_n, proofs, kmax))
+    dev, want = ([], [], []), []
+    for q in range(proofs):
+        (ad, bd, cd), (am, bm, cm) = h_inputs(seed + q, log_n, c_is_product=(q % 2 == 0))
+        for lst, t in zip(dev, (ad, bd, cd)):
+            lst.append(t)
+        want.append(oracle.h_pipeline(log_n, am, bm, cm))
+    a, b, c = (torch.cat(lst) for lst in dev)
+    with KMax(kmax):
+        ctx = g.HContext(log_n)
+    hm, hs = ctx.h_compute_batch(a, b, c)
+    n = 1 << log_n
+    hm_h, hs_h = host(hm), host(hs)
+    for q, (want_m, want_s) in enumerate(want):
+        same(hm_h[q * n:(q + 1) * n], want_m, "h_mont 2^%d proof %d" % (log_n, q))
+        same(hs_h[q * n:(q + 1) * n], want_s, "h_std 2^%d proof %d" % (log_n, q))
+    return ctx, (a, b, c), (hm, hs)
+
+
+@pytest.mark.parametrize("log_n,proofs,kmax", [(1, 3, None), (5, 4, None), (9, 2, 4),
+                                               (10, 3, None), (12, 5, None), (13, 3, 4),
+                                               (16, 3, None), (18, 2, None)])
+def test_h_compute_batch(log_n, proofs, kmax):
+    ctx, _, _ = _batch_case(log_n, proofs, kmax)
+    ctx.release()
+
+
+def test_h_compute_batch_workloads():
+    """The batch shapes the benchmark times: 64 proofs at 2^12 and 16 at 2^16, whole
+    outputs."""
+    for log_n, proofs in ((12, 64), (16, 16)):
+        ctx, _, _ = _batch_case(log_n, proofs, seed=1000 + log_n)
+        ctx.release()
+
+
+def test_h_compute_batch_edges():
+    """An empty batch, a smaller batch after a larger one on the same context and
+    scratch, a batch of one equal to g16_h_compute, and the host-side errors."""
+    import torch
+    log_n, n = 12, 1 << 12
+    ctx, (a, b, c), (hm, hs) = _batch_case(log_n, 4, seed=500)
+    scratch = g.empty_fr(4 * n)
+    # smaller batch (proofs 1 and 2) reusing the scratch the larger one left dirty
+    sm, ss = ctx.h_compute_batch(a[n:3 * n], b[n:3 * n], c[n:3 * n], scratch=scratch)
+    same(host(sm), host(hm[n:3 * n]), "second call, fewer proofs (mont)")
+    same(host(ss), host(hs[n:3 * n]), "second call, fewer proofs (std)")
+    # a batch of one is g16_h_compute
+    om, os_ = ctx.h_compute(a[:n], b[:n], c[:n])
+    bm, bs = ctx.h_compute_batch(a[:n], b[:n], c[:n], scratch=scratch)
+    same(host(bm), host(om), "batch of one (mont)")
+    same(host(bs), host(os_), "batch of one (std)")
+    # empty batch: nothing enqueued, no error
+    e = g.empty_fr(0)
+    em, es = ctx.h_compute_batch(e, e, e)
+    assert em.numel() == 0 and es.numel() == 0
+    # short scratch, overlapping buffers, a length that is not whole vectors
+    with pytest.raises(g.G16Error) as ex:
+        ctx.h_compute_batch(a, b, c, scratch=g.empty_fr(4 * n - 1))
+    assert ex.value.code == g.G16_ENOSPACE
+    with pytest.raises(g.G16Error) as ex:
+        ctx.h_compute_batch(a, b, c, h_mont=g.empty_fr(4 * n), h_std=g.empty_fr(4 * n),
+                            scratch=a)
+    assert ex.value.code == g.G16_EALIAS
+    with pytest.raises(ValueError):
+        ctx.h_compute_batch(a[:n + 1], b[:n + 1], c[:n + 1])
+    sync()
+    ctx.release()
+
+
 def test_fused_equals_unfused():
     """The fused join equals coset evaluations materialised one by one and joined by the
     standalone join (the POINTWISE_CU page keeps the unfused join for this check)."""
