@@ -50,6 +50,12 @@ SIGNATURES = {
     "g16_to_mont": (_I, [_U64, _P, _P, _P]),
     "g16_from_mont": (_I, [_U64, _P, _P, _P]),
     "g16_fr_mul": (_I, [_U64, _P, _P, _P, _P]),
+    "g16_msm_g1_window_bits": (_U32, [_U64]),
+    "g16_msm_g1_window_count": (_U32, [_U32]),
+    "g16_msm_g1_workspace_bytes": (_SZ, [_U64, _U32]),
+    "g16_msm_g1": (_I, [_U64, _P, _P, _U32, _P, _SZ, _P, _P]),
+    "g16_msm_g1_finish": (_I, [_U32, _P, _P]),
+    "g16_g1_generator_mul": (_I, [_U64, _P, _P, _P]),
 }
 
 _lib = None
@@ -317,3 +323,76 @@ def from_mont(x, out=None, stream=None):
 
 def fr_mul(a, b, out=None, stream=None):
     return _elementwise("g16_fr_mul", a, out, stream, y=b)
+
+
+# ------------------------------------------------------------------ G1 MSM
+
+G1_AFF_BYTES = 64
+G1_XYZZ_BYTES = 128
+
+
+def msm_window_bits(n: int) -> int:
+    return load().g16_msm_g1_window_bits(n)
+
+
+def msm_window_count(c: int) -> int:
+    return load().g16_msm_g1_window_count(c)
+
+
+def msm_workspace_bytes(n: int, c: int = 0) -> int:
+    return load().g16_msm_g1_workspace_bytes(n, c)
+
+
+def g1_generator_mul(scalars, out=None, stream=None):
+    """k_i G for 32-byte scalars on the GPU: affine bases, (n, 16) int32, Montgomery form."""
+    n = n_elements(scalars)
+    torch = _torch()
+    out = torch.empty((n, 16), dtype=torch.int32, device=scalars.device) if out is None else out
+    if out.numel() * out.element_size() != n * G1_AFF_BYTES:
+        raise ValueError("out must hold %d affine points" % n)
+    _check(load().g16_g1_generator_mul(n, _ptr(scalars, n, "scalars"), out.data_ptr(),
+                                       _stream(stream)), "g16_g1_generator_mul")
+    return out
+
+
+class MsmG1:
+    """Workspace for G1 MSMs of up to n terms with window width c (0: the default)."""
+
+    def __init__(self, n: int, c: int = 0, device=None):
+        torch = _torch()
+        self.n = n
+        self.c = c or msm_window_bits(n)
+        self.windows = msm_window_count(self.c)
+        nbytes = msm_workspace_bytes(n, self.c) if n else 0
+        if n and nbytes == 0:
+            raise G16Error(G16_EINVAL, "g16_msm_g1_workspace_bytes")
+        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8,
+                                     device=device or "cuda")
+        self.sums = torch.empty((self.windows, 32), dtype=torch.int32, device=device or "cuda")
+
+    def window_sums(self, scalars, bases, stream=None):
+        """Enqueue the MSM; returns the (windows, 32) int32 XYZZ window sums on the GPU."""
+        n = n_elements(scalars)
+        if n > self.n:
+            raise ValueError("%d terms, workspace for %d" % (n, self.n))
+        if bases.numel() * bases.element_size() != n * G1_AFF_BYTES:
+            raise ValueError("bases must hold %d affine points" % n)
+        ws = self.workspace
+        _check(load().g16_msm_g1(n, scalars.data_ptr() if n else None,
+                                 bases.data_ptr() if n else None, self.c,
+                                 ws.data_ptr(), ws.numel(), self.sums.data_ptr(),
+                                 _stream(stream)), "g16_msm_g1")
+        return self.sums
+
+    def finish(self, sums_host: np.ndarray) -> np.ndarray:
+        """Host combination of the window sums: (16,) uint32 affine result, standard form."""
+        s = np.ascontiguousarray(sums_host, dtype=np.uint32).reshape(self.windows, 32)
+        out = np.zeros(16, np.uint32)
+        _check(load().g16_msm_g1_finish(self.c, s.ctypes.data, out.ctypes.data),
+               "g16_msm_g1_finish")
+        return out
+
+    def __call__(self, scalars, bases, stream=None) -> np.ndarray:
+        """The whole MSM (synchronises the stream to read the window sums back)."""
+        sums = self.window_sums(scalars, bases, stream)
+        return self.finish(to_host(sums).reshape(self.windows, 32))

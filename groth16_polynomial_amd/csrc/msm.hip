@@ -1,0 +1,211 @@
+// libg16.so: host side of the G1 multi-scalar multiplication (include/g16.h, "G1 MSM").
+//
+// g16_msm_g1 only enqueues (counting sort, accumulation, merge, window reduction) and
+// leaves one XYZZ point per window in the caller's buffer; g16_msm_g1_finish combines
+// them on the host by Horner's rule, as the MSM_CU page does ("THE WINDOW REDUCTION
+// ENDS ON THE HOST").
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "g16.h"
+#include "msm_kernels.hpp"
+
+using g16::G1Aff;
+using g16::G1Xyzz;
+using g16::MsmParams;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr uint32_t kMaxC = 24;
+constexpr uint32_t kSliceLen = 32;
+constexpr uint32_t kSegLen = 8;
+constexpr uint32_t kMaxOnesGroups = 64;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+uint32_t windows_for(uint32_t c) { return (255u + c - 1u) / c; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return na && nb && x < y + nb && y < x + na;
+}
+
+bool device_pointer(const void* p) {
+    if (!p) return false;
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged ||
+           attr.type == hipMemoryTypeUnified;
+}
+
+// Window width minimising the point additions: n per window for the accumulation, and
+// about three per bucket for the merge and the weighted window sum.
+uint32_t default_c(uint64_t n) {
+    uint32_t best = 1;
+    double best_cost = 0.0;
+    for (uint32_t c = 1; c <= 20; ++c) {
+        const double cost = (double)windows_for(c) * ((double)n + 3.0 * (double)(1u << (c - 1)));
+        if (c == 1 || cost < best_cost) {
+            best = c;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
+struct Layout {
+    MsmParams mp;
+    size_t counts, cursor, entries, spill_rows, spill_pts, buckets, seg_out, ones_out, total;
+};
+
+bool make_layout(uint64_t n, uint32_t c, Layout* L) {
+    if (c < 1 || c > kMaxC) return false;
+    const uint32_t W = windows_for(c);
+    if (n == 0 || (uint64_t)W * n >= (1ull << 32) || n >= (1ull << 31)) return false;
+    MsmParams& mp = L->mp;
+    std::memset(&mp, 0, sizeof mp);
+    mp.n = (uint32_t)n;
+    mp.c = c;
+    mp.windows = W;
+    mp.buckets = 1u << (c - 1);
+    mp.slice_len = kSliceLen;
+    mp.slices = (uint32_t)((n + kSliceLen - 1) / kSliceLen);
+    mp.seg_len = mp.buckets < kSegLen ? mp.buckets : kSegLen;
+    mp.segs = mp.buckets / mp.seg_len;
+    const uint64_t groups = (n + g16::kMsmThreads - 1) / g16::kMsmThreads;
+    mp.ones_groups = (uint32_t)(groups < kMaxOnesGroups ? groups : kMaxOnesGroups);
+    const size_t rows = (size_t)W * mp.buckets;
+    const size_t spills = 2 * (size_t)W * mp.slices;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += round_up(bytes);
+        return at;
+    };
+    L->counts = take(rows * 4);
+    L->cursor = take(rows * 4);
+    L->entries = take((size_t)W * n * 8);
+    L->spill_rows = take(spills * 4);
+    L->spill_pts = take(spills * sizeof(G1Xyzz));
+    L->buckets = take(rows * sizeof(G1Xyzz));
+    L->seg_out = take((size_t)W * mp.segs * sizeof(G1Xyzz));
+    L->ones_out = take((size_t)mp.ones_groups * sizeof(G1Xyzz));
+    L->total = off;
+    return true;
+}
+
+uint32_t blocks_for(uint64_t threads) {
+    return (uint32_t)((threads + g16::kMsmThreads - 1) / g16::kMsmThreads);
+}
+
+}  // namespace
+
+extern "C" {
+
+uint32_t g16_msm_g1_window_bits(uint64_t n) { return n ? default_c(n) : 1u; }
+
+uint32_t g16_msm_g1_window_count(uint32_t c) {
+    return (c >= 1 && c <= kMaxC) ? windows_for(c) : 0u;
+}
+
+size_t g16_msm_g1_workspace_bytes(uint64_t n, uint32_t c) {
+    if (c == 0) c = g16_msm_g1_window_bits(n);
+    Layout L;
+    if (n == 0) return 0;
+    return make_layout(n, c, &L) ? L.total : 0;
+}
+
+int g16_msm_g1(uint64_t n, const void* scalars_std, const void* bases_mont, uint32_t c,
+               void* workspace, size_t workspace_bytes, void* window_sums, void* stream) {
+    if (c == 0) c = g16_msm_g1_window_bits(n);
+    if (c > kMaxC || !window_sums) return G16_EINVAL;
+    const uint32_t W = windows_for(c);
+    const size_t sums_bytes = (size_t)W * sizeof(G1Xyzz);
+    if (!device_pointer(window_sums)) return G16_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    if (n == 0) {  // the empty sum: every window at infinity
+        const uint32_t words = (uint32_t)(sums_bytes / 4);
+        hipLaunchKernelGGL(g16::msm_fill_u32, dim3(blocks_for(words)), dim3(g16::kMsmThreads), 0,
+                           s, (uint32_t*)window_sums, words, 0u);
+        return hipGetLastError() == hipSuccess ? G16_OK : G16_EHIP;
+    }
+    Layout L;
+    if (!make_layout(n, c, &L)) return G16_EINVAL;
+    if (!scalars_std || !bases_mont || !workspace) return G16_EINVAL;
+    if ((uintptr_t)workspace % kAlign) return G16_EINVAL;
+    if (workspace_bytes < L.total) return G16_ENOSPACE;
+    const size_t sb = n * 32, bb = n * sizeof(G1Aff);
+    if (overlaps(workspace, L.total, scalars_std, sb) || overlaps(workspace, L.total, bases_mont, bb) ||
+        overlaps(window_sums, sums_bytes, scalars_std, sb) ||
+        overlaps(window_sums, sums_bytes, bases_mont, bb) ||
+        overlaps(window_sums, sums_bytes, workspace, L.total))
+        return G16_EALIAS;
+    if (!device_pointer(scalars_std) || !device_pointer(bases_mont) || !device_pointer(workspace))
+        return G16_EINVAL;
+
+    uint8_t* ws = (uint8_t*)workspace;
+    const MsmParams mp = L.mp;
+    uint32_t* counts = (uint32_t*)(ws + L.counts);
+    uint32_t* cursor = (uint32_t*)(ws + L.cursor);
+    uint2* entries = (uint2*)(ws + L.entries);
+    uint32_t* spill_rows = (uint32_t*)(ws + L.spill_rows);
+    G1Xyzz* spill_pts = (G1Xyzz*)(ws + L.spill_pts);
+    G1Xyzz* buckets = (G1Xyzz*)(ws + L.buckets);
+    G1Xyzz* seg_out = (G1Xyzz*)(ws + L.seg_out);
+    G1Xyzz* ones_out = (G1Xyzz*)(ws + L.ones_out);
+    const uint32_t* sc = (const uint32_t*)scalars_std;
+    const G1Aff* bases = (const G1Aff*)bases_mont;
+    const uint32_t rows = W * mp.buckets;
+    const dim3 blk(g16::kMsmThreads);
+
+    hipLaunchKernelGGL(g16::msm_fill_u32, dim3(blocks_for(rows)), blk, 0, s, counts, rows, 0u);
+    hipLaunchKernelGGL(g16::msm_count, dim3(blocks_for(n)), blk, 0, s, sc, mp, counts);
+    hipLaunchKernelGGL(g16::msm_scan, dim3(W), dim3(g16::kMsmScanThreads), 0, s, counts, mp,
+                       cursor);
+    hipLaunchKernelGGL(g16::msm_scatter, dim3(blocks_for(n)), blk, 0, s, sc, mp, cursor, entries);
+    hipLaunchKernelGGL(g16::msm_accumulate, dim3(blocks_for((uint64_t)W * mp.slices)), blk, 0, s,
+                       entries, bases, cursor, mp, buckets, spill_pts, spill_rows);
+    hipLaunchKernelGGL(g16::msm_merge, dim3(blocks_for(rows)), blk, 0, s, counts, cursor,
+                       spill_pts, spill_rows, mp, buckets);
+    hipLaunchKernelGGL(g16::msm_reduce_segments, dim3(blocks_for((uint64_t)W * mp.segs)), blk, 0,
+                       s, counts, buckets, mp, seg_out);
+    hipLaunchKernelGGL(g16::msm_ones, dim3(mp.ones_groups), blk, 0, s, sc, bases, mp, ones_out);
+    hipLaunchKernelGGL(g16::msm_window_sums, dim3(W), blk, 0, s, seg_out, ones_out, mp,
+                       (G1Xyzz*)window_sums);
+    return hipGetLastError() == hipSuccess ? G16_OK : G16_EHIP;
+}
+
+int g16_msm_g1_finish(uint32_t c, const void* window_sums_host, void* out_affine_std) {
+    if (c < 1 || c > kMaxC || !window_sums_host || !out_affine_std) return G16_EINVAL;
+    const uint32_t W = windows_for(c);
+    const G1Xyzz* ws = (const G1Xyzz*)window_sums_host;
+    G1Xyzz acc = ws[W - 1];
+    for (uint32_t w = W - 1; w-- > 0;) {
+        for (uint32_t i = 0; i < c; ++i) acc = g16::xyzz_dbl(acc);
+        acc = g16::xyzz_add(acc, ws[w]);
+    }
+    const G1Aff a = g16::xyzz_to_aff(acc);
+    const g16::Fp x = g16::fp_from_mont(a.x), y = g16::fp_from_mont(a.y);
+    std::memcpy(out_affine_std, x.w, 32);
+    std::memcpy((uint8_t*)out_affine_std + 32, y.w, 32);
+    return G16_OK;
+}
+
+int g16_g1_generator_mul(uint64_t n, const void* scalars_std, void* out_affine_mont,
+                         void* stream) {
+    if (n == 0 || n >= (1ull << 31) || !scalars_std || !out_affine_mont) return G16_EINVAL;
+    if (overlaps(scalars_std, n * 32, out_affine_mont, n * sizeof(G1Aff))) return G16_EALIAS;
+    if (!device_pointer(scalars_std) || !device_pointer(out_affine_mont)) return G16_EINVAL;
+    hipLaunchKernelGGL(g16::g1_generator_mul, dim3(blocks_for(n)), dim3(g16::kMsmThreads), 0,
+                       (hipStream_t)stream, (const uint32_t*)scalars_std, (uint32_t)n,
+                       (G1Aff*)out_affine_mont);
+    return hipGetLastError() == hipSuccess ? G16_OK : G16_EHIP;
+}
+
+}  // extern "C"

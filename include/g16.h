@@ -203,6 +203,55 @@ int g16_from_mont(uint64_t n, const void* in_mont, void* out_std, void* stream);
 int g16_fr_mul(uint64_t n, const void* a_mont, const void* b_mont, void* out_mont,
                void* stream);
 
+/* ---------------------------------------------------------------- G1 MSM
+ *
+ * The multi-scalar multiplication that consumes h_std (the MSM_CU page): the sum over
+ * i < n of k_i P_i on BN254 G1, y^2 = x^3 + 3 over the base field p =
+ * 0x30644e72e131a029b85045b68181585d97816a916871ca8d3c208c16d87cfd47.  Pippenger with
+ * c-bit signed windows (2^(c-1) buckets per window), a counting sort of (window,
+ * bucket) entries, load-balanced bucket accumulation in XYZZ coordinates with affine
+ * bases, scalars 0 skipped and scalars 1 summed apart (the page's header, sections 1-4).
+ *
+ * Layouts.  A scalar is an Fr element in STANDARD form (32 bytes, < r; h_std is one).
+ * A base is an affine point of 64 bytes: x then y, each a 32-byte little-endian
+ * Montgomery-form Fp element (x * 2^256 mod p); (0, 0) stands for the point at infinity.
+ * A window sum is an XYZZ point of 128 bytes: X, Y, ZZ, ZZZ (Montgomery), with
+ * (x, y) = (X/ZZ, Y/ZZZ) and ZZ = 0 for infinity.  The result is affine in STANDARD form,
+ * 64 bytes, (0, 0) for infinity.
+ *
+ * c = 0 picks the default window width for n (g16_msm_g1_window_bits). */
+
+/* Default window width for n scalars (a cost model of point additions), and the number
+ * of windows ceil(255 / c) (0 for c outside [1, 24]). */
+uint32_t g16_msm_g1_window_bits(uint64_t n);
+uint32_t g16_msm_g1_window_count(uint32_t c);
+
+/* Device workspace for g16_msm_g1 (counters, sorted entries, spills, buckets, partial
+ * sums), or 0 when (n, c) is out of range: n >= 1, c in [1, 24], windows * n < 2^32. */
+size_t g16_msm_g1_workspace_bytes(uint64_t n, uint32_t c);
+
+/* Enqueues the MSM and writes g16_msm_g1_window_count(c) window sums (XYZZ, device)
+ * into window_sums; sum_w 2^(c w) window_sums[w] is the result.  scalars_std: n
+ * scalars; bases_mont: n bases; workspace: 256-byte aligned, caller-owned, at least
+ * g16_msm_g1_workspace_bytes(n, c) bytes, contents overwritten.  n == 0 sets every
+ * window sum to infinity.  Errors: G16_EINVAL (null or host pointers, (n, c) out of
+ * range, misaligned workspace), G16_ENOSPACE, G16_EALIAS (window_sums or the workspace
+ * overlapping an input or each other), G16_EHIP.  Scalars >= 2^254 are not rejected and
+ * give a wrong sum. */
+int g16_msm_g1(uint64_t n, const void* scalars_std, const void* bases_mont, uint32_t c,
+               void* workspace, size_t workspace_bytes, void* window_sums, void* stream);
+
+/* HOST: combines g16_msm_g1_window_count(c) window sums, copied to host memory, by
+ * Horner's rule (c doublings per window) into the affine result, standard form.  The
+ * MSM_CU page leaves this serial tail to the host. */
+int g16_msm_g1_finish(uint32_t c, const void* window_sums_host, void* out_affine_std);
+
+/* out_i = k_i G for the generator G = (1, 2): affine, Montgomery form, one thread per
+ * scalar.  Builds synthetic bases (multiples of G stand in for a proving key's points).
+ * n >= 1; scalars any 256-bit integers. */
+int g16_g1_generator_mul(uint64_t n, const void* scalars_std, void* out_affine_mont,
+                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

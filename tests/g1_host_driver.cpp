@@ -1,0 +1,104 @@
+// Host build of the library's base-field and G1 layers (fp.hpp, g1.hpp) and of the MSM's
+// digit recoding (msm_digit.hpp), driven by tests/test_g1_host.py.
+//
+// Input lines "op arg..." with hexadecimal arguments; field ops act on Montgomery
+// representatives as stored, point ops take and print affine STANDARD coordinates
+// (0 0 = infinity).  Output: one line of hexadecimal values per input line (digits:
+// signed decimal).
+#include <cstdio>
+#include <iostream>
+#include <sstream>
+#include <string>
+#include <vector>
+
+#include "g1.hpp"
+#include "msm_digit.hpp"
+
+using g16::Fp;
+using g16::G1Aff;
+using g16::G1Xyzz;
+
+static Fp parse(const std::string& h) {
+    Fp x = g16::fp_zero();
+    int nib = 0;
+    for (int i = (int)h.size() - 1; i >= 0 && nib < 64; --i, ++nib) {
+        char c = h[i];
+        uint32_t v = (c >= '0' && c <= '9') ? c - '0' : (c >= 'a' && c <= 'f') ? c - 'a' + 10 : c - 'A' + 10;
+        x.w[nib / 8] |= v << (4 * (nib % 8));
+    }
+    return x;
+}
+
+static void put(const Fp& x) {
+    for (int i = 7; i >= 0; --i) std::printf("%08x", x.w[i]);
+}
+
+static G1Aff aff_in(const std::string& x, const std::string& y) {
+    G1Aff a;
+    Fp xs = parse(x), ys = parse(y);
+    if (g16::fp_is_zero(xs) && g16::fp_is_zero(ys)) {
+        a.x = xs;
+        a.y = ys;
+        return a;
+    }
+    a.x = g16::fp_to_mont(xs);
+    a.y = g16::fp_to_mont(ys);
+    return a;
+}
+
+static void aff_out(const G1Xyzz& p) {
+    const G1Aff a = g16::xyzz_to_aff(p);
+    put(g16::fp_from_mont(a.x));
+    std::printf(" ");
+    put(g16::fp_from_mont(a.y));
+    std::printf("\n");
+}
+
+int main() {
+    std::string line;
+    while (std::getline(std::cin, line)) {
+        std::istringstream in(line);
+        std::string op;
+        in >> op;
+        std::vector<std::string> a;
+        for (std::string t; in >> t;) a.push_back(t);
+        if (op == "fpmul" || op == "fpadd" || op == "fpsub") {
+            Fp x = parse(a[0]), y = parse(a[1]);
+            put(op == "fpmul" ? g16::fp_mul(x, y) : op == "fpadd" ? g16::fp_add(x, y) : g16::fp_sub(x, y));
+            std::printf("\n");
+        } else if (op == "fpinv" || op == "tomont" || op == "frommont" || op == "fpneg") {
+            Fp x = parse(a[0]);
+            put(op == "fpinv" ? g16::fp_inv(x) : op == "tomont" ? g16::fp_to_mont(x)
+                : op == "frommont" ? g16::fp_from_mont(x) : g16::fp_neg(x));
+            std::printf("\n");
+        } else if (op == "madd") {        // (2 P) + Q, the accumulator with ZZ != 1
+            G1Xyzz p = g16::xyzz_dbl(g16::xyzz_from_aff(aff_in(a[0], a[1])));
+            aff_out(g16::xyzz_madd(p, aff_in(a[2], a[3])));
+        } else if (op == "madd1") {       // P + Q with P straight from affine
+            aff_out(g16::xyzz_madd(g16::xyzz_from_aff(aff_in(a[0], a[1])), aff_in(a[2], a[3])));
+        } else if (op == "add") {         // (2 P) + (2 Q)
+            G1Xyzz p = g16::xyzz_dbl(g16::xyzz_from_aff(aff_in(a[0], a[1])));
+            G1Xyzz q = g16::xyzz_dbl(g16::xyzz_from_aff(aff_in(a[2], a[3])));
+            aff_out(g16::xyzz_add(p, q));
+        } else if (op == "add1") {        // P + Q, both straight from affine
+            aff_out(g16::xyzz_add(g16::xyzz_from_aff(aff_in(a[0], a[1])),
+                                  g16::xyzz_from_aff(aff_in(a[2], a[3]))));
+        } else if (op == "dbl") {         // 2 (2 P)
+            aff_out(g16::xyzz_dbl(g16::xyzz_dbl(g16::xyzz_from_aff(aff_in(a[0], a[1])))));
+        } else if (op == "dblaff") {      // 2 P from affine
+            aff_out(g16::xyzz_dbl_aff(aff_in(a[0], a[1])));
+        } else if (op == "mulsmall") {    // k P
+            uint32_t k = (uint32_t)std::stoul(a[0], nullptr, 16);
+            aff_out(g16::xyzz_mul_small(g16::xyzz_from_aff(aff_in(a[1], a[2])), k));
+        } else if (op == "digits") {      // c k: every window's signed digit
+            uint32_t c = (uint32_t)std::stoul(a[0], nullptr, 16);
+            Fp k = parse(a[1]);
+            const uint32_t W = (255u + c - 1u) / c;
+            for (uint32_t w = 0; w < W; ++w) std::printf("%d ", g16::msm_digit(k.w, w, c));
+            std::printf("\n");
+        } else {
+            return 2;
+        }
+    }
+    return 0;
+}
