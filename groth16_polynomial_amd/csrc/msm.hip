@@ -19,10 +19,12 @@ using g16::MsmParams;
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr uint32_t kMaxC = 24;
+constexpr uint32_t kMaxC = 16;  // a window's counters fit in LDS (2^15 x 4 bytes)
 constexpr uint32_t kSliceLen = 32;
 constexpr uint32_t kSegLen = 8;
 constexpr uint32_t kMaxOnesGroups = 64;
+constexpr uint32_t kMinChunk = 65536;   // scalars per sorting workgroup, at least
+constexpr uint32_t kMaxChunks = 64;     // sorting workgroups per window, at most
 
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -44,13 +46,21 @@ bool device_pointer(const void* p) {
            attr.type == hipMemoryTypeUnified;
 }
 
-// Window width minimising the point additions: n per window for the accumulation, and
-// about three per bucket for the merge and the weighted window sum.
+// Window width minimising a cost in point additions: n per window for the accumulation,
+// about three per bucket for the merge and the weighted window sum, and the serial merge
+// of the top window's buckets.  Scalars below r < 2^254 leave the top window only
+// 254 - (W - 1) c bits, so its few buckets hold about n / 2^bits entries each, merged one
+// slice partial after another; a serial addition is priced at the 16384 additions the
+// chip does in parallel meanwhile.
 uint32_t default_c(uint64_t n) {
     uint32_t best = 1;
     double best_cost = 0.0;
-    for (uint32_t c = 1; c <= 20; ++c) {
-        const double cost = (double)windows_for(c) * ((double)n + 3.0 * (double)(1u << (c - 1)));
+    for (uint32_t c = 1; c <= kMaxC; ++c) {
+        const uint32_t W = windows_for(c);
+        const int top_bits = 254 - (int)((W - 1) * c);
+        const double fat = (double)n / (double)(1ull << (top_bits > 0 ? top_bits : 0));
+        const double cost = (double)W * ((double)n + 3.0 * (double)(1u << (c - 1))) +
+                            16384.0 * fat / (double)kSliceLen;
         if (c == 1 || cost < best_cost) {
             best = c;
             best_cost = cost;
@@ -61,7 +71,9 @@ uint32_t default_c(uint64_t n) {
 
 struct Layout {
     MsmParams mp;
-    size_t counts, cursor, entries, spill_rows, spill_pts, buckets, seg_out, ones_out, total;
+    uint32_t per_group, groups;  // segment sums per partial, partials per window
+    size_t counts, cursor, chunk_counts, entries, spill_rows, spill_pts, buckets, seg_out,
+        partials, ones_out, total;
 };
 
 bool make_layout(uint64_t n, uint32_t c, Layout* L) {
@@ -80,6 +92,13 @@ bool make_layout(uint64_t n, uint32_t c, Layout* L) {
     mp.segs = mp.buckets / mp.seg_len;
     const uint64_t groups = (n + g16::kMsmThreads - 1) / g16::kMsmThreads;
     mp.ones_groups = (uint32_t)(groups < kMaxOnesGroups ? groups : kMaxOnesGroups);
+    uint64_t chunk = (n + kMaxChunks - 1) / kMaxChunks;
+    chunk = (chunk + g16::kMsmSortThreads - 1) / g16::kMsmSortThreads * g16::kMsmSortThreads;
+    if (chunk < kMinChunk) chunk = kMinChunk;
+    mp.chunk = (uint32_t)chunk;
+    mp.chunks = (uint32_t)((n + chunk - 1) / chunk);
+    L->per_group = mp.segs < g16::kMsmThreads ? mp.segs : g16::kMsmThreads;
+    L->groups = mp.segs / L->per_group;
     const size_t rows = (size_t)W * mp.buckets;
     const size_t spills = 2 * (size_t)W * mp.slices;
     size_t off = 0;
@@ -90,11 +109,13 @@ bool make_layout(uint64_t n, uint32_t c, Layout* L) {
     };
     L->counts = take(rows * 4);
     L->cursor = take(rows * 4);
+    L->chunk_counts = take(rows * mp.chunks * 4);
     L->entries = take((size_t)W * n * 8);
     L->spill_rows = take(spills * 4);
     L->spill_pts = take(spills * sizeof(G1Xyzz));
     L->buckets = take(rows * sizeof(G1Xyzz));
     L->seg_out = take((size_t)W * mp.segs * sizeof(G1Xyzz));
+    L->partials = take((size_t)W * L->groups * sizeof(G1Xyzz));
     L->ones_out = take((size_t)mp.ones_groups * sizeof(G1Xyzz));
     L->total = off;
     return true;
@@ -153,22 +174,35 @@ int g16_msm_g1(uint64_t n, const void* scalars_std, const void* bases_mont, uint
     const MsmParams mp = L.mp;
     uint32_t* counts = (uint32_t*)(ws + L.counts);
     uint32_t* cursor = (uint32_t*)(ws + L.cursor);
+    uint32_t* chunk_counts = (uint32_t*)(ws + L.chunk_counts);
     uint2* entries = (uint2*)(ws + L.entries);
     uint32_t* spill_rows = (uint32_t*)(ws + L.spill_rows);
     G1Xyzz* spill_pts = (G1Xyzz*)(ws + L.spill_pts);
     G1Xyzz* buckets = (G1Xyzz*)(ws + L.buckets);
     G1Xyzz* seg_out = (G1Xyzz*)(ws + L.seg_out);
+    G1Xyzz* partials = (G1Xyzz*)(ws + L.partials);
     G1Xyzz* ones_out = (G1Xyzz*)(ws + L.ones_out);
     const uint32_t* sc = (const uint32_t*)scalars_std;
     const G1Aff* bases = (const G1Aff*)bases_mont;
     const uint32_t rows = W * mp.buckets;
-    const dim3 blk(g16::kMsmThreads);
+    const dim3 blk(g16::kMsmThreads), sort_blk(g16::kMsmSortThreads);
+    const size_t lds = (size_t)mp.buckets * 4;
+    if (lds > 65536) {  // LDS beyond the default 64 KiB is allowed per kernel
+        if (hipFuncSetAttribute((const void*)g16::msm_hist,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess ||
+            hipFuncSetAttribute((const void*)g16::msm_place,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+            return G16_EHIP;
+    }
 
-    hipLaunchKernelGGL(g16::msm_fill_u32, dim3(blocks_for(rows)), blk, 0, s, counts, rows, 0u);
-    hipLaunchKernelGGL(g16::msm_count, dim3(blocks_for(n)), blk, 0, s, sc, mp, counts);
-    hipLaunchKernelGGL(g16::msm_scan, dim3(W), dim3(g16::kMsmScanThreads), 0, s, counts, mp,
+    hipLaunchKernelGGL(g16::msm_hist, dim3(W * mp.chunks), sort_blk, lds, s, sc, mp, chunk_counts);
+    hipLaunchKernelGGL(g16::msm_totals, dim3(blocks_for(rows)), blk, 0, s, chunk_counts, mp,
+                       counts);
+    hipLaunchKernelGGL(g16::msm_scan, dim3(W), sort_blk, 0, s, counts, mp, cursor);
+    hipLaunchKernelGGL(g16::msm_chunk_offsets, dim3(blocks_for(rows)), blk, 0, s, chunk_counts, mp,
                        cursor);
-    hipLaunchKernelGGL(g16::msm_scatter, dim3(blocks_for(n)), blk, 0, s, sc, mp, cursor, entries);
+    hipLaunchKernelGGL(g16::msm_place, dim3(W * mp.chunks), sort_blk, lds, s, sc, mp, chunk_counts,
+                       entries);
     hipLaunchKernelGGL(g16::msm_accumulate, dim3(blocks_for((uint64_t)W * mp.slices)), blk, 0, s,
                        entries, bases, cursor, mp, buckets, spill_pts, spill_rows);
     hipLaunchKernelGGL(g16::msm_merge, dim3(blocks_for(rows)), blk, 0, s, counts, cursor,
@@ -176,8 +210,10 @@ int g16_msm_g1(uint64_t n, const void* scalars_std, const void* bases_mont, uint
     hipLaunchKernelGGL(g16::msm_reduce_segments, dim3(blocks_for((uint64_t)W * mp.segs)), blk, 0,
                        s, counts, buckets, mp, seg_out);
     hipLaunchKernelGGL(g16::msm_ones, dim3(mp.ones_groups), blk, 0, s, sc, bases, mp, ones_out);
-    hipLaunchKernelGGL(g16::msm_window_sums, dim3(W), blk, 0, s, seg_out, ones_out, mp,
-                       (G1Xyzz*)window_sums);
+    hipLaunchKernelGGL(g16::msm_sum_groups, dim3(W * L.groups), blk, 0, s, seg_out, L.per_group,
+                       (const G1Xyzz*)nullptr, 0u, partials);
+    hipLaunchKernelGGL(g16::msm_sum_groups, dim3(W), blk, 0, s, partials, L.groups, ones_out,
+                       mp.ones_groups, (G1Xyzz*)window_sums);
     return hipGetLastError() == hipSuccess ? G16_OK : G16_EHIP;
 }
 

@@ -5,9 +5,8 @@
 //     digit magnitude, and a negative digit adds the negated base;
 //   * scalars 0 and 1 never reach a bucket: zeros are skipped and ones are summed by a
 //     separate pass, one mixed addition each;
-//   * a counting sort by bucket (count with 32-bit atomics, prefix-sum per window,
-//     scatter point indices with a 32-bit atomic cursor), so that no atomic ever
-//     touches a point;
+//   * a counting sort by bucket (count, prefix-sum per window, scatter point indices
+//     through a cursor), so that no atomic ever touches a point;
 //   * load-balanced accumulation: fixed-length slices of the sorted entries, one thread
 //     each; a run strictly inside a slice is written to its bucket directly, the first
 //     and last run of a slice go to two spill slots, and a merge pass adds each bucket's
@@ -17,10 +16,12 @@
 //
 // Differences from the page (see the notes at each kernel): the digit recoding is
 // computed per window from the window's bits and the bit below it (so count and scatter
-// need no sequential carry); a bucket never written is recognised from its count and
-// from the run geometry instead of being cleared first; the window reduction is spread
-// over many threads (one per short segment of buckets) rather than one block per
-// window; the ones' partial sums are added into window 0.
+// need no sequential carry); the counting sort keeps each window's counters in LDS, one
+// workgroup per (window, chunk of scalars), so its atomics are LDS atomics and none is
+// global; a bucket never written is recognised from its count and from the run geometry
+// instead of being cleared first; the window reduction is spread over many threads (one
+// per short segment of buckets) rather than one block per window; the ones' partial
+// sums are added into window 0.
 #pragma once
 
 #include "g1.hpp"
@@ -38,11 +39,13 @@ struct MsmParams {
     uint32_t seg_len;    // buckets per reduction thread
     uint32_t segs;       // buckets / seg_len reduction threads per window
     uint32_t ones_groups;  // workgroups of the ones pass
+    uint32_t chunk;      // scalars per sorting workgroup
+    uint32_t chunks;     // ceil(n / chunk) sorting workgroups per window
 };
 
 constexpr uint32_t kMsmNoRow = 0xffffffffu;
 constexpr uint32_t kMsmThreads = 256;
-constexpr uint32_t kMsmScanThreads = 1024;
+constexpr uint32_t kMsmSortThreads = 1024;
 
 __device__ __forceinline__ void msm_load_scalar(const uint32_t* s, uint32_t i, uint32_t k[8]) {
     const uint4* q = reinterpret_cast<const uint4*>(s + 8 * (size_t)i);
@@ -102,31 +105,54 @@ __global__ void msm_fill_u32(uint32_t* p, uint32_t len, uint32_t v) {
     if (i < len) p[i] = v;
 }
 
-// Counting sort, pass 1: entries per (window, bucket).  One thread per scalar.
-__global__ void __launch_bounds__(kMsmThreads) msm_count(const uint32_t* scalars, MsmParams mp,
-                                                         uint32_t* counts) {
-    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= mp.n) return;
-    uint32_t k[8];
-    msm_load_scalar(scalars, i, k);
-    if (msm_scalar_kind(k) != 2u) return;
-    for (uint32_t w = 0; w < mp.windows; ++w) {
+// Counting sort by (window, bucket), with the counters in LDS: one workgroup per (window,
+// chunk of scalars) keeps the window's 2^(c-1) counters in LDS (c <= 16: at most
+// 128 KiB), so the only atomics are LDS ones and nothing global is contended.
+//
+// Pass 1: each (window, chunk) workgroup's histogram, written to
+// chunk_counts[(w chunks + chunk) B + bucket].
+__global__ void __launch_bounds__(kMsmSortThreads) msm_hist(const uint32_t* scalars, MsmParams mp,
+                                                            uint32_t* chunk_counts) {
+    extern __shared__ uint32_t hist[];
+    const uint32_t w = blockIdx.x / mp.chunks, ch = blockIdx.x - w * mp.chunks;
+    const uint32_t t = threadIdx.x;
+    for (uint32_t b = t; b < mp.buckets; b += kMsmSortThreads) hist[b] = 0u;
+    __syncthreads();
+    const uint32_t i0 = ch * mp.chunk;
+    const uint32_t i1 = i0 + mp.chunk < mp.n ? i0 + mp.chunk : mp.n;
+    for (uint32_t i = i0 + t; i < i1; i += kMsmSortThreads) {
+        uint32_t k[8];
+        msm_load_scalar(scalars, i, k);
+        if (msm_scalar_kind(k) != 2u) continue;
         const int32_t d = msm_digit(k, w, mp.c);
-        if (d == 0) continue;
-        const uint32_t mag = (uint32_t)(d < 0 ? -d : d);
-        atomicAdd(&counts[w * mp.buckets + mag - 1u], 1u);
+        if (d != 0) atomicAdd(&hist[(uint32_t)(d < 0 ? -d : d) - 1u], 1u);
     }
+    __syncthreads();
+    uint32_t* out = chunk_counts + (size_t)blockIdx.x * mp.buckets;
+    for (uint32_t b = t; b < mp.buckets; b += kMsmSortThreads) out[b] = hist[b];
 }
 
-// Pass 2: exclusive prefix sum of one window's counts, biased by the window's region
-// start w * n in the entry array.  One workgroup of kMsmScanThreads per window: each
-// thread sums a contiguous chunk, the chunk sums are scanned in LDS, then each thread
-// writes its chunk's offsets.
-__global__ void __launch_bounds__(kMsmScanThreads) msm_scan(const uint32_t* counts, MsmParams mp,
+// Pass 2a: one thread per bucket row: counts[row] = the row's total over the chunks.
+__global__ void __launch_bounds__(kMsmThreads) msm_totals(const uint32_t* chunk_counts,
+                                                          MsmParams mp, uint32_t* counts) {
+    const uint32_t row = blockIdx.x * blockDim.x + threadIdx.x;
+    if (row >= mp.windows * mp.buckets) return;
+    const uint32_t w = row / mp.buckets, b = row - w * mp.buckets;
+    const uint32_t* cw = chunk_counts + (size_t)w * mp.chunks * mp.buckets + b;
+    uint32_t tot = 0;
+    for (uint32_t ch = 0; ch < mp.chunks; ++ch) tot += cw[(size_t)ch * mp.buckets];
+    counts[row] = tot;
+}
+
+// Pass 2b: exclusive prefix sum of one window's totals, from the window's region start
+// w n in the entry array, into cursor[row] (the run's start).  One workgroup per window:
+// each thread sums a contiguous range of buckets, the range sums are scanned in LDS, then
+// each thread writes its range's starts.
+__global__ void __launch_bounds__(kMsmSortThreads) msm_scan(const uint32_t* counts, MsmParams mp,
                                                             uint32_t* cursor) {
-    __shared__ uint32_t sums[kMsmScanThreads];
+    __shared__ uint32_t sums[kMsmSortThreads];
     const uint32_t w = blockIdx.x, t = threadIdx.x;
-    const uint32_t per = (mp.buckets + kMsmScanThreads - 1u) / kMsmScanThreads;
+    const uint32_t per = (mp.buckets + kMsmSortThreads - 1u) / kMsmSortThreads;
     const uint32_t b0 = t * per;
     const uint32_t b1 = b0 + per < mp.buckets ? b0 + per : mp.buckets;
     const uint32_t* cw = counts + (size_t)w * mp.buckets;
@@ -135,7 +161,7 @@ __global__ void __launch_bounds__(kMsmScanThreads) msm_scan(const uint32_t* coun
     sums[t] = local;
     __syncthreads();
     // Hillis-Steele inclusive scan; every thread reaches every barrier
-    for (uint32_t d = 1; d < kMsmScanThreads; d <<= 1) {
+    for (uint32_t d = 1; d < kMsmSortThreads; d <<= 1) {
         const uint32_t add = t >= d ? sums[t - d] : 0u;
         __syncthreads();
         sums[t] += add;
@@ -149,22 +175,48 @@ __global__ void __launch_bounds__(kMsmScanThreads) msm_scan(const uint32_t* coun
     }
 }
 
-// Pass 3: each scalar's entry (row, index << 1 | negative) into its bucket's run.  After
-// this pass cursor[row] is the END of the row's run.
-__global__ void __launch_bounds__(kMsmThreads) msm_scatter(const uint32_t* scalars, MsmParams mp,
-                                                           uint32_t* cursor, uint2* entries) {
-    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= mp.n) return;
-    uint32_t k[8];
-    msm_load_scalar(scalars, i, k);
-    if (msm_scalar_kind(k) != 2u) return;
-    for (uint32_t w = 0; w < mp.windows; ++w) {
+// Pass 2c: one thread per bucket row: each chunk's histogram entry becomes the chunk's
+// first slot in the row's run, and cursor[row] moves to the run's end.
+__global__ void __launch_bounds__(kMsmThreads) msm_chunk_offsets(uint32_t* chunk_counts,
+                                                                 MsmParams mp, uint32_t* cursor) {
+    const uint32_t row = blockIdx.x * blockDim.x + threadIdx.x;
+    if (row >= mp.windows * mp.buckets) return;
+    const uint32_t w = row / mp.buckets, b = row - w * mp.buckets;
+    uint32_t* cw = chunk_counts + (size_t)w * mp.chunks * mp.buckets + b;
+    uint32_t run = cursor[row];
+    for (uint32_t ch = 0; ch < mp.chunks; ++ch) {
+        uint32_t* q = cw + (size_t)ch * mp.buckets;
+        const uint32_t c = *q;
+        *q = run;
+        run += c;
+    }
+    cursor[row] = run;
+}
+
+// Pass 3: the same (window, chunk) workgroups place each entry (row, index << 1 |
+// negative) at its chunk's next slot in the bucket's run, the slots handed out by LDS
+// atomics on the chunk's offsets.
+__global__ void __launch_bounds__(kMsmSortThreads) msm_place(const uint32_t* scalars, MsmParams mp,
+                                                             const uint32_t* chunk_offsets,
+                                                             uint2* entries) {
+    extern __shared__ uint32_t next[];
+    const uint32_t w = blockIdx.x / mp.chunks, ch = blockIdx.x - w * mp.chunks;
+    const uint32_t t = threadIdx.x;
+    const uint32_t* in = chunk_offsets + (size_t)blockIdx.x * mp.buckets;
+    for (uint32_t b = t; b < mp.buckets; b += kMsmSortThreads) next[b] = in[b];
+    __syncthreads();
+    const uint32_t i0 = ch * mp.chunk;
+    const uint32_t i1 = i0 + mp.chunk < mp.n ? i0 + mp.chunk : mp.n;
+    const uint32_t row0 = w * mp.buckets;
+    for (uint32_t i = i0 + t; i < i1; i += kMsmSortThreads) {
+        uint32_t k[8];
+        msm_load_scalar(scalars, i, k);
+        if (msm_scalar_kind(k) != 2u) continue;
         const int32_t d = msm_digit(k, w, mp.c);
         if (d == 0) continue;
-        const uint32_t mag = (uint32_t)(d < 0 ? -d : d);
-        const uint32_t row = w * mp.buckets + mag - 1u;
-        const uint32_t slot = atomicAdd(&cursor[row], 1u);
-        entries[slot] = make_uint2(row, (i << 1) | (d < 0 ? 1u : 0u));
+        const uint32_t b = (uint32_t)(d < 0 ? -d : d) - 1u;
+        const uint32_t slot = atomicAdd(&next[b], 1u);
+        entries[slot] = make_uint2(row0 + b, (i << 1) | (d < 0 ? 1u : 0u));
     }
 }
 
@@ -291,26 +343,26 @@ __global__ void __launch_bounds__(kMsmThreads) msm_ones(const uint32_t* scalars,
     if (t == 0) msm_st_xyzz(out + blockIdx.x, sh[0]);
 }
 
-// Pass 7: one workgroup per window sums its segments' contributions (and, for window 0,
-// the ones' partial sums) into window_sums[w].
-__global__ void __launch_bounds__(kMsmThreads) msm_window_sums(const G1Xyzz* seg_out,
-                                                               const G1Xyzz* ones_out,
-                                                               MsmParams mp,
-                                                               G1Xyzz* window_sums) {
+// Pass 7: group sums.  Workgroup g adds in[g per, (g + 1) per) (and, for g = 0, the
+// n_extra points of extra) into out[g], a tree in LDS after a strided serial sum.  Run
+// twice: the segments' contributions into a few partials per window, then the partials
+// (and the ones' sums, into window 0) into the window sums.
+__global__ void __launch_bounds__(kMsmThreads) msm_sum_groups(const G1Xyzz* in, uint32_t per,
+                                                              const G1Xyzz* extra,
+                                                              uint32_t n_extra, G1Xyzz* out) {
     __shared__ G1Xyzz sh[kMsmThreads];
-    const uint32_t w = blockIdx.x, t = threadIdx.x;
+    const uint32_t g = blockIdx.x, t = threadIdx.x;
     G1Xyzz acc = xyzz_zero();
-    for (uint32_t s = t; s < mp.segs; s += kMsmThreads)
-        acc = xyzz_add(acc, msm_ld_xyzz(seg_out + (size_t)w * mp.segs + s));
-    if (w == 0)
-        for (uint32_t g = t; g < mp.ones_groups; g += kMsmThreads)
-            acc = xyzz_add(acc, msm_ld_xyzz(ones_out + g));
+    for (uint32_t s = t; s < per; s += kMsmThreads)
+        acc = xyzz_add(acc, msm_ld_xyzz(in + (size_t)g * per + s));
+    if (g == 0)
+        for (uint32_t e = t; e < n_extra; e += kMsmThreads) acc = xyzz_add(acc, msm_ld_xyzz(extra + e));
     sh[t] = acc;
     for (uint32_t s = kMsmThreads / 2; s > 0; s >>= 1) {
         __syncthreads();
         if (t < s) sh[t] = xyzz_add(sh[t], sh[t + s]);
     }
-    if (t == 0) msm_st_xyzz(window_sums + w, sh[0]);
+    if (t == 0) msm_st_xyzz(out + g, sh[0]);
 }
 
 // Synthetic bases and fixed-base multiples: out_i = k_i G in affine Montgomery form, one

@@ -181,7 +181,7 @@ def _xyzz_words(points, rng):
     return out
 
 
-@pytest.mark.parametrize("c", [1, 4, 13, 16, 24])
+@pytest.mark.parametrize("c", [1, 4, 13, 16])
 def test_host_window_combination(lib, c):
     """g16_msm_g1_finish (host code of libg16.so) = sum_w 2^(cw) W_w by the oracle."""
     rng = random.Random(50 + c)
@@ -197,3 +197,4 @@ def test_host_window_combination(lib, c):
     want = msm.msm(msm.to_words([s % R for s in scal]), msm.points_to_words(pts))
     assert np.array_equal(out, want)
     assert lib.g16_msm_g1_finish(0, sums.ctypes.data, out.ctypes.data) == binding.G16_EINVAL
+    assert lib.g16_msm_g1_finish(17, sums.ctypes.data, out.ctypes.data) == binding.G16_EINVAL

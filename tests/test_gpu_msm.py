@@ -132,7 +132,7 @@ def test_msm_top_scalars():
     def mutate(bases, k):
         k[:50] = msm.to_words([R - 1 - i for i in range(50)])
         k[50:60] = msm.to_words([(1 << 253) + i for i in range(10)])
-    for c in (0, 7, 16, 17):
+    for c in (0, 7, 15, 16):
         _msm_case(600, c, seed=31 + c, mutate=mutate)
 
 
