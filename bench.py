@@ -97,12 +97,18 @@ def _code_only(text: str) -> str:
     return re.sub(r"\s+", "", text)
 
 
+# Sources of the G1 MSM only; the H pipeline's kernels are built from the others.
+MSM_SOURCES = {"fp.hpp", "g1.hpp", "msm.hip", "msm_digit.hpp", "msm_kernels.hpp"}
+
+
 def kernel_source_hash() -> str:
-    """Hash of the kernel sources' code (comments and whitespace ignored), which ties a
-    committed counter summary to the kernels it was measured on."""
+    """Hash of the H pipeline's kernel sources' code (comments and whitespace ignored),
+    which ties a committed counter summary to the kernels it was measured on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "groth16_polynomial_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
+        if f in MSM_SOURCES:
+            continue
         with open(os.path.join(csrc, f), encoding="utf-8") as fh:
             h.update(f.encode() + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
@@ -278,6 +284,36 @@ def main():
         for i in range(count):
             acc[i] += evs[i][0].elapsed_time(evs[i][1])
     stage_ms = [x / args.stage_reps for x in acc]
+
+    # ---- the H MSM: sum_i h_i P_i over G1 on the pipeline's own h_std, with synthetic
+    # bases (multiples s_i G of the generator stand in for the proving key's points)
+    bases = g.g1_generator_mul(g.to_device(synth.uniform_fr(7, n)))
+    mctx = g.MsmG1(n)
+    for _ in range(2):
+        mctx.window_sums(hs, bases)
+    torch.cuda.synchronize()
+    f0.record(stream)
+    msm_reps = max(1, args.steps // 4)
+    for _ in range(msm_reps):
+        mctx.window_sums(hs, bases)
+    f1.record(stream)
+    torch.cuda.synchronize()
+    msm_ms = f0.elapsed_time(f1) / msm_reps
+    sums_host = g.to_host(mctx.sums).reshape(mctx.windows, 32)
+    t_fin = time.perf_counter()
+    for _ in range(10):
+        mctx.finish(sums_host)
+    finish_ms = (time.perf_counter() - t_fin) / 10 * 1e3
+    msm_line = {
+        "workload": "G1 MSM of h_std at n=2^%d, bases s_i G (synthetic)" % log_n,
+        "window_bits": mctx.c,
+        "windows": mctx.windows,
+        "device_ms": round(msm_ms, 4),
+        "host_finish_ms": round(finish_ms, 4),
+        "bucket_adds_per_s_g": round(n * mctx.windows / (msm_ms / 1e3) / 1e9, 3),
+    }
+    del bases, mctx
+    print("[bench] msm: %s" % msm_line, file=sys.stderr, flush=True)
     dom = int(np.argmax(stage_ms))
     kind, join, nv, k = stages[dom]
     dom_mads, dom_bytes = stage_work(kind, join, nv, k, n)
@@ -315,6 +351,7 @@ def main():
         "gather_gnnz_s": round(nnz / (gather_ms / 1e3) / 1e9, 3),
         "gather_hbm_gbs_algorithmic": round(gather_bytes / (gather_ms / 1e3) / 1e9, 2),
         "proof_batches": proof_batches,
+        "msm_g1": msm_line,
         "hbm_gbs_algorithmic": round(total_bytes / (ms_per_step / 1e3) / 1e9, 2),
         "pipeline_tmad_s": round(total_muls / (ms_per_step / 1e3) / 1e12, 3),
         "pipeline_alu_frac": round(total_muls / (ms_per_step / 1e3) / 1e12 / MAD_PEAK_T, 4),
