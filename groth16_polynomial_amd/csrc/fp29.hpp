@@ -1,0 +1,220 @@
+// BN254 base field Fp in nine 29-bit digits for the MSM's point arithmetic.
+//
+// Why: a product of two variables on 8 x 32-bit limbs (fp.hpp) needs a carry chain per
+// limb product, about three issue slots each on gfx950 (plus wait states after the
+// add-with-carry instructions).  With 29-bit digits a digit product is below 2^58 and a
+// column of 18 products stays inside a signed 64-bit accumulator, so every product is
+// one v_mad_i64_i32 and carries move once per column (the same reasoning as the
+// transforms' digit layer, fr29.hpp).
+//
+// Value of an Fp29: sum of d[k] 2^(29k) with signed 32-bit digits, held in Montgomery
+// form with R' = 2^261 (a canonical 2^256-form element x R converts by x R 2^5, a shift).
+// "Normalized": digits 0..7 in [-4, 2^29 + 4), digit 8 small and signed.  Every function
+// here returns normalized digits.  Values are lazy.  A converted input is below 32p (the
+// shift by 2^5 is not reduced); a product of inputs below Ap and Bp in magnitude lies
+// below (A B 2^-7.4 + 1) p (the 2^-7.4 is p / 2^261).  Through the MSM's formulas that
+// keeps an accumulator's X below 20p, Y below 7p and ZZ, ZZZ below 6p after its first
+// addition; the largest value ever formed is a difference such as U2 - X1 in the first
+// mixed addition onto a converted point, below 40p, inside the 64p that fp29_canon
+// allows.
+//
+// The product is Montgomery's REDC in radix 2^29 (P. L. Montgomery, Math. Comp. 1985),
+// in the product-scanning order: column k takes carry + sum a_i b_(k-i) + sum m_i p_(k-i),
+// for k < 9 the digit m_k = (column * -p^-1) mod 2^29 that clears the column, for k >= 9
+// the result digit.  162 digit products.
+#pragma once
+
+#include "fp.hpp"
+#include "fr29.hpp"  // static_for, kM29
+
+namespace g16 {
+
+struct Fp29 {
+    int32_t d[9];
+};
+
+// p in 29-bit digits, and 64 p (fp29_canon adds it to make a lazy value positive)
+G16_HD constexpr int32_t p29_digit(int k) {
+    return k == 0 ? 0x187cfd47 : k == 1 ? 0x010460b6 : k == 2 ? 0x1c72a34f
+         : k == 3 ? 0x02d522d0 : k == 4 ? 0x1585d978 : k == 5 ? 0x02db40c0
+         : k == 6 ? 0x00a6e141 : k == 7 ? 0x0e5c2634 : 0x0030644e;
+}
+G16_HD constexpr int32_t p64_29_digit(int k) {
+    return k == 0 ? 0x1f3f51c0 : k == 1 ? 0x01182db0 : k == 2 ? 0x1ca8d3c2
+         : k == 3 ? 0x1548b438 : k == 4 ? 0x01765e05 : k == 5 ? 0x16d0302b
+         : k == 6 ? 0x09b85045 : k == 7 ? 0x17098d01 : 0x0c19139c;
+}
+// -p^-1 mod 2^29 (Montgomery digit) and -p^-1 mod 32 (the final division by 2^5)
+constexpr uint32_t kP29NInv = 0x04866389u;
+constexpr uint32_t kP5NInv = 9u;
+static_assert(((uint64_t)0x187cfd47u * kP29NInv + 1u) % (1u << 29) == 0u, "kP29NInv");
+static_assert((0xd87cfd47u * kP5NInv + 1u) % 32u == 0u, "kP5NInv");
+
+G16_HD Fp29 fp29_zero() {
+    Fp29 z;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) z.d[k] = 0;
+    return z;
+}
+
+G16_HD bool fp29_digits_zero(const Fp29& a) {
+    int32_t o = 0;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) o |= a.d[k];
+    return o == 0;
+}
+
+// canonical x (2^256 Montgomery form, < p) -> x 2^5 in digits [0, 2^29)
+G16_HD Fp29 fp29_from_fp(const Fp& x) {
+    Fp29 r;
+    r.d[0] = (int32_t)((x.w[0] << 5) & kM29);
+#pragma unroll
+    for (int k = 1; k < 9; ++k) {
+        const int pos = 29 * k - 5, w = pos >> 5, s = pos & 31;
+        uint32_t v = x.w[w] >> s;
+        if (s > 3 && w + 1 < 8) v |= x.w[w + 1] << (32 - s);
+        r.d[k] = (int32_t)(v & kM29);
+    }
+    return r;
+}
+
+// Carry-save normalization (as fr29_normalize): digit k keeps its low 29 bits plus the
+// signed carry out of digit k - 1.
+G16_HD Fp29 fp29_norm(const Fp29& a) {
+    Fp29 o;
+    o.d[0] = a.d[0] & (int32_t)kM29;
+#pragma unroll
+    for (int k = 1; k < 8; ++k) o.d[k] = (a.d[k] & (int32_t)kM29) + (a.d[k - 1] >> 29);
+    o.d[8] = a.d[8] + (a.d[7] >> 29);
+    return o;
+}
+
+G16_HD Fp29 fp29_add(const Fp29& a, const Fp29& b) {
+    Fp29 s;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) s.d[k] = a.d[k] + b.d[k];
+    return fp29_norm(s);
+}
+
+G16_HD Fp29 fp29_sub(const Fp29& a, const Fp29& b) {
+    Fp29 s;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) s.d[k] = a.d[k] - b.d[k];
+    return fp29_norm(s);
+}
+
+G16_HD Fp29 fp29_neg(const Fp29& a) { return fp29_sub(fp29_zero(), a); }
+G16_HD Fp29 fp29_dbl(const Fp29& a) { return fp29_add(a, a); }
+
+// a b 2^-261 mod p, lazily reduced (see the header).  Inputs normalized.
+G16_HD Fp29 fp29_mul(const Fp29& a, const Fp29& b) {
+    int64_t carry = 0;
+    uint32_t m[9];
+    Fp29 r;
+    static_for<17>([&](auto k_c) {
+        constexpr int k = decltype(k_c)::value;
+        int64_t col = carry;
+        static_for<9>([&](auto i_c) {
+            constexpr int i = decltype(i_c)::value;
+            constexpr int j = k - i;
+            if constexpr (j >= 0 && j < 9) col += (int64_t)a.d[i] * (int64_t)b.d[j];
+        });
+        static_for<9>([&](auto i_c) {
+            constexpr int i = decltype(i_c)::value;
+            constexpr int j = k - i;
+            if constexpr (i < k && j >= 1 && j < 9) col += (int64_t)m[i] * (int64_t)p29_digit(j);
+        });
+        if constexpr (k < 9) {
+            m[k] = ((uint32_t)col * kP29NInv) & kM29;
+            col += (int64_t)m[k] * (int64_t)p29_digit(0);
+        } else {
+            r.d[k - 9] = (int32_t)((uint32_t)col & kM29);
+        }
+        carry = col >> 29;
+    });
+    r.d[8] = (int32_t)carry;
+    return r;
+}
+
+G16_HD Fp29 fp29_sqr(const Fp29& a) { return fp29_mul(a, a); }
+
+// The value mod p, canonical, as eight 32-bit words (not converted out of the 2^261
+// Montgomery form).  |value| < 64 p: u = value + 64 p is in (0, 128 p), below 2^261; q
+// from bits 224..287 of u over the top word of p is floor(u / p) or one more or less,
+// and u - q p is brought into [0, p) by one conditional addition or subtraction of p.
+G16_HD Fp fp29_canon(const Fp29& a) {
+    uint32_t u[10];
+    {
+        // u = a + 64p with full carry propagation: digits in [0, 2^29), digit 8 >= 0
+        int32_t dg[9];
+        int32_t c = 0;
+#pragma unroll
+        for (int k = 0; k < 9; ++k) {
+            const int32_t x = a.d[k] + p64_29_digit(k) + c;
+            if (k < 8) {
+                dg[k] = x & (int32_t)kM29;
+                c = x >> 29;
+            } else {
+                dg[k] = x;
+            }
+        }
+        // pack 8 x 29 + the top digit into ten 32-bit words
+#pragma unroll
+        for (int j = 0; j < 10; ++j) {
+            const int bit = 32 * j;
+            const int k = bit / 29, off = bit - 29 * k;
+            uint32_t v = k < 9 ? (uint32_t)dg[k] >> off : 0u;
+            if (k + 1 < 9) v |= (uint32_t)dg[k + 1] << (29 - off);
+            if (k + 2 < 9 && 58 - off < 32) v |= (uint32_t)dg[k + 2] << (58 - off);
+            u[j] = v;
+        }
+    }
+    const uint64_t hi = (uint64_t)u[8] << 32 | u[7];  // bits 224..287
+    const uint32_t q = (uint32_t)(hi / 0x30644e72ull);
+    // t = u - q p over nine words (borrow propagated through a signed 64-bit carry)
+    int64_t t[9];
+    int64_t carry = 0;
+#pragma unroll
+    for (int j = 0; j < 9; ++j) {
+        const int64_t x = (int64_t)u[j] - (int64_t)((uint64_t)q * (j < 8 ? p_limb(j) : 0u)) + carry;
+        t[j] = x & 0xffffffffll;
+        carry = x >> 32;
+    }
+    // t in [-p, 2p): sign from the top word (carry below zero means negative)
+    const bool neg = carry < 0 || (int32_t)t[8] < 0;
+    Fp v;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v.w[j] = (uint32_t)t[j];
+    if (neg) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v.w[j] = addc(v.w[j], p_limb(j), c);
+        return v;
+    }
+    // top word t[8] is 0 here (t < 2p < 2^255)
+    return fp_reduce_once(v);
+}
+
+G16_HD bool fp29_is_zero(const Fp29& a) { return fp_is_zero(fp29_canon(a)); }
+
+// -> canonical 2^256 Montgomery form: (value mod p) 2^-5 = (c + k p) / 32 with
+// k = c (-p^-1) mod 32, which is below p for c < p.
+G16_HD Fp fp29_to_fp(const Fp29& a) {
+    const Fp c = fp29_canon(a);
+    const uint32_t k = (c.w[0] * kP5NInv) & 31u;
+    uint32_t t[9];
+    uint64_t carry = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint64_t x = (uint64_t)k * p_limb(j) + c.w[j] + carry;
+        t[j] = (uint32_t)x;
+        carry = x >> 32;
+    }
+    t[8] = (uint32_t)carry;
+    Fp r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r.w[j] = (t[j] >> 5) | (t[j + 1] << 27);
+    return r;
+}
+
+}  // namespace g16

@@ -14,136 +14,210 @@
 #pragma once
 
 #include "fp.hpp"
+#include "fp29.hpp"
 
 namespace g16 {
 
-struct G1Aff {
-    Fp x, y;
+// The formulas below are written once over the field representation: Fp (8 x 32-bit
+// limbs, canonical; host code and storage) or Fp29 (nine 29-bit digits, lazy; the
+// device's hot loops).  f_inf tests a coordinate for the exact zero that stands for
+// infinity: every infinity is built as all-zero limbs or digits and stays so, because
+// a product with an exact zero factor is exactly zero and no other value is zero mod p
+// (points of the group have odd order, so Y and Z are never zero).  f_is_zero is the
+// test mod p (the equal- and opposite-point cases).
+G16_HD Fp f_add(const Fp& a, const Fp& b) { return fp_add(a, b); }
+G16_HD Fp f_sub(const Fp& a, const Fp& b) { return fp_sub(a, b); }
+G16_HD Fp f_dbl(const Fp& a) { return fp_dbl(a); }
+G16_HD Fp f_neg(const Fp& a) { return fp_neg(a); }
+G16_HD Fp f_mul(const Fp& a, const Fp& b) { return fp_mul(a, b); }
+G16_HD Fp f_sqr(const Fp& a) { return fp_sqr(a); }
+G16_HD bool f_is_zero(const Fp& a) { return fp_is_zero(a); }
+G16_HD bool f_inf(const Fp& a) { return fp_is_zero(a); }
+G16_HD Fp29 f_add(const Fp29& a, const Fp29& b) { return fp29_add(a, b); }
+G16_HD Fp29 f_sub(const Fp29& a, const Fp29& b) { return fp29_sub(a, b); }
+G16_HD Fp29 f_dbl(const Fp29& a) { return fp29_dbl(a); }
+G16_HD Fp29 f_neg(const Fp29& a) { return fp29_neg(a); }
+G16_HD Fp29 f_mul(const Fp29& a, const Fp29& b) { return fp29_mul(a, b); }
+G16_HD Fp29 f_sqr(const Fp29& a) { return fp29_sqr(a); }
+G16_HD bool f_is_zero(const Fp29& a) { return fp29_is_zero(a); }
+G16_HD bool f_inf(const Fp29& a) { return fp29_digits_zero(a); }
+
+template <class F> G16_HD F f_zero();
+template <> G16_HD Fp f_zero<Fp>() { return fp_zero(); }
+template <> G16_HD Fp29 f_zero<Fp29>() { return fp29_zero(); }
+template <class F> G16_HD F f_one();
+template <> G16_HD Fp f_one<Fp>() { return fp_one(); }
+template <> G16_HD Fp29 f_one<Fp29>() { return fp29_from_fp(fp_one()); }
+
+template <class F>
+struct AffT {
+    F x, y;
 };
 
-struct G1Xyzz {
-    Fp x, y, zz, zzz;
+template <class F>
+struct XyzzT {
+    F x, y, zz, zzz;
 };
 
-G16_HD G1Xyzz xyzz_zero() {
-    G1Xyzz p;
-    p.x = fp_zero();
-    p.y = fp_zero();
-    p.zz = fp_zero();
-    p.zzz = fp_zero();
+using G1Aff = AffT<Fp>;
+using G1Xyzz = XyzzT<Fp>;
+
+template <class F = Fp>
+G16_HD XyzzT<F> xyzz_zero() {
+    XyzzT<F> p;
+    p.x = f_zero<F>();
+    p.y = f_zero<F>();
+    p.zz = f_zero<F>();
+    p.zzz = f_zero<F>();
     return p;
 }
 
-G16_HD bool aff_is_inf(const G1Aff& a) { return fp_is_zero(a.x) && fp_is_zero(a.y); }
-G16_HD bool xyzz_is_inf(const G1Xyzz& p) { return fp_is_zero(p.zz); }
+template <class F>
+G16_HD bool aff_is_inf(const AffT<F>& a) { return f_inf(a.x) && f_inf(a.y); }
+template <class F>
+G16_HD bool xyzz_is_inf(const XyzzT<F>& p) { return f_inf(p.zz); }
 
-G16_HD G1Xyzz xyzz_from_aff(const G1Aff& a) {
-    if (aff_is_inf(a)) return xyzz_zero();
-    G1Xyzz p;
+template <class F>
+G16_HD XyzzT<F> xyzz_from_aff(const AffT<F>& a) {
+    if (aff_is_inf(a)) return xyzz_zero<F>();
+    XyzzT<F> p;
     p.x = a.x;
     p.y = a.y;
-    p.zz = fp_one();
-    p.zzz = fp_one();
+    p.zz = f_one<F>();
+    p.zzz = f_one<F>();
     return p;
 }
 
-G16_HD G1Xyzz xyzz_neg(const G1Xyzz& p) {
-    G1Xyzz r = p;
-    r.y = fp_neg(p.y);
+template <class F>
+G16_HD XyzzT<F> xyzz_neg(const XyzzT<F>& p) {
+    XyzzT<F> r = p;
+    r.y = f_neg(p.y);
     return r;
 }
 
 // 3 x^2 (the tangent slope's numerator for a = 0)
-G16_HD Fp fp_three_sq(const Fp& x) {
-    const Fp xx = fp_sqr(x);
-    return fp_add(fp_dbl(xx), xx);
+template <class F>
+G16_HD F f_three_sq(const F& x) {
+    const F xx = f_sqr(x);
+    return f_add(f_dbl(xx), xx);
 }
 
 // 2 Q for an affine Q (mdbl-2008-s-1): U = 2y, V = U^2, W = U V, S = x V, M = 3 x^2,
 // X3 = M^2 - 2 S, Y3 = M (S - X3) - W y, ZZ3 = V, ZZZ3 = W.
-G16_HD G1Xyzz xyzz_dbl_aff(const G1Aff& q) {
-    const Fp u = fp_dbl(q.y);
-    const Fp v = fp_sqr(u);
-    const Fp w = fp_mul(u, v);
-    const Fp s = fp_mul(q.x, v);
-    const Fp m = fp_three_sq(q.x);
-    G1Xyzz r;
-    r.x = fp_sub(fp_sqr(m), fp_dbl(s));
-    r.y = fp_sub(fp_mul(m, fp_sub(s, r.x)), fp_mul(w, q.y));
+template <class F>
+G16_HD XyzzT<F> xyzz_dbl_aff(const AffT<F>& q) {
+    const F u = f_dbl(q.y);
+    const F v = f_sqr(u);
+    const F w = f_mul(u, v);
+    const F s = f_mul(q.x, v);
+    const F m = f_three_sq(q.x);
+    XyzzT<F> r;
+    r.x = f_sub(f_sqr(m), f_dbl(s));
+    r.y = f_sub(f_mul(m, f_sub(s, r.x)), f_mul(w, q.y));
     r.zz = v;
     r.zzz = w;
     return r;
 }
 
 // 2 P (dbl-2008-s-1); the point at infinity (ZZ = 0) maps to ZZ3 = V ZZ = 0 by itself.
-G16_HD G1Xyzz xyzz_dbl(const G1Xyzz& p) {
-    const Fp u = fp_dbl(p.y);
-    const Fp v = fp_sqr(u);
-    const Fp w = fp_mul(u, v);
-    const Fp s = fp_mul(p.x, v);
-    const Fp m = fp_three_sq(p.x);
-    G1Xyzz r;
-    r.x = fp_sub(fp_sqr(m), fp_dbl(s));
-    r.y = fp_sub(fp_mul(m, fp_sub(s, r.x)), fp_mul(w, p.y));
-    r.zz = fp_mul(v, p.zz);
-    r.zzz = fp_mul(w, p.zzz);
+template <class F>
+G16_HD XyzzT<F> xyzz_dbl(const XyzzT<F>& p) {
+    const F u = f_dbl(p.y);
+    const F v = f_sqr(u);
+    const F w = f_mul(u, v);
+    const F s = f_mul(p.x, v);
+    const F m = f_three_sq(p.x);
+    XyzzT<F> r;
+    r.x = f_sub(f_sqr(m), f_dbl(s));
+    r.y = f_sub(f_mul(m, f_sub(s, r.x)), f_mul(w, p.y));
+    r.zz = f_mul(v, p.zz);
+    r.zzz = f_mul(w, p.zzz);
     return r;
 }
 
 // P + Q for an affine Q (madd-2008-s): U2 = X2 ZZ1, S2 = Y2 ZZZ1, P = U2 - X1,
 // R = S2 - Y1, PP = P^2, PPP = P PP, Q = X1 PP, X3 = R^2 - PPP - 2 Q,
 // Y3 = R (Q - X3) - Y1 PPP, ZZ3 = ZZ1 PP, ZZZ3 = ZZZ1 PPP.
-G16_HD G1Xyzz xyzz_madd(const G1Xyzz& p, const G1Aff& q) {
+template <class F>
+G16_HD XyzzT<F> xyzz_madd(const XyzzT<F>& p, const AffT<F>& q) {
     if (aff_is_inf(q)) return p;
     if (xyzz_is_inf(p)) return xyzz_from_aff(q);
-    const Fp u2 = fp_mul(q.x, p.zz);
-    const Fp s2 = fp_mul(q.y, p.zzz);
-    const Fp pd = fp_sub(u2, p.x);
-    const Fp rd = fp_sub(s2, p.y);
-    if (fp_is_zero(pd)) return fp_is_zero(rd) ? xyzz_dbl_aff(q) : xyzz_zero();
-    const Fp pp = fp_sqr(pd);
-    const Fp ppp = fp_mul(pd, pp);
-    const Fp qv = fp_mul(p.x, pp);
-    G1Xyzz r;
-    r.x = fp_sub(fp_sub(fp_sqr(rd), ppp), fp_dbl(qv));
-    r.y = fp_sub(fp_mul(rd, fp_sub(qv, r.x)), fp_mul(p.y, ppp));
-    r.zz = fp_mul(p.zz, pp);
-    r.zzz = fp_mul(p.zzz, ppp);
+    const F u2 = f_mul(q.x, p.zz);
+    const F s2 = f_mul(q.y, p.zzz);
+    const F pd = f_sub(u2, p.x);
+    const F rd = f_sub(s2, p.y);
+    if (f_is_zero(pd)) return f_is_zero(rd) ? xyzz_dbl_aff(q) : xyzz_zero<F>();
+    const F pp = f_sqr(pd);
+    const F ppp = f_mul(pd, pp);
+    const F qv = f_mul(p.x, pp);
+    XyzzT<F> r;
+    r.x = f_sub(f_sub(f_sqr(rd), ppp), f_dbl(qv));
+    r.y = f_sub(f_mul(rd, f_sub(qv, r.x)), f_mul(p.y, ppp));
+    r.zz = f_mul(p.zz, pp);
+    r.zzz = f_mul(p.zzz, ppp);
     return r;
 }
 
 // P + Q (add-2008-s): U1 = X1 ZZ2, U2 = X2 ZZ1, S1 = Y1 ZZZ2, S2 = Y2 ZZZ1, P = U2 - U1,
 // R = S2 - S1, PP = P^2, PPP = P PP, Q = U1 PP, X3 = R^2 - PPP - 2 Q,
 // Y3 = R (Q - X3) - S1 PPP, ZZ3 = ZZ1 ZZ2 PP, ZZZ3 = ZZZ1 ZZZ2 PPP.
-G16_HD G1Xyzz xyzz_add(const G1Xyzz& p, const G1Xyzz& q) {
+template <class F>
+G16_HD XyzzT<F> xyzz_add(const XyzzT<F>& p, const XyzzT<F>& q) {
     if (xyzz_is_inf(p)) return q;
     if (xyzz_is_inf(q)) return p;
-    const Fp u1 = fp_mul(p.x, q.zz);
-    const Fp u2 = fp_mul(q.x, p.zz);
-    const Fp s1 = fp_mul(p.y, q.zzz);
-    const Fp s2 = fp_mul(q.y, p.zzz);
-    const Fp pd = fp_sub(u2, u1);
-    const Fp rd = fp_sub(s2, s1);
-    if (fp_is_zero(pd)) return fp_is_zero(rd) ? xyzz_dbl(p) : xyzz_zero();
-    const Fp pp = fp_sqr(pd);
-    const Fp ppp = fp_mul(pd, pp);
-    const Fp qv = fp_mul(u1, pp);
-    G1Xyzz r;
-    r.x = fp_sub(fp_sub(fp_sqr(rd), ppp), fp_dbl(qv));
-    r.y = fp_sub(fp_mul(rd, fp_sub(qv, r.x)), fp_mul(s1, ppp));
-    r.zz = fp_mul(fp_mul(p.zz, q.zz), pp);
-    r.zzz = fp_mul(fp_mul(p.zzz, q.zzz), ppp);
+    const F u1 = f_mul(p.x, q.zz);
+    const F u2 = f_mul(q.x, p.zz);
+    const F s1 = f_mul(p.y, q.zzz);
+    const F s2 = f_mul(q.y, p.zzz);
+    const F pd = f_sub(u2, u1);
+    const F rd = f_sub(s2, s1);
+    if (f_is_zero(pd)) return f_is_zero(rd) ? xyzz_dbl(p) : xyzz_zero<F>();
+    const F pp = f_sqr(pd);
+    const F ppp = f_mul(pd, pp);
+    const F qv = f_mul(u1, pp);
+    XyzzT<F> r;
+    r.x = f_sub(f_sub(f_sqr(rd), ppp), f_dbl(qv));
+    r.y = f_sub(f_mul(rd, f_sub(qv, r.x)), f_mul(s1, ppp));
+    r.zz = f_mul(f_mul(p.zz, q.zz), pp);
+    r.zzz = f_mul(f_mul(p.zzz, q.zzz), ppp);
     return r;
 }
 
 // k P for a small k (left to right, from k's highest set bit).
-G16_HD G1Xyzz xyzz_mul_small(const G1Xyzz& p, uint32_t k) {
-    G1Xyzz acc = xyzz_zero();
+template <class F>
+G16_HD XyzzT<F> xyzz_mul_small(const XyzzT<F>& p, uint32_t k) {
+    XyzzT<F> acc = xyzz_zero<F>();
     for (int i = 31; i >= 0; --i) {
         if (!xyzz_is_inf(acc)) acc = xyzz_dbl(acc);
         if ((k >> i) & 1u) acc = xyzz_add(acc, p);
     }
     return acc;
+}
+
+// Between the stored form (Fp, canonical) and the digit form of the hot loops.
+G16_HD AffT<Fp29> aff_to29(const G1Aff& a) {
+    AffT<Fp29> r;
+    r.x = fp29_from_fp(a.x);
+    r.y = fp29_from_fp(a.y);
+    return r;
+}
+G16_HD XyzzT<Fp29> xyzz_to29(const G1Xyzz& a) {
+    XyzzT<Fp29> r;
+    r.x = fp29_from_fp(a.x);
+    r.y = fp29_from_fp(a.y);
+    r.zz = fp29_from_fp(a.zz);
+    r.zzz = fp29_from_fp(a.zzz);
+    return r;
+}
+// Infinity stays all zero (ZZ's exact zero is kept rather than reduced).
+G16_HD G1Xyzz xyzz_from29(const XyzzT<Fp29>& a) {
+    if (xyzz_is_inf(a)) return xyzz_zero<Fp>();
+    G1Xyzz r;
+    r.x = fp29_to_fp(a.x);
+    r.y = fp29_to_fp(a.y);
+    r.zz = fp29_to_fp(a.zz);
+    r.zzz = fp29_to_fp(a.zzz);
+    return r;
 }
 
 // (X/ZZ, Y/ZZZ) with one inversion: t = (ZZ ZZZ)^-1, 1/ZZ = t ZZZ, 1/ZZZ = t ZZ.

@@ -10,7 +10,8 @@
 //   * load-balanced accumulation: fixed-length slices of the sorted entries, one thread
 //     each; a run strictly inside a slice is written to its bucket directly, the first
 //     and last run of a slice go to two spill slots, and a merge pass adds each bucket's
-//     spills; XYZZ accumulators with affine bases;
+//     spills; XYZZ accumulators with affine bases, the arithmetic of every point kernel
+//     in nine 29-bit digits (fp29.hpp) between loads and stores of canonical values;
 //   * each window reduced to sum_m m B_m on the device; the host combines the windows
 //     by Horner's rule (the page's "THE WINDOW REDUCTION ENDS ON THE HOST").
 //
@@ -249,27 +250,27 @@ __global__ void __launch_bounds__(kMsmThreads) msm_accumulate(const uint2* entri
     const uint2* ew = entries + (size_t)w * mp.n;
     uint32_t cur = ew[lo].x;
     bool first = true;
-    G1Xyzz acc = xyzz_zero();
+    XyzzT<Fp29> acc = xyzz_zero<Fp29>();
     for (uint32_t e = lo; e < hi; ++e) {
         const uint2 ent = ew[e];
         if (ent.x != cur) {
             if (first) {
                 spill_rows[head] = cur;
-                msm_st_xyzz(spill_pts + head, acc);
+                msm_st_xyzz(spill_pts + head, xyzz_from29(acc));
                 first = false;
             } else {
-                msm_st_xyzz(buckets + cur, acc);
+                msm_st_xyzz(buckets + cur, xyzz_from29(acc));
             }
-            acc = xyzz_zero();
+            acc = xyzz_zero<Fp29>();
             cur = ent.x;
         }
-        G1Aff b = msm_ld_aff(bases + (ent.y >> 1));
-        if (ent.y & 1u) b.y = fp_neg(b.y);
+        AffT<Fp29> b = aff_to29(msm_ld_aff(bases + (ent.y >> 1)));
+        if (ent.y & 1u) b.y = fp29_neg(b.y);
         acc = xyzz_madd(acc, b);
     }
     const uint32_t slot = first ? head : tail;
     spill_rows[slot] = cur;
-    msm_st_xyzz(spill_pts + slot, acc);
+    msm_st_xyzz(spill_pts + slot, xyzz_from29(acc));
 }
 
 // Pass 5: one thread per bucket row with entries.  Starts from the direct write when
@@ -292,13 +293,14 @@ __global__ void __launch_bounds__(kMsmThreads) msm_merge(const uint32_t* counts,
     const uint32_t slice_lo = k_lo * mp.slice_len;
     const uint32_t slice_hi = slice_lo + mp.slice_len < used ? slice_lo + mp.slice_len : used;
     const bool direct = k_lo == k_hi && start > slice_lo && end < slice_hi;
-    G1Xyzz acc = direct ? msm_ld_xyzz(buckets + row) : xyzz_zero();
+    XyzzT<Fp29> acc = direct ? xyzz_to29(msm_ld_xyzz(buckets + row)) : xyzz_zero<Fp29>();
     for (uint32_t k = k_lo; k <= k_hi; ++k) {
         const uint32_t slot = 2u * (w * mp.slices + k);
-        if (spill_rows[slot] == row) acc = xyzz_add(acc, msm_ld_xyzz(spill_pts + slot));
-        if (spill_rows[slot + 1u] == row) acc = xyzz_add(acc, msm_ld_xyzz(spill_pts + slot + 1u));
+        if (spill_rows[slot] == row) acc = xyzz_add(acc, xyzz_to29(msm_ld_xyzz(spill_pts + slot)));
+        if (spill_rows[slot + 1u] == row)
+            acc = xyzz_add(acc, xyzz_to29(msm_ld_xyzz(spill_pts + slot + 1u)));
     }
-    msm_st_xyzz(buckets + row, acc);
+    msm_st_xyzz(buckets + row, xyzz_from29(acc));
 }
 
 // Pass 6: the window sum sum_m m B_m, bucket j holding magnitude m = j + 1.  One thread
@@ -313,13 +315,13 @@ __global__ void __launch_bounds__(kMsmThreads) msm_reduce_segments(const uint32_
     if (w >= mp.windows) return;
     const uint32_t lo = (gid - w * mp.segs) * mp.seg_len;
     const size_t base = (size_t)w * mp.buckets;
-    G1Xyzz run = xyzz_zero(), tot = xyzz_zero();
+    XyzzT<Fp29> run = xyzz_zero<Fp29>(), tot = xyzz_zero<Fp29>();
     for (uint32_t j = lo + mp.seg_len; j-- > lo;) {
-        if (counts[base + j]) run = xyzz_add(run, msm_ld_xyzz(buckets + base + j));
+        if (counts[base + j]) run = xyzz_add(run, xyzz_to29(msm_ld_xyzz(buckets + base + j)));
         tot = xyzz_add(tot, run);
     }
     if (lo) tot = xyzz_add(tot, xyzz_mul_small(run, lo));
-    msm_st_xyzz(seg_out + gid, tot);
+    msm_st_xyzz(seg_out + gid, xyzz_from29(tot));
 }
 
 // The scalar-one pass: sum of the bases whose scalar is exactly 1, strided over the
@@ -327,20 +329,20 @@ __global__ void __launch_bounds__(kMsmThreads) msm_reduce_segments(const uint32_
 __global__ void __launch_bounds__(kMsmThreads) msm_ones(const uint32_t* scalars,
                                                         const G1Aff* bases, MsmParams mp,
                                                         G1Xyzz* out) {
-    __shared__ G1Xyzz sh[kMsmThreads];
+    __shared__ XyzzT<Fp29> sh[kMsmThreads];
     const uint32_t t = threadIdx.x;
-    G1Xyzz acc = xyzz_zero();
+    XyzzT<Fp29> acc = xyzz_zero<Fp29>();
     for (uint32_t i = blockIdx.x * kMsmThreads + t; i < mp.n; i += mp.ones_groups * kMsmThreads) {
         uint32_t k[8];
         msm_load_scalar(scalars, i, k);
-        if (msm_scalar_kind(k) == 1u) acc = xyzz_madd(acc, msm_ld_aff(bases + i));
+        if (msm_scalar_kind(k) == 1u) acc = xyzz_madd(acc, aff_to29(msm_ld_aff(bases + i)));
     }
     sh[t] = acc;
     for (uint32_t s = kMsmThreads / 2; s > 0; s >>= 1) {
         __syncthreads();
         if (t < s) sh[t] = xyzz_add(sh[t], sh[t + s]);
     }
-    if (t == 0) msm_st_xyzz(out + blockIdx.x, sh[0]);
+    if (t == 0) msm_st_xyzz(out + blockIdx.x, xyzz_from29(sh[0]));
 }
 
 // Pass 7: group sums.  Workgroup g adds in[g per, (g + 1) per) (and, for g = 0, the
@@ -350,19 +352,20 @@ __global__ void __launch_bounds__(kMsmThreads) msm_ones(const uint32_t* scalars,
 __global__ void __launch_bounds__(kMsmThreads) msm_sum_groups(const G1Xyzz* in, uint32_t per,
                                                               const G1Xyzz* extra,
                                                               uint32_t n_extra, G1Xyzz* out) {
-    __shared__ G1Xyzz sh[kMsmThreads];
+    __shared__ XyzzT<Fp29> sh[kMsmThreads];
     const uint32_t g = blockIdx.x, t = threadIdx.x;
-    G1Xyzz acc = xyzz_zero();
+    XyzzT<Fp29> acc = xyzz_zero<Fp29>();
     for (uint32_t s = t; s < per; s += kMsmThreads)
-        acc = xyzz_add(acc, msm_ld_xyzz(in + (size_t)g * per + s));
+        acc = xyzz_add(acc, xyzz_to29(msm_ld_xyzz(in + (size_t)g * per + s)));
     if (g == 0)
-        for (uint32_t e = t; e < n_extra; e += kMsmThreads) acc = xyzz_add(acc, msm_ld_xyzz(extra + e));
+        for (uint32_t e = t; e < n_extra; e += kMsmThreads)
+            acc = xyzz_add(acc, xyzz_to29(msm_ld_xyzz(extra + e)));
     sh[t] = acc;
     for (uint32_t s = kMsmThreads / 2; s > 0; s >>= 1) {
         __syncthreads();
         if (t < s) sh[t] = xyzz_add(sh[t], sh[t + s]);
     }
-    if (t == 0) msm_st_xyzz(out + g, sh[0]);
+    if (t == 0) msm_st_xyzz(out + g, xyzz_from29(sh[0]));
 }
 
 // Synthetic bases and fixed-base multiples: out_i = k_i G in affine Montgomery form, one
@@ -373,13 +376,13 @@ __global__ void __launch_bounds__(kMsmThreads) g1_generator_mul(const uint32_t* 
     if (i >= n) return;
     uint32_t k[8];
     msm_load_scalar(scalars, i, k);
-    const G1Aff g = g1_generator();
-    G1Xyzz acc = xyzz_zero();
+    const AffT<Fp29> g = aff_to29(g1_generator());
+    XyzzT<Fp29> acc = xyzz_zero<Fp29>();
     for (int bit = 255; bit >= 0; --bit) {
         acc = xyzz_dbl(acc);
         if ((k[bit >> 5] >> (bit & 31)) & 1u) acc = xyzz_madd(acc, g);
     }
-    const G1Aff a = xyzz_to_aff(acc);
+    const G1Aff a = xyzz_to_aff(xyzz_from29(acc));
     msm_st_fp(&out[i].x, a.x);
     msm_st_fp(&out[i].y, a.y);
 }

@@ -71,6 +71,40 @@ int main() {
             put(op == "fpinv" ? g16::fp_inv(x) : op == "tomont" ? g16::fp_to_mont(x)
                 : op == "frommont" ? g16::fp_from_mont(x) : g16::fp_neg(x));
             std::printf("\n");
+        } else if (op == "f29mul" || op == "f29add" || op == "f29sub" || op == "f29canon") {
+            // through the 29-bit digit form: in and out canonical 2^256 Montgomery form
+            g16::Fp29 x = g16::fp29_from_fp(parse(a[0])), y = g16::fp29_from_fp(parse(a[1]));
+            g16::Fp29 z = op == "f29mul" ? g16::fp29_mul(x, y) : op == "f29add" ? g16::fp29_add(x, y)
+                        : op == "f29sub" ? g16::fp29_sub(x, y) : x;
+            put(g16::fp29_to_fp(z));
+            std::printf("\n");
+        } else if (op == "f29lazy") {    // (x - 7y)(x - 7y) - 5 (x y): lazy inputs far from canonical
+            g16::Fp29 x = g16::fp29_from_fp(parse(a[0])), y = g16::fp29_from_fp(parse(a[1]));
+            g16::Fp29 y7 = g16::fp29_zero();
+            for (int i = 0; i < 7; ++i) y7 = g16::fp29_add(y7, y);
+            g16::Fp29 d = g16::fp29_sub(x, y7);
+            g16::Fp29 xy = g16::fp29_mul(x, y), t = xy;
+            for (int i = 0; i < 4; ++i) t = g16::fp29_add(t, xy);
+            put(g16::fp29_to_fp(g16::fp29_sub(g16::fp29_mul(d, d), t)));
+            std::printf("\n");
+        } else if (op == "madd29") {     // (2 P) + Q in digits
+            auto p = g16::xyzz_dbl(g16::xyzz_to29(g16::xyzz_from_aff(aff_in(a[0], a[1]))));
+            aff_out(g16::xyzz_from29(g16::xyzz_madd(p, g16::aff_to29(aff_in(a[2], a[3])))));
+        } else if (op == "madd129") {    // P + Q in digits, P straight from affine
+            auto p = g16::xyzz_to29(g16::xyzz_from_aff(aff_in(a[0], a[1])));
+            aff_out(g16::xyzz_from29(g16::xyzz_madd(p, g16::aff_to29(aff_in(a[2], a[3])))));
+        } else if (op == "add29") {      // (2 P) + (2 Q) in digits
+            auto p = g16::xyzz_dbl(g16::xyzz_to29(g16::xyzz_from_aff(aff_in(a[0], a[1]))));
+            auto q = g16::xyzz_dbl(g16::xyzz_to29(g16::xyzz_from_aff(aff_in(a[2], a[3]))));
+            aff_out(g16::xyzz_from29(g16::xyzz_add(p, q)));
+        } else if (op == "add129") {
+            auto p = g16::xyzz_to29(g16::xyzz_from_aff(aff_in(a[0], a[1])));
+            auto q = g16::xyzz_to29(g16::xyzz_from_aff(aff_in(a[2], a[3])));
+            aff_out(g16::xyzz_from29(g16::xyzz_add(p, q)));
+        } else if (op == "mulsmall29") {
+            uint32_t k = (uint32_t)std::stoul(a[0], nullptr, 16);
+            auto p = g16::xyzz_to29(g16::xyzz_from_aff(aff_in(a[1], a[2])));
+            aff_out(g16::xyzz_from29(g16::xyzz_mul_small(p, k)));
         } else if (op == "madd") {        // (2 P) + Q, the accumulator with ZZ != 1
             G1Xyzz p = g16::xyzz_dbl(g16::xyzz_from_aff(aff_in(a[0], a[1])));
             aff_out(g16::xyzz_madd(p, aff_in(a[2], a[3])));

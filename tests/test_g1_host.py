@@ -67,6 +67,23 @@ def test_field(driver):
         [(-x) % P for x in xs[:300]]
 
 
+def test_field_digits(driver):
+    """The 29-bit digit form: products, sums, differences and a lazy chain, all through
+    the conversions in and out of the canonical 2^256 form."""
+    rng = random.Random(12)
+    xs = EDGE + rand_below(rng, P, 2000)
+    ys = list(reversed(EDGE)) + rand_below(rng, P, 2000)
+    lines = [(op, x, y) for x, y in zip(xs, ys)
+             for op in ("f29mul", "f29add", "f29sub", "f29canon", "f29lazy")]
+    got = [ints_of(l)[0] for l in run(driver, lines)]
+    want = []
+    for x, y in zip(xs, ys):
+        d = (x - 7 * y) % P
+        want += [x * y * RINV % P, (x + y) % P, (x - y) % P, x,
+                 (d * d * RINV - 5 * x * y * RINV) % P]
+    assert got == want
+
+
 def _points(seed, n):
     ks = [random.Random(seed + i).randrange(1, R) for i in range(n)]
     return msm.words_to_points(msm.scalar_mul(msm.to_words(ks)))
@@ -111,6 +128,40 @@ def test_point_formulas_against_oracle(driver):
     d4 = _oracle_dbl(p2)
     for i in range(len(ps)):
         want += [s1[i], s2[i], s3[i], s2[i], d4[i], p2[i]]
+    assert got == want
+
+
+def test_point_formulas_in_digits(driver):
+    """The same formulas instantiated on the 29-bit digit form (what the device runs)."""
+    ps, qs = _points(110, 60), _points(210, 60)
+    p2 = _oracle_dbl(ps)
+    q2 = _oracle_dbl(qs)
+    lines = []
+    for p, q in zip(ps, qs):
+        lines += [("madd29", *p, *q), ("madd129", *p, *q), ("add29", *p, *q), ("add129", *p, *q)]
+    got = _out(run(driver, lines))
+    s1, s2, s3 = _oracle_add(p2, qs), _oracle_add(ps, qs), _oracle_add(p2, q2)
+    want = []
+    for i in range(len(ps)):
+        want += [s1[i], s2[i], s3[i], s2[i]]
+    assert got == want
+    neg = msm.words_to_points(msm.affine_op("neg", msm.points_to_words(ps)))
+    inf = (0, 0)
+    lines = []
+    for p, m in zip(ps[:10], neg[:10]):
+        lines += [("madd129", *p, *p), ("madd129", *p, *m), ("add129", *p, *p),
+                  ("add129", *p, *m), ("madd129", *inf, *p), ("madd129", *p, *inf),
+                  ("add129", *inf, *inf)]
+    got = _out(run(driver, lines))
+    want = []
+    for p, d in zip(ps[:10], p2[:10]):
+        want += [d, None, d, None, p, p, None]
+    assert got == want
+    ks = [0, 1, 2, 3, 255, 32767, 65535, 123456789]
+    got = _out(run(driver, [("mulsmall29", k, *p) for p in ps[:4] for k in ks]))
+    want = []
+    for p in ps[:4]:
+        want += msm.words_to_points(msm.scalar_mul(msm.to_words(ks), p))
     assert got == want
 
 
