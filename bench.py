@@ -32,6 +32,8 @@ FR_BYTES = 32
 # (log n, proofs) of the several-proofs-per-call measurements: small domains, where one
 # call per proof is launch-bound
 BATCH_SHAPES = ((12, 64), (16, 16))
+# the H pipeline's other single-proof workloads (timed beside the headline 2^20 one)
+OTHER_SIZES = (12, 22)
 
 
 def parse():
@@ -243,6 +245,24 @@ def main():
         del pa, pb, pc, phm, phs, pscr
     print("[bench] proof batches: %s" % proof_batches, file=sys.stderr, flush=True)
 
+    # ---- the other single-proof workloads of the H pipeline (2^12 and 2^22), same call
+    other_sizes = {}
+    for olog in OTHER_SIZES:
+        on = 1 << olog
+        octx = g.HContext(olog)
+        oa, ob = (g.to_mont(g.to_device(v)) for v in synth.h_inputs(3, olog))
+        oc = g.fr_mul(oa, ob)
+        ohm, ohs = g.empty_fr(on), g.empty_fr(on)
+        oms = time_ms(lambda: octx.h_compute(oa, ob, oc, ohm, ohs), args.steps)
+        other_sizes["2^%d" % olog] = {
+            "h_pipeline_ms": round(oms, 5),
+            "gbutterfly_s": round(6 * (on // 2) * olog / (oms / 1e3) / 1e9, 3),
+            "pass_batches": g.batch_plan(olog),
+        }
+        octx.release()
+        del oa, ob, oc, ohm, ohs
+    print("[bench] other sizes: %s" % other_sizes, file=sys.stderr, flush=True)
+
     # ---- the timed region: K whole pipelines
     for _ in range(args.warmup):
         ctx.h_compute(ad, bd, cd, hm, hs)
@@ -351,6 +371,7 @@ def main():
         "gather_gnnz_s": round(nnz / (gather_ms / 1e3) / 1e9, 3),
         "gather_hbm_gbs_algorithmic": round(gather_bytes / (gather_ms / 1e3) / 1e9, 2),
         "proof_batches": proof_batches,
+        "other_sizes": other_sizes,
         "msm_g1": msm_line,
         "hbm_gbs_algorithmic": round(total_bytes / (ms_per_step / 1e3) / 1e9, 2),
         "pipeline_tmad_s": round(total_muls / (ms_per_step / 1e3) / 1e12, 3),

@@ -25,6 +25,7 @@ constexpr uint32_t kSegLen = 8;
 constexpr uint32_t kMaxOnesGroups = 64;
 constexpr uint32_t kMinChunk = 65536;   // scalars per sorting workgroup, at least
 constexpr uint32_t kMaxChunks = 64;     // sorting workgroups per window, at most
+constexpr uint32_t kFatGroups = 128;    // workgroups of the long-run merge
 
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -47,10 +48,11 @@ bool device_pointer(const void* p) {
 }
 
 // Window width minimising a cost in point additions: n per window for the accumulation,
-// about three per bucket for the merge and the weighted window sum, and the serial merge
-// of the top window's buckets.  Scalars below r < 2^254 leave the top window only
-// 254 - (W - 1) c bits, so its few buckets hold about n / 2^bits entries each, merged one
-// slice partial after another; a serial addition is priced at the 16384 additions the
+// about three per bucket for the merge and the weighted window sum, and the merge of the
+// top window's buckets.  Scalars below r < 2^254 leave the top window only
+// 254 - (W - 1) c bits, so its few buckets hold about n / 2^bits entries each; a
+// workgroup merges such a bucket's slice partials, 256 at a time and then by a tree of
+// eight levels, and each of those serial additions is priced at the 16384 additions the
 // chip does in parallel meanwhile.
 uint32_t default_c(uint64_t n) {
     uint32_t best = 1;
@@ -59,8 +61,9 @@ uint32_t default_c(uint64_t n) {
         const uint32_t W = windows_for(c);
         const int top_bits = 254 - (int)((W - 1) * c);
         const double fat = (double)n / (double)(1ull << (top_bits > 0 ? top_bits : 0));
+        const double serial = fat / (double)kSliceLen / 256.0 + 8.0;
         const double cost = (double)W * ((double)n + 3.0 * (double)(1u << (c - 1))) +
-                            16384.0 * fat / (double)kSliceLen;
+                            16384.0 * serial;
         if (c == 1 || cost < best_cost) {
             best = c;
             best_cost = cost;
@@ -73,7 +76,7 @@ struct Layout {
     MsmParams mp;
     uint32_t per_group, groups;  // segment sums per partial, partials per window
     size_t counts, cursor, chunk_counts, entries, spill_rows, spill_pts, buckets, seg_out,
-        partials, ones_out, total;
+        partials, ones_out, fat, total;
 };
 
 bool make_layout(uint64_t n, uint32_t c, Layout* L) {
@@ -117,6 +120,7 @@ bool make_layout(uint64_t n, uint32_t c, Layout* L) {
     L->seg_out = take((size_t)W * mp.segs * sizeof(G1Xyzz));
     L->partials = take((size_t)W * L->groups * sizeof(G1Xyzz));
     L->ones_out = take((size_t)mp.ones_groups * sizeof(G1Xyzz));
+    L->fat = take((rows + 1) * 4);  // list length, then the listed rows
     L->total = off;
     return true;
 }
@@ -182,6 +186,8 @@ int g16_msm_g1(uint64_t n, const void* scalars_std, const void* bases_mont, uint
     G1Xyzz* seg_out = (G1Xyzz*)(ws + L.seg_out);
     G1Xyzz* partials = (G1Xyzz*)(ws + L.partials);
     G1Xyzz* ones_out = (G1Xyzz*)(ws + L.ones_out);
+    uint32_t* fat_count = (uint32_t*)(ws + L.fat);
+    uint32_t* fat_rows = fat_count + 1;
     const uint32_t* sc = (const uint32_t*)scalars_std;
     const G1Aff* bases = (const G1Aff*)bases_mont;
     const uint32_t rows = W * mp.buckets;
@@ -198,7 +204,7 @@ int g16_msm_g1(uint64_t n, const void* scalars_std, const void* bases_mont, uint
     hipLaunchKernelGGL(g16::msm_hist, dim3(W * mp.chunks), sort_blk, lds, s, sc, mp, chunk_counts);
     hipLaunchKernelGGL(g16::msm_totals, dim3(blocks_for(rows)), blk, 0, s, chunk_counts, mp,
                        counts);
-    hipLaunchKernelGGL(g16::msm_scan, dim3(W), sort_blk, 0, s, counts, mp, cursor);
+    hipLaunchKernelGGL(g16::msm_scan, dim3(W), sort_blk, 0, s, counts, mp, cursor, fat_count);
     hipLaunchKernelGGL(g16::msm_chunk_offsets, dim3(blocks_for(rows)), blk, 0, s, chunk_counts, mp,
                        cursor);
     hipLaunchKernelGGL(g16::msm_place, dim3(W * mp.chunks), sort_blk, lds, s, sc, mp, chunk_counts,
@@ -206,7 +212,10 @@ int g16_msm_g1(uint64_t n, const void* scalars_std, const void* bases_mont, uint
     hipLaunchKernelGGL(g16::msm_accumulate, dim3(blocks_for((uint64_t)W * mp.slices)), blk, 0, s,
                        entries, bases, cursor, mp, buckets, spill_pts, spill_rows);
     hipLaunchKernelGGL(g16::msm_merge, dim3(blocks_for(rows)), blk, 0, s, counts, cursor,
-                       spill_pts, spill_rows, mp, buckets);
+                       spill_pts, spill_rows, mp, buckets, fat_count, fat_rows);
+    hipLaunchKernelGGL(g16::msm_merge_fat, dim3(kFatGroups), blk, 0, s, counts, cursor, spill_pts,
+                       spill_rows, mp, (const uint32_t*)fat_count, (const uint32_t*)fat_rows,
+                       buckets);
     hipLaunchKernelGGL(g16::msm_reduce_segments, dim3(blocks_for((uint64_t)W * mp.segs)), blk, 0,
                        s, counts, buckets, mp, seg_out);
     hipLaunchKernelGGL(g16::msm_ones, dim3(mp.ones_groups), blk, 0, s, sc, bases, mp, ones_out);

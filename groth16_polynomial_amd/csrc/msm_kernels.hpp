@@ -45,6 +45,8 @@ struct MsmParams {
 };
 
 constexpr uint32_t kMsmNoRow = 0xffffffffu;
+// A bucket whose run spans more slices than this is merged by a workgroup of its own.
+constexpr uint32_t kMsmFatSlices = 8;
 constexpr uint32_t kMsmThreads = 256;
 constexpr uint32_t kMsmSortThreads = 1024;
 
@@ -150,9 +152,10 @@ __global__ void __launch_bounds__(kMsmThreads) msm_totals(const uint32_t* chunk_
 // each thread sums a contiguous range of buckets, the range sums are scanned in LDS, then
 // each thread writes its range's starts.
 __global__ void __launch_bounds__(kMsmSortThreads) msm_scan(const uint32_t* counts, MsmParams mp,
-                                                            uint32_t* cursor) {
+                                                            uint32_t* cursor, uint32_t* fat_count) {
     __shared__ uint32_t sums[kMsmSortThreads];
     const uint32_t w = blockIdx.x, t = threadIdx.x;
+    if (w == 0 && t == 0) *fat_count = 0u;  // the merge pass appends to the list again
     const uint32_t per = (mp.buckets + kMsmSortThreads - 1u) / kMsmSortThreads;
     const uint32_t b0 = t * per;
     const uint32_t b1 = b0 + per < mp.buckets ? b0 + per : mp.buckets;
@@ -275,12 +278,16 @@ __global__ void __launch_bounds__(kMsmThreads) msm_accumulate(const uint2* entri
 
 // Pass 5: one thread per bucket row with entries.  Starts from the direct write when
 // the run lies strictly inside one slice (the accumulation wrote it), else from
-// infinity, and adds the spills of the slices the run overlaps.
+// infinity, and adds the spills of the slices the run overlaps.  A run over more than
+// kMsmFatSlices slices (many equal digits: repeated scalars, or the few buckets of a
+// narrow top window) is appended to a list for msm_merge_fat instead, so that no thread
+// adds thousands of spills one after another.
 __global__ void __launch_bounds__(kMsmThreads) msm_merge(const uint32_t* counts,
                                                          const uint32_t* cursor,
                                                          const G1Xyzz* spill_pts,
                                                          const uint32_t* spill_rows, MsmParams mp,
-                                                         G1Xyzz* buckets) {
+                                                         G1Xyzz* buckets, uint32_t* fat_count,
+                                                         uint32_t* fat_rows) {
     const uint32_t row = blockIdx.x * blockDim.x + threadIdx.x;
     if (row >= mp.windows * mp.buckets) return;
     const uint32_t cnt = counts[row];
@@ -290,6 +297,10 @@ __global__ void __launch_bounds__(kMsmThreads) msm_merge(const uint32_t* counts,
     const uint32_t end = cursor[row] - w * mp.n;
     const uint32_t start = end - cnt;
     const uint32_t k_lo = start / mp.slice_len, k_hi = (end - 1u) / mp.slice_len;
+    if (k_hi - k_lo >= kMsmFatSlices) {
+        fat_rows[atomicAdd(fat_count, 1u)] = row;
+        return;
+    }
     const uint32_t slice_lo = k_lo * mp.slice_len;
     const uint32_t slice_hi = slice_lo + mp.slice_len < used ? slice_lo + mp.slice_len : used;
     const bool direct = k_lo == k_hi && start > slice_lo && end < slice_hi;
@@ -301,6 +312,45 @@ __global__ void __launch_bounds__(kMsmThreads) msm_merge(const uint32_t* counts,
             acc = xyzz_add(acc, xyzz_to29(msm_ld_xyzz(spill_pts + slot + 1u)));
     }
     msm_st_xyzz(buckets + row, xyzz_from29(acc));
+}
+
+// Pass 5b: the listed rows, one workgroup at a time (a grid-stride loop over the list,
+// whose length every thread reads once before the loop, so all reach every barrier):
+// the threads take the run's slices in turn, each adding the spills that carry the row,
+// then a tree in LDS.  Such a run spans at least two slices, so the accumulation never
+// wrote its bucket directly.
+__global__ void __launch_bounds__(kMsmThreads) msm_merge_fat(const uint32_t* counts,
+                                                             const uint32_t* cursor,
+                                                             const G1Xyzz* spill_pts,
+                                                             const uint32_t* spill_rows,
+                                                             MsmParams mp,
+                                                             const uint32_t* fat_count,
+                                                             const uint32_t* fat_rows,
+                                                             G1Xyzz* buckets) {
+    __shared__ XyzzT<Fp29> sh[kMsmThreads];
+    const uint32_t t = threadIdx.x;
+    const uint32_t listed = *fat_count;
+    for (uint32_t i = blockIdx.x; i < listed; i += gridDim.x) {
+        const uint32_t row = fat_rows[i];
+        const uint32_t w = row / mp.buckets;
+        const uint32_t end = cursor[row] - w * mp.n;
+        const uint32_t start = end - counts[row];
+        const uint32_t k_lo = start / mp.slice_len, k_hi = (end - 1u) / mp.slice_len;
+        XyzzT<Fp29> acc = xyzz_zero<Fp29>();
+        for (uint32_t k = k_lo + t; k <= k_hi; k += kMsmThreads) {
+            const uint32_t slot = 2u * (w * mp.slices + k);
+            if (spill_rows[slot] == row) acc = xyzz_add(acc, xyzz_to29(msm_ld_xyzz(spill_pts + slot)));
+            if (spill_rows[slot + 1u] == row)
+                acc = xyzz_add(acc, xyzz_to29(msm_ld_xyzz(spill_pts + slot + 1u)));
+        }
+        sh[t] = acc;
+        for (uint32_t s = kMsmThreads / 2; s > 0; s >>= 1) {
+            __syncthreads();
+            if (t < s) sh[t] = xyzz_add(sh[t], sh[t + s]);
+        }
+        if (t == 0) msm_st_xyzz(buckets + row, xyzz_from29(sh[0]));
+        __syncthreads();  // sh is reused by the next listed row
+    }
 }
 
 // Pass 6: the window sum sum_m m B_m, bucket j holding magnitude m = j + 1.  One thread

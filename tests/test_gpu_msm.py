@@ -151,6 +151,27 @@ def test_msm_large_by_linearity(log_n):
     assert np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("case", ["all_equal", "mixed", "narrow_windows"])
+def test_msm_long_runs(case):
+    """Buckets with runs over many slices (merged by a workgroup each): every scalar
+    equal, a third of them equal to one value and a fifth to another, and uniform scalars
+    with 6-bit windows (32 buckets of ~1000 entries per window)."""
+    n = 1 << 15 if case != "all_equal" else 1 << 14
+    say("msm long runs: %s n=%d" % (case, n))
+    s = synth.uniform_fr(400, n)
+    k = synth.uniform_fr(401, n)
+    if case == "all_equal":
+        k[:] = k[0]
+    elif case == "mixed":
+        k[: n // 3] = k[0]
+        k[n // 3: n // 3 + n // 5] = k[1]
+    c = 6 if case == "narrow_windows" else 0
+    bases = g.g1_generator_mul(dev(s))
+    got = g.MsmG1(n, c)(dev(k), bases)
+    total = sum(a * b for a, b in zip(ints(k), ints(s))) % R
+    assert np.array_equal(got, msm.scalar_mul(msm.to_words([total]))[0])
+
+
 def test_msm_of_h_std():
     """The MSM's input in a prover: h_std of the H pipeline (2^12 here), compared with
     the oracle's MSM of the oracle's own h_std."""
