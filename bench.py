@@ -133,7 +133,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only (--gpus %d requested); the "
-              "multi-GPU sharding is described in DESIGN.md and not implemented"
+              "multi-GPU sharding is designed but not implemented"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
 
