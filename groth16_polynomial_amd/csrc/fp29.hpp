@@ -197,6 +197,18 @@ G16_HD Fp fp29_canon(const Fp29& a) {
 
 G16_HD bool fp29_is_zero(const Fp29& a) { return fp_is_zero(fp29_canon(a)); }
 
+// a^(p-2) = a^-1 (Fermat; 0 -> 0), square and multiply in the 2^261 Montgomery form.
+G16_HD Fp29 fp29_inv(const Fp29& a) {
+    Fp29 acc = fp29_from_fp(fp_one());
+    for (int bit = 253; bit >= 0; --bit) {
+        acc = fp29_sqr(acc);
+        uint32_t e = p_limb(bit >> 5);
+        if ((bit >> 5) == 0) e -= 2u;  // low limb of p - 2 (p's low limb is odd and large)
+        if ((e >> (bit & 31)) & 1u) acc = fp29_mul(acc, a);
+    }
+    return acc;
+}
+
 // -> canonical 2^256 Montgomery form: (value mod p) 2^-5 = (c + k p) / 32 with
 // k = c (-p^-1) mod 32, which is below p for c < p.
 G16_HD Fp fp29_to_fp(const Fp29& a) {

@@ -234,6 +234,20 @@ G16_HD G1Aff xyzz_to_aff(const G1Xyzz& p) {
     return a;
 }
 
+// The same from the digit form: one inversion in digits, then canonical coordinates.
+G16_HD G1Aff xyzz_to_aff(const XyzzT<Fp29>& p) {
+    G1Aff a;
+    if (xyzz_is_inf(p)) {
+        a.x = fp_zero();
+        a.y = fp_zero();
+        return a;
+    }
+    const Fp29 t = fp29_inv(fp29_mul(p.zz, p.zzz));
+    a.x = fp29_to_fp(fp29_mul(p.x, fp29_mul(t, p.zzz)));
+    a.y = fp29_to_fp(fp29_mul(p.y, fp29_mul(t, p.zz)));
+    return a;
+}
+
 // The generator (1, 2), Montgomery form.
 G16_HD G1Aff g1_generator() {
     Fp one = fp_zero(), two = fp_zero();

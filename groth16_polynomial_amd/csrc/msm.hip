@@ -230,10 +230,12 @@ int g16_msm_g1_finish(uint32_t c, const void* window_sums_host, void* out_affine
     if (c < 1 || c > kMaxC || !window_sums_host || !out_affine_std) return G16_EINVAL;
     const uint32_t W = windows_for(c);
     const G1Xyzz* ws = (const G1Xyzz*)window_sums_host;
-    G1Xyzz acc = ws[W - 1];
+    // in the 29-bit digit form: on the host its digit products are native 64-bit
+    // multiplies, about half the time of the 32-bit-limb products
+    g16::XyzzT<g16::Fp29> acc = g16::xyzz_to29(ws[W - 1]);
     for (uint32_t w = W - 1; w-- > 0;) {
         for (uint32_t i = 0; i < c; ++i) acc = g16::xyzz_dbl(acc);
-        acc = g16::xyzz_add(acc, ws[w]);
+        acc = g16::xyzz_add(acc, g16::xyzz_to29(ws[w]));
     }
     const G1Aff a = g16::xyzz_to_aff(acc);
     const g16::Fp x = g16::fp_from_mont(a.x), y = g16::fp_from_mont(a.y);

@@ -432,7 +432,7 @@ __global__ void __launch_bounds__(kMsmThreads) g1_generator_mul(const uint32_t* 
         acc = xyzz_dbl(acc);
         if ((k[bit >> 5] >> (bit & 31)) & 1u) acc = xyzz_madd(acc, g);
     }
-    const G1Aff a = xyzz_to_aff(xyzz_from29(acc));
+    const G1Aff a = xyzz_to_aff(acc);
     msm_st_fp(&out[i].x, a.x);
     msm_st_fp(&out[i].y, a.y);
 }
