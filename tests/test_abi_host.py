@@ -64,6 +64,26 @@ def test_batch_scratch_bytes(lib):
     assert f(27, 17) == 0
 
 
+def test_msm_sizes(lib):
+    """Window counts, default widths and workspace limits of the G1 MSM (host only)."""
+    assert lib.g16_msm_g1_window_count(0) == 0 and lib.g16_msm_g1_window_count(17) == 0
+    for c in range(1, 17):
+        assert lib.g16_msm_g1_window_count(c) == -(-255 // c)
+    for log_n in range(0, 27):
+        c = lib.g16_msm_g1_window_bits(1 << log_n)
+        assert 1 <= c <= 16
+        assert lib.g16_msm_g1_workspace_bytes(1 << log_n, 0) > 0
+    assert lib.g16_msm_g1_window_bits(1 << 20) == 16
+    assert lib.g16_msm_g1_workspace_bytes(0, 16) == 0            # empty: nothing needed
+    assert lib.g16_msm_g1_workspace_bytes(1 << 20, 17) == 0      # c beyond the LDS counters
+    assert lib.g16_msm_g1_workspace_bytes(1 << 28, 16) == 0      # windows * n reaches 2^32
+    assert lib.g16_msm_g1_workspace_bytes((1 << 28) - 1, 16) > 0
+    fake = ctypes.c_void_p(0x100000)
+    assert lib.g16_msm_g1(16, fake, fake, 17, fake, 1 << 20, None, None) == binding.G16_EINVAL
+    assert lib.g16_g1_generator_mul(0, fake, fake, None) == binding.G16_EINVAL
+    assert lib.g16_msm_g1_finish(16, None, None) == binding.G16_EINVAL
+
+
 def test_batch_plan_matches_page(lib):
     with open(GOLDEN) as f:
         rows = [list(map(int, l.split())) for l in f if l.strip() and not l.startswith("#")]

@@ -136,7 +136,7 @@ def test_msm_top_scalars():
         _msm_case(600, c, seed=31 + c, mutate=mutate)
 
 
-@pytest.mark.parametrize("log_n", [16, 18, 20])
+@pytest.mark.parametrize("log_n", [16, 18, 20, 22])
 def test_msm_large_by_linearity(log_n):
     """Bases s_i G made on the GPU, scalars k_i: the result is (sum k_i s_i mod r) G."""
     n = 1 << log_n
