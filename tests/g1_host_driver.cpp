@@ -78,6 +78,10 @@ int main() {
                         : op == "f29sub" ? g16::fp29_sub(x, y) : x;
             put(g16::fp29_to_fp(z));
             std::printf("\n");
+        } else if (op == "f29zero") {    // zero tests of a + b and a - b (lazy, below 64p)
+            g16::Fp29 x = g16::fp29_from_fp(parse(a[0])), y = g16::fp29_from_fp(parse(a[1]));
+            std::printf("%d %d\n", (int)g16::fp29_is_zero(g16::fp29_add(x, y)),
+                        (int)g16::fp29_is_zero(g16::fp29_sub(x, y)));
         } else if (op == "f29lazy") {    // (x - 7y)(x - 7y) - 5 (x y): lazy inputs far from canonical
             g16::Fp29 x = g16::fp29_from_fp(parse(a[0])), y = g16::fp29_from_fp(parse(a[1]));
             g16::Fp29 y7 = g16::fp29_zero();

@@ -84,6 +84,22 @@ def test_field_digits(driver):
     assert got == want
 
 
+def test_digit_zero_test(driver):
+    """The exact zero test of the digit form on lazy values: 32 (a + b) is a multiple of p
+    (nonzero digits) when a + b = p, and 32 (a - b) when a = b; one off is not zero."""
+    rng = random.Random(13)
+    cases = []
+    for _ in range(300):
+        a = rng.randrange(1, P)
+        cases += [(a, P - a), (a, a), (a, (P - a + 1) % P), (a, (a + 1) % P), (a, rng.randrange(P))]
+    cases += [(0, 0), (1, P - 1), (P - 1, 1), (P - 1, P - 1)]
+    got = run(driver, [("f29zero", a, b) for a, b in cases])
+    for (a, b), line in zip(cases, got):
+        s, d = (int(v) for v in line.split())
+        assert s == int((a + b) % P == 0), (a, b)
+        assert d == int((a - b) % P == 0), (a, b)
+
+
 def _points(seed, n):
     ks = [random.Random(seed + i).randrange(1, R) for i in range(n)]
     return msm.words_to_points(msm.scalar_mul(msm.to_words(ks)))
