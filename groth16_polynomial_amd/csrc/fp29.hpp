@@ -21,7 +21,10 @@
 // The product is Montgomery's REDC in radix 2^29 (P. L. Montgomery, Math. Comp. 1985),
 // in the product-scanning order: column k takes carry + sum a_i b_(k-i) + sum m_i p_(k-i),
 // for k < 9 the digit m_k = (column * -p^-1) mod 2^29 that clears the column, for k >= 9
-// the result digit.  162 digit products.
+// the result digit.  162 digit products; a square takes 126 (the cross products once,
+// against a doubled digit), and a b - c d takes 243 with one reduction.  On the device
+// each column is one chain of multiply-adds from the carry (fp29_cols.hpp): 212
+// instructions a product against 228 for the compiler's own reassociated columns.
 #pragma once
 
 #include "fp.hpp"
@@ -106,37 +109,104 @@ G16_HD Fp29 fp29_sub(const Fp29& a, const Fp29& b) {
 G16_HD Fp29 fp29_neg(const Fp29& a) { return fp29_sub(fp29_zero(), a); }
 G16_HD Fp29 fp29_dbl(const Fp29& a) { return fp29_add(a, a); }
 
-// a b 2^-261 mod p, lazily reduced (see the header).  Inputs normalized.
-G16_HD Fp29 fp29_mul(const Fp29& a, const Fp29& b) {
-    int64_t carry = 0;
+}  // namespace g16
+
+#include "fp29_cols.hpp"
+
+namespace g16 {
+
+// REDC in the product-scanning order over the columns that COL adds to the running sum
+// (carry + the column's digit products + m_i p_(k-i) for the Montgomery digits already
+// known): below column 9 the column fixes m_k = (column (-p^-1)) mod 2^29 and adds m_k p_0,
+// which clears its low 29 bits; from column 9 on it gives result digit k - 9.
+template <class Col>
+G16_HD Fp29 fp29_redc(Col col) {
+    int64_t acc = 0;
     uint32_t m[9];
     Fp29 r;
     static_for<17>([&](auto k_c) {
         constexpr int k = decltype(k_c)::value;
-        int64_t col = carry;
-        static_for<9>([&](auto i_c) {
-            constexpr int i = decltype(i_c)::value;
-            constexpr int j = k - i;
-            if constexpr (j >= 0 && j < 9) col += (int64_t)a.d[i] * (int64_t)b.d[j];
-        });
-        static_for<9>([&](auto i_c) {
-            constexpr int i = decltype(i_c)::value;
-            constexpr int j = k - i;
-            if constexpr (i < k && j >= 1 && j < 9) col += (int64_t)m[i] * (int64_t)p29_digit(j);
-        });
+        col(k_c, acc, m);
         if constexpr (k < 9) {
-            m[k] = ((uint32_t)col * kP29NInv) & kM29;
-            col += (int64_t)m[k] * (int64_t)p29_digit(0);
+            m[k] = ((uint32_t)acc * kP29NInv) & kM29;
+            acc += (int64_t)m[k] * (int64_t)p29_digit(0);
         } else {
-            r.d[k - 9] = (int32_t)((uint32_t)col & kM29);
+            r.d[k - 9] = (int32_t)((uint32_t)acc & kM29);
         }
-        carry = col >> 29;
+        acc >>= 29;
     });
-    r.d[8] = (int32_t)carry;
+    r.d[8] = (int32_t)acc;
     return r;
 }
 
-G16_HD Fp29 fp29_sqr(const Fp29& a) { return fp29_mul(a, a); }
+// The host's columns: the digit products x_i y_(k-i) of column k, and its Montgomery
+// terms m_i p_(k-i) for the m_i already known (i < k).
+template <int k>
+G16_HD int64_t fp29_col_xy(const Fp29& x, const Fp29& y) {
+    int64_t col = 0;
+    static_for<9>([&](auto i_c) {
+        constexpr int i = decltype(i_c)::value;
+        constexpr int j = k - i;
+        if constexpr (j >= 0 && j < 9) col += (int64_t)x.d[i] * (int64_t)y.d[j];
+    });
+    return col;
+}
+template <int k>
+G16_HD int64_t fp29_col_mp(const uint32_t (&m)[9]) {
+    int64_t col = 0;
+    static_for<9>([&](auto i_c) {
+        constexpr int i = decltype(i_c)::value;
+        constexpr int j = k - i;
+        if constexpr (i < k && j >= 1 && j < 9) col += (int64_t)m[i] * (int64_t)p29_digit(j);
+    });
+    return col;
+}
+
+// a b 2^-261 mod p, lazily reduced (see the header).  Inputs normalized.  On the device
+// each column is one chain of v_mad_i64_i32 from fp29_cols.hpp.
+G16_HD Fp29 fp29_mul(const Fp29& a, const Fp29& b) {
+    return fp29_redc([&](auto k_c, int64_t& acc, const uint32_t (&m)[9]) {
+        constexpr int k = decltype(k_c)::value;
+#if defined(__HIP_DEVICE_COMPILE__)
+        fp29_col_mul<k>(acc, a, b, m);
+#else
+        acc += fp29_col_xy<k>(a, b) + fp29_col_mp<k>(m);
+#endif
+    });
+}
+
+// a^2 2^-261: the same columns as fp29_mul(a, a), formed on the device from (2 a_i) a_j
+// for i < j and a_i^2 (45 digit products instead of 81; each column's bound is that of
+// a product, as a doubled digit product counts for two).
+G16_HD Fp29 fp29_sqr(const Fp29& a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    int32_t a2[9];
+#pragma unroll
+    for (int k = 0; k < 9; ++k) a2[k] = a.d[k] + a.d[k];
+    return fp29_redc([&](auto k_c, int64_t& acc, const uint32_t (&m)[9]) {
+        fp29_col_sqr<decltype(k_c)::value>(acc, a, a2, m);
+    });
+#else
+    return fp29_mul(a, a);
+#endif
+}
+
+// (a b - c d) 2^-261 with one reduction: a column holds both products' digit products
+// (27 terms below 2^58 with the Montgomery terms, below 2^63), and the result is below
+// (|a b| + |c d|) 2^-261 + p, no more than the difference of two reduced products.
+G16_HD Fp29 fp29_mul_sub(const Fp29& a, const Fp29& b, const Fp29& c, const Fp29& d) {
+    Fp29 nc;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) nc.d[k] = -c.d[k];
+    return fp29_redc([&](auto k_c, int64_t& acc, const uint32_t (&m)[9]) {
+        constexpr int k = decltype(k_c)::value;
+#if defined(__HIP_DEVICE_COMPILE__)
+        fp29_col_mulsub<k>(acc, a, b, nc, d, m);
+#else
+        acc += fp29_col_xy<k>(a, b) + fp29_col_xy<k>(nc, d) + fp29_col_mp<k>(m);
+#endif
+    });
+}
 
 // The value mod p, canonical, as eight 32-bit words (not converted out of the 2^261
 // Montgomery form).  |value| < 64 p: u = value + 64 p is in (0, 128 p), below 2^261; q

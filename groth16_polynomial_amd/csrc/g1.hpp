@@ -31,6 +31,9 @@ G16_HD Fp f_dbl(const Fp& a) { return fp_dbl(a); }
 G16_HD Fp f_neg(const Fp& a) { return fp_neg(a); }
 G16_HD Fp f_mul(const Fp& a, const Fp& b) { return fp_mul(a, b); }
 G16_HD Fp f_sqr(const Fp& a) { return fp_sqr(a); }
+G16_HD Fp f_mul_sub(const Fp& a, const Fp& b, const Fp& c, const Fp& d) {
+    return fp_sub(fp_mul(a, b), fp_mul(c, d));
+}
 G16_HD bool f_is_zero(const Fp& a) { return fp_is_zero(a); }
 G16_HD bool f_inf(const Fp& a) { return fp_is_zero(a); }
 G16_HD Fp29 f_add(const Fp29& a, const Fp29& b) { return fp29_add(a, b); }
@@ -39,6 +42,9 @@ G16_HD Fp29 f_dbl(const Fp29& a) { return fp29_dbl(a); }
 G16_HD Fp29 f_neg(const Fp29& a) { return fp29_neg(a); }
 G16_HD Fp29 f_mul(const Fp29& a, const Fp29& b) { return fp29_mul(a, b); }
 G16_HD Fp29 f_sqr(const Fp29& a) { return fp29_sqr(a); }
+G16_HD Fp29 f_mul_sub(const Fp29& a, const Fp29& b, const Fp29& c, const Fp29& d) {
+    return fp29_mul_sub(a, b, c, d);
+}
 G16_HD bool f_is_zero(const Fp29& a) { return fp29_is_zero(a); }
 G16_HD bool f_inf(const Fp29& a) { return fp29_digits_zero(a); }
 
@@ -113,7 +119,7 @@ G16_HD XyzzT<F> xyzz_dbl_aff(const AffT<F>& q) {
     const F m = f_three_sq(q.x);
     XyzzT<F> r;
     r.x = f_sub(f_sqr(m), f_dbl(s));
-    r.y = f_sub(f_mul(m, f_sub(s, r.x)), f_mul(w, q.y));
+    r.y = f_mul_sub(m, f_sub(s, r.x), w, q.y);
     r.zz = v;
     r.zzz = w;
     return r;
@@ -129,7 +135,7 @@ G16_HD XyzzT<F> xyzz_dbl(const XyzzT<F>& p) {
     const F m = f_three_sq(p.x);
     XyzzT<F> r;
     r.x = f_sub(f_sqr(m), f_dbl(s));
-    r.y = f_sub(f_mul(m, f_sub(s, r.x)), f_mul(w, p.y));
+    r.y = f_mul_sub(m, f_sub(s, r.x), w, p.y);
     r.zz = f_mul(v, p.zz);
     r.zzz = f_mul(w, p.zzz);
     return r;
@@ -152,7 +158,7 @@ G16_HD XyzzT<F> xyzz_madd(const XyzzT<F>& p, const AffT<F>& q) {
     const F qv = f_mul(p.x, pp);
     XyzzT<F> r;
     r.x = f_sub(f_sub(f_sqr(rd), ppp), f_dbl(qv));
-    r.y = f_sub(f_mul(rd, f_sub(qv, r.x)), f_mul(p.y, ppp));
+    r.y = f_mul_sub(rd, f_sub(qv, r.x), p.y, ppp);
     r.zz = f_mul(p.zz, pp);
     r.zzz = f_mul(p.zzz, ppp);
     return r;
@@ -177,7 +183,7 @@ G16_HD XyzzT<F> xyzz_add(const XyzzT<F>& p, const XyzzT<F>& q) {
     const F qv = f_mul(u1, pp);
     XyzzT<F> r;
     r.x = f_sub(f_sub(f_sqr(rd), ppp), f_dbl(qv));
-    r.y = f_sub(f_mul(rd, f_sub(qv, r.x)), f_mul(s1, ppp));
+    r.y = f_mul_sub(rd, f_sub(qv, r.x), s1, ppp);
     r.zz = f_mul(f_mul(p.zz, q.zz), pp);
     r.zzz = f_mul(f_mul(p.zzz, q.zzz), ppp);
     return r;

@@ -78,6 +78,14 @@ int main() {
                         : op == "f29sub" ? g16::fp29_sub(x, y) : x;
             put(g16::fp29_to_fp(z));
             std::printf("\n");
+        } else if (op == "f29sqr") {
+            put(g16::fp29_to_fp(g16::fp29_sqr(g16::fp29_from_fp(parse(a[0])))));
+            std::printf("\n");
+        } else if (op == "f29mulsub") {  // a b - c d with one reduction
+            g16::Fp29 v[4];
+            for (int i = 0; i < 4; ++i) v[i] = g16::fp29_from_fp(parse(a[i]));
+            put(g16::fp29_to_fp(g16::fp29_mul_sub(v[0], v[1], v[2], v[3])));
+            std::printf("\n");
         } else if (op == "f29zero") {    // zero tests of a + b and a - b (lazy, below 64p)
             g16::Fp29 x = g16::fp29_from_fp(parse(a[0])), y = g16::fp29_from_fp(parse(a[1]));
             std::printf("%d %d\n", (int)g16::fp29_is_zero(g16::fp29_add(x, y)),

@@ -82,6 +82,14 @@ def test_field_digits(driver):
         want += [x * y * RINV % P, (x + y) % P, (x - y) % P, x,
                  (d * d * RINV - 5 * x * y * RINV) % P]
     assert got == want
+    zs = rand_below(rng, P, 2000)
+    ws = list(reversed(zs))
+    lines = [("f29sqr", x) for x in xs] + \
+        [("f29mulsub", x, y, z, w) for x, y, z, w in zip(xs, ys, zs + EDGE, ws + EDGE)]
+    got = [ints_of(l)[0] for l in run(driver, lines)]
+    want = [x * x * RINV % P for x in xs] + \
+        [(x * y - z * w) * RINV % P for x, y, z, w in zip(xs, ys, zs + EDGE, ws + EDGE)]
+    assert got == want
 
 
 def test_digit_zero_test(driver):
@@ -265,3 +273,9 @@ def test_host_window_combination(lib, c):
     assert np.array_equal(out, want)
     assert lib.g16_msm_g1_finish(0, sums.ctypes.data, out.ctypes.data) == binding.G16_EINVAL
     assert lib.g16_msm_g1_finish(17, sums.ctypes.data, out.ctypes.data) == binding.G16_EINVAL
+
+
+def test_generated_columns_up_to_date():
+    """fp29_cols.hpp is what fp29_cols_gen.py writes (the device's column chains)."""
+    gen = os.path.join(ROOT, "groth16_polynomial_amd", "csrc", "fp29_cols_gen.py")
+    assert subprocess.run(["python3", gen, "--check"]).returncode == 0
