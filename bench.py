@@ -100,7 +100,8 @@ def _code_only(text: str) -> str:
 
 
 # Sources of the G1 MSM only; the H pipeline's kernels are built from the others.
-MSM_SOURCES = {"fp.hpp", "fp29.hpp", "g1.hpp", "msm.hip", "msm_digit.hpp", "msm_kernels.hpp"}
+MSM_SOURCES = {"fp.hpp", "fp29.hpp", "fp29_cols.hpp", "fp29_cols_gen.py", "g1.hpp", "msm.hip",
+               "msm_digit.hpp", "msm_kernels.hpp"}
 
 
 def kernel_source_hash() -> str:
