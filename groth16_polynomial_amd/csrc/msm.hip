@@ -22,9 +22,9 @@ constexpr size_t kAlign = 256;
 constexpr uint32_t kMaxC = 16;  // a window's counters fit in LDS (2^15 x 4 bytes)
 constexpr uint32_t kSliceLen = 32;
 constexpr uint32_t kSegLen = 8;
-constexpr uint32_t kMaxOnesGroups = 64;
-constexpr uint32_t kMinChunk = 65536;   // scalars per sorting workgroup, at least
-constexpr uint32_t kMaxChunks = 64;     // sorting workgroups per window, at most
+constexpr uint32_t kMaxOnesGroups = 1024;  // workgroups of the scalar-one pass, at most
+constexpr uint32_t kBinEntries = 16384;  // entries per coarse bin, about (at most 1024 bins)
+constexpr uint32_t kMinChunk = 8192;     // codes per coarse-sorting workgroup, at least
 constexpr uint32_t kFatGroups = 128;    // workgroups of the long-run merge
 
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -75,8 +75,8 @@ uint32_t default_c(uint64_t n) {
 struct Layout {
     MsmParams mp;
     uint32_t per_group, groups;  // segment sums per partial, partials per window
-    size_t counts, cursor, chunk_counts, entries, spill_rows, spill_pts, buckets, seg_out,
-        partials, ones_out, fat, total;
+    size_t counts, cursor, codes, bin_counts, bin_offs, entries, spill_rows, spill_pts, buckets,
+        seg_out, partials, ones_out, fat, total;
 };
 
 bool make_layout(uint64_t n, uint32_t c, Layout* L) {
@@ -95,11 +95,22 @@ bool make_layout(uint64_t n, uint32_t c, Layout* L) {
     mp.segs = mp.buckets / mp.seg_len;
     const uint64_t groups = (n + g16::kMsmThreads - 1) / g16::kMsmThreads;
     mp.ones_groups = (uint32_t)(groups < kMaxOnesGroups ? groups : kMaxOnesGroups);
-    uint64_t chunk = (n + kMaxChunks - 1) / kMaxChunks;
-    chunk = (chunk + g16::kMsmSortThreads - 1) / g16::kMsmSortThreads * g16::kMsmSortThreads;
+    mp.n_pad = (uint32_t)((n + 7) / 8 * 8);
+    // Bins: a power of two up to the bucket count (and 1024), enough for about
+    // kBinEntries entries each and for 256 bin-sorting workgroups over the windows.
+    mp.bins = 1;
+    while (mp.bins < mp.buckets && mp.bins < 1024 &&
+           (n / mp.bins > kBinEntries || W * mp.bins < 256))
+        mp.bins *= 2;
+    for (mp.bin_shift = 0; (mp.bins << mp.bin_shift) < mp.buckets; ++mp.bin_shift) {
+    }
+    // Chunks: at most about 128 per window, whole multiples of 2048 codes (eight per
+    // thread of a 256-thread workgroup).
+    uint64_t chunk = (mp.n_pad + 127) / 128;
+    chunk = (chunk + 2047) / 2048 * 2048;
     if (chunk < kMinChunk) chunk = kMinChunk;
     mp.chunk = (uint32_t)chunk;
-    mp.chunks = (uint32_t)((n + chunk - 1) / chunk);
+    mp.chunks = (uint32_t)((mp.n_pad + chunk - 1) / chunk);
     L->per_group = mp.segs < g16::kMsmThreads ? mp.segs : g16::kMsmThreads;
     L->groups = mp.segs / L->per_group;
     const size_t rows = (size_t)W * mp.buckets;
@@ -112,7 +123,9 @@ bool make_layout(uint64_t n, uint32_t c, Layout* L) {
     };
     L->counts = take(rows * 4);
     L->cursor = take(rows * 4);
-    L->chunk_counts = take(rows * mp.chunks * 4);
+    L->codes = take((size_t)W * mp.n_pad * 2);
+    L->bin_counts = take((size_t)W * mp.bins * mp.chunks * 16);
+    L->bin_offs = take((size_t)W * mp.bins * mp.chunks * 16);
     L->entries = take((size_t)W * n * 8);
     L->spill_rows = take(spills * 4);
     L->spill_pts = take(spills * sizeof(G1Xyzz));
@@ -178,7 +191,9 @@ int g16_msm_g1(uint64_t n, const void* scalars_std, const void* bases_mont, uint
     const MsmParams mp = L.mp;
     uint32_t* counts = (uint32_t*)(ws + L.counts);
     uint32_t* cursor = (uint32_t*)(ws + L.cursor);
-    uint32_t* chunk_counts = (uint32_t*)(ws + L.chunk_counts);
+    uint16_t* codes = (uint16_t*)(ws + L.codes);
+    uint32_t* bin_counts = (uint32_t*)(ws + L.bin_counts);
+    uint32_t* bin_offs = (uint32_t*)(ws + L.bin_offs);
     uint2* entries = (uint2*)(ws + L.entries);
     uint32_t* spill_rows = (uint32_t*)(ws + L.spill_rows);
     G1Xyzz* spill_pts = (G1Xyzz*)(ws + L.spill_pts);
@@ -192,22 +207,26 @@ int g16_msm_g1(uint64_t n, const void* scalars_std, const void* bases_mont, uint
     const G1Aff* bases = (const G1Aff*)bases_mont;
     const uint32_t rows = W * mp.buckets;
     const dim3 blk(g16::kMsmThreads), sort_blk(g16::kMsmSortThreads);
-    const size_t lds = (size_t)mp.buckets * 4;
-    if (lds > 65536) {  // LDS beyond the default 64 KiB is allowed per kernel
-        if (hipFuncSetAttribute((const void*)g16::msm_hist,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess ||
-            hipFuncSetAttribute((const void*)g16::msm_place,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-            return G16_EHIP;
-    }
+    // The coarse-sorted entries live in the spill area until the accumulation: 2 W
+    // ceil(n / 32) spill points of 128 bytes hold W n entries of 8.
+    uint2* binned = (uint2*)spill_pts;
+    const size_t bin_lds = (size_t)mp.bins * 16;
+    const size_t row_lds = ((size_t)1 << mp.bin_shift) * 4;
+    if (row_lds > 65536 &&  // LDS beyond the default 64 KiB is allowed per kernel
+        hipFuncSetAttribute((const void*)g16::msm_bin_sort,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)row_lds) != hipSuccess)
+        return G16_EHIP;
+    const dim3 bin_blk(g16::kMsmBinThreads);
 
-    hipLaunchKernelGGL(g16::msm_hist, dim3(W * mp.chunks), sort_blk, lds, s, sc, mp, chunk_counts);
-    hipLaunchKernelGGL(g16::msm_totals, dim3(blocks_for(rows)), blk, 0, s, chunk_counts, mp,
-                       counts);
-    hipLaunchKernelGGL(g16::msm_scan, dim3(W), sort_blk, 0, s, counts, mp, cursor, fat_count);
-    hipLaunchKernelGGL(g16::msm_chunk_offsets, dim3(blocks_for(rows)), blk, 0, s, chunk_counts, mp,
-                       cursor);
-    hipLaunchKernelGGL(g16::msm_place, dim3(W * mp.chunks), sort_blk, lds, s, sc, mp, chunk_counts,
+    hipLaunchKernelGGL(g16::msm_digits, dim3(blocks_for(mp.n_pad)), blk, 0, s, sc, mp, codes);
+    hipLaunchKernelGGL(g16::msm_bin_count, dim3(W * mp.chunks), bin_blk, bin_lds, s,
+                       (const uint16_t*)codes, mp, bin_counts);
+    hipLaunchKernelGGL(g16::msm_scan, dim3(W), sort_blk, 0, s, (const uint32_t*)bin_counts,
+                       mp.bins * mp.chunks * 4u, mp, bin_offs, fat_count);
+    hipLaunchKernelGGL(g16::msm_bin_place, dim3(W * mp.chunks), bin_blk, bin_lds, s,
+                       (const uint16_t*)codes, mp, bin_offs, binned);
+    hipLaunchKernelGGL(g16::msm_bin_sort, dim3(W * mp.bins), sort_blk, row_lds, s,
+                       (const uint2*)binned, (const uint32_t*)bin_offs, mp, counts, cursor,
                        entries);
     hipLaunchKernelGGL(g16::msm_accumulate, dim3(blocks_for((uint64_t)W * mp.slices)), blk, 0, s,
                        entries, bases, cursor, mp, buckets, spill_pts, spill_rows);

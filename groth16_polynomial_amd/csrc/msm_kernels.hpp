@@ -15,14 +15,14 @@
 //   * each window reduced to sum_m m B_m on the device; the host combines the windows
 //     by Horner's rule (the page's "THE WINDOW REDUCTION ENDS ON THE HOST").
 //
-// Differences from the page (see the notes at each kernel): the digit recoding is
-// computed per window from the window's bits and the bit below it (so count and scatter
-// need no sequential carry); the counting sort keeps each window's counters in LDS, one
-// workgroup per (window, chunk of scalars), so its atomics are LDS atomics and none is
-// global; a bucket never written is recognised from its count and from the run geometry
-// instead of being cleared first; the window reduction is spread over many threads (one
-// per short segment of buckets) rather than one block per window; the ones' partial
-// sums are added into window 0.
+// Differences from the page (see the notes at each kernel): the digits are computed once,
+// for all windows of a scalar in one thread (a signed recoding with carries), and stored
+// as 16-bit codes; the counting sort runs in two levels (coarse bins of rows, then rows
+// within a bin) with all its counters in LDS, so its atomics are LDS atomics and none is
+// global; a bucket never written
+// is recognised from its count and from the run geometry instead of being cleared first;
+// the window reduction is spread over many threads (one per short segment of buckets)
+// rather than one block per window; the ones' partial sums are added into window 0.
 #pragma once
 
 #include "g1.hpp"
@@ -40,8 +40,11 @@ struct MsmParams {
     uint32_t seg_len;    // buckets per reduction thread
     uint32_t segs;       // buckets / seg_len reduction threads per window
     uint32_t ones_groups;  // workgroups of the ones pass
-    uint32_t chunk;      // scalars per sorting workgroup
-    uint32_t chunks;     // ceil(n / chunk) sorting workgroups per window
+    uint32_t n_pad;      // n rounded up to a multiple of 8 (a window's codes in 16-byte words)
+    uint32_t bins;       // coarse sorting bins per window, a power of two up to buckets
+    uint32_t bin_shift;  // log2(buckets / bins): rows per bin
+    uint32_t chunk;      // codes per coarse-sorting workgroup, a multiple of 8
+    uint32_t chunks;     // ceil(n_pad / chunk) coarse-sorting workgroups per window
 };
 
 constexpr uint32_t kMsmNoRow = 0xffffffffu;
@@ -108,60 +111,114 @@ __global__ void msm_fill_u32(uint32_t* p, uint32_t len, uint32_t v) {
     if (i < len) p[i] = v;
 }
 
-// Counting sort by (window, bucket), with the counters in LDS: one workgroup per (window,
-// chunk of scalars) keeps the window's 2^(c-1) counters in LDS (c <= 16: at most
-// 128 KiB), so the only atomics are LDS ones and nothing global is contended.
+// Counting sort by (window, bucket) in two levels, every counter in LDS: a coarse pass
+// moves the entries into bins of consecutive rows (few bins, so each workgroup writes long
+// runs), then one workgroup per bin sorts its entries by row within the bin's part of the
+// array (small, so its scattered writes stay in the cache).
 //
-// Pass 1: each (window, chunk) workgroup's histogram, written to
-// chunk_counts[(w chunks + chunk) B + bucket].
-__global__ void __launch_bounds__(kMsmSortThreads) msm_hist(const uint32_t* scalars, MsmParams mp,
-                                                            uint32_t* chunk_counts) {
-    extern __shared__ uint32_t hist[];
+// Pass 1: the digits of every window, one thread per scalar, as 16-bit codes
+// codes[w n_pad + i] (msm_digit.hpp); scalars 0 and 1 and the padding indices n .. n_pad - 1
+// (whole 16-byte words per window) get the zero digit in every window.
+__global__ void __launch_bounds__(kMsmThreads) msm_digits(const uint32_t* scalars, MsmParams mp,
+                                                          uint16_t* codes) {
+    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= mp.n_pad) return;
+    uint32_t k[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    if (i < mp.n) {
+        msm_load_scalar(scalars, i, k);
+        if (msm_scalar_kind(k) != 2u)
+            for (int j = 0; j < 8; ++j) k[j] = 0u;
+    }
+    msm_recode(k, mp.c, [&](uint32_t w, int32_t d) {
+        codes[(size_t)w * mp.n_pad + i] = (uint16_t)msm_code(d, mp.c);
+    });
+}
+
+// The coarse order: bin = row >> bin_shift, bins of 2^bin_shift rows, mp.bins per window.
+// Passes 2 and 4 run one workgroup of four waves per (window, chunk of scalars) over the
+// chunk's codes, eight per 16-byte load; thread t takes the words t, t + 256, ... of the
+// chunk, so that both passes give each wave the same entries.
+constexpr uint32_t kMsmBinThreads = 256;
+
+template <class F>
+__device__ __forceinline__ void msm_chunk_codes(const uint16_t* codes, const MsmParams& mp,
+                                                uint32_t w, uint32_t ch, F&& f) {
+    const uint4* cw = reinterpret_cast<const uint4*>(codes + (size_t)w * mp.n_pad);
+    const uint32_t q0 = ch * (mp.chunk / 8u);
+    const uint32_t q1 = q0 + mp.chunk / 8u < mp.n_pad / 8u ? q0 + mp.chunk / 8u : mp.n_pad / 8u;
+    for (uint32_t q = q0 + threadIdx.x; q < q1; q += kMsmBinThreads) {
+        const uint4 v = cw[q];
+        const uint32_t h[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (uint32_t j = 0; j < 8; ++j) {
+            uint32_t row, neg;
+            if (msm_decode((h[j >> 1] >> (16u * (j & 1u))) & 0xffffu, mp.c, row, neg))
+                f(row, 8u * q + j, neg);
+        }
+    }
+}
+
+// Index of the count of (window w, bin, chunk, wave): a window's counts run bin by bin,
+// then chunk by chunk, then wave by wave, the order in which pass 4 fills the bin.
+__device__ __forceinline__ size_t msm_bin_index(const MsmParams& mp, uint32_t w, uint32_t bin,
+                                                uint32_t ch, uint32_t wave) {
+    return (((size_t)w * mp.bins + bin) * mp.chunks + ch) * 4u + wave;
+}
+
+// Pass 2: each wave's count of the chunk's entries in each bin, in LDS.
+__global__ void __launch_bounds__(kMsmBinThreads) msm_bin_count(const uint16_t* codes,
+                                                                MsmParams mp,
+                                                                uint32_t* bin_counts) {
+    extern __shared__ uint32_t hist[];  // [wave][bin]
     const uint32_t w = blockIdx.x / mp.chunks, ch = blockIdx.x - w * mp.chunks;
     const uint32_t t = threadIdx.x;
-    for (uint32_t b = t; b < mp.buckets; b += kMsmSortThreads) hist[b] = 0u;
+    for (uint32_t b = t; b < 4u * mp.bins; b += kMsmBinThreads) hist[b] = 0u;
     __syncthreads();
-    const uint32_t i0 = ch * mp.chunk;
-    const uint32_t i1 = i0 + mp.chunk < mp.n ? i0 + mp.chunk : mp.n;
-    for (uint32_t i = i0 + t; i < i1; i += kMsmSortThreads) {
-        uint32_t k[8];
-        msm_load_scalar(scalars, i, k);
-        if (msm_scalar_kind(k) != 2u) continue;
-        const int32_t d = msm_digit(k, w, mp.c);
-        if (d != 0) atomicAdd(&hist[(uint32_t)(d < 0 ? -d : d) - 1u], 1u);
+    uint32_t* mine = hist + (t >> 6) * mp.bins;
+    msm_chunk_codes(codes, mp, w, ch, [&](uint32_t row, uint32_t, uint32_t) {
+        atomicAdd(&mine[row >> mp.bin_shift], 1u);
+    });
+    __syncthreads();
+    for (uint32_t b = t; b < 4u * mp.bins; b += kMsmBinThreads) {
+        const uint32_t v = b / mp.bins, bin = b - v * mp.bins;
+        bin_counts[msm_bin_index(mp, w, bin, ch, v)] = hist[b];
     }
-    __syncthreads();
-    uint32_t* out = chunk_counts + (size_t)blockIdx.x * mp.buckets;
-    for (uint32_t b = t; b < mp.buckets; b += kMsmSortThreads) out[b] = hist[b];
 }
 
-// Pass 2a: one thread per bucket row: counts[row] = the row's total over the chunks.
-__global__ void __launch_bounds__(kMsmThreads) msm_totals(const uint32_t* chunk_counts,
-                                                          MsmParams mp, uint32_t* counts) {
-    const uint32_t row = blockIdx.x * blockDim.x + threadIdx.x;
-    if (row >= mp.windows * mp.buckets) return;
-    const uint32_t w = row / mp.buckets, b = row - w * mp.buckets;
-    const uint32_t* cw = chunk_counts + (size_t)w * mp.chunks * mp.buckets + b;
-    uint32_t tot = 0;
-    for (uint32_t ch = 0; ch < mp.chunks; ++ch) tot += cw[(size_t)ch * mp.buckets];
-    counts[row] = tot;
-}
-
-// Pass 2b: exclusive prefix sum of one window's totals, from the window's region start
-// w n in the entry array, into cursor[row] (the run's start).  One workgroup per window:
-// each thread sums a contiguous range of buckets, the range sums are scanned in LDS, then
+// Pass 3: exclusive prefix sum of each window's len counts (the bins' per-wave counts, bin
+// by bin), from the window's region start w n in the entry array.  One workgroup per
+// window: each thread sums a contiguous range, the range sums are scanned in LDS, then
 // each thread writes its range's starts.
-__global__ void __launch_bounds__(kMsmSortThreads) msm_scan(const uint32_t* counts, MsmParams mp,
-                                                            uint32_t* cursor, uint32_t* fat_count) {
+__global__ void __launch_bounds__(kMsmSortThreads) msm_scan(const uint32_t* counts, uint32_t len,
+                                                            MsmParams mp, uint32_t* cursor,
+                                                            uint32_t* fat_count) {
     __shared__ uint32_t sums[kMsmSortThreads];
     const uint32_t w = blockIdx.x, t = threadIdx.x;
     if (w == 0 && t == 0) *fat_count = 0u;  // the merge pass appends to the list again
-    const uint32_t per = (mp.buckets + kMsmSortThreads - 1u) / kMsmSortThreads;
+    const uint32_t per = (len + kMsmSortThreads - 1u) / kMsmSortThreads;
     const uint32_t b0 = t * per;
-    const uint32_t b1 = b0 + per < mp.buckets ? b0 + per : mp.buckets;
-    const uint32_t* cw = counts + (size_t)w * mp.buckets;
+    const uint32_t b1 = b0 + per < len ? b0 + per : len;
+    const uint32_t* cw = counts + (size_t)w * len;
+    // When every range is whole 16-byte words (4 | per and len = 1024 per; a window's counts
+    // start 16-byte aligned as 4 | len): vector loads, all issued before the sum.
+    const bool vec = (per & 3u) == 0u && len == per * kMsmSortThreads;
     uint32_t local = 0;
-    for (uint32_t b = b0; b < b1; ++b) local += cw[b];
+    if (vec) {
+        const uint4* v = (const uint4*)(cw + b0);
+        uint4 q[8];
+#pragma unroll
+        for (uint32_t j = 0; j < 8; ++j)
+            if (j < per / 4u) q[j] = v[j];
+#pragma unroll
+        for (uint32_t j = 0; j < 8; ++j)
+            if (j < per / 4u) local += q[j].x + q[j].y + q[j].z + q[j].w;
+        for (uint32_t j = 8; j < per / 4u; ++j) {
+            const uint4 r = v[j];
+            local += r.x + r.y + r.z + r.w;
+        }
+    } else {
+        for (uint32_t b = b0; b < b1; ++b) local += cw[b];
+    }
     sums[t] = local;
     __syncthreads();
     // Hillis-Steele inclusive scan; every thread reaches every barrier
@@ -172,56 +229,125 @@ __global__ void __launch_bounds__(kMsmSortThreads) msm_scan(const uint32_t* coun
         __syncthreads();
     }
     uint32_t run = w * mp.n + sums[t] - local;
-    uint32_t* out = cursor + (size_t)w * mp.buckets;
-    for (uint32_t b = b0; b < b1; ++b) {
-        out[b] = run;
-        run += cw[b];
+    uint32_t* out = cursor + (size_t)w * len;
+    if (vec) {
+        const uint4* v = (const uint4*)(cw + b0);
+        uint4* o = (uint4*)(out + b0);
+        for (uint32_t j = 0; j < per / 4u; ++j) {
+            const uint4 c = v[j];
+            uint4 r;
+            r.x = run;
+            r.y = r.x + c.x;
+            r.z = r.y + c.y;
+            r.w = r.z + c.z;
+            run = r.w + c.w;
+            o[j] = r;
+        }
+    } else {
+        for (uint32_t b = b0; b < b1; ++b) {
+            out[b] = run;
+            run += cw[b];
+        }
     }
 }
 
-// Pass 2c: one thread per bucket row: each chunk's histogram entry becomes the chunk's
-// first slot in the row's run, and cursor[row] moves to the run's end.
-__global__ void __launch_bounds__(kMsmThreads) msm_chunk_offsets(uint32_t* chunk_counts,
-                                                                 MsmParams mp, uint32_t* cursor) {
-    const uint32_t row = blockIdx.x * blockDim.x + threadIdx.x;
-    if (row >= mp.windows * mp.buckets) return;
-    const uint32_t w = row / mp.buckets, b = row - w * mp.buckets;
-    uint32_t* cw = chunk_counts + (size_t)w * mp.chunks * mp.buckets + b;
-    uint32_t run = cursor[row];
-    for (uint32_t ch = 0; ch < mp.chunks; ++ch) {
-        uint32_t* q = cw + (size_t)ch * mp.buckets;
-        const uint32_t c = *q;
-        *q = run;
-        run += c;
-    }
-    cursor[row] = run;
-}
-
-// Pass 3: the same (window, chunk) workgroups place each entry (row, index << 1 |
-// negative) at its chunk's next slot in the bucket's run, the slots handed out by LDS
-// atomics on the chunk's offsets.
-__global__ void __launch_bounds__(kMsmSortThreads) msm_place(const uint32_t* scalars, MsmParams mp,
-                                                             const uint32_t* chunk_offsets,
-                                                             uint2* entries) {
-    extern __shared__ uint32_t next[];
+// Pass 4: the same workgroups move each entry (row, index << 1 | negative) to its wave's
+// next slot in its bin (LDS atomics on cursors that start at the scanned offsets).  A
+// (chunk, wave) fills one contiguous run per bin, so the writes come in whole lines.  The
+// cursors end at their runs' ends and are written back: the end of a bin is then the
+// cursor of its last (chunk, wave).
+__global__ void __launch_bounds__(kMsmBinThreads) msm_bin_place(const uint16_t* codes,
+                                                                MsmParams mp, uint32_t* bin_offs,
+                                                                uint2* binned) {
+    extern __shared__ uint32_t cur[];  // [wave][bin]
     const uint32_t w = blockIdx.x / mp.chunks, ch = blockIdx.x - w * mp.chunks;
     const uint32_t t = threadIdx.x;
-    const uint32_t* in = chunk_offsets + (size_t)blockIdx.x * mp.buckets;
-    for (uint32_t b = t; b < mp.buckets; b += kMsmSortThreads) next[b] = in[b];
-    __syncthreads();
-    const uint32_t i0 = ch * mp.chunk;
-    const uint32_t i1 = i0 + mp.chunk < mp.n ? i0 + mp.chunk : mp.n;
-    const uint32_t row0 = w * mp.buckets;
-    for (uint32_t i = i0 + t; i < i1; i += kMsmSortThreads) {
-        uint32_t k[8];
-        msm_load_scalar(scalars, i, k);
-        if (msm_scalar_kind(k) != 2u) continue;
-        const int32_t d = msm_digit(k, w, mp.c);
-        if (d == 0) continue;
-        const uint32_t b = (uint32_t)(d < 0 ? -d : d) - 1u;
-        const uint32_t slot = atomicAdd(&next[b], 1u);
-        entries[slot] = make_uint2(row0 + b, (i << 1) | (d < 0 ? 1u : 0u));
+    for (uint32_t b = t; b < 4u * mp.bins; b += kMsmBinThreads) {
+        const uint32_t v = b / mp.bins, bin = b - v * mp.bins;
+        cur[b] = bin_offs[msm_bin_index(mp, w, bin, ch, v)];
     }
+    __syncthreads();
+    uint32_t* mine = cur + (t >> 6) * mp.bins;
+    const uint32_t base = w * mp.buckets;
+    msm_chunk_codes(codes, mp, w, ch, [&](uint32_t row, uint32_t i, uint32_t neg) {
+        const uint32_t slot = atomicAdd(&mine[row >> mp.bin_shift], 1u);
+        binned[slot] = make_uint2(base + row, (i << 1) | neg);
+    });
+    __syncthreads();
+    for (uint32_t b = t; b < 4u * mp.bins; b += kMsmBinThreads) {
+        const uint32_t v = b / mp.bins, bin = b - v * mp.bins;
+        bin_offs[msm_bin_index(mp, w, bin, ch, v)] = cur[b];
+    }
+}
+
+// Pass 5: one workgroup per (window, bin) sorts the bin's entries by row, from their
+// contiguous part of binned into the same part of entries: a count per row in LDS, an
+// exclusive scan, then each entry to its row's next slot.  Writes counts[row] and
+// cursor[row] (the row's run end) for the bin's rows.  Every write falls inside the bin's
+// part, which is small enough for the cache to assemble whole lines.  Each thread loads
+// kMsmSortBatch entries before it uses any, so that their loads overlap.
+constexpr uint32_t kMsmSortBatch = 8;
+
+__global__ void __launch_bounds__(kMsmSortThreads) msm_bin_sort(const uint2* binned,
+                                                                const uint32_t* bin_offs,
+                                                                MsmParams mp, uint32_t* counts,
+                                                                uint32_t* cursor, uint2* entries) {
+    constexpr uint32_t T = kMsmSortThreads, NB = kMsmSortBatch;
+    extern __shared__ uint32_t cnt[];  // the bin's rows
+    __shared__ uint32_t sums[T];
+    const uint32_t w = blockIdx.x / mp.bins, bin = blockIdx.x - w * mp.bins;
+    const uint32_t t = threadIdx.x;
+    const uint32_t rows = 1u << mp.bin_shift;
+    const uint32_t last = mp.chunks * 4u - 1u;
+    const uint32_t start =
+        bin ? bin_offs[msm_bin_index(mp, w, bin - 1u, 0u, 0u) + last] : w * mp.n;
+    const uint32_t end = bin_offs[msm_bin_index(mp, w, bin, 0u, 0u) + last];
+    const uint32_t row0 = w * mp.buckets + bin * rows;
+    for (uint32_t r = t; r < rows; r += T) cnt[r] = 0u;
+    __syncthreads();
+    for (uint32_t e0 = start + t; e0 < end; e0 += NB * T) {
+        uint32_t rw[NB];
+#pragma unroll
+        for (uint32_t j = 0; j < NB; ++j)
+            rw[j] = j * T < end - e0 ? binned[e0 + j * T].x : kMsmNoRow;
+#pragma unroll
+        for (uint32_t j = 0; j < NB; ++j)
+            if (rw[j] != kMsmNoRow) atomicAdd(&cnt[rw[j] - row0], 1u);
+    }
+    __syncthreads();
+    const uint32_t per = (rows + T - 1u) / T;
+    const uint32_t r0 = t * per < rows ? t * per : rows;
+    const uint32_t r1 = r0 + per < rows ? r0 + per : rows;
+    uint32_t local = 0;
+    for (uint32_t r = r0; r < r1; ++r) local += cnt[r];
+    sums[t] = local;
+    __syncthreads();
+    // Hillis-Steele inclusive scan; every thread reaches every barrier
+    for (uint32_t d = 1; d < T; d <<= 1) {
+        const uint32_t add = t >= d ? sums[t - d] : 0u;
+        __syncthreads();
+        sums[t] += add;
+        __syncthreads();
+    }
+    uint32_t run = start + sums[t] - local;
+    for (uint32_t r = r0; r < r1; ++r) {
+        const uint32_t c = cnt[r];
+        counts[row0 + r] = c;
+        cnt[r] = run;
+        run += c;
+    }
+    __syncthreads();
+    for (uint32_t e0 = start + t; e0 < end; e0 += NB * T) {
+        uint2 x[NB];
+#pragma unroll
+        for (uint32_t j = 0; j < NB; ++j)
+            x[j] = j * T < end - e0 ? binned[e0 + j * T] : make_uint2(kMsmNoRow, 0u);
+#pragma unroll
+        for (uint32_t j = 0; j < NB; ++j)
+            if (x[j].x != kMsmNoRow) entries[atomicAdd(&cnt[x[j].x - row0], 1u)] = x[j];
+    }
+    __syncthreads();
+    for (uint32_t r = t; r < rows; r += T) cursor[row0 + r] = cnt[r];
 }
 
 // The entries of window w occupy [w n, cursor[last row of w]).
@@ -230,7 +356,7 @@ __device__ __forceinline__ uint32_t msm_used(const uint32_t* cursor, const MsmPa
     return cursor[(size_t)w * mp.buckets + mp.buckets - 1u] - w * mp.n;
 }
 
-// Pass 4: one thread per slice of slice_len sorted entries of one window.  A run that
+// Pass 5: one thread per slice of slice_len sorted entries of one window.  A run that
 // neither contains the slice's first entry nor reaches its end is complete here and is
 // written to its bucket; the first run goes to the head spill slot and the run still
 // open at the slice's end to the tail slot (a slice holding one run spills once).
@@ -276,7 +402,7 @@ __global__ void __launch_bounds__(kMsmThreads) msm_accumulate(const uint2* entri
     msm_st_xyzz(spill_pts + slot, xyzz_from29(acc));
 }
 
-// Pass 5: one thread per bucket row with entries.  Starts from the direct write when
+// Pass 6: one thread per bucket row with entries.  Starts from the direct write when
 // the run lies strictly inside one slice (the accumulation wrote it), else from
 // infinity, and adds the spills of the slices the run overlaps.  A run over more than
 // kMsmFatSlices slices (many equal digits: repeated scalars, or the few buckets of a
@@ -314,7 +440,7 @@ __global__ void __launch_bounds__(kMsmThreads) msm_merge(const uint32_t* counts,
     msm_st_xyzz(buckets + row, xyzz_from29(acc));
 }
 
-// Pass 5b: the listed rows, one workgroup at a time (a grid-stride loop over the list,
+// Pass 6b: the listed rows, one workgroup at a time (a grid-stride loop over the list,
 // whose length every thread reads once before the loop, so all reach every barrier):
 // the threads take the run's slices in turn, each adding the spills that carry the row,
 // then a tree in LDS.  Such a run spans at least two slices, so the accumulation never
@@ -353,7 +479,7 @@ __global__ void __launch_bounds__(kMsmThreads) msm_merge_fat(const uint32_t* cou
     }
 }
 
-// Pass 6: the window sum sum_m m B_m, bucket j holding magnitude m = j + 1.  One thread
+// Pass 7: the window sum sum_m m B_m, bucket j holding magnitude m = j + 1.  One thread
 // per segment [lo, lo + seg_len) of a window's buckets: the running sum from the top
 // gives T = sum_j (j - lo + 1) B_j and Q = sum_j B_j, and the segment contributes
 // T + lo Q.  Buckets with no entries are infinity (never read).
@@ -395,7 +521,7 @@ __global__ void __launch_bounds__(kMsmThreads) msm_ones(const uint32_t* scalars,
     if (t == 0) msm_st_xyzz(out + blockIdx.x, xyzz_from29(sh[0]));
 }
 
-// Pass 7: group sums.  Workgroup g adds in[g per, (g + 1) per) (and, for g = 0, the
+// Pass 8: group sums.  Workgroup g adds in[g per, (g + 1) per) (and, for g = 0, the
 // n_extra points of extra) into out[g], a tree in LDS after a strided serial sum.  Run
 // twice: the segments' contributions into a few partials per window, then the partials
 // (and the ones' sums, into window 0) into the window sums.

@@ -139,9 +139,15 @@ int main() {
         } else if (op == "digits") {      // c k: every window's signed digit
             uint32_t c = (uint32_t)std::stoul(a[0], nullptr, 16);
             Fp k = parse(a[1]);
-            const uint32_t W = (255u + c - 1u) / c;
-            for (uint32_t w = 0; w < W; ++w) std::printf("%d ", g16::msm_digit(k.w, w, c));
+            g16::msm_recode(k.w, c, [](uint32_t, int32_t d) { std::printf("%d ", d); });
             std::printf("\n");
+        } else if (op == "code") {        // c d (d as a 32-bit two's complement word): code, decoded
+            uint32_t c = (uint32_t)std::stoul(a[0], nullptr, 16);
+            const int32_t d = (int32_t)(uint32_t)std::stoul(a[1], nullptr, 16);
+            const uint32_t code = g16::msm_code(d, c);
+            uint32_t row = 0, neg = 0;
+            const bool nz = g16::msm_decode(code, c, row, neg);
+            std::printf("%u %d %u %u\n", code, (int)nz, row, neg);
         } else {
             return 2;
         }

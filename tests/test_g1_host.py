@@ -231,8 +231,28 @@ def test_signed_digits_recompose(driver, c):
     for k, line in zip(ks, got):
         ds = [int(v) for v in line.split()]
         assert len(ds) == windows
-        assert all(abs(d) <= 1 << (c - 1) for d in ds), (c, k)
+        assert all(1 - (1 << (c - 1)) <= d <= 1 << (c - 1) for d in ds), (c, k)
         assert sum(d << (c * w) for w, d in enumerate(ds)) == k, (c, k)
+
+
+@pytest.mark.parametrize("c", [1, 2, 3, 9, 15, 16])
+def test_digit_codes(driver, c):
+    """The 16-bit digit codes: every digit of [1 - 2^(c-1), 2^(c-1)] gets a distinct code
+    below 2^c; decoding gives the bucket row |d| - 1 and the sign, and only the zero digit
+    decodes as empty."""
+    half = 1 << (c - 1)
+    ds = list(range(1 - half, half + 1)) if c <= 9 else \
+        [1 - half, 2 - half, -2, -1, 0, 1, 2, 12345, half - 1, half]
+    got = run(driver, [("code", c, d & 0xffffffff) for d in ds])
+    codes = set()
+    for d, line in zip(ds, got):
+        code, nz, row, neg = (int(v) for v in line.split())
+        assert 0 <= code < 1 << c
+        codes.add(code)
+        assert nz == int(d != 0)
+        if d:
+            assert (row, neg) == (abs(d) - 1, int(d < 0)), d
+    assert len(codes) == len(ds)
 
 
 @pytest.fixture(scope="module")
