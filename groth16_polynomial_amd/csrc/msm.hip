@@ -6,6 +6,7 @@
 // ENDS ON THE HOST").
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 
@@ -23,7 +24,8 @@ constexpr uint32_t kMaxC = 16;  // a window's counters fit in LDS (2^15 x 4 byte
 constexpr uint32_t kSliceLen = 32;
 constexpr uint32_t kSegLen = 8;
 constexpr uint32_t kMaxOnesGroups = 1024;  // workgroups of the scalar-one pass, at most
-constexpr uint32_t kBinEntries = 16384;  // entries per coarse bin, about (at most 1024 bins)
+constexpr uint32_t kBinEntries = 8192;   // entries per coarse bin, about (at most 1024 bins)
+constexpr uint32_t kStage = 8192;        // entries of a bin staged in LDS by the row sort
 constexpr uint32_t kMinChunk = 8192;     // codes per coarse-sorting workgroup, at least
 constexpr uint32_t kFatGroups = 128;    // workgroups of the long-run merge
 
@@ -111,6 +113,10 @@ bool make_layout(uint64_t n, uint32_t c, Layout* L) {
     if (chunk < kMinChunk) chunk = kMinChunk;
     mp.chunk = (uint32_t)chunk;
     mp.chunks = (uint32_t)((mp.n_pad + chunk - 1) / chunk);
+    // LDS of the row sort: the staged entries and a counter per row, within 96 KiB
+    const uint64_t row_bytes = ((uint64_t)1 << mp.bin_shift) * 4;
+    mp.stage = row_bytes >= 96 * 1024 ? 0u
+               : (uint32_t)std::min<uint64_t>(kStage, (96 * 1024 - row_bytes) / 8);
     L->per_group = mp.segs < g16::kMsmThreads ? mp.segs : g16::kMsmThreads;
     L->groups = mp.segs / L->per_group;
     const size_t rows = (size_t)W * mp.buckets;
@@ -124,8 +130,8 @@ bool make_layout(uint64_t n, uint32_t c, Layout* L) {
     L->counts = take(rows * 4);
     L->cursor = take(rows * 4);
     L->codes = take((size_t)W * mp.n_pad * 2);
-    L->bin_counts = take((size_t)W * mp.bins * mp.chunks * 16);
-    L->bin_offs = take((size_t)W * mp.bins * mp.chunks * 16);
+    L->bin_counts = take((size_t)W * mp.bins * mp.chunks * 4);
+    L->bin_offs = take((size_t)W * mp.bins * mp.chunks * 4);
     L->entries = take((size_t)W * n * 8);
     L->spill_rows = take(spills * 4);
     L->spill_pts = take(spills * sizeof(G1Xyzz));
@@ -210,24 +216,29 @@ int g16_msm_g1(uint64_t n, const void* scalars_std, const void* bases_mont, uint
     // The coarse-sorted entries live in the spill area until the accumulation: 2 W
     // ceil(n / 32) spill points of 128 bytes hold W n entries of 8.
     uint2* binned = (uint2*)spill_pts;
-    const size_t bin_lds = (size_t)mp.bins * 16;
-    const size_t row_lds = ((size_t)1 << mp.bin_shift) * 4;
-    if (row_lds > 65536 &&  // LDS beyond the default 64 KiB is allowed per kernel
-        hipFuncSetAttribute((const void*)g16::msm_bin_sort,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)row_lds) != hipSuccess)
+    const size_t count_lds = (size_t)mp.bins * 16;
+    const size_t place_lds = (size_t)g16::kMsmRound * 8 + (size_t)mp.bins * 12;
+    const size_t row_lds = (size_t)mp.stage * 8 + ((size_t)1 << mp.bin_shift) * 4;
+    // LDS beyond the default 64 KiB is allowed per kernel
+    if (hipFuncSetAttribute((const void*)g16::msm_bin_place,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)place_lds) !=
+            hipSuccess ||
+        (row_lds > 65536 &&
+         hipFuncSetAttribute((const void*)g16::msm_bin_sort,
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)row_lds) != hipSuccess))
         return G16_EHIP;
     const dim3 bin_blk(g16::kMsmBinThreads);
 
     hipLaunchKernelGGL(g16::msm_digits, dim3(blocks_for(mp.n_pad)), blk, 0, s, sc, mp, codes);
-    hipLaunchKernelGGL(g16::msm_bin_count, dim3(W * mp.chunks), bin_blk, bin_lds, s,
+    hipLaunchKernelGGL(g16::msm_bin_count, dim3(W * mp.chunks), bin_blk, count_lds, s,
                        (const uint16_t*)codes, mp, bin_counts);
     hipLaunchKernelGGL(g16::msm_scan, dim3(W), sort_blk, 0, s, (const uint32_t*)bin_counts,
-                       mp.bins * mp.chunks * 4u, mp, bin_offs, fat_count);
-    hipLaunchKernelGGL(g16::msm_bin_place, dim3(W * mp.chunks), bin_blk, bin_lds, s,
-                       (const uint16_t*)codes, mp, bin_offs, binned);
+                       mp.bins * mp.chunks, mp, bin_offs, fat_count);
+    hipLaunchKernelGGL(g16::msm_bin_place, dim3(W * mp.chunks), bin_blk, place_lds, s,
+                       (const uint16_t*)codes, mp, (const uint32_t*)bin_offs, binned);
     hipLaunchKernelGGL(g16::msm_bin_sort, dim3(W * mp.bins), sort_blk, row_lds, s,
-                       (const uint2*)binned, (const uint32_t*)bin_offs, mp, counts, cursor,
-                       entries);
+                       (const uint2*)binned, (const uint32_t*)bin_counts,
+                       (const uint32_t*)bin_offs, mp, counts, cursor, entries);
     hipLaunchKernelGGL(g16::msm_accumulate, dim3(blocks_for((uint64_t)W * mp.slices)), blk, 0, s,
                        entries, bases, cursor, mp, buckets, spill_pts, spill_rows);
     hipLaunchKernelGGL(g16::msm_merge, dim3(blocks_for(rows)), blk, 0, s, counts, cursor,

@@ -45,6 +45,7 @@ struct MsmParams {
     uint32_t bin_shift;  // log2(buckets / bins): rows per bin
     uint32_t chunk;      // codes per coarse-sorting workgroup, a multiple of 8
     uint32_t chunks;     // ceil(n_pad / chunk) coarse-sorting workgroups per window
+    uint32_t stage;      // entries of a bin the row sort keeps in LDS
 };
 
 constexpr uint32_t kMsmNoRow = 0xffffffffu;
@@ -135,18 +136,16 @@ __global__ void __launch_bounds__(kMsmThreads) msm_digits(const uint32_t* scalar
 }
 
 // The coarse order: bin = row >> bin_shift, bins of 2^bin_shift rows, mp.bins per window.
-// Passes 2 and 4 run one workgroup of four waves per (window, chunk of scalars) over the
-// chunk's codes, eight per 16-byte load; thread t takes the words t, t + 256, ... of the
-// chunk, so that both passes give each wave the same entries.
+// Passes 2 and 4 run one workgroup per (window, chunk of scalars) over the chunk's codes,
+// eight per 16-byte load, in rounds of kMsmRound codes.
 constexpr uint32_t kMsmBinThreads = 256;
+constexpr uint32_t kMsmRound = 8192;
 
 template <class F>
-__device__ __forceinline__ void msm_chunk_codes(const uint16_t* codes, const MsmParams& mp,
-                                                uint32_t w, uint32_t ch, F&& f) {
+__device__ __forceinline__ void msm_round_codes(const uint16_t* codes, const MsmParams& mp,
+                                                uint32_t w, uint32_t r0, uint32_t r1, F&& f) {
     const uint4* cw = reinterpret_cast<const uint4*>(codes + (size_t)w * mp.n_pad);
-    const uint32_t q0 = ch * (mp.chunk / 8u);
-    const uint32_t q1 = q0 + mp.chunk / 8u < mp.n_pad / 8u ? q0 + mp.chunk / 8u : mp.n_pad / 8u;
-    for (uint32_t q = q0 + threadIdx.x; q < q1; q += kMsmBinThreads) {
+    for (uint32_t q = r0 + threadIdx.x; q < r1; q += kMsmBinThreads) {
         const uint4 v = cw[q];
         const uint32_t h[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -158,14 +157,50 @@ __device__ __forceinline__ void msm_chunk_codes(const uint16_t* codes, const Msm
     }
 }
 
-// Index of the count of (window w, bin, chunk, wave): a window's counts run bin by bin,
-// then chunk by chunk, then wave by wave, the order in which pass 4 fills the bin.
-__device__ __forceinline__ size_t msm_bin_index(const MsmParams& mp, uint32_t w, uint32_t bin,
-                                                uint32_t ch, uint32_t wave) {
-    return (((size_t)w * mp.bins + bin) * mp.chunks + ch) * 4u + wave;
+// The chunk's range of 16-byte code words.
+__device__ __forceinline__ void msm_chunk_words(const MsmParams& mp, uint32_t ch, uint32_t& q0,
+                                                uint32_t& q1) {
+    q0 = ch * (mp.chunk / 8u);
+    q1 = q0 + mp.chunk / 8u < mp.n_pad / 8u ? q0 + mp.chunk / 8u : mp.n_pad / 8u;
 }
 
-// Pass 2: each wave's count of the chunk's entries in each bin, in LDS.
+// Index of the count of (window w, bin, chunk): a window's counts run bin by bin, then
+// chunk by chunk, the order in which pass 4 fills a window's part of the array.
+__device__ __forceinline__ size_t msm_bin_index(const MsmParams& mp, uint32_t w, uint32_t bin,
+                                                uint32_t ch) {
+    return ((size_t)w * mp.bins + bin) * mp.chunks + ch;
+}
+
+// Exclusive scan of x[0 .. len) in LDS by one workgroup of T threads (each takes a
+// contiguous range); returns the total.  Every thread reaches every barrier.
+template <uint32_t T>
+__device__ __forceinline__ uint32_t msm_lds_scan(uint32_t* x, uint32_t len, uint32_t* sums) {
+    const uint32_t t = threadIdx.x;
+    const uint32_t per = (len + T - 1u) / T;
+    const uint32_t r0 = t * per < len ? t * per : len;
+    const uint32_t r1 = r0 + per < len ? r0 + per : len;
+    uint32_t local = 0;
+    for (uint32_t r = r0; r < r1; ++r) local += x[r];
+    sums[t] = local;
+    __syncthreads();
+    for (uint32_t d = 1; d < T; d <<= 1) {  // Hillis-Steele, inclusive
+        const uint32_t add = t >= d ? sums[t - d] : 0u;
+        __syncthreads();
+        sums[t] += add;
+        __syncthreads();
+    }
+    uint32_t run = sums[t] - local;
+    for (uint32_t r = r0; r < r1; ++r) {
+        const uint32_t c = x[r];
+        x[r] = run;
+        run += c;
+    }
+    const uint32_t total = sums[T - 1u];
+    __syncthreads();
+    return total;
+}
+
+// Pass 2: the chunk's count of entries in each bin (per-wave counters in LDS, added up).
 __global__ void __launch_bounds__(kMsmBinThreads) msm_bin_count(const uint16_t* codes,
                                                                 MsmParams mp,
                                                                 uint32_t* bin_counts) {
@@ -175,14 +210,15 @@ __global__ void __launch_bounds__(kMsmBinThreads) msm_bin_count(const uint16_t* 
     for (uint32_t b = t; b < 4u * mp.bins; b += kMsmBinThreads) hist[b] = 0u;
     __syncthreads();
     uint32_t* mine = hist + (t >> 6) * mp.bins;
-    msm_chunk_codes(codes, mp, w, ch, [&](uint32_t row, uint32_t, uint32_t) {
+    uint32_t q0, q1;
+    msm_chunk_words(mp, ch, q0, q1);
+    msm_round_codes(codes, mp, w, q0, q1, [&](uint32_t row, uint32_t, uint32_t) {
         atomicAdd(&mine[row >> mp.bin_shift], 1u);
     });
     __syncthreads();
-    for (uint32_t b = t; b < 4u * mp.bins; b += kMsmBinThreads) {
-        const uint32_t v = b / mp.bins, bin = b - v * mp.bins;
-        bin_counts[msm_bin_index(mp, w, bin, ch, v)] = hist[b];
-    }
+    for (uint32_t b = t; b < mp.bins; b += kMsmBinThreads)
+        bin_counts[msm_bin_index(mp, w, b, ch)] =
+            hist[b] + hist[mp.bins + b] + hist[2u * mp.bins + b] + hist[3u * mp.bins + b];
 }
 
 // Pass 3: exclusive prefix sum of each window's len counts (the bins' per-wave counts, bin
@@ -251,32 +287,49 @@ __global__ void __launch_bounds__(kMsmSortThreads) msm_scan(const uint32_t* coun
     }
 }
 
-// Pass 4: the same workgroups move each entry (row, index << 1 | negative) to its wave's
-// next slot in its bin (LDS atomics on cursors that start at the scanned offsets).  A
-// (chunk, wave) fills one contiguous run per bin, so the writes come in whole lines.  The
-// cursors end at their runs' ends and are written back: the end of a bin is then the
-// cursor of its last (chunk, wave).
+// Pass 4: the same workgroups move each entry (row, index << 1 | negative) to its bin, a
+// round of the chunk at a time: the round's entries are counted per bin, ranked by LDS
+// atomics into a buffer in bin order, and written out bin by bin at the bin's next
+// global slots, so that consecutive threads write consecutive slots.
 __global__ void __launch_bounds__(kMsmBinThreads) msm_bin_place(const uint16_t* codes,
-                                                                MsmParams mp, uint32_t* bin_offs,
+                                                                MsmParams mp,
+                                                                const uint32_t* bin_offs,
                                                                 uint2* binned) {
-    extern __shared__ uint32_t cur[];  // [wave][bin]
+    constexpr uint32_t T = kMsmBinThreads;
+    extern __shared__ uint2 buf[];  // kMsmRound entries, then three counters per bin
+    uint32_t* gcur = reinterpret_cast<uint32_t*>(buf + kMsmRound);  // next global slot
+    uint32_t* cur = gcur + mp.bins;                                  // the round's cursor
+    uint32_t* lst = cur + mp.bins;                                   // the round's start
+    __shared__ uint32_t sums[T];
     const uint32_t w = blockIdx.x / mp.chunks, ch = blockIdx.x - w * mp.chunks;
     const uint32_t t = threadIdx.x;
-    for (uint32_t b = t; b < 4u * mp.bins; b += kMsmBinThreads) {
-        const uint32_t v = b / mp.bins, bin = b - v * mp.bins;
-        cur[b] = bin_offs[msm_bin_index(mp, w, bin, ch, v)];
-    }
-    __syncthreads();
-    uint32_t* mine = cur + (t >> 6) * mp.bins;
     const uint32_t base = w * mp.buckets;
-    msm_chunk_codes(codes, mp, w, ch, [&](uint32_t row, uint32_t i, uint32_t neg) {
-        const uint32_t slot = atomicAdd(&mine[row >> mp.bin_shift], 1u);
-        binned[slot] = make_uint2(base + row, (i << 1) | neg);
-    });
-    __syncthreads();
-    for (uint32_t b = t; b < 4u * mp.bins; b += kMsmBinThreads) {
-        const uint32_t v = b / mp.bins, bin = b - v * mp.bins;
-        bin_offs[msm_bin_index(mp, w, bin, ch, v)] = cur[b];
+    for (uint32_t b = t; b < mp.bins; b += T) gcur[b] = bin_offs[msm_bin_index(mp, w, b, ch)];
+    uint32_t q0, q1;
+    msm_chunk_words(mp, ch, q0, q1);
+    for (uint32_t r0 = q0; r0 < q1; r0 += kMsmRound / 8u) {  // the same rounds in every thread
+        const uint32_t r1 = r0 + kMsmRound / 8u < q1 ? r0 + kMsmRound / 8u : q1;
+        for (uint32_t b = t; b < mp.bins; b += T) lst[b] = 0u;
+        __syncthreads();
+        msm_round_codes(codes, mp, w, r0, r1, [&](uint32_t row, uint32_t, uint32_t) {
+            atomicAdd(&lst[row >> mp.bin_shift], 1u);
+        });
+        __syncthreads();
+        const uint32_t total = msm_lds_scan<T>(lst, mp.bins, sums);
+        for (uint32_t b = t; b < mp.bins; b += T) cur[b] = lst[b];
+        __syncthreads();
+        msm_round_codes(codes, mp, w, r0, r1, [&](uint32_t row, uint32_t i, uint32_t neg) {
+            buf[atomicAdd(&cur[row >> mp.bin_shift], 1u)] = make_uint2(base + row, (i << 1) | neg);
+        });
+        __syncthreads();
+        for (uint32_t p = t; p < total; p += T) {
+            const uint2 x = buf[p];
+            const uint32_t b = (x.x - base) >> mp.bin_shift;
+            binned[gcur[b] + p - lst[b]] = x;
+        }
+        __syncthreads();
+        for (uint32_t b = t; b < mp.bins; b += T) gcur[b] += cur[b] - lst[b];
+        __syncthreads();
     }
 }
 
@@ -284,35 +337,45 @@ __global__ void __launch_bounds__(kMsmBinThreads) msm_bin_place(const uint16_t* 
 // contiguous part of binned into the same part of entries: a count per row in LDS, an
 // exclusive scan, then each entry to its row's next slot.  Writes counts[row] and
 // cursor[row] (the row's run end) for the bin's rows.  Every write falls inside the bin's
-// part, which is small enough for the cache to assemble whole lines.  Each thread loads
-// kMsmSortBatch entries before it uses any, so that their loads overlap.
+// part, which is small enough for the cache to assemble whole lines.  The counting pass
+// keeps the bin's first mp.stage entries in LDS for the placing pass (a larger bin, as
+// equal scalars make, reads the rest again), and each thread loads kMsmSortBatch entries
+// before it uses any, so that their loads overlap.
 constexpr uint32_t kMsmSortBatch = 8;
 
 __global__ void __launch_bounds__(kMsmSortThreads) msm_bin_sort(const uint2* binned,
+                                                                const uint32_t* bin_counts,
                                                                 const uint32_t* bin_offs,
                                                                 MsmParams mp, uint32_t* counts,
                                                                 uint32_t* cursor, uint2* entries) {
     constexpr uint32_t T = kMsmSortThreads, NB = kMsmSortBatch;
-    extern __shared__ uint32_t cnt[];  // the bin's rows
+    extern __shared__ uint2 stage[];  // mp.stage entries, then a counter per row of the bin
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(stage + mp.stage);
     __shared__ uint32_t sums[T];
     const uint32_t w = blockIdx.x / mp.bins, bin = blockIdx.x - w * mp.bins;
     const uint32_t t = threadIdx.x;
     const uint32_t rows = 1u << mp.bin_shift;
-    const uint32_t last = mp.chunks * 4u - 1u;
-    const uint32_t start =
-        bin ? bin_offs[msm_bin_index(mp, w, bin - 1u, 0u, 0u) + last] : w * mp.n;
-    const uint32_t end = bin_offs[msm_bin_index(mp, w, bin, 0u, 0u) + last];
+    // the bin's part: from its first chunk's offset to the next bin's (or the window's
+    // last entry, the last offset plus the last count)
+    const uint32_t start = bin_offs[msm_bin_index(mp, w, bin, 0u)];
+    const size_t last = msm_bin_index(mp, w, mp.bins - 1u, mp.chunks - 1u);
+    const uint32_t end = bin + 1u < mp.bins ? bin_offs[msm_bin_index(mp, w, bin + 1u, 0u)]
+                                            : bin_offs[last] + bin_counts[last];
     const uint32_t row0 = w * mp.buckets + bin * rows;
     for (uint32_t r = t; r < rows; r += T) cnt[r] = 0u;
     __syncthreads();
     for (uint32_t e0 = start + t; e0 < end; e0 += NB * T) {
-        uint32_t rw[NB];
+        uint2 x[NB];
 #pragma unroll
         for (uint32_t j = 0; j < NB; ++j)
-            rw[j] = j * T < end - e0 ? binned[e0 + j * T].x : kMsmNoRow;
+            x[j] = j * T < end - e0 ? binned[e0 + j * T] : make_uint2(kMsmNoRow, 0u);
 #pragma unroll
-        for (uint32_t j = 0; j < NB; ++j)
-            if (rw[j] != kMsmNoRow) atomicAdd(&cnt[rw[j] - row0], 1u);
+        for (uint32_t j = 0; j < NB; ++j) {
+            if (x[j].x == kMsmNoRow) continue;
+            atomicAdd(&cnt[x[j].x - row0], 1u);
+            const uint32_t k = e0 + j * T - start;
+            if (k < mp.stage) stage[k] = x[j];
+        }
     }
     __syncthreads();
     const uint32_t per = (rows + T - 1u) / T;
@@ -340,8 +403,12 @@ __global__ void __launch_bounds__(kMsmSortThreads) msm_bin_sort(const uint2* bin
     for (uint32_t e0 = start + t; e0 < end; e0 += NB * T) {
         uint2 x[NB];
 #pragma unroll
-        for (uint32_t j = 0; j < NB; ++j)
-            x[j] = j * T < end - e0 ? binned[e0 + j * T] : make_uint2(kMsmNoRow, 0u);
+        for (uint32_t j = 0; j < NB; ++j) {
+            const uint32_t k = e0 + j * T - start;
+            x[j] = j * T >= end - e0 ? make_uint2(kMsmNoRow, 0u)
+                   : k < mp.stage   ? stage[k]
+                                    : binned[e0 + j * T];
+        }
 #pragma unroll
         for (uint32_t j = 0; j < NB; ++j)
             if (x[j].x != kMsmNoRow) entries[atomicAdd(&cnt[x[j].x - row0], 1u)] = x[j];
