@@ -130,6 +130,17 @@ __global__ void __launch_bounds__(kMsmThreads) msm_digits(const uint32_t* scalar
         if (msm_scalar_kind(k) != 2u)
             for (int j = 0; j < 8; ++j) k[j] = 0u;
     }
+    if (mp.c == 16u) {  // msm_recode for c = 16, whose 16 windows are the halves of the words
+        uint32_t carry = 0;
+#pragma unroll
+        for (uint32_t w = 0; w < 16u; ++w) {
+            const uint32_t v = ((k[w >> 1] >> (16u * (w & 1u))) & 0xffffu) + carry;
+            carry = v > 32768u ? 1u : 0u;
+            codes[(size_t)w * mp.n_pad + i] =
+                (uint16_t)msm_code((int32_t)v - (int32_t)(carry << 16), 16u);
+        }
+        return;
+    }
     msm_recode(k, mp.c, [&](uint32_t w, int32_t d) {
         codes[(size_t)w * mp.n_pad + i] = (uint16_t)msm_code(d, mp.c);
     });
@@ -171,33 +182,37 @@ __device__ __forceinline__ size_t msm_bin_index(const MsmParams& mp, uint32_t w,
     return ((size_t)w * mp.bins + bin) * mp.chunks + ch;
 }
 
-// Exclusive scan of x[0 .. len) in LDS by one workgroup of T threads (each takes a
-// contiguous range); returns the total.  Every thread reaches every barrier.
-template <uint32_t T>
-__device__ __forceinline__ uint32_t msm_lds_scan(uint32_t* x, uint32_t len, uint32_t* sums) {
+// Exclusive scan of x[0 .. len) in LDS by the workgroup's first wave: each lane takes a
+// contiguous range, and the range sums are scanned by cross-lane shifts (no barrier
+// inside).  f(r, count) sees each element before it is overwritten.  Every thread of the
+// workgroup must call it (it ends with a barrier); returns the total to all of them.
+template <class F>
+__device__ __forceinline__ uint32_t msm_wave_scan(uint32_t* x, uint32_t len, uint32_t base,
+                                                  uint32_t* total, F&& f) {
     const uint32_t t = threadIdx.x;
-    const uint32_t per = (len + T - 1u) / T;
-    const uint32_t r0 = t * per < len ? t * per : len;
-    const uint32_t r1 = r0 + per < len ? r0 + per : len;
-    uint32_t local = 0;
-    for (uint32_t r = r0; r < r1; ++r) local += x[r];
-    sums[t] = local;
-    __syncthreads();
-    for (uint32_t d = 1; d < T; d <<= 1) {  // Hillis-Steele, inclusive
-        const uint32_t add = t >= d ? sums[t - d] : 0u;
-        __syncthreads();
-        sums[t] += add;
-        __syncthreads();
+    if (t < 64u) {
+        const uint32_t per = (len + 63u) / 64u;
+        const uint32_t r0 = t * per < len ? t * per : len;
+        const uint32_t r1 = r0 + per < len ? r0 + per : len;
+        uint32_t local = 0;
+        for (uint32_t r = r0; r < r1; ++r) local += x[r];
+        uint32_t inc = local;
+#pragma unroll
+        for (uint32_t d = 1; d < 64u; d <<= 1) {
+            const uint32_t y = __shfl_up(inc, d, 64);
+            if (t >= d) inc += y;
+        }
+        uint32_t run = base + inc - local;
+        for (uint32_t r = r0; r < r1; ++r) {
+            const uint32_t c = x[r];
+            f(r, c);
+            x[r] = run;
+            run += c;
+        }
+        if (t == 63u) *total = inc;
     }
-    uint32_t run = sums[t] - local;
-    for (uint32_t r = r0; r < r1; ++r) {
-        const uint32_t c = x[r];
-        x[r] = run;
-        run += c;
-    }
-    const uint32_t total = sums[T - 1u];
     __syncthreads();
-    return total;
+    return *total;
 }
 
 // Pass 2: the chunk's count of entries in each bin (per-wave counters in LDS, added up).
@@ -300,7 +315,7 @@ __global__ void __launch_bounds__(kMsmBinThreads) msm_bin_place(const uint16_t* 
     uint32_t* gcur = reinterpret_cast<uint32_t*>(buf + kMsmRound);  // next global slot
     uint32_t* cur = gcur + mp.bins;                                  // the round's cursor
     uint32_t* lst = cur + mp.bins;                                   // the round's start
-    __shared__ uint32_t sums[T];
+    __shared__ uint32_t total_sh;
     const uint32_t w = blockIdx.x / mp.chunks, ch = blockIdx.x - w * mp.chunks;
     const uint32_t t = threadIdx.x;
     const uint32_t base = w * mp.buckets;
@@ -315,7 +330,8 @@ __global__ void __launch_bounds__(kMsmBinThreads) msm_bin_place(const uint16_t* 
             atomicAdd(&lst[row >> mp.bin_shift], 1u);
         });
         __syncthreads();
-        const uint32_t total = msm_lds_scan<T>(lst, mp.bins, sums);
+        const uint32_t total =
+            msm_wave_scan(lst, mp.bins, 0u, &total_sh, [](uint32_t, uint32_t) {});
         for (uint32_t b = t; b < mp.bins; b += T) cur[b] = lst[b];
         __syncthreads();
         msm_round_codes(codes, mp, w, r0, r1, [&](uint32_t row, uint32_t i, uint32_t neg) {
@@ -351,7 +367,7 @@ __global__ void __launch_bounds__(kMsmSortThreads) msm_bin_sort(const uint2* bin
     constexpr uint32_t T = kMsmSortThreads, NB = kMsmSortBatch;
     extern __shared__ uint2 stage[];  // mp.stage entries, then a counter per row of the bin
     uint32_t* cnt = reinterpret_cast<uint32_t*>(stage + mp.stage);
-    __shared__ uint32_t sums[T];
+    __shared__ uint32_t total_sh;
     const uint32_t w = blockIdx.x / mp.bins, bin = blockIdx.x - w * mp.bins;
     const uint32_t t = threadIdx.x;
     const uint32_t rows = 1u << mp.bin_shift;
@@ -378,28 +394,8 @@ __global__ void __launch_bounds__(kMsmSortThreads) msm_bin_sort(const uint2* bin
         }
     }
     __syncthreads();
-    const uint32_t per = (rows + T - 1u) / T;
-    const uint32_t r0 = t * per < rows ? t * per : rows;
-    const uint32_t r1 = r0 + per < rows ? r0 + per : rows;
-    uint32_t local = 0;
-    for (uint32_t r = r0; r < r1; ++r) local += cnt[r];
-    sums[t] = local;
-    __syncthreads();
-    // Hillis-Steele inclusive scan; every thread reaches every barrier
-    for (uint32_t d = 1; d < T; d <<= 1) {
-        const uint32_t add = t >= d ? sums[t - d] : 0u;
-        __syncthreads();
-        sums[t] += add;
-        __syncthreads();
-    }
-    uint32_t run = start + sums[t] - local;
-    for (uint32_t r = r0; r < r1; ++r) {
-        const uint32_t c = cnt[r];
-        counts[row0 + r] = c;
-        cnt[r] = run;
-        run += c;
-    }
-    __syncthreads();
+    msm_wave_scan(cnt, rows, start, &total_sh,
+                  [&](uint32_t r, uint32_t c) { counts[row0 + r] = c; });
     for (uint32_t e0 = start + t; e0 < end; e0 += NB * T) {
         uint2 x[NB];
 #pragma unroll
