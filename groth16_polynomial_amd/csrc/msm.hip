@@ -21,7 +21,7 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr uint32_t kMaxC = 16;  // a window's counters fit in LDS (2^15 x 4 bytes)
-constexpr uint32_t kSliceLen = 32;
+constexpr uint32_t kSliceLen = 32;     // entries per accumulation thread, at least
 constexpr uint32_t kSegLen = 8;
 constexpr uint32_t kMaxOnesGroups = 1024;  // workgroups of the scalar-one pass, at most
 constexpr uint32_t kBinEntries = 8192;   // entries per coarse bin, about (at most 1024 bins)
@@ -49,29 +49,57 @@ bool device_pointer(const void* p) {
            attr.type == hipMemoryTypeUnified;
 }
 
+// Entries per accumulation thread: kSliceLen, doubled while below a bucket's mean run
+// n / 2^(c-1) as long as the windows still give 2^18 threads or more (four waves per
+// SIMD).  So at large n a typical run spans one or two slices instead of many, and only
+// repeated scalars (or a window with few buckets) make runs over many slices.
+uint32_t slice_len_for(uint64_t n, uint32_t c) {
+    const uint64_t mean = n >> (c - 1);
+    const uint64_t cap = (uint64_t)windows_for(c) * n >> 18;
+    uint32_t len = kSliceLen;
+    while (len < mean && 2u * len <= cap && len < (1u << 16)) len *= 2;
+    return len;
+}
+
 // Window width minimising a cost in point additions: n per window for the accumulation,
-// about three per bucket for the merge and the weighted window sum, and the merge of the
-// top window's buckets.  Scalars below r < 2^254 leave the top window only
-// 254 - (W - 1) c bits, so its few buckets hold about n / 2^bits entries each; a
-// workgroup merges such a bucket's slice partials, 256 at a time and then by a tree of
-// eight levels, and each of those serial additions is priced at the 16384 additions the
-// chip does in parallel meanwhile.
-uint32_t default_c(uint64_t n) {
+// about one per bucket for the merge and the weighted window sum (much of that work
+// overlaps: measured widths at 2^12 .. 2^22 fit this weight, not three), and the merge of
+// the top window's buckets when their runs are long.  Scalars below r < 2^254 leave the
+// top window only 254 - (W - 1) c bits, so its few buckets hold about n / 2^bits entries
+// each; when such a run spans more than eight slices a workgroup merges the bucket's
+// slice partials, 256 at a time and then by a tree of eight levels, and each of those
+// serial additions is priced at the 16384 additions the chip does in parallel meanwhile.
+uint32_t model_c(uint64_t n) {
     uint32_t best = 1;
     double best_cost = 0.0;
     for (uint32_t c = 1; c <= kMaxC; ++c) {
         const uint32_t W = windows_for(c);
         const int top_bits = 254 - (int)((W - 1) * c);
         const double fat = (double)n / (double)(1ull << (top_bits > 0 ? top_bits : 0));
-        const double serial = fat / (double)kSliceLen / 256.0 + 8.0;
-        const double cost = (double)W * ((double)n + 3.0 * (double)(1u << (c - 1))) +
-                            16384.0 * serial;
+        const double slices = fat / (double)slice_len_for(n, c);
+        const double serial = slices > 8.0 ? slices / 256.0 + 8.0 : 0.0;
+        const double cost = (double)W * ((double)n + (double)(1u << (c - 1))) + 16384.0 * serial;
         if (c == 1 || cost < best_cost) {
             best = c;
             best_cost = cost;
         }
     }
     return best;
+}
+
+// The default width: from 2^10 terms, the fastest width measured on MI355X at each size
+// (every width timed at 2^10, 2^12, 2^14 .. 2^22; sizes between take the entry below).
+// Up to 2^15 the MSM is bound by the latency of its serial chains (a slice's additions,
+// a segment's double-and-add, the tree passes), which grow with c, so small widths win;
+// from 2^16 the accumulation's n W additions dominate and 15 or 16 wins.  Below 2^10 the
+// cost model, at most the width of 2^10.
+uint32_t default_c(uint64_t n) {
+    if (n < (1u << 10)) return std::min<uint32_t>(model_c(n), 5u);
+    uint32_t lg = 0;
+    while ((n >> (lg + 1)) != 0) ++lg;
+    if (lg >= 17) return 16;
+    static const uint8_t kBest[7] = {5, 6, 6, 8, 8, 9, 15};  // 2^10 .. 2^16
+    return kBest[lg - 10];
 }
 
 struct Layout {
@@ -91,8 +119,8 @@ bool make_layout(uint64_t n, uint32_t c, Layout* L) {
     mp.c = c;
     mp.windows = W;
     mp.buckets = 1u << (c - 1);
-    mp.slice_len = kSliceLen;
-    mp.slices = (uint32_t)((n + kSliceLen - 1) / kSliceLen);
+    mp.slice_len = slice_len_for(n, c);
+    mp.slices = (uint32_t)((n + mp.slice_len - 1) / mp.slice_len);
     mp.seg_len = mp.buckets < kSegLen ? mp.buckets : kSegLen;
     mp.segs = mp.buckets / mp.seg_len;
     const uint64_t groups = (n + g16::kMsmThreads - 1) / g16::kMsmThreads;
@@ -134,7 +162,8 @@ bool make_layout(uint64_t n, uint32_t c, Layout* L) {
     L->bin_offs = take((size_t)W * mp.bins * mp.chunks * 4);
     L->entries = take((size_t)W * n * 8);
     L->spill_rows = take(spills * 4);
-    L->spill_pts = take(spills * sizeof(G1Xyzz));
+    // the spill points' area also holds the coarse-sorted entries before the accumulation
+    L->spill_pts = take(std::max(spills * sizeof(G1Xyzz), (size_t)W * n * 8));
     L->buckets = take(rows * sizeof(G1Xyzz));
     L->seg_out = take((size_t)W * mp.segs * sizeof(G1Xyzz));
     L->partials = take((size_t)W * L->groups * sizeof(G1Xyzz));
@@ -213,8 +242,8 @@ int g16_msm_g1(uint64_t n, const void* scalars_std, const void* bases_mont, uint
     const G1Aff* bases = (const G1Aff*)bases_mont;
     const uint32_t rows = W * mp.buckets;
     const dim3 blk(g16::kMsmThreads), sort_blk(g16::kMsmSortThreads);
-    // The coarse-sorted entries live in the spill area until the accumulation: 2 W
-    // ceil(n / 32) spill points of 128 bytes hold W n entries of 8.
+    // The coarse-sorted entries live in the spill area until the accumulation (the area
+    // holds W n entries of 8 bytes).
     uint2* binned = (uint2*)spill_pts;
     const size_t count_lds = (size_t)mp.bins * 16;
     const size_t place_lds = (size_t)g16::kMsmRound * 8 + (size_t)mp.bins * 12;

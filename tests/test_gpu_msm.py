@@ -136,15 +136,17 @@ def test_msm_top_scalars():
         _msm_case(600, c, seed=31 + c, mutate=mutate)
 
 
-@pytest.mark.parametrize("log_n", [16, 18, 20, 22])
-def test_msm_large_by_linearity(log_n):
-    """Bases s_i G made on the GPU, scalars k_i: the result is (sum k_i s_i mod r) G."""
+@pytest.mark.parametrize("log_n,c", [(16, 0), (18, 0), (20, 0), (22, 0), (20, 15), (22, 15)])
+def test_msm_large_by_linearity(log_n, c):
+    """Bases s_i G made on the GPU, scalars k_i: the result is (sum k_i s_i mod r) G.  The
+    default widths, and c = 15, whose buckets' mean runs (64 and 256 entries) take longer
+    accumulation slices."""
     n = 1 << log_n
-    say("msm linearity n=2^%d" % log_n)
+    say("msm linearity n=2^%d c=%d" % (log_n, c))
     s = synth.uniform_fr(200 + log_n, n)
     k = scalars_from(300 + log_n, n, zeros=n // 50, ones=n // 60)
     bases = g.g1_generator_mul(dev(s))
-    ctx = g.MsmG1(n)
+    ctx = g.MsmG1(n, c)
     got = ctx(dev(k), bases)
     total = sum(a * b for a, b in zip(ints(k), ints(s))) % R
     want = msm.scalar_mul(msm.to_words([total]))[0]
