@@ -27,7 +27,7 @@ constexpr uint32_t kMaxOnesGroups = 1024;  // workgroups of the scalar-one pass,
 constexpr uint32_t kBinEntries = 8192;   // entries per coarse bin, about (at most 1024 bins)
 constexpr uint32_t kStage = 8192;        // entries of a bin staged in LDS by the row sort
 constexpr uint32_t kMinChunk = 8192;     // codes per coarse-sorting workgroup, at least
-constexpr uint32_t kFatGroups = 128;    // workgroups of the long-run merge
+constexpr uint32_t kFatGroups = 2048;   // workgroups of the long-run merge, at most
 
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -51,13 +51,27 @@ bool device_pointer(const void* p) {
 
 // Entries per accumulation thread: kSliceLen, doubled while below a bucket's mean run
 // n / 2^(c-1) as long as the windows still give 2^18 threads or more (four waves per
-// SIMD).  So at large n a typical run spans one or two slices instead of many, and only
-// repeated scalars (or a window with few buckets) make runs over many slices.
+// SIMD), so that at large n a typical run spans one or two slices instead of many; and
+// halved, down to 4, while the windows give fewer than 2^16 threads (one wave per SIMD),
+// since at small n the time is a thread's chain of dependent additions.  A run over more
+// than eight slices goes to the long-run merge, a workgroup per bucket: the halving stops
+// at a quarter of the mean run unless every bucket fits in one round of that merge.
 uint32_t slice_len_for(uint64_t n, uint32_t c) {
     const uint64_t mean = n >> (c - 1);
-    const uint64_t cap = (uint64_t)windows_for(c) * n >> 18;
+    const uint64_t entries = (uint64_t)windows_for(c) * n;
+    const bool one_round = (uint64_t)windows_for(c) << (c - 1) <= kFatGroups;
     uint32_t len = kSliceLen;
-    while (len < mean && 2u * len <= cap && len < (1u << 16)) len *= 2;
+    while (len < mean && 2u * len <= (entries >> 18) && len < (1u << 16)) len *= 2;
+    while (len > 4u && entries / len < (1u << 16) && (one_round || len / 2u >= mean / 4u))
+        len /= 2;
+    return len;
+}
+
+// Buckets per window-sum thread: kSegLen, halved, down to 1, while the windows give fewer
+// than 2^16 threads (the same reason).
+uint32_t seg_len_for(uint32_t W, uint32_t buckets) {
+    uint32_t len = buckets < kSegLen ? buckets : kSegLen;
+    while (len > 1u && (uint64_t)W * (buckets / len) < (1u << 16)) len /= 2;
     return len;
 }
 
@@ -88,17 +102,17 @@ uint32_t model_c(uint64_t n) {
 }
 
 // The default width: from 2^10 terms, the fastest width measured on MI355X at each size
-// (every width timed at 2^10, 2^12, 2^14 .. 2^22; sizes between take the entry below).
+// (every width timed at 2^10, 2^12, 2^14 .. 2^21; sizes between take the entry below).
 // Up to 2^15 the MSM is bound by the latency of its serial chains (a slice's additions,
-// a segment's double-and-add, the tree passes), which grow with c, so small widths win;
-// from 2^16 the accumulation's n W additions dominate and 15 or 16 wins.  Below 2^10 the
-// cost model, at most the width of 2^10.
+// a segment's double-and-add, the tree passes) and narrower windows win; from 2^16 the
+// accumulation's n W additions dominate and 16 wins.  Below 2^10 the cost model, at most
+// 5.
 uint32_t default_c(uint64_t n) {
     if (n < (1u << 10)) return std::min<uint32_t>(model_c(n), 5u);
     uint32_t lg = 0;
     while ((n >> (lg + 1)) != 0) ++lg;
-    if (lg >= 17) return 16;
-    static const uint8_t kBest[7] = {5, 6, 6, 8, 8, 9, 15};  // 2^10 .. 2^16
+    if (lg >= 16) return 16;
+    static const uint8_t kBest[6] = {8, 8, 6, 6, 10, 10};  // 2^10 .. 2^15
     return kBest[lg - 10];
 }
 
@@ -121,7 +135,7 @@ bool make_layout(uint64_t n, uint32_t c, Layout* L) {
     mp.buckets = 1u << (c - 1);
     mp.slice_len = slice_len_for(n, c);
     mp.slices = (uint32_t)((n + mp.slice_len - 1) / mp.slice_len);
-    mp.seg_len = mp.buckets < kSegLen ? mp.buckets : kSegLen;
+    mp.seg_len = seg_len_for(W, mp.buckets);
     mp.segs = mp.buckets / mp.seg_len;
     const uint64_t groups = (n + g16::kMsmThreads - 1) / g16::kMsmThreads;
     mp.ones_groups = (uint32_t)(groups < kMaxOnesGroups ? groups : kMaxOnesGroups);
@@ -272,7 +286,8 @@ int g16_msm_g1(uint64_t n, const void* scalars_std, const void* bases_mont, uint
                        entries, bases, cursor, mp, buckets, spill_pts, spill_rows);
     hipLaunchKernelGGL(g16::msm_merge, dim3(blocks_for(rows)), blk, 0, s, counts, cursor,
                        spill_pts, spill_rows, mp, buckets, fat_count, fat_rows);
-    hipLaunchKernelGGL(g16::msm_merge_fat, dim3(kFatGroups), blk, 0, s, counts, cursor, spill_pts,
+    hipLaunchKernelGGL(g16::msm_merge_fat, dim3(rows < kFatGroups ? rows : kFatGroups), blk, 0, s,
+                       counts, cursor, spill_pts,
                        spill_rows, mp, (const uint32_t*)fat_count, (const uint32_t*)fat_rows,
                        buckets);
     hipLaunchKernelGGL(g16::msm_reduce_segments, dim3(blocks_for((uint64_t)W * mp.segs)), blk, 0,

@@ -506,7 +506,7 @@ __global__ void __launch_bounds__(kMsmThreads) msm_merge(const uint32_t* counts,
 // Pass 6b: the listed rows, one workgroup at a time (a grid-stride loop over the list,
 // whose length every thread reads once before the loop, so all reach every barrier):
 // the threads take the run's slices in turn, each adding the spills that carry the row,
-// then a tree in LDS.  Such a run spans at least two slices, so the accumulation never
+// then a tree in LDS over the threads that took one.  Such a run spans at least two slices, so the accumulation never
 // wrote its bucket directly.
 __global__ void __launch_bounds__(kMsmThreads) msm_merge_fat(const uint32_t* counts,
                                                              const uint32_t* cursor,
@@ -533,10 +533,15 @@ __global__ void __launch_bounds__(kMsmThreads) msm_merge_fat(const uint32_t* cou
                 acc = xyzz_add(acc, xyzz_to29(msm_ld_xyzz(spill_pts + slot + 1u)));
         }
         sh[t] = acc;
-        for (uint32_t s = kMsmThreads / 2; s > 0; s >>= 1) {
+        // the tree spans the threads that took a slice (the same bound in every thread)
+        const uint32_t used = k_hi - k_lo + 1u < kMsmThreads ? k_hi - k_lo + 1u : kMsmThreads;
+        uint32_t top = 1;
+        while (top < used) top *= 2;
+        for (uint32_t s = top / 2; s > 0; s >>= 1) {
             __syncthreads();
             if (t < s) sh[t] = xyzz_add(sh[t], sh[t + s]);
         }
+        __syncthreads();
         if (t == 0) msm_st_xyzz(buckets + row, xyzz_from29(sh[0]));
         __syncthreads();  // sh is reused by the next listed row
     }
