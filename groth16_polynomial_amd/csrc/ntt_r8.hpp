@@ -243,8 +243,8 @@ __device__ __forceinline__ void group_fwd(V29 (&x)[E], uint32_t c, uint32_t low,
                                           uint32_t log_n, const Tw29* tw) {
     const uint32_t cl = c & ((1u << B0) - 1u);
     auto idx_for = [&](auto u_c) {
-        constexpr int u = decltype(u_c)::value;
-        return [&](auto b_c) {
+        return [&](auto b_c) {  // u from the type alone: the lambda outlives this call
+            constexpr int u = decltype(u_c)::value;
             constexpr int m = decltype(b_c)::value & ((1 << u) - 1);
             return fwd_tw_index(log_n, s0, (uint32_t)(B0 + u), low, cl + ((uint32_t)m << B0));
         };
@@ -270,8 +270,8 @@ __device__ __forceinline__ void group_inv(V29 (&x)[E], uint32_t c, uint32_t h, u
                                           uint32_t log_n, const Tw29* tw) {
     const uint32_t ch = c >> B0;
     auto idx_for = [&](auto u_c) {
-        constexpr int u = decltype(u_c)::value;
-        return [&](auto b_c) {
+        return [&](auto b_c) {  // u from the type alone: the lambda outlives this call
+            constexpr int u = decltype(u_c)::value;
             constexpr int m = decltype(b_c)::value >> u;  // = q >> (u + 1)
             const uint32_t a = (uint32_t)m + (ch << (R - 1 - u));
             return inv_tw_index(log_n, s0, (uint32_t)K, (uint32_t)(B0 + u), a, h);
