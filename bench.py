@@ -334,6 +334,29 @@ def main():
         "bucket_adds_per_s_g": round(n * mctx.windows / (msm_ms / 1e3) / 1e9, 3),
     }
     del bases, mctx
+    # the same MSM at other sizes (default widths), uniform scalars k_i over bases k_i G
+    if log_n == 20:
+        sizes = {}
+        for lg in (12, 16, 22):
+            m = 1 << lg
+            ks = g.to_device(synth.uniform_fr(8, m))
+            mb = g.g1_generator_mul(ks)
+            mc = g.MsmG1(m)
+            for _ in range(2):
+                mc.window_sums(ks, mb)
+            torch.cuda.synchronize()
+            f0.record(stream)
+            for _ in range(5):
+                mc.window_sums(ks, mb)
+            f1.record(stream)
+            torch.cuda.synchronize()
+            t_ms = f0.elapsed_time(f1) / 5
+            sizes["2^%d" % lg] = {"window_bits": mc.c, "device_ms": round(t_ms, 4),
+                                  "bucket_adds_per_s_g":
+                                      round(m * mc.windows / (t_ms / 1e3) / 1e9, 3)}
+            del ks, mb, mc
+        torch.cuda.empty_cache()
+        msm_line["other_sizes"] = sizes
     print("[bench] msm: %s" % msm_line, file=sys.stderr, flush=True)
     dom = int(np.argmax(stage_ms))
     kind, join, nv, k = stages[dom]
