@@ -25,7 +25,8 @@ constexpr uint32_t kSliceLen = 32;     // entries per accumulation thread, at le
 constexpr uint32_t kSegLen = 8;
 constexpr uint32_t kMaxOnesGroups = 1024;  // workgroups of the scalar-one pass, at most
 constexpr uint32_t kBinEntries = 8192;   // entries per coarse bin, about (at most 1024 bins)
-constexpr uint32_t kStage = 8192;        // entries of a bin staged in LDS by the row sort
+constexpr uint32_t kStage = 9216;        // entries of a bin staged in LDS by the row sort (its
+                                         // bins hold ~8192 on average)
 constexpr uint32_t kMinChunk = 8192;     // codes per coarse-sorting workgroup, at least
 constexpr uint32_t kFatGroups = 2048;   // workgroups of the long-run merge, at most
 
@@ -155,10 +156,11 @@ bool make_layout(uint64_t n, uint32_t c, Layout* L) {
     if (chunk < kMinChunk) chunk = kMinChunk;
     mp.chunk = (uint32_t)chunk;
     mp.chunks = (uint32_t)((mp.n_pad + chunk - 1) / chunk);
-    // LDS of the row sort: the staged entries and a counter per row, within 96 KiB
+    // LDS of the row sort: two buffers of staged entries and a counter per row, within
+    // 144 KiB
     const uint64_t row_bytes = ((uint64_t)1 << mp.bin_shift) * 4;
-    mp.stage = row_bytes >= 96 * 1024 ? 0u
-               : (uint32_t)std::min<uint64_t>(kStage, (96 * 1024 - row_bytes) / 8);
+    mp.stage = row_bytes >= 144 * 1024 ? 0u
+               : (uint32_t)std::min<uint64_t>(kStage, (144 * 1024 - row_bytes) / 16);
     L->per_group = mp.segs < g16::kMsmThreads ? mp.segs : g16::kMsmThreads;
     L->groups = mp.segs / L->per_group;
     const size_t rows = (size_t)W * mp.buckets;
@@ -261,7 +263,7 @@ int g16_msm_g1(uint64_t n, const void* scalars_std, const void* bases_mont, uint
     uint2* binned = (uint2*)spill_pts;
     const size_t count_lds = (size_t)mp.bins * 16;
     const size_t place_lds = (size_t)g16::kMsmRound * 8 + (size_t)mp.bins * 12;
-    const size_t row_lds = (size_t)mp.stage * 8 + ((size_t)1 << mp.bin_shift) * 4;
+    const size_t row_lds = (size_t)mp.stage * 16 + ((size_t)1 << mp.bin_shift) * 4;
     // LDS beyond the default 64 KiB is allowed per kernel
     if (hipFuncSetAttribute((const void*)g16::msm_bin_place,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)place_lds) !=

@@ -352,11 +352,12 @@ __global__ void __launch_bounds__(kMsmBinThreads) msm_bin_place(const uint16_t* 
 // Pass 5: one workgroup per (window, bin) sorts the bin's entries by row, from their
 // contiguous part of binned into the same part of entries: a count per row in LDS, an
 // exclusive scan, then each entry to its row's next slot.  Writes counts[row] and
-// cursor[row] (the row's run end) for the bin's rows.  Every write falls inside the bin's
-// part, which is small enough for the cache to assemble whole lines.  The counting pass
-// keeps the bin's first mp.stage entries in LDS for the placing pass (a larger bin, as
-// equal scalars make, reads the rest again), and each thread loads kMsmSortBatch entries
-// before it uses any, so that their loads overlap.
+// cursor[row] (the row's run end) for the bin's rows.  A bin of at most mp.stage entries
+// (every bin of uniform scalars) is sorted in LDS: loaded once, ranked into a second
+// buffer, and written out in order, so the global writes are contiguous.  A larger bin (as
+// equal scalars make) keeps its first mp.stage entries in LDS, reads the rest again and
+// writes each entry to its slot.  Each thread loads kMsmSortBatch entries before it uses
+// any, so that their loads overlap.
 constexpr uint32_t kMsmSortBatch = 8;
 
 __global__ void __launch_bounds__(kMsmSortThreads) msm_bin_sort(const uint2* binned,
@@ -365,8 +366,10 @@ __global__ void __launch_bounds__(kMsmSortThreads) msm_bin_sort(const uint2* bin
                                                                 MsmParams mp, uint32_t* counts,
                                                                 uint32_t* cursor, uint2* entries) {
     constexpr uint32_t T = kMsmSortThreads, NB = kMsmSortBatch;
-    extern __shared__ uint2 stage[];  // mp.stage entries, then a counter per row of the bin
-    uint32_t* cnt = reinterpret_cast<uint32_t*>(stage + mp.stage);
+    // mp.stage entries as loaded, mp.stage entries in row order, a counter per row
+    extern __shared__ uint2 stage[];
+    uint2* sorted = stage + mp.stage;
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(sorted + mp.stage);
     __shared__ uint32_t total_sh;
     const uint32_t w = blockIdx.x / mp.bins, bin = blockIdx.x - w * mp.bins;
     const uint32_t t = threadIdx.x;
@@ -377,6 +380,7 @@ __global__ void __launch_bounds__(kMsmSortThreads) msm_bin_sort(const uint2* bin
     const size_t last = msm_bin_index(mp, w, mp.bins - 1u, mp.chunks - 1u);
     const uint32_t end = bin + 1u < mp.bins ? bin_offs[msm_bin_index(mp, w, bin + 1u, 0u)]
                                             : bin_offs[last] + bin_counts[last];
+    const bool in_lds = end - start <= mp.stage;  // the same in every thread
     const uint32_t row0 = w * mp.buckets + bin * rows;
     for (uint32_t r = t; r < rows; r += T) cnt[r] = 0u;
     __syncthreads();
@@ -394,8 +398,19 @@ __global__ void __launch_bounds__(kMsmSortThreads) msm_bin_sort(const uint2* bin
         }
     }
     __syncthreads();
-    msm_wave_scan(cnt, rows, start, &total_sh,
+    // the rows' run starts: relative to the bin in LDS, absolute otherwise
+    msm_wave_scan(cnt, rows, in_lds ? 0u : start, &total_sh,
                   [&](uint32_t r, uint32_t c) { counts[row0 + r] = c; });
+    if (in_lds) {
+        for (uint32_t k = t; k < end - start; k += T) {
+            const uint2 x = stage[k];
+            sorted[atomicAdd(&cnt[x.x - row0], 1u)] = x;
+        }
+        __syncthreads();
+        for (uint32_t k = t; k < end - start; k += T) entries[start + k] = sorted[k];
+        for (uint32_t r = t; r < rows; r += T) cursor[row0 + r] = start + cnt[r];
+        return;
+    }
     for (uint32_t e0 = start + t; e0 < end; e0 += NB * T) {
         uint2 x[NB];
 #pragma unroll
