@@ -179,11 +179,11 @@ bool make_layout(uint64_t n, uint32_t c, Layout* L) {
     L->entries = take((size_t)W * n * 8);
     L->spill_rows = take(spills * 4);
     // the spill points' area also holds the coarse-sorted entries before the accumulation
-    L->spill_pts = take(std::max(spills * sizeof(G1Xyzz), (size_t)W * n * 8));
-    L->buckets = take(rows * sizeof(G1Xyzz));
-    L->seg_out = take((size_t)W * mp.segs * sizeof(G1Xyzz));
-    L->partials = take((size_t)W * L->groups * sizeof(G1Xyzz));
-    L->ones_out = take((size_t)mp.ones_groups * sizeof(G1Xyzz));
+    L->spill_pts = take(std::max(spills * sizeof(g16::P29), (size_t)W * n * 8));
+    L->buckets = take(rows * sizeof(g16::P29));
+    L->seg_out = take((size_t)W * mp.segs * sizeof(g16::P29));
+    L->partials = take((size_t)W * L->groups * sizeof(g16::P29));
+    L->ones_out = take((size_t)mp.ones_groups * sizeof(g16::P29));
     L->fat = take((rows + 1) * 4);  // list length, then the listed rows
     L->total = off;
     return true;
@@ -247,11 +247,11 @@ int g16_msm_g1(uint64_t n, const void* scalars_std, const void* bases_mont, uint
     uint32_t* bin_offs = (uint32_t*)(ws + L.bin_offs);
     uint2* entries = (uint2*)(ws + L.entries);
     uint32_t* spill_rows = (uint32_t*)(ws + L.spill_rows);
-    G1Xyzz* spill_pts = (G1Xyzz*)(ws + L.spill_pts);
-    G1Xyzz* buckets = (G1Xyzz*)(ws + L.buckets);
-    G1Xyzz* seg_out = (G1Xyzz*)(ws + L.seg_out);
-    G1Xyzz* partials = (G1Xyzz*)(ws + L.partials);
-    G1Xyzz* ones_out = (G1Xyzz*)(ws + L.ones_out);
+    g16::P29* spill_pts = (g16::P29*)(ws + L.spill_pts);
+    g16::P29* buckets = (g16::P29*)(ws + L.buckets);
+    g16::P29* seg_out = (g16::P29*)(ws + L.seg_out);
+    g16::P29* partials = (g16::P29*)(ws + L.partials);
+    g16::P29* ones_out = (g16::P29*)(ws + L.ones_out);
     uint32_t* fat_count = (uint32_t*)(ws + L.fat);
     uint32_t* fat_rows = fat_count + 1;
     const uint32_t* sc = (const uint32_t*)scalars_std;
@@ -295,10 +295,11 @@ int g16_msm_g1(uint64_t n, const void* scalars_std, const void* bases_mont, uint
     hipLaunchKernelGGL(g16::msm_reduce_segments, dim3(blocks_for((uint64_t)W * mp.segs)), blk, 0,
                        s, counts, buckets, mp, seg_out);
     hipLaunchKernelGGL(g16::msm_ones, dim3(mp.ones_groups), blk, 0, s, sc, bases, mp, ones_out);
-    hipLaunchKernelGGL(g16::msm_sum_groups, dim3(W * L.groups), blk, 0, s, seg_out, L.per_group,
-                       (const G1Xyzz*)nullptr, 0u, partials);
-    hipLaunchKernelGGL(g16::msm_sum_groups, dim3(W), blk, 0, s, partials, L.groups, ones_out,
-                       mp.ones_groups, (G1Xyzz*)window_sums);
+    hipLaunchKernelGGL(g16::msm_sum_groups<g16::P29>, dim3(W * L.groups), blk, 0, s,
+                       (const g16::P29*)seg_out, L.per_group, (const g16::P29*)nullptr, 0u,
+                       partials);
+    hipLaunchKernelGGL(g16::msm_sum_groups<G1Xyzz>, dim3(W), blk, 0, s, (const g16::P29*)partials,
+                       L.groups, (const g16::P29*)ones_out, mp.ones_groups, (G1Xyzz*)window_sums);
     return hipGetLastError() == hipSuccess ? G16_OK : G16_EHIP;
 }
 

@@ -25,6 +25,8 @@
 // rather than one block per window; the ones' partial sums are added into window 0.
 #pragma once
 
+#include <type_traits>
+
 #include "g1.hpp"
 #include "msm_digit.hpp"
 
@@ -104,6 +106,38 @@ __device__ __forceinline__ void msm_st_xyzz(G1Xyzz* p, const G1Xyzz& a) {
     msm_st_fp(&p->y, a.y);
     msm_st_fp(&p->zz, a.zz);
     msm_st_fp(&p->zzz, a.zzz);
+}
+
+// A point as the point kernels pass it to one another (bucket partials, spills, segment and
+// group sums): the nine-digit form itself, 144 bytes (nine 16-byte words), lazily reduced
+// (bounds in fp29.hpp: a sum of two such points forms smaller values than a converted
+// base does), so neither side converts; infinity stays all-zero digits.  Only the window
+// sums handed to the host are canonical.
+using P29 = XyzzT<Fp29>;
+static_assert(sizeof(P29) == 144, "P29 is nine 16-byte words");
+
+__device__ __forceinline__ P29 msm_ld_p29(const P29* p) {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+    P29 a;
+    int32_t* o = reinterpret_cast<int32_t*>(&a);
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+        const uint4 v = q[i];
+        o[4 * i] = (int32_t)v.x;
+        o[4 * i + 1] = (int32_t)v.y;
+        o[4 * i + 2] = (int32_t)v.z;
+        o[4 * i + 3] = (int32_t)v.w;
+    }
+    return a;
+}
+
+__device__ __forceinline__ void msm_st_p29(P29* p, const P29& a) {
+    uint4* q = reinterpret_cast<uint4*>(p);
+    const int32_t* o = reinterpret_cast<const int32_t*>(&a);
+#pragma unroll
+    for (int i = 0; i < 9; ++i)
+        q[i] = make_uint4((uint32_t)o[4 * i], (uint32_t)o[4 * i + 1], (uint32_t)o[4 * i + 2],
+                          (uint32_t)o[4 * i + 3]);
 }
 
 // Fills a u32 array (the counters start at zero: device memory is never assumed clear).
@@ -441,7 +475,7 @@ __device__ __forceinline__ uint32_t msm_used(const uint32_t* cursor, const MsmPa
 __global__ void __launch_bounds__(kMsmThreads) msm_accumulate(const uint2* entries,
                                                               const G1Aff* bases,
                                                               const uint32_t* cursor, MsmParams mp,
-                                                              G1Xyzz* buckets, G1Xyzz* spill_pts,
+                                                              P29* buckets, P29* spill_pts,
                                                               uint32_t* spill_rows) {
     const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
     const uint32_t w = gid / mp.slices;
@@ -463,10 +497,10 @@ __global__ void __launch_bounds__(kMsmThreads) msm_accumulate(const uint2* entri
         if (ent.x != cur) {
             if (first) {
                 spill_rows[head] = cur;
-                msm_st_xyzz(spill_pts + head, xyzz_from29(acc));
+                msm_st_p29(spill_pts + head, acc);
                 first = false;
             } else {
-                msm_st_xyzz(buckets + cur, xyzz_from29(acc));
+                msm_st_p29(buckets + cur, acc);
             }
             acc = xyzz_zero<Fp29>();
             cur = ent.x;
@@ -477,7 +511,7 @@ __global__ void __launch_bounds__(kMsmThreads) msm_accumulate(const uint2* entri
     }
     const uint32_t slot = first ? head : tail;
     spill_rows[slot] = cur;
-    msm_st_xyzz(spill_pts + slot, xyzz_from29(acc));
+    msm_st_p29(spill_pts + slot, acc);
 }
 
 // Pass 6: one thread per bucket row with entries.  Starts from the direct write when
@@ -488,9 +522,9 @@ __global__ void __launch_bounds__(kMsmThreads) msm_accumulate(const uint2* entri
 // adds thousands of spills one after another.
 __global__ void __launch_bounds__(kMsmThreads) msm_merge(const uint32_t* counts,
                                                          const uint32_t* cursor,
-                                                         const G1Xyzz* spill_pts,
+                                                         const P29* spill_pts,
                                                          const uint32_t* spill_rows, MsmParams mp,
-                                                         G1Xyzz* buckets, uint32_t* fat_count,
+                                                         P29* buckets, uint32_t* fat_count,
                                                          uint32_t* fat_rows) {
     const uint32_t row = blockIdx.x * blockDim.x + threadIdx.x;
     if (row >= mp.windows * mp.buckets) return;
@@ -508,29 +542,29 @@ __global__ void __launch_bounds__(kMsmThreads) msm_merge(const uint32_t* counts,
     const uint32_t slice_lo = k_lo * mp.slice_len;
     const uint32_t slice_hi = slice_lo + mp.slice_len < used ? slice_lo + mp.slice_len : used;
     const bool direct = k_lo == k_hi && start > slice_lo && end < slice_hi;
-    XyzzT<Fp29> acc = direct ? xyzz_to29(msm_ld_xyzz(buckets + row)) : xyzz_zero<Fp29>();
+    XyzzT<Fp29> acc = direct ? msm_ld_p29(buckets + row) : xyzz_zero<Fp29>();
     for (uint32_t k = k_lo; k <= k_hi; ++k) {
         const uint32_t slot = 2u * (w * mp.slices + k);
-        if (spill_rows[slot] == row) acc = xyzz_add(acc, xyzz_to29(msm_ld_xyzz(spill_pts + slot)));
+        if (spill_rows[slot] == row) acc = xyzz_add(acc, msm_ld_p29(spill_pts + slot));
         if (spill_rows[slot + 1u] == row)
-            acc = xyzz_add(acc, xyzz_to29(msm_ld_xyzz(spill_pts + slot + 1u)));
+            acc = xyzz_add(acc, msm_ld_p29(spill_pts + slot + 1u));
     }
-    msm_st_xyzz(buckets + row, xyzz_from29(acc));
+    msm_st_p29(buckets + row, acc);
 }
 
 // Pass 6b: the listed rows, one workgroup at a time (a grid-stride loop over the list,
 // whose length every thread reads once before the loop, so all reach every barrier):
 // the threads take the run's slices in turn, each adding the spills that carry the row,
-// then a tree in LDS over the threads that took one.  Such a run spans at least two slices, so the accumulation never
-// wrote its bucket directly.
+// then a tree in LDS over the threads that took one.  Such a run spans at least two
+// slices, so the accumulation never wrote its bucket directly.
 __global__ void __launch_bounds__(kMsmThreads) msm_merge_fat(const uint32_t* counts,
                                                              const uint32_t* cursor,
-                                                             const G1Xyzz* spill_pts,
+                                                             const P29* spill_pts,
                                                              const uint32_t* spill_rows,
                                                              MsmParams mp,
                                                              const uint32_t* fat_count,
                                                              const uint32_t* fat_rows,
-                                                             G1Xyzz* buckets) {
+                                                             P29* buckets) {
     __shared__ XyzzT<Fp29> sh[kMsmThreads];
     const uint32_t t = threadIdx.x;
     const uint32_t listed = *fat_count;
@@ -543,9 +577,9 @@ __global__ void __launch_bounds__(kMsmThreads) msm_merge_fat(const uint32_t* cou
         XyzzT<Fp29> acc = xyzz_zero<Fp29>();
         for (uint32_t k = k_lo + t; k <= k_hi; k += kMsmThreads) {
             const uint32_t slot = 2u * (w * mp.slices + k);
-            if (spill_rows[slot] == row) acc = xyzz_add(acc, xyzz_to29(msm_ld_xyzz(spill_pts + slot)));
+            if (spill_rows[slot] == row) acc = xyzz_add(acc, msm_ld_p29(spill_pts + slot));
             if (spill_rows[slot + 1u] == row)
-                acc = xyzz_add(acc, xyzz_to29(msm_ld_xyzz(spill_pts + slot + 1u)));
+                acc = xyzz_add(acc, msm_ld_p29(spill_pts + slot + 1u));
         }
         sh[t] = acc;
         // the tree spans the threads that took a slice (the same bound in every thread)
@@ -557,7 +591,7 @@ __global__ void __launch_bounds__(kMsmThreads) msm_merge_fat(const uint32_t* cou
             if (t < s) sh[t] = xyzz_add(sh[t], sh[t + s]);
         }
         __syncthreads();
-        if (t == 0) msm_st_xyzz(buckets + row, xyzz_from29(sh[0]));
+        if (t == 0) msm_st_p29(buckets + row, sh[0]);
         __syncthreads();  // sh is reused by the next listed row
     }
 }
@@ -567,8 +601,8 @@ __global__ void __launch_bounds__(kMsmThreads) msm_merge_fat(const uint32_t* cou
 // gives T = sum_j (j - lo + 1) B_j and Q = sum_j B_j, and the segment contributes
 // T + lo Q.  Buckets with no entries are infinity (never read).
 __global__ void __launch_bounds__(kMsmThreads) msm_reduce_segments(const uint32_t* counts,
-                                                                   const G1Xyzz* buckets,
-                                                                   MsmParams mp, G1Xyzz* seg_out) {
+                                                                   const P29* buckets,
+                                                                   MsmParams mp, P29* seg_out) {
     const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
     const uint32_t w = gid / mp.segs;
     if (w >= mp.windows) return;
@@ -576,18 +610,18 @@ __global__ void __launch_bounds__(kMsmThreads) msm_reduce_segments(const uint32_
     const size_t base = (size_t)w * mp.buckets;
     XyzzT<Fp29> run = xyzz_zero<Fp29>(), tot = xyzz_zero<Fp29>();
     for (uint32_t j = lo + mp.seg_len; j-- > lo;) {
-        if (counts[base + j]) run = xyzz_add(run, xyzz_to29(msm_ld_xyzz(buckets + base + j)));
+        if (counts[base + j]) run = xyzz_add(run, msm_ld_p29(buckets + base + j));
         tot = xyzz_add(tot, run);
     }
     if (lo) tot = xyzz_add(tot, xyzz_mul_small(run, lo));
-    msm_st_xyzz(seg_out + gid, xyzz_from29(tot));
+    msm_st_p29(seg_out + gid, tot);
 }
 
 // The scalar-one pass: sum of the bases whose scalar is exactly 1, strided over the
 // scalars, then a tree in LDS; one partial sum per workgroup.
 __global__ void __launch_bounds__(kMsmThreads) msm_ones(const uint32_t* scalars,
                                                         const G1Aff* bases, MsmParams mp,
-                                                        G1Xyzz* out) {
+                                                        P29* out) {
     __shared__ XyzzT<Fp29> sh[kMsmThreads];
     const uint32_t t = threadIdx.x;
     XyzzT<Fp29> acc = xyzz_zero<Fp29>();
@@ -601,30 +635,36 @@ __global__ void __launch_bounds__(kMsmThreads) msm_ones(const uint32_t* scalars,
         __syncthreads();
         if (t < s) sh[t] = xyzz_add(sh[t], sh[t + s]);
     }
-    if (t == 0) msm_st_xyzz(out + blockIdx.x, xyzz_from29(sh[0]));
+    if (t == 0) msm_st_p29(out + blockIdx.x, sh[0]);
 }
 
 // Pass 8: group sums.  Workgroup g adds in[g per, (g + 1) per) (and, for g = 0, the
 // n_extra points of extra) into out[g], a tree in LDS after a strided serial sum.  Run
 // twice: the segments' contributions into a few partials per window, then the partials
 // (and the ones' sums, into window 0) into the window sums.
-__global__ void __launch_bounds__(kMsmThreads) msm_sum_groups(const G1Xyzz* in, uint32_t per,
-                                                              const G1Xyzz* extra,
-                                                              uint32_t n_extra, G1Xyzz* out) {
+template <class Out>
+__global__ void __launch_bounds__(kMsmThreads) msm_sum_groups(const P29* in, uint32_t per,
+                                                              const P29* extra, uint32_t n_extra,
+                                                              Out* out) {
     __shared__ XyzzT<Fp29> sh[kMsmThreads];
     const uint32_t g = blockIdx.x, t = threadIdx.x;
     XyzzT<Fp29> acc = xyzz_zero<Fp29>();
     for (uint32_t s = t; s < per; s += kMsmThreads)
-        acc = xyzz_add(acc, xyzz_to29(msm_ld_xyzz(in + (size_t)g * per + s)));
+        acc = xyzz_add(acc, msm_ld_p29(in + (size_t)g * per + s));
     if (g == 0)
         for (uint32_t e = t; e < n_extra; e += kMsmThreads)
-            acc = xyzz_add(acc, xyzz_to29(msm_ld_xyzz(extra + e)));
+            acc = xyzz_add(acc, msm_ld_p29(extra + e));
     sh[t] = acc;
     for (uint32_t s = kMsmThreads / 2; s > 0; s >>= 1) {
         __syncthreads();
         if (t < s) sh[t] = xyzz_add(sh[t], sh[t + s]);
     }
-    if (t == 0) msm_st_xyzz(out + g, xyzz_from29(sh[0]));
+    if (t == 0) {
+        if constexpr (std::is_same<Out, G1Xyzz>::value)  // the window sums: canonical
+            msm_st_xyzz(out + g, xyzz_from29(sh[0]));
+        else
+            msm_st_p29(out + g, sh[0]);
+    }
 }
 
 // Synthetic bases and fixed-base multiples: out_i = k_i G in affine Montgomery form, one
