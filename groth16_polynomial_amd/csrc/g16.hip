@@ -620,8 +620,9 @@ int g16_gather_abc(uint64_t n_rows, const uint32_t* row_ptr_a, const uint32_t* s
         if (ins[i] && in_bytes[i] && !device_pointer(ins[i])) return G16_EINVAL;
     for (int o = 0; o < 3; ++o)
         if (!device_pointer(outs[o])) return G16_EINVAL;
-    uint32_t blocks = (uint32_t)((n_rows + kThreads - 1) / kThreads);
-    hipLaunchKernelGGL(g16::gather_kernel, dim3(blocks), dim3(kThreads), 0, (hipStream_t)stream,
+    const uint32_t blocks = (uint32_t)((n_rows + g16::kGatherLanes - 1) / g16::kGatherLanes);
+    hipLaunchKernelGGL(g16::gather_kernel, dim3(blocks), dim3(g16::kGatherLanes), 0,
+                       (hipStream_t)stream,
                        row_ptr_a, signal_a, (const Fr*)value_a, nnz_a, row_ptr_b, signal_b,
                        (const Fr*)value_b, nnz_b, (const Fr*)witness, n_witness, (Fr*)out_a,
                        (Fr*)out_b, (Fr*)out_c, n_rows);

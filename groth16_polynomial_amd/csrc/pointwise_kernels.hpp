@@ -83,8 +83,15 @@ __global__ void __launch_bounds__(256) table_kernel(Tw29* out, Fr base, Fr facto
     }
 }
 
-// The CSR gather, one lane per row (the GATHER_CU page: rows are short and ragged, so a
-// row per lane keeps every lane busy; 64 consecutive rows share a wave here).
+// The CSR gather: 64 consecutive rows per workgroup of one wave (the GATHER_CU page puts
+// a row on a lane: rows are short and ragged).  With a row per lane a wave would form as
+// many products as its longest row has terms, while most rows have one or two; here the
+// wave flattens its rows' terms instead: in each round of 64 terms every lane forms one
+// product (value times witness), and then every lane adds the products of its own row
+// from LDS (additions only).  A row whose range or a signal is out of bounds is flagged
+// and reads nothing out of bounds.
+constexpr uint32_t kGatherLanes = 64;
+
 __device__ __forceinline__ Fr fr_invalid() {
     Fr z;
 #pragma unroll
@@ -92,30 +99,92 @@ __device__ __forceinline__ Fr fr_invalid() {
     return z;
 }
 
-__device__ __forceinline__ bool gather_row(const uint32_t* row_ptr, const uint32_t* signal,
-                                           const Fr* value, uint64_t nnz, const Fr* witness,
-                                           uint64_t n_witness, uint64_t row, Fr& acc) {
-    uint32_t lo = row_ptr[row];
-    uint32_t hi = row_ptr[row + 1];
-    acc = fr_zero();
-    if (lo > hi || (uint64_t)hi > nnz) return false;
-    for (uint32_t k = lo; k < hi; ++k) {
-        uint32_t s = signal[k];
-        if ((uint64_t)s >= n_witness) return false;
-        acc = fr_add(acc, fr_mul(ld_global(value + k), ld_global(witness + s)));
+struct GatherLds {
+    uint64_t off[kGatherLanes];  // a row's first term in the wave's flattened list
+    uint64_t total;
+    uint32_t lo[kGatherLanes];   // a row's first index in the CSR arrays
+    uint32_t len[kGatherLanes];  // its number of terms
+    uint32_t bad[kGatherLanes];  // a row named a witness index out of range
+    Fr prod[kGatherLanes];       // the round's products, by flattened term
+};
+
+// Row `row` (lane `l`, valid when in_rows) of one matrix: its sum into acc; false when the
+// row's range or one of its signals is out of bounds.  Every lane of the workgroup calls it
+// (it has barriers).
+__device__ __forceinline__ bool gather_matrix(const uint32_t* row_ptr, const uint32_t* signal,
+                                              const Fr* value, uint64_t nnz, const Fr* witness,
+                                              uint64_t n_witness, uint64_t row, bool in_rows,
+                                              GatherLds& sh, Fr& acc) {
+    const uint32_t l = threadIdx.x;
+    uint32_t lo = 0, len = 0;
+    bool ok = true;
+    if (in_rows) {
+        lo = row_ptr[row];
+        const uint32_t hi = row_ptr[row + 1];
+        ok = lo <= hi && (uint64_t)hi <= nnz;
+        len = ok ? hi - lo : 0u;
     }
-    return true;
+    // exclusive prefix of the lengths over the wave (64-bit: ranges of malformed row
+    // pointers may overlap, and each is only checked against nnz)
+    uint64_t inc = len;
+#pragma unroll
+    for (uint32_t d = 1; d < kGatherLanes; d <<= 1) {
+        const uint64_t y = __shfl_up(inc, d, kGatherLanes);
+        if (l >= d) inc += y;
+    }
+    const uint64_t off = inc - len;
+    sh.off[l] = off;
+    sh.lo[l] = lo;
+    sh.len[l] = len;
+    sh.bad[l] = 0u;
+    if (l == kGatherLanes - 1u) sh.total = inc;
+    __syncthreads();
+    const uint64_t total = sh.total;
+    acc = fr_zero();
+    for (uint64_t t0 = 0; t0 < total; t0 += kGatherLanes) {
+        const uint64_t f = t0 + l;
+        Fr p = fr_zero();
+        if (f < total) {
+            // the last row whose first term is at or before f (empty rows share their
+            // successor's offset, so that row is the one holding f)
+            uint32_t r = 0;
+#pragma unroll
+            for (uint32_t step = kGatherLanes / 2; step > 0; step >>= 1)
+                if (r + step < kGatherLanes && sh.off[r + step] <= f) r += step;
+            const uint64_t j = f - sh.off[r];  // < len[r], so k < hi <= nnz
+            if (j < sh.len[r]) {
+                const uint32_t k = sh.lo[r] + (uint32_t)j;
+                const uint32_t s = signal[k];
+                if ((uint64_t)s < n_witness)
+                    p = fr_mul(ld_global(value + k), ld_global(witness + s));
+                else
+                    sh.bad[r] = 1u;
+            }
+        }
+        sh.prod[l] = p;
+        __syncthreads();
+        const uint64_t a0 = off > t0 ? off : t0;
+        const uint64_t a1 = off + len < t0 + kGatherLanes ? off + len : t0 + kGatherLanes;
+        for (uint64_t j = a0; j < a1; ++j) acc = fr_add(acc, sh.prod[j - t0]);
+        __syncthreads();
+    }
+    return ok && sh.bad[l] == 0u;
 }
 
-__global__ void __launch_bounds__(256) gather_kernel(
+__global__ void __launch_bounds__(kGatherLanes) gather_kernel(
     const uint32_t* row_ptr_a, const uint32_t* signal_a, const Fr* value_a, uint64_t nnz_a,
     const uint32_t* row_ptr_b, const uint32_t* signal_b, const Fr* value_b, uint64_t nnz_b,
     const Fr* witness, uint64_t n_witness, Fr* out_a, Fr* out_b, Fr* out_c, uint64_t n_rows) {
-    uint64_t row = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (row >= n_rows) return;
+    __shared__ GatherLds sh;
+    const uint64_t row = (uint64_t)blockIdx.x * kGatherLanes + threadIdx.x;
+    const bool in_rows = row < n_rows;
     Fr a, b;
-    bool ok = gather_row(row_ptr_a, signal_a, value_a, nnz_a, witness, n_witness, row, a);
-    ok = gather_row(row_ptr_b, signal_b, value_b, nnz_b, witness, n_witness, row, b) && ok;
+    bool ok = gather_matrix(row_ptr_a, signal_a, value_a, nnz_a, witness, n_witness, row, in_rows,
+                            sh, a);
+    ok = gather_matrix(row_ptr_b, signal_b, value_b, nnz_b, witness, n_witness, row, in_rows, sh,
+                       b) &&
+         ok;
+    if (!in_rows) return;
     if (ok) {
         st_global(out_a + row, a);
         st_global(out_b + row, b);
