@@ -11,7 +11,8 @@
 //     each; a run strictly inside a slice is written to its bucket directly, the first
 //     and last run of a slice go to two spill slots, and a merge pass adds each bucket's
 //     spills; XYZZ accumulators with affine bases, the arithmetic of every point kernel
-//     in nine 29-bit digits (fp29.hpp) between loads and stores of canonical values;
+//     in nine 29-bit digits (fp29.hpp), which is also the form the point kernels pass
+//     to one another (only the bases and the final window sums are canonical);
 //   * each window reduced to sum_m m B_m on the device; the host combines the windows
 //     by Horner's rule (the page's "THE WINDOW REDUCTION ENDS ON THE HOST").
 //
