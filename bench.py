@@ -133,8 +133,8 @@ def traffic_from_profiles(stage_name: str, src_hash: str):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only (--gpus %d requested); the "
-              "multi-GPU sharding is designed but not implemented"
+        print("bench.py: the library runs on one GPU (--gpus %d requested); sharding "
+              "across GPUs is designed but not implemented"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
 
