@@ -8,8 +8,22 @@ shift, three forward NTTs and H = A'B' - C' in both encodings.  Prints one JSON 
 Also measured (same run, reported inside the line):
   * each kernel (stage) of the pipeline alone, with HIP events on the stream it is
     launched on; the slowest is the dominant kernel and carries the roofline;
-  * the standalone forward NTT at 2^20 (Gbutterfly/s);
-  * the CPU oracle on the host, single-threaded, on the same 2^20 workload.
+  * the instruction issue rates of the arithmetic's building blocks (the probe
+    library), which give the measured multiply-add rate beside the nominal peak;
+  * the other workloads: the 2^12 pipeline (median per call and launch count), the
+    standalone forward and inverse NTT at 2^18 and 2^20, the CSR gather and the gather
+    plus pipeline at 2^18, the 2^22 pipeline, several proofs per call, the H MSM;
+  * the CPU oracle on the host, one thread and all threads, median of three, on the
+    same 2^20 workload.
+
+Units.  Work is counted in 32 x 32-bit limb products of the textbook 8-limb CIOS
+Montgomery product: 136 per field product, 72 per reduction.  A transform of n points
+has n/2 log n butterflies of one product each (twiddle-1 butterflies included); the H
+pipeline adds n products for the 1/n scaling, n for the coset shift (both per vector)
+and n for the join, plus n reductions: 70.25 M products and 9.63 G limb products at
+2^20.  Algorithmic bytes count every transform as two HBM round trips of 32-byte
+elements, the shift table and the join's extra reads and second output: 960 bytes per
+element.
 """
 from __future__ import annotations
 
@@ -18,31 +32,34 @@ import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-MAD_PEAK_T = 256 * 64 * 2.4e9 / 1e12   # v_mad_u64_u32: 256 CUs x 64 lanes x 2.4 GHz, T/s
+NOMINAL_PEAK_T = 256 * 64 * 2.4e9 / 1e12  # 256 CUs x 64 lanes x 2.4 GHz, one op a lane a clock
 HBM_PEAK_GBS = 8000.0
 MADS_PER_MUL = 136                      # 8-limb CIOS Montgomery product: 2 s^2 + s
 MADS_PER_REDC = 72                      # Montgomery reduction alone: s^2 + s
 FR_BYTES = 32
+ALG_BYTES_PER_ELEMENT = 960             # six transforms x two round trips x 64 + 96 + 96
 # (log n, proofs) of the several-proofs-per-call measurements: small domains, where one
 # call per proof is launch-bound
 BATCH_SHAPES = ((12, 64), (16, 16))
-# the H pipeline's other single-proof workloads (timed beside the headline 2^20 one)
-OTHER_SIZES = (12, 22)
 
 
 def parse():
-    ap = argparse.ArgumentParser(description=__doc__)
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--log-n", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-side", action="store_true",
+                    help="only the timed 2^log_n pipeline and its stages (for profiling)")
     ap.add_argument("--stage-reps", type=int, default=10)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (a known-size "
@@ -51,26 +68,31 @@ def parse():
 
 
 def stage_work(kind: str, join: bool, n_vec: int, k: int, n: int):
-    """Algorithmic (limb products, bytes) of one pipeline stage.
+    """Algorithmic (field products, reductions, bytes) of one pipeline stage.
 
-    Strided batch of k passes on n_vec vectors: n_vec k n/2 butterflies, each one
-    twiddle product; reads and writes each element once.  Fused lowest batch: the last
-    k passes of the inverse and the first k of the forward transform (the pass on bit 0
-    of each needs no product) plus the coset multiply, and one read of the coset table
-    per vector.  Join: A'B' (one product), h_std (one reduction), reads A' and B',
-    writes h_mont and h_std instead of the vector.
+    Strided batch of k passes on n_vec vectors: n_vec k n/2 butterflies, one product
+    each; one read and one write per element.  Fused lowest batch: the last k passes of
+    the inverse and the first k of the forward transform (2k n/2 butterflies), the 1/n
+    scaling and the coset shift (two products per element, performed here as one table
+    product), and one read of the shift table per element.  Join: A'B' (one product),
+    h_std (one reduction), reads A' and B', writes h_mont and h_std instead of one vector.
     """
     if kind == "fused":
-        muls = n_vec * ((2 * k - 2) * n // 2 + n)
+        muls = n_vec * (2 * k * n // 2 + 2 * n)
         byts = n_vec * 3 * n * FR_BYTES
     else:
         muls = n_vec * k * n // 2
         byts = n_vec * 2 * n * FR_BYTES
-    mads = muls * MADS_PER_MUL
+    redc = 0
     if join:
-        mads += n * (MADS_PER_MUL + MADS_PER_REDC)
+        muls += n
+        redc = n
         byts += 3 * n * FR_BYTES        # + A', B' reads, + the second output
-    return mads, byts
+    return muls, redc, byts
+
+
+def mads(muls: int, redc: int) -> int:
+    return muls * MADS_PER_MUL + redc * MADS_PER_REDC
 
 
 def stage_list(plan, n_vec=3):
@@ -89,6 +111,24 @@ def stage_list(plan, n_vec=3):
         else:
             out.append(("fwd", False, n_vec, plan[b]))
     return out
+
+
+def pipeline_work(log_n: int):
+    """(products, reductions, algorithmic bytes) of one H pipeline at 2^log_n."""
+    n = 1 << log_n
+    muls = 6 * (n // 2) * log_n + 7 * n
+    return muls, n, ALG_BYTES_PER_ELEMENT * n
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def _code_only(text: str) -> str:
@@ -110,7 +150,7 @@ def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "groth16_polynomial_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        if f in MSM_SOURCES:
+        if f in MSM_SOURCES or not os.path.isfile(os.path.join(csrc, f)):
             continue
         with open(os.path.join(csrc, f), encoding="utf-8") as fh:
             h.update(f.encode() + _code_only(fh.read()).encode())
@@ -130,6 +170,63 @@ def traffic_from_profiles(stage_name: str, src_hash: str):
     return d.get("stages", {}).get(stage_name, {}).get("hbm_bytes_per_dispatch")
 
 
+class Timer:
+    """HIP events on torch's current stream, which is the stream the library launches on."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.stream = torch.cuda.current_stream()
+        self.e0 = torch.cuda.Event(enable_timing=True)
+        self.e1 = torch.cuda.Event(enable_timing=True)
+
+    def mean_ms(self, fn, reps, warm=3):
+        for _ in range(warm):
+            fn()
+        self.torch.cuda.synchronize()
+        self.e0.record(self.stream)
+        for _ in range(reps):
+            fn()
+        self.e1.record(self.stream)
+        self.torch.cuda.synchronize()
+        return self.e0.elapsed_time(self.e1) / reps
+
+    def median_ms(self, fn, reps, warm=3):
+        """Median over reps calls, each between its own pair of events."""
+        torch = self.torch
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for a, b in evs:
+            a.record(self.stream)
+            fn()
+            b.record(self.stream)
+        torch.cuda.synchronize()
+        return statistics.median(a.elapsed_time(b) for a, b in evs)
+
+
+def gbfly(log_n, transforms, ms):
+    return transforms * ((1 << log_n) // 2) * log_n / (ms / 1e3) / 1e9
+
+
+def probe_rates(log):
+    """The issue rate of the arithmetic's instructions: v_mad_i64_i32 (the transforms'
+    digit products), v_mad_u64_u32, v_add_u32 and v_mul_lo_u32; 2048 workgroups of 256
+    lanes (eight per CU), 4096 rounds of eight chains each."""
+    from groth16_polynomial_amd import probe
+    out = {}
+    for op in (1, 0, 2, 3):
+        r = probe.run(op, blocks=2048, iters=4096 if op != 3 else 1024)
+        if not r["results_match"]:
+            raise RuntimeError("probe %s: lane results differ from the host's" % r["op"])
+        out[r["op"]] = {"t_lane_ops_s": round(r["lane_ops_per_s_t"], 3),
+                        "clock_ghz_est": round(r["clock_ghz_est"], 3),
+                        "kernel_ms": round(r["kernel_ms"], 4)}
+    log("probe: %s" % out)
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -144,13 +241,16 @@ def main():
     from groth16_polynomial_amd import binding as g
     from groth16_polynomial_amd import synth
 
+    def log(msg):
+        print("[bench] " + msg, file=sys.stderr, flush=True)
+
     if not torch.cuda.is_available():
         print("bench.py needs a HIP device", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
     log_n = args.log_n
     n = 1 << log_n
-    print("[bench] preparing 2^%d inputs" % log_n, file=sys.stderr, flush=True)
+    log("preparing 2^%d inputs" % log_n)
 
     a, b = synth.h_inputs(3, log_n)
     ad, bd = g.to_mont(g.to_device(a)), g.to_mont(g.to_device(b))
@@ -158,111 +258,142 @@ def main():
     ctx = g.HContext(log_n)
     hm, hs = g.empty_fr(n), g.empty_fr(n)
     stream = torch.cuda.current_stream()
+    tm = Timer(torch)
     torch.cuda.synchronize()
+    line_extra = {}
 
     # The side measurements run first: they also bring the chip to its steady clock,
     # which the first ~20 ms of sustained load does not run at.
-    # ---- standalone forward NTT at the same size
-    x = g.to_mont(g.to_device(synth.ntt_input(2, log_n)))
-    y = g.empty_fr(n)
-    for _ in range(3):
-        ctx.ntt_forward(x, y)
-    torch.cuda.synchronize()
-    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    f0.record(stream)
-    for _ in range(args.steps):
-        ctx.ntt_forward(x, y)
-    f1.record(stream)
-    torch.cuda.synchronize()
-    ntt_ms = f0.elapsed_time(f1) / args.steps
-    ntt_gbfly = (n // 2) * log_n / (ntt_ms / 1e3) / 1e9
+    if not args.no_side:
+        rates = probe_rates(log)
+        line_extra["instruction_rates"] = rates
 
-    # ---- the CSR gather front end on the 2^18 proving-key shape (its own workload: the
-    # GATHER_CU page's largest key, synthetic rows with its statistics)
-    ma, mb, wit = synth.gather_inputs(4)
+        # ---- standalone transforms: 2^18 (its own workload) and 2^log_n, both directions
+        ntt = {}
+        for lg in sorted({18, log_n}):
+            nctx = ctx if lg == log_n else g.HContext(lg)
+            x = g.to_mont(g.to_device(synth.ntt_input(2, lg)))
+            y = g.empty_fr(1 << lg)
+            fwd = tm.mean_ms(lambda: nctx.ntt_forward(x, y), args.steps)
+            inv = tm.mean_ms(lambda: nctx.ntt_inverse(x, y), args.steps)
+            ntt["2^%d" % lg] = {"forward_ms": round(fwd, 5),
+                                "forward_gbutterfly_s": round(gbfly(lg, 1, fwd), 3),
+                                "inverse_ms": round(inv, 5),
+                                "inverse_gbutterfly_s": round(gbfly(lg, 1, inv), 3),
+                                "pass_batches": g.batch_plan(lg)}
+            if nctx is not ctx:
+                nctx.release()
+            del x, y
+        line_extra["ntt"] = ntt
+        log("ntt: %s" % ntt)
 
-    def idx(a):
-        return torch.from_numpy(np.ascontiguousarray(a, np.uint32).view(np.int32)).cuda()
+        # ---- the CSR gather front end on the 2^18 proving-key shape (the GATHER_CU
+        # page's largest key, synthetic rows with its statistics), alone and followed by
+        # the 2^18 H pipeline
+        ma, mb, wit = synth.gather_inputs(4)
 
-    ga = (idx(ma.row_ptr), idx(ma.signal), g.to_mont(g.to_device(ma.value)))
-    gb = (idx(mb.row_ptr), idx(mb.signal), g.to_mont(g.to_device(mb.value)))
-    gw = g.to_mont(g.to_device(wit))
-    grows = len(ma.row_ptr) - 1
-    gouts = [g.empty_fr(grows) for _ in range(3)]
-    for _ in range(3):
-        g.gather_abc(*ga, *gb, gw, *gouts)
-    torch.cuda.synchronize()
-    f0.record(stream)
-    for _ in range(args.steps):
-        g.gather_abc(*ga, *gb, gw, *gouts)
-    f1.record(stream)
-    torch.cuda.synchronize()
-    gather_ms = f0.elapsed_time(f1) / args.steps
-    nnz = ma.nnz + mb.nnz
-    # algorithmic bytes: row pointers, column indices and coefficients of both matrices,
-    # one 32-byte witness read per non-zero, three 32-byte outputs per row
-    gather_bytes = 2 * 4 * (grows + 1) + nnz * (4 + 32 + 32) + 3 * 32 * grows
+        def idx(v):
+            return torch.from_numpy(np.ascontiguousarray(v, np.uint32).view(np.int32)).cuda()
 
-    # ---- several proofs per call at small domains, against one call per proof
-    def time_ms(fn, reps):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        f0.record(stream)
-        for _ in range(reps):
-            fn()
-        f1.record(stream)
-        torch.cuda.synchronize()
-        return f0.elapsed_time(f1) / reps
+        ga = (idx(ma.row_ptr), idx(ma.signal), g.to_mont(g.to_device(ma.value)))
+        gb = (idx(mb.row_ptr), idx(mb.signal), g.to_mont(g.to_device(mb.value)))
+        gw = g.to_mont(g.to_device(wit))
+        grows = len(ma.row_ptr) - 1
+        gouts = [g.empty_fr(grows) for _ in range(3)]
+        gctx = g.HContext(18)
+        ghm, ghs = g.empty_fr(grows), g.empty_fr(grows)
+        gather_ms = tm.mean_ms(lambda: g.gather_abc(*ga, *gb, gw, *gouts), args.steps)
 
-    proof_batches = {}
-    for blog, proofs in BATCH_SHAPES:
-        bn = 1 << blog
-        bctx = g.HContext(blog)
-        pa = torch.cat([g.to_mont(g.to_device(synth.h_inputs(2000 + q, blog)[0]))
-                        for q in range(proofs)])
-        pb = torch.cat([g.to_mont(g.to_device(synth.h_inputs(2000 + q, blog)[1]))
-                        for q in range(proofs)])
-        pc = g.fr_mul(pa, pb)
-        phm, phs = torch.empty_like(pa), torch.empty_like(pa)
-        pscr = g.empty_fr(proofs * bn)
-        batched = time_ms(lambda: bctx.h_compute_batch(pa, pb, pc, phm, phs, pscr),
-                          args.steps)
+        def gather_h():
+            g.gather_abc(*ga, *gb, gw, *gouts)
+            gctx.h_compute(*gouts, ghm, ghs)
 
-        def one_by_one():
-            for q in range(proofs):
-                sl = slice(q * bn, (q + 1) * bn)
-                bctx.h_compute(pa[sl], pb[sl], pc[sl], phm[sl], phs[sl])
-
-        single = time_ms(one_by_one, max(1, args.steps // 4))
-        bfly = proofs * 6 * (bn // 2) * blog
-        proof_batches["2^%d_x%d" % (blog, proofs)] = {
-            "batch_ms": round(batched, 5),
-            "batch_gbutterfly_s": round(bfly / (batched / 1e3) / 1e9, 3),
-            "one_call_per_proof_ms": round(single, 5),
-            "one_call_per_proof_gbutterfly_s": round(bfly / (single / 1e3) / 1e9, 3),
+        gather_h_ms = tm.mean_ms(gather_h, args.steps)
+        h18_ms = tm.mean_ms(lambda: gctx.h_compute(*gouts, ghm, ghs), args.steps)
+        gctx.release()
+        nnz = ma.nnz + mb.nnz
+        # algorithmic bytes: row pointers, column indices and coefficients of both matrices,
+        # one 32-byte witness read per non-zero, three 32-byte outputs per row
+        gather_bytes = 2 * 4 * (grows + 1) + nnz * (4 + 32 + 32) + 3 * 32 * grows
+        line_extra["gather_2_18"] = {
+            "gather_ms": round(gather_ms, 5),
+            "gather_gnnz_s": round(nnz / (gather_ms / 1e3) / 1e9, 3),
+            "gather_hbm_gbs_algorithmic": round(gather_bytes / (gather_ms / 1e3) / 1e9, 2),
+            "gather_plus_h_ms": round(gather_h_ms, 5),
+            "h_only_ms": round(h18_ms, 5),
+            "nnz": nnz, "rows": grows,
         }
-        bctx.release()
-        del pa, pb, pc, phm, phs, pscr
-    print("[bench] proof batches: %s" % proof_batches, file=sys.stderr, flush=True)
+        del ga, gb, gw, gouts, ghm, ghs
+        log("gather: %s" % line_extra["gather_2_18"])
 
-    # ---- the other single-proof workloads of the H pipeline (2^12 and 2^22), same call
-    other_sizes = {}
-    for olog in OTHER_SIZES:
-        on = 1 << olog
-        octx = g.HContext(olog)
-        oa, ob = (g.to_mont(g.to_device(v)) for v in synth.h_inputs(3, olog))
-        oc = g.fr_mul(oa, ob)
-        ohm, ohs = g.empty_fr(on), g.empty_fr(on)
-        oms = time_ms(lambda: octx.h_compute(oa, ob, oc, ohm, ohs), args.steps)
-        other_sizes["2^%d" % olog] = {
-            "h_pipeline_ms": round(oms, 5),
-            "gbutterfly_s": round(6 * (on // 2) * olog / (oms / 1e3) / 1e9, 3),
-            "pass_batches": g.batch_plan(olog),
-        }
-        octx.release()
-        del oa, ob, oc, ohm, ohs
-    print("[bench] other sizes: %s" % other_sizes, file=sys.stderr, flush=True)
+        # ---- several proofs per call at small domains, against one call per proof
+        proof_batches = {}
+        for blog, proofs in BATCH_SHAPES:
+            bn = 1 << blog
+            bctx = g.HContext(blog)
+            pa = torch.cat([g.to_mont(g.to_device(synth.h_inputs(2000 + q, blog)[0]))
+                            for q in range(proofs)])
+            pb = torch.cat([g.to_mont(g.to_device(synth.h_inputs(2000 + q, blog)[1]))
+                            for q in range(proofs)])
+            pc = g.fr_mul(pa, pb)
+            phm, phs = torch.empty_like(pa), torch.empty_like(pa)
+            pscr = g.empty_fr(proofs * bn)
+            batched = tm.mean_ms(lambda: bctx.h_compute_batch(pa, pb, pc, phm, phs, pscr),
+                                 args.steps)
+
+            def one_by_one():
+                for q in range(proofs):
+                    sl = slice(q * bn, (q + 1) * bn)
+                    bctx.h_compute(pa[sl], pb[sl], pc[sl], phm[sl], phs[sl])
+
+            single = tm.mean_ms(one_by_one, max(1, args.steps // 4))
+            proof_batches["2^%d_x%d" % (blog, proofs)] = {
+                "batch_ms": round(batched, 5),
+                "batch_gbutterfly_s": round(proofs * gbfly(blog, 6, batched), 3),
+                "one_call_per_proof_ms": round(single, 5),
+                "one_call_per_proof_gbutterfly_s": round(proofs * gbfly(blog, 6, single), 3),
+            }
+            bctx.release()
+            del pa, pb, pc, phm, phs, pscr
+        line_extra["proof_batches"] = proof_batches
+        log("proof batches: %s" % proof_batches)
+
+        # ---- the other single-proof workloads of the H pipeline: 2^12 (latency: median
+        # of 50 calls, each between its own events, the launch count, and the host's
+        # enqueue time per call) and 2^22
+        other_sizes = {}
+        for olog in (12, 22):
+            on = 1 << olog
+            octx = g.HContext(olog)
+            oa, ob = (g.to_mont(g.to_device(v)) for v in synth.h_inputs(3, olog))
+            oc = g.fr_mul(oa, ob)
+            ohm, ohs = g.empty_fr(on), g.empty_fr(on)
+
+            def call():
+                octx.h_compute(oa, ob, oc, ohm, ohs)
+
+            entry = {"pass_batches": g.batch_plan(olog), "launches": octx.stage_count()}
+            if olog == 12:
+                med = tm.median_ms(call, 50)
+                entry["h_pipeline_median_us"] = round(med * 1e3, 2)
+                entry["h_pipeline_mean_ms"] = round(tm.mean_ms(call, args.steps), 5)
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(200):
+                    call()
+                host_us = (time.perf_counter() - t0) / 200 * 1e6
+                torch.cuda.synchronize()
+                entry["host_enqueue_us_per_call"] = round(host_us, 2)
+                ms = med
+            else:
+                ms = tm.mean_ms(call, max(2, args.steps // 2))
+                entry["h_pipeline_ms"] = round(ms, 5)
+            entry["gbutterfly_s"] = round(gbfly(olog, 6, ms), 3)
+            other_sizes["2^%d" % olog] = entry
+            octx.release()
+            del oa, ob, oc, ohm, ohs
+        line_extra["other_sizes"] = other_sizes
+        log("other sizes: %s" % other_sizes)
 
     # ---- the timed region: K whole pipelines
     for _ in range(args.warmup):
@@ -277,18 +408,14 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = e0.elapsed_time(e1) / args.steps
-    print("[bench] h_compute 2^%d: %.4f ms/step (wall %.3f s)" % (log_n, ms_per_step, wall),
-          file=sys.stderr, flush=True)
+    log("h_compute 2^%d: %.4f ms/step (wall %.3f s)" % (log_n, ms_per_step, wall))
 
     plan = g.batch_plan(log_n)
     butterflies = 6 * (n // 2) * log_n
-    total_muls = 0
-    total_bytes = 0
+    p_muls, p_redc, p_bytes = pipeline_work(log_n)
+    p_mads = mads(p_muls, p_redc)
     stages = stage_list(plan)
-    for kind, join, nv, k in stages:
-        m, by = stage_work(kind, join, nv, k, n)
-        total_muls += m
-        total_bytes += by
+    assert sum(stage_work(*st, n)[0] for st in stages) == p_muls
 
     # ---- each stage alone, HIP events on the launch stream
     count = ctx.stage_count()
@@ -306,68 +433,70 @@ def main():
             acc[i] += evs[i][0].elapsed_time(evs[i][1])
     stage_ms = [x / args.stage_reps for x in acc]
 
-    # ---- the H MSM: sum_i h_i P_i over G1 on the pipeline's own h_std, with synthetic
-    # bases (multiples s_i G of the generator stand in for the proving key's points)
-    bases = g.g1_generator_mul(g.to_device(synth.uniform_fr(7, n)))
-    mctx = g.MsmG1(n)
-    for _ in range(2):
-        mctx.window_sums(hs, bases)
-    torch.cuda.synchronize()
-    f0.record(stream)
-    msm_reps = max(1, args.steps // 4)
-    for _ in range(msm_reps):
-        mctx.window_sums(hs, bases)
-    f1.record(stream)
-    torch.cuda.synchronize()
-    msm_ms = f0.elapsed_time(f1) / msm_reps
-    sums_host = g.to_host(mctx.sums).reshape(mctx.windows, 32)
-    t_fin = time.perf_counter()
-    for _ in range(10):
-        mctx.finish(sums_host)
-    finish_ms = (time.perf_counter() - t_fin) / 10 * 1e3
-    msm_line = {
-        "workload": "G1 MSM of h_std at n=2^%d, bases s_i G (synthetic)" % log_n,
-        "window_bits": mctx.c,
-        "windows": mctx.windows,
-        "device_ms": round(msm_ms, 4),
-        "host_finish_ms": round(finish_ms, 4),
-        "bucket_adds_per_s_g": round(n * mctx.windows / (msm_ms / 1e3) / 1e9, 3),
-    }
-    del bases, mctx
-    # the same MSM at other sizes (default widths), uniform scalars k_i over bases k_i G
-    if log_n == 20:
-        sizes = {}
-        for lg in (12, 16, 22):
-            m = 1 << lg
-            ks = g.to_device(synth.uniform_fr(8, m))
-            mb = g.g1_generator_mul(ks)
-            mc = g.MsmG1(m)
-            for _ in range(2):
-                mc.window_sums(ks, mb)
-            torch.cuda.synchronize()
-            f0.record(stream)
-            for _ in range(5):
-                mc.window_sums(ks, mb)
-            f1.record(stream)
-            torch.cuda.synchronize()
-            t_ms = f0.elapsed_time(f1) / 5
-            sizes["2^%d" % lg] = {"window_bits": mc.c, "device_ms": round(t_ms, 4),
-                                  "bucket_adds_per_s_g":
-                                      round(m * mc.windows / (t_ms / 1e3) / 1e9, 3)}
-            del ks, mb, mc
-        torch.cuda.empty_cache()
-        msm_line["other_sizes"] = sizes
-    print("[bench] msm: %s" % msm_line, file=sys.stderr, flush=True)
+    def stage_name(st):
+        kind, join, nv, k = st
+        return "%s_k%d_v%d%s" % (kind, k, nv, "_join" if join else "")
+
+    stage_report = []
+    for st, ms in zip(stages, stage_ms):
+        m, r, by = stage_work(*st, n)
+        t = mads(m, r) / (ms / 1e3) / 1e12
+        stage_report.append({"kernel": stage_name(st), "ms": round(ms, 5),
+                             "t_limb_products_s": round(t, 3),
+                             "alu_frac": round(t / NOMINAL_PEAK_T, 4)})
+
+    msm_line = None
+    if not args.no_side:
+        # ---- the H MSM: sum_i h_i P_i over G1 on the pipeline's own h_std, with synthetic
+        # bases (multiples s_i G of the generator stand in for the proving key's points)
+        bases = g.g1_generator_mul(g.to_device(synth.uniform_fr(7, n)))
+        mctx = g.MsmG1(n)
+        msm_reps = max(1, args.steps // 4)
+        msm_ms = tm.mean_ms(lambda: mctx.window_sums(hs, bases), msm_reps, warm=2)
+        sums_host = g.to_host(mctx.sums).reshape(mctx.windows, 32)
+        t_fin = time.perf_counter()
+        for _ in range(10):
+            mctx.finish(sums_host)
+        finish_ms = (time.perf_counter() - t_fin) / 10 * 1e3
+        msm_line = {
+            "workload": "G1 MSM of h_std at n=2^%d, bases s_i G (synthetic)" % log_n,
+            "window_bits": mctx.c,
+            "windows": mctx.windows,
+            "device_ms": round(msm_ms, 4),
+            "host_finish_ms": round(finish_ms, 4),
+            "bucket_adds_per_s_g": round(n * mctx.windows / (msm_ms / 1e3) / 1e9, 3),
+        }
+        del bases, mctx
+        # the same MSM at other sizes (default widths), uniform scalars k_i over bases k_i G
+        if log_n == 20:
+            sizes = {}
+            for lg in (12, 16, 22):
+                m = 1 << lg
+                ks = g.to_device(synth.uniform_fr(8, m))
+                mb = g.g1_generator_mul(ks)
+                mc = g.MsmG1(m)
+                t_ms = tm.mean_ms(lambda: mc.window_sums(ks, mb), 5, warm=2)
+                sizes["2^%d" % lg] = {"window_bits": mc.c, "device_ms": round(t_ms, 4),
+                                      "bucket_adds_per_s_g":
+                                          round(m * mc.windows / (t_ms / 1e3) / 1e9, 3)}
+                del ks, mb, mc
+            torch.cuda.empty_cache()
+            msm_line["other_sizes"] = sizes
+        log("msm: %s" % msm_line)
+
     dom = int(np.argmax(stage_ms))
-    kind, join, nv, k = stages[dom]
-    dom_mads, dom_bytes = stage_work(kind, join, nv, k, n)
-    dom_s = stage_ms[dom] / 1e3
-    dom_name = "%s_k%d_v%d%s" % (kind, k, nv, "_join" if join else "")
-    achieved_t = dom_mads / dom_s / 1e12
+    d_muls, d_redc, d_bytes = stage_work(*stages[dom], n)
+    dom_mads = mads(d_muls, d_redc)
+    dom_name = stage_name(stages[dom])
+    achieved_t = dom_mads / (stage_ms[dom] / 1e3) / 1e12
     src_hash = kernel_source_hash()
     traffic = traffic_from_profiles(dom_name, src_hash)
+    measured_peak = None
+    if "instruction_rates" in line_extra:
+        measured_peak = line_extra["instruction_rates"]["v_mad_i64_i32"]["t_lane_ops_s"]
 
     value = butterflies / (ms_per_step / 1e3) / 1e9
+    pipe_t = p_mads / (ms_per_step / 1e3) / 1e12
     line = {
         "metric": "Groth16 H-pipeline ms & Fr NTT Gbutterfly/s at n=2^20; achieved HBM GB/s",
         "value": round(value, 3),
@@ -389,33 +518,33 @@ def main():
             "stages": count,
         },
         "h_pipeline_ms": round(ms_per_step, 5),
-        "ntt_forward_ms": round(ntt_ms, 5),
-        "ntt_gbutterfly_s": round(ntt_gbfly, 3),
-        "gather_2_18_ms": round(gather_ms, 5),
-        "gather_gnnz_s": round(nnz / (gather_ms / 1e3) / 1e9, 3),
-        "gather_hbm_gbs_algorithmic": round(gather_bytes / (gather_ms / 1e3) / 1e9, 2),
-        "proof_batches": proof_batches,
-        "other_sizes": other_sizes,
-        "msm_g1": msm_line,
-        "hbm_gbs_algorithmic": round(total_bytes / (ms_per_step / 1e3) / 1e9, 2),
-        "pipeline_tmad_s": round(total_muls / (ms_per_step / 1e3) / 1e12, 3),
-        "pipeline_alu_frac": round(total_muls / (ms_per_step / 1e3) / 1e12 / MAD_PEAK_T, 4),
-        "stage_ms": [round(v, 5) for v in stage_ms],
+        "hbm_gbs_algorithmic": round(p_bytes / (ms_per_step / 1e3) / 1e9, 2),
+        "hbm_frac_algorithmic": round(p_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "pipeline_limb_products": p_mads,
+        "pipeline_t_limb_products_s": round(pipe_t, 3),
+        "pipeline_alu_frac": round(pipe_t / NOMINAL_PEAK_T, 4),
+        "pipeline_alu_frac_of_measured_rate": (round(pipe_t / measured_peak, 4)
+                                               if measured_peak else None),
+        "stages": stage_report,
         "roofline": {
             "bound": "alu",
             "kernel": dom_name,
             "achieved": round(achieved_t, 3),
-            "peak": round(MAD_PEAK_T, 3),
-            "unit": "Tmad/s",
-            "frac": round(achieved_t / MAD_PEAK_T, 4),
+            "peak": round(NOMINAL_PEAK_T, 3),
+            "unit": "T limb-products/s",
+            "frac": round(achieved_t / NOMINAL_PEAK_T, 4),
             "traffic": traffic,
-            "algorithmic_bytes": dom_bytes,
+            "peak_measured": measured_peak,
+            "algorithmic_bytes": d_bytes,
             "algorithmic_mads": dom_mads,
             "avg_launch_ms": round(stage_ms[dom], 5),
             "kernel_source_sha256_16": src_hash,
         },
         "cpu_baseline": None,
     }
+    line.update(line_extra)
+    if msm_line:
+        line["msm_g1"] = msm_line
 
     if args.copy_calibration_mib:
         nbytes = args.copy_calibration_mib << 20
@@ -430,20 +559,32 @@ def main():
 
     if not args.no_cpu_baseline:
         import oracle
-        print("[bench] oracle (CPU, 1 thread) on the same 2^%d pipeline" % log_n,
-              file=sys.stderr, flush=True)
         am, bm = oracle.to_mont(a), oracle.to_mont(b)
         cm = oracle.pointwise_mul_mont(am, bm)
-        c0 = time.perf_counter()
-        oracle.h_pipeline(log_n, am, bm, cm)
-        cpu_s = time.perf_counter() - c0
+        nproc = os.cpu_count() or 1
+        all_threads = oracle.default_threads()
+        runs = {}
+        for threads in (1, all_threads):
+            oracle.set_threads(threads)
+            times = []
+            for _ in range(3):
+                c0 = time.perf_counter()
+                oracle.h_pipeline(log_n, am, bm, cm)
+                times.append(time.perf_counter() - c0)
+            runs[threads] = statistics.median(times)
+            log("oracle (CPU, %d threads): median %.2f s of %s" % (threads, runs[threads],
+                                                                   times))
         line["cpu_baseline"] = {
-            "value": round(butterflies / cpu_s / 1e9, 6),
+            "value": round(butterflies / runs[all_threads] / 1e9, 6),
             "unit": "Gbutterfly/s",
-            "cores": 1,
+            "cores": all_threads,
             "kind": "oracle",
-            "sample": "the whole 2^%d H pipeline once (%.1f s), single-threaded C oracle"
-                      % (log_n, cpu_s),
+            "sample": "the whole 2^%d H pipeline, median of 3 runs: %.2f s on %d threads, "
+                      "%.2f s on one" % (log_n, runs[all_threads], all_threads, runs[1]),
+            "one_core": {"value": round(butterflies / runs[1] / 1e9, 6), "seconds": round(runs[1], 3)},
+            "all_cores_seconds": round(runs[all_threads], 3),
+            "nproc": nproc,
+            "cpu_model": cpu_model(),
         }
     ctx.release()
     print(json.dumps(line), flush=True)

@@ -1,4 +1,5 @@
-"""Builds libg16.so (the HIP library) for gfx950 with hipcc, in-tree."""
+"""Builds libg16.so (the HIP library) and libg16_probe.so (the instruction-rate probe the
+benchmark uses for its roofline) for gfx950 with hipcc, in-tree."""
 from __future__ import annotations
 
 import os
@@ -8,6 +9,7 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libg16.so")
+PROBE_LIB = os.path.join(PKG, "libg16_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -42,23 +44,26 @@ def _run(cmd, verbose):
 
 def build(verbose: bool = False, jobs: int | None = None) -> str:
     """Compile every translation unit (always recompiles) in parallel, link, and return
-    the library path."""
+    the library path.  The probe library is built alongside."""
     csrc = os.path.join(PKG, "csrc")
     units = sorted(f for f in os.listdir(csrc) if f.endswith(".hip"))
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include")]
     compile_flags = [f for f in FLAGS if f != "-shared"]
-    jobs = jobs or min(len(units), int(os.environ.get("MAX_JOBS", "8")), os.cpu_count() or 1)
+    jobs = jobs or min(len(units) + 1, int(os.environ.get("MAX_JOBS", "8")), os.cpu_count() or 1)
     objs = []
     cmds = []
     for u in units:
         obj = os.path.join(objdir, u.replace(".hip", ".o"))
         objs.append(obj)
         cmds.append([HIPCC, *compile_flags, *inc, "-c", "-o", obj, os.path.join(csrc, u)])
+    probe_tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    cmds.append([HIPCC, *FLAGS, "-o", probe_tmp, os.path.join(csrc, "probe", "mad_rate.hip")])
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:
             f.result()
+    os.replace(probe_tmp, PROBE_LIB)
     tmp = LIB + ".tmp%d" % os.getpid()
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)

@@ -10,8 +10,11 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
+#include <unordered_set>
 
+#include "host_util.hpp"
 #include "kernels.hpp"
 #include "pointwise_kernels.hpp"
 #include "r8_launch.hpp"
@@ -42,6 +45,7 @@ struct g16_ctx {
     size_t ws_bytes;
     Fr omega, omega_inv, shift, size_inv;  // Montgomery form
     g16::Tw29 size_inv_entry;              // n^-1 as a table entry (inverse transform)
+    bool radix2;  // G16_RADIX2 set at prepare time: every batch on the radix-2 kernel
     uint32_t n_batches;
     uint32_t batch_k[kMaxBatches];  // lowest bits first
 };
@@ -68,25 +72,24 @@ uint32_t plan_batches(uint32_t log_n, uint32_t kmax, uint32_t* ks) {
     return nb;
 }
 
-bool ctx_ok(const g16_ctx* c) { return c && c->magic == kMagic; }
+// Contexts handed out and not yet released.  Every entry point looks its context up
+// here before touching it, so a released (freed) or foreign pointer is refused without
+// being read.
+std::mutex g_live_mu;
+std::unordered_set<const g16_ctx*> g_live;
+
+bool ctx_ok(const g16_ctx* c) {
+    if (!c) return false;
+    std::lock_guard<std::mutex> lock(g_live_mu);
+    return g_live.count(c) != 0;
+}
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
     return x < y + nb && y < x + na;
 }
 
-// True when p is memory the current device can address (device or managed memory).
-bool device_pointer(const void* p) {
-    if (!p) return false;
-    hipPointerAttribute_t attr;
-    hipError_t e = hipPointerGetAttributes(&attr, p);
-    if (e != hipSuccess) {
-        (void)hipGetLastError();
-        return false;
-    }
-    return attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged ||
-           attr.type == hipMemoryTypeUnified;
-}
+using g16::device_range;
 
 int launch_status() {
     hipError_t e = hipGetLastError();
@@ -119,7 +122,6 @@ void domain_roots(uint32_t log_n, Fr* omega, Fr* shift, Fr* size_inv) {
 template <g16::Mode M, bool J>
 bool try_r8(const g16::BatchParams& p, uint32_t n_vec, hipStream_t stream, int* rc) {
     const uint32_t k = p.k, L = p.log_n;
-    if (std::getenv("G16_RADIX2")) return false;
     auto fits = [&](uint32_t spw) { return (1ull << (L - k)) >= spw; };
     hipError_t e;
     switch (k) {
@@ -141,9 +143,9 @@ bool try_r8(const g16::BatchParams& p, uint32_t n_vec, hipStream_t stream, int* 
 }
 
 template <g16::Mode M, bool J>
-int launch_batch(const g16::BatchParams& p, uint32_t n_vec, hipStream_t stream) {
+int launch_batch(const g16::BatchParams& p, uint32_t n_vec, bool radix2, hipStream_t stream) {
     int rc = G16_OK;
-    if (try_r8<M, J>(p, n_vec, stream, &rc)) return rc;
+    if (!radix2 && try_r8<M, J>(p, n_vec, stream, &rc)) return rc;
     // radix-2 batch kernel: small batches and small domains
     const uint32_t k = p.k, L = p.log_n;
     g16::BatchParams q = p;
@@ -152,6 +154,9 @@ int launch_batch(const g16::BatchParams& p, uint32_t n_vec, hipStream_t stream) 
     q.log_spw = log_spw;
     uint64_t groups = (1ull << (L - k)) >> log_spw;
     size_t lds = (size_t(1) << (k + log_spw)) * sizeof(Fr);
+    // batches of 12 passes (G16_MAX_K = 12) need 128 KiB
+    if (g16::allow_lds((const void*)g16::ntt_batch_kernel<M, J>, lds) != hipSuccess)
+        return G16_EHIP;
     dim3 grid((uint32_t)groups, n_vec, 1);
     hipLaunchKernelGGL((g16::ntt_batch_kernel<M, J>), grid, dim3(kThreads), lds, stream, q);
     return launch_status();
@@ -182,7 +187,7 @@ int run_ntt(g16_ctx* c, const void* in, void* out, void* stream, bool inverse) {
     if (overlaps(in, nbytes, c->ws_begin, c->ws_bytes) ||
         overlaps(out, nbytes, c->ws_begin, c->ws_bytes))
         return G16_EALIAS;
-    if (!device_pointer(in) || !device_pointer(out)) return G16_EINVAL;
+    if (!device_range(in, nbytes) || !device_range(out, nbytes)) return G16_EINVAL;
     hipStream_t s = (hipStream_t)stream;
     Fr* scr = c->scratch;
     g16::BatchParams p = base_params(c);
@@ -195,7 +200,7 @@ int run_ntt(g16_ctx* c, const void* in, void* out, void* stream, bool inverse) {
     p.src[0] = (const Fr*)in;
     const bool single = c->n_batches == 1;
     p.dst[0] = (single && in != out) ? (Fr*)out : scr;
-    int rc = launch_batch<g16::Mode::HeadBitrev, false>(p, 1, s);
+    int rc = launch_batch<g16::Mode::HeadBitrev, false>(p, 1, c->radix2, s);
     if (rc) return rc;
     if (single) {
         if (in == out) {
@@ -211,7 +216,7 @@ int run_ntt(g16_ctx* c, const void* in, void* out, void* stream, bool inverse) {
         t.k = c->batch_k[b];
         t.src[0] = scr;
         t.dst[0] = (b + 1 == c->n_batches) ? (Fr*)out : scr;
-        rc = launch_batch<g16::Mode::FwdStrided, false>(t, 1, s);
+        rc = launch_batch<g16::Mode::FwdStrided, false>(t, 1, c->radix2, s);
         if (rc) return rc;
     }
     return G16_OK;
@@ -221,6 +226,7 @@ int run_ntt(g16_ctx* c, const void* in, void* out, void* stream, bool inverse) {
 struct Launch {
     g16::Mode mode;
     bool join;
+    bool radix2;
     g16::BatchParams p;
     uint32_t n_vec;
 };
@@ -229,17 +235,18 @@ constexpr uint32_t kMaxLaunches = 2 * kMaxBatches + 2;
 
 int exec_launch(const Launch& l, hipStream_t s) {
     using g16::Mode;
+    const bool r2 = l.radix2;
     switch (l.mode) {
         case Mode::Fused:
-            return l.join ? launch_batch<Mode::Fused, true>(l.p, l.n_vec, s)
-                          : launch_batch<Mode::Fused, false>(l.p, l.n_vec, s);
+            return l.join ? launch_batch<Mode::Fused, true>(l.p, l.n_vec, r2, s)
+                          : launch_batch<Mode::Fused, false>(l.p, l.n_vec, r2, s);
         case Mode::FwdStrided:
-            return l.join ? launch_batch<Mode::FwdStrided, true>(l.p, l.n_vec, s)
-                          : launch_batch<Mode::FwdStrided, false>(l.p, l.n_vec, s);
+            return l.join ? launch_batch<Mode::FwdStrided, true>(l.p, l.n_vec, r2, s)
+                          : launch_batch<Mode::FwdStrided, false>(l.p, l.n_vec, r2, s);
         case Mode::InvStrided:
-            return launch_batch<Mode::InvStrided, false>(l.p, l.n_vec, s);
+            return launch_batch<Mode::InvStrided, false>(l.p, l.n_vec, r2, s);
         default:
-            return launch_batch<Mode::HeadBitrev, false>(l.p, l.n_vec, s);
+            return launch_batch<Mode::HeadBitrev, false>(l.p, l.n_vec, r2, s);
     }
 }
 
@@ -259,6 +266,7 @@ uint32_t plan_coset(const g16_ctx* c, const Fr* const* srcs, Fr* const* dsts, ui
         p.vstride = vstride;
         out[count].mode = m;
         out[count].join = j;
+        out[count].radix2 = c->radix2;
         out[count].p = p;
         out[count].n_vec = kinds * n_proof;
         ++count;
@@ -346,9 +354,9 @@ int plan_h(g16_ctx* ctx, const void* a_mont, const void* b_mont, const void* c_m
     for (const void* i : ins)
         if (overlaps(i, nbytes, ctx->ws_begin, ctx->ws_bytes)) return G16_EALIAS;
     for (const void* p : ins)
-        if (!device_pointer(p)) return G16_EINVAL;
+        if (!device_range(p, nbytes)) return G16_EINVAL;
     for (const void* p : outs)
-        if (!device_pointer(p)) return G16_EINVAL;
+        if (!device_range(p, nbytes)) return G16_EINVAL;
     const size_t n = size_t(1) << ctx->log_n;
     const Fr* srcs[3] = {(const Fr*)a_mont, (const Fr*)b_mont, (const Fr*)c_mont};
     Fr* dsts[3] = {ctx->scratch, ctx->scratch + n, ctx->scratch + 2 * n};
@@ -399,7 +407,7 @@ int g16_h_prepare(uint32_t log_n, void* workspace, size_t workspace_bytes, void*
     if (log_n < G16_MIN_LOG_N || log_n > G16_MAX_LOG_N) return G16_ERANGE;
     if ((uintptr_t)workspace % kAlign) return G16_EINVAL;
     if (workspace_bytes < g16_h_workspace_bytes(log_n)) return G16_ENOSPACE;
-    if (!device_pointer(workspace)) return G16_EINVAL;
+    if (!device_range(workspace, g16_h_workspace_bytes(log_n))) return G16_EINVAL;
     g16_ctx* c = new (std::nothrow) g16_ctx;
     if (!c) return G16_EINVAL;
     std::memset(c, 0, sizeof *c);
@@ -421,6 +429,7 @@ int g16_h_prepare(uint32_t log_n, void* workspace, size_t workspace_bytes, void*
     c->omega_inv = g16::fr_inv(c->omega);
     c->size_inv_entry = g16::tw29_entry(c->size_inv);
     c->n_batches = plan_batches(log_n, max_batch_k(), c->batch_k);
+    c->radix2 = std::getenv("G16_RADIX2") != nullptr;
 
     // bits where the plan's batches start (the forward table's layout follows them)
     uint32_t starts = 0, bit = 0;
@@ -444,13 +453,22 @@ int g16_h_prepare(uint32_t log_n, void* workspace, size_t workspace_bytes, void*
         return rc;
     }
     c->magic = kMagic;
+    {
+        std::lock_guard<std::mutex> lock(g_live_mu);
+        g_live.insert(c);
+    }
     *out_ctx = c;
     return G16_OK;
 }
 
 int g16_release(g16_ctx* ctx) {
     if (!ctx) return G16_EINVAL;
-    if (ctx->magic != kMagic) return G16_ESTATE;
+    {
+        // a pointer that is not a live context (released before, or never handed out) is
+        // refused without being read
+        std::lock_guard<std::mutex> lock(g_live_mu);
+        if (g_live.erase(ctx) == 0) return G16_ESTATE;
+    }
     ctx->magic = kDead;
     delete ctx;
     return G16_OK;
@@ -485,7 +503,7 @@ int g16_coset_eval(g16_ctx* ctx, const void* in_mont, void* out_mont, void* stre
     if (overlaps(in_mont, nbytes, ctx->ws_begin, ctx->ws_bytes) ||
         overlaps(out_mont, nbytes, ctx->ws_begin, ctx->ws_bytes))
         return G16_EALIAS;
-    if (!device_pointer(in_mont) || !device_pointer(out_mont)) return G16_EINVAL;
+    if (!device_range(in_mont, nbytes) || !device_range(out_mont, nbytes)) return G16_EINVAL;
     hipStream_t s = (hipStream_t)stream;
     const Fr* src = (const Fr*)in_mont;
     Launch ls[kMaxLaunches];
@@ -536,11 +554,11 @@ int g16_h_compute_batch(g16_ctx* ctx, uint64_t n_proofs, const void* a_mont,
         for (const void* i : ins)
             if (overlaps(outs[o], bytes, i, bytes)) return G16_EALIAS;
         if (overlaps(outs[o], bytes, ctx->ws_begin, ctx->ws_bytes)) return G16_EALIAS;
-        if (!device_pointer(outs[o])) return G16_EINVAL;
+        if (!device_range(outs[o], bytes)) return G16_EINVAL;
     }
     for (const void* i : ins) {
         if (overlaps(i, bytes, ctx->ws_begin, ctx->ws_bytes)) return G16_EALIAS;
-        if (!device_pointer(i)) return G16_EINVAL;
+        if (!device_range(i, bytes)) return G16_EINVAL;
     }
     // A' and B' live in h_mont and h_std until the join overwrites them element by
     // element; C' (only when there is more than one batch) lives in the scratch.
@@ -584,7 +602,7 @@ int g16_h_join(uint64_t n, const void* a_mont, const void* b_mont, const void* c
         if (overlaps(h_mont, nbytes, i, nbytes) || overlaps(h_std, nbytes, i, nbytes))
             return G16_EALIAS;
     for (const void* p : {a_mont, b_mont, c_mont, (const void*)h_mont, (const void*)h_std})
-        if (!device_pointer(p)) return G16_EINVAL;
+        if (!device_range(p, nbytes)) return G16_EINVAL;
     hipLaunchKernelGGL(g16::h_join_kernel, dim3(ew_blocks(n)), dim3(kThreads), 0,
                        (hipStream_t)stream, (const Fr*)a_mont, (const Fr*)b_mont,
                        (const Fr*)c_mont, (Fr*)h_mont, (Fr*)h_std, n);
@@ -617,9 +635,9 @@ int g16_gather_abc(uint64_t n_rows, const uint32_t* row_ptr_a, const uint32_t* s
             if (ins[i] && in_bytes[i] && overlaps(outs[o], ob, ins[i], in_bytes[i]))
                 return G16_EALIAS;
     for (int i = 0; i < 7; ++i)
-        if (ins[i] && in_bytes[i] && !device_pointer(ins[i])) return G16_EINVAL;
+        if (ins[i] && in_bytes[i] && !device_range(ins[i], in_bytes[i])) return G16_EINVAL;
     for (int o = 0; o < 3; ++o)
-        if (!device_pointer(outs[o])) return G16_EINVAL;
+        if (!device_range(outs[o], ob)) return G16_EINVAL;
     const uint32_t blocks = (uint32_t)((n_rows + g16::kGatherLanes - 1) / g16::kGatherLanes);
     hipLaunchKernelGGL(g16::gather_kernel, dim3(blocks), dim3(g16::kGatherLanes), 0,
                        (hipStream_t)stream,
@@ -635,7 +653,8 @@ static int elementwise(uint64_t n, const void* a, const void* b, void* out, int 
     const size_t nbytes = n * sizeof(Fr);
     if (a != out && overlaps(a, nbytes, out, nbytes)) return G16_EALIAS;
     if (op == 2 && b != out && overlaps(b, nbytes, out, nbytes)) return G16_EALIAS;
-    if (!device_pointer(a) || !device_pointer(out) || (op == 2 && !device_pointer(b)))
+    if (!device_range(a, nbytes) || !device_range(out, nbytes) ||
+        (op == 2 && !device_range(b, nbytes)))
         return G16_EINVAL;
     hipLaunchKernelGGL(g16::elementwise_kernel, dim3(ew_blocks(n)), dim3(kThreads), 0,
                        (hipStream_t)stream, (const Fr*)a, (const Fr*)b, (Fr*)out, n, op);

@@ -11,6 +11,7 @@
 #include <cstring>
 
 #include "g16.h"
+#include "host_util.hpp"
 #include "msm_kernels.hpp"
 
 using g16::G1Aff;
@@ -39,16 +40,7 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return na && nb && x < y + nb && y < x + na;
 }
 
-bool device_pointer(const void* p) {
-    if (!p) return false;
-    hipPointerAttribute_t attr;
-    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
-        (void)hipGetLastError();
-        return false;
-    }
-    return attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged ||
-           attr.type == hipMemoryTypeUnified;
-}
+using g16::device_range;
 
 // Entries per accumulation thread: kSliceLen, doubled while below a bucket's mean run
 // n / 2^(c-1) as long as the windows still give 2^18 threads or more (four waves per
@@ -216,7 +208,7 @@ int g16_msm_g1(uint64_t n, const void* scalars_std, const void* bases_mont, uint
     if (c > kMaxC || !window_sums) return G16_EINVAL;
     const uint32_t W = windows_for(c);
     const size_t sums_bytes = (size_t)W * sizeof(G1Xyzz);
-    if (!device_pointer(window_sums)) return G16_EINVAL;
+    if (!device_range(window_sums, sums_bytes)) return G16_EINVAL;
     hipStream_t s = (hipStream_t)stream;
     if (n == 0) {  // the empty sum: every window at infinity
         const uint32_t words = (uint32_t)(sums_bytes / 4);
@@ -235,7 +227,8 @@ int g16_msm_g1(uint64_t n, const void* scalars_std, const void* bases_mont, uint
         overlaps(window_sums, sums_bytes, bases_mont, bb) ||
         overlaps(window_sums, sums_bytes, workspace, L.total))
         return G16_EALIAS;
-    if (!device_pointer(scalars_std) || !device_pointer(bases_mont) || !device_pointer(workspace))
+    if (!device_range(scalars_std, sb) || !device_range(bases_mont, bb) ||
+        !device_range(workspace, L.total))
         return G16_EINVAL;
 
     uint8_t* ws = (uint8_t*)workspace;
@@ -265,12 +258,8 @@ int g16_msm_g1(uint64_t n, const void* scalars_std, const void* bases_mont, uint
     const size_t place_lds = (size_t)g16::kMsmRound * 8 + (size_t)mp.bins * 12;
     const size_t row_lds = (size_t)mp.stage * 16 + ((size_t)1 << mp.bin_shift) * 4;
     // LDS beyond the default 64 KiB is allowed per kernel
-    if (hipFuncSetAttribute((const void*)g16::msm_bin_place,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)place_lds) !=
-            hipSuccess ||
-        (row_lds > 65536 &&
-         hipFuncSetAttribute((const void*)g16::msm_bin_sort,
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)row_lds) != hipSuccess))
+    if (g16::allow_lds((const void*)g16::msm_bin_place, place_lds) != hipSuccess ||
+        g16::allow_lds((const void*)g16::msm_bin_sort, row_lds) != hipSuccess)
         return G16_EHIP;
     const dim3 bin_blk(g16::kMsmBinThreads);
 
@@ -325,7 +314,8 @@ int g16_g1_generator_mul(uint64_t n, const void* scalars_std, void* out_affine_m
                          void* stream) {
     if (n == 0 || n >= (1ull << 31) || !scalars_std || !out_affine_mont) return G16_EINVAL;
     if (overlaps(scalars_std, n * 32, out_affine_mont, n * sizeof(G1Aff))) return G16_EALIAS;
-    if (!device_pointer(scalars_std) || !device_pointer(out_affine_mont)) return G16_EINVAL;
+    if (!device_range(scalars_std, n * 32) || !device_range(out_affine_mont, n * sizeof(G1Aff)))
+        return G16_EINVAL;
     hipLaunchKernelGGL(g16::g1_generator_mul, dim3(blocks_for(n)), dim3(g16::kMsmThreads), 0,
                        (hipStream_t)stream, (const uint32_t*)scalars_std, (uint32_t)n,
                        (G1Aff*)out_affine_mont);

@@ -2,6 +2,7 @@
 // batch size G16_R8_K.
 #pragma once
 
+#include "host_util.hpp"
 #include "r8_launch.hpp"
 
 namespace g16 {
@@ -11,9 +12,7 @@ hipError_t launch_r8(const BatchParams& p, uint32_t n_vec, hipStream_t stream) {
     using G = R8GeomFor<K, kR8Group, M>;
     // LDS beyond the default 64 KiB has to be allowed per kernel (on the current device)
     if constexpr (G::kLdsBytes > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)ntt_r8_kernel<K, kR8Group, M, JOIN>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           G::kLdsBytes);
+        hipError_t e = allow_lds((const void*)ntt_r8_kernel<K, kR8Group, M, JOIN>, G::kLdsBytes);
         if (e != hipSuccess) return e;
     }
     const uint64_t groups = (1ull << (p.log_n - K)) / G::kSpw;

@@ -26,6 +26,13 @@
  *   - the CSR gather and C = A o B (the GATHER_CU page, kernel description and
  *     "WHY C IS COMPUTED HERE AND NOT GATHERED").
  *
+ * Threads.  The transform passes, the element-wise loops and the barycentric sums run
+ * over a fixed number of threads (oracle_set_threads; 1 by default): each thread takes a
+ * contiguous range of the butterflies of one pass, or of the elements, and a pass ends
+ * when every thread has finished it.  The butterflies of one pass are independent, so
+ * every butterfly computes exactly what it computes single-threaded; only wall time
+ * changes.
+ *
  * Readings where the pages are silent (each stated in the design notes):
  *   - the primitive root: g = 5, omega_{2^28} = 5^((r-1)/2^28), the coset shift for
  *     a domain of 2^L points is omega_{2^28}^(2^(27-L)) and the domain root is its
@@ -33,6 +40,7 @@
  *   - the inverse transform uses the natural-order table of omega^{-1};
  *   - Fr elements are 32-byte little-endian integers (8 x u32 = 4 x u64 words).
  */
+#include <pthread.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -51,6 +59,42 @@ static fe R_MOD_R;            /* 2^256 mod r */
 static fe R_INV;              /* (2^256)^-1 mod r */
 static fe ROOT_2_28;          /* 5^((r-1)/2^28), a primitive 2^28-th root of unity */
 static int INITIALISED = 0;
+static int THREADS = 1;       /* oracle_set_threads */
+
+/* ---------------------------------------------------------------- threads */
+
+typedef void (*range_fn)(void* arg, size_t lo, size_t hi);
+typedef struct { range_fn fn; void* arg; size_t lo, hi; } range_task;
+
+static void* range_entry(void* t) {
+    range_task* r = (range_task*)t;
+    r->fn(r->arg, r->lo, r->hi);
+    return NULL;
+}
+
+/* fn(arg, lo, hi) over [0, count) split into THREADS contiguous ranges, one per thread;
+ * returns when all are done.  Small counts run on the calling thread. */
+static void parallel_for(size_t count, range_fn fn, void* arg) {
+    int t = THREADS;
+    if (t > 256) t = 256;
+    if (t <= 1 || count < 1024) { fn(arg, 0, count); return; }
+    pthread_t th[256];
+    range_task task[256];
+    int started[256];
+    size_t per = (count + (size_t)t - 1) / (size_t)t;
+    for (int i = 0; i < t; ++i) {
+        size_t lo = (size_t)i * per < count ? (size_t)i * per : count;
+        size_t hi = lo + per < count ? lo + per : count;
+        task[i].fn = fn; task[i].arg = arg; task[i].lo = lo; task[i].hi = hi;
+        started[i] = 0;
+        if (i > 0 && lo < hi) started[i] = pthread_create(&th[i], NULL, range_entry, &task[i]) == 0;
+    }
+    fn(arg, task[0].lo, task[0].hi);
+    for (int i = 1; i < t; ++i) {
+        if (started[i]) pthread_join(th[i], NULL);
+        else if (task[i].lo < task[i].hi) fn(arg, task[i].lo, task[i].hi);
+    }
+}
 
 /* ---------------------------------------------------------------- multi-limb helpers */
 
@@ -220,6 +264,34 @@ static size_t bitrev(size_t i, unsigned L) {
     return r;
 }
 
+/* One pass of the DIT: butterflies b in [lo, hi) of the pass with half-size `half`;
+ * butterfly b is position j = b mod half of block b / half. */
+typedef struct { fe* x; const fe* tw; size_t half, step; } pass_job;
+
+static void pass_range(void* arg, size_t lo, size_t hi) {
+    const pass_job* p = (const pass_job*)arg;
+    fe* x = p->x;
+    const fe* tw = p->tw;
+    size_t half = p->half, step = p->step;
+    for (size_t b = lo; b < hi; ++b) {
+        size_t start = (b / half) * 2 * half, j = b % half;
+        fe u = x[start + j];
+        fe v = fe_mul(x[start + j + half], tw[j * step]);
+        x[start + j] = fe_add(u, v);
+        x[start + j + half] = fe_sub(u, v);
+    }
+}
+
+/* x[i] *= k for i in [lo, hi) */
+typedef struct { fe* x; fe k; } scale_job;
+
+static void scale_range(void* arg, size_t lo, size_t hi) {
+    scale_job* p = (scale_job*)arg;
+    fe* x = p->x;
+    fe size_inv = p->k;
+    for (size_t i = lo; i < hi; ++i) x[i] = fe_mul(x[i], size_inv);
+}
+
 /* Forward DIT with the CPU backend's order: swap pass, then half = 1, 2, ..., n/2. */
 static void dit_in_place(fe* x, unsigned L, fe root) {
     size_t n = (size_t)1 << L;
@@ -233,15 +305,8 @@ static void dit_in_place(fe* x, unsigned L, fe root) {
         if (j > i) { fe t = x[i]; x[i] = x[j]; x[j] = t; }
     }
     for (size_t half = 1; half < n; half *= 2) {
-        size_t step = n / (2 * half);
-        for (size_t start = 0; start < n; start += 2 * half) {
-            for (size_t j = 0; j < half; ++j) {
-                fe u = x[start + j];
-                fe v = fe_mul(x[start + j + half], tw[j * step]);
-                x[start + j] = fe_add(u, v);
-                x[start + j + half] = fe_sub(u, v);
-            }
-        }
+        pass_job job = {x, tw, half, n / (2 * half)};
+        parallel_for(n / 2, pass_range, &job);
     }
     free(tw);
 }
@@ -257,7 +322,26 @@ static void intt_std(fe* x, unsigned L) {
     domain_roots(L, &omega, &shift, &size_inv);
     dit_in_place(x, L, fe_inv(omega));
     size_t n = (size_t)1 << L;
-    for (size_t i = 0; i < n; ++i) x[i] = fe_mul(x[i], size_inv);
+    scale_job job = {x, size_inv};
+    parallel_for(n, scale_range, &job);
+}
+
+/* Element-wise conversions of n Montgomery inputs to standard form (dir 1) or of
+ * standard-form values to Montgomery outputs (dir 0). */
+typedef struct { int dir; const u64* in; u64* out; } convert_job;
+
+static void convert_range(void* arg, size_t lo, size_t hi) {
+    convert_job* p = (convert_job*)arg;
+    for (size_t i = lo; i < hi; ++i) {
+        fe x; memcpy(x.v, p->in + 4 * i, 32);
+        fe z = p->dir == 0 ? to_mont(x) : from_mont(x);
+        memcpy(p->out + 4 * i, z.v, 32);
+    }
+}
+
+static void convert_n(int dir, size_t n, const u64* in, u64* out) {
+    convert_job job = {dir, in, out};
+    parallel_for(n, convert_range, &job);
 }
 
 /* ================================================================ exported API
@@ -266,6 +350,14 @@ static void intt_std(fe* x, unsigned L) {
  * return 0 on success, -1 on bad arguments. */
 
 int oracle_modulus(u64 out[4]) { memcpy(out, MOD.v, 32); return 0; }
+
+/* Threads used by the transforms, the element-wise loops and the barycentric sums
+ * (1 .. 256); returns the previous setting. */
+int oracle_set_threads(int threads) {
+    int prev = THREADS;
+    if (threads >= 1 && threads <= 256) THREADS = threads;
+    return prev;
+}
 
 int oracle_constants(u64 mu[5], u64 r_mod_r[4], u64 root_2_28[4]) {
     oracle_init();
@@ -311,11 +403,7 @@ int oracle_inv(const u64 a[4], u64 out[4]) {
 /* dir: 0 std -> mont, 1 mont -> std */
 int oracle_convert(int dir, size_t n, const u64* in, u64* out) {
     oracle_init();
-    for (size_t i = 0; i < n; ++i) {
-        fe x; memcpy(x.v, in + 4 * i, 32);
-        fe z = dir == 0 ? to_mont(x) : from_mont(x);
-        memcpy(out + 4 * i, z.v, 32);
-    }
+    convert_n(dir, n, in, out);
     return 0;
 }
 
@@ -360,6 +448,22 @@ int oracle_dft_naive(unsigned L, int inverse, const u64* x, u64* y) {
     return 0;
 }
 
+/* The coset shift x_j *= shift^j for j in [lo, hi), the powers by repeated
+ * multiplication from shift^lo. */
+typedef struct { fe* x; fe shift; } shift_job;
+
+static void shift_range(void* arg, size_t lo, size_t hi) {
+    shift_job* p = (shift_job*)arg;
+    fe* x = p->x;
+    fe shift = p->shift;
+    u64 e[4] = {lo, 0, 0, 0};
+    fe sj = fe_pow(shift, e);
+    for (size_t j = lo; j < hi; ++j) {
+        x[j] = fe_mul(x[j], sj);
+        sj = fe_mul(sj, shift);
+    }
+}
+
 /* Stages 1 to 3 on one standard-form vector, in place: the inverse transform, the
  * coset shift x_j *= shift^j, the forward transform. */
 static void coset_eval_std(fe* x, unsigned L) {
@@ -367,11 +471,8 @@ static void coset_eval_std(fe* x, unsigned L) {
     fe omega, shift, size_inv;
     domain_roots(L, &omega, &shift, &size_inv);
     intt_std(x, L);                              /* stage 1 */
-    fe sj = fe_small(1);                         /* stage 2: x_j *= shift^j */
-    for (size_t j = 0; j < n; ++j) {
-        x[j] = fe_mul(x[j], sj);
-        sj = fe_mul(sj, shift);
-    }
+    shift_job job = {x, shift};                  /* stage 2: x_j *= shift^j */
+    parallel_for(n, shift_range, &job);
     ntt_std(x, L);                               /* stage 3 */
 }
 
@@ -382,17 +483,27 @@ int oracle_coset_eval(unsigned L, const u64* in_mont, u64* out_mont) {
     size_t n = (size_t)1 << L;
     fe* v = (fe*)malloc(sizeof(fe) * n);
     if (!v) return -1;
-    for (size_t i = 0; i < n; ++i) {
-        fe y; memcpy(y.v, in_mont + 4 * i, 32);
-        v[i] = from_mont(y);
-    }
+    convert_n(1, n, in_mont, (u64*)v);
     coset_eval_std(v, L);
-    for (size_t i = 0; i < n; ++i) {
-        fe m = to_mont(v[i]);
-        memcpy(out_mont + 4 * i, m.v, 32);
-    }
+    convert_n(0, n, (const u64*)v, out_mont);
     free(v);
     return 0;
+}
+
+/* Stage 4 for i in [lo, hi): H = A'B' - C', both encodings. */
+typedef struct { fe* v[3]; u64* h_mont; u64* h_std; } join_job;
+
+static void join_range(void* arg, size_t lo, size_t hi) {
+    join_job* p = (join_job*)arg;
+    fe** v = p->v;
+    u64* h_mont = p->h_mont;
+    u64* h_std = p->h_std;
+    for (size_t i = lo; i < hi; ++i) {
+        fe h = fe_sub(fe_mul(v[0][i], v[1][i]), v[2][i]);
+        memcpy(h_std + 4 * i, h.v, 32);
+        fe hm = to_mont(h);
+        memcpy(h_mont + 4 * i, hm.v, 32);
+    }
 }
 
 /* The H pipeline on Montgomery inputs: three inverse transforms, the coset shift,
@@ -403,23 +514,17 @@ int oracle_h_pipeline(unsigned L, const u64* a_mont, const u64* b_mont, const u6
     oracle_init();
     size_t n = (size_t)1 << L;
     const u64* ins[3] = {a_mont, b_mont, c_mont};
-    fe* v[3];
+    join_job job;
     for (int k = 0; k < 3; ++k) {
-        v[k] = (fe*)malloc(sizeof(fe) * n);
-        if (!v[k]) return -1;
-        for (size_t i = 0; i < n; ++i) {
-            fe y; memcpy(y.v, ins[k] + 4 * i, 32);
-            v[k][i] = from_mont(y);
-        }
-        coset_eval_std(v[k], L);                 /* stages 1 to 3 */
+        job.v[k] = (fe*)malloc(sizeof(fe) * n);
+        if (!job.v[k]) return -1;
+        convert_n(1, n, ins[k], (u64*)job.v[k]);
+        coset_eval_std(job.v[k], L);             /* stages 1 to 3 */
     }
-    for (size_t i = 0; i < n; ++i) {             /* stage 4 */
-        fe h = fe_sub(fe_mul(v[0][i], v[1][i]), v[2][i]);
-        memcpy(h_std + 4 * i, h.v, 32);
-        fe hm = to_mont(h);
-        memcpy(h_mont + 4 * i, hm.v, 32);
-    }
-    for (int k = 0; k < 3; ++k) free(v[k]);
+    job.h_mont = h_mont;                         /* stage 4 */
+    job.h_std = h_std;
+    parallel_for(n, join_range, &job);
+    for (int k = 0; k < 3; ++k) free(job.v[k]);
     return 0;
 }
 
@@ -427,8 +532,56 @@ int oracle_h_pipeline(unsigned L, const u64* a_mont, const u64* b_mont, const u6
  * polynomial interpolating A (and B, C) on the domain, from the barycentric form of
  * the Lagrange basis on the n-th roots of unity,
  *     a(x) = (x^n - 1) / n * sum_j A_j omega^j / (x - omega^j),
- * then H_i = a(x) b(x) - c(x).  O(n) per index (one batched inversion).
+ * then H_i = a(x) b(x) - c(x).  O(n) per index.  The sums over j are split into ranges,
+ * one per thread; each range inverts its own denominators with one inversion (prefix
+ * products, then back substitution), and the ranges' partial sums are added at the end.
  * Inputs Montgomery, outputs both encodings for the chosen indices. */
+typedef struct {
+    const fe* wj;          /* omega^j, j < n */
+    const u64* ins[3];     /* A, B, C, Montgomery */
+    fe x;                  /* the evaluation point */
+    fe* pre;               /* scratch, n elements */
+    fe* part;              /* partial sums, 3 per range */
+    size_t per;            /* range length */
+} bary_job;
+
+typedef struct { fe* wj; fe omega; } powers_job;
+
+static void powers_range(void* arg, size_t lo, size_t hi) {   /* wj[j] = omega^j */
+    fe* wj = ((powers_job*)arg)->wj;
+    fe omega = ((powers_job*)arg)->omega;
+    u64 e[4] = {lo, 0, 0, 0};
+    fe w = fe_pow(omega, e);
+    for (size_t j = lo; j < hi; ++j) {
+        wj[j] = w;
+        w = fe_mul(w, omega);
+    }
+}
+
+static void bary_range(void* arg, size_t lo, size_t hi) {
+    bary_job* p = (bary_job*)arg;
+    const fe* wj = p->wj;
+    fe* pre = p->pre;
+    fe x = p->x;
+    fe acc = fe_small(1);                      /* prefix products of (x - omega^j) */
+    for (size_t j = lo; j < hi; ++j) {
+        acc = fe_mul(acc, fe_sub(x, wj[j]));
+        pre[j] = acc;
+    }
+    fe inv = fe_inv(acc);                      /* 1 / prod over the range */
+    fe sum[3] = {fe_zero(), fe_zero(), fe_zero()};
+    for (size_t jj = hi; jj-- > lo;) {
+        fe inv_d = jj > lo ? fe_mul(inv, pre[jj - 1]) : inv;   /* 1 / (x - omega^j) */
+        inv = fe_mul(inv, fe_sub(x, wj[jj]));
+        fe weight = fe_mul(wj[jj], inv_d);
+        for (int k = 0; k < 3; ++k) {
+            fe y; memcpy(y.v, p->ins[k] + 4 * jj, 32);
+            sum[k] = fe_add(sum[k], fe_mul(from_mont(y), weight));
+        }
+    }
+    for (int k = 0; k < 3; ++k) p->part[3 * (lo / p->per) + (size_t)k] = sum[k];
+}
+
 int oracle_h_at(unsigned L, const u64* a_mont, const u64* b_mont, const u64* c_mont,
                 size_t count, const uint32_t* idx, u64* h_mont, u64* h_std) {
     if (L < 1 || L > 27) return -1;
@@ -437,30 +590,23 @@ int oracle_h_at(unsigned L, const u64* a_mont, const u64* b_mont, const u64* c_m
     for (size_t q = 0; q < count; ++q) if (idx[q] >= n) return -1;
     fe omega, shift, size_inv;
     domain_roots(L, &omega, &shift, &size_inv);
-    fe* wj = (fe*)malloc(sizeof(fe) * n);     /* omega^j */
-    fe* pre = (fe*)malloc(sizeof(fe) * n);    /* prefix products of (x - omega^j) */
-    if (!wj || !pre) { free(wj); free(pre); return -1; }
-    wj[0] = fe_small(1);
-    for (size_t j = 1; j < n; ++j) wj[j] = fe_mul(wj[j - 1], omega);
-    const u64* ins[3] = {a_mont, b_mont, c_mont};
+    fe* wj = (fe*)malloc(sizeof(fe) * n);      /* omega^j */
+    fe* pre = (fe*)malloc(sizeof(fe) * n);
+    fe* part = (fe*)malloc(sizeof(fe) * 3 * 257);
+    if (!wj || !pre || !part) { free(wj); free(pre); free(part); return -1; }
+    powers_job pw = {wj, omega};
+    parallel_for(n, powers_range, &pw);
+    /* the same split as parallel_for makes (or one range on the calling thread) */
+    size_t ranges = (THREADS > 1 && n >= 1024) ? (size_t)(THREADS > 256 ? 256 : THREADS) : 1;
+    bary_job job = {wj, {a_mont, b_mont, c_mont}, fe_zero(), pre, part, (n + ranges - 1) / ranges};
     for (size_t q = 0; q < count; ++q) {
         fe x = fe_mul(shift, wj[idx[q]]);     /* shift * omega^i */
-        fe acc = fe_small(1);
-        for (size_t j = 0; j < n; ++j) {
-            acc = fe_mul(acc, fe_sub(x, wj[j]));
-            pre[j] = acc;
-        }
-        fe inv = fe_inv(acc);                  /* 1 / prod_j (x - omega^j) */
+        job.x = x;
+        for (size_t t = 0; t < 3 * ranges; ++t) part[t] = fe_zero();
+        parallel_for(n, bary_range, &job);
         fe sum[3] = {fe_zero(), fe_zero(), fe_zero()};
-        for (size_t jj = n; jj-- > 0;) {
-            fe inv_d = jj ? fe_mul(inv, pre[jj - 1]) : inv;   /* 1 / (x - omega^j) */
-            inv = fe_mul(inv, fe_sub(x, wj[jj]));
-            fe weight = fe_mul(wj[jj], inv_d);
-            for (int k = 0; k < 3; ++k) {
-                fe y; memcpy(y.v, ins[k] + 4 * jj, 32);
-                sum[k] = fe_add(sum[k], fe_mul(from_mont(y), weight));
-            }
-        }
+        for (size_t t = 0; t < ranges; ++t)
+            for (int k = 0; k < 3; ++k) sum[k] = fe_add(sum[k], part[3 * t + (size_t)k]);
         /* (x^n - 1) / n */
         u64 e[4] = {n, 0, 0, 0};
         fe scale = fe_mul(fe_sub(fe_pow(x, e), fe_small(1)), size_inv);
@@ -470,20 +616,28 @@ int oracle_h_at(unsigned L, const u64* a_mont, const u64* b_mont, const u64* c_m
         fe hm = to_mont(h);
         memcpy(h_mont + 4 * q, hm.v, 32);
     }
-    free(wj); free(pre);
+    free(wj); free(pre); free(part);
     return 0;
 }
 
 /* Pointwise product out_i = a_i * b_i of Montgomery vectors (Montgomery out). */
+typedef struct { const u64* a; const u64* b; u64* out; } product_job;
+
+static void product_range(void* arg, size_t lo, size_t hi) {
+    product_job* p = (product_job*)arg;
+    for (size_t i = lo; i < hi; ++i) {
+        fe x, y;
+        memcpy(x.v, p->a + 4 * i, 32);
+        memcpy(y.v, p->b + 4 * i, 32);
+        fe z = to_mont(fe_mul(from_mont(x), from_mont(y)));
+        memcpy(p->out + 4 * i, z.v, 32);
+    }
+}
+
 int oracle_pointwise_mul_mont(size_t n, const u64* a_mont, const u64* b_mont, u64* out_mont) {
     oracle_init();
-    for (size_t i = 0; i < n; ++i) {
-        fe x, y;
-        memcpy(x.v, a_mont + 4 * i, 32);
-        memcpy(y.v, b_mont + 4 * i, 32);
-        fe z = to_mont(fe_mul(from_mont(x), from_mont(y)));
-        memcpy(out_mont + 4 * i, z.v, 32);
-    }
+    product_job job = {a_mont, b_mont, out_mont};
+    parallel_for(n, product_range, &job);
     return 0;
 }
 

@@ -22,13 +22,14 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC",
-                               "-o", tmp, _SRC])
+                               "-pthread", "-o", tmp, _SRC])
         os.replace(tmp, _LIB)
     return _LIB
 
 
 _SIGNATURES = {
     "oracle_modulus": "P",
+    "oracle_set_threads": "I",
     "oracle_constants": "PPP",
     "oracle_field_op": "IZPPP",
     "oracle_pow": "PPP",
@@ -61,8 +62,8 @@ def compile_source(source: str, out_path: str) -> str:
     src_path = out_path + ".c"
     with open(src_path, "w") as f:
         f.write(source)
-    subprocess.check_call(["gcc", "-O2", "-std=c11", "-shared", "-fPIC", "-o", out_path,
-                           src_path])
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-shared", "-fPIC", "-pthread", "-o",
+                           out_path, src_path])
     return out_path
 
 
@@ -92,6 +93,15 @@ class use_library:
         return False
 
 
+def default_threads() -> int:
+    """Threads the oracle uses unless told otherwise: G16_ORACLE_THREADS, else the
+    host's cores, at most 16 (a GPU machine's CPU share)."""
+    env = os.environ.get("G16_ORACLE_THREADS")
+    if env:
+        return max(1, min(256, int(env)))
+    return max(1, min(16, os.cpu_count() or 1))
+
+
 def _load():
     global _lib
     if _override is not None:
@@ -100,7 +110,14 @@ def _load():
         if not os.path.exists(_LIB):
             build(force=False)
         _lib = open_library(_LIB)
+        _lib.oracle_set_threads(default_threads())
     return _lib
+
+
+def set_threads(threads: int) -> int:
+    """Threads for the transforms, element-wise loops and barycentric sums; returns the
+    previous setting.  Results do not depend on it."""
+    return _load().oracle_set_threads(int(threads))
 
 
 def _arr(x, rows=None) -> np.ndarray:

@@ -150,3 +150,57 @@ def test_host_side_argument_errors(lib):
                               P(3 << 24), None) == binding.G16_EINVAL
     assert lib.g16_gather_abc(8, z, z, z, 1, z, z, z, 1, z, 1, P(1 << 24), P(1 << 24),
                               P(3 << 24), None) == binding.G16_EALIAS
+
+
+def test_probe_library_exports_its_header():
+    """libg16_probe.so loads and exports what include/g16_probe.h declares."""
+    from groth16_polynomial_amd import probe
+    if not os.path.exists(probe.PROBE_PATH):
+        from groth16_polynomial_amd import build
+        build.build()
+    text = open(os.path.join(ROOT, "include", "g16_probe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(g16_\w+)\s*\(", text)))
+    assert names == ["g16_probe_rate"]
+    lib = probe.load()
+    for name in names:
+        assert hasattr(lib, name), name
+    # host-side argument checks (nothing is launched)
+    assert lib.g16_probe_rate(9, 1, 1, 0, None, None, None) == -1
+
+
+def test_probe_host_reference_small():
+    """The probe's host reference of its chains, against plain Python integers."""
+    from groth16_polynomial_amd import probe
+    blocks, iters, seed = 1, 5, 99
+    got = probe.expected(0, blocks, iters, seed)
+    m = (1 << 64) - 1
+    for gid in (0, 1, 200):
+        x = ((gid * 2654435761) & 0xffffffff) ^ seed
+        want = 0
+        for k in range(8):
+            a = ((gid + k) * 0x9E3779B97F4A7C15) & m
+            for _ in range(iters):
+                a = (a + x * (seed | 1)) & m
+            want ^= a
+        assert int(got[gid]) == want
+    got3 = probe.expected(3, blocks, iters, seed)
+    for gid in (0, 7):
+        x = ((gid * 2654435761) & 0xffffffff) ^ seed
+        want = 0
+        for k in range(8):
+            a = (((gid + k) * 0x9E3779B9) | 1) & 0xffffffff
+            for _ in range(iters):
+                a = (a * x) & 0xffffffff
+            want ^= a
+        assert int(got3[gid]) == want
+
+
+def test_release_of_unknown_context_is_refused(lib):
+    """g16_release and the context calls refuse a pointer that is not a live context
+    (never handed out, or released before) without reading through it."""
+    bogus = ctypes.c_void_p(0x1000)
+    assert lib.g16_release(bogus) == binding.G16_ESTATE
+    assert lib.g16_ctx_log_n(bogus) == 0
+    assert lib.g16_h_stage_count(bogus) == binding.G16_ESTATE
+    assert lib.g16_release(None) == binding.G16_EINVAL

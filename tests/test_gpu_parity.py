@@ -154,7 +154,8 @@ def test_ntt_default_batching(log_n):
 
 
 @pytest.mark.parametrize("log_n,kmax", [(5, 2), (7, 3), (9, 4), (12, 4), (12, 5), (13, 6),
-                                        (16, 11), (16, 12), (18, 12)])
+                                        (12, 11), (12, 12), (16, 11), (16, 12), (18, 12),
+                                        (23, 12), (24, 12)])
 def test_ntt_other_batchings(log_n, kmax):
     _ntt_case(log_n, kmax)
 
@@ -186,14 +187,15 @@ def _h_case(log_n, kmax=None, workload=1, c_is_product=True):
     return ctx, (ad, bd, cd), (hm, hs)
 
 
-@pytest.mark.parametrize("log_n", list(range(1, 17)) + [18])
+# every domain from 2^1 to 2^21 (2^20 is the workload test below), whole outputs
+@pytest.mark.parametrize("log_n", [L for L in range(1, 22) if L != 20])
 def test_h_compute_default_batching(log_n):
     ctx, _, _ = _h_case(log_n)
     ctx.release()
 
 
 @pytest.mark.parametrize("log_n,kmax", [(4, 2), (8, 3), (10, 4), (12, 5), (13, 4), (14, 12),
-                                        (17, 6)])
+                                        (12, 12), (17, 6)])
 def test_h_compute_other_batchings(log_n, kmax):
     ctx, _, _ = _h_case(log_n, kmax)
     ctx.release()
@@ -236,48 +238,31 @@ def test_h_compute_workload_2_20():
     ctx.release()
 
 
-def test_h_compute_workload_2_22_sampled():
-    """The 2^22 workload: sampled outputs by the oracle's barycentric route, plus the
-    quotient-degree property on every output."""
-    log_n, n = 22, 1 << 22
-    say("h_compute 2^22 sampled")
-    a, b = synth.h_inputs(5, log_n)
-    ad, bd = gpu_mont(a), gpu_mont(b)
-    cd = g.fr_mul(ad, bd)
-    ctx = g.HContext(log_n)
-    hm, hs = ctx.h_compute(ad, bd, cd)
-    am, bm = host(ad), host(bd)
-    same(am[:4096], oracle.to_mont(a[:4096]), "A to Montgomery (prefix)")
-    cm = oracle.pointwise_mul_mont(am, bm)
-    same(host(cd)[:4096], cm[:4096], "C = A o B (prefix)")
-    rng = np.random.default_rng(22)
-    idx = np.array([0, 1, n - 1] + sorted(rng.integers(0, n, 2).tolist()), np.uint32)
-    want_m, want_s = oracle.h_at(log_n, am, bm, cm, idx)
-    hm_h, hs_h = host(hm), host(hs)
-    same(hm_h[idx], want_m, "h_mont 2^22 sampled")
-    same(hs_h[idx], want_s, "h_std 2^22 sampled")
-    # every output: canonical, and the two encodings agree
-    same(oracle.to_mont(hs_h[:65536]), hm_h[:65536], "dual encoding (prefix)")
-    # quotient degree <= n - 2: the top coefficient of the inverse transform is zero
-    coeffs = host(ctx.ntt_inverse(hm))
-    assert not coeffs[n - 1].any()
+def test_h_compute_workload_2_22():
+    """The 2^22 workload (three batches, 8 + 7 + 7) in the benchmark's launch
+    configuration, every output of both encodings against the oracle's pipeline."""
+    log_n = 22
+    assert g.batch_plan(log_n) == [8, 7, 7]
+    ctx, _, _ = _h_case(log_n, workload=5)
     ctx.release()
 
 
-def test_ntt_2_24():
-    """Standalone transforms at 2^24 (three batches of 8 passes): forward against the
-    oracle's whole output, inverse by the round trip."""
+@pytest.mark.parametrize("log_n,plan", [(23, [8, 8, 7]), (24, [8, 8, 8])])
+def test_ntt_large(log_n, plan):
+    """Standalone transforms at 2^23 and 2^24 (three batches): forward and inverse against
+    the oracle's whole output, and the round trip."""
     import torch
-    log_n = 24
-    say("ntt 2^24")
+    say("ntt 2^%d" % log_n)
     x = synth.ntt_input(6, log_n)
     xm = oracle.to_mont(x)
     ctx = g.HContext(log_n)
-    assert g.batch_plan(log_n) == [8, 8, 8]
+    assert g.batch_plan(log_n) == plan
     xd = g.to_device(xm)
     fwd = ctx.ntt_forward(xd)
-    same(host(fwd), oracle.ntt_mont(xm, log_n), "forward 2^24")
-    assert torch.equal(ctx.ntt_inverse(fwd), xd), "round trip 2^24"
+    same(host(fwd), oracle.ntt_mont(xm, log_n), "forward 2^%d" % log_n)
+    inv = ctx.ntt_inverse(xd)
+    same(host(inv), oracle.ntt_mont(xm, log_n, inverse=True), "inverse 2^%d" % log_n)
+    assert torch.equal(ctx.ntt_inverse(fwd), xd), "round trip 2^%d" % log_n
     ctx.release()
 
 
@@ -320,18 +305,25 @@ def _h_large(log_n, inputs, samples):
     ctx.release()
 
 
+def test_h_compute_2_23_full():
+    """2^23 (8 + 8 + 7), every output of both encodings against the oracle's pipeline."""
+    ctx, _, _ = _h_case(23, workload=6)
+    ctx.release()
+
+
 def test_h_compute_2_24_sampled():
     a, b = synth.h_inputs(7, 24)
-    _h_large(24, (gpu_mont(a), gpu_mont(b)), 2)
+    _h_large(24, (gpu_mont(a), gpu_mont(b)), 4)
 
 
-@pytest.mark.parametrize("log_n", [23, 25, 26])
-def test_large_domains_properties(log_n):
-    """2^23, 2^25 and 2^26 (three near-equal batches each): the quotient-degree property
+@pytest.mark.parametrize("log_n", [25, 26])
+def test_large_domains(log_n):
+    """2^25 and 2^26 (three near-equal batches each): H at sampled outputs (the last
+    one among them) against the oracle's barycentric route, the quotient-degree property
     on every output, the encodings on a prefix, and the transforms' round trip."""
     import torch
     n = 1 << log_n
-    _h_large(log_n, (_gpu_canonical(n, log_n), _gpu_canonical(n, 100 + log_n)), 0)
+    _h_large(log_n, (_gpu_canonical(n, log_n), _gpu_canonical(n, 100 + log_n)), 3)
     ctx = g.HContext(log_n)
     x = _gpu_canonical(n, 200 + log_n)
     assert torch.equal(ctx.ntt_inverse(ctx.ntt_forward(x)), x), "round trip 2^%d" % log_n

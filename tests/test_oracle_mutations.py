@@ -17,13 +17,13 @@ fr = synth.ints_to_fr
 
 # (name, original text, planted text)
 MUTATIONS = [
-    ("coset shift by the domain root", "sj = fe_mul(sj, shift);", "sj = fe_mul(sj, omega);"),
+    ("coset shift by the domain root", "shift_job job = {x, shift};", "shift_job job = {x, omega};"),
     ("shift applied one index late", "x[j] = fe_mul(x[j], sj);\n        sj = fe_mul(sj, shift);",
      "sj = fe_mul(sj, shift);\n        x[j] = fe_mul(x[j], sj);"),
-    ("size_inv dropped", "for (size_t i = 0; i < n; ++i) x[i] = fe_mul(x[i], size_inv);", ""),
+    ("size_inv dropped", "for (size_t i = lo; i < hi; ++i) x[i] = fe_mul(x[i], size_inv);", ""),
     ("twiddle index without stride", "tw[j * step]", "tw[j]"),
-    ("butterfly outputs swapped", "x[start + j] = fe_add(u, v);\n                x[start + j + half] = fe_sub(u, v);",
-     "x[start + j] = fe_sub(u, v);\n                x[start + j + half] = fe_add(u, v);"),
+    ("butterfly outputs swapped", "x[start + j] = fe_add(u, v);\n        x[start + j + half] = fe_sub(u, v);",
+     "x[start + j] = fe_sub(u, v);\n        x[start + j + half] = fe_add(u, v);"),
     ("bit reversal dropped", "if (j > i) { fe t = x[i]; x[i] = x[j]; x[j] = t; }", ""),
     ("H operands transposed", "fe h = fe_sub(fe_mul(v[0][i], v[1][i]), v[2][i]);",
      "fe h = fe_sub(v[2][i], fe_mul(v[0][i], v[1][i]));"),
