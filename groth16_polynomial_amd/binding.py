@@ -40,6 +40,7 @@ SIGNATURES = {
     "g16_ntt_inverse": (_I, [_P, _P, _P, _P]),
     "g16_coset_eval": (_I, [_P, _P, _P, _P]),
     "g16_h_compute": (_I, [_P, _P, _P, _P, _P, _P, _P]),
+    "g16_h_compute_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P]),
     "g16_h_batch_scratch_bytes": (_SZ, [_U32, _U64]),
     "g16_h_compute_batch": (_I, [_P, _U64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "g16_h_stage_count": (_I, [_P]),
@@ -226,6 +227,15 @@ class HContext:
                                     _ptr(c, self.n, "c"), _ptr(h_mont, self.n, "h_mont"),
                                     _ptr(h_std, self.n, "h_std"), _stream(stream)),
                "g16_h_compute")
+        return h_mont, h_std
+
+    def h_compute_noalloc(self, a, b, c, h_mont, h_std, stream=None):
+        """g16_h_compute_noalloc: h_compute with the library's own device scratch
+        (outputs must be given: the call allocates nothing)."""
+        _check(load().g16_h_compute_noalloc(
+            self.handle, _ptr(a, self.n, "a"), _ptr(b, self.n, "b"), _ptr(c, self.n, "c"),
+            _ptr(h_mont, self.n, "h_mont"), _ptr(h_std, self.n, "h_std"), _stream(stream)),
+            "g16_h_compute_noalloc")
         return h_mont, h_std
 
     def h_compute_batch(self, a, b, c, h_mont=None, h_std=None, scratch=None, stream=None):

@@ -337,9 +337,9 @@ int run_plan(const Launch* ls, uint32_t count, hipStream_t s) {
     return G16_OK;
 }
 
-// Host checks of g16_h_compute / g16_h_stage, then the launch list.
-int plan_h(g16_ctx* ctx, const void* a_mont, const void* b_mont, const void* c_mont,
-           void* h_mont, void* h_std, Launch* ls, uint32_t* count) {
+// Host checks shared by g16_h_compute, g16_h_stage and g16_h_compute_noalloc.
+int check_h(g16_ctx* ctx, const void* a_mont, const void* b_mont, const void* c_mont,
+            void* h_mont, void* h_std) {
     if (!ctx_ok(ctx)) return ctx ? G16_ESTATE : G16_EINVAL;
     if (!a_mont || !b_mont || !c_mont || !h_mont || !h_std) return G16_EINVAL;
     const size_t nbytes = vec_bytes(ctx);
@@ -357,10 +357,56 @@ int plan_h(g16_ctx* ctx, const void* a_mont, const void* b_mont, const void* c_m
         if (!device_range(p, nbytes)) return G16_EINVAL;
     for (const void* p : outs)
         if (!device_range(p, nbytes)) return G16_EINVAL;
+    return G16_OK;
+}
+
+// Host checks of g16_h_compute / g16_h_stage, then the launch list.
+int plan_h(g16_ctx* ctx, const void* a_mont, const void* b_mont, const void* c_mont,
+           void* h_mont, void* h_std, Launch* ls, uint32_t* count) {
+    const int rc = check_h(ctx, a_mont, b_mont, c_mont, h_mont, h_std);
+    if (rc) return rc;
     const size_t n = size_t(1) << ctx->log_n;
     const Fr* srcs[3] = {(const Fr*)a_mont, (const Fr*)b_mont, (const Fr*)c_mont};
     Fr* dsts[3] = {ctx->scratch, ctx->scratch + n, ctx->scratch + 2 * n};
     *count = plan_coset(ctx, srcs, dsts, 3, 1, 0, true, (Fr*)h_mont, (Fr*)h_std, ls);
+    return G16_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- no-allocation variant
+//
+// g16_h_compute_noalloc keeps C' between its launches in this array instead of the
+// context's workspace scratch (A' and B' live in h_mont and h_std until the join
+// overwrites them, as in g16_h_compute_batch), so a call allocates nothing and touches
+// no caller memory beyond its arguments.  Every process that loads the library holds the
+// array on each device it runs on until it exits.  Host code never uses the array's name
+// as an address: the device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[(size_t(1) << G16_NOALLOC_MAX_LOG_N) * 32];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};  // device address of `scratch` on each device
+
+// The array's address on `device`, which must be the current device the first time
+// (g16_h_prepare calls this for the device it prepares on).  G16_EHIP if the runtime
+// cannot resolve it.
+int static_scratch(int device, void** out) {
+    if (device < 0 || device >= kMaxDevices) return G16_EHIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[device]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess || cur != device) return G16_EHIP;
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return G16_EHIP;
+        }
+        g_scratch_ptr[device] = p;
+    }
+    *out = g_scratch_ptr[device];
     return G16_OK;
 }
 
@@ -430,6 +476,12 @@ int g16_h_prepare(uint32_t log_n, void* workspace, size_t workspace_bytes, void*
     c->size_inv_entry = g16::tw29_entry(c->size_inv);
     c->n_batches = plan_batches(log_n, max_batch_k(), c->batch_k);
     c->radix2 = std::getenv("G16_RADIX2") != nullptr;
+    {
+        // the no-allocation entry point's scratch on this device (resolved here, with the
+        // device current; a failure only disables that entry point, which reports it)
+        void* unused = nullptr;
+        (void)static_scratch(c->device, &unused);
+    }
 
     // bits where the plan's batches start (the forward table's layout follows them)
     uint32_t starts = 0, bit = 0;
@@ -527,6 +579,22 @@ int g16_h_compute(g16_ctx* ctx, const void* a_mont, const void* b_mont, const vo
     uint32_t count = 0;
     int rc = plan_h(ctx, a_mont, b_mont, c_mont, h_mont, h_std, ls, &count);
     if (rc) return rc;
+    return run_plan(ls, count, (hipStream_t)stream);
+}
+
+int g16_h_compute_noalloc(g16_ctx* ctx, const void* a_mont, const void* b_mont,
+                          const void* c_mont, void* h_mont, void* h_std, void* stream) {
+    int rc = check_h(ctx, a_mont, b_mont, c_mont, h_mont, h_std);
+    if (rc) return rc;
+    if (ctx->log_n > G16_NOALLOC_MAX_LOG_N) return G16_ENOSPACE;
+    void* scr = nullptr;
+    rc = static_scratch(ctx->device, &scr);
+    if (rc) return rc;
+    const Fr* srcs[3] = {(const Fr*)a_mont, (const Fr*)b_mont, (const Fr*)c_mont};
+    Fr* dsts[3] = {(Fr*)h_mont, (Fr*)h_std, (Fr*)scr};
+    Launch ls[kMaxLaunches];
+    const uint32_t count = plan_coset(ctx, srcs, dsts, 3, 1, uint64_t(1) << ctx->log_n, true,
+                                      (Fr*)h_mont, (Fr*)h_std, ls);
     return run_plan(ls, count, (hipStream_t)stream);
 }
 

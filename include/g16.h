@@ -137,6 +137,21 @@ int g16_coset_eval(g16_ctx* ctx, const void* in_mont, void* out_mont, void* stre
 int g16_h_compute(g16_ctx* ctx, const void* a_mont, const void* b_mont, const void* c_mont,
                   void* h_mont, void* h_std, void* stream);
 
+/* g16_h_compute for callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same results, but the call uses
+ * no workspace scratch and allocates nothing.  A' and B' are kept in h_mont and h_std
+ * until the join overwrites them; C' goes to a device array of the library's own, of
+ * 2^G16_NOALLOC_MAX_LOG_N * 32 bytes (128 MiB), which each device the library runs on
+ * holds until the process ends.  Domains above 2^G16_NOALLOC_MAX_LOG_N are refused with
+ * G16_ENOSPACE before anything is enqueued.  All calls on one device share that array
+ * (it keeps the last call's contents; every element is written before it is read), so
+ * calls that overlap in time on one device race, whatever their contexts and streams.
+ * Arguments and the other errors as g16_h_compute; G16_EHIP also when the array's
+ * device address cannot be resolved. */
+#define G16_NOALLOC_MAX_LOG_N 22u
+int g16_h_compute_noalloc(g16_ctx* ctx, const void* a_mont, const void* b_mont,
+                          const void* c_mont, void* h_mont, void* h_std, void* stream);
+
 /* Several proofs over one domain in one call (the same launches as g16_h_compute,
  * each covering every proof's vectors, so small domains pay the per-launch cost once
  * per batch rather than once per proof; the NTT_CU page's "BATCHING" section counts
