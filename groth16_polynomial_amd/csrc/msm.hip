@@ -1,6 +1,6 @@
 // libg16.so: host side of the G1 multi-scalar multiplication (include/g16.h, "G1 MSM").
 //
-// g16_msm_g1 only enqueues (counting sort, accumulation, merge, window reduction) and
+// g16_msm_g1 only enqueues (counting sort, bucket sums, window reduction) and
 // leaves one XYZZ point per window in the caller's buffer; g16_msm_g1_finish combines
 // them on the host by Horner's rule, as the MSM_CU page does ("THE WINDOW REDUCTION
 // ENDS ON THE HOST").
@@ -22,14 +22,13 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr uint32_t kMaxC = 16;  // a window's counters fit in LDS (2^15 x 4 bytes)
-constexpr uint32_t kSliceLen = 32;     // entries per accumulation thread, at least
 constexpr uint32_t kSegLen = 8;
 constexpr uint32_t kMaxOnesGroups = 1024;  // workgroups of the scalar-one pass, at most
 constexpr uint32_t kBinEntries = 8192;   // entries per coarse bin, about (at most 1024 bins)
 constexpr uint32_t kStage = 9216;        // entries of a bin staged in LDS by the row sort (its
                                          // bins hold ~8192 on average)
 constexpr uint32_t kMinChunk = 8192;     // codes per coarse-sorting workgroup, at least
-constexpr uint32_t kFatGroups = 2048;   // workgroups of the long-run merge, at most
+constexpr uint32_t kMaxLevels = 8;      // levels of the bucket sums (a few suffice)
 
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -42,21 +41,20 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 using g16::device_range;
 
-// Entries per accumulation thread: kSliceLen, doubled while below a bucket's mean run
-// n / 2^(c-1) as long as the windows still give 2^18 threads or more (four waves per
-// SIMD), so that at large n a typical run spans one or two slices instead of many; and
-// halved, down to 4, while the windows give fewer than 2^16 threads (one wave per SIMD),
-// since at small n the time is a thread's chain of dependent additions.  A run over more
-// than eight slices goes to the long-run merge, a workgroup per bucket: the halving stops
-// at a quarter of the mean run unless every bucket fits in one round of that merge.
+// Entries per lane at the bucket sums' first level.  Lanes whose entries all belong to
+// one bucket make the wave join them by a scan of log2 steps, so the lane length grows
+// from 32 toward twice a bucket's mean run n / 2^(c-1), where such lanes become rare, up
+// to 64 and while the windows still give 4096 waves (16 per CU); and it shrinks, down to
+// 2, while they give fewer than 1024 waves, since at small n the time is the chain of
+// dependent additions in a lane.  Measured at c = 16: 2^20 (mean run 32) 32 / 64 / 128
+// entries: 1.77 / 1.67 / 1.74 ms; 2^22 (mean run 128) 64 / 128 / 256 / 512: 6.13 / 6.10 /
+// 6.29 / 6.47 ms.
 uint32_t slice_len_for(uint64_t n, uint32_t c) {
     const uint64_t mean = n >> (c - 1);
     const uint64_t entries = (uint64_t)windows_for(c) * n;
-    const bool one_round = (uint64_t)windows_for(c) << (c - 1) <= kFatGroups;
-    uint32_t len = kSliceLen;
-    while (len < mean && 2u * len <= (entries >> 18) && len < (1u << 16)) len *= 2;
-    while (len > 4u && entries / len < (1u << 16) && (one_round || len / 2u >= mean / 4u))
-        len /= 2;
+    uint32_t len = 32;
+    while (len < 2 * mean && len < 64u && entries / (64u * 2u * len) >= 4096u) len *= 2;
+    while (len > 2u && entries / (64u * len) < 1024u) len /= 2;
     return len;
 }
 
@@ -68,24 +66,15 @@ uint32_t seg_len_for(uint32_t W, uint32_t buckets) {
     return len;
 }
 
-// Window width minimising a cost in point additions: n per window for the accumulation,
-// about one per bucket for the merge and the weighted window sum (much of that work
-// overlaps: measured widths at 2^12 .. 2^22 fit this weight, not three), and the merge of
-// the top window's buckets when their runs are long.  Scalars below r < 2^254 leave the
-// top window only 254 - (W - 1) c bits, so its few buckets hold about n / 2^bits entries
-// each; when such a run spans more than eight slices a workgroup merges the bucket's
-// slice partials, 256 at a time and then by a tree of eight levels, and each of those
-// serial additions is priced at the 16384 additions the chip does in parallel meanwhile.
+// Window width minimising a cost in point additions: n per window for the bucket sums and
+// about one per bucket for the joins and the weighted window sum (much of that work
+// overlaps: measured widths at 2^12 .. 2^22 fit this weight, not three).
 uint32_t model_c(uint64_t n) {
     uint32_t best = 1;
     double best_cost = 0.0;
     for (uint32_t c = 1; c <= kMaxC; ++c) {
         const uint32_t W = windows_for(c);
-        const int top_bits = 254 - (int)((W - 1) * c);
-        const double fat = (double)n / (double)(1ull << (top_bits > 0 ? top_bits : 0));
-        const double slices = fat / (double)slice_len_for(n, c);
-        const double serial = slices > 8.0 ? slices / 256.0 + 8.0 : 0.0;
-        const double cost = (double)W * ((double)n + (double)(1u << (c - 1))) + 16384.0 * serial;
+        const double cost = (double)W * ((double)n + (double)(1u << (c - 1)));
         if (c == 1 || cost < best_cost) {
             best = c;
             best_cost = cost;
@@ -112,8 +101,11 @@ uint32_t default_c(uint64_t n) {
 struct Layout {
     MsmParams mp;
     uint32_t per_group, groups;  // segment sums per partial, partials per window
-    size_t counts, cursor, codes, bin_counts, bin_offs, entries, spill_rows, spill_pts, buckets,
-        seg_out, partials, ones_out, fat, total;
+    uint32_t n_levels;
+    g16::MsmLevel levels[kMaxLevels];
+    size_t item_cap;  // items per ping-pong buffer of the levels above the first
+    size_t counts, cursor, codes, bin_counts, bin_offs, entries, items, buckets, seg_out,
+        partials, ones_out, total;
 };
 
 bool make_layout(uint64_t n, uint32_t c, Layout* L) {
@@ -127,7 +119,26 @@ bool make_layout(uint64_t n, uint32_t c, Layout* L) {
     mp.windows = W;
     mp.buckets = 1u << (c - 1);
     mp.slice_len = slice_len_for(n, c);
-    mp.slices = (uint32_t)((n + mp.slice_len - 1) / mp.slice_len);
+    // the bucket sums' levels: the first over each window's n entries (at most), each
+    // next one over two items per tile of the one below, two items per lane
+    {
+        uint32_t items = (uint32_t)n, len = mp.slice_len, stride = (uint32_t)n;
+        L->n_levels = 0;
+        L->item_cap = 0;
+        for (;;) {
+            if (L->n_levels == kMaxLevels) return false;
+            g16::MsmLevel& lv = L->levels[L->n_levels++];
+            lv.lane_len = len;
+            lv.tiles = (uint32_t)((items + 64ull * len - 1) / (64ull * len));
+            lv.stride = stride;
+            lv.last = lv.tiles == 1u ? 1u : 0u;
+            if (lv.last) break;
+            items = 2u * lv.tiles + 2u;
+            stride = items;
+            len = 2u;
+            L->item_cap = std::max<size_t>(L->item_cap, (size_t)W * items);
+        }
+    }
     mp.seg_len = seg_len_for(W, mp.buckets);
     mp.segs = mp.buckets / mp.seg_len;
     const uint64_t groups = (n + g16::kMsmThreads - 1) / g16::kMsmThreads;
@@ -156,7 +167,6 @@ bool make_layout(uint64_t n, uint32_t c, Layout* L) {
     L->per_group = mp.segs < g16::kMsmThreads ? mp.segs : g16::kMsmThreads;
     L->groups = mp.segs / L->per_group;
     const size_t rows = (size_t)W * mp.buckets;
-    const size_t spills = 2 * (size_t)W * mp.slices;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t at = off;
@@ -169,14 +179,14 @@ bool make_layout(uint64_t n, uint32_t c, Layout* L) {
     L->bin_counts = take((size_t)W * mp.bins * mp.chunks * 4);
     L->bin_offs = take((size_t)W * mp.bins * mp.chunks * 4);
     L->entries = take((size_t)W * n * 8);
-    L->spill_rows = take(spills * 4);
-    // the spill points' area also holds the coarse-sorted entries before the accumulation
-    L->spill_pts = take(std::max(spills * sizeof(g16::P29), (size_t)W * n * 8));
+    // the coarse-sorted entries, then (once the row sort has read them) two buffers of
+    // the upper levels' items, rows then points
+    const size_t item_bytes = 2 * L->item_cap * (4 + sizeof(g16::P29)) + 1024;
+    L->items = take(std::max(item_bytes, (size_t)W * n * 8));
     L->buckets = take(rows * sizeof(g16::P29));
     L->seg_out = take((size_t)W * mp.segs * sizeof(g16::P29));
     L->partials = take((size_t)W * L->groups * sizeof(g16::P29));
     L->ones_out = take((size_t)mp.ones_groups * sizeof(g16::P29));
-    L->fat = take((rows + 1) * 4);  // list length, then the listed rows
     L->total = off;
     return true;
 }
@@ -239,21 +249,24 @@ int g16_msm_g1(uint64_t n, const void* scalars_std, const void* bases_mont, uint
     uint32_t* bin_counts = (uint32_t*)(ws + L.bin_counts);
     uint32_t* bin_offs = (uint32_t*)(ws + L.bin_offs);
     uint2* entries = (uint2*)(ws + L.entries);
-    uint32_t* spill_rows = (uint32_t*)(ws + L.spill_rows);
-    g16::P29* spill_pts = (g16::P29*)(ws + L.spill_pts);
     g16::P29* buckets = (g16::P29*)(ws + L.buckets);
     g16::P29* seg_out = (g16::P29*)(ws + L.seg_out);
     g16::P29* partials = (g16::P29*)(ws + L.partials);
     g16::P29* ones_out = (g16::P29*)(ws + L.ones_out);
-    uint32_t* fat_count = (uint32_t*)(ws + L.fat);
-    uint32_t* fat_rows = fat_count + 1;
     const uint32_t* sc = (const uint32_t*)scalars_std;
     const G1Aff* bases = (const G1Aff*)bases_mont;
-    const uint32_t rows = W * mp.buckets;
     const dim3 blk(g16::kMsmThreads), sort_blk(g16::kMsmSortThreads);
-    // The coarse-sorted entries live in the spill area until the accumulation (the area
-    // holds W n entries of 8 bytes).
-    uint2* binned = (uint2*)spill_pts;
+    // The coarse-sorted entries live in the items area until the row sort has read them
+    // (the area holds W n entries of 8 bytes); then the levels' items take it over.
+    uint2* binned = (uint2*)(ws + L.items);
+    uint32_t* item_rows[2] = {(uint32_t*)(ws + L.items),
+                              (uint32_t*)(ws + L.items) + L.item_cap};
+    g16::P29* item_pts[2];
+    {
+        const size_t pts_at = round_up(2 * L.item_cap * 4);
+        item_pts[0] = (g16::P29*)(ws + L.items + pts_at);
+        item_pts[1] = item_pts[0] + L.item_cap;
+    }
     const size_t count_lds = (size_t)mp.bins * 16;
     const size_t place_lds = (size_t)g16::kMsmRound * 8 + (size_t)mp.bins * 12;
     const size_t row_lds = (size_t)mp.stage * 16 + ((size_t)1 << mp.bin_shift) * 4;
@@ -267,20 +280,30 @@ int g16_msm_g1(uint64_t n, const void* scalars_std, const void* bases_mont, uint
     hipLaunchKernelGGL(g16::msm_bin_count, dim3(W * mp.chunks), bin_blk, count_lds, s,
                        (const uint16_t*)codes, mp, bin_counts);
     hipLaunchKernelGGL(g16::msm_scan, dim3(W), sort_blk, 0, s, (const uint32_t*)bin_counts,
-                       mp.bins * mp.chunks, mp, bin_offs, fat_count);
+                       mp.bins * mp.chunks, mp, bin_offs);
     hipLaunchKernelGGL(g16::msm_bin_place, dim3(W * mp.chunks), bin_blk, place_lds, s,
                        (const uint16_t*)codes, mp, (const uint32_t*)bin_offs, binned);
     hipLaunchKernelGGL(g16::msm_bin_sort, dim3(W * mp.bins), sort_blk, row_lds, s,
                        (const uint2*)binned, (const uint32_t*)bin_counts,
                        (const uint32_t*)bin_offs, mp, counts, cursor, entries);
-    hipLaunchKernelGGL(g16::msm_accumulate, dim3(blocks_for((uint64_t)W * mp.slices)), blk, 0, s,
-                       entries, bases, cursor, mp, buckets, spill_pts, spill_rows);
-    hipLaunchKernelGGL(g16::msm_merge, dim3(blocks_for(rows)), blk, 0, s, counts, cursor,
-                       spill_pts, spill_rows, mp, buckets, fat_count, fat_rows);
-    hipLaunchKernelGGL(g16::msm_merge_fat, dim3(rows < kFatGroups ? rows : kFatGroups), blk, 0, s,
-                       counts, cursor, spill_pts,
-                       spill_rows, mp, (const uint32_t*)fat_count, (const uint32_t*)fat_rows,
-                       buckets);
+    // the bucket sums, level by level (each level's items go to the other buffer)
+    for (uint32_t k = 0; k < L.n_levels; ++k) {
+        const g16::MsmLevel& lv = L.levels[k];
+        const uint32_t blocks = blocks_for((uint64_t)W * lv.tiles * 64u);
+        uint32_t* out_r = item_rows[k & 1u];
+        g16::P29* out_p = item_pts[k & 1u];
+        if (k == 0)
+            hipLaunchKernelGGL(g16::msm_tile_sums<true>, dim3(blocks), blk, 0, s,
+                               (const uint2*)entries, bases, (const uint32_t*)nullptr,
+                               (const g16::P29*)nullptr, (const uint32_t*)cursor, mp, lv,
+                               buckets, out_r, out_p);
+        else
+            hipLaunchKernelGGL(g16::msm_tile_sums<false>, dim3(blocks), blk, 0, s,
+                               (const uint2*)nullptr, bases,
+                               (const uint32_t*)item_rows[(k - 1) & 1u],
+                               (const g16::P29*)item_pts[(k - 1) & 1u], (const uint32_t*)cursor,
+                               mp, lv, buckets, out_r, out_p);
+    }
     hipLaunchKernelGGL(g16::msm_reduce_segments, dim3(blocks_for((uint64_t)W * mp.segs)), blk, 0,
                        s, counts, buckets, mp, seg_out);
     hipLaunchKernelGGL(g16::msm_ones, dim3(mp.ones_groups), blk, 0, s, sc, bases, mp, ones_out);

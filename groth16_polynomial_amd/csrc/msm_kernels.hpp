@@ -7,16 +7,18 @@
 //     separate pass, one mixed addition each;
 //   * a counting sort by bucket (count, prefix-sum per window, scatter point indices
 //     through a cursor), so that no atomic ever touches a point;
-//   * load-balanced accumulation: fixed-length slices of the sorted entries, one thread
-//     each; a run strictly inside a slice is written to its bucket directly, the first
-//     and last run of a slice go to two spill slots, and a merge pass adds each bucket's
-//     spills; XYZZ accumulators with affine bases, the arithmetic of every point kernel
-//     in nine 29-bit digits (fp29.hpp), which is also the form the point kernels pass
-//     to one another (only the bases and the final window sums are canonical);
+//   * load-balanced accumulation: fixed-length runs of the sorted entries per thread, so
+//     that a bucket with many entries is shared by several threads and its parts are
+//     added afterwards; XYZZ accumulators with affine bases, the arithmetic of every point
+//     kernel in nine 29-bit digits (fp29.hpp), which is also the form the point kernels
+//     pass to one another (only the bases and the final window sums are canonical);
 //   * each window reduced to sum_m m B_m on the device; the host combines the windows
 //     by Horner's rule (the page's "THE WINDOW REDUCTION ENDS ON THE HOST").
 //
-// Differences from the page (see the notes at each kernel): the digits are computed once,
+// Differences from the page (see the notes at each kernel): the parts of a bucket shared by
+// several threads are joined inside the wave by shuffles and, across waves, by the same
+// kernel run again on each wave's two boundary parts (a segmented reduction in levels),
+// so there is no per-thread spill and no separate merge pass; the digits are computed once,
 // for all windows of a scalar in one thread (a signed recoding with carries), and stored
 // as 16-bit codes; the counting sort runs in two levels (coarse bins of rows, then rows
 // within a bin) with all its counters in LDS, so its atomics are LDS atomics and none is
@@ -38,8 +40,7 @@ struct MsmParams {
     uint32_t c;          // window width in bits
     uint32_t windows;    // ceil(255 / c)
     uint32_t buckets;    // 2^(c - 1) per window
-    uint32_t slice_len;  // sorted entries per accumulation thread
-    uint32_t slices;     // ceil(n / slice_len) accumulation threads per window
+    uint32_t slice_len;  // sorted entries per lane of the bucket sums' first level
     uint32_t seg_len;    // buckets per reduction thread
     uint32_t segs;       // buckets / seg_len reduction threads per window
     uint32_t ones_groups;  // workgroups of the ones pass
@@ -52,8 +53,6 @@ struct MsmParams {
 };
 
 constexpr uint32_t kMsmNoRow = 0xffffffffu;
-// A bucket whose run spans more slices than this is merged by a workgroup of its own.
-constexpr uint32_t kMsmFatSlices = 8;
 constexpr uint32_t kMsmThreads = 256;
 constexpr uint32_t kMsmSortThreads = 1024;
 
@@ -109,7 +108,7 @@ __device__ __forceinline__ void msm_st_xyzz(G1Xyzz* p, const G1Xyzz& a) {
     msm_st_fp(&p->zzz, a.zzz);
 }
 
-// A point as the point kernels pass it to one another (bucket partials, spills, segment and
+// A point as the point kernels pass it to one another (bucket partials, level items, segment and
 // group sums): the nine-digit form itself, 144 bytes (nine 16-byte words), lazily reduced
 // (bounds in fp29.hpp: a sum of two such points forms smaller values than a converted
 // base does), so neither side converts; infinity stays all-zero digits.  Only the window
@@ -276,11 +275,9 @@ __global__ void __launch_bounds__(kMsmBinThreads) msm_bin_count(const uint16_t* 
 // window: each thread sums a contiguous range, the range sums are scanned in LDS, then
 // each thread writes its range's starts.
 __global__ void __launch_bounds__(kMsmSortThreads) msm_scan(const uint32_t* counts, uint32_t len,
-                                                            MsmParams mp, uint32_t* cursor,
-                                                            uint32_t* fat_count) {
+                                                            MsmParams mp, uint32_t* cursor) {
     __shared__ uint32_t sums[kMsmSortThreads];
     const uint32_t w = blockIdx.x, t = threadIdx.x;
-    if (w == 0 && t == 0) *fat_count = 0u;  // the merge pass appends to the list again
     const uint32_t per = (len + kMsmSortThreads - 1u) / kMsmSortThreads;
     const uint32_t b0 = t * per;
     const uint32_t b1 = b0 + per < len ? b0 + per : len;
@@ -469,131 +466,165 @@ __device__ __forceinline__ uint32_t msm_used(const uint32_t* cursor, const MsmPa
     return cursor[(size_t)w * mp.buckets + mp.buckets - 1u] - w * mp.n;
 }
 
-// Pass 5: one thread per slice of slice_len sorted entries of one window.  A run that
-// neither contains the slice's first entry nor reaches its end is complete here and is
-// written to its bucket; the first run goes to the head spill slot and the run still
-// open at the slice's end to the tail slot (a slice holding one run spills once).
-__global__ void __launch_bounds__(kMsmThreads) msm_accumulate(const uint2* entries,
-                                                              const G1Aff* bases,
-                                                              const uint32_t* cursor, MsmParams mp,
-                                                              P29* buckets, P29* spill_pts,
-                                                              uint32_t* spill_rows) {
-    const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
-    const uint32_t w = gid / mp.slices;
-    if (w >= mp.windows) return;
-    const uint32_t s = gid - w * mp.slices;
-    const uint32_t head = 2u * gid, tail = head + 1u;
-    spill_rows[head] = kMsmNoRow;
-    spill_rows[tail] = kMsmNoRow;
-    const uint32_t used = msm_used(cursor, mp, w);
-    const uint32_t lo = s * mp.slice_len;
-    if (lo >= used) return;
-    const uint32_t hi = lo + mp.slice_len < used ? lo + mp.slice_len : used;
-    const uint2* ew = entries + (size_t)w * mp.n;
-    uint32_t cur = ew[lo].x;
-    bool first = true;
+// Pass 6: the bucket sums, as a segmented reduction over each window's row-sorted items
+// (an item is a row and a point: an entry and its signed base at level 0, a partial
+// bucket sum at the levels above), in tiles of one wave each.
+//
+// A tile is 64 lane_len consecutive items of one window; lane l takes lane_len of them
+// and adds up each run of equal rows it sees.  A run that begins and ends inside the
+// lane's items is a whole bucket and is stored right away.  What is left per lane is
+// its first run (which may have begun in lanes to its left) and its last run (which may
+// go on in lanes to its right), or one run when all its items share a row.  The wave
+// then joins those pieces across lanes by shuffles:
+//   * a lane whose items are all one row takes over the sum of the run from the lanes to
+//     its left whenever their last row is its row: a segmented inclusive scan over the
+//     lanes (steps of 1, 2, 4, ...; the wave stops as soon as no lane still waits), so a
+//     run over m lanes costs log2 m additions, and none when no lane is covered by a
+//     single run;
+//   * every other lane adds its left neighbour's running sum to its first run when the
+//     rows match, which completes that run.
+// Each completed run is stored to its bucket, except the tile's first and last runs,
+// which may continue in the neighbouring tiles: those two go up as the tile's two items
+// of the next level (a tile that is one run sends one item and a blank), and the next
+// level runs this same kernel on them, with fewer tiles, until a window's items fit in
+// one tile and nothing goes up.  Every row with entries is thus stored exactly once, by
+// the level and lane where its run is complete; buckets without entries are never
+// written (the window sums read the counts).
+//
+// Items of the levels above the first come two per tile of the level below: the tile's
+// first run at index 2t + 1 and its last at 2t + 2 of the window's stride (index 0 and
+// the last index are blanks), so that the pair most likely to be one bucket, the last
+// run of tile t and the first of tile t + 1, falls on one even-aligned pair and, with an
+// even lane_len, inside one lane.  A blank (kMsmNoRow) is skipped by the lanes; blanks
+// come from single-run tiles (their second item) and from empty tiles past a window's
+// entries, so a lane without any row is never followed by one with rows.
+struct MsmLevel {
+    uint32_t lane_len;  // items per lane (even above the first level)
+    uint32_t tiles;     // tiles per window
+    uint32_t stride;    // items per window in the item arrays (level 0: n)
+    uint32_t last;      // 1: each window's items fit in one tile; nothing goes up
+};
+
+__device__ __forceinline__ P29 msm_shfl_up(const P29& a, uint32_t d) {
+    P29 r;
+    const int32_t* s = reinterpret_cast<const int32_t*>(&a);
+    int32_t* o = reinterpret_cast<int32_t*>(&r);
+#pragma unroll
+    for (int i = 0; i < 36; ++i) o[i] = __shfl_up(s[i], d, 64);
+    return r;
+}
+
+template <bool BASES>
+__global__ void __launch_bounds__(kMsmThreads, 4) msm_tile_sums(const uint2* entries,
+                                                             const G1Aff* bases,
+                                                             const uint32_t* in_rows,
+                                                             const P29* in_pts,
+                                                             const uint32_t* cursor,
+                                                             MsmParams mp, MsmLevel lv,
+                                                             P29* buckets, uint32_t* out_rows,
+                                                             P29* out_pts) {
+    __shared__ P29 first_run[kMsmThreads];  // each lane's first run, until the joins
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = (blockIdx.x * kMsmThreads + threadIdx.x) >> 6;
+    const uint32_t w = wave / lv.tiles;
+    if (w >= mp.windows) return;  // whole waves: the grid is a whole number of waves
+    const uint32_t t = wave - w * lv.tiles;
+    const uint32_t count = BASES ? msm_used(cursor, mp, w) : lv.stride;
+    const uint32_t start = (t * 64u + lane) * lv.lane_len;
+    const uint32_t lo = start < count ? start : count;
+    const uint32_t hi = lo + lv.lane_len < count ? lo + lv.lane_len : count;
+    const size_t base = (size_t)w * lv.stride;
+
+    // ---- the lane's items: runs inside the lane are stored, the first one is kept
+    uint32_t first = kMsmNoRow, cur = kMsmNoRow;
     XyzzT<Fp29> acc = xyzz_zero<Fp29>();
     for (uint32_t e = lo; e < hi; ++e) {
-        const uint2 ent = ew[e];
-        if (ent.x != cur) {
-            if (first) {
-                spill_rows[head] = cur;
-                msm_st_p29(spill_pts + head, acc);
-                first = false;
-            } else {
-                msm_st_p29(buckets + cur, acc);
-            }
-            acc = xyzz_zero<Fp29>();
-            cur = ent.x;
+        uint32_t row;
+        uint2 ent;
+        if constexpr (BASES) {
+            ent = entries[base + e];
+            row = ent.x;
+        } else {
+            row = in_rows[base + e];
+            if (row == kMsmNoRow) continue;
         }
-        AffT<Fp29> b = aff_to29(msm_ld_aff(bases + (ent.y >> 1)));
-        if (ent.y & 1u) b.y = fp29_neg(b.y);
-        acc = xyzz_madd(acc, b);
+        if (row != cur) {
+            if (cur == first && cur != kMsmNoRow) first_run[threadIdx.x] = acc;
+            else if (cur != kMsmNoRow) msm_st_p29(buckets + cur, acc);
+            if (first == kMsmNoRow) first = row;
+            acc = xyzz_zero<Fp29>();
+            cur = row;
+        }
+        if constexpr (BASES) {
+            AffT<Fp29> b = aff_to29(msm_ld_aff(bases + (ent.y >> 1)));
+            if (ent.y & 1u) b.y = fp29_neg(b.y);
+            acc = xyzz_madd(acc, b);
+        } else {
+            acc = xyzz_add(acc, msm_ld_p29(in_pts + base + e));
+        }
     }
-    const uint32_t slot = first ? head : tail;
-    spill_rows[slot] = cur;
-    msm_st_p29(spill_pts + slot, acc);
-}
+    const uint32_t last = cur;  // acc: the lane's last run (its only one when single)
+    const bool active = first != kMsmNoRow;
+    const bool single = active && first == last;
 
-// Pass 6: one thread per bucket row with entries.  Starts from the direct write when
-// the run lies strictly inside one slice (the accumulation wrote it), else from
-// infinity, and adds the spills of the slices the run overlaps.  A run over more than
-// kMsmFatSlices slices (many equal digits: repeated scalars, or the few buckets of a
-// narrow top window) is appended to a list for msm_merge_fat instead, so that no thread
-// adds thousands of spills one after another.
-__global__ void __launch_bounds__(kMsmThreads) msm_merge(const uint32_t* counts,
-                                                         const uint32_t* cursor,
-                                                         const P29* spill_pts,
-                                                         const uint32_t* spill_rows, MsmParams mp,
-                                                         P29* buckets, uint32_t* fat_count,
-                                                         uint32_t* fat_rows) {
-    const uint32_t row = blockIdx.x * blockDim.x + threadIdx.x;
-    if (row >= mp.windows * mp.buckets) return;
-    const uint32_t cnt = counts[row];
-    if (cnt == 0u) return;
-    const uint32_t w = row / mp.buckets;
-    const uint32_t used = msm_used(cursor, mp, w);
-    const uint32_t end = cursor[row] - w * mp.n;
-    const uint32_t start = end - cnt;
-    const uint32_t k_lo = start / mp.slice_len, k_hi = (end - 1u) / mp.slice_len;
-    if (k_hi - k_lo >= kMsmFatSlices) {
-        fat_rows[atomicAdd(fat_count, 1u)] = row;
+    // ---- the tile's rows at both ends, the neighbours' rows
+    const uint64_t act = __ballot(active);
+    const size_t slot = (size_t)w * (2u * lv.tiles + 2u) + 2u * t;  // next level's items
+    if (act == 0u) {  // an empty tile (past the window's entries): blanks go up
+        if (!lv.last && lane == 0) {
+            out_rows[slot + 1u] = kMsmNoRow;
+            out_rows[slot + 2u] = kMsmNoRow;
+            if (t == 0) out_rows[slot] = kMsmNoRow;
+            if (t + 1u == lv.tiles) out_rows[slot + 3u] = kMsmNoRow;
+        }
         return;
     }
-    const uint32_t slice_lo = k_lo * mp.slice_len;
-    const uint32_t slice_hi = slice_lo + mp.slice_len < used ? slice_lo + mp.slice_len : used;
-    const bool direct = k_lo == k_hi && start > slice_lo && end < slice_hi;
-    XyzzT<Fp29> acc = direct ? msm_ld_p29(buckets + row) : xyzz_zero<Fp29>();
-    for (uint32_t k = k_lo; k <= k_hi; ++k) {
-        const uint32_t slot = 2u * (w * mp.slices + k);
-        if (spill_rows[slot] == row) acc = xyzz_add(acc, msm_ld_p29(spill_pts + slot));
-        if (spill_rows[slot + 1u] == row)
-            acc = xyzz_add(acc, msm_ld_p29(spill_pts + slot + 1u));
+    const uint32_t head_lane = (uint32_t)__builtin_ctzll(act);
+    const uint32_t tail_lane = 63u - (uint32_t)__builtin_clzll(act);
+    const uint32_t head_row = __shfl(first, head_lane, 64);
+    const uint32_t tail_row = __shfl(last, tail_lane, 64);
+    const uint32_t prev_last = __shfl_up(last, 1u, 64);
+    const uint32_t next_first = __shfl_down(first, 1u, 64);
+    if (!lv.last && lane == 0) {  // the blanks at both ends of the window's item list
+        if (t == 0) out_rows[slot] = kMsmNoRow;
+        if (t + 1u == lv.tiles) out_rows[slot + 3u] = kMsmNoRow;
     }
-    msm_st_p29(buckets + row, acc);
-}
 
-// Pass 6b: the listed rows, one workgroup at a time (a grid-stride loop over the list,
-// whose length every thread reads once before the loop, so all reach every barrier):
-// the threads take the run's slices in turn, each adding the spills that carry the row,
-// then a tree in LDS over the threads that took one.  Such a run spans at least two
-// slices, so the accumulation never wrote its bucket directly.
-__global__ void __launch_bounds__(kMsmThreads) msm_merge_fat(const uint32_t* counts,
-                                                             const uint32_t* cursor,
-                                                             const P29* spill_pts,
-                                                             const uint32_t* spill_rows,
-                                                             MsmParams mp,
-                                                             const uint32_t* fat_count,
-                                                             const uint32_t* fat_rows,
-                                                             P29* buckets) {
-    __shared__ XyzzT<Fp29> sh[kMsmThreads];
-    const uint32_t t = threadIdx.x;
-    const uint32_t listed = *fat_count;
-    for (uint32_t i = blockIdx.x; i < listed; i += gridDim.x) {
-        const uint32_t row = fat_rows[i];
-        const uint32_t w = row / mp.buckets;
-        const uint32_t end = cursor[row] - w * mp.n;
-        const uint32_t start = end - counts[row];
-        const uint32_t k_lo = start / mp.slice_len, k_hi = (end - 1u) / mp.slice_len;
-        XyzzT<Fp29> acc = xyzz_zero<Fp29>();
-        for (uint32_t k = k_lo + t; k <= k_hi; k += kMsmThreads) {
-            const uint32_t slot = 2u * (w * mp.slices + k);
-            if (spill_rows[slot] == row) acc = xyzz_add(acc, msm_ld_p29(spill_pts + slot));
-            if (spill_rows[slot + 1u] == row)
-                acc = xyzz_add(acc, msm_ld_p29(spill_pts + slot + 1u));
+    // ---- single lanes take over the running sum from their left
+    bool wait = single && lane > 0 && prev_last == first;
+    for (uint32_t d = 1; d < 64u && __any(wait); d <<= 1) {
+        const XyzzT<Fp29> left = msm_shfl_up(acc, d);
+        const bool left_wait = __shfl_up((int)wait, d, 64) != 0;
+        if (wait && lane >= d) {
+            acc = xyzz_add(left, acc);
+            wait = left_wait;
         }
-        sh[t] = acc;
-        // the tree spans the threads that took a slice (the same bound in every thread)
-        const uint32_t used = k_hi - k_lo + 1u < kMsmThreads ? k_hi - k_lo + 1u : kMsmThreads;
-        uint32_t top = 1;
-        while (top < used) top *= 2;
-        for (uint32_t s = top / 2; s > 0; s >>= 1) {
-            __syncthreads();
-            if (t < s) sh[t] = xyzz_add(sh[t], sh[t + s]);
+    }
+    const XyzzT<Fp29> carry = msm_shfl_up(acc, 1u);  // the left lane's running sum
+
+    // ---- completed runs: to the bucket, or up as the tile's first or last item
+    auto put = [&](uint32_t row, const XyzzT<Fp29>& p, bool tail_run) {
+        if (lv.last) {
+            msm_st_p29(buckets + row, p);
+        } else if (row == head_row) {
+            out_rows[slot + 1u] = row;
+            msm_st_p29(out_pts + slot + 1u, p);
+            if (tail_run) out_rows[slot + 2u] = kMsmNoRow;  // the whole tile was one run
+        } else if (tail_run) {
+            out_rows[slot + 2u] = row;
+            msm_st_p29(out_pts + slot + 2u, p);
+        } else {
+            msm_st_p29(buckets + row, p);
         }
-        __syncthreads();
-        if (t == 0) msm_st_p29(buckets + row, sh[0]);
-        __syncthreads();  // sh is reused by the next listed row
+    };
+    // the last run, unless the next lane goes on with it
+    if (active && !(lane < tail_lane && next_first == last)) put(last, acc, lane == tail_lane);
+    // the first run of a lane with more than one run, with the left lane's sum when the
+    // rows match
+    if (active && !single) {
+        XyzzT<Fp29> f = first_run[threadIdx.x];
+        if (lane > 0 && prev_last == first) f = xyzz_add(carry, f);
+        put(first, f, false);
     }
 }
 

@@ -153,17 +153,24 @@ def test_msm_large_by_linearity(log_n, c):
     assert np.array_equal(got, want)
 
 
-@pytest.mark.parametrize("case", ["all_equal", "mixed", "narrow_windows"])
+@pytest.mark.parametrize("case", ["all_equal", "mixed", "narrow_windows", "all_equal_large",
+                                  "two_values_large"])
 def test_msm_long_runs(case):
-    """Buckets with runs over many slices (merged by a workgroup each): every scalar
-    equal, a third of them equal to one value and a fifth to another, and uniform scalars
-    with 6-bit windows (32 buckets of ~1000 entries per window)."""
-    n = 1 << 15 if case != "all_equal" else 1 << 14
+    """Buckets whose runs cover many lanes and many tiles (joined by the in-wave scan and
+    by the upper levels of the bucket sums): every scalar equal, a third of them equal to
+    one value and a fifth to another, uniform scalars with 6-bit windows (32 buckets of
+    ~1000 entries per window), and at 2^18 every scalar equal (each window one run over
+    every tile, three levels) or one of two values."""
+    n = {"all_equal": 1 << 14, "all_equal_large": 1 << 18,
+         "two_values_large": 1 << 18}.get(case, 1 << 15)
     say("msm long runs: %s n=%d" % (case, n))
     s = synth.uniform_fr(400, n)
     k = synth.uniform_fr(401, n)
-    if case == "all_equal":
+    if case in ("all_equal", "all_equal_large"):
         k[:] = k[0]
+    elif case == "two_values_large":
+        k[0::2] = k[0]
+        k[1::2] = k[1]
     elif case == "mixed":
         k[: n // 3] = k[0]
         k[n // 3: n // 3 + n // 5] = k[1]
