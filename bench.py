@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-side", action="store_true",
                     help="only the timed 2^log_n pipeline and its stages (for profiling)")
+    ap.add_argument("--part", choices=("all", "h", "msm"), default="all",
+                    help="h: only the timed pipeline and its stages (as --no-side, no CPU "
+                         "baseline); msm: only the G1 MSM legs (for profiling)")
     ap.add_argument("--stage-reps", type=int, default=10)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (a known-size "
@@ -95,17 +98,22 @@ def mads(muls: int, redc: int) -> int:
     return muls * MADS_PER_MUL + redc * MADS_PER_REDC
 
 
-def stage_list(plan, n_vec=3):
-    """(kind, join, n_vec, k) of each stage of g16_h_compute, in launch order."""
+def stage_list(plan, count, n_vec=3):
+    """(kind, join, n_vec, k) of each stage of g16_h_compute, in launch order; `count` is
+    the library's stage count, which tells whether the last forward batch runs A, B and C
+    in one launch (with the join) or C in a launch of its own."""
     nb = len(plan)
     out = []
     if nb == 1:
         return [("fused", False, 2, plan[0]), ("fused", True, 1, plan[0])]
+    merged = count == 2 * (nb - 1) + 1
     for b in range(nb - 1, 0, -1):
         out.append(("inv", False, n_vec, plan[b]))
     out.append(("fused", False, n_vec, plan[0]))
     for b in range(1, nb):
-        if b == nb - 1:
+        if b == nb - 1 and merged:
+            out.append(("fwd", True, n_vec, plan[b]))
+        elif b == nb - 1:
             out.append(("fwd", False, n_vec - 1, plan[b]))
             out.append(("fwd", True, 1, plan[b]))
         else:
@@ -212,12 +220,13 @@ def gbfly(log_n, transforms, ms):
 
 def probe_rates(log):
     """The issue rate of the arithmetic's instructions: v_mad_i64_i32 (the transforms'
-    digit products), v_mad_u64_u32, v_add_u32 and v_mul_lo_u32; 2048 workgroups of 256
-    lanes (eight per CU), 4096 rounds of eight chains each."""
+    digit products), v_mad_u64_u32, v_add_u32, v_mul_lo_u32, v_ashrrev_i64 (the digit
+    products' carries) and v_alignbit_b32; 2048 workgroups of 256 lanes (eight per CU),
+    4096 (1024 for the multiply and the shift) rounds of eight chains each."""
     from groth16_polynomial_amd import probe
     out = {}
-    for op in (1, 0, 2, 3):
-        r = probe.run(op, blocks=2048, iters=4096 if op != 3 else 1024)
+    for op in (1, 0, 2, 3, 4, 5):
+        r = probe.run(op, blocks=2048, iters=4096 if op not in (3, 4) else 1024)
         if not r["results_match"]:
             raise RuntimeError("probe %s: lane results differ from the host's" % r["op"])
         out[r["op"]] = {"t_lane_ops_s": round(r["lane_ops_per_s_t"], 3),
@@ -227,8 +236,58 @@ def probe_rates(log):
     return out
 
 
+def hs_of(ctx, ad, bd, cd, hm, hs):
+    """h_std of the timed pipeline (the MSM's input in a prover)."""
+    ctx.h_compute(ad, bd, cd, hm, hs)
+    return hs
+
+
+def msm_leg(g, synth, torch, tm, hs, log_n, steps, log):
+    """The H MSM: sum_i h_i P_i over G1 on the pipeline's own h_std, with synthetic bases
+    (multiples s_i G of the generator stand in for the proving key's points); then the
+    same call at 2^12, 2^16 and 2^22 on uniform scalars k_i over bases k_i G."""
+    n = 1 << log_n
+    bases = g.g1_generator_mul(g.to_device(synth.uniform_fr(7, n)))
+    mctx = g.MsmG1(n)
+    msm_reps = max(1, steps // 4)
+    msm_ms = tm.mean_ms(lambda: mctx.window_sums(hs, bases), msm_reps, warm=2)
+    sums_host = g.to_host(mctx.sums).reshape(mctx.windows, 32)
+    t_fin = time.perf_counter()
+    for _ in range(10):
+        mctx.finish(sums_host)
+    finish_ms = (time.perf_counter() - t_fin) / 10 * 1e3
+    line = {
+        "workload": "G1 MSM of h_std at n=2^%d, bases s_i G (synthetic)" % log_n,
+        "window_bits": mctx.c,
+        "windows": mctx.windows,
+        "device_ms": round(msm_ms, 4),
+        "host_finish_ms": round(finish_ms, 4),
+        "bucket_adds_per_s_g": round(n * mctx.windows / (msm_ms / 1e3) / 1e9, 3),
+    }
+    del bases, mctx
+    if log_n == 20:
+        sizes = {}
+        for lg in (12, 16, 22):
+            m = 1 << lg
+            ks = g.to_device(synth.uniform_fr(8, m))
+            mb = g.g1_generator_mul(ks)
+            mc = g.MsmG1(m)
+            t_ms = tm.mean_ms(lambda: mc.window_sums(ks, mb), 5, warm=2)
+            sizes["2^%d" % lg] = {"window_bits": mc.c, "device_ms": round(t_ms, 4),
+                                  "bucket_adds_per_s_g":
+                                      round(m * mc.windows / (t_ms / 1e3) / 1e9, 3)}
+            del ks, mb, mc
+        torch.cuda.empty_cache()
+        line["other_sizes"] = sizes
+    log("msm: %s" % line)
+    return line
+
+
 def main():
     args = parse()
+    if args.part == "h":
+        args.no_side = True
+        args.no_cpu_baseline = True
     if args.gpus != 1:
         print("bench.py: the library runs on one GPU (--gpus %d requested); sharding "
               "across GPUs is designed but not implemented"
@@ -261,6 +320,11 @@ def main():
     tm = Timer(torch)
     torch.cuda.synchronize()
     line_extra = {}
+    if args.part == "msm":
+        print(json.dumps({"msm_g1": msm_leg(g, synth, torch, tm, hs_of(ctx, ad, bd, cd, hm, hs),
+                                            log_n, args.steps, log)}), flush=True)
+        ctx.release()
+        return
 
     # The side measurements run first: they also bring the chip to its steady clock,
     # which the first ~20 ms of sustained load does not run at.
@@ -414,12 +478,12 @@ def main():
     butterflies = 6 * (n // 2) * log_n
     p_muls, p_redc, p_bytes = pipeline_work(log_n)
     p_mads = mads(p_muls, p_redc)
-    stages = stage_list(plan)
+    count = ctx.stage_count()
+    stages = stage_list(plan, count)
+    assert count == len(stages)
     assert sum(stage_work(*st, n)[0] for st in stages) == p_muls
 
     # ---- each stage alone, HIP events on the launch stream
-    count = ctx.stage_count()
-    assert count == len(stages)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(count)]
     acc = [0.0] * count
@@ -447,42 +511,7 @@ def main():
 
     msm_line = None
     if not args.no_side:
-        # ---- the H MSM: sum_i h_i P_i over G1 on the pipeline's own h_std, with synthetic
-        # bases (multiples s_i G of the generator stand in for the proving key's points)
-        bases = g.g1_generator_mul(g.to_device(synth.uniform_fr(7, n)))
-        mctx = g.MsmG1(n)
-        msm_reps = max(1, args.steps // 4)
-        msm_ms = tm.mean_ms(lambda: mctx.window_sums(hs, bases), msm_reps, warm=2)
-        sums_host = g.to_host(mctx.sums).reshape(mctx.windows, 32)
-        t_fin = time.perf_counter()
-        for _ in range(10):
-            mctx.finish(sums_host)
-        finish_ms = (time.perf_counter() - t_fin) / 10 * 1e3
-        msm_line = {
-            "workload": "G1 MSM of h_std at n=2^%d, bases s_i G (synthetic)" % log_n,
-            "window_bits": mctx.c,
-            "windows": mctx.windows,
-            "device_ms": round(msm_ms, 4),
-            "host_finish_ms": round(finish_ms, 4),
-            "bucket_adds_per_s_g": round(n * mctx.windows / (msm_ms / 1e3) / 1e9, 3),
-        }
-        del bases, mctx
-        # the same MSM at other sizes (default widths), uniform scalars k_i over bases k_i G
-        if log_n == 20:
-            sizes = {}
-            for lg in (12, 16, 22):
-                m = 1 << lg
-                ks = g.to_device(synth.uniform_fr(8, m))
-                mb = g.g1_generator_mul(ks)
-                mc = g.MsmG1(m)
-                t_ms = tm.mean_ms(lambda: mc.window_sums(ks, mb), 5, warm=2)
-                sizes["2^%d" % lg] = {"window_bits": mc.c, "device_ms": round(t_ms, 4),
-                                      "bucket_adds_per_s_g":
-                                          round(m * mc.windows / (t_ms / 1e3) / 1e9, 3)}
-                del ks, mb, mc
-            torch.cuda.empty_cache()
-            msm_line["other_sizes"] = sizes
-        log("msm: %s" % msm_line)
+        msm_line = msm_leg(g, synth, torch, tm, hs, log_n, args.steps, log)
 
     dom = int(np.argmax(stage_ms))
     d_muls, d_redc, d_bytes = stage_work(*stages[dom], n)

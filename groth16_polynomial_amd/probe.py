@@ -17,7 +17,8 @@ import numpy as np
 _PKG = os.path.dirname(os.path.abspath(__file__))
 PROBE_PATH = os.path.join(_PKG, "libg16_probe.so")
 
-OPS = {0: "v_mad_u64_u32", 1: "v_mad_i64_i32", 2: "v_add_u32", 3: "v_mul_lo_u32"}
+OPS = {0: "v_mad_u64_u32", 1: "v_mad_i64_i32", 2: "v_add_u32", 3: "v_mul_lo_u32",
+       4: "v_ashrrev_i64", 5: "v_alignbit_b32"}
 CHAINS = 8
 LANES = 256           # per workgroup
 WAVES_PER_GROUP = 4
@@ -58,6 +59,16 @@ def expected(op: int, blocks: int, iters: int, seed: int) -> np.ndarray:
                     ys = np.int64(np.uint32(seed | 1).astype(np.int32))
                     prod = (xs * ys).astype(np.uint64)
                 a = a + np.uint64(iters) * prod
+            elif op == 4:  # arithmetic shift right by x & 63, iters times: by the sum,
+                # capped at 63 (the sign fills everything from there on)
+                a = ((gid + np.uint64(k)) * np.uint64(0x9E3779B97F4A7C15)).view(np.int64)
+                sh = np.minimum((x & np.uint64(63)) * np.uint64(iters), np.uint64(63))
+                a = (a >> sh.astype(np.int64)).view(np.uint64)
+            elif op == 5:  # a = low 32 bits of (a:x) >> 29 = (a << 3) | (x >> 29); after
+                # 11 rounds every starting bit has left and a repeats x's top three bits
+                a = (((gid + np.uint64(k)) * np.uint64(0x9E3779B9)) | np.uint64(1)) & np.uint64(M32)
+                for _ in range(min(iters, 11)):
+                    a = ((a << np.uint64(3)) | (x >> np.uint64(29))) & np.uint64(M32)
             elif op == 2:
                 a = (((gid + np.uint64(k)) * np.uint64(0x9E3779B9)) | np.uint64(1)) & np.uint64(M32)
                 a = (a + np.uint64(iters) * x) & np.uint64(M32)

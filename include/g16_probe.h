@@ -21,9 +21,11 @@ extern "C" {
  *   1 v_mad_i64_i32  the same, signed operands
  *   2 v_add_u32      a = x + a
  *   3 v_mul_lo_u32   a = x * a (low 32 bits)
+ *   4 v_ashrrev_i64  a = a >> (x & 63) (64-bit accumulator, arithmetic shift)
+ *   5 v_alignbit_b32 a = low 32 bits of ((a << 32 | x) >> 29)
  * with x = (lane id * 2654435761) ^ seed and y = seed | 1 (a lane's chain k starts from
  * (lane id + k) * 0x9e3779b97f4a7c15 for the 64-bit ops, (lane id + k) * 0x9e3779b9 | 1 for
- * the 32-bit ones).  Writes the xor of the lane's eight chains to out[lane] (u64, device,
+ * the 32-bit ones; op 4 starts as ops 0 and 1).  Writes the xor of the lane's eight chains to out[lane] (u64, device,
  * blocks * 256 entries) and, per wave w, the elapsed s_memtime and s_memrealtime counts to
  * clocks[2w], clocks[2w + 1] (u64, device, blocks * 8 entries).  Returns 0, -1 for a bad op,
  * a null pointer or zero blocks, -5 for a launch error. */

@@ -9,7 +9,7 @@ from groth16_polynomial_amd import probe
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("op", [0, 1, 2, 3])
+@pytest.mark.parametrize("op", [0, 1, 2, 3, 4, 5])
 def test_probe_chains_match_host(op):
     import torch
     assert torch.cuda.is_available()
