@@ -57,6 +57,13 @@ SIGNATURES = {
     "g16_msm_g1": (_I, [_U64, _P, _P, _U32, _P, _SZ, _P, _P]),
     "g16_msm_g1_finish": (_I, [_U32, _P, _P]),
     "g16_g1_generator_mul": (_I, [_U64, _P, _P, _P]),
+    "g16_bb_workspace_bytes": (_SZ, [_U32]),
+    "g16_bb_batch_plan": (_I, [_U32, _P, _U32]),
+    "g16_bb_prepare": (_I, [_U32, _P, _SZ, _P, ctypes.POINTER(_P)]),
+    "g16_bb_release": (_I, [_P]),
+    "g16_bb_lde": (_I, [_P, _U32, _U32, _U64, _P, _P, _P]),
+    "g16_bb_to_mont": (_I, [_U64, _P, _P, _P]),
+    "g16_bb_from_mont": (_I, [_U64, _P, _P, _P]),
 }
 
 _lib = None
@@ -406,3 +413,100 @@ class MsmG1:
         """The whole MSM (synchronises the stream to read the window sums back)."""
         sums = self.window_sums(scalars, bases, stream)
         return self.finish(to_host(sums).reshape(self.windows, 32))
+
+
+# ------------------------------------------------------------------ BabyBear transform
+
+def bb_batch_plan(log_n: int) -> list:
+    ks = (ctypes.c_uint32 * 8)()
+    rc = load().g16_bb_batch_plan(log_n, ks, 8)
+    if rc < 0:
+        raise G16Error(rc, "g16_bb_batch_plan")
+    return list(ks[:rc])
+
+
+def bb_to_device(words: np.ndarray, device=None):
+    """uint32 numpy array -> int32 GPU tensor with the same bytes."""
+    torch = _torch()
+    a = np.ascontiguousarray(words, dtype=np.uint32).reshape(-1)
+    return torch.from_numpy(a.view(np.int32).copy()).to(device or "cuda")
+
+
+def bb_to_host(t) -> np.ndarray:
+    return t.detach().contiguous().view(_torch().int32).reshape(-1).cpu().numpy().view(np.uint32)
+
+
+def _bb_words(t, what):
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous GPU tensor" % what)
+    nbytes = t.numel() * t.element_size()
+    if nbytes % 4:
+        raise ValueError("%s is not a whole number of 32-bit words" % what)
+    return nbytes // 4
+
+
+def bb_to_mont(x, out=None, stream=None):
+    n = _bb_words(x, "x")
+    out = _torch().empty_like(x) if out is None else out
+    _check(load().g16_bb_to_mont(n, x.data_ptr(), out.data_ptr(), _stream(stream)),
+           "g16_bb_to_mont")
+    return out
+
+
+def bb_from_mont(x, out=None, stream=None):
+    n = _bb_words(x, "x")
+    out = _torch().empty_like(x) if out is None else out
+    _check(load().g16_bb_from_mont(n, x.data_ptr(), out.data_ptr(), _stream(stream)),
+           "g16_bb_from_mont")
+    return out
+
+
+class BbContext:
+    """A prepared 2^log_n BabyBear domain: the twiddle levels in a torch-owned workspace."""
+
+    def __init__(self, log_n: int, device=None, stream=None):
+        torch = _torch()
+        self.log_n = log_n
+        nbytes = load().g16_bb_workspace_bytes(log_n)
+        if nbytes == 0:
+            _check(G16_ERANGE, "g16_bb_workspace_bytes")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device or "cuda")
+        ctx = ctypes.c_void_p()
+        _check(load().g16_bb_prepare(log_n, self.workspace.data_ptr(), nbytes, _stream(stream),
+                                     ctypes.byref(ctx)), "g16_bb_prepare")
+        self._ctx = ctx
+
+    @property
+    def handle(self) -> int:
+        if self._ctx is None or not self._ctx.value:
+            raise RuntimeError("context released")
+        return self._ctx.value
+
+    def release(self):
+        if self._ctx is not None and self._ctx.value:
+            _check(load().g16_bb_release(self._ctx), "g16_bb_release")
+        self._ctx = None
+
+    def __del__(self):
+        try:
+            self.release()
+        except Exception:
+            pass
+
+    def lde(self, x, log_in: int | None = None, log_w: int = 0, count: int = 1, out=None,
+            stream=None):
+        """`count` row-major matrices of 2^log_in rows and 2^log_w columns (Montgomery, a
+        GPU tensor of 32-bit words) -> their columns' values on the 2^log_n-th roots of
+        unity (2^log_n rows each)."""
+        torch = _torch()
+        log_in = self.log_n if log_in is None else log_in
+        n_in = count << (log_in + log_w)
+        if _bb_words(x, "x") != n_in:
+            raise ValueError("x holds %d words, expected %d" % (_bb_words(x, "x"), n_in))
+        n_out = count << (self.log_n + log_w)
+        out = torch.empty(n_out, dtype=torch.int32, device=x.device) if out is None else out
+        if _bb_words(out, "out") != n_out:
+            raise ValueError("out holds the wrong number of words")
+        _check(load().g16_bb_lde(self.handle, log_in, log_w, count, x.data_ptr(),
+                                 out.data_ptr(), _stream(stream)), "g16_bb_lde")
+        return out

@@ -582,7 +582,6 @@ __global__ void __launch_bounds__(kMsmThreads, 4) msm_tile_sums(const uint2* ent
     const uint32_t head_lane = (uint32_t)__builtin_ctzll(act);
     const uint32_t tail_lane = 63u - (uint32_t)__builtin_clzll(act);
     const uint32_t head_row = __shfl(first, head_lane, 64);
-    const uint32_t tail_row = __shfl(last, tail_lane, 64);
     const uint32_t prev_last = __shfl_up(last, 1u, 64);
     const uint32_t next_first = __shfl_down(first, 1u, 64);
     if (!lv.last && lane == 0) {  // the blanks at both ends of the window's item list

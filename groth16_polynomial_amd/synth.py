@@ -97,6 +97,34 @@ def uniform_fr(seed: int, n: int) -> np.ndarray:
     return out.view(np.uint32).reshape(n, 8).copy()
 
 
+# BabyBear modulus (the WHIR forum post's field), for the Reed-Solomon encoding workload.
+BB_MODULUS = (1 << 31) - (1 << 27) + 1
+
+
+def uniform_bb(seed: int, n: int) -> np.ndarray:
+    """n uniform elements of [0, p) for BabyBear p, standard form, uint32.  Candidate j is
+    the low 31 bits of stream output j, kept iff it is < p (15 in 16 are kept)."""
+    out = np.empty(n, dtype=np.uint32)
+    got = 0
+    cand = 0
+    while got < n:
+        want = max(1024, int((n - got) * 1.08) + 64)
+        z = (splitmix64(seed, want, cand) & np.uint64(0x7FFFFFFF)).astype(np.uint32)
+        keep = z[z < np.uint32(BB_MODULUS)]
+        take = min(len(keep), n - got)
+        out[got:got + take] = keep[:take]
+        got += take
+        cand += want
+    return out
+
+
+def bb_lde_input(workload: int, log_in: int, log_w: int, count: int = 1) -> np.ndarray:
+    """The coefficients of a Reed-Solomon encoding workload: `count` row-major matrices of
+    2^log_in rows and 2^log_w columns of uniform BabyBear elements (standard form), as a
+    flat uint32 array."""
+    return uniform_bb(seed_for(workload, STREAM_VECTOR), count << (log_in + log_w))
+
+
 def unit_floats(seed: int, count: int, start: int = 0) -> np.ndarray:
     """Uniform doubles in [0, 1) from the top 53 bits of each stream output."""
     z = splitmix64(seed, count, start)

@@ -269,6 +269,59 @@ int g16_msm_g1_finish(uint32_t c, const void* window_sums_host, void* out_affine
 int g16_g1_generator_mul(uint64_t n, const void* scalars_std, void* out_affine_mont,
                          void* stream);
 
+/* ======================================================================================
+ * BabyBear transform: the Reed-Solomon encoding step of WHIR proving (the forum post
+ * "GPU-Accelerated WHIR Proving on Apple Silicon", sections 2, 3.2 and 3.4).
+ *
+ * Field: p = 2^31 - 2^27 + 1.  An element is one 32-bit word, canonical (< p), in
+ * Montgomery form with R = 2^32 ("mont") or plain ("std").  Roots (a reading; the post
+ * names none): 31 generates the multiplicative group and omega_(2^L) = 31^((p-1)/2^L).
+ *
+ * The transform (g16_bb_lde): `count` matrices one after another, each row-major with
+ * 2^log_w columns (element (i, c) at i * 2^log_w + c); an input matrix has 2^log_in rows,
+ * an output matrix 2^log_n rows (log_n fixed by the context).  Output column c holds
+ * y_i = sum_j x_j omega^(i j), i < 2^log_n, where x is input column c zero-padded to
+ * 2^log_n rows: the values of the column's polynomial on the 2^log_n-th roots of unity,
+ * natural order, i.e. the low-degree extension at rate 2^-(log_n - log_in).
+ * ====================================================================================== */
+typedef struct g16_bb_ctx g16_bb_ctx; /* opaque host object, owned by the library */
+#define G16_BB_MAX_LOG_N 27u
+#define G16_BB_MAX_LOG_W 10u
+
+/* Bytes of device workspace for the twiddle levels of a 2^log_n domain ((2^log_n - 1)
+ * entries of 8 bytes, rounded up to 256), or 0 for log_n outside [1, 27]. */
+size_t g16_bb_workspace_bytes(uint32_t log_n);
+
+/* The pass batches of a 2^log_n transform (lowest bits first; at most 8 passes each,
+ * near-equal, larger first; one batch of log_n for log_n <= 4).  Writes up to `cap` sizes
+ * and returns the count, or G16_ERANGE / G16_EINVAL.  Host only. */
+int g16_bb_batch_plan(uint32_t log_n, uint32_t* ks, uint32_t cap);
+
+/* Enqueues the twiddle table build into `workspace` (device memory, 256-byte aligned, at
+ * least g16_bb_workspace_bytes(log_n) bytes, owned by the caller and kept alive until
+ * g16_bb_release) and returns a new context.  Errors: G16_EINVAL (null or misaligned),
+ * G16_ERANGE, G16_ENOSPACE, G16_EHIP. */
+int g16_bb_prepare(uint32_t log_n, void* workspace, size_t workspace_bytes, void* stream,
+                   g16_bb_ctx** out_ctx);
+
+/* Frees the context (not the workspace).  G16_ESTATE for a pointer that is not a live
+ * context (never read), G16_EINVAL for NULL. */
+int g16_bb_release(g16_bb_ctx* ctx);
+
+/* The batched low-degree extension described above, in_mont -> out_mont (device
+ * pointers, count * 2^(log_in + log_w) and count * 2^(log_n + log_w) words).  count == 0
+ * enqueues nothing.  Errors: G16_ESTATE (bad context), G16_EINVAL (log_in > log_n,
+ * log_w > G16_BB_MAX_LOG_W, log_n + log_w > 30, count > 2^20, null, host or short
+ * buffers), G16_EALIAS (input and output overlap, or the output overlaps the
+ * workspace), G16_EHIP.  Inputs must be canonical (not checked).  Calls on one context
+ * may overlap in time: the context holds only the read-only table. */
+int g16_bb_lde(g16_bb_ctx* ctx, uint32_t log_in, uint32_t log_w, uint64_t count,
+               const void* in_mont, void* out_mont, void* stream);
+
+/* Element-wise conversions (in == out allowed): plain -> Montgomery and back. */
+int g16_bb_to_mont(uint64_t n, const void* in_std, void* out_mont, void* stream);
+int g16_bb_from_mont(uint64_t n, const void* in_mont, void* out_std, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
