@@ -60,9 +60,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-side", action="store_true",
                     help="only the timed 2^log_n pipeline and its stages (for profiling)")
-    ap.add_argument("--part", choices=("all", "h", "msm"), default="all",
+    ap.add_argument("--part", choices=("all", "h", "msm", "bb"), default="all",
                     help="h: only the timed pipeline and its stages (as --no-side, no CPU "
-                         "baseline); msm: only the G1 MSM legs (for profiling)")
+                         "baseline); msm: only the G1 MSM legs; bb: only the BabyBear "
+                         "encoding legs (for profiling)")
     ap.add_argument("--stage-reps", type=int, default=10)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (a known-size "
@@ -236,6 +237,46 @@ def probe_rates(log):
     return out
 
 
+# The BabyBear Reed-Solomon encodings (the WHIR forum post's NTT): (label, log_n rows out,
+# log_w columns, rate): the n = 24 cells of the post's grids with fold 3 and fold 1 at
+# rate 1, the n = 22 fold-3 cell, and one unfolded polynomial of 2^23 coefficients.
+BB_SHAPES = (("n=24 fold=3 rate=1", 22, 3, 1), ("n=24 fold=1 rate=1", 24, 1, 1),
+             ("n=22 fold=3 rate=1", 20, 3, 1), ("2^23 coefficients rate=1", 24, 0, 1))
+
+
+def bb_leg(g, synth, torch, tm, steps, log):
+    """Times g16_bb_lde on the BB_SHAPES: output words per second; bytes the batches move
+    (the first reads the input and writes the output, each later one reads and writes the
+    output) and the minimum (input once, output once) per second; butterflies per
+    second."""
+    out = {}
+    for label, log_n, log_w, rate in BB_SHAPES:
+        log_in = log_n - rate
+        ctx = g.BbContext(log_n)
+        x = g.bb_to_mont(g.bb_to_device(synth.bb_lde_input(40, log_in, log_w)))
+        y = torch.empty(1 << (log_n + log_w), dtype=torch.int32, device="cuda")
+        ms = tm.mean_ms(lambda: ctx.lde(x, log_in=log_in, log_w=log_w, out=y), steps)
+        n_out = 1 << (log_n + log_w)
+        n_in = 1 << (log_in + log_w)
+        plan = g.bb_batch_plan(log_n)
+        moved = 4 * (n_in + n_out) + (len(plan) - 1) * 8 * n_out
+        minimum = 4 * (n_in + n_out)
+        bfly = (n_out // 2) * log_n
+        out[label] = {
+            "log_n": log_n, "log_w": log_w, "rate": rate, "pass_batches": plan,
+            "ms": round(ms, 5),
+            "g_words_out_s": round(n_out / (ms / 1e3) / 1e9, 3),
+            "gbutterfly_s": round(bfly / (ms / 1e3) / 1e9, 3),
+            "hbm_gbs_batches": round(moved / (ms / 1e3) / 1e9, 1),
+            "hbm_gbs_minimum": round(minimum / (ms / 1e3) / 1e9, 1),
+            "hbm_frac_batches": round(moved / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        }
+        ctx.release()
+        del x, y
+    log("bb: %s" % out)
+    return out
+
+
 def hs_of(ctx, ad, bd, cd, hm, hs):
     """h_std of the timed pipeline (the MSM's input in a prover)."""
     ctx.h_compute(ad, bd, cd, hm, hs)
@@ -320,6 +361,10 @@ def main():
     tm = Timer(torch)
     torch.cuda.synchronize()
     line_extra = {}
+    if args.part == "bb":
+        print(json.dumps({"bb_lde": bb_leg(g, synth, torch, tm, args.steps, log)}), flush=True)
+        ctx.release()
+        return
     if args.part == "msm":
         print(json.dumps({"msm_g1": msm_leg(g, synth, torch, tm, hs_of(ctx, ad, bd, cd, hm, hs),
                                             log_n, args.steps, log)}), flush=True)
@@ -458,6 +503,8 @@ def main():
             del oa, ob, oc, ohm, ohs
         line_extra["other_sizes"] = other_sizes
         log("other sizes: %s" % other_sizes)
+
+        line_extra["bb_lde"] = bb_leg(g, synth, torch, tm, args.steps, log)
 
     # ---- the timed region: K whole pipelines
     for _ in range(args.warmup):
