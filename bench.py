@@ -79,19 +79,23 @@ def stage_work(kind: str, join: bool, n_vec: int, k: int, n: int):
     the inverse and the first k of the forward transform (2k n/2 butterflies), the 1/n
     scaling and the coset shift (two products per element, performed here as one table
     product), and one read of the shift table per element.  Join: A'B' (one product),
-    h_std (one reduction), reads A' and B', writes h_mont and h_std instead of one vector.
+    h_std (one reduction); writes h_mont and h_std instead of the vectors, and reads A'
+    and B' when C runs alone (n_vec = 1; with all three kinds in the launch they meet in
+    LDS).
     """
     if kind == "fused":
         muls = n_vec * (2 * k * n // 2 + 2 * n)
-        byts = n_vec * 3 * n * FR_BYTES
     else:
         muls = n_vec * k * n // 2
-        byts = n_vec * 2 * n * FR_BYTES
+    reads = n_vec + (2 if join and n_vec == 1 else 0)
+    writes = 2 if join else n_vec
+    byts = (reads + writes) * n * FR_BYTES
+    if kind == "fused":
+        byts += n_vec * n * FR_BYTES    # the shift table
     redc = 0
     if join:
         muls += n
         redc = n
-        byts += 3 * n * FR_BYTES        # + A', B' reads, + the second output
     return muls, redc, byts
 
 
@@ -106,7 +110,9 @@ def stage_list(plan, count, n_vec=3):
     nb = len(plan)
     out = []
     if nb == 1:
-        return [("fused", False, 2, plan[0]), ("fused", True, 1, plan[0])]
+        if count == 1:
+            return [("fused", True, n_vec, plan[0])]
+        return [("fused", False, n_vec - 1, plan[0]), ("fused", True, 1, plan[0])]
     merged = count == 2 * (nb - 1) + 1
     for b in range(nb - 1, 0, -1):
         out.append(("inv", False, n_vec, plan[b]))

@@ -17,7 +17,7 @@
 #include "host_util.hpp"
 #include "kernels.hpp"
 #include "pointwise_kernels.hpp"
-#include "r8_launch.hpp"
+#include "group_launch.hpp"
 
 using g16::Fr;
 
@@ -46,6 +46,7 @@ struct g16_ctx {
     Fr omega, omega_inv, shift, size_inv;  // Montgomery form
     g16::Tw29 size_inv_entry;              // n^-1 as a table entry (inverse transform)
     bool radix2;  // G16_RADIX2 set at prepare time: every batch on the radix-2 kernel
+    int narrow;   // G16_NARROW at prepare time: 0 never, 1 always, -1 by launch size
     uint32_t n_batches;
     uint32_t batch_k[kMaxBatches];  // lowest bits first
 };
@@ -117,35 +118,88 @@ void domain_roots(uint32_t log_n, Fr* omega, Fr* shift, Fr* size_inv) {
     *size_inv = g16::fr_inv(g16::fr_to_mont(n));
 }
 
+// Launches of at most this many elements (vectors x 2^log_n) take the narrow geometry of
+// the register-group kernel unless G16_NARROW says otherwise.  Below it the radix-4
+// groups leave CUs idle or thinly occupied and each thread's chain of products sets the
+// time; the narrow geometry halves the chain and doubles the threads.  Above it the
+// radix-4 groups' fewer LDS exchanges and table loads win.  Measured on MI355X, the two
+// geometries alternating (H pipeline, three vectors): 2^12 55 / 26 us, 2^16 77 / 56,
+// 2^18 141 / 138, 2^19 262 / 269, 2^20 527 / 600 (radix-4 / narrow); proof batches of
+// 64 x 2^12 125 / 121 us and 16 x 2^16 524 / 599; one forward transform of 2^19 54 / 54.
+constexpr uint64_t kNarrowMaxElems = uint64_t(3) << 18;
+
+bool use_narrow(const g16_ctx* c, uint64_t n_vec) {
+    if (c->narrow >= 0) return c->narrow != 0;
+    return (n_vec << c->log_n) <= kNarrowMaxElems;
+}
+
 // The register-group kernel takes batches of 6..10 passes with at least one full workgroup
 // of slices; the radix-2 kernel takes the rest (small domains, other batch sizes).
 template <g16::Mode M, bool J>
-bool try_r8(const g16::BatchParams& p, uint32_t n_vec, hipStream_t stream, int* rc) {
+bool try_groups(const g16::BatchParams& p, uint32_t n_vec, bool narrow, hipStream_t stream,
+                int* rc) {
     const uint32_t k = p.k, L = p.log_n;
     auto fits = [&](uint32_t spw) { return (1ull << (L - k)) >= spw; };
     hipError_t e;
     switch (k) {
-#define G16_R8_CASE(KK)                                                        \
-        case KK:                                                               \
-            if (!fits(g16::R8GeomFor<KK, g16::kR8Group, M>::kSpw)) return false; \
-            e = g16::launch_r8<KK, M, J>(p, n_vec, stream);                     \
-            *rc = e == hipSuccess ? G16_OK : G16_EHIP;                          \
+#define G16_GROUP_CASE(KK)                                                              \
+        case KK:                                                                       \
+            if (!fits(narrow ? g16::NarrowGeomFor<KK, M>::kSpw                         \
+                             : g16::GroupGeomFor<KK, g16::kGroupPasses, M>::kSpw))    \
+                return false;                                                          \
+            e = g16::launch_groups<KK, M, J>(p, n_vec, narrow, stream);                \
+            *rc = e == hipSuccess ? G16_OK : G16_EHIP;                                 \
             return true;
-        G16_R8_CASE(6)
-        G16_R8_CASE(7)
-        G16_R8_CASE(8)
-        G16_R8_CASE(9)
-        G16_R8_CASE(10)
-#undef G16_R8_CASE
+        G16_GROUP_CASE(6)
+        G16_GROUP_CASE(7)
+        G16_GROUP_CASE(8)
+        G16_GROUP_CASE(9)
+        G16_GROUP_CASE(10)
+#undef G16_GROUP_CASE
         default:
             return false;
     }
 }
 
+// Whether the pipeline's last launch (M = FwdStrided or Fused) of batch size k can take
+// the three kinds of a proof in one narrow workgroup (ntt_group_kernel with NK = 3).
+template <g16::Mode M>
+bool join3_fits(uint32_t k, uint32_t L) {
+    switch (k) {
+#define G16_J3_CASE(KK)                                                               \
+        case KK:                                                                      \
+            return g16::narrow_join3_fits<KK, M>() &&                                 \
+                   (1ull << (L - KK)) >= (uint64_t)g16::NarrowGeomFor<KK, M>::kSpw;
+        G16_J3_CASE(6)
+        G16_J3_CASE(7)
+        G16_J3_CASE(8)
+        G16_J3_CASE(9)
+        G16_J3_CASE(10)
+#undef G16_J3_CASE
+        default:
+            return false;
+    }
+}
+
+template <g16::Mode M>
+int launch_join3(const g16::BatchParams& p, uint32_t n_proof, hipStream_t stream) {
+    hipError_t e;
+    switch (p.k) {
+        case 6: e = g16::launch_groups_join3<6, M>(p, n_proof, stream); break;
+        case 7: e = g16::launch_groups_join3<7, M>(p, n_proof, stream); break;
+        case 8: e = g16::launch_groups_join3<8, M>(p, n_proof, stream); break;
+        case 9: e = g16::launch_groups_join3<9, M>(p, n_proof, stream); break;
+        case 10: e = g16::launch_groups_join3<10, M>(p, n_proof, stream); break;
+        default: return G16_EINVAL;
+    }
+    return e == hipSuccess ? G16_OK : G16_EHIP;
+}
+
 template <g16::Mode M, bool J>
-int launch_batch(const g16::BatchParams& p, uint32_t n_vec, bool radix2, hipStream_t stream) {
+int launch_batch(const g16::BatchParams& p, uint32_t n_vec, bool radix2, bool narrow,
+                 hipStream_t stream) {
     int rc = G16_OK;
-    if (!radix2 && try_r8<M, J>(p, n_vec, stream, &rc)) return rc;
+    if (!radix2 && try_groups<M, J>(p, n_vec, narrow, stream, &rc)) return rc;
     // radix-2 batch kernel: small batches and small domains
     const uint32_t k = p.k, L = p.log_n;
     g16::BatchParams q = p;
@@ -200,7 +254,8 @@ int run_ntt(g16_ctx* c, const void* in, void* out, void* stream, bool inverse) {
     p.src[0] = (const Fr*)in;
     const bool single = c->n_batches == 1;
     p.dst[0] = (single && in != out) ? (Fr*)out : scr;
-    int rc = launch_batch<g16::Mode::HeadBitrev, false>(p, 1, c->radix2, s);
+    const bool narrow = use_narrow(c, 1);
+    int rc = launch_batch<g16::Mode::HeadBitrev, false>(p, 1, c->radix2, narrow, s);
     if (rc) return rc;
     if (single) {
         if (in == out) {
@@ -216,7 +271,7 @@ int run_ntt(g16_ctx* c, const void* in, void* out, void* stream, bool inverse) {
         t.k = c->batch_k[b];
         t.src[0] = scr;
         t.dst[0] = (b + 1 == c->n_batches) ? (Fr*)out : scr;
-        rc = launch_batch<g16::Mode::FwdStrided, false>(t, 1, c->radix2, s);
+        rc = launch_batch<g16::Mode::FwdStrided, false>(t, 1, c->radix2, narrow, s);
         if (rc) return rc;
     }
     return G16_OK;
@@ -226,7 +281,9 @@ int run_ntt(g16_ctx* c, const void* in, void* out, void* stream, bool inverse) {
 struct Launch {
     g16::Mode mode;
     bool join;
+    bool join3;  // the three kinds of each proof in one workgroup (n_vec counts proofs)
     bool radix2;
+    bool narrow;
     g16::BatchParams p;
     uint32_t n_vec;
 };
@@ -235,18 +292,21 @@ constexpr uint32_t kMaxLaunches = 2 * kMaxBatches + 2;
 
 int exec_launch(const Launch& l, hipStream_t s) {
     using g16::Mode;
-    const bool r2 = l.radix2;
+    const bool r2 = l.radix2, nw = l.narrow;
+    if (l.join3)
+        return l.mode == Mode::Fused ? launch_join3<Mode::Fused>(l.p, l.n_vec, s)
+                                     : launch_join3<Mode::FwdStrided>(l.p, l.n_vec, s);
     switch (l.mode) {
         case Mode::Fused:
-            return l.join ? launch_batch<Mode::Fused, true>(l.p, l.n_vec, r2, s)
-                          : launch_batch<Mode::Fused, false>(l.p, l.n_vec, r2, s);
+            return l.join ? launch_batch<Mode::Fused, true>(l.p, l.n_vec, r2, nw, s)
+                          : launch_batch<Mode::Fused, false>(l.p, l.n_vec, r2, nw, s);
         case Mode::FwdStrided:
-            return l.join ? launch_batch<Mode::FwdStrided, true>(l.p, l.n_vec, r2, s)
-                          : launch_batch<Mode::FwdStrided, false>(l.p, l.n_vec, r2, s);
+            return l.join ? launch_batch<Mode::FwdStrided, true>(l.p, l.n_vec, r2, nw, s)
+                          : launch_batch<Mode::FwdStrided, false>(l.p, l.n_vec, r2, nw, s);
         case Mode::InvStrided:
-            return launch_batch<Mode::InvStrided, false>(l.p, l.n_vec, r2, s);
+            return launch_batch<Mode::InvStrided, false>(l.p, l.n_vec, r2, nw, s);
         default:
-            return launch_batch<Mode::HeadBitrev, false>(l.p, l.n_vec, r2, s);
+            return launch_batch<Mode::HeadBitrev, false>(l.p, l.n_vec, r2, nw, s);
     }
 }
 
@@ -254,7 +314,9 @@ int exec_launch(const Launch& l, hipStream_t s) {
 // of each of n_proof proofs, proof q's vectors vstride elements after proof q - 1's
 // (dsts may equal srcs only when the context has a single batch).  With join, the last
 // kind's final batch writes H = dsts[0] * dsts[1] - x into h_mont / h_std instead, in a
-// launch of its own after the other vectors are finished.
+// launch of its own after the other vectors are finished; or, for launches small enough
+// for the narrow geometry, the final batch of all three kinds is one launch whose
+// workgroups join A', B' and C' in LDS (dsts[0], dsts[1] are then not written by it).
 uint32_t plan_coset(const g16_ctx* c, const Fr* const* srcs, Fr* const* dsts, uint32_t n_kind,
                     uint32_t n_proof, uint64_t vstride, bool join, Fr* h_mont, Fr* h_std,
                     Launch* out) {
@@ -266,9 +328,27 @@ uint32_t plan_coset(const g16_ctx* c, const Fr* const* srcs, Fr* const* dsts, ui
         p.vstride = vstride;
         out[count].mode = m;
         out[count].join = j;
+        out[count].join3 = false;
         out[count].radix2 = c->radix2;
+        out[count].narrow = use_narrow(c, (uint64_t)kinds * n_proof);
         out[count].p = p;
         out[count].n_vec = kinds * n_proof;
+        ++count;
+    };
+    // the final batch of the three kinds, joined in the workgroup
+    const bool j3 = join && n_kind == 3 && !c->radix2 && use_narrow(c, 3ull * n_proof);
+    auto add_join3 = [&](g16::Mode m, g16::BatchParams p) {
+        p.n_kind = 3;
+        p.vstride = vstride;
+        p.h_mont = h_mont;
+        p.h_std = h_std;
+        out[count].mode = m;
+        out[count].join = true;
+        out[count].join3 = true;
+        out[count].radix2 = false;
+        out[count].narrow = true;
+        out[count].p = p;
+        out[count].n_vec = n_proof;
         ++count;
     };
     auto joined = [&](g16::BatchParams p) {
@@ -304,6 +384,10 @@ uint32_t plan_coset(const g16_ctx* c, const Fr* const* srcs, Fr* const* dsts, ui
         f.dst[v] = dsts[v];
     }
     if (nb == 1) {
+        if (j3 && join3_fits<g16::Mode::Fused>(f.k, c->log_n)) {
+            add_join3(g16::Mode::Fused, f);
+            return count;
+        }
         if (plain_kind) add(g16::Mode::Fused, false, f, plain_kind);
         if (join) add(g16::Mode::Fused, true, joined(f), 1);
         return count;
@@ -319,7 +403,9 @@ uint32_t plan_coset(const g16_ctx* c, const Fr* const* srcs, Fr* const* dsts, ui
             p.src[v] = dsts[v];
             p.dst[v] = dsts[v];
         }
-        if (b + 1 == nb && join) {
+        if (b + 1 == nb && j3 && join3_fits<g16::Mode::FwdStrided>(p.k, c->log_n)) {
+            add_join3(g16::Mode::FwdStrided, p);
+        } else if (b + 1 == nb && join) {
             if (plain_kind) add(g16::Mode::FwdStrided, false, p, plain_kind);
             add(g16::Mode::FwdStrided, true, joined(p), 1);
         } else {
@@ -476,6 +562,10 @@ int g16_h_prepare(uint32_t log_n, void* workspace, size_t workspace_bytes, void*
     c->size_inv_entry = g16::tw29_entry(c->size_inv);
     c->n_batches = plan_batches(log_n, max_batch_k(), c->batch_k);
     c->radix2 = std::getenv("G16_RADIX2") != nullptr;
+    {
+        const char* nw = std::getenv("G16_NARROW");
+        c->narrow = nw ? (std::atoi(nw) != 0 ? 1 : 0) : -1;
+    }
     {
         // the no-allocation entry point's scratch on this device (resolved here, with the
         // device current; a failure only disables that entry point, which reports it)
@@ -641,8 +731,11 @@ int g16_h_compute_batch(g16_ctx* ctx, uint64_t n_proofs, const void* a_mont,
 
 int g16_h_stage_count(const g16_ctx* ctx) {
     if (!ctx_ok(ctx)) return ctx ? G16_ESTATE : G16_EINVAL;
-    const uint32_t nb = ctx->n_batches;
-    return nb == 1 ? 2 : (int)(2 * (nb - 1) + 2);
+    // the single-proof plan (planning reads no buffer)
+    Launch ls[kMaxLaunches];
+    const Fr* srcs[3] = {nullptr, nullptr, nullptr};
+    Fr* dsts[3] = {nullptr, nullptr, nullptr};
+    return (int)plan_coset(ctx, srcs, dsts, 3, 1, 0, true, nullptr, nullptr, ls);
 }
 
 int g16_h_stage(g16_ctx* ctx, uint32_t stage, const void* a_mont, const void* b_mont,

@@ -193,6 +193,14 @@ __device__ __forceinline__ void store_h(const BatchParams& p, uint64_t i, const 
     st_global(p.h_std + i, fr_from_mont(h));
 }
 
+// The same with A' and B' at hand (canonical).
+__device__ __forceinline__ void store_h3(const BatchParams& p, uint64_t i, const Fr& a,
+                                         const Fr& b, const Fr& x) {
+    Fr h = fr_sub(fr_mul(a, b), x);
+    st_global(p.h_mont + i, h);
+    st_global(p.h_std + i, fr_from_mont(h));
+}
+
 // x w mod r, canonical, for a canonical x and a table entry (radix-2 kernel and
 // element-wise use).
 __device__ __forceinline__ Fr fr_mul_entry(const Fr& x, const Tw29& t) {
@@ -304,7 +312,7 @@ __global__ void __launch_bounds__(256) ntt_batch_kernel(BatchParams p) {
 
 }  // namespace g16
 
-#include "ntt_r8.hpp"
+#include "ntt_groups.hpp"
 
 namespace g16 {
 

@@ -35,6 +35,10 @@ namespace g16 {
 #endif
 constexpr int kStridedCols = G16_STRIDED_COLS;
 
+#ifndef G16_NARROW_PREFETCH
+#define G16_NARROW_PREFETCH 1
+#endif
+
 constexpr bool strided_mode(Mode m) { return m == Mode::FwdStrided || m == Mode::InvStrided; }
 
 // The head batch (bit-reversed load) pairs its slices the same way: slice g reads input
@@ -49,7 +53,7 @@ constexpr int slices_per_wg(int k, Mode m) {
 // K passes per batch in groups of GR (the last group may be shorter); each thread
 // holds 2^GR elements; SPW slices per workgroup.
 template <int K, int GR, int SPW>
-struct R8Geom {
+struct GroupGeom {
     static constexpr int kE = 1 << GR;
     static constexpr int kThreadsPerSlice = 1 << (K - GR);
     static constexpr int kSpw = SPW;
@@ -62,7 +66,22 @@ struct R8Geom {
 };
 
 template <int K, int GR, Mode M>
-using R8GeomFor = R8Geom<K, GR, slices_per_wg(K, M)>;
+using GroupGeomFor = GroupGeom<K, GR, slices_per_wg(K, M)>;
+
+// Narrow geometry, for launches too small to fill the chip, where each thread's chain of
+// dependent products sets the time: one pass per group (two elements and one butterfly per
+// thread and pass, half the products of the radix-4 groups in each chain, twice the
+// threads) and the fewest slices a workgroup may hold (a workgroup is one or two waves),
+// so the slices spread over as many CUs as there are.
+constexpr int narrow_slices_per_wg(int k, Mode m) {
+    return interleaved_mode(m) ? kStridedCols : (k >= 7 ? 1 : (64 >> (k - 1)));
+}
+template <int K, Mode M>
+using NarrowGeomFor = GroupGeom<K, 1, narrow_slices_per_wg(K, M)>;
+
+// Threads of a workgroup that takes three kinds in the narrow geometry (NK = 3 below).
+template <int K, Mode M>
+constexpr bool narrow_join3_fits() { return 3 * NarrowGeomFor<K, M>::kThreads <= 1024; }
 
 // c with the r bits of q inserted at bit b0
 __device__ __forceinline__ uint32_t insert_bits(uint32_t c, uint32_t q, int b0, int r) {
@@ -183,12 +202,16 @@ __device__ __forceinline__ void ct_pass(V29 (&x)[E], const Tw29 (&pw)[1 << (R - 
 // Without PF each entry is loaded just before its product, which needs fewer registers.
 // NORM: the elements that are "lo" in the first pass are normalized first.  UNI: every
 // entry of the group is the same in all lanes of the wave (scalar loads; only without PF).
+// PRE: a one-pass group whose entry the caller loaded earlier (pre).
 template <int OFF, int R, bool INV, bool NORM, int CH, bool PF, bool UNI, unsigned TM0,
-          unsigned TM1, unsigned TM2, int E, typename IdxFor>
-__device__ __forceinline__ void run_passes(V29 (&x)[E], const Tw29* tw, IdxFor&& idx_for) {
+          unsigned TM1, unsigned TM2, bool PRE, int E, typename IdxFor>
+__device__ __forceinline__ void run_passes(V29 (&x)[E], const Tw29* tw, IdxFor&& idx_for,
+                                           const Tw29& pre) {
+    static_assert(!PRE || (R == 1 && !PF), "a preloaded entry serves one-pass groups");
     constexpr int NB = 1 << (R - 1);
     constexpr unsigned tm[3] = {TM0, TM1, TM2};
     Tw29 ent[R][NB];
+    if constexpr (PRE) ent[0][0] = pre;
     auto fetch = [&](auto s_c, auto j0_c, auto j1_c) {
         constexpr int s = decltype(s_c)::value;
         if constexpr (s < R) {
@@ -230,17 +253,17 @@ __device__ __forceinline__ void run_passes(V29 (&x)[E], const Tw29* tw, IdxFor&&
             fetch(std::integral_constant<int, s + 1>{}, I0{}, I1{});
             __builtin_amdgcn_sched_barrier(0);
         }
-        ct_pass<OFF, R, u, tm[u], CH, !PF, UNI && !PF>(x, ent[s], tw,
-                                                      idx_for(std::integral_constant<int, u>{}));
+        ct_pass<OFF, R, u, tm[u], CH, !PF && !PRE, UNI && !PF && !PRE>(
+            x, ent[s], tw, idx_for(std::integral_constant<int, u>{}));
     });
 }
 
 // The R forward-order passes of one group on x[OFF .. OFF + 2^R): pass u flips local
 // bit B0 + u (global bit s0 + B0 + u); the pair (q, q + 2^u) has local index bits below
 // the pass equal to (c mod 2^B0) + (q mod 2^u) 2^B0.  Global bit 0 has twiddle 1.
-template <int OFF, int R, int B0, bool NORM, bool CONTIG, int CH, bool PF, int E>
+template <int OFF, int R, int B0, bool NORM, bool CONTIG, int CH, bool PF, int E, bool PRE>
 __device__ __forceinline__ void group_fwd(V29 (&x)[E], uint32_t c, uint32_t low, uint32_t s0,
-                                          uint32_t log_n, const Tw29* tw) {
+                                          uint32_t log_n, const Tw29* tw, const Tw29& pre) {
     const uint32_t cl = c & ((1u << B0) - 1u);
     auto idx_for = [&](auto u_c) {
         return [&](auto b_c) {  // u from the type alone: the lambda outlives this call
@@ -257,7 +280,8 @@ __device__ __forceinline__ void group_fwd(V29 (&x)[E], uint32_t c, uint32_t low,
     constexpr unsigned t1 = (CONTIG && B0 == 0 && R == 2) ? (0x55555555u & all) : 0u;
     // in the first group of a contiguous batch (B0 = 0, column 0) the entry index depends
     // on the butterfly only: the same in every lane
-    run_passes<OFF, R, false, NORM, CH, PF, (CONTIG && B0 == 0), t0, t1, 0u>(x, tw, idx_for);
+    run_passes<OFF, R, false, NORM, CH, PF, (CONTIG && B0 == 0), t0, t1, 0u, PRE>(x, tw, idx_for,
+                                                                                pre);
 }
 
 // The R inverse-order passes of one group, u = R-1 down to 0: the pair (q, q + 2^u) has
@@ -265,9 +289,9 @@ __device__ __forceinline__ void group_fwd(V29 (&x)[E], uint32_t c, uint32_t low,
 // The pass on the transform's top bit (only in the top batch) has twiddle 1 throughout.
 // LB: the bits of c that differ between the lanes of a wave are bits 0 .. LB-1 (and h is
 // the same in all of them), so for B0 >= LB every entry of the group is wave-uniform.
-template <int OFF, int R, int B0, int K, bool NORM, int CH, bool PF, int LB, int E>
+template <int OFF, int R, int B0, int K, bool NORM, int CH, bool PF, int LB, int E, bool PRE>
 __device__ __forceinline__ void group_inv(V29 (&x)[E], uint32_t c, uint32_t h, uint32_t s0,
-                                          uint32_t log_n, const Tw29* tw) {
+                                          uint32_t log_n, const Tw29* tw, const Tw29& pre) {
     const uint32_t ch = c >> B0;
     auto idx_for = [&](auto u_c) {
         return [&](auto b_c) {  // u from the type alone: the lambda outlives this call
@@ -287,7 +311,7 @@ __device__ __forceinline__ void group_inv(V29 (&x)[E], uint32_t c, uint32_t h, u
         constexpr unsigned t_top = tv ? all : 0u;                // pass u = R - 1
         constexpr unsigned t_0 = (tv && R == 2) ? 1u : 0u;       // pass u = 0 of two
         run_passes<OFF, R, true, NORM, CH, PF, (B0 >= LB), (R == 1 ? t_top : t_0),
-                   (R == 2 ? t_top : 0u), (R == 3 ? t_top : 0u)>(x, tw, idx_for);
+                   (R == 2 ? t_top : 0u), (R == 3 ? t_top : 0u), PRE>(x, tw, idx_for, pre);
     };
     if constexpr (top_group) {
         if (s0 + (uint32_t)K == log_n) run(std::true_type{});
@@ -297,15 +321,22 @@ __device__ __forceinline__ void group_inv(V29 (&x)[E], uint32_t c, uint32_t h, u
     }
 }
 
-// Grid: (2^(L-K) / kSpw) slice groups x n_vec vectors, one-dimensional;
-// block = R8GeomFor<K, GR, M>::kThreads; dynamic LDS = R8GeomFor<K, GR, M>::kLdsBytes.
-// Launch bounds: at least four waves per SIMD (the second argument is the minimum waves
-// per execution unit), i.e. at most 128 VGPRs, whatever the workgroup size.
-template <int K, int GR, Mode M, bool JOIN>
-__global__ void __launch_bounds__((R8GeomFor<K, GR, M>::kThreads), 4)
-ntt_r8_kernel(BatchParams p) {
-    using G = R8GeomFor<K, GR, M>;
-    extern __shared__ uint2 lds[];
+// Grid: (2^(L-K) / SPW) slice groups x n_vec vectors, one-dimensional;
+// block = NK x GroupGeom<K, GR, SPW>::kThreads; dynamic LDS = NK x GroupGeom<K, GR, SPW>::
+// kLdsBytes.  Launch bounds: at least four waves per SIMD (the second argument is the
+// minimum waves per execution unit), i.e. at most 128 VGPRs, whatever the workgroup size.
+//
+// NK = 3 (with JOIN, the last batch of the pipeline): a workgroup takes the same slices of
+// a proof's three vectors, kind = thread / kThreads, each kind in an LDS region of its
+// own, and the grid's vectors are proofs.  After the last group the three kinds meet in
+// LDS and the A and B threads form H = A' B' - C' (one element each), so A' and B' never
+// go back to HBM and the join needs no launch of its own.
+template <int K, int GR, Mode M, bool JOIN, int SPW, int NK>
+__global__ void __launch_bounds__((GroupGeom<K, GR, SPW>::kThreads * NK), 4)
+ntt_group_kernel(BatchParams p) {
+    using G = GroupGeom<K, GR, SPW>;
+    static_assert(NK == 1 || (NK == 3 && JOIN), "three kinds per workgroup only with the join");
+    extern __shared__ uint2 lds_all[];
     constexpr bool kStrided = strided_mode(M);
     // lanes interleave the workgroup's slices (strided batches and the head batch)
     constexpr bool kInterleaved = interleaved_mode(M);
@@ -323,10 +354,19 @@ ntt_r8_kernel(BatchParams p) {
     if ((gridDim.x & 7u) == 0u) lin = (lin & 7u) * (gridDim.x >> 3) + (lin >> 3);
     const uint32_t wg = lin / nv;
     uint32_t kind;
-    const uint64_t off = proof_offset(p, lin - wg * nv, kind);
+    uint64_t off;
+    uint32_t tid = threadIdx.x;
+    if constexpr (NK == 1) {
+        off = proof_offset(p, lin - wg * nv, kind);
+    } else {
+        kind = tid / G::kThreads;
+        tid -= kind * G::kThreads;
+        off = (uint64_t)(lin - wg * nv) * p.vstride;
+    }
+    constexpr uint32_t kRegion = G::kLdsBytes / sizeof(uint2);  // one kind's LDS, in uint2
+    uint2* lds = lds_all + (NK == 1 ? 0u : kind * kRegion);
     const Fr* src = p.src[kind] + off;
     Fr* dst = p.dst[kind] + off;
-    const uint32_t tid = threadIdx.x;
     // strided and head: adjacent lanes take adjacent columns; contiguous: one slice per run
     // of lanes
     const uint32_t sl = kInterleaved ? tid % G::kSpw : tid / G::kThreadsPerSlice;
@@ -345,6 +385,9 @@ ntt_r8_kernel(BatchParams p) {
     // row.  Contiguous: the low 6 bits when a wave holds one slice.
     constexpr int kLaneBits = kStrided ? 6 - __builtin_ctz(G::kSpw)
                               : kInterleaved ? 32 : (G::kThreadsPerSlice >= 64 ? 6 : 32);
+
+    // narrow geometry: each group's table entry loaded one group ahead (entry below)
+    constexpr bool kPre = GR == 1 && G16_NARROW_PREFETCH;
 
     auto gidx = [&](uint32_t e) -> uint64_t { return slice_base + ((uint64_t)e << s0); };
     auto slot = [&](uint32_t e) -> uint32_t {
@@ -380,6 +423,29 @@ ntt_r8_kernel(BatchParams p) {
         });
     };
     auto store_global = [&](auto gi_c) {
+        if constexpr (NK == 3) {
+            // Every thread holds two elements (one pass per group).  The A thread joins its
+            // first element and the B thread its second, so each does one join; each kind
+            // leaves in its own slots what the other two need, and C's threads are done.
+            static_assert(G::kE == 2, "three kinds per workgroup only in the narrow geometry");
+            for_group(gi_c, [&](auto xi_c, uint32_t e) {
+                constexpr uint32_t xi = decltype(xi_c)::value;
+                if (kind == 2u || xi != kind) lds_put(lds, G::kPlane, slot(e), x[xi]);
+            });
+            __syncthreads();
+            if (kind < 2u) {
+                for_group(gi_c, [&](auto xi_c, uint32_t e) {
+                    constexpr uint32_t xi = decltype(xi_c)::value;
+                    if (xi != kind) return;
+                    const uint32_t se = slot(e);
+                    const Fr other = fr29_canon(lds_get(lds_all + (1u - kind) * kRegion,
+                                                        G::kPlane, se));
+                    const Fr cv = fr29_canon(lds_get(lds_all + 2u * kRegion, G::kPlane, se));
+                    store_h3(p, off + gidx(e), fr29_canon(x[xi]), other, cv);
+                });
+            }
+            return;
+        }
         for_group(gi_c, [&](auto xi_c, uint32_t e) {
             constexpr int xi = decltype(xi_c)::value;
             const uint64_t i = gidx(e);
@@ -401,9 +467,10 @@ ntt_r8_kernel(BatchParams p) {
         });
     };
     // passes of group GI in the forward or inverse order; FRESH: the elements come
-    // straight from HBM or from a product (no normalization needed)
+    // straight from HBM or from a product (no normalization needed); pre: the group's
+    // entry, loaded ahead (narrow geometry)
     auto passes = [&](auto gi_c, auto inv_c, auto fresh_c, const Tw29* tw, uint32_t ls0,
-                      uint32_t llow, uint32_t lrow) {
+                      uint32_t llow, uint32_t lrow, const Tw29& pre) {
         constexpr int gi = decltype(gi_c)::value;
         constexpr bool inv = decltype(inv_c)::value;
         constexpr bool norm = !decltype(fresh_c)::value;
@@ -412,30 +479,48 @@ ntt_r8_kernel(BatchParams p) {
         static_for<nsets>([&](auto s_c) {
             constexpr int s = decltype(s_c)::value;
             if constexpr (inv)
-                group_inv<s * (1 << r), r, b0, K, norm, chains_for(M), prefetch_for(M),
-                          kLaneBits, G::kE>(x, t * nsets + s, lrow, ls0, L, tw);
+                group_inv<s * (1 << r), r, b0, K, norm, chains_for(M), prefetch_for(M) && !kPre,
+                          kLaneBits, G::kE, kPre>(x, t * nsets + s, lrow, ls0, L, tw, pre);
             else
-                group_fwd<s * (1 << r), r, b0, norm, !kStrided, chains_for(M), prefetch_for(M),
-                          G::kE>(x, t * nsets + s, llow, ls0, L, tw);
+                group_fwd<s * (1 << r), r, b0, norm, !kStrided, chains_for(M),
+                          prefetch_for(M) && !kPre, G::kE, kPre>(x, t * nsets + s, llow, ls0, L,
+                                                                 tw, pre);
         });
+    };
+    // Narrow geometry (one pass per group, one product per thread and group): the table
+    // entry of the next group is loaded while this one runs (its index depends only on
+    // the thread's position), so no product waits for its entry.  entry(GI): group GI's
+    // entry (group_fwd / group_inv with R = 1, c = t).
+    auto entry = [&](auto gi_c, auto inv_c, const Tw29* tw, uint32_t ls0, uint32_t llow,
+                     uint32_t lrow) -> Tw29 {
+        constexpr uint32_t b0 = decltype(gi_c)::value;
+        if constexpr (decltype(inv_c)::value)
+            return ld_tw(tw + inv_tw_index(L, ls0, K, b0, t >> b0, lrow));
+        else
+            return ld_tw(tw + fwd_tw_index(L, ls0, b0, llow, t & ((1u << b0) - 1u)));
     };
     using FWD = std::false_type;
     using INV = std::true_type;
     using FRESH = std::true_type;
     using OLD = std::false_type;
+    Tw29 nxt{};  // kPre: the next group's entry
 
     // One barrier after every LDS write: a group reads and rewrites the same slots, all
     // owned by the one thread, so the only ordering needed is that a group's writes land
     // before the next group's reads.
     if constexpr (M == Mode::FwdStrided || M == Mode::HeadBitrev) {
+        if constexpr (kPre) nxt = entry(std::integral_constant<int, 0>{}, FWD{}, p.tw, s0, low, row);
         static_for<NG>([&](auto gi_c) {
             constexpr int gi = decltype(gi_c)::value;
+            const Tw29 cur = nxt;
+            if constexpr (kPre && gi + 1 < NG)
+                nxt = entry(std::integral_constant<int, gi + 1>{}, FWD{}, p.tw, s0, low, row);
             if constexpr (gi == 0) {
                 load_global(gi_c);
-                passes(gi_c, FWD{}, FRESH{}, p.tw, s0, low, row);
+                passes(gi_c, FWD{}, FRESH{}, p.tw, s0, low, row, cur);
             } else {
                 lds_read(gi_c);
-                passes(gi_c, FWD{}, OLD{}, p.tw, s0, low, row);
+                passes(gi_c, FWD{}, OLD{}, p.tw, s0, low, row, cur);
             }
             if constexpr (gi == NG - 1) {
                 store_global(gi_c);
@@ -445,15 +530,20 @@ ntt_r8_kernel(BatchParams p) {
             }
         });
     } else if constexpr (M == Mode::InvStrided) {
+        if constexpr (kPre)
+            nxt = entry(std::integral_constant<int, NG - 1>{}, INV{}, p.tw, s0, low, row);
         static_for<NG>([&](auto step_c) {
             constexpr int gi = NG - 1 - decltype(step_c)::value;
             using GI = std::integral_constant<int, gi>;
+            const Tw29 cur = nxt;
+            if constexpr (kPre && gi > 0)
+                nxt = entry(std::integral_constant<int, gi - 1>{}, INV{}, p.tw, s0, low, row);
             if constexpr (gi == NG - 1) {
                 load_global(GI{});
-                passes(GI{}, INV{}, FRESH{}, p.tw, s0, low, row);
+                passes(GI{}, INV{}, FRESH{}, p.tw, s0, low, row, cur);
             } else {
                 lds_read(GI{});
-                passes(GI{}, INV{}, OLD{}, p.tw, s0, low, row);
+                passes(GI{}, INV{}, OLD{}, p.tw, s0, low, row, cur);
             }
             if constexpr (gi == 0) {
                 store_global(GI{});
@@ -463,15 +553,24 @@ ntt_r8_kernel(BatchParams p) {
             }
         });
     } else {  // Fused: inverse groups high to low, coset multiply, forward groups low to high
+        if constexpr (kPre)
+            nxt = entry(std::integral_constant<int, NG - 1>{}, INV{}, p.tw, 0u, 0u, g);
         static_for<NG>([&](auto step_c) {
             constexpr int gi = NG - 1 - decltype(step_c)::value;
             using GI = std::integral_constant<int, gi>;
+            const Tw29 cur = nxt;
+            // after the last inverse group: the second forward group's (the first
+            // forward group, local bit 0, has twiddle 1)
+            if constexpr (kPre && gi > 0)
+                nxt = entry(std::integral_constant<int, gi - 1>{}, INV{}, p.tw, 0u, 0u, g);
+            else if constexpr (kPre && NG > 1)
+                nxt = entry(std::integral_constant<int, 1>{}, FWD{}, p.tw_fwd, 0u, 0u, g);
             if constexpr (gi == NG - 1) {
                 load_global(GI{});
-                passes(GI{}, INV{}, FRESH{}, p.tw, 0u, 0u, g);
+                passes(GI{}, INV{}, FRESH{}, p.tw, 0u, 0u, g, cur);
             } else {
                 lds_read(GI{});
-                passes(GI{}, INV{}, OLD{}, p.tw, 0u, 0u, g);
+                passes(GI{}, INV{}, OLD{}, p.tw, 0u, 0u, g, cur);
             }
             if constexpr (gi > 0) {
                 lds_write(GI{});
@@ -501,11 +600,14 @@ ntt_r8_kernel(BatchParams p) {
         });
         static_for<NG>([&](auto gi_c) {
             constexpr int gi = decltype(gi_c)::value;
+            const Tw29 cur = nxt;  // group 0: unused (twiddle 1); group 1: loaded above
+            if constexpr (kPre && gi >= 1 && gi + 1 < NG)
+                nxt = entry(std::integral_constant<int, gi + 1>{}, FWD{}, p.tw_fwd, 0u, 0u, g);
             if constexpr (gi == 0) {
-                passes(gi_c, FWD{}, FRESH{}, p.tw_fwd, 0u, 0u, g);  // coset products
+                passes(gi_c, FWD{}, FRESH{}, p.tw_fwd, 0u, 0u, g, cur);  // coset products
             } else {
                 lds_read(gi_c);
-                passes(gi_c, FWD{}, OLD{}, p.tw_fwd, 0u, 0u, g);
+                passes(gi_c, FWD{}, OLD{}, p.tw_fwd, 0u, 0u, g, cur);
             }
             if constexpr (gi == NG - 1) {
                 store_global(gi_c);

@@ -175,7 +175,9 @@ int g16_h_compute_batch(g16_ctx* ctx, uint64_t n_proofs, const void* a_mont,
  * transform's high batches, the fused lowest batch (end of the inverse, coset
  * multiply, start of the forward transform), the forward transform's high batches,
  * and the final batch of C with the join epilogue.  g16_h_stage_count returns their
- * number (2 * number of pass batches), or a negative code for a bad context.
+ * number (2 * number of pass batches; one fewer on small domains, where the final batch
+ * of A, B and C is one launch that joins them in LDS), or a negative code for a bad
+ * context.
  * g16_h_stage enqueues stage `stage` alone, with g16_h_compute's arguments and
  * checks; enqueueing stages 0 .. count-1 in order on one stream is exactly
  * g16_h_compute.  Lets a caller time or interleave individual kernels.

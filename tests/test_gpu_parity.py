@@ -61,24 +61,31 @@ def gpu_mont(words_std):
     return g.to_mont(g.to_device(words_std))
 
 
-class KMax:
-    """Run a block with a given batching cap (read by the library at prepare time)."""
+class Env:
+    """Run a block with library settings read at prepare time: the batching cap
+    (G16_MAX_K) and the register-group geometry (G16_NARROW: 1 narrow, 0 radix-4 groups,
+    unset: by launch size)."""
 
-    def __init__(self, kmax):
-        self.kmax = kmax
+    def __init__(self, **values):
+        self.values = {k: v for k, v in values.items() if v is not None}
 
     def __enter__(self):
-        self.prev = os.environ.get("G16_MAX_K")
-        if self.kmax is not None:
-            os.environ["G16_MAX_K"] = str(self.kmax)
+        self.prev = {k: os.environ.get(k) for k in self.values}
+        for k, v in self.values.items():
+            os.environ[k] = str(v)
         return self
 
     def __exit__(self, *exc):
-        if self.prev is None:
-            os.environ.pop("G16_MAX_K", None)
-        else:
-            os.environ["G16_MAX_K"] = self.prev
+        for k, v in self.prev.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
         return False
+
+
+def KMax(kmax, narrow=None):
+    return Env(G16_MAX_K=kmax, G16_NARROW=narrow)
 
 
 def h_inputs(workload, log_n, c_is_product=True):
@@ -129,11 +136,11 @@ def test_h_join(n):
 
 # ------------------------------------------------------------------ transforms
 
-def _ntt_case(log_n, kmax=None, workload=2):
-    say("ntt log_n=%d kmax=%s" % (log_n, kmax))
+def _ntt_case(log_n, kmax=None, workload=2, narrow=None):
+    say("ntt log_n=%d kmax=%s narrow=%s" % (log_n, kmax, narrow))
     x = synth.ntt_input(workload, log_n)
     xm = oracle.to_mont(x)
-    with KMax(kmax):
+    with KMax(kmax, narrow):
         ctx = g.HContext(log_n)
     xd = g.to_device(xm)
     fwd = ctx.ntt_forward(xd)
@@ -160,6 +167,15 @@ def test_ntt_other_batchings(log_n, kmax):
     _ntt_case(log_n, kmax)
 
 
+@pytest.mark.parametrize("log_n,kmax,narrow", [
+    (7, None, 1), (12, None, 1), (13, None, 1), (17, None, 1), (18, None, 1), (20, None, 1),
+    (12, None, 0), (14, None, 0)])
+def test_ntt_geometries(log_n, kmax, narrow):
+    """The register-group kernel's two geometries forced on domains where the size rule
+    would pick the other one (narrow: one pass per group; 0: radix-4 groups)."""
+    _ntt_case(log_n, kmax, narrow=narrow)
+
+
 def test_domain_roots_match_oracle():
     for log_n in (1, 12, 20, 27 - 5):
         ctx = g.HContext(log_n)
@@ -172,13 +188,13 @@ def test_domain_roots_match_oracle():
 
 # ------------------------------------------------------------------ H pipeline
 
-def _h_case(log_n, kmax=None, workload=1, c_is_product=True):
-    say("h_compute log_n=%d kmax=%s workload=%d c=A*B:%s" % (log_n, kmax, workload,
-                                                               c_is_product))
+def _h_case(log_n, kmax=None, workload=1, c_is_product=True, narrow=None):
+    say("h_compute log_n=%d kmax=%s workload=%d c=A*B:%s narrow=%s" % (
+        log_n, kmax, workload, c_is_product, narrow))
     (ad, bd, cd), (am, bm, cm) = h_inputs(workload, log_n, c_is_product)
     same(host(ad), am, "A to Montgomery")
     same(host(cd), cm, "C = A o B")
-    with KMax(kmax):
+    with KMax(kmax, narrow):
         ctx = g.HContext(log_n)
     hm, hs = ctx.h_compute(ad, bd, cd)
     want_m, want_s = oracle.h_pipeline(log_n, am, bm, cm)
@@ -201,16 +217,29 @@ def test_h_compute_other_batchings(log_n, kmax):
     ctx.release()
 
 
+# Both geometries of the register-group kernel on every batch size it takes (6..10) in
+# each of its modes (inverse strided, fused, forward strided, forward strided with the
+# join): narrow forced on larger domains, radix-4 groups forced on small ones.
+@pytest.mark.parametrize("log_n,kmax,narrow", [
+    (6, None, 1), (9, None, 1), (10, None, 1), (12, None, 1), (13, None, 1), (15, None, 1),
+    (16, None, 1), (18, None, 1), (20, None, 1), (12, 12, 1), (19, 7, 1),
+    (10, None, 0), (12, None, 0), (13, None, 0), (14, None, 0)])
+def test_h_compute_geometries(log_n, kmax, narrow):
+    ctx, _, _ = _h_case(log_n, kmax, workload=9, narrow=narrow)
+    ctx.release()
+
+
 def test_h_stages_compose_to_h_compute():
     import torch
-    for log_n, kmax in ((10, None), (16, None), (12, 4)):
+    for log_n, kmax in ((10, None), (16, None), (12, 4), (12, None), (9, None)):
         say("h stages log_n=%d kmax=%s" % (log_n, kmax))
         (ad, bd, cd), _ = h_inputs(8, log_n)
         with KMax(kmax):
             ctx = g.HContext(log_n)
         hm, hs = ctx.h_compute(ad, bd, cd)
         count = ctx.stage_count()
-        assert count == 2 * len(g.batch_plan(log_n, kmax or 0))
+        nb = len(g.batch_plan(log_n, kmax or 0))
+        assert count in (2 * nb, 2 * nb - 1)
         sm, ss = g.empty_fr(1 << log_n), g.empty_fr(1 << log_n)
         for i in range(count):
             ctx.h_stage(i, ad, bd, cd, sm, ss)
@@ -330,12 +359,12 @@ def test_large_domains(log_n):
     ctx.release()
 
 
-def _batch_case(log_n, proofs, kmax=None, seed=300):
+def _batch_case(log_n, proofs, kmax=None, seed=300, narrow=None):
     """proofs independent proofs stacked back to back through g16_h_compute_batch; every
     output of every proof against the oracle.  Even proofs use C = A o B, odd ones an
     independent C."""
     import torch
-    say("h_compute_batch 2^%d x %d proofs kmax=%s" % (log_n, proofs, kmax))
+    say("h_compute_batch 2^%d x %d proofs kmax=%s narrow=%s" % (log_n, proofs, kmax, narrow))
     dev, want = ([], [], []), []
     for q in range(proofs):
         (ad, bd, cd), (am, bm, cm) = h_inputs(seed + q, log_n, c_is_product=(q % 2 == 0))
@@ -343,7 +372,7 @@ def _batch_case(log_n, proofs, kmax=None, seed=300):
             lst.append(t)
         want.append(oracle.h_pipeline(log_n, am, bm, cm))
     a, b, c = (torch.cat(lst) for lst in dev)
-    with KMax(kmax):
+    with KMax(kmax, narrow):
         ctx = g.HContext(log_n)
     hm, hs = ctx.h_compute_batch(a, b, c)
     n = 1 << log_n
@@ -354,11 +383,12 @@ def _batch_case(log_n, proofs, kmax=None, seed=300):
     return ctx, (a, b, c), (hm, hs)
 
 
-@pytest.mark.parametrize("log_n,proofs,kmax", [(1, 3, None), (5, 4, None), (9, 2, 4),
-                                               (10, 3, None), (12, 5, None), (13, 3, 4),
-                                               (16, 3, None), (18, 2, None)])
-def test_h_compute_batch(log_n, proofs, kmax):
-    ctx, _, _ = _batch_case(log_n, proofs, kmax)
+@pytest.mark.parametrize("log_n,proofs,kmax,narrow", [
+    (1, 3, None, None), (5, 4, None, None), (9, 2, 4, None), (10, 3, None, None),
+    (12, 5, None, None), (13, 3, 4, None), (16, 3, None, None), (18, 2, None, None),
+    (8, 3, None, 1), (12, 3, None, 1), (14, 2, None, 1), (16, 2, None, 1), (12, 2, None, 0)])
+def test_h_compute_batch(log_n, proofs, kmax, narrow):
+    ctx, _, _ = _batch_case(log_n, proofs, kmax, narrow=narrow)
     ctx.release()
 
 
