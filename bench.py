@@ -159,13 +159,17 @@ MSM_SOURCES = {"fp.hpp", "fp29.hpp", "fp29_cols.hpp", "fp29_cols_gen.py", "g1.hp
                "msm_digit.hpp", "msm_kernels.hpp"}
 
 
+# Sources of the BabyBear transform only.
+BB_SOURCES = {"bb.hip", "bb_field.hpp", "bb_ntt.hpp"}
+
+
 def kernel_source_hash() -> str:
     """Hash of the H pipeline's kernel sources' code (comments and whitespace ignored),
     which ties a committed counter summary to the kernels it was measured on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "groth16_polynomial_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        if f in MSM_SOURCES or not os.path.isfile(os.path.join(csrc, f)):
+        if f in MSM_SOURCES or f in BB_SOURCES or not os.path.isfile(os.path.join(csrc, f)):
             continue
         with open(os.path.join(csrc, f), encoding="utf-8") as fh:
             h.update(f.encode() + _code_only(fh.read()).encode())
@@ -330,6 +334,22 @@ def msm_leg(g, synth, torch, tm, hs, log_n, steps, log):
     return line
 
 
+def copy_calibration(torch, mib):
+    """A plain device copy of mib MiB, three times: a kernel of known traffic that scales
+    rocprofv3's FETCH_SIZE and WRITE_SIZE of the same run."""
+    if not mib:
+        return None
+    nbytes = mib << 20
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    return nbytes
+
+
 def main():
     args = parse()
     if args.part == "h":
@@ -368,12 +388,16 @@ def main():
     torch.cuda.synchronize()
     line_extra = {}
     if args.part == "bb":
-        print(json.dumps({"bb_lde": bb_leg(g, synth, torch, tm, args.steps, log)}), flush=True)
+        out = {"bb_lde": bb_leg(g, synth, torch, tm, args.steps, log),
+               "copy_calibration_bytes": copy_calibration(torch, args.copy_calibration_mib)}
+        print(json.dumps(out), flush=True)
         ctx.release()
         return
     if args.part == "msm":
-        print(json.dumps({"msm_g1": msm_leg(g, synth, torch, tm, hs_of(ctx, ad, bd, cd, hm, hs),
-                                            log_n, args.steps, log)}), flush=True)
+        out = {"msm_g1": msm_leg(g, synth, torch, tm, hs_of(ctx, ad, bd, cd, hm, hs), log_n,
+                                 args.steps, log),
+               "copy_calibration_bytes": copy_calibration(torch, args.copy_calibration_mib)}
+        print(json.dumps(out), flush=True)
         ctx.release()
         return
 
@@ -629,15 +653,7 @@ def main():
         line["msm_g1"] = msm_line
 
     if args.copy_calibration_mib:
-        nbytes = args.copy_calibration_mib << 20
-        src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        line["copy_calibration_bytes"] = nbytes
-        del src, dst
+        line["copy_calibration_bytes"] = copy_calibration(torch, args.copy_calibration_mib)
 
     if not args.no_cpu_baseline:
         import oracle
