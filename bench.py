@@ -60,10 +60,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-side", action="store_true",
                     help="only the timed 2^log_n pipeline and its stages (for profiling)")
-    ap.add_argument("--part", choices=("all", "h", "msm", "bb"), default="all",
+    ap.add_argument("--part", choices=("all", "h", "msm", "bb", "probe"), default="all",
                     help="h: only the timed pipeline and its stages (as --no-side, no CPU "
                          "baseline); msm: only the G1 MSM legs; bb: only the BabyBear "
-                         "encoding legs (for profiling)")
+                         "encoding legs; probe: only the instruction-rate probe (for "
+                         "profiling)")
     ap.add_argument("--stage-reps", type=int, default=10)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (a known-size "
@@ -387,6 +388,10 @@ def main():
     tm = Timer(torch)
     torch.cuda.synchronize()
     line_extra = {}
+    if args.part == "probe":
+        print(json.dumps({"instruction_rates": probe_rates(log)}), flush=True)
+        ctx.release()
+        return
     if args.part == "bb":
         out = {"bb_lde": bb_leg(g, synth, torch, tm, args.steps, log),
                "copy_calibration_bytes": copy_calibration(torch, args.copy_calibration_mib)}

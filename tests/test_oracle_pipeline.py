@@ -157,3 +157,26 @@ def test_coset_eval_is_the_pipeline_first_half(log_n):
                         oracle.from_mont(cc))
     _, h_std = oracle.h_pipeline(log_n, am, bm, cm)
     assert (H == h_std).all()
+
+
+def test_thread_count_does_not_change_results():
+    """The oracle splits independent loops over threads; the same inputs give the same
+    words on one thread and on several (H pipeline, both encodings, and the sampled
+    barycentric route)."""
+    log_n = 13
+    a, b = synth.h_inputs(17, log_n)
+    am, bm = oracle.to_mont(a), oracle.to_mont(b)
+    cm = oracle.pointwise_mul_mont(am, bm)
+    idx = np.array([0, 1, 4095, (1 << log_n) - 1], np.uint32)
+    prev = oracle.set_threads(1)
+    try:
+        one = oracle.h_pipeline(log_n, am, bm, cm)
+        one_at = oracle.h_at(log_n, am, bm, cm, idx)
+        oracle.set_threads(8)
+        many = oracle.h_pipeline(log_n, am, bm, cm)
+        many_at = oracle.h_at(log_n, am, bm, cm, idx)
+    finally:
+        oracle.set_threads(prev)
+    for x, y in zip(one + one_at, many + many_at):
+        assert np.array_equal(x, y)
+    assert np.array_equal(one[0][idx], one_at[0])
