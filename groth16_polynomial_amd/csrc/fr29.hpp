@@ -397,13 +397,15 @@ G16_HD V29 shoup_mul(const V29& x, const Tw29& t) {
     return ys[0];
 }
 
-// Any V29 with digits below 2^31 in magnitude -> canonical 8 x 32-bit.
+// Any V29 with digits below 2^31 in magnitude -> 8 x 32-bit words of a value in [0, 2r)
+// congruent to it (fr29_canon without the last step; what the transform batches hand to
+// one another, since fr29_from_fr and the table products take any value below 2^256).
 //   1. exact carry propagation (digits 0..7 in [0, 2^29), digit 8 signed);
 //   2. q = floor(value / r) or one less, from the top two digits in double precision
 //      (the error of the estimate is below 2^-40, the margin 2^-10);
 //   3. value - q r = (value + q (-r)) mod 2^261, in [0, 2r);
-//   4. pack and one conditional subtraction.
-G16_HD Fr fr29_canon(const V29& a) {
+//   4. pack.
+G16_HD Fr fr29_reduce_2r(const V29& a) {
     int32_t l[9];
 #pragma unroll
     for (int k = 0; k < 9; ++k) l[k] = a.l[k];
@@ -424,8 +426,12 @@ G16_HD Fr fr29_canon(const V29& a) {
         y.l[k] = (int32_t)((uint32_t)acc & kM29);
         acc >>= 29;
     }
-    return fr_reduce_once(fr29_pack(y));
+    return fr29_pack(y);
 }
+
+// Any V29 with digits below 2^31 in magnitude -> canonical 8 x 32-bit: fr29_reduce_2r and
+// one conditional subtraction.
+G16_HD Fr fr29_canon(const V29& a) { return fr_reduce_once(fr29_reduce_2r(a)); }
 
 // Unsigned 29-bit digits (the top one below 2^29) -> balanced digits, value unchanged.
 G16_HD void balance29(const uint32_t (&d)[9], int32_t (&o)[9]) {

@@ -254,6 +254,7 @@ int run_ntt(g16_ctx* c, const void* in, void* out, void* stream, bool inverse) {
     p.src[0] = (const Fr*)in;
     const bool single = c->n_batches == 1;
     p.dst[0] = (single && in != out) ? (Fr*)out : scr;
+    p.lazy_out = single ? 0u : 1u;  // only the last batch's output must be canonical
     const bool narrow = use_narrow(c, 1);
     int rc = launch_batch<g16::Mode::HeadBitrev, false>(p, 1, c->radix2, narrow, s);
     if (rc) return rc;
@@ -271,6 +272,7 @@ int run_ntt(g16_ctx* c, const void* in, void* out, void* stream, bool inverse) {
         t.k = c->batch_k[b];
         t.src[0] = scr;
         t.dst[0] = (b + 1 == c->n_batches) ? (Fr*)out : scr;
+        t.lazy_out = (b + 1 == c->n_batches) ? 0u : 1u;
         rc = launch_batch<g16::Mode::FwdStrided, false>(t, 1, c->radix2, narrow, s);
         if (rc) return rc;
     }
@@ -361,9 +363,12 @@ uint32_t plan_coset(const g16_ctx* c, const Fr* const* srcs, Fr* const* dsts, ui
         p.h_std = h_std;
         return p;
     };
+    // Outputs that only further transform batches read are stored in [0, 2r) (lazy_out);
+    // the last batch's outputs, and A' and B' that the join reads, are canonical.
     // inverse transform, high batches first (DIF), the first one reading the inputs
     for (uint32_t b = nb - 1; b >= 1; --b) {
         g16::BatchParams p = base_params(c);
+        p.lazy_out = 1u;
         p.tw = c->tw_inv;
         p.s0 = batch_s0(c, b);
         p.k = c->batch_k[b];
@@ -379,6 +384,7 @@ uint32_t plan_coset(const g16_ctx* c, const Fr* const* srcs, Fr* const* dsts, ui
     f.tw_fwd = c->tw_fwd;
     f.scale = c->coset;
     f.k = c->batch_k[0];
+    f.lazy_out = nb > 1 ? 1u : 0u;
     for (uint32_t v = 0; v < n_kind; ++v) {
         f.src[v] = (nb == 1) ? srcs[v] : dsts[v];
         f.dst[v] = dsts[v];
@@ -399,6 +405,7 @@ uint32_t plan_coset(const g16_ctx* c, const Fr* const* srcs, Fr* const* dsts, ui
         p.tw = c->tw_fwd;
         p.s0 = batch_s0(c, b);
         p.k = c->batch_k[b];
+        p.lazy_out = b + 1 < nb ? 1u : 0u;
         for (uint32_t v = 0; v < n_kind; ++v) {
             p.src[v] = dsts[v];
             p.dst[v] = dsts[v];

@@ -65,6 +65,8 @@ struct BatchParams {
     uint32_t head_inverse;  // HeadBitrev: the inverse transform (see the head load)
     uint32_t n_vec;       // register-group kernel: number of vectors (grid = groups x n_vec)
     uint32_t n_kind;      // vectors per proof in this launch, 1..3
+    uint32_t lazy_out;    // register-group kernel: the output feeds only further transform
+                          // batches, so it is stored in [0, 2r) (no final subtraction)
     uint64_t vstride;     // elements from one proof's vectors to the next proof's
 };
 
@@ -272,10 +274,10 @@ __global__ void __launch_bounds__(256) ntt_batch_kernel(BatchParams p) {
         uint64_t i = gindex(sl, m);
         Fr x;
         if (M == Mode::HeadBitrev) {
-            x = ld_global(src + head_index(i, p.log_n, p.head_inverse));
+            x = ld_global(src + head_index(i, p.log_n, p.head_inverse));  // caller's, canonical
             if (p.head_inverse) x = fr_mul_entry(x, p.kscale);
         } else {
-            x = ld_global(src + i);
+            x = fr_reduce_once(ld_global(src + i));  // another batch's output: [0, 2r)
         }
         st_lds(sh + ((size_t)sl << k) + m, x);
     }

@@ -449,9 +449,12 @@ ntt_group_kernel(BatchParams p) {
         for_group(gi_c, [&](auto xi_c, uint32_t e) {
             constexpr int xi = decltype(xi_c)::value;
             const uint64_t i = gidx(e);
-            const Fr v = fr29_canon(x[xi]);
-            if constexpr (JOIN) store_h(p, off + i, v);
-            else st_global(dst + i, v);
+            if constexpr (JOIN) {
+                store_h(p, off + i, fr29_canon(x[xi]));
+            } else {
+                const Fr v = fr29_reduce_2r(x[xi]);
+                st_global(dst + i, p.lazy_out ? v : fr_reduce_once(v));
+            }
         });
     };
     auto lds_write = [&](auto gi_c) {
