@@ -397,23 +397,20 @@ G16_HD V29 shoup_mul(const V29& x, const Tw29& t) {
     return ys[0];
 }
 
-// Any V29 with digits below 2^31 in magnitude -> 8 x 32-bit words of a value in [0, 2r)
-// congruent to it (fr29_canon without the last step; what the transform batches hand to
-// one another, since fr29_from_fr and the table products take any value below 2^256).
-//   1. exact carry propagation (digits 0..7 in [0, 2^29), digit 8 signed);
-//   2. q = floor(value / r) or one less, from the top two digits in double precision
-//      (the error of the estimate is below 2^-40, the margin 2^-10);
-//   3. value - q r = (value + q (-r)) mod 2^261, in [0, 2r);
-//   4. pack.
+// Any V29 with digits 0..7 below 2^31 and digit 8 below 2^30 in magnitude -> 8 x 32-bit
+// words of a value in [0, 2r) congruent to it (fr29_canon without the last step; what the
+// transform batches hand to one another, since fr29_from_fr and the table products take
+// any value below 2^256).
+//   1. q = floor(value / r) or one less, from the top two digits as they are, in double
+//      precision: the digits below contribute less than 2^205 (2^-48 of r), the
+//      estimate's own error is below 2^-40, the margin 2^-10;
+//   2. value - q r = (value + q (-r)) mod 2^261, in [0, 2r), its digits' carries taken
+//      along one multiply-add row (so the digits need no normalization first);
+//   3. pack.
 G16_HD Fr fr29_reduce_2r(const V29& a) {
     int32_t l[9];
 #pragma unroll
     for (int k = 0; k < 9; ++k) l[k] = a.l[k];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        l[k + 1] += l[k] >> 29;
-        l[k] &= (int32_t)kM29;
-    }
     // 2^232 / r and 2^203 / r
     const double c8 = 0x1.5291d18988e81p-22, c7 = 0x1.5291d18988e81p-51;
     const double qd = floor((double)l[8] * c8 + (double)l[7] * c7 - 0x1p-10);
