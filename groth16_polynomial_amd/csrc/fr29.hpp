@@ -47,13 +47,22 @@ struct V29 {
 };
 
 // A table entry: w and w' = floor(w 2^261 / r) in balanced 29-bit digits, padded to
-// 80 bytes so an entry is five 16-byte loads.
+// 80 bytes: five 16-byte parts (w0-3, w4-7, w8 w'0-2, w'3-6, w'7-8 and padding).
 struct Tw29 {
     int32_t w[9];
     int32_t wp[9];
     int32_t pad[2];
 };
 static_assert(sizeof(Tw29) == 80, "table entries are 80 bytes");
+
+// A table of entries in five planes: part q of entry e at base[q * stride + e], so the
+// lanes of a wave that read neighbouring entries read one contiguous run per part (a few
+// cache lines per load instruction) instead of 80-byte records spread over five times
+// as many lines.
+struct TwTab {
+    uint4* base;
+    uint32_t stride;  // entries per plane
+};
 
 // -r in balanced 29-bit digits (x w - q r is formed as x w + q (-r))
 G16_HD constexpr int32_t mr29_digit(int k) {

@@ -37,9 +37,10 @@ struct g16_ctx {
     uint32_t magic;
     uint32_t log_n;
     int device;
-    g16::Tw29* tw_fwd;  // powers of omega by level (n - 1 entries)
-    g16::Tw29* tw_inv;  // powers of omega^-1 by level, bit-reversed within each level
-    g16::Tw29* coset;   // n^-1 s^bitrev(p), p < n
+    g16::TwTab tw_fwd;  // powers of omega by level (n - 1 entries)
+    g16::TwTab tw_inv;  // powers of omega^-1 by level, bit-reversed within each level
+    g16::TwTab coset;   // n^-1 s^bitrev(p), p < n
+                        // (each in five planes of n 16-byte parts)
     Fr* scratch;  // three n-element vectors
     const uint8_t* ws_begin;
     size_t ws_bytes;
@@ -558,9 +559,9 @@ int g16_h_prepare(uint32_t log_n, void* workspace, size_t workspace_bytes, void*
     const size_t n = size_t(1) << log_n;
     uint8_t* ws = (uint8_t*)workspace;
     size_t tab = round_up(n * sizeof(g16::Tw29));
-    c->tw_fwd = (g16::Tw29*)ws;
-    c->tw_inv = (g16::Tw29*)(ws + tab);
-    c->coset = (g16::Tw29*)(ws + 2 * tab);
+    c->tw_fwd = g16::TwTab{(uint4*)ws, (uint32_t)n};
+    c->tw_inv = g16::TwTab{(uint4*)(ws + tab), (uint32_t)n};
+    c->coset = g16::TwTab{(uint4*)(ws + 2 * tab), (uint32_t)n};
     c->scratch = (Fr*)(ws + 3 * tab);
     c->ws_begin = ws;
     c->ws_bytes = g16_h_workspace_bytes(log_n);

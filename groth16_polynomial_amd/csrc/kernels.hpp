@@ -50,9 +50,9 @@ struct BatchParams {
     // below, and so do its join inputs and outputs.
     const Fr* src[3];
     Fr* dst[3];
-    const Tw29* tw;       // twiddles of this batch's passes (Fused: the inverse table)
-    const Tw29* tw_fwd;   // Fused only: the forward table
-    const Tw29* scale;    // Fused only: S[p]
+    TwTab tw;             // twiddles of this batch's passes (Fused: the inverse table)
+    TwTab tw_fwd;         // Fused only: the forward table
+    TwTab scale;          // Fused only: S[p]
     const Fr* join_a;     // store epilogue H = A' B' - x (join kernels only)
     const Fr* join_b;
     Fr* h_mont;
@@ -97,38 +97,52 @@ __device__ __forceinline__ void st_global(Fr* p, const Fr& x) {
 __device__ __forceinline__ Fr ld_lds(const Fr* p) { return ld_global(p); }
 __device__ __forceinline__ void st_lds(Fr* p, const Fr& x) { st_global(p, x); }
 
-// A table entry: four 16-byte and one 8-byte vector load.  The address goes through an opaque zero
+// Table entry e: four 16-byte and one 8-byte vector load, one per plane, each a wave-
+// uniform plane base plus the lane's 32-bit offset.  The index goes through an opaque zero
 // held in a VGPR: an entry every lane of a wave needs would otherwise be read with
 // scalar loads into SGPRs, and the compiler lowers a signed 32 x 32-bit multiply-add
 // with a sign-extended SGPR operand as four instructions instead of one
 // v_mad_i64_i32.
-__device__ __forceinline__ Tw29 ld_tw(const Tw29* p) {
+__device__ __forceinline__ Tw29 ld_tw(const TwTab& tab, uint32_t e) {
     uint32_t z;
     asm("v_mov_b32 %0, 0" : "=v"(z));
-    const uint4* q = reinterpret_cast<const uint4*>(p + z);
-    uint4 a = q[0], b = q[1], c = q[2], d = q[3];
-    uint2 e = *reinterpret_cast<const uint2*>(q + 4);
+    // a 32-bit byte offset (tables hold at most 2^27 entries) on wave-uniform plane bases:
+    // one address computation per entry, the planes' bases in SGPRs
+    const uint32_t off = (e + z) * 16u;
+    const char* b0 = reinterpret_cast<const char*>(tab.base);
+    const size_t ps = (size_t)tab.stride * 16u;
+    const uint4 a = *reinterpret_cast<const uint4*>(b0 + off);
+    const uint4 b = *reinterpret_cast<const uint4*>(b0 + ps + off);
+    const uint4 c = *reinterpret_cast<const uint4*>(b0 + 2 * ps + off);
+    const uint4 d = *reinterpret_cast<const uint4*>(b0 + 3 * ps + off);
+    const uint2 e_ = *reinterpret_cast<const uint2*>(b0 + 4 * ps + off);
     Tw29 t;
     t.w[0] = a.x; t.w[1] = a.y; t.w[2] = a.z; t.w[3] = a.w;
     t.w[4] = b.x; t.w[5] = b.y; t.w[6] = b.z; t.w[7] = b.w;
     t.w[8] = c.x; t.wp[0] = c.y; t.wp[1] = c.z; t.wp[2] = c.w;
     t.wp[3] = d.x; t.wp[4] = d.y; t.wp[5] = d.z; t.wp[6] = d.w;
-    t.wp[7] = e.x; t.wp[8] = e.y; t.pad[0] = 0u; t.pad[1] = 0u;
+    t.wp[7] = e_.x; t.wp[8] = e_.y; t.pad[0] = 0u; t.pad[1] = 0u;
     return t;
 }
 
 // An entry every lane of the wave needs (idx equal in all lanes, which the caller
 // guarantees): scalar loads into SGPRs, which the product takes as scalar operands and
 // which leave the vector memory path to the lanes' own data.
-__device__ __forceinline__ Tw29 ld_tw_uniform(const Tw29* tab, uint32_t idx) {
+__device__ __forceinline__ Tw29 ld_tw_uniform(const TwTab& tab, uint32_t idx) {
     typedef const __attribute__((address_space(4))) uint32_t* cptr;
     const uint32_t u = __builtin_amdgcn_readfirstlane(idx);
-    cptr q = (cptr)(tab + u);
+    uint32_t d[20];
+#pragma unroll
+    for (int q = 0; q < 5; ++q) {
+        cptr part = (cptr)(tab.base + (size_t)q * tab.stride + u);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) d[4 * q + k] = part[k];
+    }
     Tw29 t;
 #pragma unroll
-    for (int k = 0; k < 9; ++k) t.w[k] = (int32_t)q[k];
+    for (int k = 0; k < 9; ++k) t.w[k] = (int32_t)d[k];
 #pragma unroll
-    for (int k = 0; k < 9; ++k) t.wp[k] = (int32_t)q[9 + k];
+    for (int k = 0; k < 9; ++k) t.wp[k] = (int32_t)d[9 + k];
     t.pad[0] = t.pad[1] = 0;
     return t;
 }
@@ -213,7 +227,7 @@ __device__ __forceinline__ Fr fr_mul_entry(const Fr& x, const Tw29& t) {
 //   bit t of the local index is flipped; the global bit is s0 + t; slice g0 + sl has
 //   column low = (g0 + sl) mod 2^s0 and row h = (g0 + sl) >> s0.
 template <bool INV>
-__device__ __forceinline__ void lds_pass(Fr* sh, const Tw29* tw, uint32_t log_n, uint32_t s0,
+__device__ __forceinline__ void lds_pass(Fr* sh, const TwTab& tw, uint32_t log_n, uint32_t s0,
                                          uint32_t k, uint32_t t, uint32_t n_bfly,
                                          uint32_t g0) {
     const uint32_t half_k = 1u << (k - 1u);
@@ -232,7 +246,7 @@ __device__ __forceinline__ void lds_pass(Fr* sh, const Tw29* tw, uint32_t log_n,
         const uint32_t idx = INV ? inv_tw_index(log_n, s0, k, t, bf >> t, g >> s0)
                                  : fwd_tw_index(log_n, s0, t, low, jm);
         // exponent 0 is the twiddle 1
-        Fr vw = ex == 0u ? v : fr_mul_entry(v, ld_tw(tw + idx));
+        Fr vw = ex == 0u ? v : fr_mul_entry(v, ld_tw(tw, idx));
         st_lds(base + lo, fr_add(u, vw));
         st_lds(base + hi, fr_sub(u, vw));
     }
@@ -293,7 +307,7 @@ __global__ void __launch_bounds__(256) ntt_batch_kernel(BatchParams p) {
         for (uint32_t e = threadIdx.x; e < total; e += blockDim.x) {
             uint32_t sl = e >> k, m = e & (slice_len - 1u);
             Fr* q = sh + ((size_t)sl << k) + m;
-            st_lds(q, fr_mul_entry(ld_lds(q), ld_tw(p.scale + gindex(sl, m))));
+            st_lds(q, fr_mul_entry(ld_lds(q), ld_tw(p.scale, (uint32_t)gindex(sl, m))));
         }
         __syncthreads();
         for (uint32_t t = 0; t < k; ++t)

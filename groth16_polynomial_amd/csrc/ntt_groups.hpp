@@ -157,7 +157,7 @@ constexpr int nth_nontrivial(int nb, int k) {
 // inside 32 bits.
 template <int OFF, int R, int U, unsigned TRIV, int CH, bool LAZY, bool UNI, int E, typename IdxF>
 __device__ __forceinline__ void ct_pass(V29 (&x)[E], const Tw29 (&pw)[1 << (R - 1)],
-                                        const Tw29* tw, IdxF&& idx) {
+                                        const TwTab& tw, IdxF&& idx) {
     constexpr int NB = 1 << (R - 1);
     constexpr int NT = count_nontrivial<TRIV>(NB);
     auto lower = [](int b) { return ((b >> U) << (U + 1)) | (b & ((1 << U) - 1)); };
@@ -177,7 +177,7 @@ __device__ __forceinline__ void ct_pass(V29 (&x)[E], const Tw29 (&pw)[1 << (R - 
             constexpr int b = nth_nontrivial<TRIV>(NB, c0 + j);
             h[j] = x[OFF + lower(b) + (1 << U)];
             if constexpr (LAZY && UNI) w[j] = ld_tw_uniform(tw, idx(std::integral_constant<int, b>{}));
-            else if constexpr (LAZY) w[j] = ld_tw(tw + idx(std::integral_constant<int, b>{}));
+            else if constexpr (LAZY) w[j] = ld_tw(tw, idx(std::integral_constant<int, b>{}));
             else w[j] = pw[c0 + j];
         });
         shoup_mul_n<nc, LAZY && UNI>(h, w, y);
@@ -205,7 +205,7 @@ __device__ __forceinline__ void ct_pass(V29 (&x)[E], const Tw29 (&pw)[1 << (R - 
 // PRE: a one-pass group whose entry the caller loaded earlier (pre).
 template <int OFF, int R, bool INV, bool NORM, int CH, bool PF, bool UNI, unsigned TM0,
           unsigned TM1, unsigned TM2, bool PRE, int E, typename IdxFor>
-__device__ __forceinline__ void run_passes(V29 (&x)[E], const Tw29* tw, IdxFor&& idx_for,
+__device__ __forceinline__ void run_passes(V29 (&x)[E], const TwTab& tw, IdxFor&& idx_for,
                                            const Tw29& pre) {
     static_assert(!PRE || (R == 1 && !PF), "a preloaded entry serves one-pass groups");
     constexpr int NB = 1 << (R - 1);
@@ -224,7 +224,7 @@ __device__ __forceinline__ void run_passes(V29 (&x)[E], const Tw29* tw, IdxFor&&
                 static_for<j1 - j0>([&](auto j_c) {
                     constexpr int j = j0 + decltype(j_c)::value;
                     constexpr int b = nth_nontrivial<tm[u]>(NB, j);
-                    ent[s][j] = ld_tw(tw + idx(std::integral_constant<int, b>{}));
+                    ent[s][j] = ld_tw(tw, idx(std::integral_constant<int, b>{}));
                 });
             }
         }
@@ -263,7 +263,7 @@ __device__ __forceinline__ void run_passes(V29 (&x)[E], const Tw29* tw, IdxFor&&
 // the pass equal to (c mod 2^B0) + (q mod 2^u) 2^B0.  Global bit 0 has twiddle 1.
 template <int OFF, int R, int B0, bool NORM, bool CONTIG, int CH, bool PF, int E, bool PRE>
 __device__ __forceinline__ void group_fwd(V29 (&x)[E], uint32_t c, uint32_t low, uint32_t s0,
-                                          uint32_t log_n, const Tw29* tw, const Tw29& pre) {
+                                          uint32_t log_n, const TwTab& tw, const Tw29& pre) {
     const uint32_t cl = c & ((1u << B0) - 1u);
     auto idx_for = [&](auto u_c) {
         return [&](auto b_c) {  // u from the type alone: the lambda outlives this call
@@ -291,7 +291,7 @@ __device__ __forceinline__ void group_fwd(V29 (&x)[E], uint32_t c, uint32_t low,
 // the same in all of them), so for B0 >= LB every entry of the group is wave-uniform.
 template <int OFF, int R, int B0, int K, bool NORM, int CH, bool PF, int LB, int E, bool PRE>
 __device__ __forceinline__ void group_inv(V29 (&x)[E], uint32_t c, uint32_t h, uint32_t s0,
-                                          uint32_t log_n, const Tw29* tw, const Tw29& pre) {
+                                          uint32_t log_n, const TwTab& tw, const Tw29& pre) {
     const uint32_t ch = c >> B0;
     auto idx_for = [&](auto u_c) {
         return [&](auto b_c) {  // u from the type alone: the lambda outlives this call
@@ -472,7 +472,7 @@ ntt_group_kernel(BatchParams p) {
     // passes of group GI in the forward or inverse order; FRESH: the elements come
     // straight from HBM or from a product (no normalization needed); pre: the group's
     // entry, loaded ahead (narrow geometry)
-    auto passes = [&](auto gi_c, auto inv_c, auto fresh_c, const Tw29* tw, uint32_t ls0,
+    auto passes = [&](auto gi_c, auto inv_c, auto fresh_c, const TwTab& tw, uint32_t ls0,
                       uint32_t llow, uint32_t lrow, const Tw29& pre) {
         constexpr int gi = decltype(gi_c)::value;
         constexpr bool inv = decltype(inv_c)::value;
@@ -494,13 +494,13 @@ ntt_group_kernel(BatchParams p) {
     // entry of the next group is loaded while this one runs (its index depends only on
     // the thread's position), so no product waits for its entry.  entry(GI): group GI's
     // entry (group_fwd / group_inv with R = 1, c = t).
-    auto entry = [&](auto gi_c, auto inv_c, const Tw29* tw, uint32_t ls0, uint32_t llow,
+    auto entry = [&](auto gi_c, auto inv_c, const TwTab& tw, uint32_t ls0, uint32_t llow,
                      uint32_t lrow) -> Tw29 {
         constexpr uint32_t b0 = decltype(gi_c)::value;
         if constexpr (decltype(inv_c)::value)
-            return ld_tw(tw + inv_tw_index(L, ls0, K, b0, t >> b0, lrow));
+            return ld_tw(tw, inv_tw_index(L, ls0, K, b0, t >> b0, lrow));
         else
-            return ld_tw(tw + fwd_tw_index(L, ls0, b0, llow, t & ((1u << b0) - 1u)));
+            return ld_tw(tw, fwd_tw_index(L, ls0, b0, llow, t & ((1u << b0) - 1u)));
     };
     using FWD = std::false_type;
     using INV = std::true_type;
@@ -593,7 +593,7 @@ ntt_group_kernel(BatchParams p) {
             static_for<NC>([&](auto j_c) {
                 constexpr int j = decltype(j_c)::value;
                 h[j] = x[i0 + j];
-                w[j] = ld_tw(p.scale + gidx(ce[i0 + j]));
+                w[j] = ld_tw(p.scale, (uint32_t)gidx(ce[i0 + j]));
             });
             shoup_mul_n<NC>(h, w, y);
             static_for<NC>([&](auto j_c) {

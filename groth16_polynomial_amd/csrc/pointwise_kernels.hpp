@@ -39,13 +39,14 @@ __global__ void __launch_bounds__(256) elementwise_kernel(const Fr* a, const Fr*
 //   kind 2: the same levels bit-reversed: entry n - n/2^m + j is
 //           base^(2^m bitrev_(L-1-m)(j))
 //   kind 1: T[p] = factor * base^bitrev_L(p)      (coset table, p < count = 2^L)
-__device__ __forceinline__ void st_tw(Tw29* p, const Tw29& t) {
-    uint4* q = reinterpret_cast<uint4*>(p);
+__device__ __forceinline__ void st_tw(const TwTab& tab, uint64_t e, const Tw29& t) {
+    uint4* q = tab.base + e;
+    const size_t s = tab.stride;
     q[0] = make_uint4(t.w[0], t.w[1], t.w[2], t.w[3]);
-    q[1] = make_uint4(t.w[4], t.w[5], t.w[6], t.w[7]);
-    q[2] = make_uint4(t.w[8], t.wp[0], t.wp[1], t.wp[2]);
-    q[3] = make_uint4(t.wp[3], t.wp[4], t.wp[5], t.wp[6]);
-    q[4] = make_uint4(t.wp[7], t.wp[8], 0u, 0u);
+    q[s] = make_uint4(t.w[4], t.w[5], t.w[6], t.w[7]);
+    q[2 * s] = make_uint4(t.w[8], t.wp[0], t.wp[1], t.wp[2]);
+    q[3 * s] = make_uint4(t.wp[3], t.wp[4], t.wp[5], t.wp[6]);
+    q[4 * s] = make_uint4(t.wp[7], t.wp[8], 0u, 0u);
 }
 
 // Twiddle and coset tables, one 80-byte entry per thread (grid-stride loop).
@@ -53,7 +54,7 @@ __device__ __forceinline__ void st_tw(Tw29* p, const Tw29& t) {
 //           batch plan whose start bits are set in batch_starts (bit 0 always);
 //   kind 2: inverse levels (omega^-1 = base), bit-reversed within each level;
 //   kind 1: coset table, entry p = factor base^bitrev(p).
-__global__ void __launch_bounds__(256) table_kernel(Tw29* out, Fr base, Fr factor,
+__global__ void __launch_bounds__(256) table_kernel(TwTab out, Fr base, Fr factor,
                                                     uint64_t count, uint32_t log_n, int kind,
                                                     uint32_t batch_starts) {
     const uint64_t n = 1ull << log_n;
@@ -79,7 +80,7 @@ __global__ void __launch_bounds__(256) table_kernel(Tw29* out, Fr base, Fr facto
             uint64_t e = bitrev_bits((uint32_t)j, log_n);
             v = fr_mul(factor, fr_pow_u64(base, e));
         }
-        st_tw(out + j, tw29_entry(v));
+        st_tw(out, j, tw29_entry(v));
     }
 }
 
