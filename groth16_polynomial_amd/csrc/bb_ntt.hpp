@@ -49,6 +49,17 @@ __device__ __forceinline__ void bb_static_for(F&& f) {
     bb_static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// Word i of an array by a 32-bit byte offset on a wave-uniform base (a matrix holds at most
+// 2^30 words): one address computation per access, the base in SGPRs.
+template <typename T>
+__device__ __forceinline__ T& bb_at(T* base, uint32_t i) {
+    return *reinterpret_cast<T*>(reinterpret_cast<char*>(base) + i * (uint32_t)sizeof(T));
+}
+template <typename T>
+__device__ __forceinline__ const T& bb_at(const T* base, uint32_t i) {
+    return *reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + i * (uint32_t)sizeof(T));
+}
+
 struct BbParams {
     const uint32_t* src;  // input matrices (first batch), else == dst
     uint32_t* dst;
@@ -137,7 +148,7 @@ __global__ void __launch_bounds__(512) bb_batch_kernel(BbParams p) {
             const uint32_t sp = q & (spw - 1u);
             const uint32_t gr = sp >> lwc, ci = sp & (wc - 1u);
             const uint32_t row = (mrev << (L - K)) + (rev_h0 << lg) + gr;
-            const uint32_t v = row < h_in ? in[((uint64_t)row << lw) + cb * wc + ci] : 0u;
+            const uint32_t v = row < h_in ? bb_at(in, (row << lw) + cb * wc + ci) : 0u;
             const uint32_t slot_sl = (bb_bitrev(gr, lg) << lwc) + ci;
             lds[bb_bitrev(mrev, K) * pitch + slot_sl] = v;
         }
@@ -155,7 +166,7 @@ __global__ void __launch_bounds__(512) bb_batch_kernel(BbParams p) {
         auto m_of = [&](uint32_t e) { return bb_insert(u * nsets + (e >> r), e & ((1u << r) - 1u), b0, r); };
         if (g == 0 && !HEAD) {
 #pragma unroll
-            for (uint32_t e = 0; e < 16; ++e) x[e] = out[(uint64_t)base_flat + (uint64_t)m_of(e) * mstride];
+            for (uint32_t e = 0; e < 16; ++e) x[e] = bb_at(out, base_flat + m_of(e) * mstride);
         } else {
 #pragma unroll
             for (uint32_t e = 0; e < 16; ++e) x[e] = lds[m_of(e) * pitch + sl];
@@ -170,7 +181,7 @@ __global__ void __launch_bounds__(512) bb_batch_kernel(BbParams p) {
                 const uint32_t hi = e + (1u << t);
                 const uint32_t m = m_of(e);
                 const uint32_t j = low_row + ((m & ((1u << (b0 + t)) - 1u)) << s0);
-                const uint2 wv = level[j];
+                const uint2 wv = bb_at(level, j);
                 const uint32_t tt = bb_shoup(x[hi], wv.x, wv.y);
                 x[hi] = bb_sub(x[e], tt);
                 x[e] = bb_add(x[e], tt);
@@ -178,7 +189,7 @@ __global__ void __launch_bounds__(512) bb_batch_kernel(BbParams p) {
         }
         if (g == NG - 1 && !HEAD) {
 #pragma unroll
-            for (uint32_t e = 0; e < 16; ++e) out[(uint64_t)base_flat + (uint64_t)m_of(e) * mstride] = x[e];
+            for (uint32_t e = 0; e < 16; ++e) bb_at(out, base_flat + m_of(e) * mstride) = x[e];
         } else {
             // a thread writes back exactly the slots it read for this group, so only the
             // next group's reads (or the staged store) wait for the barrier
@@ -199,7 +210,7 @@ __global__ void __launch_bounds__(512) bb_batch_kernel(BbParams p) {
             const uint64_t row0 = (uint64_t)high << K;
             for (uint32_t q = tid; q < SLICE * wc; q += nthreads) {
                 const uint32_t m = q >> lwc, ci = q & (wc - 1u);
-                out[((row0 + m) << lw) + cb * wc + ci] = lds[m * pitch + (gi << lwc) + ci];
+                bb_at(out, (((uint32_t)row0 + m) << lw) + cb * wc + ci) = lds[m * pitch + (gi << lwc) + ci];
             }
         }
     }
