@@ -1,5 +1,9 @@
 // Register-group batch kernel: the k passes of a batch run in groups of up to GR
-// passes, each group entirely in registers, on the 29-bit limb representation.
+// passes, each group entirely in registers, on the 29-bit limb representation.  Two
+// geometries: radix-4 groups (GR = 2, four elements a thread) for large launches, and the
+// narrow one (GR = 1, two elements a thread, one- or two-wave workgroups, each group's
+// table entry loaded one group ahead) for launches too small to fill the chip, where
+// each thread's chain of dependent products sets the time.
 //
 // A thread owns 2^GR elements of its slice for a group covering local index bits
 // [b0, b0 + r): the elements whose local index has the thread's value in every other

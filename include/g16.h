@@ -97,6 +97,10 @@ int g16_batch_plan(uint32_t log_n, uint32_t kmax, uint32_t* ks, uint32_t cap);
  * at least g16_h_workspace_bytes(log_n) bytes) stays owned by the caller and must
  * outlive the context.  Work later enqueued on another stream must be ordered after
  * this call by the caller.  On success *out_ctx receives a new context.
+ * Settings read from the environment here, once, for the context's lifetime (results
+ * never depend on them): G16_MAX_K (see g16_batch_plan), G16_RADIX2 (set: every batch
+ * on the radix-2 kernel), G16_NARROW ("1": the register-group kernel's narrow geometry
+ * for every launch, "0": never; unset: for launches of at most 3 * 2^18 elements).
  * Errors: G16_EINVAL (null out_ctx or workspace, misaligned workspace),
  * G16_ERANGE, G16_ENOSPACE, G16_EHIP. */
 int g16_h_prepare(uint32_t log_n, void* workspace, size_t workspace_bytes, void* stream,
