@@ -520,7 +520,10 @@ def main():
             if olog == 12:
                 med = tm.median_ms(call, 50)
                 entry["h_pipeline_median_us"] = round(med * 1e3, 2)
-                entry["h_pipeline_mean_ms"] = round(tm.mean_ms(call, args.steps), 5)
+                mean = tm.mean_ms(call, max(args.steps, 200))
+                # back to back, as the 2^22 figure and the main step are timed
+                entry["h_pipeline_ms"] = round(mean, 5)
+                entry["h_pipeline_mean_ms"] = round(mean, 5)
                 torch.cuda.synchronize()
                 t0 = time.perf_counter()
                 for _ in range(200):
