@@ -78,8 +78,9 @@ def stage_work(kind: str, join: bool, n_vec: int, k: int, n: int):
     Strided batch of k passes on n_vec vectors: n_vec k n/2 butterflies, one product
     each; one read and one write per element.  Fused lowest batch: the last k passes of
     the inverse and the first k of the forward transform (2k n/2 butterflies), the 1/n
-    scaling and the coset shift (two products per element, performed here as one table
-    product), and one read of the shift table per element.  Join: A'B' (one product),
+    scaling and the coset shift (two products per element, performed here as one product
+    by one of four resident constants), and, as the survey's byte count has it, one
+    read of a shift table per element.  Join: A'B' (one product),
     h_std (one reduction); writes h_mont and h_std instead of the vectors, and reads A'
     and B' when C runs alone (n_vec = 1; with all three kinds in the launch they meet in
     LDS).
@@ -92,7 +93,7 @@ def stage_work(kind: str, join: bool, n_vec: int, k: int, n: int):
     writes = 2 if join else n_vec
     byts = (reads + writes) * n * FR_BYTES
     if kind == "fused":
-        byts += n_vec * n * FR_BYTES    # the shift table
+        byts += n_vec * n * FR_BYTES    # a shift table (counted; the kernel reads none)
     redc = 0
     if join:
         muls += n

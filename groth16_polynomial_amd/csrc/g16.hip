@@ -37,10 +37,11 @@ struct g16_ctx {
     uint32_t magic;
     uint32_t log_n;
     int device;
-    g16::TwTab tw_fwd;  // powers of omega by level (n - 1 entries)
-    g16::TwTab tw_inv;  // powers of omega^-1 by level, bit-reversed within each level
-    g16::TwTab coset;   // n^-1 s^bitrev(p), p < n
-                        // (each in five planes of n 16-byte parts)
+    g16::TwTab tw_fwd;    // powers of omega by level (n - 1 entries)
+    g16::TwTab tw_inv;    // powers of omega^-1 by level, bit-reversed within each level
+    g16::TwTab tw_coset;  // tw_fwd with the coset shift folded into the levels of bits >= 2
+                          // (each in five planes of n 16-byte parts)
+    g16::TwTab kappa;     // the rest of the shift and 1/n, by position mod 4 (four entries)
     Fr* scratch;  // three n-element vectors
     const uint8_t* ws_begin;
     size_t ws_bytes;
@@ -379,11 +380,12 @@ uint32_t plan_coset(const g16_ctx* c, const Fr* const* srcs, Fr* const* dsts, ui
         }
         add(g16::Mode::InvStrided, false, p, n_kind);
     }
-    // lowest batch of both transforms with the coset multiply between them
+    // lowest batch of both transforms with the coset multiply between them; the forward
+    // passes read the shifted table
     g16::BatchParams f = base_params(c);
     f.tw = c->tw_inv;
-    f.tw_fwd = c->tw_fwd;
-    f.scale = c->coset;
+    f.tw_fwd = c->tw_coset;
+    f.kappa = c->kappa;
     f.k = c->batch_k[0];
     f.lazy_out = nb > 1 ? 1u : 0u;
     for (uint32_t v = 0; v < n_kind; ++v) {
@@ -403,7 +405,7 @@ uint32_t plan_coset(const g16_ctx* c, const Fr* const* srcs, Fr* const* dsts, ui
     // forward transform, remaining batches (DIT), low to high
     for (uint32_t b = 1; b < nb; ++b) {
         g16::BatchParams p = base_params(c);
-        p.tw = c->tw_fwd;
+        p.tw = c->tw_coset;
         p.s0 = batch_s0(c, b);
         p.k = c->batch_k[b];
         p.lazy_out = b + 1 < nb ? 1u : 0u;
@@ -538,7 +540,7 @@ size_t g16_h_workspace_bytes(uint32_t log_n) {
     size_t n = size_t(1) << log_n;
     size_t tab = round_up(n * sizeof(g16::Tw29));
     size_t full = round_up(n * sizeof(Fr));
-    return 3 * tab + 3 * full;
+    return 3 * tab + 3 * full + round_up(4 * sizeof(g16::Tw29));
 }
 
 int g16_h_prepare(uint32_t log_n, void* workspace, size_t workspace_bytes, void* stream,
@@ -561,8 +563,9 @@ int g16_h_prepare(uint32_t log_n, void* workspace, size_t workspace_bytes, void*
     size_t tab = round_up(n * sizeof(g16::Tw29));
     c->tw_fwd = g16::TwTab{(uint4*)ws, (uint32_t)n};
     c->tw_inv = g16::TwTab{(uint4*)(ws + tab), (uint32_t)n};
-    c->coset = g16::TwTab{(uint4*)(ws + 2 * tab), (uint32_t)n};
+    c->tw_coset = g16::TwTab{(uint4*)(ws + 2 * tab), (uint32_t)n};
     c->scratch = (Fr*)(ws + 3 * tab);
+    c->kappa = g16::TwTab{(uint4*)(ws + 3 * tab + 3 * round_up(n * sizeof(Fr))), 4u};
     c->ws_begin = ws;
     c->ws_bytes = g16_h_workspace_bytes(log_n);
     domain_roots(log_n, &c->omega, &c->shift, &c->size_inv);
@@ -595,8 +598,10 @@ int g16_h_prepare(uint32_t log_n, void* workspace, size_t workspace_bytes, void*
                        c->omega, one, (uint64_t)(n - 1), log_n, 0, starts);
     hipLaunchKernelGGL(g16::table_kernel, dim3(blocks), dim3(kThreads), 0, s, c->tw_inv,
                        c->omega_inv, one, (uint64_t)(n - 1), log_n, 2, starts);
-    hipLaunchKernelGGL(g16::table_kernel, dim3(blocks), dim3(kThreads), 0, s, c->coset,
-                       c->shift, c->size_inv, (uint64_t)n, log_n, 1, starts);
+    hipLaunchKernelGGL(g16::table_kernel, dim3(blocks), dim3(kThreads), 0, s, c->tw_coset,
+                       c->omega, c->shift, (uint64_t)(n - 1), log_n, 3, starts);
+    hipLaunchKernelGGL(g16::table_kernel, dim3(1), dim3(kThreads), 0, s, c->kappa, c->shift,
+                       c->size_inv, (uint64_t)4, log_n, 1, starts);
     int rc = launch_status();
     if (rc) {
         delete c;

@@ -26,8 +26,11 @@
 // Pipeline mapping (per vector; the pages fold the bit reversal into the first load,
 // here it disappears instead): the inverse transform runs in the inverse order on the
 // natural-order input with the powers of omega^-1, leaving coefficients in bit-reversed
-// order; the coset shift and 1/n become one multiply by a table S[p] = n^-1 s^bitrev(p)
-// stored in bit-reversed order; the forward transform runs in the forward order on that
+// order; the coset shift and 1/n (position p holds coefficient bitrev(p) and needs the
+// factor n^-1 s^bitrev(p)) are split by the bits of p (the coset shift, below): the part of bits 0
+// and 1, with n^-1, is one multiply by one of four constants; the part of every higher bit
+// is folded into the forward twiddles of that bit's pass; the forward transform runs in
+// the forward order on that
 // bit-reversed vector and produces natural order.  The lowest batch of passes of both
 // transforms covers the same contiguous slices, so the end of the inverse, the shift
 // and the start of the forward transform share one kernel and one HBM round trip.
@@ -41,7 +44,7 @@ enum class Mode : int {
     HeadBitrev = 0,  // load src[bitrev(i)] (inverse: src[-bitrev(i)] x kscale), forward [0, k)
     FwdStrided = 1,  // forward-order passes [s0, s0 + k) on slices strided by 2^s0
     InvStrided = 2,  // inverse-order passes s0 + k - 1 down to s0, slices strided by 2^s0
-    Fused = 3,       // contiguous slices: inverse passes k-1..0, x S[p], forward 0..k-1
+    Fused = 3,       // contiguous slices: inverse passes k-1..0, x kappa[p mod 4], forward 0..k-1
 };
 
 struct BatchParams {
@@ -52,12 +55,13 @@ struct BatchParams {
     Fr* dst[3];
     TwTab tw;             // twiddles of this batch's passes (Fused: the inverse table)
     TwTab tw_fwd;         // Fused only: the forward table
-    TwTab scale;          // Fused only: S[p]
     const Fr* join_a;     // store epilogue H = A' B' - x (join kernels only)
     const Fr* join_b;
     Fr* h_mont;
     Fr* h_std;
     Tw29 kscale;          // HeadBitrev, inverse transform: multiplier applied on load
+    TwTab kappa;          // Fused only: four entries, the factor between the transforms
+                          // of the elements at positions p = q mod 4 (coset shift below)
     uint32_t log_n;
     uint32_t s0;
     uint32_t k;
@@ -199,6 +203,20 @@ __device__ __forceinline__ uint32_t head_index(uint64_t i, uint32_t log_n, uint3
     return inverse ? ((0u - br) & ((1u << log_n) - 1u)) : br;
 }
 
+// The coset shift of the H pipeline.  Position p of the bit-reversed coefficient vector
+// holds coefficient j = bitrev_L(p), which the shift multiplies by s^j / n; bit b of p
+// contributes s^(2^(L-1-b)) to s^j.  A forward-order pass on bit b pairs p (bit b clear)
+// with p + 2^b, whose factors differ by sigma_b = s^(2^(L-1-b)) alone, so with every
+// element still owing the factor of its bits above the passes done so far,
+//   F(p) x_lo + w F(p) sigma_b x_hi  and  F(p) x_lo - w F(p) sigma_b x_hi
+// are F(p) times a butterfly with twiddle w sigma_b, and both outputs owe F(p), the factor
+// without bit b.  So the shifted forward table holds w sigma_b for the passes on bits
+// b >= 2 (after the last pass nothing is owed), and the elements are multiplied before the
+// forward transform only by kappa[p mod 4] = n^-1 s^(2^(L-1) p_0 + 2^(L-2) p_1), the part of
+// bits 0 and 1 (whose passes keep their twiddles of 1).  One product per element, like a
+// table S[p] = n^-1 s^bitrev(p), whose n entries would have to be read from HBM; the four
+// kappa entries stay in the caches.
+
 // The H epilogue: h_mont[i] = A'[i] B'[i] - x, h_std[i] = the same without the factor R.
 // i counts from the join pointers, proof offset included.  A' and B' may be stored in
 // h_mont and h_std themselves: element i is read here before it is written, by this
@@ -245,8 +263,9 @@ __device__ __forceinline__ void lds_pass(Fr* sh, const TwTab& tw, uint32_t log_n
         const uint32_t ex = INV ? inv_tw_exp(k, t, bf >> t, g >> s0) : fwd_tw_exp(s0, low, jm);
         const uint32_t idx = INV ? inv_tw_index(log_n, s0, k, t, bf >> t, g >> s0)
                                  : fwd_tw_index(log_n, s0, t, low, jm);
-        // exponent 0 is the twiddle 1
-        Fr vw = ex == 0u ? v : fr_mul_entry(v, ld_tw(tw, idx));
+        // exponent 0 is the twiddle 1, except in the forward passes on bits 2 and up,
+        // whose entries may carry the coset shift's factor (sigma_b above)
+        Fr vw = (ex == 0u && (INV || s0 + t < 2u)) ? v : fr_mul_entry(v, ld_tw(tw, idx));
         st_lds(base + lo, fr_add(u, vw));
         st_lds(base + hi, fr_sub(u, vw));
     }
@@ -307,7 +326,7 @@ __global__ void __launch_bounds__(256) ntt_batch_kernel(BatchParams p) {
         for (uint32_t e = threadIdx.x; e < total; e += blockDim.x) {
             uint32_t sl = e >> k, m = e & (slice_len - 1u);
             Fr* q = sh + ((size_t)sl << k) + m;
-            st_lds(q, fr_mul_entry(ld_lds(q), ld_tw(p.scale, (uint32_t)gindex(sl, m))));
+            st_lds(q, fr_mul_entry(ld_lds(q), ld_tw(p.kappa, (uint32_t)gindex(sl, m) & 3u)));
         }
         __syncthreads();
         for (uint32_t t = 0; t < k; ++t)

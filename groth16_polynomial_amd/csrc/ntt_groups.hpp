@@ -584,10 +584,14 @@ ntt_group_kernel(BatchParams p) {
                 __syncthreads();
             }
         });
-        // group 0 stays in registers: the coset multiply between the two transforms
-        uint32_t ce[G::kE];
+        // group 0 stays in registers: the coset multiply between the two transforms, by
+        // kappa[p mod 4] (the coset shift, kernels.hpp).  With four elements a thread and
+        // at least two passes, element xi of group 0 sits at p = xi mod 4, the same in
+        // every lane: scalar loads and scalar operands; otherwise p mod 4 varies by lane.
+        constexpr bool kUniKappa = G::kE == 4 && K >= 2;
+        uint32_t cq[G::kE];
         for_group(std::integral_constant<int, 0>{}, [&](auto xi_c, uint32_t e) {
-            ce[decltype(xi_c)::value] = e;
+            cq[decltype(xi_c)::value] = (uint32_t)gidx(e) & 3u;
         });
         constexpr int NC = G::kE < chains_for(M) ? G::kE : chains_for(M);
         static_for<G::kE / NC>([&](auto ch_c) {
@@ -597,9 +601,10 @@ ntt_group_kernel(BatchParams p) {
             static_for<NC>([&](auto j_c) {
                 constexpr int j = decltype(j_c)::value;
                 h[j] = x[i0 + j];
-                w[j] = ld_tw(p.scale, (uint32_t)gidx(ce[i0 + j]));
+                if constexpr (kUniKappa) w[j] = ld_tw_uniform(p.kappa, (uint32_t)(i0 + j));
+                else w[j] = ld_tw(p.kappa, cq[i0 + j]);
             });
-            shoup_mul_n<NC>(h, w, y);
+            shoup_mul_n<NC, kUniKappa>(h, w, y);
             static_for<NC>([&](auto j_c) {
                 constexpr int j = decltype(j_c)::value;
                 x[i0 + j] = y[j];

@@ -38,7 +38,10 @@ __global__ void __launch_bounds__(256) elementwise_kernel(const Fr* a, const Fr*
 //           base^(2^m j), for the n - 1 entries of a 2^L domain
 //   kind 2: the same levels bit-reversed: entry n - n/2^m + j is
 //           base^(2^m bitrev_(L-1-m)(j))
-//   kind 1: T[p] = factor * base^bitrev_L(p)      (coset table, p < count = 2^L)
+//   kind 3: kind 0 with the coset shift folded in: the levels of the passes on bits
+//           b = L-1-m >= 2 times factor^(2^m) (factor = s; the coset shift, kernels.hpp)
+//   kind 1: the four kappa entries, q < 4: factor base^(2^(L-1) q_0 + 2^(L-2) q_1)
+//           (base = s, factor = n^-1; q_1 only for L >= 2)
 __device__ __forceinline__ void st_tw(const TwTab& tab, uint64_t e, const Tw29& t) {
     uint4* q = tab.base + e;
     const size_t s = tab.stride;
@@ -49,37 +52,40 @@ __device__ __forceinline__ void st_tw(const TwTab& tab, uint64_t e, const Tw29& 
     q[4 * s] = make_uint4(t.wp[7], t.wp[8], 0u, 0u);
 }
 
-// Twiddle and coset tables, one 80-byte entry per thread (grid-stride loop).
-//   kind 0: forward levels (omega = base); entry positions follow fwd_tw_index, for the
-//           batch plan whose start bits are set in batch_starts (bit 0 always);
+// Tables, one 80-byte entry per thread (grid-stride loop) for the count entries (n - 1
+// for the levels, 4 for kind 1).
+//   kinds 0 and 3: forward levels (omega = base); entry positions follow fwd_tw_index,
+//           for the batch plan whose start bits are set in batch_starts (bit 0 always);
 //   kind 2: inverse levels (omega^-1 = base), bit-reversed within each level;
-//   kind 1: coset table, entry p = factor base^bitrev(p).
+//   kind 1: the kappa entries.
 __global__ void __launch_bounds__(256) table_kernel(TwTab out, Fr base, Fr factor,
                                                     uint64_t count, uint32_t log_n, int kind,
                                                     uint32_t batch_starts) {
     const uint64_t n = 1ull << log_n;
     for (uint64_t j = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; j < count;
          j += (uint64_t)gridDim.x * blockDim.x) {
-        Fr v;
-        if (kind == 0 || kind == 2) {
-            // level m spans [n - n/2^m, n - n/2^(m+1)) and has L-1-m index bits
-            uint32_t m = 0;
-            while (j >= n - (n >> (m + 1))) ++m;
-            uint64_t jj = j - (n - (n >> m));
-            const uint32_t bits = log_n - 1u - m;
-            if (kind == 2 && bits > 0u) jj = bitrev_bits((uint32_t)jj, bits);
-            if (kind == 0) {
-                // position jm + low 2^t -> exponent low + jm 2^s0 (t = bits - s0)
-                const uint32_t s0 = 31u - __builtin_clz(batch_starts & ((2u << bits) - 1u));
-                const uint32_t t = bits - s0;
-                const uint64_t low = jj >> t, jm = jj & ((1ull << t) - 1ull);
-                jj = low + (jm << s0);
-            }
-            v = fr_pow_u64(base, jj << m);
-        } else {
-            uint64_t e = bitrev_bits((uint32_t)j, log_n);
-            v = fr_mul(factor, fr_pow_u64(base, e));
+        if (kind == 1) {
+            uint64_t e = (j & 1u) << (log_n - 1u);
+            if (log_n >= 2u) e += (j >> 1) << (log_n - 2u);
+            st_tw(out, j, tw29_entry(fr_mul(factor, fr_pow_u64(base, e))));
+            continue;
         }
+        // level m spans [n - n/2^m, n - n/2^(m+1)) and has L-1-m index bits
+        uint32_t m = 0;
+        while (j >= n - (n >> (m + 1))) ++m;
+        uint64_t jj = j - (n - (n >> m));
+        const uint32_t bits = log_n - 1u - m;
+        if (kind == 2 && bits > 0u) jj = bitrev_bits((uint32_t)jj, bits);
+        if (kind != 2) {
+            // position jm + low 2^t -> exponent low + jm 2^s0 (t = bits - s0)
+            const uint32_t s0 = 31u - __builtin_clz(batch_starts & ((2u << bits) - 1u));
+            const uint32_t t = bits - s0;
+            const uint64_t low = jj >> t, jm = jj & ((1ull << t) - 1ull);
+            jj = low + (jm << s0);
+        }
+        Fr v = fr_pow_u64(base, jj << m);
+        // the pass on bit L-1-m >= 2 of the shifted forward table: times s^(2^m)
+        if (kind == 3 && bits >= 2u) v = fr_mul(v, fr_pow_u64(factor, 1ull << m));
         st_tw(out, j, tw29_entry(v));
     }
 }

@@ -73,11 +73,12 @@ const char* g16_strerror(int code);
 
 /* Bytes of device workspace g16_h_prepare needs for a 2^log_n domain, or 0 when
  * log_n is out of range.  The workspace holds the resident tables (the powers of omega
- * and of omega^-1 stored by level, n - 1 entries each, and the n-entry coset table
- * n^-1 * s^bitrev(p); each entry is 80 bytes: the plain value and its companion
- * floor(w 2^261 / r) in nine 29-bit digits) and three n-element scratch vectors of
- * 32-byte elements: 3 * n * 80 + 3 * n * 32 bytes, each section rounded up to 256
- * bytes. */
+ * and of omega^-1 stored by level, n - 1 entries each; the same levels of omega with the
+ * coset shift folded into the passes on bits 2 and up, n - 1 entries; and four entries
+ * that hold the rest of the shift and n^-1; each entry is 80 bytes: the plain value and
+ * its companion floor(w 2^261 / r) in nine 29-bit digits) and three n-element scratch
+ * vectors of 32-byte elements: 3 * n * 80 + 3 * n * 32 + 320 bytes, each of the seven
+ * sections rounded up to 256 bytes. */
 size_t g16_h_workspace_bytes(uint32_t log_n);
 
 /* The pass batching the library uses for a 2^log_n transform when each workgroup

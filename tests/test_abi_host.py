@@ -49,7 +49,7 @@ def test_workspace_bytes(lib):
     for L in (1, 2, 12, 20, 27):
         n = 1 << L
         rnd = lambda x: -(-x // 256) * 256
-        assert binding.workspace_bytes(L) == 3 * rnd(n * 80) + 3 * rnd(n * 32)
+        assert binding.workspace_bytes(L) == 3 * rnd(n * 80) + 3 * rnd(n * 32) + rnd(4 * 80)
 
 
 def test_batch_scratch_bytes(lib):
