@@ -87,6 +87,62 @@ using NarrowGeomFor = GroupGeom<K, 1, narrow_slices_per_wg(K, M)>;
 template <int K, Mode M>
 constexpr bool narrow_join3_fits() { return 3 * NarrowGeomFor<K, M>::kThreads <= 1024; }
 
+// Whether the exchange from group GA to group GB stays inside every wave: the lanes of a
+// wave (64 consecutive threads) hold the elements whose index has the wave's value in the
+// bits that thread-index bits above the lane bits land on, and the exchange needs no
+// workgroup barrier when those bits are the same in both groups (each wave then reads
+// back only elements it wrote; LDS operations of one wave complete in issue order).
+// Thread t's element for set s and group member q is e = insert_bits(t 2^(GR-r) + s, q,
+// b0, r).  The wave bits of t: contiguous layout (tid = slice * threads-per-slice + t) the
+// bits from 6 up, or none when a wave holds whole slices; interleaved (tid = t SPW + slice)
+// the bits from 6 - log2(SPW) up.
+template <int K, int GR, int SPW, bool INTERLEAVED>
+constexpr bool exchange_in_wave(int ga, int gb) {
+    using G = GroupGeom<K, GR, SPW>;
+    int tbits = 0;
+    while ((1 << tbits) < G::kThreadsPerSlice) ++tbits;
+    int sbits = 0;
+    while ((1 << sbits) < SPW) ++sbits;
+    const int w0 = INTERLEAVED ? (6 - sbits > 0 ? 6 - sbits : 0) : 6;
+    if (!INTERLEAVED && tbits <= 6) return true;  // a wave holds whole slices
+    auto pos = [](int g, int j) {  // element bit that bit j of t lands on in group g
+        const int r = G::group_r(g), b0 = G::group_b0(g);
+        const int cj = j + (GR - r);
+        return cj < b0 ? cj : cj + r;
+    };
+    for (int j = w0; j < tbits; ++j)
+        if (pos(ga, j) != pos(gb, j)) return false;
+    return true;
+}
+
+// The same by enumeration (checked against exchange_in_wave at compile time): every
+// element that a wave writes after group GA is read before group GB by a thread of the
+// same wave.
+template <int K, int GR, int SPW, bool INTERLEAVED>
+constexpr bool exchange_in_wave_enum(int ga, int gb) {
+    using G = GroupGeom<K, GR, SPW>;
+    constexpr int kElems = SPW << K;
+    int wave_of[kElems] = {};
+    for (int pass = 0; pass < 2; ++pass) {
+        const int g = pass == 0 ? ga : gb;
+        const int r = G::group_r(g), b0 = G::group_b0(g);
+        const int nsets = 1 << (GR - r);
+        for (int tid = 0; tid < G::kThreads; ++tid) {
+            const int sl = INTERLEAVED ? tid % SPW : tid / G::kThreadsPerSlice;
+            const int t = INTERLEAVED ? tid / SPW : tid % G::kThreadsPerSlice;
+            for (int st = 0; st < nsets; ++st)
+                for (int q = 0; q < (1 << r); ++q) {
+                    const int c = t * nsets + st;
+                    const int e = (c & ((1 << b0) - 1)) | (q << b0) | ((c >> b0) << (b0 + r));
+                    const int id = sl * (1 << K) + e;
+                    if (pass == 0) wave_of[id] = tid / 64;
+                    else if (wave_of[id] != tid / 64) return false;
+                }
+        }
+    }
+    return true;
+}
+
 // c with the r bits of q inserted at bit b0
 __device__ __forceinline__ uint32_t insert_bits(uint32_t c, uint32_t q, int b0, int r) {
     return (c & ((1u << b0) - 1u)) | (q << b0) | ((c >> b0) << (b0 + r));
@@ -400,6 +456,19 @@ ntt_group_kernel(BatchParams p) {
 
     V29 x[G::kE];
 
+    // After the LDS writes of group GA, before the reads of group GB.  Three kinds per
+    // workgroup: always the barrier (a wave may hold threads of two kinds).
+    auto exchange = [&](auto ga_c, auto gb_c) {
+        constexpr int ga = decltype(ga_c)::value, gb = decltype(gb_c)::value;
+        static_assert(!exchange_in_wave<K, GR, SPW, kInterleaved>(ga, gb) ||
+                          exchange_in_wave_enum<K, GR, SPW, kInterleaved>(ga, gb),
+                      "an exchange taken as inside every wave crosses waves");
+        if constexpr (NK == 1 && exchange_in_wave<K, GR, SPW, kInterleaved>(ga, gb))
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // order for the compiler
+        else
+            __syncthreads();
+    };
+
     // Visits the elements of group GI: f(index into x, local element index e).
     auto for_group = [&](auto gi_c, auto&& f) {
         constexpr int gi = decltype(gi_c)::value;
@@ -512,9 +581,9 @@ ntt_group_kernel(BatchParams p) {
     using OLD = std::false_type;
     Tw29 nxt{};  // kPre: the next group's entry
 
-    // One barrier after every LDS write: a group reads and rewrites the same slots, all
-    // owned by the one thread, so the only ordering needed is that a group's writes land
-    // before the next group's reads.
+    // One synchronization after every LDS write (exchange): a group reads and rewrites the
+    // same slots, all owned by the one thread, so the only ordering needed is that a
+    // group's writes land before the next group's reads.
     if constexpr (M == Mode::FwdStrided || M == Mode::HeadBitrev) {
         if constexpr (kPre) nxt = entry(std::integral_constant<int, 0>{}, FWD{}, p.tw, s0, low, row);
         static_for<NG>([&](auto gi_c) {
@@ -533,7 +602,7 @@ ntt_group_kernel(BatchParams p) {
                 store_global(gi_c);
             } else {
                 lds_write(gi_c);
-                __syncthreads();
+                exchange(gi_c, std::integral_constant<int, gi + 1>{});
             }
         });
     } else if constexpr (M == Mode::InvStrided) {
@@ -556,7 +625,7 @@ ntt_group_kernel(BatchParams p) {
                 store_global(GI{});
             } else {
                 lds_write(GI{});
-                __syncthreads();
+                exchange(GI{}, std::integral_constant<int, gi - 1>{});
             }
         });
     } else {  // Fused: inverse groups high to low, coset multiply, forward groups low to high
@@ -581,7 +650,7 @@ ntt_group_kernel(BatchParams p) {
             }
             if constexpr (gi > 0) {
                 lds_write(GI{});
-                __syncthreads();
+                exchange(GI{}, std::integral_constant<int, gi - 1>{});
             }
         });
         // group 0 stays in registers: the coset multiply between the two transforms, by
@@ -625,7 +694,7 @@ ntt_group_kernel(BatchParams p) {
                 store_global(gi_c);
             } else {
                 lds_write(gi_c);
-                __syncthreads();
+                exchange(gi_c, std::integral_constant<int, gi + 1>{});
             }
         });
     }
