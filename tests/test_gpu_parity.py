@@ -188,13 +188,13 @@ def test_domain_roots_match_oracle():
 
 # ------------------------------------------------------------------ H pipeline
 
-def _h_case(log_n, kmax=None, workload=1, c_is_product=True, narrow=None):
-    say("h_compute log_n=%d kmax=%s workload=%d c=A*B:%s narrow=%s" % (
-        log_n, kmax, workload, c_is_product, narrow))
+def _h_case(log_n, kmax=None, workload=1, c_is_product=True, narrow=None, radix2=None):
+    say("h_compute log_n=%d kmax=%s workload=%d c=A*B:%s narrow=%s radix2=%s" % (
+        log_n, kmax, workload, c_is_product, narrow, radix2))
     (ad, bd, cd), (am, bm, cm) = h_inputs(workload, log_n, c_is_product)
     same(host(ad), am, "A to Montgomery")
     same(host(cd), cm, "C = A o B")
-    with KMax(kmax, narrow):
+    with KMax(kmax, narrow), Env(G16_RADIX2=radix2):
         ctx = g.HContext(log_n)
     hm, hs = ctx.h_compute(ad, bd, cd)
     want_m, want_s = oracle.h_pipeline(log_n, am, bm, cm)
@@ -226,6 +226,14 @@ def test_h_compute_other_batchings(log_n, kmax):
     (10, None, 0), (12, None, 0), (13, None, 0), (14, None, 0)])
 def test_h_compute_geometries(log_n, kmax, narrow):
     ctx, _, _ = _h_case(log_n, kmax, workload=9, narrow=narrow)
+    ctx.release()
+
+
+# Every batch on the radix-2 kernel (G16_RADIX2): one batch, two, and the 2^20 plan, with
+# the coset shift's four constants and the shifted forward twiddles on that kernel too.
+@pytest.mark.parametrize("log_n", [3, 10, 14, 20])
+def test_h_compute_radix2_kernel(log_n):
+    ctx, _, _ = _h_case(log_n, workload=10, radix2=1)
     ctx.release()
 
 
