@@ -79,8 +79,8 @@ def stage_work(kind: str, join: bool, n_vec: int, k: int, n: int):
     each; one read and one write per element.  Fused lowest batch: the last k passes of
     the inverse and the first k of the forward transform (2k n/2 butterflies), the 1/n
     scaling and the coset shift (two products per element, performed here as one product
-    by one of four resident constants), and, as the survey's byte count has it, one
-    read of a shift table per element.  Join: A'B' (one product),
+    by one of four resident constants), and, as the pipeline's algorithmic byte count
+    (960 bytes per element) has it, one read of a shift table per element.  Join: A'B' (one product),
     h_std (one reduction); writes h_mont and h_std instead of the vectors, and reads A'
     and B' when C runs alone (n_vec = 1; with all three kinds in the launch they meet in
     LDS).

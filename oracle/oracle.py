@@ -95,7 +95,7 @@ class use_library:
 
 def default_threads() -> int:
     """Threads the oracle uses unless told otherwise: G16_ORACLE_THREADS, else the
-    host's cores, at most 16 (a GPU machine's CPU share)."""
+    host's cores, at most 16."""
     env = os.environ.get("G16_ORACLE_THREADS")
     if env:
         return max(1, min(256, int(env)))
