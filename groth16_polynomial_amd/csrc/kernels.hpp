@@ -348,7 +348,3 @@ __global__ void __launch_bounds__(256) ntt_batch_kernel(BatchParams p) {
 }  // namespace g16
 
 #include "ntt_groups.hpp"
-
-namespace g16 {
-
-}  // namespace g16
