@@ -492,7 +492,8 @@ def _extreme_values(n, phase):
 def test_extreme_values():
     """Transforms and the H pipeline on inputs at the edges of the canonical range, as
     standard-form values converted on the device, against the oracle."""
-    for log_n in (12, 16):
+    # 2^12 and 2^16: narrow geometry; 2^20: radix-4 groups (the 2^20 plan's launches)
+    for log_n in (12, 16, 20):
         n = 1 << log_n
         say("extreme values log_n=%d" % log_n)
         a = synth.ints_to_fr(_extreme_values(n, 0))
@@ -517,6 +518,30 @@ def test_extreme_values():
             same(host(hm), want_m, "h_mont 2^%d" % log_n)
             same(host(hs), want_s, "h_std 2^%d" % log_n)
         ctx.release()
+
+
+def test_closed_forms_at_2_20():
+    """Closed forms, no oracle: the forward transform of the unit vector at 0 is all ones and
+    that of the all-ones vector is n at index 0; the inverse undoes both; the coset
+    evaluations of a constant polynomial equal that constant; H of A = B = 1, C = 0 is one
+    everywhere."""
+    import torch
+    log_n = 20
+    n = 1 << log_n
+    say("closed forms log_n=%d" % log_n)
+    ctx = g.HContext(log_n)
+    delta = [1] + [0] * (n - 1)
+    ones = [1] * n
+    dd, od = gpu_mont(synth.ints_to_fr(delta)), gpu_mont(synth.ints_to_fr(ones))
+    assert synth.fr_to_ints(host(g.from_mont(ctx.ntt_forward(dd)))) == ones
+    assert synth.fr_to_ints(host(g.from_mont(ctx.ntt_forward(od)))) == [n] + [0] * (n - 1)
+    assert synth.fr_to_ints(host(g.from_mont(ctx.ntt_inverse(od)))) == delta
+    seven = gpu_mont(synth.ints_to_fr([7] * n))  # evaluations of the constant 7
+    assert synth.fr_to_ints(host(g.from_mont(ctx.coset_eval(seven)))) == [7] * n
+    z = torch.zeros((n, 8), dtype=torch.int32, device="cuda")
+    hm, hs = ctx.h_compute(od, od, z)
+    assert synth.fr_to_ints(host(hs)) == ones
+    ctx.release()
 
 
 def test_aliasing_and_bad_pointers():
