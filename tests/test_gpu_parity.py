@@ -492,8 +492,9 @@ def _extreme_values(n, phase):
 def test_extreme_values():
     """Transforms and the H pipeline on inputs at the edges of the canonical range, as
     standard-form values converted on the device, against the oracle."""
-    # 2^12 and 2^16: narrow geometry; 2^20: radix-4 groups (the 2^20 plan's launches)
-    for log_n in (12, 16, 20):
+    # 2^12 and 2^16: narrow geometry; 2^20: radix-4 groups (the 2^20 plan's launches);
+    # 2^22: three batches, the middle one strided from bit 8
+    for log_n in (12, 16, 20, 22):
         n = 1 << log_n
         say("extreme values log_n=%d" % log_n)
         a = synth.ints_to_fr(_extreme_values(n, 0))
