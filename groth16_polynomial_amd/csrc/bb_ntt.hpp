@@ -19,11 +19,12 @@
 // are enough), and neighbouring lanes take neighbouring slices: in the later batches
 // those are neighbouring flat addresses (the slice coordinate below the batch is the
 // column plus the lower row bits), so every global access of a wave covers whole 128-byte
-// lines.  The first batch reads its input through the bit reversal, from positions that
-// neighbouring slices do not share; it stages its load and its store through LDS
-// instead, with the workgroup's slices chosen so that both are whole runs of addresses:
+// lines.  The first batch reads its input through the bit reversal; its workgroup takes
 // its columns (up to 32) times the 32 / columns row blocks whose reversed indices are
-// consecutive.  Rows at or past 2^log_in read as zero (the extension's padding) and are
+// consecutive, so for each element the workgroup's loads are one run of addresses and go
+// straight into registers.  Its stores are one run per row block: at 8 or more columns
+// they go straight out of registers too, with fewer they are staged through LDS into
+// whole rows.  Rows at or past 2^log_in read as zero (the extension's padding) and are
 // never loaded.
 //
 // Twiddles: level b of the table holds w_(2^(b+1))^j for j < 2^b at offset 2^b - 1 (the
@@ -136,23 +137,24 @@ __global__ void __launch_bounds__(512) bb_batch_kernel(BbParams p) {
 
     uint32_t x[kBbE];
 
-    // ---- load
+    // ---- the first batch's source: slice sl = (gi, ci) (row block gi, column ci of the
+    // workgroup's wc) holds at element m the input row bitrev_K(m) 2^(L-K) + bitrev(h0) 2^lg
+    // + bitrev_lg(gi): for one m the workgroup's slices read 2^lg consecutive rows (in
+    // reversed order) of wc consecutive columns, one run of addresses, so group 0 loads
+    // its elements straight into registers.
+    const uint32_t* head_in = nullptr;
+    uint32_t head_row0 = 0u, head_col = 0u;
+    // The first batch's output: slice (gi, ci) writes rows (h0 + gi 2^(L-K-lg)) 2^K + m, so
+    // for one m the workgroup writes 2^lg runs of wc words.  At 8 or more columns (runs of
+    // 32 bytes and up) the last group stores them directly; with fewer, the runs are
+    // staged through LDS into whole rows of the row blocks (measured: direct stores were
+    // 5% faster at 8 columns, 36-43% slower at 1 or 2).
+    const bool head_direct_store = HEAD && wc >= 8u;
     if constexpr (HEAD) {
-        // staged: lanes run over consecutive input addresses, each element to its slot
-        const uint32_t* in = p.src + vec * p.in_stride;
-        const uint32_t h_in = 1u << p.log_in;
         const uint32_t lwc = lw < p.log_spw ? lw : p.log_spw;
-        const uint32_t rev_h0 = bb_bitrev(h0, L - K - lg);
-        for (uint32_t q = tid; q < spw * SLICE; q += nthreads) {
-            const uint32_t mrev = q >> p.log_spw;  // bitrev_K(m): the source row's top part
-            const uint32_t sp = q & (spw - 1u);
-            const uint32_t gr = sp >> lwc, ci = sp & (wc - 1u);
-            const uint32_t row = (mrev << (L - K)) + (rev_h0 << lg) + gr;
-            const uint32_t v = row < h_in ? bb_at(in, (row << lw) + cb * wc + ci) : 0u;
-            const uint32_t slot_sl = (bb_bitrev(gr, lg) << lwc) + ci;
-            lds[bb_bitrev(mrev, K) * pitch + slot_sl] = v;
-        }
-        __syncthreads();
+        head_in = p.src + vec * p.in_stride;
+        head_row0 = (bb_bitrev(h0, L - K - lg) << lg) + bb_bitrev(sl >> lwc, lg);
+        head_col = cb * wc + (sl & (wc - 1u));
     }
 
     // ---- passes, in groups of four row bits (the last group may be shorter)
@@ -164,7 +166,14 @@ __global__ void __launch_bounds__(512) bb_batch_kernel(BbParams p) {
         constexpr uint32_t nsets = 16u >> r;
         // element e of the thread: set e >> r, position q = e & (2^r - 1)
         auto m_of = [&](uint32_t e) { return bb_insert(u * nsets + (e >> r), e & ((1u << r) - 1u), b0, r); };
-        if (g == 0 && !HEAD) {
+        if (g == 0 && HEAD) {
+            const uint32_t h_in = 1u << p.log_in;
+#pragma unroll
+            for (uint32_t e = 0; e < 16; ++e) {
+                const uint32_t row = (bb_bitrev(m_of(e), K) << (L - K)) + head_row0;
+                x[e] = row < h_in ? bb_at(head_in, (row << lw) + head_col) : 0u;  // padding: 0
+            }
+        } else if (g == 0) {
 #pragma unroll
             for (uint32_t e = 0; e < 16; ++e) x[e] = bb_at(out, base_flat + m_of(e) * mstride);
         } else {
@@ -187,7 +196,7 @@ __global__ void __launch_bounds__(512) bb_batch_kernel(BbParams p) {
                 x[e] = bb_add(x[e], tt);
             }
         }
-        if (g == NG - 1 && !HEAD) {
+        if (g == NG - 1 && (!HEAD || head_direct_store)) {
 #pragma unroll
             for (uint32_t e = 0; e < 16; ++e) bb_at(out, base_flat + m_of(e) * mstride) = x[e];
         } else {
@@ -200,9 +209,10 @@ __global__ void __launch_bounds__(512) bb_batch_kernel(BbParams p) {
     };
     bb_static_for<NG>(group);
 
-    // ---- staged store of the first batch: per row block, lanes over consecutive
-    // addresses (element m, column ci of block gi at ((high 2^K + m) << lw) + cb wc + ci)
-    if constexpr (HEAD) {
+    // ---- staged store of the first batch (fewer than 8 columns): per row block, lanes
+    // over consecutive addresses (element m, column ci of block gi at
+    // ((high 2^K + m) << lw) + cb wc + ci)
+    if (HEAD && !head_direct_store) {
         const uint32_t lwc = lw < p.log_spw ? lw : p.log_spw;
         const uint32_t g = 1u << lg;
         for (uint32_t gi = 0; gi < g; ++gi) {
