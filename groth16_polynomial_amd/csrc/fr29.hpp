@@ -439,6 +439,102 @@ G16_HD Fr fr29_reduce_2r(const V29& a) {
 // one conditional subtraction.
 G16_HD Fr fr29_canon(const V29& a) { return fr_reduce_once(fr29_reduce_2r(a)); }
 
+// Products of two variables (the join of the H epilogue and the CSR gather).  Montgomery's
+// REDC (P. L. Montgomery, Math. Comp. 1985) in radix 2^29 with R' = 2^261, in the
+// product-scanning order: column k adds the digit products x_i y_(k-i) and the terms
+// m_i r_(k-i) of the Montgomery digits already fixed; below column 9 the column fixes
+// m_k = column (-r^-1) mod 2^29, whose m_k r_0 clears its low 29 bits, and from column 9
+// on it yields result digit k - 9.  r = 1 + 2^28 mod 2^29, so -r^-1 = 2^28 - 1 mod 2^29.
+// Every product is one multiply-add into a signed 64-bit column and carries move once a
+// column: no add-with-carry chains (fr_mul's CIOS needs one per 32-bit limb product).
+// The interface keeps R = 2^256: one factor enters shifted by 2^5 (fr29_from_fr_shl5), and
+// x 2^5 y 2^-261 = x y 2^-256.
+
+// r in 29-bit digits
+G16_HD constexpr int32_t r29_digit(int k) {
+    return k == 0 ? 0x10000001 : k == 1 ? 0x1f0fac9f : k == 2 ? 0x0e5c2450
+         : k == 3 ? 0x07d090f3 : k == 4 ? 0x1585d283 : k == 5 ? 0x02db40c0
+         : k == 6 ? 0x00a6e141 : k == 7 ? 0x0e5c2634 : 0x0030644e;
+}
+constexpr uint32_t kR29NInv = 0x0fffffffu;  // -r^-1 mod 2^29
+static_assert((0x10000001ull * kR29NInv + 1ull) % (1ull << 29) == 0ull, "kR29NInv");
+
+// canonical 8 x 32-bit x -> digits of x 2^5, all in [0, 2^29) (x 2^5 < 2^259)
+G16_HD V29 fr29_from_fr_shl5(const Fr& x) {
+    V29 r;
+    r.l[0] = (int32_t)((x.w[0] << 5) & kM29);
+#pragma unroll
+    for (int k = 1; k < 9; ++k) {
+        const int pos = 29 * k - 5, w = pos >> 5, s = pos & 31;
+        uint32_t v = x.w[w] >> s;
+        if (s > 3 && w + 1 < 8) v |= x.w[w + 1] << (32 - s);
+        r.l[k] = (int32_t)((k < 8) ? (v & kM29) : v);
+    }
+    return r;
+}
+
+// REDC over the columns that XY adds (the digit products of column k, or nothing): the
+// value (X + m r) / 2^261 with m < 2^261 chosen so that 2^261 divides X + m r, where X is
+// the sum XY forms.  Result digits 0..7 in [0, 2^29), digit 8 the signed remainder.
+template <class XY>
+G16_HD V29 fr29_redc_cols(XY xy) {
+    int64_t acc = 0;
+    int32_t m[9];
+    V29 o;
+    static_for<17>([&](auto k_c) {
+        constexpr int k = decltype(k_c)::value;
+        xy(k_c, acc);
+        static_for<9>([&](auto i_c) {
+            constexpr int i = decltype(i_c)::value;
+            constexpr int j = k - i;
+            if constexpr (i < k && j >= 1 && j < 9) acc += (int64_t)m[i] * r29_digit(j);
+        });
+        if constexpr (k < 9) {
+            m[k] = (int32_t)(((uint32_t)acc * kR29NInv) & kM29);
+            acc += (int64_t)m[k] * r29_digit(0);
+        } else {
+            o.l[k - 9] = (int32_t)((uint32_t)acc & kM29);
+        }
+        acc >>= 29;
+    });
+    o.l[8] = (int32_t)acc;
+    return o;
+}
+
+// x y 2^-261 for digits below 2^29 + 8 in magnitude: a column holds at most 18 products
+// below 2^58.01 and a carry, inside 2^63.  For 0 <= x, y the result is below
+// x y / 2^261 + r.
+G16_HD V29 fr29_mont_mul(const V29& x, const V29& y) {
+    return fr29_redc_cols([&](auto k_c, int64_t& acc) {
+        constexpr int k = decltype(k_c)::value;
+        static_for<9>([&](auto i_c) {
+            constexpr int i = decltype(i_c)::value;
+            constexpr int j = k - i;
+            if constexpr (j >= 0 && j < 9) acc += (int64_t)x.l[i] * (int64_t)y.l[j];
+        });
+    });
+}
+
+// x 2^-261 for digits in [0, 2^29) (x < 2^261): below x / 2^261 + r < 2r.
+G16_HD V29 fr29_redc1(const V29& x) {
+    return fr29_redc_cols([&](auto k_c, int64_t& acc) {
+        constexpr int k = decltype(k_c)::value;
+        if constexpr (k < 9) acc += x.l[k];
+    });
+}
+
+// Montgomery product of canonical a, b (R = 2^256): a b 2^-256 mod r, canonical.  The
+// REDC value is below 32 a b / 2^261 + r < (32 r / 2^261 + 1) r < 2r, with digits in
+// [0, 2^29), so one conditional subtraction after packing.
+G16_HD Fr fr_mul29(const Fr& a, const Fr& b) {
+    return fr_reduce_once(fr29_pack(fr29_mont_mul(fr29_from_fr_shl5(a), fr29_from_fr(b))));
+}
+
+// Montgomery form -> standard form of a canonical a: a 2^5 2^-261, below 2r.
+G16_HD Fr fr_from_mont29(const Fr& a) {
+    return fr_reduce_once(fr29_pack(fr29_redc1(fr29_from_fr_shl5(a))));
+}
+
 // Unsigned 29-bit digits (the top one below 2^29) -> balanced digits, value unchanged.
 G16_HD void balance29(const uint32_t (&d)[9], int32_t (&o)[9]) {
     int32_t carry = 0;

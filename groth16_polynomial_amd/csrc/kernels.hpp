@@ -220,19 +220,31 @@ __device__ __forceinline__ uint32_t head_index(uint64_t i, uint32_t log_n, uint3
 // The H epilogue: h_mont[i] = A'[i] B'[i] - x, h_std[i] = the same without the factor R.
 // i counts from the join pointers, proof offset included.  A' and B' may be stored in
 // h_mont and h_std themselves: element i is read here before it is written, by this
-// thread alone.
-__device__ __forceinline__ void store_h(const BatchParams& p, uint64_t i, const Fr& x) {
-    Fr h = fr_sub(fr_mul(ld_global(p.join_a + i), ld_global(p.join_b + i)), x);
+// thread alone.  The product and the conversion to standard form are radix-2^29 REDCs
+// (fr29.hpp); xn has normalized digits (any value fr29_canon takes).
+__device__ __forceinline__ void store_h_digits(const BatchParams& p, uint64_t i, const V29& xn) {
+    const V29 ab = fr29_mont_mul(fr29_from_fr_shl5(ld_global(p.join_a + i)),
+                                 fr29_from_fr(ld_global(p.join_b + i)));
+    const Fr h = fr29_canon(fr29_sub(ab, xn));
     st_global(p.h_mont + i, h);
-    st_global(p.h_std + i, fr_from_mont(h));
+    st_global(p.h_std + i, fr_from_mont29(h));
+}
+// x canonical
+__device__ __forceinline__ void store_h(const BatchParams& p, uint64_t i, const Fr& x) {
+    store_h_digits(p, i, fr29_from_fr(x));
+}
+// x a transform's lazy digits
+__device__ __forceinline__ void store_h(const BatchParams& p, uint64_t i, const V29& x) {
+    store_h_digits(p, i, fr29_normalize(x));
 }
 
 // The same with A' and B' at hand (canonical).
 __device__ __forceinline__ void store_h3(const BatchParams& p, uint64_t i, const Fr& a,
                                          const Fr& b, const Fr& x) {
-    Fr h = fr_sub(fr_mul(a, b), x);
+    const V29 ab = fr29_mont_mul(fr29_from_fr_shl5(a), fr29_from_fr(b));
+    const Fr h = fr29_canon(fr29_sub(ab, fr29_from_fr(x)));
     st_global(p.h_mont + i, h);
-    st_global(p.h_std + i, fr_from_mont(h));
+    st_global(p.h_std + i, fr_from_mont29(h));
 }
 
 // x w mod r, canonical, for a canonical x and a table entry (radix-2 kernel and

@@ -523,7 +523,7 @@ ntt_group_kernel(BatchParams p) {
             constexpr int xi = decltype(xi_c)::value;
             const uint64_t i = gidx(e);
             if constexpr (JOIN) {
-                store_h(p, off + i, fr29_canon(x[xi]));
+                store_h(p, off + i, x[xi]);
             } else {
                 const Fr v = fr29_reduce_2r(x[xi]);
                 st_global(dst + i, p.lazy_out ? v : fr_reduce_once(v));

@@ -93,10 +93,12 @@ __global__ void __launch_bounds__(256) table_kernel(TwTab out, Fr base, Fr facto
 // The CSR gather: 64 consecutive rows per workgroup of one wave (the GATHER_CU page puts
 // a row on a lane: rows are short and ragged).  With a row per lane a wave would form as
 // many products as its longest row has terms, while most rows have one or two; here the
-// wave flattens its rows' terms instead: in each round of 64 terms every lane forms one
-// product (value times witness), and then every lane adds the products of its own row
-// from LDS (additions only).  A row whose range or a signal is out of bounds is flagged
-// and reads nothing out of bounds.
+// wave flattens its rows' terms instead, the terms of its A rows followed by those of its
+// B rows, so that both matrices share each dependent load: the row pointers of A and B
+// are read together, and in each round of 64 terms every lane forms one product (value
+// times witness, from A or B).  Then every lane adds the products of its own A row and
+// its own B row from LDS (additions only).  A row whose range or a signal is out of
+// bounds is flagged and reads nothing out of bounds.
 constexpr uint32_t kGatherLanes = 64;
 
 __device__ __forceinline__ Fr fr_invalid() {
@@ -106,48 +108,75 @@ __device__ __forceinline__ Fr fr_invalid() {
     return z;
 }
 
+// Per row of the wave, A rows at [0, 64) and B rows at [64, 128).
 struct GatherLds {
-    uint64_t off[kGatherLanes];  // a row's first term in the wave's flattened list
-    uint64_t total;
-    uint32_t lo[kGatherLanes];   // a row's first index in the CSR arrays
-    uint32_t len[kGatherLanes];  // its number of terms
-    uint32_t bad[kGatherLanes];  // a row named a witness index out of range
-    Fr prod[kGatherLanes];       // the round's products, by flattened term
+    uint64_t off[2 * kGatherLanes];  // the row's first term in the wave's flattened list
+    uint32_t lo[2 * kGatherLanes];   // its first index in its matrix's CSR arrays
+    uint32_t len[2 * kGatherLanes];  // its number of terms
+    uint32_t bad[2 * kGatherLanes];  // it named a witness index out of range
+    Fr prod[kGatherLanes];           // the round's products, by flattened term
 };
 
-// Row `row` (lane `l`, valid when in_rows) of one matrix: its sum into acc; false when the
-// row's range or one of its signals is out of bounds.  Every lane of the workgroup calls it
-// (it has barriers).
-__device__ __forceinline__ bool gather_matrix(const uint32_t* row_ptr, const uint32_t* signal,
-                                              const Fr* value, uint64_t nnz, const Fr* witness,
-                                              uint64_t n_witness, uint64_t row, bool in_rows,
-                                              GatherLds& sh, Fr& acc) {
+// Row `row` of one matrix: its CSR range, or an empty range and false when the range is
+// not within [0, nnz].
+__device__ __forceinline__ bool gather_range(const uint32_t* row_ptr, uint64_t nnz,
+                                             uint64_t row, bool in_rows, uint32_t& lo,
+                                             uint32_t& len) {
+    lo = 0;
+    len = 0;
+    if (!in_rows) return true;
+    lo = row_ptr[row];
+    const uint32_t hi = row_ptr[row + 1];
+    const bool ok = lo <= hi && (uint64_t)hi <= nnz;
+    len = ok ? hi - lo : 0u;
+    return ok;
+}
+
+// The sum of this lane's row's products that fall in the round's window [t0, t0 + 64).
+__device__ __forceinline__ void gather_add_round(Fr& acc, const GatherLds& sh, uint64_t off,
+                                                 uint32_t len, uint64_t t0) {
+    const uint64_t a0 = off > t0 ? off : t0;
+    const uint64_t a1 = off + len < t0 + kGatherLanes ? off + len : t0 + kGatherLanes;
+    for (uint64_t j = a0; j < a1; ++j) acc = fr_add(acc, sh.prod[j - t0]);
+}
+
+__global__ void __launch_bounds__(kGatherLanes) gather_kernel(
+    const uint32_t* row_ptr_a, const uint32_t* signal_a, const Fr* value_a, uint64_t nnz_a,
+    const uint32_t* row_ptr_b, const uint32_t* signal_b, const Fr* value_b, uint64_t nnz_b,
+    const Fr* witness, uint64_t n_witness, Fr* out_a, Fr* out_b, Fr* out_c, uint64_t n_rows) {
+    __shared__ GatherLds sh;
     const uint32_t l = threadIdx.x;
-    uint32_t lo = 0, len = 0;
-    bool ok = true;
-    if (in_rows) {
-        lo = row_ptr[row];
-        const uint32_t hi = row_ptr[row + 1];
-        ok = lo <= hi && (uint64_t)hi <= nnz;
-        len = ok ? hi - lo : 0u;
-    }
-    // exclusive prefix of the lengths over the wave (64-bit: ranges of malformed row
-    // pointers may overlap, and each is only checked against nnz)
-    uint64_t inc = len;
+    const uint64_t row = (uint64_t)blockIdx.x * kGatherLanes + l;
+    const bool in_rows = row < n_rows;
+    uint32_t lo_a, len_a, lo_b, len_b;
+    const bool ok_a = gather_range(row_ptr_a, nnz_a, row, in_rows, lo_a, len_a);
+    const bool ok_b = gather_range(row_ptr_b, nnz_b, row, in_rows, lo_b, len_b);
+    // exclusive prefixes of the lengths over the wave (64-bit: ranges of malformed row
+    // pointers may overlap, and each is only checked against its nnz)
+    uint64_t inc_a = len_a, inc_b = len_b;
 #pragma unroll
     for (uint32_t d = 1; d < kGatherLanes; d <<= 1) {
-        const uint64_t y = __shfl_up(inc, d, kGatherLanes);
-        if (l >= d) inc += y;
+        const uint64_t ya = __shfl_up(inc_a, d, kGatherLanes);
+        const uint64_t yb = __shfl_up(inc_b, d, kGatherLanes);
+        if (l >= d) {
+            inc_a += ya;
+            inc_b += yb;
+        }
     }
-    const uint64_t off = inc - len;
-    sh.off[l] = off;
-    sh.lo[l] = lo;
-    sh.len[l] = len;
+    const uint64_t total_a = __shfl(inc_a, kGatherLanes - 1u, kGatherLanes);
+    const uint64_t total = total_a + __shfl(inc_b, kGatherLanes - 1u, kGatherLanes);
+    const uint64_t off_a = inc_a - len_a;
+    const uint64_t off_b = total_a + inc_b - len_b;
+    sh.off[l] = off_a;
+    sh.off[kGatherLanes + l] = off_b;
+    sh.lo[l] = lo_a;
+    sh.lo[kGatherLanes + l] = lo_b;
+    sh.len[l] = len_a;
+    sh.len[kGatherLanes + l] = len_b;
     sh.bad[l] = 0u;
-    if (l == kGatherLanes - 1u) sh.total = inc;
+    sh.bad[kGatherLanes + l] = 0u;
     __syncthreads();
-    const uint64_t total = sh.total;
-    acc = fr_zero();
+    Fr a = fr_zero(), b = fr_zero();
     for (uint64_t t0 = 0; t0 < total; t0 += kGatherLanes) {
         const uint64_t f = t0 + l;
         Fr p = fr_zero();
@@ -156,46 +185,31 @@ __device__ __forceinline__ bool gather_matrix(const uint32_t* row_ptr, const uin
             // successor's offset, so that row is the one holding f)
             uint32_t r = 0;
 #pragma unroll
-            for (uint32_t step = kGatherLanes / 2; step > 0; step >>= 1)
-                if (r + step < kGatherLanes && sh.off[r + step] <= f) r += step;
+            for (uint32_t step = kGatherLanes; step > 0; step >>= 1)
+                if (r + step < 2u * kGatherLanes && sh.off[r + step] <= f) r += step;
             const uint64_t j = f - sh.off[r];  // < len[r], so k < hi <= nnz
             if (j < sh.len[r]) {
+                const bool in_b = r >= kGatherLanes;
                 const uint32_t k = sh.lo[r] + (uint32_t)j;
-                const uint32_t s = signal[k];
+                const uint32_t s = (in_b ? signal_b : signal_a)[k];
+                const Fr v = ld_global((in_b ? value_b : value_a) + k);
                 if ((uint64_t)s < n_witness)
-                    p = fr_mul(ld_global(value + k), ld_global(witness + s));
+                    p = fr_mul29(v, ld_global(witness + s));
                 else
                     sh.bad[r] = 1u;
             }
         }
         sh.prod[l] = p;
         __syncthreads();
-        const uint64_t a0 = off > t0 ? off : t0;
-        const uint64_t a1 = off + len < t0 + kGatherLanes ? off + len : t0 + kGatherLanes;
-        for (uint64_t j = a0; j < a1; ++j) acc = fr_add(acc, sh.prod[j - t0]);
+        gather_add_round(a, sh, off_a, len_a, t0);
+        gather_add_round(b, sh, off_b, len_b, t0);
         __syncthreads();
     }
-    return ok && sh.bad[l] == 0u;
-}
-
-__global__ void __launch_bounds__(kGatherLanes) gather_kernel(
-    const uint32_t* row_ptr_a, const uint32_t* signal_a, const Fr* value_a, uint64_t nnz_a,
-    const uint32_t* row_ptr_b, const uint32_t* signal_b, const Fr* value_b, uint64_t nnz_b,
-    const Fr* witness, uint64_t n_witness, Fr* out_a, Fr* out_b, Fr* out_c, uint64_t n_rows) {
-    __shared__ GatherLds sh;
-    const uint64_t row = (uint64_t)blockIdx.x * kGatherLanes + threadIdx.x;
-    const bool in_rows = row < n_rows;
-    Fr a, b;
-    bool ok = gather_matrix(row_ptr_a, signal_a, value_a, nnz_a, witness, n_witness, row, in_rows,
-                            sh, a);
-    ok = gather_matrix(row_ptr_b, signal_b, value_b, nnz_b, witness, n_witness, row, in_rows, sh,
-                       b) &&
-         ok;
     if (!in_rows) return;
-    if (ok) {
+    if (ok_a && ok_b && sh.bad[l] == 0u && sh.bad[kGatherLanes + l] == 0u) {
         st_global(out_a + row, a);
         st_global(out_b + row, b);
-        st_global(out_c + row, fr_mul(a, b));
+        st_global(out_c + row, fr_mul29(a, b));
     } else {
         Fr bad = fr_invalid();
         st_global(out_a + row, bad);

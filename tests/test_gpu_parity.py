@@ -599,6 +599,49 @@ def test_gather_small(rows, n_witness):
         same(host(got), exp, "gather out_" + name)
 
 
+@pytest.mark.parametrize("rows,a_ne,b_ne,a_mean,b_mean", [
+    (1000, None, 0, 1.13, 1.70),   # B has no terms at all (nnz_b = 0)
+    (1000, 0, None, 1.13, 1.70),   # A has no terms at all
+    (777, 700, 650, 30.0, 50.0),   # long rows: a wave's terms span many 64-term rounds
+    (130, 130, 3, 95.0, 1.001),    # every A row at the cap, B nearly empty; ragged tail
+    (65, 1, 65, 1.001, 95.0),      # one A term, then every B row at the cap
+])
+def test_gather_row_mixes(rows, a_ne, b_ne, a_mean, b_mean):
+    """A's and B's terms of a wave are gathered as one list: shapes where one matrix is
+    empty, rows cross 64-term rounds, or the split between A and B falls anywhere."""
+    say("gather mix rows=%d a=%s/%g b=%s/%g" % (rows, a_ne, a_mean, b_ne, b_mean))
+    ma, mb, w = synth.gather_inputs(6, rows=rows, n_witness=500, a_nonempty=a_ne,
+                                    b_nonempty=b_ne, a_mean=a_mean, b_mean=b_mean)
+    oa, ob, oc = _gather_device(ma, mb, w)
+    want = oracle.gather(ma.row_ptr, ma.signal, oracle.to_mont(ma.value), mb.row_ptr,
+                         mb.signal, oracle.to_mont(mb.value), oracle.to_mont(w))
+    for got, exp, name in zip((oa, ob, oc), want, "abc"):
+        same(host(got), exp, "gather out_" + name)
+
+
+def test_gather_bad_b_range_spares_the_wave():
+    """A malformed B row (first index past its end) is flagged; the other rows of its
+    wave, whose terms share the wave's flattened list, are still exact."""
+    say("gather bad B range")
+    ma, mb, w = synth.gather_inputs(7, rows=200, n_witness=300, a_nonempty=200,
+                                    b_nonempty=200, a_mean=3.0, b_mean=4.0)
+    bad_row = 70
+    want = oracle.gather(ma.row_ptr, ma.signal, oracle.to_mont(ma.value), mb.row_ptr,
+                         mb.signal, oracle.to_mont(mb.value), oracle.to_mont(w))
+    rp = mb.row_ptr
+    mb.row_ptr = rp.copy()
+    mb.row_ptr[bad_row] = rp[bad_row + 1] + 1   # row 70: lo > hi; row 69 ends later
+    assert mb.row_ptr[bad_row] <= mb.nnz
+    oa, ob, oc = _gather_device(ma, mb, w)
+    ha, hb, hc = host(oa), host(ob), host(oc)
+    for hx in (ha, hb, hc):
+        assert (hx[bad_row] == 0xffffffff).all()
+    good = np.ones(200, bool)
+    good[bad_row - 1:bad_row + 1] = False   # the two rows whose ranges changed
+    for hx, exp, name in zip((ha, hb, hc), want, "abc"):
+        same(hx[good], exp[good], "gather out_%s, good rows" % name)
+
+
 def test_gather_bad_indices_are_flagged():
     say("gather bad indices")
     ma, mb, w = synth.gather_inputs(4, rows=300, n_witness=100)
