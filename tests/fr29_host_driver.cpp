@@ -9,6 +9,13 @@
 //   norm   x[0..8]            -> digits after fr29_normalize
 //   sub    a[0..8] b[0..8]    -> digits of a - b
 //   split  x                  -> digits of a canonical 256-bit value
+//   shl5   x                  -> digits of x 2^5 for a canonical x
+//   mmul   x[0..8] y[0..8]    -> digits of the radix-2^29 REDC product x y 2^-261
+//   redc1  x[0..8]            -> digits of x 2^-261
+//   mul29  a b                -> fr_mul29(a, b), canonical 256-bit value
+//   fm29   a                  -> fr_from_mont29(a), canonical 256-bit value
+//   join   a b x[0..8]        -> h = canon(REDC(a 2^5, b) - normalize(x)) and REDC(h 2^5):
+//                                the join epilogue's arithmetic on a transform's lazy x
 //   batch  K inv triv seed x_0 .. x_{2^K-1}
 //                             -> "ok M" or "bad i": one slice of 2^K canonical values run
 //                                through K passes in the transform kernels' schedule (see
@@ -210,6 +217,33 @@ int main() {
             V29 a = read_v(in);
             V29 b = read_v(in);
             print_v(fr29_sub(a, b).l);
+        } else if (op == "shl5") {
+            std::string h;
+            in >> h;
+            print_v(fr29_from_fr_shl5(parse_fr(h)).l);
+        } else if (op == "mmul") {
+            V29 x = read_v(in);
+            V29 y = read_v(in);
+            print_v(fr29_mont_mul(x, y).l);
+        } else if (op == "redc1") {
+            print_v(fr29_redc1(read_v(in)).l);
+        } else if (op == "mul29") {
+            std::string ha, hb;
+            in >> ha >> hb;
+            print_fr(fr_mul29(parse_fr(ha), parse_fr(hb)));
+        } else if (op == "fm29") {
+            std::string h;
+            in >> h;
+            print_fr(fr_from_mont29(parse_fr(h)));
+        } else if (op == "join") {
+            std::string ha, hb;
+            in >> ha >> hb;
+            V29 x = read_v(in);
+            const V29 ab = fr29_mont_mul(fr29_from_fr_shl5(parse_fr(ha)), fr29_from_fr(parse_fr(hb)));
+            const Fr h = fr29_canon(fr29_sub(ab, fr29_normalize(x)));
+            print_fr(h);
+            std::printf(" ");
+            print_fr(fr_from_mont29(h));
         } else if (op == "split") {
             std::string h;
             in >> h;

@@ -1,7 +1,9 @@
 """The library's 29-bit digit layer (fr29.hpp) compiled for the host and checked against
 Python integers: the table entry (w, floor(w 2^261 / r)) in balanced digits, the product
 by an entry for any 32-bit digits (both extremes of both signs), the carry-save
-normalization, the digit-wise subtraction and the final reduction to canonical form."""
+normalization, the digit-wise subtraction, the final reduction to canonical form, and the
+radix-2^29 Montgomery products of two variables (REDC with R' = 2^261) that the join and
+the gather use."""
 import os
 import random
 import subprocess
@@ -200,3 +202,102 @@ def test_batch_schedule_stays_in_int32(driver, K):
     assert worst <= 4 * (2**29 - 1)
     # the bound is nearly reached (the check exercises the worst path)
     assert worst > 3 * 2**29
+
+
+RINV261 = pow(1 << 261, -1, R)
+DMAX = 2**29 + 7              # the REDC product's input bound (normalized digits and more)
+
+
+def test_shl5_is_exact(driver):
+    rng = random.Random(7)
+    xs = [0, 1, R - 1, R - 2, 2**253] + [rng.randrange(R) for _ in range(300)]
+    got = run(driver, [("shl5", H(x)) for x in xs])
+    for x, line in zip(xs, got):
+        d = digits(line)
+        assert val(d) == x << 5 and all(0 <= v <= M for v in d)
+
+
+def test_redc_product_any_admissible_digits(driver):
+    """x y 2^-261 mod r for digit vectors at the bound of either sign (every column then
+    holds its largest sums), normalized forms, and canonical values; the result's digits
+    0..7 are 29-bit and, for non-negative inputs, its value is below x y / 2^261 + r."""
+    rng = random.Random(8)
+    cases = []
+    for t in range(3000):
+        kind = t % 6
+        if kind == 0:
+            x, y = [DMAX] * 9, [DMAX] * 9
+        elif kind == 1:
+            x, y = [-DMAX] * 9, [DMAX] * 9
+        elif kind == 2:
+            x = [rng.randrange(-DMAX, DMAX + 1) for _ in range(9)]
+            y = [rng.randrange(-DMAX, DMAX + 1) for _ in range(9)]
+        elif kind == 3:
+            x = [rng.randrange(-4, 2**29 + 3) for _ in range(8)] + [rng.randrange(-2**26, 2**26)]
+            y = split(rng.randrange(R))
+        elif kind == 4:  # the join's operands: a 2^5 and b
+            x, y = split(rng.randrange(R) << 5), split(rng.randrange(R))
+        else:
+            x = [rng.choice([0, M, DMAX, -DMAX, 2**29, 1]) for _ in range(9)]
+            y = [rng.choice([0, M, DMAX, -DMAX, 2**29, 1]) for _ in range(9)]
+        cases.append((x, y))
+    got = run(driver, [("mmul", D(x) + D(y)) for x, y in cases])
+    for (x, y), line in zip(cases, got):
+        z = digits(line)
+        assert all(0 <= v <= M for v in z[:8])
+        assert val(z) % R == val(x) * val(y) * RINV261 % R
+        if val(x) >= 0 and val(y) >= 0:
+            assert 0 <= val(z) < val(x) * val(y) // 2**261 + R
+
+
+def test_redc_one_operand(driver):
+    rng = random.Random(9)
+    xs = [[0] * 9, [M] * 9, split(R), split(R - 1)] + \
+         [[rng.randrange(0, 2**29) for _ in range(9)] for _ in range(1000)]
+    got = run(driver, [("redc1", D(x)) for x in xs])
+    for x, line in zip(xs, got):
+        z = digits(line)
+        assert val(z) % R == val(x) * RINV261 % R and 0 <= val(z) < 2 * R
+
+
+def test_montgomery_product_and_conversion(driver):
+    """fr_mul29 and fr_from_mont29 on canonical Montgomery words: a b 2^-256 mod r and
+    a 2^-256 mod r, canonical, on edge and random values."""
+    rng = random.Random(10)
+    rinv = pow(RR, -1, R)
+    vals = [0, 1, 2, R - 1, R - 2, RR % R, 2**253, (1 << 232) - 1, 2**29 - 1]
+    pairs = [(a, b) for a in vals for b in vals] + \
+            [(rng.randrange(R), rng.randrange(R)) for _ in range(2000)]
+    lines = []
+    for a, b in pairs:
+        lines.append(("mul29", H(a) + H(b)))
+        lines.append(("fm29", H(a)))
+    got = run(driver, lines)
+    for i, (a, b) in enumerate(pairs):
+        assert int(got[2 * i], 16) == a * b * rinv % R
+        assert int(got[2 * i + 1], 16) == a * rinv % R
+
+
+def test_join_arithmetic_on_lazy_digits(driver):
+    """The join epilogue's composition: h_mont = a b 2^-256 - x and h_std = h_mont 2^-256
+    for canonical a, b and a transform's lazy x, whose digits (two passes from normalized)
+    reach about 3 2^29 in magnitude."""
+    rng = random.Random(11)
+    rinv = pow(RR, -1, R)
+    lines, want = [], []
+    for t in range(2000):
+        a, b = rng.randrange(R), rng.randrange(R)
+        if t % 4 == 0:
+            x = [3 * 2**29] * 8 + [2**26]
+        elif t % 4 == 1:
+            x = [-3 * 2**29] * 8 + [-2**26]
+        else:
+            x = [rng.randrange(-3 * 2**29, 3 * 2**29) for _ in range(8)] + \
+                [rng.randrange(-2**26, 2**26)]
+        lines.append(("join", H(a) + H(b) + D(x)))
+        hm = (a * b * rinv - val(x)) % R
+        want.append((hm, hm * rinv % R))
+    got = run(driver, lines)
+    for line, (hm, hs) in zip(got, want):
+        g_hm, g_hs = line.split()
+        assert int(g_hm, 16) == hm and int(g_hs, 16) == hs

@@ -521,6 +521,54 @@ def test_extreme_values():
         ctx.release()
 
 
+def _const(v, n):
+    return np.tile(synth.ints_to_fr([v]), (n, 1))
+
+
+MONT_EXTREMES = [0, 1, 2, R - 1, R - 2, R - (1 << 29), 2**253, (1 << 232) - 1, (1 << 29) - 1]
+
+
+@pytest.mark.parametrize("log_n,radix2", [(12, None), (14, None), (20, None), (10, 1)])
+def test_join_operands_at_extremes(log_n, radix2):
+    """The join's product and conversion on extreme Montgomery words.  Constant evaluation
+    vectors have constant coset evaluations (the polynomial is a constant), so A' = A,
+    B' = B and C' = C reach the join as given, and H = A B - C holds element by element in
+    plain integers.  Covers the join of three kinds in one workgroup (2^12), the joins
+    after the register groups (2^14, 2^20) and after the radix-2 passes (2^10)."""
+    n = 1 << log_n
+    rinv = pow(1 << 256, -1, R)
+    triples = [(R - 1, R - 1, 0), (R - 1, R - 2, R - 1), (2**253, (1 << 232) - 1, 1),
+               (R - (1 << 29), R - 1, 2**253), (0, R - 1, R - 1), (1, 1, 2),
+               ((1 << 29) - 1, 2, R - 2)]
+    with Env(G16_RADIX2=radix2):
+        ctx = g.HContext(log_n)
+    for ea, eb, ec in triples:
+        say("join extremes log_n=%d radix2=%s (%x, %x, %x)" % (log_n, radix2, ea, eb, ec))
+        a, b, c = (g.to_device(_const(e, n)) for e in (ea, eb, ec))
+        hm, hs = ctx.h_compute(a, b, c)
+        h_std = (ea * rinv * eb * rinv - ec * rinv) % R
+        same(host(hs), _const(h_std, n), "h_std")
+        same(host(hm), _const(h_std * (1 << 256) % R, n), "h_mont")
+    ctx.release()
+
+
+def test_gather_extreme_values():
+    """Gather products on extreme coefficients and witness values (canonical standard
+    values at the edges of the range, and values whose Montgomery words are extreme)."""
+    say("gather extreme values")
+    ma, mb, w = synth.gather_inputs(8, rows=700, n_witness=64, a_mean=3.0, b_mean=3.0)
+    rinv = pow(1 << 256, -1, R)
+    ext = EDGE_INTS + [e * rinv % R for e in MONT_EXTREMES]
+    ma.value = synth.ints_to_fr([ext[i % len(ext)] for i in range(ma.nnz)])
+    mb.value = synth.ints_to_fr([ext[(3 * i + 1) % len(ext)] for i in range(mb.nnz)])
+    w = synth.ints_to_fr([ext[(5 * i + 2) % len(ext)] for i in range(64)])
+    oa, ob, oc = _gather_device(ma, mb, w)
+    want = oracle.gather(ma.row_ptr, ma.signal, oracle.to_mont(ma.value), mb.row_ptr,
+                         mb.signal, oracle.to_mont(mb.value), oracle.to_mont(w))
+    for got, exp, name in zip((oa, ob, oc), want, "abc"):
+        same(host(got), exp, "gather extreme out_" + name)
+
+
 def test_closed_forms_at_2_20():
     """Closed forms, no oracle: the forward transform of the unit vector at 0 is all ones and
     that of the all-ones vector is n at index 0; the inverse undoes both; the coset
