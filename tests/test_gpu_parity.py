@@ -276,12 +276,22 @@ def test_h_compute_workload_2_20():
 
 
 def test_h_compute_workload_2_22():
-    """The 2^22 workload (three batches, 8 + 7 + 7) in the benchmark's launch
-    configuration, every output of both encodings against the oracle's pipeline."""
+    """The 2^22 workload in the benchmark's launch configuration (the default plan,
+    8 + 6 + 8) and under the pages' near-equal split (8 + 7 + 7): every output of both
+    encodings against the oracle's pipeline."""
     log_n = 22
-    assert g.batch_plan(log_n) == [8, 7, 7]
-    ctx, _, _ = _h_case(log_n, workload=5)
-    ctx.release()
+    assert g.batch_plan(log_n) == [8, 6, 8]
+    assert g.batch_plan(log_n, 10) == [8, 7, 7]
+    (ad, bd, cd), (am, bm, cm) = h_inputs(5, log_n)
+    want_m, want_s = oracle.h_pipeline(log_n, am, bm, cm)
+    for kmax in (None, 10):
+        say("h_compute log_n=22 kmax=%s" % kmax)
+        with KMax(kmax):
+            ctx = g.HContext(log_n)
+        hm, hs = ctx.h_compute(ad, bd, cd)
+        same(host(hm), want_m, "h_mont 2^22 kmax=%s" % kmax)
+        same(host(hs), want_s, "h_std 2^22 kmax=%s" % kmax)
+        ctx.release()
 
 
 @pytest.mark.parametrize("log_n,plan", [(23, [8, 8, 7]), (24, [8, 8, 8])])
@@ -326,7 +336,7 @@ def _h_large(log_n, inputs, samples):
     cd = g.fr_mul(ad, bd)
     ctx = g.HContext(log_n)
     plan = g.batch_plan(log_n)
-    assert len(plan) == 3 and max(plan) - min(plan) <= 1 and plan == sorted(plan, reverse=True)
+    assert len(plan) == 3 and sum(plan) == log_n and 6 <= min(plan) and max(plan) <= 10
     hm, hs = ctx.h_compute(ad, bd, cd)
     if samples:
         am, bm = host(ad), host(bd)
@@ -355,7 +365,7 @@ def test_h_compute_2_24_sampled():
 
 @pytest.mark.parametrize("log_n", [25, 26])
 def test_large_domains(log_n):
-    """2^25 and 2^26 (three near-equal batches each): H at sampled outputs (the last
+    """2^25 and 2^26 (default plans 10 + 8 + 7 and 10 + 8 + 8): H at sampled outputs (the last
     one among them) against the oracle's barycentric route, the quotient-degree property
     on every output, the encodings on a prefix, and the transforms' round trip."""
     import torch
