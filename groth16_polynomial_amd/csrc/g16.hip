@@ -77,14 +77,14 @@ uint32_t plan_batches(uint32_t log_n, uint32_t kmax, uint32_t* ks) {
 }
 
 // The default plan: the near-equal split under a cap of 10 passes, except on the domains
-// where a plan of mostly even batches measured faster (2^21 -2.5%, 2^22 -3.0%, 2^25
-// -2.2%, 2^26 -2.4%; the same three batches, every batch 6..10 passes, so still no tiny
-// tail).  In the radix-4 geometry a batch of an odd number of passes ends in a one-pass
+// where a plan of mostly even batches measured faster (2^21 -2.5%, 2^22 -3.0%, 2^23 -1%,
+// 2^25 -2.2%, 2^26 -2.4%; the same three batches, every batch 6..10 passes, so still no
+// tiny tail).  In the radix-4 geometry a batch of an odd number of passes ends in a one-pass
 // register group, which loads, exchanges and stores its elements for half the products of
 // a two-pass group.  Lowest bits first.
 uint32_t default_plan(uint32_t log_n, uint32_t* ks) {
     static constexpr uint8_t kMeasured[][4] = {
-        {21, 6, 7, 8}, {22, 8, 6, 8}, {25, 10, 8, 7}, {26, 10, 8, 8}};
+        {21, 6, 7, 8}, {22, 8, 6, 8}, {23, 8, 7, 8}, {25, 10, 8, 7}, {26, 10, 8, 8}};
     for (const auto& m : kMeasured)
         if (m[0] == log_n) {
             for (int i = 0; i < 3; ++i) ks[i] = m[1 + i];

@@ -86,9 +86,9 @@ size_t g16_h_workspace_bytes(uint32_t log_n);
  * ones first (the NTT_CU page, "SHARED MEMORY BUDGET": 18 passes under a cap of 10
  * split 9 + 9, not 10 + 8).  kmax = 0: the library's default, which the environment
  * variable G16_MAX_K in [1, 12] overrides: the same split under a cap of 10, except
- * 2^21, 2^22, 2^25 and 2^26, which take the measured plans 6 + 7 + 8, 8 + 6 + 8,
- * 10 + 8 + 7 and 10 + 8 + 8 (mostly even batches: 2-3% faster there; results do not
- * depend on the plan).  Writes up to `cap` batch sizes, lowest bits first, and returns
+ * 2^21, 2^22, 2^23, 2^25 and 2^26, which take the measured plans 6 + 7 + 8, 8 + 6 + 8,
+ * 8 + 7 + 8, 10 + 8 + 7 and 10 + 8 + 8 (mostly even batches, no odd one at the top:
+ * 1-3% faster there; results do not depend on the plan).  Writes up to `cap` batch sizes, lowest bits first, and returns
  * the number of batches, or a negative code (G16_ERANGE for log_n, G16_EINVAL for
  * kmax > 12 or a NULL ks with cap > 0).  Host only; never touches the GPU. */
 int g16_batch_plan(uint32_t log_n, uint32_t kmax, uint32_t* ks, uint32_t cap);

@@ -104,10 +104,10 @@ def test_batch_plan_rule(lib, kmax):
 
 def test_default_batch_plan(lib, monkeypatch):
     """kmax = 0 without G16_MAX_K: the near-equal split under a cap of 10, except the
-    measured plans at 2^21, 2^22, 2^25 and 2^26; from 2^12 up every batch keeps 6..10
+    measured plans at 2^21, 2^22, 2^23, 2^25 and 2^26; from 2^12 up every batch keeps 6..10
     passes (no tiny tail)."""
     monkeypatch.delenv("G16_MAX_K", raising=False)
-    measured = {21: [6, 7, 8], 22: [8, 6, 8], 25: [10, 8, 7], 26: [10, 8, 8]}
+    measured = {21: [6, 7, 8], 22: [8, 6, 8], 23: [8, 7, 8], 25: [10, 8, 7], 26: [10, 8, 8]}
     for L in range(1, 28):
         ks = binding.batch_plan(L, 0)
         assert ks == measured.get(L, binding.batch_plan(L, 10)), L

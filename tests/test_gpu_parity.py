@@ -294,7 +294,7 @@ def test_h_compute_workload_2_22():
         ctx.release()
 
 
-@pytest.mark.parametrize("log_n,plan", [(23, [8, 8, 7]), (24, [8, 8, 8])])
+@pytest.mark.parametrize("log_n,plan", [(23, [8, 7, 8]), (24, [8, 8, 8])])
 def test_ntt_large(log_n, plan):
     """Standalone transforms at 2^23 and 2^24 (three batches): forward and inverse against
     the oracle's whole output, and the round trip."""
@@ -353,7 +353,7 @@ def _h_large(log_n, inputs, samples):
 
 
 def test_h_compute_2_23_full():
-    """2^23 (8 + 8 + 7), every output of both encodings against the oracle's pipeline."""
+    """2^23 (8 + 7 + 8), every output of both encodings against the oracle's pipeline."""
     ctx, _, _ = _h_case(23, workload=6)
     ctx.release()
 
