@@ -18,6 +18,7 @@
 struct g16_bb_ctx {
     uint32_t log_n;
     const uint2* tw;
+    const uint32_t* twm;
     const uint8_t* ws_begin;
     size_t ws_bytes;
 };
@@ -26,6 +27,16 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr uint32_t kMaxBatchK = 8;
+// The later batches of matrices of at most 2^kMontMaxLogW columns take the 4-byte
+// Montgomery-form twiddles: with one or two columns a twiddle serves only one or two
+// elements of a row, so the table is as large as the data and its bytes bind; with more
+// columns each entry is shared and the Shoup product's two fewer instructions win.
+#ifndef G16_BB_MONT_MAX_LW
+#define G16_BB_MONT_MAX_LW 1
+#endif
+constexpr int kMontMaxLogW = G16_BB_MONT_MAX_LW;
+
+size_t round_up(size_t b) { return (b + kAlign - 1) / kAlign * kAlign; }
 
 std::mutex g_bb_mu;
 std::unordered_set<const g16_bb_ctx*> g_bb_live;
@@ -42,24 +53,31 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 template <int K>
-hipError_t launch_k(bool head, const g16::BbParams& p, uint32_t blocks, hipStream_t s) {
+hipError_t launch_k(bool head, bool mont, const g16::BbParams& p, uint32_t blocks,
+                    hipStream_t s) {
     const uint32_t spw = 1u << p.log_spw;
     const uint32_t threads = spw * ((1u << K) / g16::kBbE);
     const size_t lds = (size_t)(spw + 1u) * (1u << K) * 4u;
     if (head)
-        hipLaunchKernelGGL((g16::bb_batch_kernel<K, true>), dim3(blocks), dim3(threads), lds, s, p);
+        hipLaunchKernelGGL((g16::bb_batch_kernel<K, true, false>), dim3(blocks), dim3(threads),
+                           lds, s, p);
+    else if (mont)
+        hipLaunchKernelGGL((g16::bb_batch_kernel<K, false, true>), dim3(blocks), dim3(threads),
+                           lds, s, p);
     else
-        hipLaunchKernelGGL((g16::bb_batch_kernel<K, false>), dim3(blocks), dim3(threads), lds, s, p);
+        hipLaunchKernelGGL((g16::bb_batch_kernel<K, false, false>), dim3(blocks),
+                           dim3(threads), lds, s, p);
     return hipGetLastError();
 }
 
-hipError_t launch_batch(bool head, const g16::BbParams& p, uint32_t blocks, hipStream_t s) {
+hipError_t launch_batch(bool head, bool mont, const g16::BbParams& p, uint32_t blocks,
+                        hipStream_t s) {
     switch (p.k) {
-        case 4: return launch_k<4>(head, p, blocks, s);
-        case 5: return launch_k<5>(head, p, blocks, s);
-        case 6: return launch_k<6>(head, p, blocks, s);
-        case 7: return launch_k<7>(head, p, blocks, s);
-        case 8: return launch_k<8>(head, p, blocks, s);
+        case 4: return launch_k<4>(head, mont, p, blocks, s);
+        case 5: return launch_k<5>(head, mont, p, blocks, s);
+        case 6: return launch_k<6>(head, mont, p, blocks, s);
+        case 7: return launch_k<7>(head, mont, p, blocks, s);
+        case 8: return launch_k<8>(head, mont, p, blocks, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -70,8 +88,8 @@ extern "C" {
 
 size_t g16_bb_workspace_bytes(uint32_t log_n) {
     if (log_n < 1 || log_n > G16_BB_MAX_LOG_N) return 0;
-    const size_t bytes = ((size_t(1) << log_n) - 1) * sizeof(uint2);
-    return (bytes + kAlign - 1) / kAlign * kAlign;
+    const size_t entries = (size_t(1) << log_n) - 1;
+    return round_up(entries * sizeof(uint2)) + round_up(entries * sizeof(uint32_t));
 }
 
 int g16_bb_batch_plan(uint32_t log_n, uint32_t* ks, uint32_t cap) {
@@ -99,10 +117,12 @@ int g16_bb_prepare(uint32_t log_n, void* workspace, size_t workspace_bytes, void
     if (!c) return G16_EINVAL;
     c->log_n = log_n;
     c->tw = (const uint2*)workspace;
+    c->twm = (const uint32_t*)((const uint8_t*)workspace +
+                               round_up(((size_t(1) << log_n) - 1) * sizeof(uint2)));
     c->ws_begin = (const uint8_t*)workspace;
     c->ws_bytes = need;
     hipLaunchKernelGGL(g16::bb_table_kernel, dim3(1024), dim3(256), 0, (hipStream_t)stream,
-                       (uint2*)workspace, log_n);
+                       (uint2*)workspace, (uint32_t*)c->twm, log_n);
     if (hipGetLastError() != hipSuccess) {
         delete c;
         return G16_EHIP;
@@ -142,6 +162,7 @@ int g16_bb_lde(g16_bb_ctx* ctx, uint32_t log_in, uint32_t log_w, uint64_t count,
     p.src = (const uint32_t*)in_mont;
     p.dst = (uint32_t*)out_mont;
     p.tw = ctx->tw;
+    p.twm = ctx->twm;
     p.in_stride = in_elems;
     p.out_stride = out_elems;
     p.log_n = L;
@@ -166,7 +187,8 @@ int g16_bb_lde(g16_bb_ctx* ctx, uint32_t log_in, uint32_t log_w, uint64_t count,
         if (b > 0) p.src = p.dst;
         const uint64_t blocks = (uint64_t)p.groups * count;
         if (blocks >= (1ull << 31)) return G16_EINVAL;
-        if (launch_batch(b == 0, p, (uint32_t)blocks, s) != hipSuccess) return G16_EHIP;
+        const bool mont = (int)log_w <= kMontMaxLogW;
+        if (launch_batch(b == 0, mont, p, (uint32_t)blocks, s) != hipSuccess) return G16_EHIP;
         s0 += K;
     }
     return G16_OK;

@@ -28,7 +28,10 @@
 // never loaded.
 //
 // Twiddles: level b of the table holds w_(2^(b+1))^j for j < 2^b at offset 2^b - 1 (the
-// same entries for every domain size), each as (w, floor(w 2^32 / p)); in a batch at s0
+// same entries for every domain size), each as (w, floor(w 2^32 / p)), and a second table
+// holds the same entries as w 2^32 mod p (4 bytes, a Montgomery product: two more
+// instructions, half the bytes; the later batches of matrices of one or two columns read
+// this one, since there each entry serves one or two rows' elements only); in a batch at s0
 // the pass on row bit b = s0 + t of the pair whose lower element is slice element m needs
 // j = (the slice's row bits below s0) + (m mod 2^t) 2^s0, so neighbouring slices read
 // neighbouring entries.
@@ -65,6 +68,7 @@ struct BbParams {
     const uint32_t* src;  // input matrices (first batch), else == dst
     uint32_t* dst;
     const uint2* tw;      // levels of (w, w')
+    const uint32_t* twm;  // the same levels as w 2^32 mod p
     uint64_t in_stride;   // elements from one input matrix to the next
     uint64_t out_stride;  // elements from one output matrix to the next
     uint32_t log_n;       // L: rows of an output matrix, log2
@@ -90,7 +94,8 @@ __device__ __forceinline__ uint32_t bb_insert(uint32_t c, uint32_t q, uint32_t b
 
 // Grid: groups * matrices workgroups of (SPW 2^K / 16) threads; LDS (SPW + 1) 2^K words.
 // HEAD: the first batch (s0 = 0), staged load through the bit reversal and staged store.
-template <int K, bool HEAD>
+// MONT: products by the 4-byte Montgomery-form table (later batches only).
+template <int K, bool HEAD, bool MONT>
 __global__ void __launch_bounds__(512) bb_batch_kernel(BbParams p) {
     extern __shared__ uint32_t lds[];
     constexpr uint32_t SLICE = 1u << K;
@@ -184,14 +189,20 @@ __global__ void __launch_bounds__(512) bb_batch_kernel(BbParams p) {
         for (uint32_t t = 0; t < r; ++t) {
             const uint32_t b = s0 + b0 + t;  // row bit of this pass
             const uint2* level = p.tw + ((1u << b) - 1u);
+            const uint32_t* mlevel = p.twm + ((1u << b) - 1u);
 #pragma unroll
             for (uint32_t e = 0; e < 16; ++e) {
                 if ((e >> t) & 1u) continue;  // e is the upper element of its pair
                 const uint32_t hi = e + (1u << t);
                 const uint32_t m = m_of(e);
                 const uint32_t j = low_row + ((m & ((1u << (b0 + t)) - 1u)) << s0);
-                const uint2 wv = bb_at(level, j);
-                const uint32_t tt = bb_shoup(x[hi], wv.x, wv.y);
+                uint32_t tt;
+                if constexpr (MONT) {
+                    tt = bb_mont_mul(x[hi], bb_at(mlevel, j));
+                } else {
+                    const uint2 wv = bb_at(level, j);
+                    tt = bb_shoup(x[hi], wv.x, wv.y);
+                }
                 x[hi] = bb_sub(x[e], tt);
                 x[e] = bb_add(x[e], tt);
             }
@@ -227,8 +238,9 @@ __global__ void __launch_bounds__(512) bb_batch_kernel(BbParams p) {
 }
 
 // Table entries: level b (0 <= b < L) at offset 2^b - 1 holds (w^j, floor(w^j 2^32 / p))
-// for j < 2^b, w a primitive 2^(b+1)-th root.  One thread per entry.
-__global__ void bb_table_kernel(uint2* tw, uint32_t log_n) {
+// in tw and w^j 2^32 mod p in twm, for j < 2^b, w a primitive 2^(b+1)-th root.  One thread
+// per entry.
+__global__ void bb_table_kernel(uint2* tw, uint32_t* twm, uint32_t log_n) {
     const uint64_t total = (1ull << log_n) - 1u;
     for (uint64_t e = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
          e += (uint64_t)gridDim.x * blockDim.x) {
@@ -236,6 +248,7 @@ __global__ void bb_table_kernel(uint2* tw, uint32_t log_n) {
         const uint32_t j = (uint32_t)(e + 1u - (1ull << b));
         const uint32_t w = bb_pow_plain(bb_root(b + 1u), j);
         tw[e] = make_uint2(w, bb_shoup_companion(w));
+        twm[e] = (uint32_t)(((uint64_t)w << 32) % kBbP);
     }
 }
 

@@ -297,8 +297,9 @@ typedef struct g16_bb_ctx g16_bb_ctx; /* opaque host object, owned by the librar
 #define G16_BB_MAX_LOG_N 27u
 #define G16_BB_MAX_LOG_W 10u
 
-/* Bytes of device workspace for the twiddle levels of a 2^log_n domain ((2^log_n - 1)
- * entries of 8 bytes, rounded up to 256), or 0 for log_n outside [1, 27]. */
+/* Bytes of device workspace for the twiddle levels of a 2^log_n domain: (2^log_n - 1)
+ * entries of 8 bytes (w and its Shoup companion) and the same entries again as 4 bytes
+ * (Montgomery form), each table rounded up to 256 bytes; 0 for log_n outside [1, 27]. */
 size_t g16_bb_workspace_bytes(uint32_t log_n);
 
 /* The pass batches of a 2^log_n transform (lowest bits first; at most 8 passes each,

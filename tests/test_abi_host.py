@@ -52,6 +52,15 @@ def test_workspace_bytes(lib):
         assert binding.workspace_bytes(L) == 3 * rnd(n * 80) + 3 * rnd(n * 32) + rnd(4 * 80)
 
 
+def test_bb_workspace_bytes(lib):
+    f = lib.g16_bb_workspace_bytes
+    assert f(0) == 0 and f(28) == 0
+    rnd = lambda x: -(-x // 256) * 256
+    for L in (1, 2, 12, 20, 27):
+        e = (1 << L) - 1
+        assert f(L) == rnd(8 * e) + rnd(4 * e)   # Shoup pairs, then the 4-byte form
+
+
 def test_batch_scratch_bytes(lib):
     f = lib.g16_h_batch_scratch_bytes
     assert f(0, 1) == 0 and f(28, 1) == 0            # log_n out of range
