@@ -404,8 +404,10 @@ def _batch_case(log_n, proofs, kmax=None, seed=300, narrow=None):
 @pytest.mark.parametrize("log_n,proofs,kmax,narrow", [
     (1, 3, None, None), (5, 4, None, None), (9, 2, 4, None), (10, 3, None, None),
     (12, 5, None, None), (13, 3, 4, None), (16, 3, None, None), (18, 2, None, None),
-    (8, 3, None, 1), (12, 3, None, 1), (14, 2, None, 1), (16, 2, None, 1), (12, 2, None, 0)])
+    (8, 3, None, 1), (12, 3, None, 1), (14, 2, None, 1), (16, 2, None, 1), (12, 2, None, 0),
+    (21, 2, None, None)])
 def test_h_compute_batch(log_n, proofs, kmax, narrow):
+    """(21, 2): three batches of the measured default plan (6 + 7 + 8) over two proofs."""
     ctx, _, _ = _batch_case(log_n, proofs, kmax, narrow=narrow)
     ctx.release()
 
