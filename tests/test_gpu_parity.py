@@ -679,6 +679,19 @@ def test_gather_row_mixes(rows, a_ne, b_ne, a_mean, b_mean):
         same(host(got), exp, "gather out_" + name)
 
 
+@pytest.mark.parametrize("rows,n_witness", [(1, 1), (70, 1), (64, 2)])
+def test_gather_tiny(rows, n_witness):
+    """One row; a one-slot witness (every signal 0); exactly one wave of rows."""
+    say("gather tiny rows=%d n_witness=%d" % (rows, n_witness))
+    ma, mb, w = synth.gather_inputs(9, rows=rows, n_witness=n_witness, a_nonempty=rows,
+                                    b_nonempty=rows, a_mean=2.0, b_mean=3.0)
+    oa, ob, oc = _gather_device(ma, mb, w)
+    want = oracle.gather(ma.row_ptr, ma.signal, oracle.to_mont(ma.value), mb.row_ptr,
+                         mb.signal, oracle.to_mont(mb.value), oracle.to_mont(w))
+    for got, exp, name in zip((oa, ob, oc), want, "abc"):
+        same(host(got), exp, "gather out_" + name)
+
+
 def test_gather_bad_b_range_spares_the_wave():
     """A malformed B row (first index past its end) is flagged; the other rows of its
     wave, whose terms share the wave's flattened list, are still exact."""
