@@ -4,6 +4,8 @@
 One step = one g16_h_compute over device-resident inputs at n = 2^20 (A, B seeded
 uniform Fr, C = A o B, tables prepared beforehand): three inverse NTTs, the coset
 shift, three forward NTTs and H = A'B' - C' in both encodings.  Prints one JSON line.
+The K timed steps follow --settle-ms of untimed pipelines (the chip reaches its working
+clock only after some tens of ms of sustained load) and the W warmup steps.
 
 Also measured (same run, reported inside the line):
   * each kernel (stage) of the pipeline alone, with HIP events on the stream it is
@@ -56,6 +58,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed pipelines run before the warmup steps, in ms of wall time")
     ap.add_argument("--log-n", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-side", action="store_true",
@@ -192,18 +196,35 @@ def traffic_from_profiles(stage_name: str, src_hash: str):
 
 
 class Timer:
-    """HIP events on torch's current stream, which is the stream the library launches on."""
+    """HIP events on torch's current stream, which is the stream the library launches on.
 
-    def __init__(self, torch):
+    From idle the chip needs some tens of milliseconds of sustained load to reach its
+    working clock (2^20 pipelines back to back after 2 s idle: 0.68 ms a step for the
+    first 20, 0.48-0.50 ms from about 60 ms on), and the host work between legs lets it
+    fall back, so every measurement first runs its call untimed for settle_ms."""
+
+    def __init__(self, torch, settle_ms=50.0):
         self.torch = torch
         self.stream = torch.cuda.current_stream()
         self.e0 = torch.cuda.Event(enable_timing=True)
         self.e1 = torch.cuda.Event(enable_timing=True)
+        self.settle_ms = settle_ms
+
+    def settle(self, fn, ms=None, warm=3):
+        """Runs fn untimed at least `warm` times and for at least `ms` milliseconds of
+        wall time (in chunks, each waited for); returns the number of calls."""
+        ms = self.settle_ms if ms is None else ms
+        end = time.perf_counter() + ms / 1e3
+        calls = 0
+        while calls < warm or time.perf_counter() < end:
+            for _ in range(max(1, warm)):
+                fn()
+            calls += max(1, warm)
+            self.torch.cuda.synchronize()
+        return calls
 
     def mean_ms(self, fn, reps, warm=3):
-        for _ in range(warm):
-            fn()
-        self.torch.cuda.synchronize()
+        self.settle(fn, warm=warm)
         self.e0.record(self.stream)
         for _ in range(reps):
             fn()
@@ -214,9 +235,7 @@ class Timer:
     def median_ms(self, fn, reps, warm=3):
         """Median over reps calls, each between its own pair of events."""
         torch = self.torch
-        for _ in range(warm):
-            fn()
-        torch.cuda.synchronize()
+        self.settle(fn, warm=warm)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(reps)]
         for a, b in evs:
@@ -386,7 +405,7 @@ def main():
     ctx = g.HContext(log_n)
     hm, hs = g.empty_fr(n), g.empty_fr(n)
     stream = torch.cuda.current_stream()
-    tm = Timer(torch)
+    tm = Timer(torch, settle_ms=min(50.0, args.settle_ms))
     torch.cuda.synchronize()
     line_extra = {}
     if args.part == "probe":
@@ -545,7 +564,9 @@ def main():
 
         line_extra["bb_lde"] = bb_leg(g, synth, torch, tm, args.steps, log)
 
-    # ---- the timed region: K whole pipelines
+    # ---- the timed region: K whole pipelines, after args.settle_ms of untimed pipelines
+    # (the chip at its working clock, see Timer) and the W warmup steps
+    settle_calls = tm.settle(lambda: ctx.h_compute(ad, bd, cd, hm, hs), args.settle_ms, warm=8)
     for _ in range(args.warmup):
         ctx.h_compute(ad, bd, cd, hm, hs)
     torch.cuda.synchronize()
@@ -619,6 +640,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"ms": args.settle_ms, "untimed_pipelines": settle_calls},
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "strong",
