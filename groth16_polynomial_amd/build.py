@@ -23,6 +23,14 @@ FLAGS = [
     "-Wall",
 ]
 
+# The narrow-geometry units (small launches, each thread's chain of dependent products
+# sets the time) are scheduled for instruction-level parallelism.
+UNIT_FLAGS = {"_narrow.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+
+
+def unit_flags(unit: str) -> list:
+    return [f for suffix, fl in UNIT_FLAGS.items() if unit.endswith(suffix) for f in fl]
+
 
 def sources() -> list:
     csrc = os.path.join(PKG, "csrc")
@@ -57,7 +65,8 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     for u in units:
         obj = os.path.join(objdir, u.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([HIPCC, *compile_flags, *inc, "-c", "-o", obj, os.path.join(csrc, u)])
+        cmds.append([HIPCC, *compile_flags, *unit_flags(u), *inc, "-c", "-o", obj,
+                     os.path.join(csrc, u)])
     probe_tmp = PROBE_LIB + ".tmp%d" % os.getpid()
     cmds.append([HIPCC, *FLAGS, "-o", probe_tmp, os.path.join(csrc, "probe", "mad_rate.hip")])
     with ThreadPoolExecutor(max_workers=jobs) as ex:

@@ -24,11 +24,19 @@ hipError_t launch_geom(const BatchParams& p, uint32_t n_vec, hipStream_t stream)
     return hipGetLastError();
 }
 
+#ifndef G16_GROUP_NARROW
 template <int K, Mode M, bool JOIN>
-hipError_t launch_groups(const BatchParams& p, uint32_t n_vec, bool narrow, hipStream_t stream) {
-    if (narrow)
-        return launch_geom<K, 1, narrow_slices_per_wg(K, M), M, JOIN>(p, n_vec, stream);
+hipError_t launch_groups_wide(const BatchParams& p, uint32_t n_vec, hipStream_t stream) {
     return launch_geom<K, kGroupPasses, slices_per_wg(K, M), M, JOIN>(p, n_vec, stream);
+}
+
+#define G16_INST(M, J)                                                                   \
+    template hipError_t launch_groups_wide<G16_GROUP_K, M, J>(const BatchParams&, uint32_t, \
+                                                              hipStream_t);
+#else
+template <int K, Mode M, bool JOIN>
+hipError_t launch_groups_narrow(const BatchParams& p, uint32_t n_vec, hipStream_t stream) {
+    return launch_geom<K, 1, narrow_slices_per_wg(K, M), M, JOIN>(p, n_vec, stream);
 }
 
 template <int K, Mode M>
@@ -40,21 +48,22 @@ hipError_t launch_groups_join3(const BatchParams& p, uint32_t n_proof, hipStream
     }
 }
 
-template hipError_t launch_groups<G16_GROUP_K, Mode::HeadBitrev, false>(const BatchParams&, uint32_t,
-                                  bool, hipStream_t);
-template hipError_t launch_groups<G16_GROUP_K, Mode::FwdStrided, false>(const BatchParams&, uint32_t,
-                                  bool, hipStream_t);
-template hipError_t launch_groups<G16_GROUP_K, Mode::FwdStrided, true>(const BatchParams&, uint32_t,
-                                  bool, hipStream_t);
-template hipError_t launch_groups<G16_GROUP_K, Mode::InvStrided, false>(const BatchParams&, uint32_t,
-                                  bool, hipStream_t);
-template hipError_t launch_groups<G16_GROUP_K, Mode::Fused, false>(const BatchParams&, uint32_t,
-                                  bool, hipStream_t);
-template hipError_t launch_groups<G16_GROUP_K, Mode::Fused, true>(const BatchParams&, uint32_t,
-                                  bool, hipStream_t);
 template hipError_t launch_groups_join3<G16_GROUP_K, Mode::FwdStrided>(const BatchParams&,
                                                                       uint32_t, hipStream_t);
 template hipError_t launch_groups_join3<G16_GROUP_K, Mode::Fused>(const BatchParams&, uint32_t,
                                                                  hipStream_t);
+
+#define G16_INST(M, J)                                                                     \
+    template hipError_t launch_groups_narrow<G16_GROUP_K, M, J>(const BatchParams&, uint32_t, \
+                                                                hipStream_t);
+#endif
+
+G16_INST(Mode::HeadBitrev, false)
+G16_INST(Mode::FwdStrided, false)
+G16_INST(Mode::FwdStrided, true)
+G16_INST(Mode::InvStrided, false)
+G16_INST(Mode::Fused, false)
+G16_INST(Mode::Fused, true)
+#undef G16_INST
 
 }  // namespace g16

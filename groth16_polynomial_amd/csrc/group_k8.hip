@@ -1,4 +1,4 @@
-// Register-group batch kernels (radix-4 groups of two passes, or one pass in the narrow
-// geometry) for k = 8 passes per batch.
+// Register-group batch kernels in the radix-4 geometry (groups of two passes) for
+// k = 8 passes per batch.
 #define G16_GROUP_K 8
 #include "group_inst.hpp"

@@ -1,0 +1,5 @@
+// Register-group batch kernels in the narrow geometry (one pass per group) for k = 9
+// passes per batch, with the three-kind last batch of small launches.
+#define G16_GROUP_K 9
+#define G16_GROUP_NARROW 1
+#include "group_inst.hpp"

@@ -20,8 +20,19 @@ constexpr int kGroupPasses = G16_GROUP_PASSES;
 // radix-4 groups (GroupGeomFor<K, kGroupPasses, M>) or, with narrow, one pass per group
 // (NarrowGeomFor<K, M>).  2^(log_n - K) must be at least the geometry's slices per
 // workgroup.
+// The two geometries are instantiated in separate units (group_kK.hip and
+// group_kK_narrow.hip), which the build compiles with different scheduling.
 template <int K, Mode M, bool JOIN>
-hipError_t launch_groups(const BatchParams& p, uint32_t n_vec, bool narrow, hipStream_t stream);
+hipError_t launch_groups_wide(const BatchParams& p, uint32_t n_vec, hipStream_t stream);
+template <int K, Mode M, bool JOIN>
+hipError_t launch_groups_narrow(const BatchParams& p, uint32_t n_vec, hipStream_t stream);
+
+template <int K, Mode M, bool JOIN>
+inline hipError_t launch_groups(const BatchParams& p, uint32_t n_vec, bool narrow,
+                                hipStream_t stream) {
+    return narrow ? launch_groups_narrow<K, M, JOIN>(p, n_vec, stream)
+                  : launch_groups_wide<K, M, JOIN>(p, n_vec, stream);
+}
 
 // The last launch of the pipeline (M = FwdStrided or Fused, with the join) in the narrow
 // geometry with the three kinds of a proof in one workgroup, over n_proof proofs
